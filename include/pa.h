@@ -1,0 +1,169 @@
+/*
+ * pa.h -- C ABI of the MI355X (gfx950) paged split-KV decode library (libpa.so).
+ *
+ * One decode step is three asynchronous calls on one HIP stream:
+ *
+ *   pa_plan    length-proportional work planner: splits every request's KV range into a number of
+ *              partitions proportional to its context length, under a workgroup budget of
+ *              budget_mult x CU and a per-request ceiling (ROCm/ATOM PR #2366 "Route the paged decode
+ *              to aiter's FlyDSL kernel with work planner", sections 1 and 3; ROCm/ATOM PR #2514
+ *              "adapt the FlyDSL paged decode to aiter #5809 (explicit work plans)", Design).
+ *   pa_decode  split-KV grouped-query decode over a block-table KV cache: one partial softmax state per
+ *              (plan slot, query token, query head).  Query token i of a request with L query tokens
+ *              and KV length S sees keys [0, S - (L - 1 - i)) (opengfx1030/vllm-rdna PR #29, Change 1).
+ *   pa_merge   log-sum-exp merge of a request's partials into the output rows; rows past the last
+ *              cumulative query length and rows with no visible key are written as exact zeros
+ *              (same vllm-rdna page, Change 1; ATOM #2366 review, "Claims checked and not upheld").
+ *
+ * Conventions shared by every entry point:
+ *   - All array arguments are DEVICE pointers (memory of the current HIP device), except where a
+ *     parameter says host.  The caller owns all memory; the library allocates nothing, keeps no
+ *     global state, never synchronises and never copies device to host.  Every call is stream-ordered
+ *     and may be captured in a HIP graph.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   - Integer arrays are int32, contiguous.  Floating arrays are contiguous, innermost dimension last.
+ *   - Storage types: PA_F32 (IEEE binary32), PA_BF16 (bfloat16), PA_FP8_E4M3 (OCP E4M3 "fn" codes,
+ *     dequantised value = decoded code x per-tensor scale).
+ *   - Host-side argument checks run before any launch; a failing check returns a nonzero status and
+ *     launches nothing.  Device-side preconditions (in-range block ids for every key below S, query
+ *     lengths <= max_q_len, non-decreasing cumulative lengths, num_rows >= last cumulative length,
+ *     non-negative context lengths) cannot be checked without a synchronisation; kernels clamp their
+ *     indexing so a violation gives unspecified values in the affected rows but no out-of-bounds access.
+ *
+ * Memory layouts:
+ *   q, out         [num_rows, num_q_heads, head_dim]
+ *   k_cache,       [num_blocks, num_kv_heads, block_size, head_dim]   (one page = block_size tokens)
+ *   v_cache
+ *   block_tables   [num_seqs, max_blocks_per_seq]   page ids; entries past a request's last page unused
+ *   context_lens   [num_seqs]                       S_b, the request's KV length (query tokens included)
+ *   cu_query_lens  [num_seqs + 1] or NULL           cumulative query lengths; NULL = one row per request
+ *   work_info      [capacity, 4]  (request, tile_begin, tile_end, S_b); unused slots (-1, 0, 0, 0)
+ *   reduce_info    [num_seqs, 2]  (first_slot, num_partitions)
+ *   num_work       [1]            number of used slots
+ *   workspace      pa_workspace_bytes(...) bytes of fp32 partials, written by pa_decode, read by pa_merge
+ *
+ * Query head h reads kv head h / (num_q_heads / num_kv_heads).
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PA_F32 = 0,
+    PA_BF16 = 1,
+    PA_FP8_E4M3 = 2
+} pa_dtype;
+
+typedef enum {
+    PA_OK = 0,
+    PA_INVALID_ARG = 1,   /* null pointer, negative size, inconsistent shapes or dtypes */
+    PA_UNSUPPORTED = 2,   /* valid but outside what the kernels implement (head_dim, block size, ...) */
+    PA_CAPACITY = 3,      /* plan capacity or workspace smaller than the call needs */
+    PA_HIP_ERROR = 4      /* a HIP runtime call or kernel launch failed */
+} pa_status;
+
+/* Limits of this implementation (checked on the host). */
+#define PA_MAX_SEQS 8192           /* pa_plan keeps per-request prefix sums in LDS */
+#define PA_MAX_GROUP_ROWS 64       /* (num_q_heads / num_kv_heads) x max_q_len */
+
+/*
+ * Number of plan slots a batch needs:
+ *   min(num_seqs x max_partitions, max(num_seqs, ceil(budget_mult x cu_count / num_kv_heads)))
+ * (ATOM #2366 review item 3).  Pure host arithmetic; no device access.
+ * Returns PA_INVALID_ARG for num_seqs < 0, any other argument < 1, or a null capacity_out.
+ */
+pa_status pa_plan_capacity(int32_t num_seqs, int32_t num_kv_heads, int32_t cu_count,
+                           int32_t budget_mult, int32_t max_partitions, int32_t* capacity_out);
+
+/*
+ * Bytes of workspace pa_decode writes and pa_merge reads for a plan of `capacity` slots:
+ * fp32 partial outputs [capacity, max_q_len, num_q_heads, head_dim] followed by fp32
+ * (max, sum) pairs [capacity, max_q_len, num_q_heads, 2], each region 256-byte aligned.
+ * Returns 0 if any argument is < 1 (capacity may be 0) or the size overflows.
+ */
+size_t pa_workspace_bytes(int32_t capacity, int32_t max_q_len, int32_t num_q_heads, int32_t head_dim);
+
+/*
+ * Build the work plan on the device from context_lens (device, [num_seqs]).
+ *   tile_tokens   partition granularity in tokens (256 in the pages' deployment)
+ *   capacity      length of work_info; must be >= pa_plan_capacity(...) for the same arguments
+ * Apportionment: every request with S_b > 0 gets
+ *   min(max_partitions, ceil(S_b / tile_tokens), 1 + floor((C - B') S_b / W))
+ * partitions, C = the capacity formula, B' = number of requests with S_b > 0, W = sum S_b (64-bit);
+ * requests with S_b = 0 get none.  Partition j of request b covers tiles
+ * [floor(j tiles_b / parts_b), floor((j + 1) tiles_b / parts_b)).  Every slot of work_info is
+ * rewritten (unused ones to (-1, 0, 0, 0)), so a plan never carries data from an earlier call.
+ * Negative S_b (a precondition violation) are planned as 0.
+ * Errors: PA_INVALID_ARG (null pointers, num_seqs < 0, arguments < 1), PA_UNSUPPORTED
+ * (num_seqs > PA_MAX_SEQS), PA_CAPACITY (capacity too small), PA_HIP_ERROR (launch failure).
+ */
+pa_status pa_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
+                  int32_t cu_count, int32_t budget_mult, int32_t max_partitions,
+                  int32_t tile_tokens, int32_t capacity, int32_t* work_info, int32_t* reduce_info,
+                  int32_t* num_work, void* stream);
+
+/*
+ * Split-KV decode: for every used plan slot w = (b, tile_begin, tile_end, .) and kv head g, one
+ * workgroup computes, for each query token i of request b and each query head h of group g, the
+ * softmax state of the keys [tile_begin x T, min(tile_end x T, S_b)) intersected with the token's
+ * visible range [0, S_b - (L_b - 1 - i)):
+ *   m = max score, l = sum exp(score - m), acc = sum exp(score - m) v,   score = scale x k_scale x (q . k)
+ * (V is multiplied by v_scale), stored unnormalised in the workspace; a slot/token with no visible
+ * key stores m = -inf, l = 0, acc = 0.
+ * Arguments:
+ *   q, q_dtype                 [num_rows, num_q_heads, head_dim], PA_F32 or PA_BF16
+ *   k_cache, v_cache, kv_dtype [num_blocks, num_kv_heads, block_size, head_dim], PA_F32/PA_BF16/PA_FP8_E4M3
+ *   block_tables               [num_seqs, max_blocks_per_seq]
+ *   context_lens               [num_seqs]
+ *   cu_query_lens              [num_seqs + 1] or NULL (then row b is request b's only token)
+ *   max_q_len                  upper bound on every request's query length (1 when cu is NULL)
+ *   scale, k_scale, v_scale    softmax scale (typically 1/sqrt(head_dim)) and per-tensor dequant scales
+ *   work_info, num_work        the plan from pa_plan (capacity slots)
+ *   tile_tokens                the plan's tile size; a multiple of block_size
+ *   workspace                  >= pa_workspace_bytes(capacity, max_q_len, num_q_heads, head_dim)
+ * Supported: head_dim in {64, 128, 256}; block_size in {16, 64, 128};
+ * (num_q_heads / num_kv_heads) x max_q_len <= PA_MAX_GROUP_ROWS.
+ * KV types bf16 and fp8 run on the matrix cores in bf16 (fp8 codes widen exactly to bf16; q is
+ * rounded to bf16; probabilities are rounded to bf16 for the P.V product; accumulation is fp32).
+ * KV type f32 runs in fp32 on the vector ALUs.
+ */
+pa_status pa_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t num_q_heads,
+                    int32_t head_dim, const void* k_cache, const void* v_cache, pa_dtype kv_dtype,
+                    int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t num_seqs, const int32_t* cu_query_lens,
+                    int32_t max_q_len, float scale, float k_scale, float v_scale,
+                    const int32_t* work_info, const int32_t* num_work, int32_t capacity,
+                    int32_t tile_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Log-sum-exp merge.  For output row r and head h: the owning request b is found by binary search
+ * of r in cu_query_lens (row b when NULL); token i = r - cu[b].  Over the request's partials j with
+ * l_j > 0:  M = max m_j,  out = sum_j e^(m_j - M) acc_j / sum_j e^(m_j - M) l_j, rounded to nearest
+ * even in out_dtype.  Rows r >= cu[num_seqs] (or >= num_seqs without cu), requests without
+ * partitions, and rows whose partials are all empty are written as +0.0.  Every element of out
+ * ([num_rows, num_q_heads, head_dim]) is written.
+ * out_dtype must equal the q dtype given to pa_decode (PA_F32 or PA_BF16).
+ */
+pa_status pa_merge(int32_t num_rows, int32_t num_q_heads, int32_t head_dim, int32_t num_seqs,
+                   const int32_t* cu_query_lens, int32_t max_q_len, const int32_t* reduce_info,
+                   int32_t capacity, const void* workspace, size_t workspace_bytes, void* out,
+                   pa_dtype out_dtype, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* pa_status_string(pa_status status);
+
+/* Compute-unit count of a HIP device (the cu_count the planner's budget is built from). */
+pa_status pa_device_cu_count(int32_t device, int32_t* cu_count_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

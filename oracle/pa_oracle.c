@@ -60,17 +60,25 @@ static double orc_fp8e4m3_to_double(uint8_t code) {
     return sign ? -mag : mag;
 }
 
+/* The 256 e4m3fn values, filled once from orc_fp8e4m3_to_double (a lookup, not a different rule). */
+static double orc_fp8_table[256];
+static pthread_once_t orc_fp8_once = PTHREAD_ONCE_INIT;
+static void orc_fp8_fill(void) {
+    for (int c = 0; c < 256; ++c) orc_fp8_table[c] = orc_fp8e4m3_to_double((uint8_t)c);
+}
+
 static double orc_load(const void* base, int dtype, int64_t idx) {
     switch (dtype) {
         case ORC_F32: return (double)((const float*)base)[idx];
         case ORC_BF16: return orc_bf16_to_double(((const uint16_t*)base)[idx]);
-        case ORC_FP8E4M3: return orc_fp8e4m3_to_double(((const uint8_t*)base)[idx]);
+        case ORC_FP8E4M3: return orc_fp8_table[((const uint8_t*)base)[idx]];
         default: return NAN;
     }
 }
 
 int orc_decode_array(const void* src, int dtype, int64_t n, double* dst) {
     if (dtype != ORC_F32 && dtype != ORC_BF16 && dtype != ORC_FP8E4M3) return ORC_INVALID;
+    pthread_once(&orc_fp8_once, orc_fp8_fill);
     for (int64_t i = 0; i < n; ++i) dst[i] = orc_load(src, dtype, i);
     return ORC_OK;
 }
@@ -353,6 +361,7 @@ static int orc_check(const orc_problem* p) {
 static int orc_run(orc_problem* p, int mode, const int32_t* work, const int32_t* reduce,
                    int tile_tokens, double* out, int nthreads) {
     if (orc_check(p)) return ORC_INVALID;
+    pthread_once(&orc_fp8_once, orc_fp8_fill);
     const int64_t D = p->head_dim;
     /* rows not owned by any request (graph padding past the last cumulative length) are zero */
     memset(out, 0, sizeof(double) * (size_t)p->num_rows * p->num_q_heads * D);
@@ -402,6 +411,7 @@ int orc_attention_rows(ORC_PROBLEM_ARGS, const int32_t* rows, const int32_t* hea
                        double* out) {
     ORC_FILL(p);
     if (orc_check(&p)) return ORC_INVALID;
+    pthread_once(&orc_fp8_once, orc_fp8_fill);
     const int D = head_dim;
     int64_t max_ctx = 1;
     for (int b = 0; b < num_seqs; ++b)

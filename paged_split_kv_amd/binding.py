@@ -1,0 +1,214 @@
+"""Thin Python binding over libpa.so (include/pa.h).  Argument marshalling only.
+
+Every function has the name of the C entry point it calls.  Tensors are passed as raw device
+pointers with the current torch stream; no computation of the decode path happens here.  If the
+library is not built, every call raises: there is no fallback path.
+
+torch must be imported before the library is loaded so that libpa.so binds to the same HIP runtime
+(libamdhip64.so.7) that owns torch's device memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpa.so")
+
+PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+PA_OK, PA_INVALID_ARG, PA_UNSUPPORTED, PA_CAPACITY, PA_HIP_ERROR = 0, 1, 2, 3, 4
+PA_MAX_SEQS = 8192
+PA_MAX_GROUP_ROWS = 64
+
+_DTYPE_OF_NAME = {"f32": PA_F32, "bf16": PA_BF16, "fp8": PA_FP8_E4M3}
+_TORCH_OF_NAME = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
+
+SYMBOLS = ("pa_plan_capacity", "pa_workspace_bytes", "pa_plan", "pa_decode", "pa_merge",
+           "pa_status_string", "pa_device_cu_count")
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libpa.so once.  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m paged_split_kv_amd.build` "
+                           "(the decode path has no fallback)")
+    lib = ctypes.CDLL(path)
+    i32 = ctypes.c_int32
+    vp = ctypes.c_void_p
+    f32 = ctypes.c_float
+    lib.pa_plan_capacity.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(i32)]
+    lib.pa_plan_capacity.restype = ctypes.c_int
+    lib.pa_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.pa_workspace_bytes.restype = ctypes.c_size_t
+    lib.pa_plan.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]
+    lib.pa_plan.restype = ctypes.c_int
+    lib.pa_decode.argtypes = [vp, ctypes.c_int, i32, i32, i32, vp, vp, ctypes.c_int, i32, i32, i32,
+                              vp, i32, vp, i32, vp, i32, f32, f32, f32, vp, vp, i32, i32, vp,
+                              ctypes.c_size_t, vp]
+    lib.pa_decode.restype = ctypes.c_int
+    lib.pa_merge.argtypes = [i32, i32, i32, i32, vp, i32, vp, i32, vp, ctypes.c_size_t, vp,
+                             ctypes.c_int, vp]
+    lib.pa_merge.restype = ctypes.c_int
+    lib.pa_status_string.argtypes = [ctypes.c_int]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_device_cu_count.argtypes = [i32, ctypes.POINTER(i32)]
+    lib.pa_device_cu_count.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().pa_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != PA_OK:
+        raise PaError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, device=None) -> None:
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+# ---------------------------------------------------------------------------------------------
+# C entry points
+# ---------------------------------------------------------------------------------------------
+
+def pa_plan_capacity(num_seqs: int, num_kv_heads: int, cu_count: int, budget_mult: int = 2,
+                     max_partitions: int = 256) -> int:
+    out = ctypes.c_int32(0)
+    _check(load().pa_plan_capacity(num_seqs, num_kv_heads, cu_count, budget_mult, max_partitions,
+                                   ctypes.byref(out)), "pa_plan_capacity")
+    return int(out.value)
+
+
+def pa_workspace_bytes(capacity: int, max_q_len: int, num_q_heads: int, head_dim: int) -> int:
+    return int(load().pa_workspace_bytes(capacity, max_q_len, num_q_heads, head_dim))
+
+
+def pa_device_cu_count(device: Optional[int] = None) -> int:
+    dev = torch.cuda.current_device() if device is None else int(device)
+    out = ctypes.c_int32(0)
+    _check(load().pa_device_cu_count(dev, ctypes.byref(out)), "pa_device_cu_count")
+    return int(out.value)
+
+
+def pa_plan(context_lens: torch.Tensor, num_kv_heads: int, *, cu_count: int, budget_mult: int = 2,
+            max_partitions: int = 256, tile_tokens: int = 256, capacity: Optional[int] = None,
+            work_info: Optional[torch.Tensor] = None, reduce_info: Optional[torch.Tensor] = None,
+            num_work: Optional[torch.Tensor] = None, stream=None
+            ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Plan on the device.  Returns (work_info [capacity, 4], reduce_info [B, 2], num_work [1]),
+    all int32 on the device of context_lens; passed-in buffers are refilled in place."""
+    _need(context_lens, "context_lens", torch.int32)
+    dev = context_lens.device
+    B = int(context_lens.shape[0])
+    if capacity is None:
+        capacity = pa_plan_capacity(B, num_kv_heads, cu_count, budget_mult, max_partitions)
+    if work_info is None:
+        work_info = torch.empty((capacity, 4), dtype=torch.int32, device=dev)
+    if reduce_info is None:
+        reduce_info = torch.empty((B, 2), dtype=torch.int32, device=dev)
+    if num_work is None:
+        num_work = torch.empty((1,), dtype=torch.int32, device=dev)
+    _need(work_info, "work_info", torch.int32, dev)
+    _need(reduce_info, "reduce_info", torch.int32, dev)
+    _need(num_work, "num_work", torch.int32, dev)
+    if work_info.numel() < 4 * capacity or reduce_info.numel() < 2 * B:
+        raise ValueError("plan buffers smaller than capacity / num_seqs")
+    _check(load().pa_plan(_ptr(context_lens), B, num_kv_heads, cu_count, budget_mult, max_partitions,
+                          tile_tokens, capacity, _ptr(work_info), _ptr(reduce_info), _ptr(num_work),
+                          _stream(stream)), "pa_plan")
+    return work_info, reduce_info, num_work
+
+
+def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_dtype: str,
+              block_tables: torch.Tensor, context_lens: torch.Tensor, work_info: torch.Tensor,
+              num_work: torch.Tensor, workspace: torch.Tensor, *, scale: float,
+              cu_query_lens: Optional[torch.Tensor] = None, max_q_len: int = 1,
+              k_scale: float = 1.0, v_scale: float = 1.0, tile_tokens: int = 256,
+              stream=None) -> None:
+    """Split-KV decode into the workspace (see include/pa.h).  kv_dtype is "f32", "bf16" or
+    "fp8" (uint8 tensors holding OCP e4m3fn codes)."""
+    dev = q.device
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("q must be float32 or bfloat16")
+    _need(q, "q", q.dtype)
+    _need(k_cache, "k_cache", _TORCH_OF_NAME[kv_dtype], dev)
+    _need(v_cache, "v_cache", _TORCH_OF_NAME[kv_dtype], dev)
+    _need(block_tables, "block_tables", torch.int32, dev)
+    _need(context_lens, "context_lens", torch.int32, dev)
+    _need(work_info, "work_info", torch.int32, dev)
+    _need(num_work, "num_work", torch.int32, dev)
+    _need(workspace, "workspace", torch.uint8, dev)
+    if cu_query_lens is not None:
+        _need(cu_query_lens, "cu_query_lens", torch.int32, dev)
+    R, Hq, D = q.shape
+    nb, Hkv, bs, D2 = k_cache.shape
+    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shapes do not match q")
+    B = int(context_lens.shape[0])
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs, max_blocks]")
+    if cu_query_lens is not None and cu_query_lens.shape[0] != B + 1:
+        raise ValueError("cu_query_lens must be [num_seqs + 1]")
+    capacity = int(work_info.shape[0])
+    _check(load().pa_decode(_ptr(q), PA_F32 if q.dtype == torch.float32 else PA_BF16, R, Hq, D,
+                            _ptr(k_cache), _ptr(v_cache), _DTYPE_OF_NAME[kv_dtype], nb, Hkv, bs,
+                            _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), B,
+                            _ptr(cu_query_lens), max_q_len, scale, k_scale, v_scale,
+                            _ptr(work_info), _ptr(num_work), capacity, tile_tokens, _ptr(workspace),
+                            workspace.numel(), _stream(stream)), "pa_decode")
+
+
+def pa_merge(out: torch.Tensor, reduce_info: torch.Tensor, workspace: torch.Tensor, *, capacity: int,
+             cu_query_lens: Optional[torch.Tensor] = None, max_q_len: int = 1, stream=None) -> None:
+    """Log-sum-exp merge of the workspace into out ([R, Hq, D], float32 or bfloat16), in place."""
+    dev = out.device
+    if out.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out must be float32 or bfloat16")
+    _need(out, "out", out.dtype)
+    _need(reduce_info, "reduce_info", torch.int32, dev)
+    _need(workspace, "workspace", torch.uint8, dev)
+    if cu_query_lens is not None:
+        _need(cu_query_lens, "cu_query_lens", torch.int32, dev)
+    R, Hq, D = out.shape
+    B = int(reduce_info.shape[0])
+    _check(load().pa_merge(R, Hq, D, B, _ptr(cu_query_lens), max_q_len, _ptr(reduce_info), capacity,
+                           _ptr(workspace), workspace.numel(), _ptr(out),
+                           PA_F32 if out.dtype == torch.float32 else PA_BF16, _stream(stream)),
+           "pa_merge")

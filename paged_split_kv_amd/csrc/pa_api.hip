@@ -1,0 +1,183 @@
+// pa_api.hip -- the C ABI of libpa: host-side argument checks and kernel launches.
+//
+// Every check below runs before any launch and returns a status; nothing here allocates, copies,
+// synchronises or reads device memory.
+#include <limits.h>
+
+#include "pa_device.h"
+
+namespace {
+
+bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+bool supported_head_dim(int d) { return d == 64 || d == 128 || d == 256; }
+bool supported_block_size(int bs) { return bs == 16 || bs == 64 || bs == 128; }
+
+pa_status capacity_formula(int32_t num_seqs, int32_t num_kv_heads, int32_t cu_count,
+                           int32_t budget_mult, int32_t max_partitions, int32_t* out) {
+    if (num_seqs < 0 || num_kv_heads < 1 || cu_count < 1 || budget_mult < 1 || max_partitions < 1)
+        return PA_INVALID_ARG;
+    const long long budget = ((long long)budget_mult * cu_count + num_kv_heads - 1) / num_kv_heads;
+    const long long a = (long long)num_seqs * max_partitions;
+    const long long b = num_seqs > budget ? (long long)num_seqs : budget;
+    const long long c = a < b ? a : b;
+    if (c > INT_MAX) return PA_INVALID_ARG;
+    *out = (int32_t)c;
+    return PA_OK;
+}
+
+pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_HIP_ERROR; }
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_plan_capacity(int32_t num_seqs, int32_t num_kv_heads, int32_t cu_count,
+                           int32_t budget_mult, int32_t max_partitions, int32_t* capacity_out) {
+    if (!capacity_out) return PA_INVALID_ARG;
+    return capacity_formula(num_seqs, num_kv_heads, cu_count, budget_mult, max_partitions, capacity_out);
+}
+
+size_t pa_workspace_bytes(int32_t capacity, int32_t max_q_len, int32_t num_q_heads, int32_t head_dim) {
+    if (capacity < 0 || max_q_len < 1 || num_q_heads < 1 || head_dim < 1) return 0;
+    const unsigned long long states = (unsigned long long)capacity * max_q_len * num_q_heads;
+    if (states > (1ull << 40)) return 0;
+    return pa::workspace_acc_bytes(capacity, max_q_len, num_q_heads, head_dim) +
+           pa::workspace_ml_bytes(capacity, max_q_len, num_q_heads);
+}
+
+pa_status pa_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
+                  int32_t cu_count, int32_t budget_mult, int32_t max_partitions,
+                  int32_t tile_tokens, int32_t capacity, int32_t* work_info, int32_t* reduce_info,
+                  int32_t* num_work, void* stream) {
+    if (num_seqs < 0 || tile_tokens < 1 || capacity < 0) return PA_INVALID_ARG;
+    if (!num_work || (num_seqs > 0 && (!context_lens || !reduce_info)) || (capacity > 0 && !work_info))
+        return PA_INVALID_ARG;
+    if ((work_info && !aligned(work_info, 16)) || (reduce_info && !aligned(reduce_info, 8)))
+        return PA_INVALID_ARG;
+    if (num_seqs > PA_MAX_SEQS) return PA_UNSUPPORTED;
+    int32_t cap = 0;
+    pa_status st = capacity_formula(num_seqs, num_kv_heads, cu_count, budget_mult, max_partitions, &cap);
+    if (st != PA_OK) return st;
+    if (capacity < cap) return PA_CAPACITY;
+    return from_hip(pa::launch_plan(context_lens, num_seqs, cap, capacity, max_partitions, tile_tokens,
+                                    work_info, reduce_info, num_work, pa::as_stream(stream)));
+}
+
+pa_status pa_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t num_q_heads,
+                    int32_t head_dim, const void* k_cache, const void* v_cache, pa_dtype kv_dtype,
+                    int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t num_seqs, const int32_t* cu_query_lens,
+                    int32_t max_q_len, float scale, float k_scale, float v_scale,
+                    const int32_t* work_info, const int32_t* num_work, int32_t capacity,
+                    int32_t tile_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+    if (num_rows < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_blocks < 0 || num_seqs < 0 ||
+        max_blocks_per_seq < 0 || max_q_len < 1 || capacity < 0 || tile_tokens < 1 || head_dim < 1 ||
+        block_size < 1)
+        return PA_INVALID_ARG;
+    if (q_dtype != PA_F32 && q_dtype != PA_BF16) return PA_INVALID_ARG;
+    if (kv_dtype != PA_F32 && kv_dtype != PA_BF16 && kv_dtype != PA_FP8_E4M3) return PA_INVALID_ARG;
+    if (num_q_heads % num_kv_heads != 0) return PA_INVALID_ARG;
+    if (!cu_query_lens && (max_q_len != 1 || num_rows < num_seqs)) return PA_INVALID_ARG;
+    if (!(scale == scale) || !(k_scale == k_scale) || !(v_scale == v_scale)) return PA_INVALID_ARG;
+    if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PA_UNSUPPORTED;
+    if (tile_tokens % block_size != 0) return PA_UNSUPPORTED;
+    const int group = num_q_heads / num_kv_heads;
+    if ((long long)group * max_q_len > PA_MAX_GROUP_ROWS) return PA_UNSUPPORTED;
+    if (capacity > 0) {
+        if (!work_info || !num_work || !workspace) return PA_INVALID_ARG;
+        if (num_seqs > 0 && (!q || !k_cache || !v_cache || !block_tables || !context_lens))
+            return PA_INVALID_ARG;
+    }
+    if ((q && !aligned(q, 16)) || (k_cache && !aligned(k_cache, 16)) || (v_cache && !aligned(v_cache, 16)) ||
+        (work_info && !aligned(work_info, 16)) || (workspace && !aligned(workspace, 256)))
+        return PA_INVALID_ARG;
+    const size_t need = pa_workspace_bytes(capacity, max_q_len, num_q_heads, head_dim);
+    if (capacity > 0 && (need == 0 || workspace_bytes < need)) return PA_CAPACITY;
+    if (capacity == 0 || num_seqs == 0) return PA_OK;
+
+    pa::DecodeArgs a;
+    a.q = q;
+    a.k_cache = static_cast<const uint8_t*>(k_cache);
+    a.v_cache = static_cast<const uint8_t*>(v_cache);
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.cu = cu_query_lens;
+    a.work_info = reinterpret_cast<const int4*>(work_info);
+    a.num_work = num_work;
+    a.ws_acc = static_cast<float*>(workspace);
+    a.ws_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                       pa::workspace_acc_bytes(capacity, max_q_len, num_q_heads, head_dim));
+    a.num_rows = num_rows;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = group;
+    a.num_blocks = num_blocks;
+    a.block_size = block_size;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_seqs = num_seqs;
+    a.max_q_len = max_q_len;
+    a.capacity = capacity;
+    a.tile_tokens = tile_tokens;
+    a.score_scale_log2 = scale * k_scale * pa::kLog2e;
+    a.v_scale = v_scale;
+    return from_hip(pa::launch_decode(a, head_dim, kv_dtype, q_dtype == PA_F32, pa::as_stream(stream)));
+}
+
+pa_status pa_merge(int32_t num_rows, int32_t num_q_heads, int32_t head_dim, int32_t num_seqs,
+                   const int32_t* cu_query_lens, int32_t max_q_len, const int32_t* reduce_info,
+                   int32_t capacity, const void* workspace, size_t workspace_bytes, void* out,
+                   pa_dtype out_dtype, void* stream) {
+    if (num_rows < 0 || num_q_heads < 1 || num_seqs < 0 || max_q_len < 1 || capacity < 0)
+        return PA_INVALID_ARG;
+    if (out_dtype != PA_F32 && out_dtype != PA_BF16) return PA_INVALID_ARG;
+    if (!cu_query_lens && max_q_len != 1) return PA_INVALID_ARG;
+    if (!supported_head_dim(head_dim)) return PA_UNSUPPORTED;
+    if (num_rows > 0 && !out) return PA_INVALID_ARG;
+    if (num_seqs > 0 && (!reduce_info || (capacity > 0 && !workspace))) return PA_INVALID_ARG;
+    if ((reduce_info && !aligned(reduce_info, 8)) || (workspace && !aligned(workspace, 256)))
+        return PA_INVALID_ARG;
+    const size_t need = pa_workspace_bytes(capacity, max_q_len, num_q_heads, head_dim);
+    if (capacity > 0 && (need == 0 || workspace_bytes < need)) return PA_CAPACITY;
+    if ((long long)num_rows * num_q_heads > (long long)INT_MAX) return PA_UNSUPPORTED;
+    if (num_rows == 0) return PA_OK;
+
+    pa::MergeArgs a;
+    a.cu = cu_query_lens;
+    a.reduce_info = reinterpret_cast<const int2*>(reduce_info);
+    a.ws_acc = static_cast<const float*>(workspace);
+    a.ws_ml = workspace ? reinterpret_cast<const float*>(
+                              static_cast<const uint8_t*>(workspace) +
+                              pa::workspace_acc_bytes(capacity, max_q_len, num_q_heads, head_dim))
+                        : nullptr;
+    a.out = out;
+    a.num_rows = num_rows;
+    a.num_q_heads = num_q_heads;
+    a.num_seqs = (capacity > 0) ? num_seqs : 0;   // without slots every row is zero
+    a.max_q_len = max_q_len;
+    a.capacity = capacity;
+    return from_hip(pa::launch_merge(a, head_dim, out_dtype == PA_BF16, pa::as_stream(stream)));
+}
+
+const char* pa_status_string(pa_status status) {
+    switch (status) {
+        case PA_OK: return "ok";
+        case PA_INVALID_ARG: return "invalid argument";
+        case PA_UNSUPPORTED: return "unsupported configuration";
+        case PA_CAPACITY: return "plan capacity or workspace too small";
+        case PA_HIP_ERROR: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+pa_status pa_device_cu_count(int32_t device, int32_t* cu_count_out) {
+    if (!cu_count_out) return PA_INVALID_ARG;
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
+        return PA_HIP_ERROR;
+    *cu_count_out = v;
+    return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,510 @@
+// pa_decode.hip -- split-KV grouped-query paged decode on gfx950 (MI355X).
+//
+// What is computed (opengfx1030/vllm-rdna PR #29, Change item 1; ROCm/ATOM PR #2366 sections 1 and 3):
+// for every plan slot w = (request b, tiles [tb, te)) and kv head g, the softmax state of the keys
+// [tb*T, min(te*T, S_b)) for each query token i of request b (visible keys [0, S_b - (L_b-1-i))) and
+// each query head of group g.  The state (running max m in base-2 units, sum l, unnormalised acc)
+// goes to the workspace; pa_merge combines a request's slots.
+//
+// Design (bf16 / fp8 caches, the matrix-core kernel):
+//  * one workgroup of 4 waves per (slot, kv head).  The slot's keys are cut into 16-key chunks (a
+//    chunk never straddles a page: pages hold 16, 64 or 128 tokens and slots start on tile
+//    boundaries); wave w takes chunks w, w+4, ...; the 4 states are merged in LDS at the end.
+//  * all query rows of the group -- G heads x L verify tokens, M = G*L <= 64 -- form the columns
+//    of 16-wide MFMA blocks, so each K/V byte is read from HBM once per (slot, kv head) whatever L is.
+//  * each chunk's K and V (16 x D each) are fetched with 16-byte coalesced loads two chunks ahead into
+//    registers, written to a per-wave LDS buffer with an XOR swizzle on the 16-byte column, and read
+//    back in matrix-core operand order.  Rows past the slot's last key are written as zeros, so
+//    whatever a page holds past the context (even NaN) never reaches the products.
+//  * S^T = K . Q^T on v_mfma_f32_16x16x32_bf16: output lane l holds query row (l & 15) and keys
+//    4*(l >> 4) + j, so the per-row softmax max needs only 2 cross-lane steps and the probabilities
+//    are already in the B-operand order of O^T = V^T . P^T on v_mfma_f32_16x16x16_bf16, whose
+//    output lane again holds query row (l & 15): the per-row rescale factors stay in-lane.
+//  * fp8 (OCP e4m3fn) codes are widened exactly to bf16 in registers; k_scale folds into the score
+//    scale and v_scale into the final state.  Probabilities are rounded to bf16 for P.V.
+// The fp32-cache kernel is plain vector code (fp32 throughout) with the same outputs.
+#include "pa_device.h"
+
+namespace pa {
+
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// Request geometry of slot work item: first row, query length (clamped), KV length.
+struct SlotInfo {
+    int b, row0, L, S;
+    int k_lo, k_hi;   // key range of the slot
+};
+
+__device__ __forceinline__ bool slot_info(const DecodeArgs& a, int slot, SlotInfo& si) {
+    if (slot >= a.capacity) return false;
+    const int used = *a.num_work;
+    if (slot >= used) return false;
+    const int4 w = a.work_info[slot];
+    const int b = w.x;
+    if (b < 0 || b >= a.num_seqs) return false;
+    const int S = max(a.context_lens[b], 0);
+    int row0, L;
+    if (a.cu) {
+        row0 = a.cu[b];
+        L = a.cu[b + 1] - row0;
+    } else {
+        row0 = b;
+        L = 1;
+    }
+    L = min(max(L, 0), a.max_q_len);
+    if (row0 < 0 || row0 >= a.num_rows) L = 0;
+    else L = min(L, a.num_rows - row0);
+    // keys covered by this slot, clipped to the context and to the block table's reach
+    const long long lo = static_cast<long long>(max(w.y, 0)) * a.tile_tokens;
+    long long hi = static_cast<long long>(max(w.z, 0)) * a.tile_tokens;
+    hi = min(hi, static_cast<long long>(S));
+    hi = min(hi, static_cast<long long>(a.max_blocks) * a.block_size);
+    si.b = b;
+    si.row0 = row0;
+    si.L = L;
+    si.S = S;
+    si.k_lo = static_cast<int>(min(lo, static_cast<long long>(S)));
+    si.k_hi = static_cast<int>(max(hi, static_cast<long long>(si.k_lo)));
+    return true;
+}
+
+// ---------------------------------------------------------------------------------------------
+// matrix-core kernel (bf16 or fp8 caches)
+// ---------------------------------------------------------------------------------------------
+template <int D, int NCB, bool KV8, bool QF32>
+struct Mfma {
+    static constexpr int ESZ = KV8 ? 1 : 2;            // bytes per cache element
+    static constexpr int RB = D * ESZ;                 // bytes per cache row (one token, one kv head)
+    static constexpr int CPR = RB / 16;                // 16-byte columns per row
+    static constexpr int SWM = (CPR < 16 ? CPR : 16) - 1;  // XOR swizzle mask on the column index
+    static constexpr int NLD = 16 * RB / 1024;         // 16-byte loads per lane per 16-row chunk
+    static constexpr int KSTEPS = D / 32;              // k-steps of the S^T product
+    static constexpr int DT = D / 16;                  // 16-wide d tiles of the P.V product
+    static constexpr int WAVE_LDS = 2 * 16 * RB;       // K then V chunk, per wave
+    static constexpr int STAGE_LDS = 4 * WAVE_LDS;
+    static constexpr int ROWS = 16 * NCB;              // query rows per workgroup (padded)
+    static constexpr int APITCH = D + 4;               // fp32 pitch of the LDS merge buffer
+    static constexpr int MERGE_LDS = (4 * ROWS + 2 * ROWS + ROWS * APITCH) * 4;
+    static constexpr int LDS = STAGE_LDS > MERGE_LDS ? STAGE_LDS : MERGE_LDS;
+    static constexpr int PF = 2;                       // chunks in flight per wave
+};
+
+template <int D, int NCB, bool KV8, bool QF32>
+__global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
+    using C = Mfma<D, NCB, KV8, QF32>;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int slot = blockIdx.x / a.num_kv_heads;
+    const int g = blockIdx.x - slot * a.num_kv_heads;
+
+    SlotInfo si;
+    if (!slot_info(a, slot, si)) return;
+    const int G = a.group;
+    const int M = G * si.L;                       // valid query rows (<= ROWS)
+    const int col = lane & 15;                    // MFMA column = query row within a block
+    const int grp = lane >> 4;                    // 4 lane groups
+
+    // ---- query operands (B of S^T = K.Q^T): qop[cb][s] = q[row][32s + 8*grp .. +8] as bf16 ----
+    bf16x8_t qop[NCB][C::KSTEPS];
+    int nvis[NCB];                                // keys visible to this lane's query row
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        const int n = 16 * cb + col;
+        const bool valid = n < M;
+        const int i = valid ? n / G : 0;
+        const int h = g * G + (valid ? n - i * G : 0);
+        nvis[cb] = valid ? si.S - (si.L - 1 - i) : 0;
+        const size_t qoff = (static_cast<size_t>(si.row0 + i) * a.num_q_heads + h) * D;
+#pragma unroll
+        for (int s = 0; s < C::KSTEPS; ++s) {
+            const int d0 = 32 * s + 8 * grp;
+            u32x4_t v = {0u, 0u, 0u, 0u};
+            if (valid) {
+                if constexpr (QF32) {
+                    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + qoff + d0);
+                    const float4 x = p[0], y = p[1];
+                    v[0] = pack_bf16x2(x.x, x.y);
+                    v[1] = pack_bf16x2(x.z, x.w);
+                    v[2] = pack_bf16x2(y.x, y.y);
+                    v[3] = pack_bf16x2(y.z, y.w);
+                } else {
+                    v = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.q) + qoff + d0);
+                }
+            }
+            qop[cb][s] = __builtin_bit_cast(bf16x8_t, v);
+        }
+    }
+
+    float m_run[NCB], l_run[NCB];
+    float4_t acc[NCB][C::DT];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        m_run[cb] = -INFINITY;
+        l_run[cb] = 0.f;
+#pragma unroll
+        for (int t = 0; t < C::DT; ++t) acc[cb][t] = float4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const int nkeys = si.k_hi - si.k_lo;
+    const int nchunks = nkeys > 0 ? (nkeys + 15) >> 4 : 0;
+    const int* bt_row = a.block_tables + static_cast<size_t>(si.b) * a.max_blocks;
+    const size_t head_stride = static_cast<size_t>(a.block_size) * C::RB;   // bytes per (block, kv head)
+    uint8_t* wlds = lds + wave * C::WAVE_LDS;
+    uint8_t* klds = wlds;
+    uint8_t* vlds = wlds + 16 * C::RB;
+
+    // Page ids of this wave's chunks, one per lane, refreshed every 64 chunks of the wave.
+    int pages = -1;
+    int pages_base = -1;
+    auto chunk_block = [&](int c) -> int {
+        const int k = (c - wave) >> 2;            // this wave's chunk ordinal
+        const int base = k & ~63;
+        if (base != pages_base) {
+            pages_base = base;
+            const int my_c = wave + 4 * (base + lane);
+            int blk = -1;
+            if (my_c < nchunks) {
+                const int key = si.k_lo + 16 * my_c;
+                const int page = key / a.block_size;
+                if (page < a.max_blocks) blk = bt_row[page];
+                if (blk < 0 || blk >= a.num_blocks) blk = -1;
+            }
+            pages = blk;
+        }
+        return __builtin_amdgcn_readlane(pages, k - base);
+    };
+
+    u32x4_t kreg[C::PF][C::NLD], vreg[C::PF][C::NLD];
+    int nvalid_st[C::PF];
+    auto issue = [&](int st, int c) {
+        const int key0 = si.k_lo + 16 * c;
+        const int blk = chunk_block(c);
+        const int nv = blk < 0 ? 0 : min(16, si.k_hi - key0);
+        nvalid_st[st] = nv;
+        if (nv > 0) {
+            const int off = key0 % a.block_size;
+            const size_t base = (static_cast<size_t>(blk) * a.num_kv_heads + g) * head_stride +
+                                static_cast<size_t>(off) * C::RB;
+            const u32x4_t* kp = reinterpret_cast<const u32x4_t*>(a.k_cache + base);
+            const u32x4_t* vp = reinterpret_cast<const u32x4_t*>(a.v_cache + base);
+#pragma unroll
+            for (int it = 0; it < C::NLD; ++it) {
+                kreg[st][it] = __builtin_nontemporal_load(kp + it * 64 + lane);
+                vreg[st][it] = __builtin_nontemporal_load(vp + it * 64 + lane);
+            }
+        }
+    };
+
+    // prologue
+#pragma unroll
+    for (int st = 0; st < C::PF; ++st) {
+        const int c = wave + 4 * st;
+        if (c < nchunks) issue(st, c);
+    }
+
+    for (int c0 = wave; c0 < nchunks; c0 += 4 * C::PF) {
+#pragma unroll
+        for (int st = 0; st < C::PF; ++st) {
+            const int c = c0 + 4 * st;
+            if (c >= nchunks) break;
+            const int key0 = si.k_lo + 16 * c;
+            const int nv = nvalid_st[st];
+
+            // stage chunk -> LDS (swizzled), zero rows past the valid keys
+            compiler_fence();
+#pragma unroll
+            for (int it = 0; it < C::NLD; ++it) {
+                const int f = it * 64 + lane;
+                const int r = f / C::CPR;
+                const int cc = f - r * C::CPR;
+                const int off = r * C::RB + ((cc ^ (r & C::SWM)) << 4);
+                const bool ok = r < nv;
+                const u32x4_t z = {0u, 0u, 0u, 0u};
+                *reinterpret_cast<u32x4_t*>(klds + off) = ok ? kreg[st][it] : z;
+                *reinterpret_cast<u32x4_t*>(vlds + off) = ok ? vreg[st][it] : z;
+            }
+            compiler_fence();
+            if (c + 4 * C::PF < nchunks) issue(st, c + 4 * C::PF);
+
+            // K operands (A of S^T): row = col, d = 32s + 8*grp .. +8
+            bf16x8_t kop[C::KSTEPS];
+#pragma unroll
+            for (int s = 0; s < C::KSTEPS; ++s) {
+                const int r = col;
+                if constexpr (!KV8) {
+                    const int cc = 4 * s + grp;
+                    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(klds + r * C::RB + ((cc ^ (r & C::SWM)) << 4));
+                    kop[s] = __builtin_bit_cast(bf16x8_t, v);
+                } else {
+                    const int cc = 2 * s + (grp >> 1);
+                    const u32x2_t v = *reinterpret_cast<const u32x2_t*>(
+                        klds + r * C::RB + ((cc ^ (r & C::SWM)) << 4) + 8 * (grp & 1));
+                    uint32_t w0, w1, w2, w3;
+                    fp8x4_to_bf16x4(v[0], w0, w1);
+                    fp8x4_to_bf16x4(v[1], w2, w3);
+                    const u32x4_t w = {w0, w1, w2, w3};
+                    kop[s] = __builtin_bit_cast(bf16x8_t, w);
+                }
+            }
+            // V^T operands (A of O^T = V^T.P^T): d = 16t + col, keys 4*grp + j
+            short4_t vop[C::DT];
+#pragma unroll
+            for (int t = 0; t < C::DT; ++t) {
+                const int d = 16 * t + col;
+                uint32_t e[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 4 * grp + j;
+                    if constexpr (!KV8) {
+                        const int cc = d >> 3;
+                        e[j] = *reinterpret_cast<const uint16_t*>(vlds + r * C::RB + ((cc ^ (r & C::SWM)) << 4) + ((d & 7) << 1));
+                    } else {
+                        const int cc = d >> 4;
+                        e[j] = fp8e4m3_to_bf16(vlds[r * C::RB + ((cc ^ (r & C::SWM)) << 4) + (d & 15)]);
+                    }
+                }
+                u32x2_t pk = {e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+                vop[t] = __builtin_bit_cast(short4_t, pk);
+            }
+            compiler_fence();
+
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                float4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < C::KSTEPS; ++s)
+                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[s], qop[cb][s], sacc, 0, 0, 0);
+                // lane holds keys key0 + 4*grp + j for query row 16cb + col
+                const int lim = min(nv, nvis[cb] - key0);
+                float x[4];
+                float mt = -INFINITY;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 4 * grp + j;
+                    x[j] = r < lim ? sacc[j] * a.score_scale_log2 : -INFINITY;
+                    mt = fmaxf(mt, x[j]);
+                }
+                mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+                mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+                const float mnew = fmaxf(m_run[cb], mt);
+                const float mref = mnew == -INFINITY ? 0.f : mnew;
+                const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - mref);
+                float p[4];
+                float ps = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    p[j] = __builtin_amdgcn_exp2f(x[j] - mref);
+                    ps += p[j];
+                }
+                l_run[cb] = l_run[cb] * alpha + ps;
+                m_run[cb] = mnew;
+                u32x2_t pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+                const short4_t pop = __builtin_bit_cast(short4_t, pk);
+#pragma unroll
+                for (int t = 0; t < C::DT; ++t) {
+                    acc[cb][t] *= alpha;
+                    acc[cb][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop[t], pop, acc[cb][t], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    // ---- merge the 4 wave states in LDS ----
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        l_run[cb] += __shfl_xor(l_run[cb], 16, 64);
+        l_run[cb] += __shfl_xor(l_run[cb], 32, 64);
+    }
+    __syncthreads();   // staging buffers are free from here on
+    float* mbuf = reinterpret_cast<float*>(lds);           // [4][ROWS]
+    float* lbuf = mbuf + 4 * C::ROWS;                       // [ROWS]
+    float* Mbuf = lbuf + C::ROWS;                           // [ROWS]
+    float* abuf = Mbuf + C::ROWS;                           // [ROWS][APITCH]
+    if (grp == 0) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) mbuf[wave * C::ROWS + 16 * cb + col] = m_run[cb];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        const int n = 16 * cb + col;
+        float Mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) Mx = fmaxf(Mx, mbuf[w * C::ROWS + n]);
+        const float mref = Mx == -INFINITY ? 0.f : Mx;
+        const float f = __builtin_amdgcn_exp2f(m_run[cb] - mref);
+        l_run[cb] *= f;
+#pragma unroll
+        for (int t = 0; t < C::DT; ++t) acc[cb][t] *= f;
+        if (wave == 0 && grp == 0) Mbuf[n] = Mx;
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        if (wave == w) {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                const int n = 16 * cb + col;
+#pragma unroll
+                for (int t = 0; t < C::DT; ++t) {
+                    float4_t* dst = reinterpret_cast<float4_t*>(abuf + n * C::APITCH + 16 * t + 4 * grp);
+                    *dst = (w == 0) ? acc[cb][t] : (*dst + acc[cb][t]);
+                }
+                if (grp == 0) lbuf[n] = (w == 0) ? l_run[cb] : (lbuf[n] + l_run[cb]);
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- write the slot's states: rows n < M, token i = n / G, head g*G + n % G ----
+    constexpr int D4 = D / 4;
+    const size_t slot_base = static_cast<size_t>(slot) * a.max_q_len;
+    for (int e = tid; e < M * D4; e += 256) {
+        const int n = e / D4;
+        const int d4 = e - n * D4;
+        const int i = n / G;
+        const int h = g * G + (n - i * G);
+        const size_t st = (slot_base + i) * a.num_q_heads + h;
+        float4_t v = *reinterpret_cast<const float4_t*>(abuf + n * C::APITCH + 4 * d4);
+        v *= a.v_scale;
+        *reinterpret_cast<float4_t*>(a.ws_acc + st * D + 4 * d4) = v;
+        if (d4 == 0) *reinterpret_cast<float2*>(a.ws_ml + st * 2) = make_float2(Mbuf[n], lbuf[n]);
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// fp32-cache kernel: plain vector ALU code, fp32 throughout
+// ---------------------------------------------------------------------------------------------
+template <int D, bool QF32>
+__global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeArgs a) {
+    __shared__ float qbuf[4][D];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int slot = blockIdx.x / a.num_kv_heads;
+    const int g = blockIdx.x - slot * a.num_kv_heads;
+    SlotInfo si;
+    if (!slot_info(a, slot, si)) return;
+    const int G = a.group;
+    const int M = G * si.L;
+    constexpr int E = D / 64;
+    const int* bt_row = a.block_tables + static_cast<size_t>(si.b) * a.max_blocks;
+    const float* kc = reinterpret_cast<const float*>(a.k_cache);
+    const float* vc = reinterpret_cast<const float*>(a.v_cache);
+
+    for (int n = wave; n < M; n += 4) {
+        const int i = n / G;
+        const int h = g * G + (n - i * G);
+        const int nv = si.S - (si.L - 1 - i);
+        const int lo = si.k_lo;
+        const int hi = min(si.k_hi, nv);
+        const size_t qoff = (static_cast<size_t>(si.row0 + i) * a.num_q_heads + h) * D;
+        compiler_fence();
+        for (int d = lane; d < D; d += 64) {
+            if constexpr (QF32) qbuf[wave][d] = static_cast<const float*>(a.q)[qoff + d];
+            else qbuf[wave][d] = bf16_to_f32(static_cast<const uint16_t*>(a.q)[qoff + d]);
+        }
+        compiler_fence();
+        float m = -INFINITY, l = 0.f;
+        float acc[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = 0.f;
+        for (int base = lo; base < hi; base += 64) {
+            const int p = base + lane;
+            int blk = -1;
+            float x = -INFINITY;
+            if (p < hi) {
+                blk = bt_row[p / a.block_size];
+                if (blk < 0 || blk >= a.num_blocks) blk = -1;
+            }
+            if (blk >= 0) {
+                const float* kp = kc + ((static_cast<size_t>(blk) * a.num_kv_heads + g) * a.block_size + p % a.block_size) * D;
+                float dot = 0.f;
+                for (int d = 0; d < D; d += 4) {
+                    const float4 kv = *reinterpret_cast<const float4*>(kp + d);
+                    dot = fmaf(qbuf[wave][d], kv.x, dot);
+                    dot = fmaf(qbuf[wave][d + 1], kv.y, dot);
+                    dot = fmaf(qbuf[wave][d + 2], kv.z, dot);
+                    dot = fmaf(qbuf[wave][d + 3], kv.w, dot);
+                }
+                x = dot * a.score_scale_log2;
+            }
+            const float mt = wave_max(x);
+            const float mnew = fmaxf(m, mt);
+            const float mref = mnew == -INFINITY ? 0.f : mnew;
+            const float alpha = __builtin_amdgcn_exp2f(m - mref);
+            const float pr = blk >= 0 ? __builtin_amdgcn_exp2f(x - mref) : 0.f;
+            l = l * alpha + wave_sum(pr);
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[e] *= alpha;
+            const int cnt = min(64, hi - base);
+            for (int k = 0; k < cnt; ++k) {
+                const int bk = __builtin_amdgcn_readlane(blk, k);
+                if (bk < 0) continue;
+                const float pk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pr), k));
+                const int pos = base + k;
+                const float* vp = vc + ((static_cast<size_t>(bk) * a.num_kv_heads + g) * a.block_size + pos % a.block_size) * D;
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[e] = fmaf(pk, vp[lane + 64 * e], acc[e]);
+            }
+            m = mnew;
+        }
+        const size_t st = (static_cast<size_t>(slot) * a.max_q_len + i) * a.num_q_heads + h;
+#pragma unroll
+        for (int e = 0; e < E; ++e) a.ws_acc[st * D + lane + 64 * e] = acc[e] * a.v_scale;
+        if (lane == 0) *reinterpret_cast<float2*>(a.ws_ml + st * 2) = make_float2(m, l);
+    }
+}
+
+template <int D, int NCB, bool KV8>
+hipError_t launch_mfma_q(const DecodeArgs& a, bool qf32, dim3 grid, hipStream_t stream) {
+    if (qf32) hipLaunchKernelGGL((decode_mfma_kernel<D, NCB, KV8, true>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((decode_mfma_kernel<D, NCB, KV8, false>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int D, bool KV8>
+hipError_t launch_mfma_ncb(const DecodeArgs& a, int ncb, bool qf32, dim3 grid, hipStream_t stream) {
+    if (ncb == 1) return launch_mfma_q<D, 1, KV8>(a, qf32, grid, stream);
+    if (ncb == 2) return launch_mfma_q<D, 2, KV8>(a, qf32, grid, stream);
+    return launch_mfma_q<D, 4, KV8>(a, qf32, grid, stream);
+}
+
+template <int D>
+hipError_t launch_d(const DecodeArgs& a, pa_dtype kv, int ncb, bool qf32, dim3 grid, hipStream_t stream) {
+    if (kv == PA_F32) {
+        if (qf32) hipLaunchKernelGGL((decode_f32_kernel<D, true>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((decode_f32_kernel<D, false>), grid, dim3(256), 0, stream, a);
+        return hipGetLastError();
+    }
+    if (kv == PA_BF16) return launch_mfma_ncb<D, false>(a, ncb, qf32, grid, stream);
+    return launch_mfma_ncb<D, true>(a, ncb, qf32, grid, stream);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, int head_dim, pa_dtype kv_dtype, bool q_f32,
+                         hipStream_t stream) {
+    const int rows = a.group * a.max_q_len;
+    const int ncb = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+    const dim3 grid(static_cast<unsigned>(a.capacity) * static_cast<unsigned>(a.num_kv_heads));
+    if (grid.x == 0) return hipSuccess;
+    switch (head_dim) {
+        case 64: return launch_d<64>(a, kv_dtype, ncb, q_f32, grid, stream);
+        case 128: return launch_d<128>(a, kv_dtype, ncb, q_f32, grid, stream);
+        default: return launch_d<256>(a, kv_dtype, ncb, q_f32, grid, stream);
+    }
+}
+
+}  // namespace pa

@@ -1,0 +1,149 @@
+// pa_plan.hip -- the length-proportional work planner on gfx950.
+//
+// What it computes is stated in ROCm/ATOM PR #2366 "[MiniMax-M3] Route the paged decode to aiter's
+// FlyDSL kernel with work planner" (section 1: a partition count proportional to each request's real
+// context length under a 2 x CU workgroup budget; section 3: ceiling 256; review item 2: work entries
+// hold begin/end tiles and the request's length; review item 3: the capacity formula).  The rounding of
+// the shares is this library's reading, documented in pa.h.
+//
+// One workgroup of 1024 threads does the whole plan: a reduction for the total length and the number
+// of non-empty requests, the per-request counts, a block-wide exclusive scan into LDS, and then one
+// thread per slot fills work_info by binary-searching the scanned offsets.  Integer-only, 64-bit where
+// products can exceed 32 bits, so the result is bit-identical to any other exact evaluation.
+#include "pa_device.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / 64;
+
+__device__ __forceinline__ long long wave_sum_ll(long long v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        int lo = __shfl_xor(static_cast<int>(v & 0xffffffffll), o, 64);
+        int hi = __shfl_xor(static_cast<int>(v >> 32), o, 64);
+        v += (static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo);
+    }
+    return v;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int t = __shfl_up(v, o, 64);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(
+    const int32_t* __restrict__ context_lens, int num_seqs, int cap_formula, int capacity,
+    int max_partitions, int tile_tokens, int4* __restrict__ work_info,
+    int2* __restrict__ reduce_info, int32_t* __restrict__ num_work) {
+    __shared__ int32_t first[PA_MAX_SEQS + 1];
+    __shared__ long long red_total[kPlanWaves];
+    __shared__ int red_count[kPlanWaves];
+    __shared__ int scan_carry[kPlanWaves];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+
+    // --- W = sum S_b and B' = #{S_b > 0} ---
+    long long total = 0;
+    int nonempty = 0;
+    for (int b = tid; b < num_seqs; b += kPlanThreads) {
+        const int s = max(context_lens[b], 0);
+        total += s;
+        nonempty += (s > 0);
+    }
+    total = wave_sum_ll(total);
+    for (int o = 32; o >= 1; o >>= 1) nonempty += __shfl_xor(nonempty, o, 64);
+    if (lane == 0) {
+        red_total[wave] = total;
+        red_count[wave] = nonempty;
+    }
+    __syncthreads();
+    total = 0;
+    nonempty = 0;
+    for (int w = 0; w < kPlanWaves; ++w) {
+        total += red_total[w];
+        nonempty += red_count[w];
+    }
+    const long long extra = static_cast<long long>(cap_formula) - nonempty;
+
+    // --- per-request partition counts over a contiguous range per thread, then an exclusive scan ---
+    const int per = (num_seqs + kPlanThreads - 1) / kPlanThreads;
+    const int b0 = min(tid * per, num_seqs);
+    const int b1 = min(b0 + per, num_seqs);
+    int local = 0;
+    for (int b = b0; b < b1; ++b) {
+        const long long s = max(context_lens[b], 0);
+        int parts = 0;
+        if (s > 0) {
+            const long long tiles = (s + tile_tokens - 1) / tile_tokens;
+            long long p = 1 + (extra * s) / total;
+            if (p > tiles) p = tiles;
+            if (p > max_partitions) p = max_partitions;
+            parts = static_cast<int>(p);
+        }
+        first[b] = parts;
+        local += parts;
+    }
+    const int incl = wave_incl_scan(local, lane);
+    if (lane == 63) scan_carry[wave] = incl;
+    __syncthreads();
+    int offset = incl - local;
+    for (int w = 0; w < wave; ++w) offset += scan_carry[w];
+    for (int b = b0; b < b1; ++b) {
+        const int parts = first[b];
+        first[b] = offset;
+        offset += parts;
+    }
+    if (tid == kPlanThreads - 1) first[num_seqs] = offset;  // the last thread's offset is the grand total
+    __syncthreads();
+
+    const int used = first[num_seqs];
+    if (tid == 0) *num_work = used;
+    for (int b = tid; b < num_seqs; b += kPlanThreads)
+        reduce_info[b] = make_int2(first[b], first[b + 1] - first[b]);
+
+    // --- one thread per slot ---
+    for (int s = tid; s < capacity; s += kPlanThreads) {
+        if (s < used) {
+            // last request whose first slot is <= s (it has at least one partition because s < used)
+            int lo = 0, hi = num_seqs - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (first[mid] <= s) lo = mid;
+                else hi = mid - 1;
+            }
+            const int b = lo;
+            const long long j = s - first[b];
+            const long long parts = first[b + 1] - first[b];
+            const int len = max(context_lens[b], 0);
+            const long long tiles = (static_cast<long long>(len) + tile_tokens - 1) / tile_tokens;
+            const int tb = static_cast<int>((j * tiles) / parts);
+            const int te = static_cast<int>(((j + 1) * tiles) / parts);
+            work_info[s] = make_int4(b, tb, te, len);
+        } else {
+            work_info[s] = make_int4(-1, 0, 0, 0);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_plan(const int32_t* context_lens, int num_seqs, int cap_formula, int capacity,
+                       int max_partitions, int tile_tokens, int32_t* work_info, int32_t* reduce_info,
+                       int32_t* num_work, hipStream_t stream) {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, context_lens, num_seqs,
+                       cap_formula, capacity, max_partitions, tile_tokens,
+                       reinterpret_cast<int4*>(work_info), reinterpret_cast<int2*>(reduce_info),
+                       num_work);
+    return hipGetLastError();
+}
+
+}  // namespace pa

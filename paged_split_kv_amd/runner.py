@@ -1,0 +1,80 @@
+"""One decode step on the device: pa_plan -> pa_decode -> pa_merge on one stream.
+
+``DecodeStep`` owns the plan buffers, the workspace and the output for one batch geometry, so a
+timed loop issues exactly the three library calls and allocates nothing.  All arithmetic happens in
+libpa.so.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import binding as B
+
+
+@dataclass
+class PlanConfig:
+    cu_count: int
+    budget_mult: int = 2
+    max_partitions: int = 256
+    tile_tokens: int = 256
+
+
+class DecodeStep:
+    def __init__(self, *, num_seqs: int, num_rows: int, num_q_heads: int, num_kv_heads: int,
+                 head_dim: int, max_q_len: int, out_dtype: torch.dtype, device,
+                 plan: Optional[PlanConfig] = None):
+        self.device = torch.device(device)
+        self.plan_cfg = plan or PlanConfig(cu_count=B.pa_device_cu_count(self.device.index or 0))
+        p = self.plan_cfg
+        self.num_seqs = num_seqs
+        self.num_kv_heads = num_kv_heads
+        self.max_q_len = max_q_len
+        self.capacity = B.pa_plan_capacity(num_seqs, num_kv_heads, p.cu_count, p.budget_mult,
+                                           p.max_partitions)
+        self.work_info = torch.empty((self.capacity, 4), dtype=torch.int32, device=self.device)
+        self.reduce_info = torch.empty((num_seqs, 2), dtype=torch.int32, device=self.device)
+        self.num_work = torch.empty((1,), dtype=torch.int32, device=self.device)
+        nbytes = B.pa_workspace_bytes(self.capacity, max_q_len, num_q_heads, head_dim)
+        self.workspace = torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=self.device)
+        self.out = torch.empty((num_rows, num_q_heads, head_dim), dtype=out_dtype, device=self.device)
+
+    @classmethod
+    def for_case(cls, case, plan: Optional[PlanConfig] = None) -> "DecodeStep":
+        return cls(num_seqs=case.num_seqs, num_rows=case.num_rows, num_q_heads=case.num_q_heads,
+                   num_kv_heads=case.num_kv_heads, head_dim=case.head_dim, max_q_len=case.max_q_len,
+                   out_dtype=case.q.dtype, device=case.q.device, plan=plan)
+
+    def plan(self, context_lens: torch.Tensor, stream=None) -> None:
+        p = self.plan_cfg
+        B.pa_plan(context_lens, self.num_kv_heads, cu_count=p.cu_count, budget_mult=p.budget_mult,
+                  max_partitions=p.max_partitions, tile_tokens=p.tile_tokens, capacity=self.capacity,
+                  work_info=self.work_info, reduce_info=self.reduce_info, num_work=self.num_work,
+                  stream=stream)
+
+    def decode(self, q, k_cache, v_cache, kv_dtype, block_tables, context_lens, *, scale,
+               cu_query_lens=None, k_scale=1.0, v_scale=1.0, stream=None) -> None:
+        B.pa_decode(q, k_cache, v_cache, kv_dtype, block_tables, context_lens, self.work_info,
+                    self.num_work, self.workspace, scale=scale, cu_query_lens=cu_query_lens,
+                    max_q_len=self.max_q_len, k_scale=k_scale, v_scale=v_scale,
+                    tile_tokens=self.plan_cfg.tile_tokens, stream=stream)
+
+    def merge(self, cu_query_lens=None, stream=None) -> torch.Tensor:
+        B.pa_merge(self.out, self.reduce_info, self.workspace, capacity=self.capacity,
+                   cu_query_lens=cu_query_lens, max_q_len=self.max_q_len, stream=stream)
+        return self.out
+
+    def run_case(self, case, stream=None, replan: bool = True) -> torch.Tensor:
+        if replan:
+            self.plan(case.context_lens, stream)
+        self.decode(case.q, case.k_cache, case.v_cache, case.kv_dtype, case.block_tables,
+                    case.context_lens, scale=case.scale, cu_query_lens=case.cu_query_lens,
+                    k_scale=case.k_scale, v_scale=case.v_scale, stream=stream)
+        return self.merge(case.cu_query_lens, stream)
+
+
+def run_case(case, plan: Optional[PlanConfig] = None) -> torch.Tensor:
+    """Plan, decode and merge one workload Case; returns the output tensor (device)."""
+    return DecodeStep.for_case(case, plan).run_case(case)

@@ -1,0 +1,149 @@
+"""CPU-side checks of the C ABI: the library loads, exports every declared entry point, and the
+host-side argument checks return their status codes before any launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_split_kv_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "pa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = B.load()
+    names = _declared_functions()
+    assert set(names) == set(B.SYMBOLS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    assert B.status_string(B.PA_OK) == "ok"
+    for s in (B.PA_INVALID_ARG, B.PA_UNSUPPORTED, B.PA_CAPACITY, B.PA_HIP_ERROR):
+        assert B.status_string(s) not in ("ok", "unknown status")
+    assert B.status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_capacity_matches_oracle(seed):
+    rng = np.random.default_rng(seed)
+    for _ in range(200):
+        Bn = int(rng.integers(0, 9000))
+        hkv = int(rng.choice([1, 2, 3, 4, 8, 16]))
+        cu = int(rng.choice([1, 80, 256, 304, 1000]))
+        mult = int(rng.choice([1, 2, 3, 4]))
+        P = int(rng.choice([1, 8, 64, 256, 1000]))
+        assert B.pa_plan_capacity(Bn, hkv, cu, mult, P) == oracle.plan_capacity(Bn, hkv, cu, mult, P)
+
+
+def test_workspace_bytes():
+    # fp32 partials [C, Lmax, Hq, D] then (m, l) pairs [C, Lmax, Hq, 2], each rounded up to 256 bytes
+    def expect(c, l, h, d):
+        up = lambda x: (x + 255) // 256 * 256
+        return up(c * l * h * d * 4) + up(c * l * h * 2 * 4)
+    for args in [(512, 1, 4, 64), (256, 1, 16, 128), (512, 3, 6, 256), (1, 1, 1, 64), (0, 1, 1, 64)]:
+        assert B.pa_workspace_bytes(*args) == expect(*args)
+    assert B.pa_workspace_bytes(10, 0, 1, 64) == 0
+    assert B.pa_workspace_bytes(-1, 1, 1, 64) == 0
+
+
+def _plan_status(**kw):
+    a = dict(ctx=ctypes.c_void_p(16), B=4, hkv=1, cu=256, mult=2, P=256, T=256, cap=512,
+             work=ctypes.c_void_p(256), red=ctypes.c_void_p(256), nw=ctypes.c_void_p(256))
+    a.update(kw)
+    return B.load().pa_plan(a["ctx"], a["B"], a["hkv"], a["cu"], a["mult"], a["P"], a["T"], a["cap"],
+                            a["work"], a["red"], a["nw"], None)
+
+
+def test_plan_argument_checks():
+    # (no valid call is made: every case below must be refused before a launch)
+    assert _plan_status(cap=511) == B.PA_CAPACITY
+    assert _plan_status(B=-1) == B.PA_INVALID_ARG
+    assert _plan_status(hkv=0) == B.PA_INVALID_ARG
+    assert _plan_status(cu=0) == B.PA_INVALID_ARG
+    assert _plan_status(mult=0) == B.PA_INVALID_ARG
+    assert _plan_status(P=0) == B.PA_INVALID_ARG
+    assert _plan_status(T=0) == B.PA_INVALID_ARG
+    assert _plan_status(nw=None) == B.PA_INVALID_ARG
+    assert _plan_status(ctx=None) == B.PA_INVALID_ARG
+    assert _plan_status(work=None) == B.PA_INVALID_ARG
+    assert _plan_status(work=ctypes.c_void_p(8)) == B.PA_INVALID_ARG       # misaligned int4 entries
+    assert _plan_status(B=B.PA_MAX_SEQS + 1, cap=1 << 22) == B.PA_UNSUPPORTED
+
+
+_GOOD = dict(q=256, qd=B.PA_BF16, R=4, Hq=16, D=128, k=256, v=256, kvd=B.PA_BF16, nb=10, Hkv=2, bs=16,
+             bt=256, mb=4, ctx=256, Bn=4, cu=None, ql=1, scale=0.1, ks=1.0, vs=1.0, work=256, nw=256,
+             cap=256, T=256, ws=256, wsb=1 << 30)
+
+
+def _decode_status(**kw):
+    a = dict(_GOOD)
+    a.update(kw)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return B.load().pa_decode(vp(a["q"]), a["qd"], a["R"], a["Hq"], a["D"], vp(a["k"]), vp(a["v"]),
+                              a["kvd"], a["nb"], a["Hkv"], a["bs"], vp(a["bt"]), a["mb"], vp(a["ctx"]),
+                              a["Bn"], vp(a["cu"]), a["ql"], a["scale"], a["ks"], a["vs"], vp(a["work"]),
+                              vp(a["nw"]), a["cap"], a["T"], vp(a["ws"]), a["wsb"], None)
+
+
+def test_decode_argument_checks():
+    assert _decode_status(qd=B.PA_FP8_E4M3) == B.PA_INVALID_ARG        # q must be f32 or bf16
+    assert _decode_status(kvd=7) == B.PA_INVALID_ARG
+    assert _decode_status(Hq=15) == B.PA_INVALID_ARG                   # Hq % Hkv != 0
+    assert _decode_status(D=96) == B.PA_UNSUPPORTED
+    assert _decode_status(D=512) == B.PA_UNSUPPORTED
+    assert _decode_status(bs=32) == B.PA_UNSUPPORTED
+    assert _decode_status(T=200) == B.PA_UNSUPPORTED                   # tile not a multiple of bs
+    assert _decode_status(Hq=32, Hkv=1, cu=256, ql=3) == B.PA_UNSUPPORTED   # 96 rows per group
+    assert _decode_status(ql=2) == B.PA_INVALID_ARG                    # no cu but max_q_len 2
+    assert _decode_status(R=3) == B.PA_INVALID_ARG                     # no cu and fewer rows than requests
+    assert _decode_status(q=None) == B.PA_INVALID_ARG
+    assert _decode_status(k=None) == B.PA_INVALID_ARG
+    assert _decode_status(bt=None) == B.PA_INVALID_ARG
+    assert _decode_status(work=None) == B.PA_INVALID_ARG
+    assert _decode_status(ws=None) == B.PA_INVALID_ARG
+    assert _decode_status(ws=512 + 16) == B.PA_INVALID_ARG             # workspace not 256-aligned
+    assert _decode_status(q=8) == B.PA_INVALID_ARG                     # q not 16-aligned
+    assert _decode_status(wsb=1000) == B.PA_CAPACITY
+    assert _decode_status(scale=float("nan")) == B.PA_INVALID_ARG
+    assert _decode_status(Bn=-1) == B.PA_INVALID_ARG
+    assert _decode_status(cap=0) == B.PA_OK                            # nothing to do: no launch
+    assert _decode_status(Bn=0) == B.PA_OK
+
+
+def _merge_status(**kw):
+    a = dict(R=4, Hq=16, D=128, Bn=4, cu=None, ql=1, red=256, cap=256, ws=256, wsb=1 << 30, out=256,
+             od=B.PA_BF16)
+    a.update(kw)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return B.load().pa_merge(a["R"], a["Hq"], a["D"], a["Bn"], vp(a["cu"]), a["ql"], vp(a["red"]),
+                             a["cap"], vp(a["ws"]), a["wsb"], vp(a["out"]), a["od"], None)
+
+
+def test_merge_argument_checks():
+    assert _merge_status(od=B.PA_FP8_E4M3) == B.PA_INVALID_ARG
+    assert _merge_status(D=80) == B.PA_UNSUPPORTED
+    assert _merge_status(out=None) == B.PA_INVALID_ARG
+    assert _merge_status(red=None) == B.PA_INVALID_ARG
+    assert _merge_status(ws=None) == B.PA_INVALID_ARG
+    assert _merge_status(ql=2) == B.PA_INVALID_ARG
+    assert _merge_status(wsb=10) == B.PA_CAPACITY
+    assert _merge_status(red=260) == B.PA_INVALID_ARG                  # int2 entries misaligned
+    assert _merge_status(R=0) == B.PA_OK
+
+
+def test_binding_refuses_host_tensors():
+    ctx = torch.tensor([1, 2], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        B.pa_plan(ctx, 1, cu_count=256)

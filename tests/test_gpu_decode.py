@@ -1,0 +1,184 @@
+"""GPU decode + merge (pa_decode, pa_merge) against the fp64 oracle, element by element.
+
+Tolerances: fp32 1e-4 abs; bf16 2e-2 abs + 1e-2 rel; fp8 KV 5e-2 abs (see _util.TOL).
+Semantics pinned: per-token causal range S - (L - 1 - i) (opengfx1030/vllm-rdna PR #29, Change 1),
+exact zeros for padding rows and empty rows, bitwise equality with and without cumulative query
+lengths when every request has one token, independence from the plan's slot order.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from paged_split_kv_amd import binding as B
+from paged_split_kv_amd import workloads as W
+from paged_split_kv_amd.runner import DecodeStep, PlanConfig
+from _util import announce, assert_close, oracle_direct, to_f64, tolerance_kind
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+# (name, ctx, q_lens, Hq, Hkv, D, bs, kv, q, pad, P, T)
+SMALL = [
+    ("bf16_d128_g8", [700, 33, 1, 2000, 256, 257], None, 16, 2, 128, 16, "bf16", "bf16", 0, 256, 256),
+    ("bf16_d64_verify", [37, 5, 64, 1290], [3, 1, 2, 4], 8, 2, 64, 64, "bf16", "bf16", 2, 256, 256),
+    ("bf16_d256_verify3", [1500, 900, 2, 700], [3, 3, 1, 1], 6, 1, 256, 16, "bf16", "bf16", 2, 256, 256),
+    ("bf16_d128_64rows", [3000, 17, 600], [4, 4, 1], 16, 1, 128, 16, "bf16", "bf16", 1, 64, 64),
+    ("bf16_d128_bs128", [5000, 129, 128, 4000], None, 8, 1, 128, 128, "bf16", "bf16", 3, 256, 512),
+    ("bf16_zero_len", [0, 300, 0, 2, 40], [2, 2, 1, 3, 1], 4, 2, 128, 16, "bf16", "bf16", 1, 8, 16),
+    ("qf32_kvbf16", [800, 64, 3], None, 16, 2, 128, 16, "bf16", "f32", 0, 256, 256),
+    ("fp8_d128", [900, 1, 4000, 77], None, 16, 2, 128, 16, "fp8", "bf16", 0, 256, 256),
+    ("fp8_d64_verify", [300, 45], [2, 3], 12, 4, 64, 64, "fp8", "bf16", 1, 256, 64),
+    ("fp8_d256", [1200, 600], [1, 2], 8, 2, 256, 16, "fp8", "f32", 0, 256, 256),
+    ("f32_d64", [1, 17, 100, 300, 0], None, 4, 1, 64, 16, "f32", "f32", 2, 256, 256),
+    ("f32_d128_verify", [500, 31, 2], [3, 2, 2], 8, 2, 128, 64, "f32", "f32", 1, 8, 64),
+    ("f32_d256_qbf16", [700, 90], [1, 2], 4, 2, 256, 16, "f32", "bf16", 0, 256, 256),
+    ("bf16_many_slots", [4096, 4096, 100, 5000], None, 8, 1, 128, 16, "bf16", "bf16", 0, 256, 16),
+]
+
+
+def _small_case(spec, seed):
+    name, ctx, ql, Hq, Hkv, D, bs, kv, qd, pad, P, T = spec
+    return W.build_case(name, ctx, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs,
+                        kv_dtype=kv, q_dtype=qd, seed=seed, q_lens=ql, pad_rows=pad, device=DEV), P, T
+
+
+def _run(case, P=256, T=256, cu_count=256):
+    step = DecodeStep.for_case(case, PlanConfig(cu_count=cu_count, max_partitions=P, tile_tokens=T))
+    step.out.fill_(float("nan"))
+    step.workspace.fill_(0xFF)              # NaN pattern in every fp32 slot
+    out = step.run_case(case)
+    torch.cuda.synchronize()
+    return out, step
+
+
+def _zero_rows(case):
+    """Rows that must be exactly zero: padding rows, rows of empty requests, tokens with no keys."""
+    R = case.num_rows
+    ctx = case.context_lens.cpu().numpy()
+    zero = np.ones(R, dtype=bool)
+    if case.cu_query_lens is None:
+        for b, s in enumerate(ctx):
+            zero[b] = s <= 0
+    else:
+        cu = case.cu_query_lens.cpu().numpy()
+        for b, s in enumerate(ctx):
+            L = cu[b + 1] - cu[b]
+            for i in range(L):
+                zero[cu[b] + i] = (s - (L - 1 - i)) <= 0
+    return zero
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=[s[0] for s in SMALL])
+def test_small_cases_match_oracle(spec):
+    case, P, T = _small_case(spec, seed=11)
+    announce(f"small {spec[0]}")
+    out, _ = _run(case, P, T)
+    got = to_f64(out)
+    ref = oracle_direct(case)
+    assert_close(got, ref, tolerance_kind(case), spec[0])
+    z = _zero_rows(case)
+    assert (got[z] == 0.0).all()
+    assert (np.abs(got[~z]).sum(axis=(1, 2)) > 0).all()
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "long_bf16", "verify_bf16", "fp8_kv"])
+def test_full_size_workloads(name):
+    announce(f"full {name}")
+    case = W.make_config(name, device=DEV)
+    out, step = _run(case, cu_count=256)
+    got = to_f64(out)
+    ref = oracle_direct(case)
+    assert_close(got, ref, tolerance_kind(case), name)
+    z = _zero_rows(case)
+    assert (got[z] == 0.0).all()
+    if name == "verify_bf16":
+        assert z.sum() == 2 and z[-2:].all()     # the two rows past the last cumulative length
+
+
+@pytest.mark.parametrize("which", ["p50", "p90", "max_tokens"])
+def test_skewed_steps(which):
+    steps = W.skewed_step_set()
+    idx = W.skewed_named_steps(steps)[which]
+    announce(f"skewed step {which} (#{idx}, {int(steps[idx].sum())} tokens)")
+    case = W.make_config("skewed_bf16", device=DEV, step=idx)
+    out, _ = _run(case, cu_count=256)
+    assert_close(to_f64(out), oracle_direct(case), "bf16", f"skewed {which}")
+
+
+def test_single_key_row_is_the_value_row_fp32():
+    case = W.make_config("tiny_fp32", device=DEV)   # request 0 has exactly one key
+    out, _ = _run(case)
+    blk = int(case.block_tables[0, 0].item())
+    v0 = case.v_cache[blk, 0, 0, :].cpu()
+    for h in range(case.num_q_heads):
+        assert torch.equal(out[0, h].cpu(), v0)
+
+
+def test_without_cu_equals_cu_of_ones_bitwise():
+    spec = ("x", [700, 33, 1, 2000, 0, 513], None, 16, 2, 128, 16, "bf16", "bf16", 0, 256, 256)
+    case, P, T = _small_case(spec, seed=5)
+    a, _ = _run(case, P, T)
+    a = a.clone()
+    case.cu_query_lens = torch.arange(case.num_seqs + 1, dtype=torch.int32, device=DEV)
+    b, _ = _run(case, P, T)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_slot_order_does_not_change_the_output():
+    spec = ("x", [3000, 33, 1, 2000, 900], [2, 1, 1, 3, 1], 8, 2, 128, 16, "bf16", "bf16", 1, 256, 256)
+    case, P, T = _small_case(spec, seed=6)
+    ref, step = _run(case, P, T)
+    ref = ref.clone()
+    work = step.work_info.cpu().numpy()
+    red = step.reduce_info.cpu().numpy()
+    nw = int(step.num_work.item())
+    # reverse the order of the requests' slot blocks; each request keeps its own slots in order
+    new_work = np.tile(np.array([-1, 0, 0, 0], np.int32), (work.shape[0], 1))
+    new_red = red.copy()
+    pos = 0
+    for b in reversed(range(case.num_seqs)):
+        first, parts = red[b]
+        new_work[pos:pos + parts] = work[first:first + parts]
+        new_red[b] = (pos, parts)
+        pos += parts
+    assert pos == nw
+    step.work_info.copy_(torch.from_numpy(new_work))
+    step.reduce_info.copy_(torch.from_numpy(new_red))
+    step.out.fill_(float("nan"))
+    out = step.run_case(case, replan=False)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+def test_output_guard_bands_untouched():
+    spec = ("x", [400, 30], [2, 1], 8, 2, 128, 16, "bf16", "bf16", 2, 256, 256)
+    case, P, T = _small_case(spec, seed=7)
+    step = DecodeStep.for_case(case, PlanConfig(cu_count=256, max_partitions=P, tile_tokens=T))
+    n = step.out.numel()
+    big = torch.full((n + 2048,), -3.0, dtype=torch.bfloat16, device=DEV)
+    step.out = big[1024:1024 + n].view(step.out.shape)
+    step.run_case(case)
+    torch.cuda.synchronize()
+    assert (big[:1024] == -3.0).all() and (big[1024 + n:] == -3.0).all()
+    assert_close(to_f64(step.out), oracle_direct(case), "bf16", "guard")
+
+
+@pytest.mark.parametrize("P,T", [(1, 256), (2, 64), (8, 16), (256, 16), (256, 512)])
+def test_split_count_invariance(P, T):
+    spec = ("x", [6000, 2500, 40], [1, 2, 1], 8, 1, 128, 16, "bf16", "bf16", 0, P, T)
+    case, _, _ = _small_case(spec, seed=8)
+    announce(f"split invariance P={P} T={T}")
+    out, step = _run(case, P, T)
+    assert_close(to_f64(out), oracle_direct(case), "bf16", f"P={P} T={T}")
+
+
+def test_repeated_calls_are_deterministic():
+    spec = ("x", [3000, 700], [3, 1], 6, 1, 256, 16, "bf16", "bf16", 1, 256, 256)
+    case, P, T = _small_case(spec, seed=9)
+    a, _ = _run(case, P, T)
+    a = a.clone()
+    b, _ = _run(case, P, T)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
