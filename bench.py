@@ -1,0 +1,254 @@
+"""Benchmark of the paged split-KV decode step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--graph]
+
+Workload: the skewed 32-request bf16 decode (Hq 16 / Hkv 2, D 128, pages of 16 tokens).  128 decode
+steps whose in-batch max/min context ratio follows the agentic trace (p50 ~2.5, p90 ~21); every step
+draws its pages at random from a 4 GiB K/V pool, so the 256 MB last-level cache cannot hold a step's
+data across steps.  One timed step = pa_plan + pa_decode + pa_merge over one batch, inputs resident in
+HBM.  value = KV bytes read / step time (GB/s).
+
+The roofline object is for the decode kernel: algorithmic bytes (sum of context lengths x Hkv x 2 x D
+x 2 bytes per launch) over its average launch duration measured with HIP events on the launch stream.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "µs/step + achieved KV-read HBM GB/s (% peak), skewed 32-req bf16 decode"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_skewed_bf16_counters.json")
+DECODE_SRC = os.path.join(ROOT, "paged_split_kv_amd", "csrc", "pa_decode.hip")
+
+
+def decode_source_sha() -> str:
+    with open(DECODE_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counter_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary, if it was taken on
+    the current decode source; else None."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("decode_source_sha") != decode_source_sha():
+        return None
+    return c.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(pool, budget_s: float, max_steps: int):
+    """The CPU oracle (direct fp64 attention over the gathered pages) on a bounded sample of steps."""
+    import oracle
+
+    threads = oracle.default_threads()
+    done_bytes = 0
+    spent = 0.0
+    n = 0
+    order = np.argsort(pool.steps.sum(axis=1))          # smallest steps first keeps the sample bounded
+    picks = order[:: max(1, len(order) // max_steps)][:max_steps]
+    for i in picks:
+        ctx = pool.steps[i]
+        bs = pool.block_size
+        pages = (ctx + bs - 1) // bs
+        bt = pool.block_tables[i].cpu().numpy()
+        used = np.concatenate([bt[b, :pages[b]] for b in range(len(ctx))])
+        idx = torch.from_numpy(used.astype(np.int64)).to(pool.k_cache.device)
+        k = pool.k_cache.index_select(0, idx).cpu().view(torch.int16).numpy().view(np.uint16)
+        v = pool.v_cache.index_select(0, idx).cpu().view(torch.int16).numpy().view(np.uint16)
+        remap = np.full(bt.shape, -1, dtype=np.int32)
+        pos = 0
+        for b in range(len(ctx)):
+            remap[b, :pages[b]] = np.arange(pos, pos + pages[b], dtype=np.int32)
+            pos += pages[b]
+        q = pool.q[i].cpu().view(torch.int16).numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        oracle.attention_direct(q, "bf16", k, v, "bf16", remap, ctx.astype(np.int32), None, pool.scale,
+                                threads=threads)
+        spent += time.perf_counter() - t0
+        done_bytes += int(ctx.sum()) * k.shape[1] * 2 * k.shape[3] * 2
+        n += 1
+        if spent >= budget_s:
+            break
+    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "us_per_step": round(spent / n * 1e6, 1),
+            "sample": f"{n} of the 128 skewed steps (smallest first), fp64 direct attention over the "
+                      f"gathered pages, {spent:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=512)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--graph", action="store_true", help="also time a HIP-graph replay of the steps")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a 1 GiB device copy first (reference kernel for the HBM counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the decode path has no multi-GPU mode (see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    from paged_split_kv_amd import binding as B
+    from paged_split_kv_amd import workloads as W
+    from paged_split_kv_amd.runner import DecodeStep, PlanConfig
+
+    B.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    print("[bench] building the 4 GiB page pool and 128 skewed steps", file=sys.stderr, flush=True)
+    pool = W.skewed_pool(dev)
+    nsteps = pool.steps.shape[0]
+    B_ = pool.steps.shape[1]
+    Hq, D = pool.q.shape[2], pool.q.shape[3]
+    Hkv = pool.k_cache.shape[1]
+    cu_count = B.pa_device_cu_count(0)
+    step = DecodeStep(num_seqs=B_, num_rows=B_, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                      max_q_len=1, out_dtype=torch.bfloat16, device=dev,
+                      plan=PlanConfig(cu_count=cu_count))
+    kv_bytes = pool.steps.sum(axis=1) * Hkv * 2 * D * 2                 # per step
+    stream = torch.cuda.current_stream()
+
+    def run(i, ev=None):
+        i %= nsteps
+        ctx = pool.context_lens[i]
+        if ev is not None:
+            ev[0].record(stream)
+        step.plan(ctx)
+        if ev is not None:
+            ev[1].record(stream)
+        step.decode(pool.q[i], pool.k_cache, pool.v_cache, "bf16", pool.block_tables[i], ctx,
+                    scale=pool.scale)
+        if ev is not None:
+            ev[2].record(stream)
+        step.merge()
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(K):
+        run(i, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    plan_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    mrg_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    step_ms = plan_ms + dec_ms + mrg_ms
+    bytes_done = float(sum(kv_bytes[i % nsteps] for i in range(K)))
+
+    # the same steps without per-kernel events in between (only the outer events)
+    s2 = torch.cuda.Event(enable_timing=True)
+    e2 = torch.cuda.Event(enable_timing=True)
+    s2.record(stream)
+    for i in range(K):
+        run(i)
+    e2.record(stream)
+    torch.cuda.synchronize()
+    plain_ms = s2.elapsed_time(e2)
+
+    graph = None
+    if args.graph:
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(nsteps):
+                    run(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        gs = torch.cuda.Event(enable_timing=True)
+        ge = torch.cuda.Event(enable_timing=True)
+        reps = max(1, K // nsteps)
+        gs.record(stream)
+        for _ in range(reps):
+            g.replay()
+        ge.record(stream)
+        torch.cuda.synchronize()
+        g_ms = gs.elapsed_time(ge) / (reps * nsteps)
+        graph = {"us_per_step": round(g_ms * 1e3, 2),
+                 "kv_gbps": round(float(kv_bytes.mean()) / (g_ms * 1e-3) / 1e9, 1)}
+
+    us_step = plain_ms * 1e3 / K
+    gbps = bytes_done / (plain_ms * 1e-3) / 1e9
+    dec_gbps = bytes_done / (dec_ms.sum() * 1e-3) / 1e9
+    traffic = counter_traffic()
+    result = {
+        "metric": METRIC,
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(plain_ms / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "skewed 32-request bf16 decode, Hq 16 / Hkv 2, D 128, page 16, "
+                               "128 stratified steps over a 4 GiB pool",
+                   "num_seqs": B_, "q_len": 1, "mean_tokens_per_step": round(float(pool.steps.sum(1).mean()), 1),
+                   "planner": {"budget": "2 x CU", "cu_count": cu_count, "max_partitions": 256,
+                               "tile_tokens": 256}},
+        "us_per_step": round(us_step, 2),
+        "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 1),
+        "us_per_step_p50": round(float(np.median(step_ms)) * 1e3, 2),
+        "us_per_step_p90": round(float(np.quantile(step_ms, 0.9)) * 1e3, 2),
+        "kernel_us": {"pa_plan": round(float(plan_ms.mean()) * 1e3, 2),
+                      "pa_decode": round(float(dec_ms.mean()) * 1e3, 2),
+                      "pa_merge": round(float(mrg_ms.mean()) * 1e3, 2)},
+        "timed_wall_s": round(wall, 3),
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "kernel": "pa_decode",
+                     "algorithmic_bytes_per_launch": round(float(kv_bytes.mean()), 1)},
+        "hip_graph": graph,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(pool, args.cpu_seconds, 24)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

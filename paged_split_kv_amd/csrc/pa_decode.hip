@@ -7,9 +7,10 @@
 // goes to the workspace; pa_merge combines a request's slots.
 //
 // Design (bf16 / fp8 caches, the matrix-core kernel):
-//  * one workgroup of 4 waves per (slot, kv head).  The slot's keys are cut into 16-key chunks (a
+//  * one workgroup of NW waves per (slot, kv head).  The slot's keys are cut into 16-key chunks (a
 //    chunk never straddles a page: pages hold 16, 64 or 128 tokens and slots start on tile
-//    boundaries); wave w takes chunks w, w+4, ...; the 4 states are merged in LDS at the end.
+//    boundaries); wave w takes the slot's tiles w, w+NW, ... whole, so every streaming wave carries
+//    one tile and long slots get proportionally more bandwidth; the NW states merge in LDS at the end.
 //  * all query rows of the group -- G heads x L verify tokens, M = G*L <= 64 -- form the columns
 //    of 16-wide MFMA blocks, so each K/V byte is read from HBM once per (slot, kv head) whatever L is.
 //  * each chunk's K and V (16 x D each) are fetched with 16-byte coalesced loads two chunks ahead into
@@ -45,20 +46,16 @@ struct SlotInfo {
 };
 
 __device__ __forceinline__ bool slot_info(const DecodeArgs& a, int slot, SlotInfo& si) {
-    if (slot >= a.capacity) return false;
-    const int used = *a.num_work;
-    if (slot >= used) return false;
+    // the slot's work entry and the used-slot count are independent loads
     const int4 w = a.work_info[slot];
+    const int used = *a.num_work;
     const int b = w.x;
-    if (b < 0 || b >= a.num_seqs) return false;
+    if (slot >= used || b < 0 || b >= a.num_seqs) return false;
     const int S = max(a.context_lens[b], 0);
-    int row0, L;
+    int row0 = b, L = 1;
     if (a.cu) {
         row0 = a.cu[b];
         L = a.cu[b + 1] - row0;
-    } else {
-        row0 = b;
-        L = 1;
     }
     L = min(max(L, 0), a.max_q_len);
     if (row0 < 0 || row0 >= a.num_rows) L = 0;
@@ -80,27 +77,43 @@ __device__ __forceinline__ bool slot_info(const DecodeArgs& a, int slot, SlotInf
 // ---------------------------------------------------------------------------------------------
 // matrix-core kernel (bf16 or fp8 caches)
 // ---------------------------------------------------------------------------------------------
-template <int D, int NCB, bool KV8, bool QF32>
+template <int D, int NCB, bool KV8>
 struct Mfma {
-    static constexpr int ESZ = KV8 ? 1 : 2;            // bytes per cache element
-    static constexpr int RB = D * ESZ;                 // bytes per cache row (one token, one kv head)
-    static constexpr int CPR = RB / 16;                // 16-byte columns per row
-    static constexpr int SWM = (CPR < 16 ? CPR : 16) - 1;  // XOR swizzle mask on the column index
-    static constexpr int NLD = 16 * RB / 1024;         // 16-byte loads per lane per 16-row chunk
+    static constexpr int ESZ = KV8 ? 1 : 2;            // bytes per cache element in HBM
+    static constexpr int GRB = D * ESZ;                // HBM bytes per cache row (one token, one kv head)
+    static constexpr int GCPR = GRB / 16;              // 16-byte HBM columns per row
+    static constexpr int NLD = 16 * GRB / 1024;        // 16-byte loads per lane per 16-row chunk
+    static constexpr int LRB = D * 2;                  // LDS bytes per row (always bf16)
+    static constexpr int LCPR = LRB / 16;              // 16-byte LDS columns per row
+    static constexpr int SWM = (LCPR < 16 ? LCPR : 16) - 1;  // XOR swizzle mask on the column
     static constexpr int KSTEPS = D / 32;              // k-steps of the S^T product
     static constexpr int DT = D / 16;                  // 16-wide d tiles of the P.V product
-    static constexpr int WAVE_LDS = 2 * 16 * RB;       // K then V chunk, per wave
-    static constexpr int STAGE_LDS = 4 * WAVE_LDS;
+    static constexpr int NW = 4;                       // waves per workgroup
+    static constexpr int WAVE_LDS = 2 * 16 * LRB;      // K then V chunk, per wave
+    static constexpr int STAGE_LDS = NW * WAVE_LDS;
     static constexpr int ROWS = 16 * NCB;              // query rows per workgroup (padded)
     static constexpr int APITCH = D + 4;               // fp32 pitch of the LDS merge buffer
-    static constexpr int MERGE_LDS = (4 * ROWS + 2 * ROWS + ROWS * APITCH) * 4;
+    static constexpr int MERGE_LDS = (NW * ROWS + 2 * ROWS + ROWS * APITCH) * 4;
     static constexpr int LDS = STAGE_LDS > MERGE_LDS ? STAGE_LDS : MERGE_LDS;
-    static constexpr int PF = 2;                       // chunks in flight per wave
+    // Waves per SIMD the register budget is cut for: 2 (two workgroups per CU, 256 registers per lane)
+    // where operands and accumulators fit, else 1 (512 registers) rather than spilling.
+    static constexpr int WAVES = (D == 64 || (D == 128 && NCB == 1)) ? 2 : 1;
+    // chunks in flight per wave
+    static constexpr int PF = D == 64 ? 4 : (D == 128 ? 3 : (NCB == 1 ? 2 : 1));
 };
 
+// Byte offset of 16-byte column c of row r in a per-wave bf16 LDS tile (XOR swizzle on the column).
+template <int LRB, int SWM>
+__device__ __forceinline__ int lds_col(int r, int c) {
+    return r * LRB + ((c ^ (r & SWM)) << 4);
+}
+
+// Rescale threshold of the running maximum, in base-2 units: probabilities stay below 2^8.
+constexpr float kRescaleSlack = 8.0f;
+
 template <int D, int NCB, bool KV8, bool QF32>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
-    using C = Mfma<D, NCB, KV8, QF32>;
+__global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::WAVES)) void decode_mfma_kernel(const DecodeArgs a) {
+    using C = Mfma<D, NCB, KV8>;
     __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS];
 
     const int tid = threadIdx.x;
@@ -109,8 +122,63 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
     const int slot = blockIdx.x / a.num_kv_heads;
     const int g = blockIdx.x - slot * a.num_kv_heads;
 
+    // ---- slot geometry.  Dependent loads are kept to three levels: the work entry; then the
+    // request's length, cumulative query lengths and (speculatively, over the plan's tile range)
+    // this wave's page ids; then queries and K/V. ----
+    const int4 wk = a.work_info[slot];
+    const int used = *a.num_work;
+    const int b = wk.x;
+    if (slot >= used || b < 0 || b >= a.num_seqs) return;
+    const int* bt_row = a.block_tables + static_cast<size_t>(b) * a.max_blocks;
+    const long long reach = static_cast<long long>(a.max_blocks) * a.block_size;
+    const int plan_lo = static_cast<int>(min(static_cast<long long>(max(wk.y, 0)) * a.tile_tokens, reach));
+    const int plan_hi = static_cast<int>(max(min(static_cast<long long>(max(wk.z, 0)) * a.tile_tokens, reach),
+                                             static_cast<long long>(plan_lo)));
+    const int plan_chunks = (plan_hi - plan_lo + 15) >> 4;
+
+    // Chunks are dealt to waves in whole plan tiles: wave w owns tiles w, w + NW, ... of the slot and
+    // its k-th chunk is chunk_of(k).  The planner sizes slots in tiles, so a slot of up to NW tiles
+    // runs one streaming wave per tile: every wave carries the same load whatever the slot size,
+    // and big slots draw proportionally more bandwidth instead of finishing last.
+    const int cpt = a.tile_tokens >> 4;          // 16-key chunks per tile
+    auto chunk_of = [&](int k) -> int {
+        const int j = k / cpt;
+        return (wave + C::NW * j) * cpt + (k - j * cpt);
+    };
+
+    // Page ids of this wave's chunks, one per lane (lane = chunk ordinal - base), refreshed every 64.
+    int pages = -1;
+    int pages_base = 0;
+    auto load_pages = [&](int base) {
+        const int my_c = chunk_of(base + lane);
+        int blk = -1;
+        if (my_c < plan_chunks) {
+            blk = bt_row[(plan_lo + 16 * my_c) / a.block_size];
+            if (blk < 0 || blk >= a.num_blocks) blk = -1;
+        }
+        pages = blk;
+        pages_base = base;
+    };
+    load_pages(0);
+
     SlotInfo si;
-    if (!slot_info(a, slot, si)) return;
+    {
+        const int S = max(a.context_lens[b], 0);
+        int row0 = b, L = 1;
+        if (a.cu) {
+            row0 = a.cu[b];
+            L = a.cu[b + 1] - row0;
+        }
+        L = min(max(L, 0), a.max_q_len);
+        if (row0 < 0 || row0 >= a.num_rows) L = 0;
+        else L = min(L, a.num_rows - row0);
+        si.b = b;
+        si.row0 = row0;
+        si.L = L;
+        si.S = S;
+        si.k_hi = min(plan_hi, S);
+        si.k_lo = min(plan_lo, si.k_hi);
+    }
     const int G = a.group;
     const int M = G * si.L;                       // valid query rows (<= ROWS)
     const int col = lane & 15;                    // MFMA column = query row within a block
@@ -147,8 +215,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
         }
     }
 
-    float m_run[NCB], l_run[NCB];
-    float4_t acc[NCB][C::DT];
+    float m_run[NCB], l_run[NCB];                 // running reference max (base 2) and lane-partial sum
+    float4_t acc[NCB][C::DT];                     // O^T tile: lane holds d = 16t + 4*grp + j, row = col
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
         m_run[cb] = -INFINITY;
@@ -159,44 +227,34 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
 
     const int nkeys = si.k_hi - si.k_lo;
     const int nchunks = nkeys > 0 ? (nkeys + 15) >> 4 : 0;
-    const int* bt_row = a.block_tables + static_cast<size_t>(si.b) * a.max_blocks;
-    const size_t head_stride = static_cast<size_t>(a.block_size) * C::RB;   // bytes per (block, kv head)
-    uint8_t* wlds = lds + wave * C::WAVE_LDS;
-    uint8_t* klds = wlds;
-    uint8_t* vlds = wlds + 16 * C::RB;
+    const size_t head_stride = static_cast<size_t>(a.block_size) * C::GRB;   // HBM bytes per (block, kv head)
+    uint8_t* klds = lds + wave * C::WAVE_LDS;
+    uint8_t* vlds = klds + 16 * C::LRB;
 
-    // Page ids of this wave's chunks, one per lane, refreshed every 64 chunks of the wave.
-    int pages = -1;
-    int pages_base = -1;
-    auto chunk_block = [&](int c) -> int {
-        const int k = (c - wave) >> 2;            // this wave's chunk ordinal
+    // this wave's number of chunks: its full tiles, plus the ragged last tile if it owns it
+    const int full_tiles = nchunks / cpt;
+    const int rem = nchunks - full_tiles * cpt;
+    int my_chunks = (full_tiles > wave ? (full_tiles - wave + C::NW - 1) / C::NW : 0) * cpt;
+    if (rem > 0 && full_tiles % C::NW == wave) my_chunks += rem;
+
+    auto chunk_block = [&](int k) -> int {
         const int base = k & ~63;
-        if (base != pages_base) {
-            pages_base = base;
-            const int my_c = wave + 4 * (base + lane);
-            int blk = -1;
-            if (my_c < nchunks) {
-                const int key = si.k_lo + 16 * my_c;
-                const int page = key / a.block_size;
-                if (page < a.max_blocks) blk = bt_row[page];
-                if (blk < 0 || blk >= a.num_blocks) blk = -1;
-            }
-            pages = blk;
-        }
+        if (base != pages_base) load_pages(base);
         return __builtin_amdgcn_readlane(pages, k - base);
     };
 
     u32x4_t kreg[C::PF][C::NLD], vreg[C::PF][C::NLD];
     int nvalid_st[C::PF];
-    auto issue = [&](int st, int c) {
+    auto issue = [&](int st, int k) {
+        const int c = chunk_of(k);
         const int key0 = si.k_lo + 16 * c;
-        const int blk = chunk_block(c);
+        const int blk = chunk_block(k);
         const int nv = blk < 0 ? 0 : min(16, si.k_hi - key0);
         nvalid_st[st] = nv;
         if (nv > 0) {
             const int off = key0 % a.block_size;
             const size_t base = (static_cast<size_t>(blk) * a.num_kv_heads + g) * head_stride +
-                                static_cast<size_t>(off) * C::RB;
+                                static_cast<size_t>(off) * C::GRB;
             const u32x4_t* kp = reinterpret_cast<const u32x4_t*>(a.k_cache + base);
             const u32x4_t* vp = reinterpret_cast<const u32x4_t*>(a.v_cache + base);
 #pragma unroll
@@ -207,76 +265,83 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
         }
     };
 
-    // prologue
+    // Write a staged chunk into the wave's LDS tiles as bf16 rows; rows >= nv are zero.
+    auto stage = [&](int st, int nv) {
 #pragma unroll
-    for (int st = 0; st < C::PF; ++st) {
-        const int c = wave + 4 * st;
-        if (c < nchunks) issue(st, c);
-    }
+        for (int it = 0; it < C::NLD; ++it) {
+            const int f = it * 64 + lane;
+            const int r = f / C::GCPR;
+            const int c = f - r * C::GCPR;
+            const bool ok = r < nv;
+            const u32x4_t z = {0u, 0u, 0u, 0u};
+            u32x4_t kv = ok ? kreg[st][it] : z;
+            u32x4_t vv = ok ? vreg[st][it] : z;
+            if constexpr (!KV8) {
+                const int off = lds_col<C::LRB, C::SWM>(r, c);
+                *reinterpret_cast<u32x4_t*>(klds + off) = kv;
+                *reinterpret_cast<u32x4_t*>(vlds + off) = vv;
+            } else {
+                // 16 fp8 codes -> 16 bf16 values = two LDS columns (2c, 2c+1), widened exactly
+                u32x4_t klo, khi, vlo, vhi;
+#pragma unroll
+                for (int w = 0; w < 2; ++w) {
+                    klo[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kv[w], 1.0f, false));
+                    klo[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kv[w], 1.0f, true));
+                    khi[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kv[w + 2], 1.0f, false));
+                    khi[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kv[w + 2], 1.0f, true));
+                    vlo[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vv[w], 1.0f, false));
+                    vlo[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vv[w], 1.0f, true));
+                    vhi[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vv[w + 2], 1.0f, false));
+                    vhi[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vv[w + 2], 1.0f, true));
+                }
+                const int o0 = lds_col<C::LRB, C::SWM>(r, 2 * c);
+                const int o1 = lds_col<C::LRB, C::SWM>(r, 2 * c + 1);
+                *reinterpret_cast<u32x4_t*>(klds + o0) = klo;
+                *reinterpret_cast<u32x4_t*>(klds + o1) = khi;
+                *reinterpret_cast<u32x4_t*>(vlds + o0) = vlo;
+                *reinterpret_cast<u32x4_t*>(vlds + o1) = vhi;
+            }
+        }
+    };
 
-    for (int c0 = wave; c0 < nchunks; c0 += 4 * C::PF) {
+    // Per-lane address of the transposed V read for d-tile 0: lane (16G + 4k + m) reads the 4 bf16
+    // of row 4G + k at d = 4m; the hardware hands lane 16G + i the column d = i of rows 4G..4G+3.
+    const int tr_row = 4 * grp + ((lane >> 2) & 3);
+    const int tr_d0 = 4 * (lane & 3);
+
+#pragma unroll
+    for (int st = 0; st < C::PF; ++st)
+        if (st < my_chunks) issue(st, st);
+
+    for (int k0 = 0; k0 < my_chunks; k0 += C::PF) {
 #pragma unroll
         for (int st = 0; st < C::PF; ++st) {
-            const int c = c0 + 4 * st;
-            if (c >= nchunks) break;
-            const int key0 = si.k_lo + 16 * c;
+            const int k = k0 + st;
+            if (k >= my_chunks) break;
+            const int key0 = si.k_lo + 16 * chunk_of(k);
             const int nv = nvalid_st[st];
 
-            // stage chunk -> LDS (swizzled), zero rows past the valid keys
             compiler_fence();
-#pragma unroll
-            for (int it = 0; it < C::NLD; ++it) {
-                const int f = it * 64 + lane;
-                const int r = f / C::CPR;
-                const int cc = f - r * C::CPR;
-                const int off = r * C::RB + ((cc ^ (r & C::SWM)) << 4);
-                const bool ok = r < nv;
-                const u32x4_t z = {0u, 0u, 0u, 0u};
-                *reinterpret_cast<u32x4_t*>(klds + off) = ok ? kreg[st][it] : z;
-                *reinterpret_cast<u32x4_t*>(vlds + off) = ok ? vreg[st][it] : z;
-            }
+            stage(st, nv);
             compiler_fence();
-            if (c + 4 * C::PF < nchunks) issue(st, c + 4 * C::PF);
+            if (k + C::PF < my_chunks) issue(st, k + C::PF);
 
             // K operands (A of S^T): row = col, d = 32s + 8*grp .. +8
             bf16x8_t kop[C::KSTEPS];
 #pragma unroll
-            for (int s = 0; s < C::KSTEPS; ++s) {
-                const int r = col;
-                if constexpr (!KV8) {
-                    const int cc = 4 * s + grp;
-                    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(klds + r * C::RB + ((cc ^ (r & C::SWM)) << 4));
-                    kop[s] = __builtin_bit_cast(bf16x8_t, v);
-                } else {
-                    const int cc = 2 * s + (grp >> 1);
-                    const u32x2_t v = *reinterpret_cast<const u32x2_t*>(
-                        klds + r * C::RB + ((cc ^ (r & C::SWM)) << 4) + 8 * (grp & 1));
-                    uint32_t w0, w1, w2, w3;
-                    fp8x4_to_bf16x4(v[0], w0, w1);
-                    fp8x4_to_bf16x4(v[1], w2, w3);
-                    const u32x4_t w = {w0, w1, w2, w3};
-                    kop[s] = __builtin_bit_cast(bf16x8_t, w);
-                }
-            }
-            // V^T operands (A of O^T = V^T.P^T): d = 16t + col, keys 4*grp + j
+            for (int s = 0; s < C::KSTEPS; ++s)
+                kop[s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
+                                                          klds + lds_col<C::LRB, C::SWM>(col, 4 * s + grp)));
+            // V^T operands (A of O^T = V^T.P^T): d = 16t + col, keys 4*grp + j, via transposed reads
             short4_t vop[C::DT];
 #pragma unroll
             for (int t = 0; t < C::DT; ++t) {
-                const int d = 16 * t + col;
-                uint32_t e[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 4 * grp + j;
-                    if constexpr (!KV8) {
-                        const int cc = d >> 3;
-                        e[j] = *reinterpret_cast<const uint16_t*>(vlds + r * C::RB + ((cc ^ (r & C::SWM)) << 4) + ((d & 7) << 1));
-                    } else {
-                        const int cc = d >> 4;
-                        e[j] = fp8e4m3_to_bf16(vlds[r * C::RB + ((cc ^ (r & C::SWM)) << 4) + (d & 15)]);
-                    }
-                }
-                u32x2_t pk = {e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
-                vop[t] = __builtin_bit_cast(short4_t, pk);
+                const int d0 = 16 * t + tr_d0;
+                const int off = lds_col<C::LRB, C::SWM>(tr_row, d0 >> 3) + ((d0 & 7) << 1);
+                typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+                typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+                const bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(vlds + off));
+                vop[t] = __builtin_bit_cast(short4_t, v);
             }
             compiler_fence();
 
@@ -292,44 +357,46 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
                 float mt = -INFINITY;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int r = 4 * grp + j;
-                    x[j] = r < lim ? sacc[j] * a.score_scale_log2 : -INFINITY;
+                    x[j] = (4 * grp + j) < lim ? sacc[j] * a.score_scale_log2 : -INFINITY;
                     mt = fmaxf(mt, x[j]);
                 }
                 mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
                 mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-                const float mnew = fmaxf(m_run[cb], mt);
-                const float mref = mnew == -INFINITY ? 0.f : mnew;
-                const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - mref);
+                // lazy rescale: move the reference only when the row max passes it by the slack
+                const bool grow = mt > m_run[cb] + kRescaleSlack;
+                if (__builtin_amdgcn_ballot_w64(grow)) {
+                    const float mnew = grow ? mt : m_run[cb];
+                    const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - mnew);
+                    l_run[cb] *= alpha;
+#pragma unroll
+                    for (int t = 0; t < C::DT; ++t) acc[cb][t] *= alpha;
+                    m_run[cb] = mnew;
+                }
+                const float mref = m_run[cb] == -INFINITY ? 0.f : m_run[cb];
                 float p[4];
-                float ps = 0.f;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     p[j] = __builtin_amdgcn_exp2f(x[j] - mref);
-                    ps += p[j];
+                    l_run[cb] += p[j];
                 }
-                l_run[cb] = l_run[cb] * alpha + ps;
-                m_run[cb] = mnew;
                 u32x2_t pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
                 const short4_t pop = __builtin_bit_cast(short4_t, pk);
 #pragma unroll
-                for (int t = 0; t < C::DT; ++t) {
-                    acc[cb][t] *= alpha;
+                for (int t = 0; t < C::DT; ++t)
                     acc[cb][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop[t], pop, acc[cb][t], 0, 0, 0);
-                }
             }
         }
     }
 
-    // ---- merge the 4 wave states in LDS ----
+    // ---- merge the wave states in LDS ----
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
         l_run[cb] += __shfl_xor(l_run[cb], 16, 64);
         l_run[cb] += __shfl_xor(l_run[cb], 32, 64);
     }
     __syncthreads();   // staging buffers are free from here on
-    float* mbuf = reinterpret_cast<float*>(lds);           // [4][ROWS]
-    float* lbuf = mbuf + 4 * C::ROWS;                       // [ROWS]
+    float* mbuf = reinterpret_cast<float*>(lds);           // [NW][ROWS]
+    float* lbuf = mbuf + C::NW * C::ROWS;                   // [ROWS]
     float* Mbuf = lbuf + C::ROWS;                           // [ROWS]
     float* abuf = Mbuf + C::ROWS;                           // [ROWS][APITCH]
     if (grp == 0) {
@@ -342,7 +409,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
         const int n = 16 * cb + col;
         float Mx = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) Mx = fmaxf(Mx, mbuf[w * C::ROWS + n]);
+        for (int w = 0; w < C::NW; ++w) Mx = fmaxf(Mx, mbuf[w * C::ROWS + n]);
         const float mref = Mx == -INFINITY ? 0.f : Mx;
         const float f = __builtin_amdgcn_exp2f(m_run[cb] - mref);
         l_run[cb] *= f;
@@ -351,7 +418,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
         if (wave == 0 && grp == 0) Mbuf[n] = Mx;
     }
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < C::NW; ++w) {
         if (wave == w) {
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
@@ -370,7 +437,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
     // ---- write the slot's states: rows n < M, token i = n / G, head g*G + n % G ----
     constexpr int D4 = D / 4;
     const size_t slot_base = static_cast<size_t>(slot) * a.max_q_len;
-    for (int e = tid; e < M * D4; e += 256) {
+    for (int e = tid; e < M * D4; e += 64 * C::NW) {
         const int n = e / D4;
         const int d4 = e - n * D4;
         const int i = n / G;
@@ -469,8 +536,9 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeArgs a) {
 
 template <int D, int NCB, bool KV8>
 hipError_t launch_mfma_q(const DecodeArgs& a, bool qf32, dim3 grid, hipStream_t stream) {
-    if (qf32) hipLaunchKernelGGL((decode_mfma_kernel<D, NCB, KV8, true>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((decode_mfma_kernel<D, NCB, KV8, false>), grid, dim3(256), 0, stream, a);
+    const dim3 block(64 * Mfma<D, NCB, KV8>::NW);
+    if (qf32) hipLaunchKernelGGL((decode_mfma_kernel<D, NCB, KV8, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((decode_mfma_kernel<D, NCB, KV8, false>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 

@@ -6,8 +6,7 @@
 //   b = last request with cu[b] <= r, token i = r - cu[b];
 //   over the request's partials j with l_j > 0:  M = max m_j,
 //   out = sum_j 2^(m_j - M) acc_j / sum_j 2^(m_j - M) l_j       (m is kept in base-2 units)
-// One wave per (row, head): lanes split the head dimension for the weighted sum and the partial list
-// for the max.  Every element of out is written.
+// Every element of out is written.
 #include "pa_device.h"
 
 namespace pa {
@@ -15,16 +14,10 @@ namespace pa {
 
 namespace {
 
-template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
-    constexpr int E = D / 64;
-    const int lane = threadIdx.x & 63;
-    const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int r = wid / a.num_q_heads;
-    const int h = wid - r * a.num_q_heads;
-    if (r >= a.num_rows) return;
-
-    int b = -1, i = 0;
+// Owning request and token of output row r (-1 when the row is padding or otherwise unowned).
+__device__ __forceinline__ int owner_of_row(const MergeArgs& a, int r, int& i) {
+    i = 0;
+    int b = -1;
     if (a.cu) {
         if (a.num_seqs > 0 && r >= a.cu[0] && r < a.cu[a.num_seqs]) {
             int lo = 0, hi = a.num_seqs - 1;          // last b with cu[b] <= r
@@ -41,45 +34,90 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
         b = r;
     }
     if (i >= a.max_q_len) b = -1;
+    return b;
+}
 
-    float num[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) num[e] = 0.f;
-    float den = 0.f;
+// One workgroup of 256 threads per (row, head).  Thread t owns the 16-byte column dc = t % (D/4) of
+// the head dimension and the partials j = pg, pg + NPG, ... with pg = t / (D/4); it folds them into a
+// running (max, sum, acc) with independent loads, then the NPG states of a column are combined in LDS.
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
+    constexpr int NDC = D / 4;          // float4 columns
+    constexpr int NPG = 256 / NDC;      // partial groups
+    __shared__ float4 s_acc[NPG][NDC];
+    __shared__ float s_m[NPG];
+    __shared__ float s_l[NPG];
 
+    const int tid = threadIdx.x;
+    const int dc = tid % NDC;
+    const int pg = tid / NDC;
+    const int r = blockIdx.x / a.num_q_heads;
+    const int h = blockIdx.x - r * a.num_q_heads;
+
+    int i;
+    const int b = owner_of_row(a, r, i);
+    float m = -INFINITY, l = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (b >= 0) {
         const int2 ri = a.reduce_info[b];
         const int first = max(ri.x, 0);
         const int parts = max(min(ri.y, a.capacity - first), 0);
         const size_t step = static_cast<size_t>(a.max_q_len) * a.num_q_heads;       // states per slot
         const size_t st0 = (static_cast<size_t>(first) * a.max_q_len + i) * a.num_q_heads + h;
-        float Mx = -INFINITY;
-        for (int j = lane; j < parts; j += 64) {
-            const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + (st0 + j * step) * 2);
-            if (ml.y > 0.f) Mx = fmaxf(Mx, ml.x);
-        }
-        Mx = wave_max(Mx);
-        if (Mx != -INFINITY) {
-            for (int j = 0; j < parts; ++j) {
-                const size_t st = st0 + j * step;
-                const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + st * 2);
-                if (!(ml.y > 0.f)) continue;
-                const float f = __builtin_amdgcn_exp2f(ml.x - Mx);
-                den = fmaf(f, ml.y, den);
-                const float* src = a.ws_acc + st * D;
-#pragma unroll
-                for (int e = 0; e < E; ++e) num[e] = fmaf(f, src[lane + 64 * e], num[e]);
+#pragma unroll 4
+        for (int j = pg; j < parts; j += NPG) {
+            const size_t st = st0 + static_cast<size_t>(j) * step;
+            const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + st * 2);
+            const float4 v = *reinterpret_cast<const float4*>(a.ws_acc + st * D + 4 * dc);
+            if (ml.y > 0.f) {
+                const float mn = fmaxf(m, ml.x);
+                const float fo = __builtin_amdgcn_exp2f(m - mn);      // 0 while m = -inf
+                const float fn = __builtin_amdgcn_exp2f(ml.x - mn);
+                l = l * fo + ml.y * fn;
+                acc.x = acc.x * fo + v.x * fn;
+                acc.y = acc.y * fo + v.y * fn;
+                acc.z = acc.z * fo + v.z * fn;
+                acc.w = acc.w * fo + v.w * fn;
+                m = mn;
             }
         }
     }
-
-    const size_t o = (static_cast<size_t>(r) * a.num_q_heads + h) * D;
-    const float inv = den > 0.f ? 1.f / den : 0.f;
+    s_acc[pg][dc] = acc;
+    if (dc == 0) {
+        s_m[pg] = m;
+        s_l[pg] = l;
+    }
+    __syncthreads();
+    if (pg != 0) return;
+    float Mx = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const float v = den > 0.f ? num[e] * inv : 0.f;
-        if constexpr (OUT_BF16) static_cast<uint16_t*>(a.out)[o + lane + 64 * e] = f32_to_bf16(v);
-        else static_cast<float*>(a.out)[o + lane + 64 * e] = v;
+    for (int k = 0; k < NPG; ++k) Mx = fmaxf(Mx, s_l[k] > 0.f ? s_m[k] : -INFINITY);
+    float den = 0.f;
+    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (Mx != -INFINITY) {
+#pragma unroll
+        for (int k = 0; k < NPG; ++k) {
+            if (!(s_l[k] > 0.f)) continue;
+            const float f = __builtin_amdgcn_exp2f(s_m[k] - Mx);
+            const float4 v = s_acc[k][dc];
+            den += f * s_l[k];
+            num.x += f * v.x;
+            num.y += f * v.y;
+            num.z += f * v.z;
+            num.w += f * v.w;
+        }
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    const float4 o = den > 0.f ? make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+    const size_t base = (static_cast<size_t>(r) * a.num_q_heads + h) * D + 4 * dc;
+    if constexpr (OUT_BF16) {
+        uint2 w;
+        w.x = pack_bf16x2(o.x, o.y);
+        w.y = pack_bf16x2(o.z, o.w);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + base) = w;
+    } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + base) = o;
     }
 }
 
@@ -93,8 +131,7 @@ hipError_t launch_merge_d(const MergeArgs& a, bool out_bf16, dim3 grid, hipStrea
 }  // namespace
 
 hipError_t launch_merge(const MergeArgs& a, int head_dim, bool out_bf16, hipStream_t stream) {
-    const long long waves = static_cast<long long>(a.num_rows) * a.num_q_heads;
-    const dim3 grid(static_cast<unsigned>((waves + 3) / 4));
+    const dim3 grid(static_cast<unsigned>(static_cast<long long>(a.num_rows) * a.num_q_heads));
     if (grid.x == 0) return hipSuccess;
     switch (head_dim) {
         case 64: return launch_merge_d<64>(a, out_bf16, grid, stream);
