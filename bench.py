@@ -6,10 +6,11 @@ Workload: the skewed 32-request bf16 decode (Hq 16 / Hkv 2, D 128, pages of 16 t
 steps whose in-batch max/min context ratio follows the agentic trace (p50 ~2.5, p90 ~21); every step
 draws its pages at random from a 4 GiB K/V pool, so the 256 MB last-level cache cannot hold a step's
 data across steps.  One timed step = pa_plan + pa_decode + pa_merge over one batch, inputs resident in
-HBM.  value = KV bytes read / step time (GB/s).
+HBM.  value = KV bytes read / step time (GB/s).  The variant with the merge inside the decode launch
+is timed too and reported beside it.
 
 The roofline object is for the decode kernel: algorithmic bytes (sum of context lengths x Hkv x 2 x D
-x 2 bytes per launch) over its average launch duration measured with HIP events on the launch stream.
+x 2 bytes per launch) over its average launch duration, measured with HIP events on the launch stream.
 """
 from __future__ import annotations
 
@@ -58,9 +59,8 @@ def cpu_baseline(pool, budget_s: float, max_steps: int):
     done_bytes = 0
     spent = 0.0
     n = 0
-    order = np.argsort(pool.steps.sum(axis=1))          # smallest steps first keeps the sample bounded
-    picks = order[:: max(1, len(order) // max_steps)][:max_steps]
-    for i in picks:
+    picks = np.random.default_rng(0).permutation(len(pool.steps))
+    for i in picks[:max_steps]:
         ctx = pool.steps[i]
         bs = pool.block_size
         pages = (ctx + bs - 1) // bs
@@ -86,8 +86,8 @@ def cpu_baseline(pool, budget_s: float, max_steps: int):
     return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "us_per_step": round(spent / n * 1e6, 1),
-            "sample": f"{n} of the 128 skewed steps (smallest first), fp64 direct attention over the "
-                      f"gathered pages, {spent:.1f} s"}
+            "sample": f"{n} of the 128 skewed steps (seeded random order, stopped after "
+                      f"{budget_s:.0f} s), fp64 direct attention over the gathered pages, {spent:.1f} s"}
 
 
 def main():
@@ -134,7 +134,9 @@ def main():
     kv_bytes = pool.steps.sum(axis=1) * Hkv * 2 * D * 2                 # per step
     stream = torch.cuda.current_stream()
 
-    def run(i, ev=None):
+    def run(i, ev=None, fused=False):
+        """One step: pa_plan, pa_decode writing partial states, then pa_merge (fused=True: the
+        merge runs inside the pa_decode launch instead)."""
         i %= nsteps
         ctx = pool.context_lens[i]
         if ev is not None:
@@ -143,10 +145,11 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         step.decode(pool.q[i], pool.k_cache, pool.v_cache, "bf16", pool.block_tables[i], ctx,
-                    scale=pool.scale)
+                    scale=pool.scale, merge=fused)
         if ev is not None:
             ev[2].record(stream)
-        step.merge()
+        if not fused:
+            step.merge()
         if ev is not None:
             ev[3].record(stream)
 
@@ -182,6 +185,18 @@ def main():
     e2.record(stream)
     torch.cuda.synchronize()
     plain_ms = s2.elapsed_time(e2)
+
+    # the same steps with the merge inside the decode launch, for comparison
+    s3 = torch.cuda.Event(enable_timing=True)
+    e3 = torch.cuda.Event(enable_timing=True)
+    for i in range(8):
+        run(i, fused=True)
+    s3.record(stream)
+    for i in range(K):
+        run(i, fused=True)
+    e3.record(stream)
+    torch.cuda.synchronize()
+    fused_ms = s3.elapsed_time(e3)
 
     graph = None
     if args.graph:
@@ -236,6 +251,7 @@ def main():
         "kernel_us": {"pa_plan": round(float(plan_ms.mean()) * 1e3, 2),
                       "pa_decode": round(float(dec_ms.mean()) * 1e3, 2),
                       "pa_merge": round(float(mrg_ms.mean()) * 1e3, 2)},
+        "merge_in_decode_launch_us_per_step": round(fused_ms * 1e3 / K, 2),
         "timed_wall_s": round(wall, 3),
         "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
@@ -246,7 +262,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(pool, args.cpu_seconds, 24)
+        result["cpu_baseline"] = cpu_baseline(pool, args.cpu_seconds, nsteps)
     print(json.dumps(result), flush=True)
 
 

@@ -40,7 +40,8 @@
  *   work_info      [capacity, 4]  (request, tile_begin, tile_end, S_b); unused slots (-1, 0, 0, 0)
  *   reduce_info    [num_seqs, 2]  (first_slot, num_partitions)
  *   num_work       [1]            number of used slots
- *   workspace      pa_workspace_bytes(...) bytes of fp32 partials, written by pa_decode, read by pa_merge
+ *   workspace      pa_workspace_bytes(...) bytes: fp32 partials written by pa_decode and read by
+ *                  pa_merge, plus the counters of the merge pa_decode can run in the same launch
  *
  * Query head h reads kv head h / (num_q_heads / num_kv_heads).
  */
@@ -82,9 +83,10 @@ pa_status pa_plan_capacity(int32_t num_seqs, int32_t num_kv_heads, int32_t cu_co
                            int32_t budget_mult, int32_t max_partitions, int32_t* capacity_out);
 
 /*
- * Bytes of workspace pa_decode writes and pa_merge reads for a plan of `capacity` slots:
- * fp32 partial outputs [capacity, max_q_len, num_q_heads, head_dim] followed by fp32
- * (max, sum) pairs [capacity, max_q_len, num_q_heads, 2], each region 256-byte aligned.
+ * Bytes of workspace pa_decode and pa_merge use for a plan of `capacity` slots: fp32 partial outputs
+ * [capacity, max_q_len, num_q_heads, head_dim], fp32 (max, sum) pairs [capacity, max_q_len,
+ * num_q_heads, 2], and int32 arrival counters [capacity x num_q_heads] for the merge pa_decode can run
+ * in the same launch; each region 256-byte aligned.
  * Returns 0 if any argument is < 1 (capacity may be 0) or the size overflows.
  */
 size_t pa_workspace_bytes(int32_t capacity, int32_t max_q_len, int32_t num_q_heads, int32_t head_dim);
@@ -115,7 +117,8 @@ pa_status pa_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_
  * visible range [0, S_b - (L_b - 1 - i)):
  *   m = max score, l = sum exp(score - m), acc = sum exp(score - m) v,   score = scale x k_scale x (q . k)
  * (V is multiplied by v_scale), stored unnormalised in the workspace; a slot/token with no visible
- * key stores m = -inf, l = 0, acc = 0.
+ * key stores l = 0, acc = 0.  S_b is context_lens[b]; the plan must have been built from the same
+ * lengths (a stale plan covers the wrong key ranges).
  * Arguments:
  *   q, q_dtype                 [num_rows, num_q_heads, head_dim], PA_F32 or PA_BF16
  *   k_cache, v_cache, kv_dtype [num_blocks, num_kv_heads, block_size, head_dim], PA_F32/PA_BF16/PA_FP8_E4M3
@@ -124,14 +127,22 @@ pa_status pa_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_
  *   cu_query_lens              [num_seqs + 1] or NULL (then row b is request b's only token)
  *   max_q_len                  upper bound on every request's query length (1 when cu is NULL)
  *   scale, k_scale, v_scale    softmax scale (typically 1/sqrt(head_dim)) and per-tensor dequant scales
- *   work_info, num_work        the plan from pa_plan (capacity slots)
+ *   work_info, reduce_info,    the plan from pa_plan (capacity slots); reduce_info is only read when
+ *   num_work                   out is given and may then not be NULL
  *   tile_tokens                the plan's tile size; a multiple of block_size
  *   workspace                  >= pa_workspace_bytes(capacity, max_q_len, num_q_heads, head_dim)
+ *   out, out_dtype             NULL: write the partial states only (pa_merge combines them later).
+ *                              Non-NULL: also merge, in the same launch, exactly as pa_merge would
+ *                              (out_dtype must equal q_dtype).  The last workgroup of each (request,
+ *                              kv head) to finish merges it, counted by the workspace's arrival
+ *                              counters: they must be zero before the first such call (allocate the
+ *                              workspace zero-filled) and every completed call leaves them zero.
+ *                              Calls that share a workspace must not overlap.
  * Supported: head_dim in {64, 128, 256}; block_size in {16, 64, 128};
  * (num_q_heads / num_kv_heads) x max_q_len <= PA_MAX_GROUP_ROWS.
  * KV types bf16 and fp8 run on the matrix cores in bf16 (fp8 codes widen exactly to bf16; q is
  * rounded to bf16; probabilities are rounded to bf16 for the P.V product; accumulation is fp32).
- * KV type f32 runs in fp32 on the vector ALUs.
+ * KV type f32 runs in fp32 on the vector ALUs (with out, the merge is a second launch).
  */
 pa_status pa_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t num_q_heads,
                     int32_t head_dim, const void* k_cache, const void* v_cache, pa_dtype kv_dtype,
@@ -139,8 +150,9 @@ pa_status pa_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t n
                     const int32_t* block_tables, int32_t max_blocks_per_seq,
                     const int32_t* context_lens, int32_t num_seqs, const int32_t* cu_query_lens,
                     int32_t max_q_len, float scale, float k_scale, float v_scale,
-                    const int32_t* work_info, const int32_t* num_work, int32_t capacity,
-                    int32_t tile_tokens, void* workspace, size_t workspace_bytes, void* stream);
+                    const int32_t* work_info, const int32_t* reduce_info, const int32_t* num_work,
+                    int32_t capacity, int32_t tile_tokens, void* workspace, size_t workspace_bytes,
+                    void* out, pa_dtype out_dtype, void* stream);
 
 /*
  * Log-sum-exp merge.  For output row r and head h: the owning request b is found by binary search

@@ -58,8 +58,8 @@ def load(path: str = LIB_PATH):
     lib.pa_plan.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]
     lib.pa_plan.restype = ctypes.c_int
     lib.pa_decode.argtypes = [vp, ctypes.c_int, i32, i32, i32, vp, vp, ctypes.c_int, i32, i32, i32,
-                              vp, i32, vp, i32, vp, i32, f32, f32, f32, vp, vp, i32, i32, vp,
-                              ctypes.c_size_t, vp]
+                              vp, i32, vp, i32, vp, i32, f32, f32, f32, vp, vp, vp, i32, i32, vp,
+                              ctypes.c_size_t, vp, ctypes.c_int, vp]
     lib.pa_decode.restype = ctypes.c_int
     lib.pa_merge.argtypes = [i32, i32, i32, i32, vp, i32, vp, i32, vp, ctypes.c_size_t, vp,
                              ctypes.c_int, vp]
@@ -161,9 +161,11 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_
               num_work: torch.Tensor, workspace: torch.Tensor, *, scale: float,
               cu_query_lens: Optional[torch.Tensor] = None, max_q_len: int = 1,
               k_scale: float = 1.0, v_scale: float = 1.0, tile_tokens: int = 256,
+              reduce_info: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
               stream=None) -> None:
     """Split-KV decode into the workspace (see include/pa.h).  kv_dtype is "f32", "bf16" or
-    "fp8" (uint8 tensors holding OCP e4m3fn codes)."""
+    "fp8" (uint8 tensors holding OCP e4m3fn codes).  With ``out`` (and ``reduce_info``) the merge
+    runs in the same call; the workspace must then have been allocated zero-filled."""
     dev = q.device
     if q.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("q must be float32 or bfloat16")
@@ -177,6 +179,14 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_
     _need(workspace, "workspace", torch.uint8, dev)
     if cu_query_lens is not None:
         _need(cu_query_lens, "cu_query_lens", torch.int32, dev)
+    if out is not None:
+        _need(out, "out", q.dtype, dev)
+        if tuple(out.shape) != tuple(q.shape):
+            raise ValueError("out must have the shape of q")
+        if reduce_info is None:
+            raise ValueError("reduce_info is required when out is given")
+    if reduce_info is not None:
+        _need(reduce_info, "reduce_info", torch.int32, dev)
     R, Hq, D = q.shape
     nb, Hkv, bs, D2 = k_cache.shape
     if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
@@ -191,8 +201,10 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_
                             _ptr(k_cache), _ptr(v_cache), _DTYPE_OF_NAME[kv_dtype], nb, Hkv, bs,
                             _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), B,
                             _ptr(cu_query_lens), max_q_len, scale, k_scale, v_scale,
-                            _ptr(work_info), _ptr(num_work), capacity, tile_tokens, _ptr(workspace),
-                            workspace.numel(), _stream(stream)), "pa_decode")
+                            _ptr(work_info), _ptr(reduce_info), _ptr(num_work), capacity, tile_tokens,
+                            _ptr(workspace), workspace.numel(), _ptr(out),
+                            PA_F32 if q.dtype == torch.float32 else PA_BF16, _stream(stream)),
+           "pa_decode")
 
 
 def pa_merge(out: torch.Tensor, reduce_info: torch.Tensor, workspace: torch.Tensor, *, capacity: int,

@@ -43,7 +43,8 @@ size_t pa_workspace_bytes(int32_t capacity, int32_t max_q_len, int32_t num_q_hea
     const unsigned long long states = (unsigned long long)capacity * max_q_len * num_q_heads;
     if (states > (1ull << 40)) return 0;
     return pa::workspace_acc_bytes(capacity, max_q_len, num_q_heads, head_dim) +
-           pa::workspace_ml_bytes(capacity, max_q_len, num_q_heads);
+           pa::workspace_ml_bytes(capacity, max_q_len, num_q_heads) +
+           pa::workspace_counter_bytes(capacity, num_q_heads);
 }
 
 pa_status pa_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
@@ -70,8 +71,9 @@ pa_status pa_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t n
                     const int32_t* block_tables, int32_t max_blocks_per_seq,
                     const int32_t* context_lens, int32_t num_seqs, const int32_t* cu_query_lens,
                     int32_t max_q_len, float scale, float k_scale, float v_scale,
-                    const int32_t* work_info, const int32_t* num_work, int32_t capacity,
-                    int32_t tile_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+                    const int32_t* work_info, const int32_t* reduce_info, const int32_t* num_work,
+                    int32_t capacity, int32_t tile_tokens, void* workspace, size_t workspace_bytes,
+                    void* out, pa_dtype out_dtype, void* stream) {
     if (num_rows < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_blocks < 0 || num_seqs < 0 ||
         max_blocks_per_seq < 0 || max_q_len < 1 || capacity < 0 || tile_tokens < 1 || head_dim < 1 ||
         block_size < 1)
@@ -90,12 +92,23 @@ pa_status pa_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t n
         if (num_seqs > 0 && (!q || !k_cache || !v_cache || !block_tables || !context_lens))
             return PA_INVALID_ARG;
     }
+    if (out) {
+        if (out_dtype != q_dtype) return PA_INVALID_ARG;
+        if (num_seqs > 0 && !reduce_info) return PA_INVALID_ARG;
+        if (!aligned(out, 16) || (reduce_info && !aligned(reduce_info, 8))) return PA_INVALID_ARG;
+        if ((long long)num_rows * num_q_heads > (long long)INT_MAX) return PA_UNSUPPORTED;
+    }
     if ((q && !aligned(q, 16)) || (k_cache && !aligned(k_cache, 16)) || (v_cache && !aligned(v_cache, 16)) ||
         (work_info && !aligned(work_info, 16)) || (workspace && !aligned(workspace, 256)))
         return PA_INVALID_ARG;
     const size_t need = pa_workspace_bytes(capacity, max_q_len, num_q_heads, head_dim);
     if (capacity > 0 && (need == 0 || workspace_bytes < need)) return PA_CAPACITY;
-    if (capacity == 0 || num_seqs == 0) return PA_OK;
+    if (capacity == 0 || num_seqs == 0) {
+        if (!out || num_rows == 0) return PA_OK;
+        // nothing to decode: the merge's contract still writes every row (all zero here)
+        return pa_merge(num_rows, num_q_heads, head_dim, 0, nullptr, 1, nullptr, 0, nullptr, 0, out,
+                        out_dtype, stream);
+    }
 
     pa::DecodeArgs a;
     a.q = q;
@@ -107,8 +120,13 @@ pa_status pa_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t n
     a.work_info = reinterpret_cast<const int4*>(work_info);
     a.num_work = num_work;
     a.ws_acc = static_cast<float*>(workspace);
-    a.ws_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
-                                       pa::workspace_acc_bytes(capacity, max_q_len, num_q_heads, head_dim));
+    const size_t acc_bytes = pa::workspace_acc_bytes(capacity, max_q_len, num_q_heads, head_dim);
+    const size_t ml_bytes = pa::workspace_ml_bytes(capacity, max_q_len, num_q_heads);
+    a.ws_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + acc_bytes);
+    a.ws_counters = reinterpret_cast<int*>(static_cast<uint8_t*>(workspace) + acc_bytes + ml_bytes);
+    a.reduce_info = reinterpret_cast<const int2*>(reduce_info);
+    a.out = out;
+    a.out_bf16 = out_dtype == PA_BF16 ? 1 : 0;
     a.num_rows = num_rows;
     a.num_q_heads = num_q_heads;
     a.num_kv_heads = num_kv_heads;

@@ -75,6 +75,79 @@ __device__ __forceinline__ bool slot_info(const DecodeArgs& a, int slot, SlotInf
 }
 
 // ---------------------------------------------------------------------------------------------
+// merge inside the decode launch
+// ---------------------------------------------------------------------------------------------
+
+// Log-sum-exp merge of request b's partial states for the rows of kv head g (rows n < M: token n / G,
+// query head g*G + n % G) into out.  The states were written by other workgroups of this launch, so
+// they are read with device-coherent loads.  Thread t handles the 16-byte columns u = t, t + nthreads, ...
+// of the M x D/4 row-column grid and folds the request's partitions in order with a running max.
+template <int D>
+__device__ __forceinline__ void merge_request_rows(const DecodeArgs& a, int b, int g, int row0, int M,
+                                                   int nthreads) {
+    constexpr int NDC = D / 4;
+    const int2 ri = a.reduce_info[b];
+    const int first = max(ri.x, 0);
+    const int parts = max(min(ri.y, a.capacity - first), 0);
+    const int G = a.group;
+    const size_t step = static_cast<size_t>(a.max_q_len) * a.num_q_heads;
+    for (int u = threadIdx.x; u < M * NDC; u += nthreads) {
+        const int n = u / NDC;
+        const int dc = u - n * NDC;
+        const int i = n / G;
+        const int h = g * G + (n - i * G);
+        const size_t st0 = (static_cast<size_t>(first) * a.max_q_len + i) * a.num_q_heads + h;
+        float m = -INFINITY, l = 0.f;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+        for (int j = 0; j < parts; ++j) {
+            const size_t st = st0 + static_cast<size_t>(j) * step;
+            const float2 ml = load_f2_coherent(a.ws_ml + st * 2);
+            const float2 v01 = load_f2_coherent(a.ws_acc + st * D + 4 * dc);
+            const float2 v23 = load_f2_coherent(a.ws_acc + st * D + 4 * dc + 2);
+            if (ml.y > 0.f) {
+                const float mn = fmaxf(m, ml.x);
+                const float fo = __builtin_amdgcn_exp2f(m - mn);
+                const float fn = __builtin_amdgcn_exp2f(ml.x - mn);
+                l = l * fo + ml.y * fn;
+                acc.x = acc.x * fo + v01.x * fn;
+                acc.y = acc.y * fo + v01.y * fn;
+                acc.z = acc.z * fo + v23.x * fn;
+                acc.w = acc.w * fo + v23.y * fn;
+                m = mn;
+            }
+        }
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        const size_t o = (static_cast<size_t>(row0 + i) * a.num_q_heads + h) * D + 4 * dc;
+        const float4 r = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+        if (a.out_bf16) {
+            uint2 w;
+            w.x = pack_bf16x2(r.x, r.y);
+            w.y = pack_bf16x2(r.z, r.w);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + o) = w;
+        } else {
+            *reinterpret_cast<float4*>(static_cast<float*>(a.out) + o) = r;
+        }
+    }
+}
+
+// Write row r of out as zeros when no plan slot owns it: padding rows past the last cumulative
+// query length, rows of requests without partitions, and tokens past max_q_len.  One wave per row.
+template <int D>
+__device__ __forceinline__ void zero_unowned_row(const DecodeArgs& a, int r, int lane) {
+    if (r >= a.num_rows) return;
+    int i;
+    const int b = owner_of_row(a.cu, a.num_seqs, a.max_q_len, r, i);
+    if (b >= 0 && a.reduce_info[b].y > 0) return;
+    const size_t base = static_cast<size_t>(r) * a.num_q_heads * D;
+    const int n4 = a.num_q_heads * D / 4;
+    for (int e = lane; e < n4; e += 64) {
+        if (a.out_bf16) *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + base + 4 * e) = make_uint2(0u, 0u);
+        else *reinterpret_cast<float4*>(static_cast<float*>(a.out) + base + 4 * e) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
 // matrix-core kernel (bf16 or fp8 caches)
 // ---------------------------------------------------------------------------------------------
 template <int D, int NCB, bool KV8>
@@ -115,10 +188,17 @@ template <int D, int NCB, bool KV8, bool QF32>
 __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::WAVES)) void decode_mfma_kernel(const DecodeArgs a) {
     using C = Mfma<D, NCB, KV8>;
     __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS];
+    __shared__ int s_last;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const int work_groups = a.capacity * a.num_kv_heads;
+    if (static_cast<int>(blockIdx.x) >= work_groups) {
+        // merge launched with the decode: trailing workgroups write the rows no slot owns as zeros
+        zero_unowned_row<D>(a, (blockIdx.x - work_groups) * C::NW + wave, lane);
+        return;
+    }
     const int slot = blockIdx.x / a.num_kv_heads;
     const int g = blockIdx.x - slot * a.num_kv_heads;
 
@@ -266,16 +346,20 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
     };
 
     // Write a staged chunk into the wave's LDS tiles as bf16 rows; rows >= nv are zero.
-    auto stage = [&](int st, int nv) {
+    auto stage = [&](int st, int nv, bool full) {
 #pragma unroll
         for (int it = 0; it < C::NLD; ++it) {
             const int f = it * 64 + lane;
             const int r = f / C::GCPR;
             const int c = f - r * C::GCPR;
-            const bool ok = r < nv;
-            const u32x4_t z = {0u, 0u, 0u, 0u};
-            u32x4_t kv = ok ? kreg[st][it] : z;
-            u32x4_t vv = ok ? vreg[st][it] : z;
+            u32x4_t kv = kreg[st][it];
+            u32x4_t vv = vreg[st][it];
+            if (!full) {
+                const bool ok = r < nv;
+                const u32x4_t z = {0u, 0u, 0u, 0u};
+                kv = ok ? kv : z;
+                vv = ok ? vv : z;
+            }
             if constexpr (!KV8) {
                 const int off = lds_col<C::LRB, C::SWM>(r, c);
                 *reinterpret_cast<u32x4_t*>(klds + off) = kv;
@@ -322,7 +406,8 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
             const int nv = nvalid_st[st];
 
             compiler_fence();
-            stage(st, nv);
+            if (nv == 16) stage(st, 16, true);     // uniform: only a slot's ragged last chunk is partial
+            else stage(st, nv, false);
             compiler_fence();
             if (k + C::PF < my_chunks) issue(st, k + C::PF);
 
@@ -366,7 +451,8 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
                 const bool grow = mt > m_run[cb] + kRescaleSlack;
                 if (__builtin_amdgcn_ballot_w64(grow)) {
                     const float mnew = grow ? mt : m_run[cb];
-                    const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - mnew);
+                    // a row with no visible key yet keeps (-inf, 0, 0): never form -inf - -inf
+                    const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[cb] - mnew);
                     l_run[cb] *= alpha;
 #pragma unroll
                     for (int t = 0; t < C::DT; ++t) acc[cb][t] *= alpha;
@@ -437,7 +523,8 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
     // ---- write the slot's states: rows n < M, token i = n / G, head g*G + n % G ----
     constexpr int D4 = D / 4;
     const size_t slot_base = static_cast<size_t>(slot) * a.max_q_len;
-    for (int e = tid; e < M * D4; e += 64 * C::NW) {
+    const bool single = a.out != nullptr && a.reduce_info[b].y == 1;
+    for (int e = tid; e < (single ? 0 : M * D4); e += 64 * C::NW) {
         const int n = e / D4;
         const int d4 = e - n * D4;
         const int i = n / G;
@@ -445,9 +532,53 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
         const size_t st = (slot_base + i) * a.num_q_heads + h;
         float4_t v = *reinterpret_cast<const float4_t*>(abuf + n * C::APITCH + 4 * d4);
         v *= a.v_scale;
-        *reinterpret_cast<float4_t*>(a.ws_acc + st * D + 4 * d4) = v;
-        if (d4 == 0) *reinterpret_cast<float2*>(a.ws_ml + st * 2) = make_float2(Mbuf[n], lbuf[n]);
+        if (a.out == nullptr) {
+            *reinterpret_cast<float4_t*>(a.ws_acc + st * D + 4 * d4) = v;
+            if (d4 == 0) *reinterpret_cast<float2*>(a.ws_ml + st * 2) = make_float2(Mbuf[n], lbuf[n]);
+        } else {
+            // merged in this launch by another workgroup: write through to memory
+            store_f2_coherent(a.ws_acc + st * D + 4 * d4, v[0], v[1]);
+            store_f2_coherent(a.ws_acc + st * D + 4 * d4 + 2, v[2], v[3]);
+            if (d4 == 0) store_f2_coherent(a.ws_ml + st * 2, Mbuf[n], lbuf[n]);
+        }
     }
+    if (a.out == nullptr) return;
+
+    // ---- merge in the same launch: the last workgroup of (request, kv head) to finish merges ----
+    if (a.reduce_info[b].y == 1) {
+        // a request with one partition: this workgroup holds the whole softmax state
+        for (int e = tid; e < M * D4; e += 64 * C::NW) {
+            const int n = e / D4;
+            const int d4 = e - n * D4;
+            const int i = n / G;
+            const int h = g * G + (n - i * G);
+            const float l = lbuf[n];
+            const float inv = l > 0.f ? a.v_scale / l : 0.f;
+            const float4_t v = *reinterpret_cast<const float4_t*>(abuf + n * C::APITCH + 4 * d4) * inv;
+            const size_t o = (static_cast<size_t>(si.row0 + i) * a.num_q_heads + h) * D + 4 * d4;
+            if (a.out_bf16) {
+                uint2 w;
+                w.x = pack_bf16x2(v[0], v[1]);
+                w.y = pack_bf16x2(v[2], v[3]);
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + o) = w;
+            } else {
+                *reinterpret_cast<float4_t*>(static_cast<float*>(a.out) + o) = v;
+            }
+        }
+        return;
+    }
+    wait_memory_acks();                               // this thread's states are in memory
+    __syncthreads();                                  // ... and every other thread's
+    int* counter = a.ws_counters + b * a.num_kv_heads + g;
+    if (tid == 0) {
+        const int parts = a.reduce_info[b].y;
+        const int seen = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (seen + 1 == parts) ? 1 : 0;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    merge_request_rows<D>(a, b, g, si.row0, M, 64 * C::NW);
+    if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -536,7 +667,9 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeArgs a) {
 
 template <int D, int NCB, bool KV8>
 hipError_t launch_mfma_q(const DecodeArgs& a, bool qf32, dim3 grid, hipStream_t stream) {
-    const dim3 block(64 * Mfma<D, NCB, KV8>::NW);
+    constexpr int NW = Mfma<D, NCB, KV8>::NW;
+    const dim3 block(64 * NW);
+    if (a.out) grid.x += (a.num_rows + NW - 1) / NW;   // one wave per row for the zero fill
     if (qf32) hipLaunchKernelGGL((decode_mfma_kernel<D, NCB, KV8, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((decode_mfma_kernel<D, NCB, KV8, false>), grid, block, 0, stream, a);
     return hipGetLastError();
@@ -554,7 +687,20 @@ hipError_t launch_d(const DecodeArgs& a, pa_dtype kv, int ncb, bool qf32, dim3 g
     if (kv == PA_F32) {
         if (qf32) hipLaunchKernelGGL((decode_f32_kernel<D, true>), grid, dim3(256), 0, stream, a);
         else hipLaunchKernelGGL((decode_f32_kernel<D, false>), grid, dim3(256), 0, stream, a);
-        return hipGetLastError();
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || !a.out) return e;
+        MergeArgs m;                                  // fp32 caches: the merge is a second launch
+        m.cu = a.cu;
+        m.reduce_info = a.reduce_info;
+        m.ws_acc = a.ws_acc;
+        m.ws_ml = a.ws_ml;
+        m.out = a.out;
+        m.num_rows = a.num_rows;
+        m.num_q_heads = a.num_q_heads;
+        m.num_seqs = a.num_seqs;
+        m.max_q_len = a.max_q_len;
+        m.capacity = a.capacity;
+        return launch_merge(m, D, a.out_bf16 != 0, stream);
     }
     if (kv == PA_BF16) return launch_mfma_ncb<D, false>(a, ncb, qf32, grid, stream);
     return launch_mfma_ncb<D, true>(a, ncb, qf32, grid, stream);

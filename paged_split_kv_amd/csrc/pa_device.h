@@ -30,9 +30,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return static_cast<uint16_t>(u >> 16);
 }
 
-// Two floats -> packed bf16 pair (lo in bits 0..15).
+// Two floats -> packed bf16 pair (lo in bits 0..15), round to nearest even: one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
 // OCP E4M3 ("fn") code -> bfloat16 bits, exact: every e4m3fn value is a bf16 value.
@@ -75,20 +78,74 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Device-coherent 8-byte accesses (agent-scope relaxed atomics: per instruction they bypass the
+// per-XCD L2, writing through to memory or reading from it), used to hand partial states from one
+// workgroup to another inside a launch without writing back or invalidating whole caches.
+__device__ __forceinline__ void store_f2_coherent(float* p, float a, float b) {
+    const unsigned long long bits =
+        (static_cast<unsigned long long>(__float_as_uint(b)) << 32) | __float_as_uint(a);
+    __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), bits, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float2 load_f2_coherent(const float* p) {
+    const unsigned long long bits = __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p),
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__uint_as_float(static_cast<unsigned>(bits)),
+                       __uint_as_float(static_cast<unsigned>(bits >> 32)));
+}
+
+// Wait until this wave's outstanding memory operations are acknowledged (stores included).
+__device__ __forceinline__ void wait_memory_acks() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Workspace layout (see pa_workspace_bytes): acc region then (m, l) region, each 256-byte aligned.
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-struct WorkspaceView {
-    float* acc;   // [capacity, max_q_len, num_q_heads, head_dim]
-    float* ml;    // [capacity, max_q_len, num_q_heads, 2]   (running max in base-2 units, sum)
-};
-
+// Workspace regions: acc [capacity, max_q_len, num_q_heads, head_dim] fp32, then (m, l) pairs
+// [capacity, max_q_len, num_q_heads, 2] fp32 (m is the running max in base-2 units), then the arrival
+// counters of the fused merge [capacity * num_q_heads] int32 (one per (request, kv head) is used).
 __host__ __device__ inline size_t workspace_acc_bytes(int capacity, int max_q_len, int hq, int d) {
     return align256(static_cast<size_t>(capacity) * max_q_len * hq * d * sizeof(float));
 }
 
 __host__ __device__ inline size_t workspace_ml_bytes(int capacity, int max_q_len, int hq) {
     return align256(static_cast<size_t>(capacity) * max_q_len * hq * 2 * sizeof(float));
+}
+
+__host__ __device__ inline size_t workspace_counter_bytes(int capacity, int hq) {
+    return align256(static_cast<size_t>(capacity) * hq * sizeof(int32_t));
+}
+
+// Owning request and token of output row r (-1 when the row is padding or otherwise unowned).
+// With cumulative query lengths this is the last b with cu[b] <= r, found by a 64-way search in which
+// every lane of the wave loads one probe: one round of loads for up to 64 requests, two up to 4096.
+// All lanes of the wave must call it with the same r.
+__device__ __forceinline__ int owner_of_row(const int32_t* cu, int num_seqs, int max_q_len, int r, int& i) {
+    i = 0;
+    int b = -1;
+    if (cu) {
+        if (num_seqs > 0 && r >= cu[0] && r < cu[num_seqs]) {
+            const int lane = threadIdx.x & 63;
+            int lo = 0, hi = num_seqs;                    // cu[lo] <= r; answer in [lo, hi)
+            while (hi - lo > 1) {
+                const int step = (hi - lo + 63) >> 6;
+                const int idx = lo + lane * step;
+                const int v = idx < hi ? cu[idx] : 0x7fffffff;
+                const unsigned long long m = __builtin_amdgcn_ballot_w64(v <= r);
+                const int k = __builtin_popcountll(m);     // probes are monotone: lanes 0..k-1 hold
+                const int nlo = lo + (k - 1) * step;
+                hi = min(hi, nlo + step);
+                lo = nlo;
+            }
+            b = lo;
+            i = r - cu[b];
+            if (i >= cu[b + 1] - cu[b]) b = -1;
+        }
+    } else if (r < num_seqs) {
+        b = r;
+    }
+    if (i >= max_q_len) b = -1;
+    return b;
 }
 
 
@@ -106,6 +163,10 @@ struct DecodeArgs {
     const int32_t* num_work;
     float* ws_acc;
     float* ws_ml;
+    int* ws_counters;           // arrival counters of the fused merge
+    const int2* reduce_info;    // (first slot, partitions) per request; needed when out is set
+    void* out;                  // nullable: when set, the merge runs inside the decode launch
+    int out_bf16;
     int num_rows, num_q_heads, num_kv_heads, group;   // group = Hq / Hkv
     int num_blocks, block_size, max_blocks, num_seqs;
     int max_q_len, capacity, tile_tokens;

@@ -14,29 +14,6 @@ namespace pa {
 
 namespace {
 
-// Owning request and token of output row r (-1 when the row is padding or otherwise unowned).
-__device__ __forceinline__ int owner_of_row(const MergeArgs& a, int r, int& i) {
-    i = 0;
-    int b = -1;
-    if (a.cu) {
-        if (a.num_seqs > 0 && r >= a.cu[0] && r < a.cu[a.num_seqs]) {
-            int lo = 0, hi = a.num_seqs - 1;          // last b with cu[b] <= r
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (a.cu[mid] <= r) lo = mid;
-                else hi = mid - 1;
-            }
-            b = lo;
-            i = r - a.cu[b];
-            if (i >= a.cu[b + 1] - a.cu[b]) b = -1;
-        }
-    } else if (r < a.num_seqs) {
-        b = r;
-    }
-    if (i >= a.max_q_len) b = -1;
-    return b;
-}
-
 // One workgroup of 256 threads per (row, head).  Thread t owns the 16-byte column dc = t % (D/4) of
 // the head dimension and the partials j = pg, pg + NPG, ... with pg = t / (D/4); it folds them into a
 // running (max, sum, acc) with independent loads, then the NPG states of a column are combined in LDS.
@@ -55,7 +32,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
     const int h = blockIdx.x - r * a.num_q_heads;
 
     int i;
-    const int b = owner_of_row(a, r, i);
+    const int b = owner_of_row(a.cu, a.num_seqs, a.max_q_len, r, i);
     float m = -INFINITY, l = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (b >= 0) {
@@ -64,7 +41,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
         const int parts = max(min(ri.y, a.capacity - first), 0);
         const size_t step = static_cast<size_t>(a.max_q_len) * a.num_q_heads;       // states per slot
         const size_t st0 = (static_cast<size_t>(first) * a.max_q_len + i) * a.num_q_heads + h;
-#pragma unroll 4
+#pragma unroll 8
         for (int j = pg; j < parts; j += NPG) {
             const size_t st = st0 + static_cast<size_t>(j) * step;
             const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + st * 2);

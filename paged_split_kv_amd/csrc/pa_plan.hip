@@ -7,8 +7,8 @@
 // the shares is this library's reading, documented in pa.h.
 //
 // One workgroup of 1024 threads does the whole plan: a reduction for the total length and the number
-// of non-empty requests, the per-request counts, a block-wide exclusive scan into LDS, and then one
-// thread per slot fills work_info by binary-searching the scanned offsets.  Integer-only, 64-bit where
+// of non-empty requests, the per-request counts, an exclusive scan into LDS, and then one thread per
+// slot fills work_info by binary-searching the scanned offsets.  Integer-only, 64-bit where
 // products can exceed 32 bits, so the result is bit-identical to any other exact evaluation.
 #include "pa_device.h"
 
@@ -121,12 +121,19 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
                 else hi = mid - 1;
             }
             const int b = lo;
-            const long long j = s - first[b];
-            const long long parts = first[b + 1] - first[b];
+            const int j = s - first[b];
+            const int parts = first[b + 1] - first[b];
             const int len = max(context_lens[b], 0);
-            const long long tiles = (static_cast<long long>(len) + tile_tokens - 1) / tile_tokens;
-            const int tb = static_cast<int>((j * tiles) / parts);
-            const int te = static_cast<int>(((j + 1) * tiles) / parts);
+            const unsigned tiles = static_cast<unsigned>((static_cast<long long>(len) + tile_tokens - 1) / tile_tokens);
+            int tb, te;
+            if (static_cast<unsigned long long>(parts) * tiles < (1ull << 32)) {
+                // (j + 1) * tiles <= parts * tiles fits 32 bits: exact unsigned division
+                tb = static_cast<int>((static_cast<unsigned>(j) * tiles) / static_cast<unsigned>(parts));
+                te = static_cast<int>((static_cast<unsigned>(j + 1) * tiles) / static_cast<unsigned>(parts));
+            } else {
+                tb = static_cast<int>((static_cast<long long>(j) * tiles) / parts);
+                te = static_cast<int>((static_cast<long long>(j + 1) * tiles) / parts);
+            }
             work_info[s] = make_int4(b, tb, te, len);
         } else {
             work_info[s] = make_int4(-1, 0, 0, 0);

@@ -38,7 +38,8 @@ class DecodeStep:
         self.reduce_info = torch.empty((num_seqs, 2), dtype=torch.int32, device=self.device)
         self.num_work = torch.empty((1,), dtype=torch.int32, device=self.device)
         nbytes = B.pa_workspace_bytes(self.capacity, max_q_len, num_q_heads, head_dim)
-        self.workspace = torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=self.device)
+        # zero-filled once: the fused merge's arrival counters start (and are left) at zero
+        self.workspace = torch.zeros((max(nbytes, 256),), dtype=torch.uint8, device=self.device)
         self.out = torch.empty((num_rows, num_q_heads, head_dim), dtype=out_dtype, device=self.device)
 
     @classmethod
@@ -55,26 +56,33 @@ class DecodeStep:
                   stream=stream)
 
     def decode(self, q, k_cache, v_cache, kv_dtype, block_tables, context_lens, *, scale,
-               cu_query_lens=None, k_scale=1.0, v_scale=1.0, stream=None) -> None:
+               cu_query_lens=None, k_scale=1.0, v_scale=1.0, merge: bool = False, stream=None) -> None:
+        """pa_decode; with merge=True the log-sum-exp merge into self.out runs in the same call."""
         B.pa_decode(q, k_cache, v_cache, kv_dtype, block_tables, context_lens, self.work_info,
                     self.num_work, self.workspace, scale=scale, cu_query_lens=cu_query_lens,
                     max_q_len=self.max_q_len, k_scale=k_scale, v_scale=v_scale,
-                    tile_tokens=self.plan_cfg.tile_tokens, stream=stream)
+                    tile_tokens=self.plan_cfg.tile_tokens,
+                    reduce_info=self.reduce_info if merge else None,
+                    out=self.out if merge else None, stream=stream)
 
     def merge(self, cu_query_lens=None, stream=None) -> torch.Tensor:
         B.pa_merge(self.out, self.reduce_info, self.workspace, capacity=self.capacity,
                    cu_query_lens=cu_query_lens, max_q_len=self.max_q_len, stream=stream)
         return self.out
 
-    def run_case(self, case, stream=None, replan: bool = True) -> torch.Tensor:
+    def run_case(self, case, stream=None, replan: bool = True, fused: bool = True) -> torch.Tensor:
+        """Plan, decode and merge one Case.  fused=True merges inside pa_decode (two launches per
+        step); fused=False calls pa_merge separately."""
         if replan:
             self.plan(case.context_lens, stream)
         self.decode(case.q, case.k_cache, case.v_cache, case.kv_dtype, case.block_tables,
                     case.context_lens, scale=case.scale, cu_query_lens=case.cu_query_lens,
-                    k_scale=case.k_scale, v_scale=case.v_scale, stream=stream)
+                    k_scale=case.k_scale, v_scale=case.v_scale, merge=fused, stream=stream)
+        if fused:
+            return self.out
         return self.merge(case.cu_query_lens, stream)
 
 
-def run_case(case, plan: Optional[PlanConfig] = None) -> torch.Tensor:
+def run_case(case, plan: Optional[PlanConfig] = None, fused: bool = True) -> torch.Tensor:
     """Plan, decode and merge one workload Case; returns the output tensor (device)."""
-    return DecodeStep.for_case(case, plan).run_case(case)
+    return DecodeStep.for_case(case, plan).run_case(case, fused=fused)

@@ -48,10 +48,11 @@ def test_capacity_matches_oracle(seed):
 
 
 def test_workspace_bytes():
-    # fp32 partials [C, Lmax, Hq, D] then (m, l) pairs [C, Lmax, Hq, 2], each rounded up to 256 bytes
+    # fp32 partials [C, Lmax, Hq, D], (m, l) pairs [C, Lmax, Hq, 2] and int32 counters [C * Hq],
+    # each rounded up to 256 bytes
     def expect(c, l, h, d):
         up = lambda x: (x + 255) // 256 * 256
-        return up(c * l * h * d * 4) + up(c * l * h * 2 * 4)
+        return up(c * l * h * d * 4) + up(c * l * h * 2 * 4) + up(c * h * 4)
     for args in [(512, 1, 4, 64), (256, 1, 16, 128), (512, 3, 6, 256), (1, 1, 1, 64), (0, 1, 1, 64)]:
         assert B.pa_workspace_bytes(*args) == expect(*args)
     assert B.pa_workspace_bytes(10, 0, 1, 64) == 0
@@ -83,8 +84,8 @@ def test_plan_argument_checks():
 
 
 _GOOD = dict(q=256, qd=B.PA_BF16, R=4, Hq=16, D=128, k=256, v=256, kvd=B.PA_BF16, nb=10, Hkv=2, bs=16,
-             bt=256, mb=4, ctx=256, Bn=4, cu=None, ql=1, scale=0.1, ks=1.0, vs=1.0, work=256, nw=256,
-             cap=256, T=256, ws=256, wsb=1 << 30)
+             bt=256, mb=4, ctx=256, Bn=4, cu=None, ql=1, scale=0.1, ks=1.0, vs=1.0, work=256, red=256,
+             nw=256, cap=256, T=256, ws=256, wsb=1 << 30, out=None, od=B.PA_BF16)
 
 
 def _decode_status(**kw):
@@ -94,7 +95,8 @@ def _decode_status(**kw):
     return B.load().pa_decode(vp(a["q"]), a["qd"], a["R"], a["Hq"], a["D"], vp(a["k"]), vp(a["v"]),
                               a["kvd"], a["nb"], a["Hkv"], a["bs"], vp(a["bt"]), a["mb"], vp(a["ctx"]),
                               a["Bn"], vp(a["cu"]), a["ql"], a["scale"], a["ks"], a["vs"], vp(a["work"]),
-                              vp(a["nw"]), a["cap"], a["T"], vp(a["ws"]), a["wsb"], None)
+                              vp(a["red"]), vp(a["nw"]), a["cap"], a["T"], vp(a["ws"]), a["wsb"],
+                              vp(a["out"]), a["od"], None)
 
 
 def test_decode_argument_checks():
@@ -118,6 +120,11 @@ def test_decode_argument_checks():
     assert _decode_status(wsb=1000) == B.PA_CAPACITY
     assert _decode_status(scale=float("nan")) == B.PA_INVALID_ARG
     assert _decode_status(Bn=-1) == B.PA_INVALID_ARG
+    assert _decode_status(out=512, od=B.PA_F32) == B.PA_INVALID_ARG    # merged output dtype != q dtype
+    assert _decode_status(out=512, red=None, D=96) == B.PA_UNSUPPORTED
+    assert _decode_status(out=512, red=None) == B.PA_INVALID_ARG       # merging needs reduce_info
+    assert _decode_status(out=520) == B.PA_INVALID_ARG                 # out not 16-aligned
+    assert _decode_status(out=512, red=260) == B.PA_INVALID_ARG        # reduce_info entries misaligned
     assert _decode_status(cap=0) == B.PA_OK                            # nothing to do: no launch
     assert _decode_status(Bn=0) == B.PA_OK
 

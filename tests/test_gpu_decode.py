@@ -36,6 +36,10 @@ SMALL = [
     ("f32_d128_verify", [500, 31, 2], [3, 2, 2], 8, 2, 128, 64, "f32", "f32", 1, 8, 64),
     ("f32_d256_qbf16", [700, 90], [1, 2], 4, 2, 256, 16, "f32", "bf16", 0, 256, 256),
     ("bf16_many_slots", [4096, 4096, 100, 5000], None, 8, 1, 128, 16, "bf16", "bf16", 0, 256, 16),
+    # last tile holds fewer keys than the request has query tokens: early tokens see nothing in the
+    # wave that owns it while the last token does (regression: such rows must stay (-inf, 0, 0))
+    ("bf16_short_last_tile", [257, 513, 258, 769], [3, 3, 2, 4], 8, 2, 128, 16, "bf16", "bf16", 1, 1, 256),
+    ("fp8_short_last_tile", [257, 1025], [3, 4], 8, 2, 64, 16, "fp8", "bf16", 0, 1, 256),
 ]
 
 
@@ -45,11 +49,18 @@ def _small_case(spec, seed):
                         kv_dtype=kv, q_dtype=qd, seed=seed, q_lens=ql, pad_rows=pad, device=DEV), P, T
 
 
-def _run(case, P=256, T=256, cu_count=256):
+def _partial_bytes(step):
+    """Bytes of the workspace's partial-state regions (the arrival counters follow them)."""
+    up = lambda x: (x + 255) // 256 * 256
+    c, l, h, d = step.capacity, step.max_q_len, step.out.shape[1], step.out.shape[2]
+    return up(c * l * h * d * 4) + up(c * l * h * 2 * 4)
+
+
+def _run(case, P=256, T=256, cu_count=256, fused=True):
     step = DecodeStep.for_case(case, PlanConfig(cu_count=cu_count, max_partitions=P, tile_tokens=T))
     step.out.fill_(float("nan"))
-    step.workspace.fill_(0xFF)              # NaN pattern in every fp32 slot
-    out = step.run_case(case)
+    step.workspace[:_partial_bytes(step)].fill_(0xFF)    # NaN pattern in every partial-state slot
+    out = step.run_case(case, fused=fused)
     torch.cuda.synchronize()
     return out, step
 
@@ -71,11 +82,12 @@ def _zero_rows(case):
     return zero
 
 
+@pytest.mark.parametrize("fused", [True, False], ids=["fused_merge", "separate_merge"])
 @pytest.mark.parametrize("spec", SMALL, ids=[s[0] for s in SMALL])
-def test_small_cases_match_oracle(spec):
+def test_small_cases_match_oracle(spec, fused):
     case, P, T = _small_case(spec, seed=11)
-    announce(f"small {spec[0]}")
-    out, _ = _run(case, P, T)
+    announce(f"small {spec[0]} fused={fused}")
+    out, _ = _run(case, P, T, fused=fused)
     got = to_f64(out)
     ref = oracle_direct(case)
     assert_close(got, ref, tolerance_kind(case), spec[0])
@@ -106,6 +118,32 @@ def test_skewed_steps(which):
     case = W.make_config("skewed_bf16", device=DEV, step=idx)
     out, _ = _run(case, cu_count=256)
     assert_close(to_f64(out), oracle_direct(case), "bf16", f"skewed {which}")
+
+
+def test_full_size_separate_merge_fp8():
+    announce("full fp8_kv, separate merge")
+    case = W.make_config("fp8_kv", device=DEV)
+    out, _ = _run(case, cu_count=256, fused=False)
+    assert_close(to_f64(out), oracle_direct(case), "fp8", "fp8 separate merge")
+
+
+def test_fused_calls_back_to_back_reuse_the_workspace():
+    # one step object (one workspace) across several different batches: the arrival counters must
+    # return to zero after every call for the next merge to fire correctly
+    specs = [("a", [700, 33, 1, 2000], [2, 1, 1, 3], 8, 2, 128, 16, "bf16", "bf16", 2, 256, 256),
+             ("b", [90, 5000, 12, 64], [1, 3, 2, 1], 8, 2, 128, 16, "bf16", "bf16", 2, 256, 256),
+             ("c", [0, 300, 4096, 7], [2, 1, 3, 1], 8, 2, 128, 16, "bf16", "bf16", 2, 256, 256)]
+    cases = [_small_case(sp, seed=20 + k)[0] for k, sp in enumerate(specs)]
+    step = DecodeStep.for_case(cases[0], PlanConfig(cu_count=256))
+    for rep in range(2):
+        for k, case in enumerate(cases):
+            announce(f"back-to-back {rep} {k}")
+            step.out.fill_(float("nan"))
+            out = step.run_case(case, fused=True)
+            torch.cuda.synchronize()
+            assert_close(to_f64(out), oracle_direct(case), "bf16", f"back-to-back {rep} {k}")
+    nbytes = _partial_bytes(step)
+    assert int(step.workspace[nbytes:].view(torch.int32).abs().sum().item()) == 0
 
 
 def test_single_key_row_is_the_value_row_fp32():
