@@ -39,7 +39,7 @@
  *   cu_query_lens  [num_seqs + 1] or NULL           cumulative query lengths; NULL = one row per request
  *   work_info      [capacity, 4]  (request, tile_begin, tile_end, S_b); unused slots (-1, 0, 0, 0)
  *   reduce_info    [num_seqs, 2]  (first_slot, num_partitions)
- *   num_work       [1]            number of used slots
+ *   num_work       [2]            (number of used slots, tiles in the largest slot); 8-byte aligned
  *   workspace      pa_workspace_bytes(...) bytes: fp32 partials written by pa_decode and read by
  *                  pa_merge, plus the counters of the merge pa_decode can run in the same launch
  *
@@ -101,6 +101,7 @@ size_t pa_workspace_bytes(int32_t capacity, int32_t max_q_len, int32_t num_q_hea
  * requests with S_b = 0 get none.  Partition j of request b covers tiles
  * [floor(j tiles_b / parts_b), floor((j + 1) tiles_b / parts_b)).  Every slot of work_info is
  * rewritten (unused ones to (-1, 0, 0, 0)), so a plan never carries data from an earlier call.
+ * num_work receives the number of used slots and the tile count of the largest slot.
  * Negative S_b (a precondition violation) are planned as 0.
  * Errors: PA_INVALID_ARG (null pointers, num_seqs < 0, arguments < 1), PA_UNSUPPORTED
  * (num_seqs > PA_MAX_SEQS), PA_CAPACITY (capacity too small), PA_HIP_ERROR (launch failure).

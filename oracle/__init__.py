@@ -102,9 +102,10 @@ def plan_capacity(num_seqs: int, num_kv_heads: int, cu_count: int = 256, budget_
 
 
 def plan(context_lens, num_kv_heads: int, cu_count: int = 256, budget_mult: int = 2,
-         max_partitions: int = 256, tile_tokens: int = 256,
-         capacity: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray, int]:
-    """Returns (work_info int32 [capacity, 4], reduce_info int32 [B, 2], num_work)."""
+         max_partitions: int = 256, tile_tokens: int = 256, capacity: Optional[int] = None,
+         with_largest: bool = False):
+    """Returns (work_info int32 [capacity, 4], reduce_info int32 [B, 2], num_work) and, with
+    with_largest, also the tile count of the largest slot."""
     ctx = _i32(context_lens)
     B = int(ctx.shape[0])
     cap = plan_capacity(B, num_kv_heads, cu_count, budget_mult, max_partitions)
@@ -112,11 +113,13 @@ def plan(context_lens, num_kv_heads: int, cu_count: int = 256, budget_mult: int 
         capacity = cap
     work = np.zeros((max(capacity, 0), 4), dtype=np.int32)
     red = np.zeros((B, 2), dtype=np.int32)
-    nw = np.zeros(1, dtype=np.int32)
+    nw = np.zeros(2, dtype=np.int32)
     st = _load().orc_plan(_ptr(ctx), B, num_kv_heads, cu_count, budget_mult, max_partitions,
                           tile_tokens, capacity, _ptr(work), _ptr(red), _ptr(nw))
     if st != OK:
         raise OracleError("invalid planner arguments")
+    if with_largest:
+        return work, red, int(nw[0]), int(nw[1])
     return work, red, int(nw[0])
 
 

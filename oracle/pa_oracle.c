@@ -116,7 +116,8 @@ int orc_plan_capacity(int num_seqs, int num_kv_heads, int cu_count, int budget_m
  *   W = sum S_b;  any remainder is left unused.
  * Slots are filled request by request; partition j of request b spans tiles
  * [floor(j tiles_b / parts_b), floor((j+1) tiles_b / parts_b)).  Unused slots hold (-1, 0, 0, 0).
- * work_info[slot] = (request, tile_begin, tile_end, S_b); reduce_info[b] = (first_slot, parts_b).
+ * work_info[slot] = (request, tile_begin, tile_end, S_b); reduce_info[b] = (first_slot, parts_b);
+ * num_work = (used slots, tiles of the largest slot).
  */
 int orc_plan(const int32_t* context_lens, int num_seqs, int num_kv_heads, int cu_count,
              int budget_mult, int max_partitions, int tile_tokens, int capacity,
@@ -138,6 +139,7 @@ int orc_plan(const int32_t* context_lens, int num_seqs, int num_kv_heads, int cu
     int64_t extra = (int64_t)cap - nonempty;
 
     int64_t slot = 0;
+    int32_t largest = 0;
     for (int b = 0; b < num_seqs; ++b) {
         int64_t s = context_lens[b];
         int64_t parts = 0;
@@ -155,6 +157,7 @@ int orc_plan(const int32_t* context_lens, int num_seqs, int num_kv_heads, int cu
             w[1] = (int32_t)((j * tiles) / parts);
             w[2] = (int32_t)(((j + 1) * tiles) / parts);
             w[3] = (int32_t)s;
+            if (w[2] - w[1] > largest) largest = w[2] - w[1];
         }
         slot += parts;
     }
@@ -165,7 +168,8 @@ int orc_plan(const int32_t* context_lens, int num_seqs, int num_kv_heads, int cu
         work_info[4 * w + 2] = 0;
         work_info[4 * w + 3] = 0;
     }
-    *num_work = (int32_t)slot;
+    num_work[0] = (int32_t)slot;
+    num_work[1] = largest;
     return ORC_OK;
 }
 

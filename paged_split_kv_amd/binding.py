@@ -132,8 +132,9 @@ def pa_plan(context_lens: torch.Tensor, num_kv_heads: int, *, cu_count: int, bud
             work_info: Optional[torch.Tensor] = None, reduce_info: Optional[torch.Tensor] = None,
             num_work: Optional[torch.Tensor] = None, stream=None
             ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """Plan on the device.  Returns (work_info [capacity, 4], reduce_info [B, 2], num_work [1]),
-    all int32 on the device of context_lens; passed-in buffers are refilled in place."""
+    """Plan on the device.  Returns (work_info [capacity, 4], reduce_info [B, 2], num_work [2] =
+    (used slots, tiles of the largest slot)), all int32 on the device of context_lens; passed-in
+    buffers are refilled in place."""
     _need(context_lens, "context_lens", torch.int32)
     dev = context_lens.device
     B = int(context_lens.shape[0])
@@ -144,12 +145,12 @@ def pa_plan(context_lens: torch.Tensor, num_kv_heads: int, *, cu_count: int, bud
     if reduce_info is None:
         reduce_info = torch.empty((B, 2), dtype=torch.int32, device=dev)
     if num_work is None:
-        num_work = torch.empty((1,), dtype=torch.int32, device=dev)
+        num_work = torch.empty((2,), dtype=torch.int32, device=dev)
     _need(work_info, "work_info", torch.int32, dev)
     _need(reduce_info, "reduce_info", torch.int32, dev)
     _need(num_work, "num_work", torch.int32, dev)
-    if work_info.numel() < 4 * capacity or reduce_info.numel() < 2 * B:
-        raise ValueError("plan buffers smaller than capacity / num_seqs")
+    if work_info.numel() < 4 * capacity or reduce_info.numel() < 2 * B or num_work.numel() < 2:
+        raise ValueError("plan buffers smaller than capacity / num_seqs / 2")
     _check(load().pa_plan(_ptr(context_lens), B, num_kv_heads, cu_count, budget_mult, max_partitions,
                           tile_tokens, capacity, _ptr(work_info), _ptr(reduce_info), _ptr(num_work),
                           _stream(stream)), "pa_plan")

@@ -54,7 +54,8 @@ pa_status pa_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_
     if (num_seqs < 0 || tile_tokens < 1 || capacity < 0) return PA_INVALID_ARG;
     if (!num_work || (num_seqs > 0 && (!context_lens || !reduce_info)) || (capacity > 0 && !work_info))
         return PA_INVALID_ARG;
-    if ((work_info && !aligned(work_info, 16)) || (reduce_info && !aligned(reduce_info, 8)))
+    if ((work_info && !aligned(work_info, 16)) || (reduce_info && !aligned(reduce_info, 8)) ||
+        !aligned(num_work, 8))
         return PA_INVALID_ARG;
     if (num_seqs > PA_MAX_SEQS) return PA_UNSUPPORTED;
     int32_t cap = 0;
@@ -99,7 +100,8 @@ pa_status pa_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t n
         if ((long long)num_rows * num_q_heads > (long long)INT_MAX) return PA_UNSUPPORTED;
     }
     if ((q && !aligned(q, 16)) || (k_cache && !aligned(k_cache, 16)) || (v_cache && !aligned(v_cache, 16)) ||
-        (work_info && !aligned(work_info, 16)) || (workspace && !aligned(workspace, 256)))
+        (work_info && !aligned(work_info, 16)) || (workspace && !aligned(workspace, 256)) ||
+        (num_work && !aligned(num_work, 8)))
         return PA_INVALID_ARG;
     const size_t need = pa_workspace_bytes(capacity, max_q_len, num_q_heads, head_dim);
     if (capacity > 0 && (need == 0 || workspace_bytes < need)) return PA_CAPACITY;

@@ -206,7 +206,8 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
     // request's length, cumulative query lengths and (speculatively, over the plan's tile range)
     // this wave's page ids; then queries and K/V. ----
     const int4 wk = a.work_info[slot];
-    const int used = *a.num_work;
+    const int2 nwk = *reinterpret_cast<const int2*>(a.num_work);   // (used slots, largest slot in tiles)
+    const int used = nwk.x;
     const int b = wk.x;
     if (slot >= used || b < 0 || b >= a.num_seqs) return;
     const int* bt_row = a.block_tables + static_cast<size_t>(b) * a.max_blocks;
@@ -216,14 +217,17 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
                                              static_cast<long long>(plan_lo)));
     const int plan_chunks = (plan_hi - plan_lo + 15) >> 4;
 
-    // Chunks are dealt to waves in whole plan tiles: wave w owns tiles w, w + NW, ... of the slot and
-    // its k-th chunk is chunk_of(k).  The planner sizes slots in tiles, so a slot of up to NW tiles
-    // runs one streaming wave per tile: every wave carries the same load whatever the slot size,
-    // and big slots draw proportionally more bandwidth instead of finishing last.
+    // Chunks are dealt to waves in units of `unit` consecutive chunks: wave w owns units w, w + NW, ...
+    // of the slot and its k-th chunk is chunk_of(k).  The unit is the largest slot of the plan split
+    // over the NW waves, so that slot's waves and every other wave with a full unit carry the same
+    // load and finish together, while a smaller slot runs fewer streaming waves and leaves more of the
+    // bandwidth to the big ones.  Any unit >= 1 covers every chunk of every slot exactly once.
     const int cpt = a.tile_tokens >> 4;          // 16-key chunks per tile
+    const int unit = static_cast<int>(min(max(1LL, (static_cast<long long>(max(nwk.y, 1)) * cpt + C::NW - 1) /
+                                                       C::NW), 1LL << 30));
     auto chunk_of = [&](int k) -> int {
-        const int j = k / cpt;
-        return (wave + C::NW * j) * cpt + (k - j * cpt);
+        const int j = k / unit;
+        return (wave + C::NW * j) * unit + (k - j * unit);
     };
 
     // Page ids of this wave's chunks, one per lane (lane = chunk ordinal - base), refreshed every 64.
@@ -311,11 +315,11 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
     uint8_t* klds = lds + wave * C::WAVE_LDS;
     uint8_t* vlds = klds + 16 * C::LRB;
 
-    // this wave's number of chunks: its full tiles, plus the ragged last tile if it owns it
-    const int full_tiles = nchunks / cpt;
-    const int rem = nchunks - full_tiles * cpt;
-    int my_chunks = (full_tiles > wave ? (full_tiles - wave + C::NW - 1) / C::NW : 0) * cpt;
-    if (rem > 0 && full_tiles % C::NW == wave) my_chunks += rem;
+    // this wave's number of chunks: its full units, plus the ragged last unit if it owns it
+    const int full_units = nchunks / unit;
+    const int rem = nchunks - full_units * unit;
+    int my_chunks = (full_units > wave ? (full_units - wave + C::NW - 1) / C::NW : 0) * unit;
+    if (rem > 0 && full_units % C::NW == wave) my_chunks += rem;
 
     auto chunk_block = [&](int k) -> int {
         const int base = k & ~63;

@@ -46,6 +46,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     __shared__ long long red_total[kPlanWaves];
     __shared__ int red_count[kPlanWaves];
     __shared__ int scan_carry[kPlanWaves];
+    __shared__ int largest_of_wave[kPlanWaves];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -106,11 +107,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     __syncthreads();
 
     const int used = first[num_seqs];
-    if (tid == 0) *num_work = used;
     for (int b = tid; b < num_seqs; b += kPlanThreads)
         reduce_info[b] = make_int2(first[b], first[b + 1] - first[b]);
 
     // --- one thread per slot ---
+    int largest = 0;
     for (int s = tid; s < capacity; s += kPlanThreads) {
         if (s < used) {
             // last request whose first slot is <= s (it has at least one partition because s < used)
@@ -135,9 +136,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
                 te = static_cast<int>((static_cast<long long>(j + 1) * tiles) / parts);
             }
             work_info[s] = make_int4(b, tb, te, len);
+            largest = max(largest, te - tb);
         } else {
             work_info[s] = make_int4(-1, 0, 0, 0);
         }
+    }
+    for (int o = 32; o >= 1; o >>= 1) largest = max(largest, __shfl_xor(largest, o, 64));
+    if (lane == 0) largest_of_wave[wave] = largest;
+    __syncthreads();
+    if (tid == 0) {
+        for (int w = 0; w < kPlanWaves; ++w) largest = max(largest, largest_of_wave[w]);
+        *reinterpret_cast<int2*>(num_work) = make_int2(used, largest);
     }
 }
 

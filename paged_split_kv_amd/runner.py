@@ -36,7 +36,7 @@ class DecodeStep:
                                            p.max_partitions)
         self.work_info = torch.empty((self.capacity, 4), dtype=torch.int32, device=self.device)
         self.reduce_info = torch.empty((num_seqs, 2), dtype=torch.int32, device=self.device)
-        self.num_work = torch.empty((1,), dtype=torch.int32, device=self.device)
+        self.num_work = torch.empty((2,), dtype=torch.int32, device=self.device)
         nbytes = B.pa_workspace_bytes(self.capacity, max_q_len, num_q_heads, head_dim)
         # zero-filled once: the fused merge's arrival counters start (and are left) at zero
         self.workspace = torch.zeros((max(nbytes, 256),), dtype=torch.uint8, device=self.device)

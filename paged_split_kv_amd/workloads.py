@@ -296,6 +296,27 @@ CONFIG_NAMES: List[str] = ["tiny_fp32", "skewed_bf16", "long_bf16", "verify_bf16
 
 
 # ----------------------------------------------------------------------------------------------
+# sparse / top-k layers: every request reads a fixed-size selection of pages, so lengths are
+# near-uniform (ROCm/ATOM PR #2366 section 3: sparse sites read a fixed top-k window; PR #2514
+# Design: sparse plans use a partition cap of 8)
+# ----------------------------------------------------------------------------------------------
+
+SPARSE_TOPK_TOKENS = 2048     # selected tokens per request
+SPARSE_LOCAL_TOKENS = 256     # plus up to this many local (most recent) tokens
+
+
+def sparse_lengths(num_steps: int, batch: int, seed: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    return SPARSE_TOPK_TOKENS + rng.integers(1, SPARSE_LOCAL_TOKENS + 1, size=(num_steps, batch))
+
+
+def make_sparse_case(device="cpu", batch: int = 16, seed: int = 9) -> Case:
+    ctx = sparse_lengths(1, batch, seed)[0]
+    return build_case("sparse_topk", ctx.tolist(), num_q_heads=16, num_kv_heads=2, head_dim=128,
+                      block_size=16, kv_dtype="bf16", q_dtype="bf16", seed=seed, device=device)
+
+
+# ----------------------------------------------------------------------------------------------
 # the skewed-batch pool used for timing: one large page pool, fresh random pages per step
 # ----------------------------------------------------------------------------------------------
 
@@ -313,10 +334,13 @@ class StepPool:
 
 def skewed_pool(device, pool_bytes: int = 4 << 30, num_steps: int = 128, seed: int = 7,
                 num_q_heads: int = 16, num_kv_heads: int = 2, head_dim: int = 128,
-                block_size: int = 16) -> StepPool:
+                block_size: int = 16, steps: Optional[np.ndarray] = None) -> StepPool:
     """K/V page pool much larger than the 256 MB last-level cache, with each step's pages drawn
-    at random from it, so consecutive steps share almost no pages."""
-    steps = skewed_step_set(num_steps=num_steps)
+    at random from it, so consecutive steps share almost no pages.  ``steps`` (int [num_steps, B])
+    replaces the skewed step set."""
+    if steps is None:
+        steps = skewed_step_set(num_steps=num_steps)
+    num_steps = steps.shape[0]
     elem = 2
     page_bytes = 2 * num_kv_heads * block_size * head_dim * elem
     num_blocks = pool_bytes // page_bytes

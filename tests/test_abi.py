@@ -80,6 +80,7 @@ def test_plan_argument_checks():
     assert _plan_status(ctx=None) == B.PA_INVALID_ARG
     assert _plan_status(work=None) == B.PA_INVALID_ARG
     assert _plan_status(work=ctypes.c_void_p(8)) == B.PA_INVALID_ARG       # misaligned int4 entries
+    assert _plan_status(nw=ctypes.c_void_p(260)) == B.PA_INVALID_ARG       # num_work pair misaligned
     assert _plan_status(B=B.PA_MAX_SEQS + 1, cap=1 << 22) == B.PA_UNSUPPORTED
 
 

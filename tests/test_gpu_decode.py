@@ -120,6 +120,15 @@ def test_skewed_steps(which):
     assert_close(to_f64(out), oracle_direct(case), "bf16", f"skewed {which}")
 
 
+@pytest.mark.parametrize("fused", [True, False], ids=["fused_merge", "separate_merge"])
+def test_sparse_topk_workload_with_cap_8(fused):
+    announce(f"sparse top-k, cap 8, fused={fused}")
+    case = W.make_sparse_case(device=DEV)
+    out, step = _run(case, P=8, T=256, cu_count=256, fused=fused)
+    assert (step.reduce_info[:, 1] <= 8).all()
+    assert_close(to_f64(out), oracle_direct(case), "bf16", "sparse top-k")
+
+
 def test_full_size_separate_merge_fp8():
     announce("full fp8_kv, separate merge")
     case = W.make_config("fp8_kv", device=DEV)
@@ -172,7 +181,7 @@ def test_slot_order_does_not_change_the_output():
     ref = ref.clone()
     work = step.work_info.cpu().numpy()
     red = step.reduce_info.cpu().numpy()
-    nw = int(step.num_work.item())
+    nw = int(step.num_work[0].item())
     # reverse the order of the requests' slot blocks; each request keeps its own slots in order
     new_work = np.tile(np.array([-1, 0, 0, 0], np.int32), (work.shape[0], 1))
     new_red = red.copy()

@@ -18,7 +18,7 @@ def _gpu_plan(ctx, hkv, cu, mult=2, P=256, T=256, capacity=None, poison=True):
     cap = B.pa_plan_capacity(len(ctx), hkv, cu, mult, P) if capacity is None else capacity
     work = torch.empty((cap, 4), dtype=torch.int32, device=DEV)
     red = torch.empty((len(ctx), 2), dtype=torch.int32, device=DEV)
-    nw = torch.empty((1,), dtype=torch.int32, device=DEV)
+    nw = torch.empty((2,), dtype=torch.int32, device=DEV)
     if poison:
         work.fill_(0x5A5A5A5A)
         red.fill_(-7)
@@ -26,13 +26,13 @@ def _gpu_plan(ctx, hkv, cu, mult=2, P=256, T=256, capacity=None, poison=True):
     B.pa_plan(c, hkv, cu_count=cu, budget_mult=mult, max_partitions=P, tile_tokens=T, capacity=cap,
               work_info=work, reduce_info=red, num_work=nw)
     torch.cuda.synchronize()
-    return work.cpu().numpy(), red.cpu().numpy(), int(nw.item())
+    return work.cpu().numpy(), red.cpu().numpy(), nw.cpu().numpy().tolist()
 
 
 def _compare(ctx, hkv, cu, mult=2, P=256, T=256, capacity=None):
     gw, gr, gn = _gpu_plan(ctx, hkv, cu, mult, P, T, capacity)
-    ow, orr, on = oracle.plan(np.asarray(ctx), hkv, cu, mult, P, T, capacity)
-    assert gn == on
+    ow, orr, on, olarge = oracle.plan(np.asarray(ctx), hkv, cu, mult, P, T, capacity, with_largest=True)
+    assert gn == [on, olarge]
     assert np.array_equal(gr, orr)
     assert np.array_equal(gw, ow)
 
@@ -49,6 +49,12 @@ def test_plan_bit_exact_on_the_five_workloads(name):
            "fp8_kv": W.fp8_context_lens().tolist()}[name]
     hkv = {"tiny_fp32": 1, "long_bf16": 2, "verify_bf16": 1, "fp8_kv": 2}[name]
     _compare(ctx, hkv, 256)
+
+
+def test_plan_bit_exact_on_sparse_steps_with_cap_8():
+    steps = W.sparse_lengths(64, 16, seed=11)
+    for idx in range(0, 64, 5):
+        _compare(steps[idx], 2, 256, P=8)
 
 
 def test_plan_uses_device_cu_count():
@@ -86,7 +92,7 @@ def test_replan_in_place_leaves_nothing_stale():
     B.pa_plan(c2, 1, cu_count=256, work_info=work, reduce_info=red, num_work=nw)
     torch.cuda.synchronize()
     ow, orr, on = oracle.plan([10, 0, 20, 30], 1, 256)
-    assert int(nw.item()) == on
+    assert int(nw[0].item()) == on
     assert np.array_equal(work.cpu().numpy(), ow) and np.array_equal(red.cpu().numpy(), orr)
 
 

@@ -121,6 +121,18 @@ def _brute_parts(ctx, C, P, T):
     return out
 
 
+def test_largest_slot_is_the_largest_tile_range():
+    rng = np.random.default_rng(77)
+    for _ in range(30):
+        ctx = rng.integers(0, 200000, size=int(rng.integers(1, 300)))
+        work, red, nw, largest = oracle.plan(ctx, 2, 256, 2, 256, 256, with_largest=True)
+        brute = 0
+        for w in work[:nw]:
+            brute = max(brute, int(w[2] - w[1]))
+        assert largest == brute
+    assert oracle.plan([0, 0], 1, with_largest=True)[3] == 0
+
+
 def _check_invariants(ctx, Hkv, cu, mult, P, T, work, red, nw):
     B = len(ctx)
     C = min(B * P, max(B, -(-(mult * cu) // Hkv)))
