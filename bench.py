@@ -5,12 +5,15 @@
 Workload: the skewed 32-request bf16 decode (Hq 16 / Hkv 2, D 128, pages of 16 tokens).  128 decode
 steps whose in-batch max/min context ratio follows the agentic trace (p50 ~2.5, p90 ~21); every step
 draws its pages at random from a 4 GiB K/V pool, so the 256 MB last-level cache cannot hold a step's
-data across steps.  One timed step = pa_plan + pa_decode + pa_merge over one batch, inputs resident in
-HBM.  value = KV bytes read / step time (GB/s).  The variant with the merge inside the decode launch
-is timed too and reported beside it.
+data across steps.  One timed step = one pa_attention call over one batch (plan, decode and merge; the
+decode launch plans in place, so two launches), inputs resident in HBM.  value = KV bytes read / step
+time (GB/s).  The three-call form (pa_plan + pa_decode + pa_merge) and the form with the merge inside
+the decode launch are timed too and reported beside it.
 
 The roofline object is for the decode kernel: algorithmic bytes (sum of context lengths x Hkv x 2 x D
-x 2 bytes per launch) over its average launch duration, measured with HIP events on the launch stream.
+x 2 bytes per launch, averaged over the batches) over its average launch duration, measured with HIP
+events on the launch stream around K pa_decode launches issued back to back over the batches, each
+with its own plan made beforehand.
 """
 from __future__ import annotations
 
@@ -142,69 +145,103 @@ def main():
     kv_bytes = pool.steps.sum(axis=1) * Hkv * 2 * D * 2                 # per step
     stream = torch.cuda.current_stream()
 
-    def run(i, ev=None, fused=False):
-        """One step: pa_plan, pa_decode writing partial states, then pa_merge (fused=True: the
-        merge runs inside the pa_decode launch instead)."""
+    def run(i, ev=None, mode="attention"):
+        """One step over batch i.  attention: one pa_attention call (the decode plans in place, then
+        the merge: two launches).  three: pa_plan, pa_decode writing partial states, pa_merge.
+        fused: pa_plan, then pa_decode with the merge inside its launch."""
         i %= nsteps
         ctx = pool.context_lens[i]
+        if mode == "attention":
+            step.attention(pool.q[i], pool.k_cache, pool.v_cache, "bf16", pool.block_tables[i], ctx,
+                           scale=pool.scale)
+            return
         if ev is not None:
             ev[0].record(stream)
         step.plan(ctx)
         if ev is not None:
             ev[1].record(stream)
         step.decode(pool.q[i], pool.k_cache, pool.v_cache, "bf16", pool.block_tables[i], ctx,
-                    scale=pool.scale, merge=fused)
+                    scale=pool.scale, merge=mode == "fused")
         if ev is not None:
             ev[2].record(stream)
-        if not fused:
+        if mode == "three":
             step.merge()
         if ev is not None:
             ev[3].record(stream)
 
+    def timed(mode, warm=8):
+        for i in range(warm):
+            run(i, mode=mode)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(K):
+            run(i, mode=mode)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    K = args.steps
     for i in range(args.warmup):
         run(i)
     torch.cuda.synchronize()
 
-    K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    # the timed region: K steps of the whole path, synchronised on both sides
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
     for i in range(K):
-        run(i, evs[i])
+        run(i)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(end)
+    plain_ms = start.elapsed_time(end)
+    bytes_done = float(sum(kv_bytes[i % nsteps] for i in range(K)))
+
+    # per-kernel durations: the three-call form of the same steps with events around each launch
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    for i in range(8):
+        run(i, mode="three")
+    torch.cuda.synchronize()
+    for i in range(K):
+        run(i, evs[i], mode="three")
+    torch.cuda.synchronize()
     plan_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     mrg_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
     step_ms = plan_ms + dec_ms + mrg_ms
-    bytes_done = float(sum(kv_bytes[i % nsteps] for i in range(K)))
 
-    # the same steps without per-kernel events in between (only the outer events)
-    s2 = torch.cuda.Event(enable_timing=True)
-    e2 = torch.cuda.Event(enable_timing=True)
-    s2.record(stream)
-    for i in range(K):
-        run(i)
-    e2.record(stream)
+    # the decode kernel alone: launches back to back over the batches, each with its own plan made
+    # beforehand, so consecutive launches read different pages and no event sits between them
+    plans = []
+    for i in range(nsteps):
+        w, r, n = B.pa_plan(pool.context_lens[i], Hkv, cu_count=cu_count, max_partitions=max_parts,
+                            capacity=step.capacity)
+        plans.append((w, n))
     torch.cuda.synchronize()
-    plain_ms = s2.elapsed_time(e2)
 
-    # the same steps with the merge inside the decode launch, for comparison
-    s3 = torch.cuda.Event(enable_timing=True)
-    e3 = torch.cuda.Event(enable_timing=True)
+    def decode_only(i):
+        i %= nsteps
+        B.pa_decode(pool.q[i], pool.k_cache, pool.v_cache, "bf16", pool.block_tables[i], pool.context_lens[i],
+                    plans[i][0], plans[i][1], step.workspace, scale=pool.scale)
+
     for i in range(8):
-        run(i, fused=True)
-    s3.record(stream)
-    for i in range(K):
-        run(i, fused=True)
-    e3.record(stream)
+        decode_only(i)
+    da = torch.cuda.Event(enable_timing=True)
+    db = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    fused_ms = s3.elapsed_time(e3)
+    da.record(stream)
+    for i in range(K):
+        decode_only(i)
+    db.record(stream)
+    torch.cuda.synchronize()
+    decode_ms = da.elapsed_time(db) / K
+
+    three_ms = timed("three")          # pa_plan + pa_decode + pa_merge, no events in between
+    fused_ms = timed("fused")          # pa_plan + pa_decode with the merge in its launch
 
     graph = None
     if args.graph:
@@ -232,7 +269,7 @@ def main():
 
     us_step = plain_ms * 1e3 / K
     gbps = bytes_done / (plain_ms * 1e-3) / 1e9
-    dec_gbps = bytes_done / (dec_ms.sum() * 1e-3) / 1e9
+    dec_gbps = float(kv_bytes.mean()) / (decode_ms * 1e-3) / 1e9
     traffic = counter_traffic()
     if args.workload == "skewed":
         metric = METRIC
@@ -261,16 +298,20 @@ def main():
                                "tile_tokens": 256}},
         "us_per_step": round(us_step, 2),
         "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 1),
-        "us_per_step_p50": round(float(np.median(step_ms)) * 1e3, 2),
-        "us_per_step_p90": round(float(np.quantile(step_ms, 0.9)) * 1e3, 2),
-        "kernel_us": {"pa_plan": round(float(plan_ms.mean()) * 1e3, 2),
-                      "pa_decode": round(float(dec_ms.mean()) * 1e3, 2),
-                      "pa_merge": round(float(mrg_ms.mean()) * 1e3, 2)},
+        "step": "pa_attention: the decode launch plans in place, then pa_merge",
+        "three_call_us_per_step": round(three_ms * 1e3 / K, 2),
         "merge_in_decode_launch_us_per_step": round(fused_ms * 1e3 / K, 2),
+        "evented_three_call_us_p50": round(float(np.median(step_ms)) * 1e3, 2),
+        "evented_three_call_us_p90": round(float(np.quantile(step_ms, 0.9)) * 1e3, 2),
+        "kernel_us": {"pa_decode_back_to_back": round(decode_ms * 1e3, 2),
+                      "evented": {"pa_plan": round(float(plan_ms.mean()) * 1e3, 2),
+                                  "pa_decode": round(float(dec_ms.mean()) * 1e3, 2),
+                                  "pa_merge": round(float(mrg_ms.mean()) * 1e3, 2)}},
         "timed_wall_s": round(wall, 3),
         "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic if args.workload == "skewed" else None, "kernel": "pa_decode",
+                     "duration_us": round(decode_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": round(float(kv_bytes.mean()), 1)},
         "hip_graph": graph,
         "cpu_baseline": None,

@@ -15,6 +15,9 @@
  *              cumulative query length and rows with no visible key are written as exact zeros
  *              (same vllm-rdna page, Change 1; ATOM #2366 review, "Claims checked and not upheld").
  *
+ * pa_attention runs the same three steps with one launch fewer: the decode plans in place (for
+ * batches of up to PA_INLINE_PLAN_SEQS requests) and stores the plan it used.
+ *
  * Conventions shared by every entry point:
  *   - All array arguments are DEVICE pointers (memory of the current HIP device), except where a
  *     parameter says host.  The caller owns all memory; the library allocates nothing, keeps no
@@ -22,6 +25,8 @@
  *     and may be captured in a HIP graph.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *   - Integer arrays are int32, contiguous.  Floating arrays are contiguous, innermost dimension last.
+ *   - Alignment: q, k_cache, v_cache, out and work_info 16 bytes; reduce_info and num_work 8 bytes;
+ *     workspace 256 bytes (PA_INVALID_ARG otherwise).
  *   - Storage types: PA_F32 (IEEE binary32), PA_BF16 (bfloat16), PA_FP8_E4M3 (OCP E4M3 "fn" codes,
  *     dequantised value = decoded code x per-tensor scale).
  *   - Host-side argument checks run before any launch; a failing check returns a nonzero status and
@@ -72,6 +77,7 @@ typedef enum {
 /* Limits of this implementation (checked on the host). */
 #define PA_MAX_SEQS 8192           /* pa_plan keeps per-request prefix sums in LDS */
 #define PA_MAX_GROUP_ROWS 64       /* (num_q_heads / num_kv_heads) x max_q_len */
+#define PA_INLINE_PLAN_SEQS 256    /* largest batch pa_attention plans inside the decode launch */
 
 /*
  * Number of plan slots a batch needs:
@@ -168,6 +174,29 @@ pa_status pa_merge(int32_t num_rows, int32_t num_q_heads, int32_t head_dim, int3
                    const int32_t* cu_query_lens, int32_t max_q_len, const int32_t* reduce_info,
                    int32_t capacity, const void* workspace, size_t workspace_bytes, void* out,
                    pa_dtype out_dtype, void* stream);
+
+/*
+ * The whole step -- plan, decode, merge -- on one stream, with results identical to pa_plan followed
+ * by pa_decode (out = NULL) and pa_merge with the same arguments: work_info, reduce_info and num_work
+ * receive the plan bit for bit as pa_plan writes it, the workspace the same partial states, and out
+ * the same rows.  Arguments are those of the three calls (cu_count, budget_mult, max_partitions as
+ * for pa_plan; capacity as for pa_plan and pa_decode); the plan buffers are outputs here.
+ * With num_seqs <= PA_INLINE_PLAN_SEQS and a bf16 or fp8 cache, the decode launch evaluates the
+ * planner's rule itself (every workgroup over all requests, one request per thread) and stores the
+ * plan, so the step is two launches (decode, merge); otherwise it is the three launches.  The
+ * single-launch merge of pa_decode is not used here, so the workspace needs no zero fill.
+ * Errors: the union of pa_plan's, pa_decode's and pa_merge's checks, before any launch.
+ */
+pa_status pa_attention(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t num_q_heads,
+                       int32_t head_dim, const void* k_cache, const void* v_cache, pa_dtype kv_dtype,
+                       int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* context_lens, int32_t num_seqs, const int32_t* cu_query_lens,
+                       int32_t max_q_len, float scale, float k_scale, float v_scale,
+                       int32_t cu_count, int32_t budget_mult, int32_t max_partitions,
+                       int32_t tile_tokens, int32_t capacity, int32_t* work_info,
+                       int32_t* reduce_info, int32_t* num_work, void* workspace,
+                       size_t workspace_bytes, void* out, pa_dtype out_dtype, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* pa_status_string(pa_status status);

@@ -30,27 +30,14 @@ pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_HIP_ERROR
 
 }  // namespace
 
-extern "C" {
+extern "C" size_t pa_workspace_bytes(int32_t capacity, int32_t max_q_len, int32_t num_q_heads, int32_t head_dim);
 
-pa_status pa_plan_capacity(int32_t num_seqs, int32_t num_kv_heads, int32_t cu_count,
-                           int32_t budget_mult, int32_t max_partitions, int32_t* capacity_out) {
-    if (!capacity_out) return PA_INVALID_ARG;
-    return capacity_formula(num_seqs, num_kv_heads, cu_count, budget_mult, max_partitions, capacity_out);
-}
+namespace {
 
-size_t pa_workspace_bytes(int32_t capacity, int32_t max_q_len, int32_t num_q_heads, int32_t head_dim) {
-    if (capacity < 0 || max_q_len < 1 || num_q_heads < 1 || head_dim < 1) return 0;
-    const unsigned long long states = (unsigned long long)capacity * max_q_len * num_q_heads;
-    if (states > (1ull << 40)) return 0;
-    return pa::workspace_acc_bytes(capacity, max_q_len, num_q_heads, head_dim) +
-           pa::workspace_ml_bytes(capacity, max_q_len, num_q_heads) +
-           pa::workspace_counter_bytes(capacity, num_q_heads);
-}
-
-pa_status pa_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
-                  int32_t cu_count, int32_t budget_mult, int32_t max_partitions,
-                  int32_t tile_tokens, int32_t capacity, int32_t* work_info, int32_t* reduce_info,
-                  int32_t* num_work, void* stream) {
+pa_status check_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
+                     int32_t cu_count, int32_t budget_mult, int32_t max_partitions, int32_t tile_tokens,
+                     int32_t capacity, const int32_t* work_info, const int32_t* reduce_info,
+                     const int32_t* num_work, int32_t* cap) {
     if (num_seqs < 0 || tile_tokens < 1 || capacity < 0) return PA_INVALID_ARG;
     if (!num_work || (num_seqs > 0 && (!context_lens || !reduce_info)) || (capacity > 0 && !work_info))
         return PA_INVALID_ARG;
@@ -58,23 +45,23 @@ pa_status pa_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_
         !aligned(num_work, 8))
         return PA_INVALID_ARG;
     if (num_seqs > PA_MAX_SEQS) return PA_UNSUPPORTED;
-    int32_t cap = 0;
-    pa_status st = capacity_formula(num_seqs, num_kv_heads, cu_count, budget_mult, max_partitions, &cap);
+    const pa_status st = capacity_formula(num_seqs, num_kv_heads, cu_count, budget_mult, max_partitions, cap);
     if (st != PA_OK) return st;
-    if (capacity < cap) return PA_CAPACITY;
-    return from_hip(pa::launch_plan(context_lens, num_seqs, cap, capacity, max_partitions, tile_tokens,
-                                    work_info, reduce_info, num_work, pa::as_stream(stream)));
+    if (capacity < *cap) return PA_CAPACITY;
+    return PA_OK;
 }
 
-pa_status pa_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t num_q_heads,
-                    int32_t head_dim, const void* k_cache, const void* v_cache, pa_dtype kv_dtype,
-                    int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
-                    const int32_t* block_tables, int32_t max_blocks_per_seq,
-                    const int32_t* context_lens, int32_t num_seqs, const int32_t* cu_query_lens,
-                    int32_t max_q_len, float scale, float k_scale, float v_scale,
-                    const int32_t* work_info, const int32_t* reduce_info, const int32_t* num_work,
-                    int32_t capacity, int32_t tile_tokens, void* workspace, size_t workspace_bytes,
-                    void* out, pa_dtype out_dtype, void* stream) {
+// Checks of pa_decode; on success fills the kernel arguments and says whether there is nothing to
+// decode (no slot or no request).
+pa_status prepare_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t num_q_heads,
+                         int32_t head_dim, const void* k_cache, const void* v_cache, pa_dtype kv_dtype,
+                         int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t num_seqs, const int32_t* cu_query_lens,
+                         int32_t max_q_len, float scale, float k_scale, float v_scale,
+                         const int32_t* work_info, const int32_t* reduce_info, const int32_t* num_work,
+                         int32_t capacity, int32_t tile_tokens, void* workspace, size_t workspace_bytes,
+                         void* out, pa_dtype out_dtype, pa::DecodeArgs* args, bool* nothing) {
     if (num_rows < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_blocks < 0 || num_seqs < 0 ||
         max_blocks_per_seq < 0 || max_q_len < 1 || capacity < 0 || tile_tokens < 1 || head_dim < 1 ||
         block_size < 1)
@@ -105,14 +92,10 @@ pa_status pa_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t n
         return PA_INVALID_ARG;
     const size_t need = pa_workspace_bytes(capacity, max_q_len, num_q_heads, head_dim);
     if (capacity > 0 && (need == 0 || workspace_bytes < need)) return PA_CAPACITY;
-    if (capacity == 0 || num_seqs == 0) {
-        if (!out || num_rows == 0) return PA_OK;
-        // nothing to decode: the merge's contract still writes every row (all zero here)
-        return pa_merge(num_rows, num_q_heads, head_dim, 0, nullptr, 1, nullptr, 0, nullptr, 0, out,
-                        out_dtype, stream);
-    }
+    *nothing = capacity == 0 || num_seqs == 0;
 
-    pa::DecodeArgs a;
+    pa::DecodeArgs& a = *args;
+    a = pa::DecodeArgs{};
     a.q = q;
     a.k_cache = static_cast<const uint8_t*>(k_cache);
     a.v_cache = static_cast<const uint8_t*>(v_cache);
@@ -124,8 +107,9 @@ pa_status pa_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t n
     a.ws_acc = static_cast<float*>(workspace);
     const size_t acc_bytes = pa::workspace_acc_bytes(capacity, max_q_len, num_q_heads, head_dim);
     const size_t ml_bytes = pa::workspace_ml_bytes(capacity, max_q_len, num_q_heads);
-    a.ws_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + acc_bytes);
-    a.ws_counters = reinterpret_cast<int*>(static_cast<uint8_t*>(workspace) + acc_bytes + ml_bytes);
+    a.ws_ml = workspace ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + acc_bytes) : nullptr;
+    a.ws_counters = workspace ? reinterpret_cast<int*>(static_cast<uint8_t*>(workspace) + acc_bytes + ml_bytes)
+                              : nullptr;
     a.reduce_info = reinterpret_cast<const int2*>(reduce_info);
     a.out = out;
     a.out_bf16 = out_dtype == PA_BF16 ? 1 : 0;
@@ -142,13 +126,13 @@ pa_status pa_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t n
     a.tile_tokens = tile_tokens;
     a.score_scale_log2 = scale * k_scale * pa::kLog2e;
     a.v_scale = v_scale;
-    return from_hip(pa::launch_decode(a, head_dim, kv_dtype, q_dtype == PA_F32, pa::as_stream(stream)));
+    return PA_OK;
 }
 
-pa_status pa_merge(int32_t num_rows, int32_t num_q_heads, int32_t head_dim, int32_t num_seqs,
-                   const int32_t* cu_query_lens, int32_t max_q_len, const int32_t* reduce_info,
-                   int32_t capacity, const void* workspace, size_t workspace_bytes, void* out,
-                   pa_dtype out_dtype, void* stream) {
+pa_status prepare_merge(int32_t num_rows, int32_t num_q_heads, int32_t head_dim, int32_t num_seqs,
+                        const int32_t* cu_query_lens, int32_t max_q_len, const int32_t* reduce_info,
+                        int32_t capacity, const void* workspace, size_t workspace_bytes, void* out,
+                        pa_dtype out_dtype, pa::MergeArgs* args) {
     if (num_rows < 0 || num_q_heads < 1 || num_seqs < 0 || max_q_len < 1 || capacity < 0)
         return PA_INVALID_ARG;
     if (out_dtype != PA_F32 && out_dtype != PA_BF16) return PA_INVALID_ARG;
@@ -156,14 +140,14 @@ pa_status pa_merge(int32_t num_rows, int32_t num_q_heads, int32_t head_dim, int3
     if (!supported_head_dim(head_dim)) return PA_UNSUPPORTED;
     if (num_rows > 0 && !out) return PA_INVALID_ARG;
     if (num_seqs > 0 && (!reduce_info || (capacity > 0 && !workspace))) return PA_INVALID_ARG;
-    if ((reduce_info && !aligned(reduce_info, 8)) || (workspace && !aligned(workspace, 256)))
+    if ((reduce_info && !aligned(reduce_info, 8)) || (workspace && !aligned(workspace, 256)) ||
+        (out && !aligned(out, 16)))
         return PA_INVALID_ARG;
     const size_t need = pa_workspace_bytes(capacity, max_q_len, num_q_heads, head_dim);
     if (capacity > 0 && (need == 0 || workspace_bytes < need)) return PA_CAPACITY;
     if ((long long)num_rows * num_q_heads > (long long)INT_MAX) return PA_UNSUPPORTED;
-    if (num_rows == 0) return PA_OK;
 
-    pa::MergeArgs a;
+    pa::MergeArgs& a = *args;
     a.cu = cu_query_lens;
     a.reduce_info = reinterpret_cast<const int2*>(reduce_info);
     a.ws_acc = static_cast<const float*>(workspace);
@@ -177,7 +161,130 @@ pa_status pa_merge(int32_t num_rows, int32_t num_q_heads, int32_t head_dim, int3
     a.num_seqs = (capacity > 0) ? num_seqs : 0;   // without slots every row is zero
     a.max_q_len = max_q_len;
     a.capacity = capacity;
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_plan_capacity(int32_t num_seqs, int32_t num_kv_heads, int32_t cu_count,
+                           int32_t budget_mult, int32_t max_partitions, int32_t* capacity_out) {
+    if (!capacity_out) return PA_INVALID_ARG;
+    return capacity_formula(num_seqs, num_kv_heads, cu_count, budget_mult, max_partitions, capacity_out);
+}
+
+size_t pa_workspace_bytes(int32_t capacity, int32_t max_q_len, int32_t num_q_heads, int32_t head_dim) {
+    if (capacity < 0 || max_q_len < 1 || num_q_heads < 1 || head_dim < 1) return 0;
+    const unsigned long long states = (unsigned long long)capacity * max_q_len * num_q_heads;
+    if (states > (1ull << 40)) return 0;
+    return pa::workspace_acc_bytes(capacity, max_q_len, num_q_heads, head_dim) +
+           pa::workspace_ml_bytes(capacity, max_q_len, num_q_heads) +
+           pa::workspace_counter_bytes(capacity, num_q_heads);
+}
+
+pa_status pa_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
+                  int32_t cu_count, int32_t budget_mult, int32_t max_partitions,
+                  int32_t tile_tokens, int32_t capacity, int32_t* work_info, int32_t* reduce_info,
+                  int32_t* num_work, void* stream) {
+    int32_t cap = 0;
+    const pa_status st = check_plan(context_lens, num_seqs, num_kv_heads, cu_count, budget_mult,
+                                    max_partitions, tile_tokens, capacity, work_info, reduce_info,
+                                    num_work, &cap);
+    if (st != PA_OK) return st;
+    return from_hip(pa::launch_plan(context_lens, num_seqs, cap, capacity, max_partitions, tile_tokens,
+                                    work_info, reduce_info, num_work, pa::as_stream(stream)));
+}
+
+pa_status pa_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t num_q_heads,
+                    int32_t head_dim, const void* k_cache, const void* v_cache, pa_dtype kv_dtype,
+                    int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t num_seqs, const int32_t* cu_query_lens,
+                    int32_t max_q_len, float scale, float k_scale, float v_scale,
+                    const int32_t* work_info, const int32_t* reduce_info, const int32_t* num_work,
+                    int32_t capacity, int32_t tile_tokens, void* workspace, size_t workspace_bytes,
+                    void* out, pa_dtype out_dtype, void* stream) {
+    pa::DecodeArgs a;
+    bool nothing = false;
+    const pa_status st = prepare_decode(q, q_dtype, num_rows, num_q_heads, head_dim, k_cache, v_cache,
+                                        kv_dtype, num_blocks, num_kv_heads, block_size, block_tables,
+                                        max_blocks_per_seq, context_lens, num_seqs, cu_query_lens,
+                                        max_q_len, scale, k_scale, v_scale, work_info, reduce_info,
+                                        num_work, capacity, tile_tokens, workspace, workspace_bytes, out,
+                                        out_dtype, &a, &nothing);
+    if (st != PA_OK) return st;
+    if (nothing) {
+        if (!out || num_rows == 0) return PA_OK;
+        // nothing to decode: the merge's contract still writes every row (all zero here)
+        return pa_merge(num_rows, num_q_heads, head_dim, 0, nullptr, 1, nullptr, 0, nullptr, 0, out,
+                        out_dtype, stream);
+    }
+    return from_hip(pa::launch_decode(a, head_dim, kv_dtype, q_dtype == PA_F32, pa::as_stream(stream)));
+}
+
+pa_status pa_merge(int32_t num_rows, int32_t num_q_heads, int32_t head_dim, int32_t num_seqs,
+                   const int32_t* cu_query_lens, int32_t max_q_len, const int32_t* reduce_info,
+                   int32_t capacity, const void* workspace, size_t workspace_bytes, void* out,
+                   pa_dtype out_dtype, void* stream) {
+    pa::MergeArgs a;
+    const pa_status st = prepare_merge(num_rows, num_q_heads, head_dim, num_seqs, cu_query_lens,
+                                       max_q_len, reduce_info, capacity, workspace, workspace_bytes, out,
+                                       out_dtype, &a);
+    if (st != PA_OK || num_rows == 0) return st;
     return from_hip(pa::launch_merge(a, head_dim, out_dtype == PA_BF16, pa::as_stream(stream)));
+}
+
+pa_status pa_attention(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t num_q_heads,
+                       int32_t head_dim, const void* k_cache, const void* v_cache, pa_dtype kv_dtype,
+                       int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* context_lens, int32_t num_seqs, const int32_t* cu_query_lens,
+                       int32_t max_q_len, float scale, float k_scale, float v_scale,
+                       int32_t cu_count, int32_t budget_mult, int32_t max_partitions,
+                       int32_t tile_tokens, int32_t capacity, int32_t* work_info,
+                       int32_t* reduce_info, int32_t* num_work, void* workspace,
+                       size_t workspace_bytes, void* out, pa_dtype out_dtype, void* stream) {
+    // every check of the three calls first, so a failure launches nothing
+    int32_t cap = 0;
+    pa_status st = check_plan(context_lens, num_seqs, num_kv_heads, cu_count, budget_mult,
+                              max_partitions, tile_tokens, capacity, work_info, reduce_info, num_work,
+                              &cap);
+    if (st != PA_OK) return st;
+    pa::DecodeArgs d;
+    bool nothing = false;
+    st = prepare_decode(q, q_dtype, num_rows, num_q_heads, head_dim, k_cache, v_cache, kv_dtype,
+                        num_blocks, num_kv_heads, block_size, block_tables, max_blocks_per_seq,
+                        context_lens, num_seqs, cu_query_lens, max_q_len, scale, k_scale, v_scale,
+                        work_info, reduce_info, num_work, capacity, tile_tokens, workspace,
+                        workspace_bytes, nullptr, q_dtype, &d, &nothing);
+    if (st != PA_OK) return st;
+    if (out_dtype != q_dtype) return PA_INVALID_ARG;
+    pa::MergeArgs m;
+    st = prepare_merge(num_rows, num_q_heads, head_dim, num_seqs, cu_query_lens, max_q_len, reduce_info,
+                       capacity, workspace, workspace_bytes, out, out_dtype, &m);
+    if (st != PA_OK) return st;
+
+    hipStream_t s = pa::as_stream(stream);
+    const bool in_place = !nothing && kv_dtype != PA_F32 && num_seqs <= PA_INLINE_PLAN_SEQS;
+    if (in_place) {
+        d.plan_inline = 1;
+        d.plan_cap = cap;
+        d.max_partitions = max_partitions;
+        d.plan_work_out = reinterpret_cast<int4*>(work_info);
+        d.plan_reduce_out = reinterpret_cast<int2*>(reduce_info);
+        d.plan_num_work_out = num_work;
+    } else {
+        st = from_hip(pa::launch_plan(context_lens, num_seqs, cap, capacity, max_partitions, tile_tokens,
+                                      work_info, reduce_info, num_work, s));
+        if (st != PA_OK) return st;
+    }
+    if (!nothing) {
+        st = from_hip(pa::launch_decode(d, head_dim, kv_dtype, q_dtype == PA_F32, s));
+        if (st != PA_OK) return st;
+    }
+    if (num_rows == 0) return PA_OK;
+    return from_hip(pa::launch_merge(m, head_dim, out_dtype == PA_BF16, s));
 }
 
 const char* pa_status_string(pa_status status) {

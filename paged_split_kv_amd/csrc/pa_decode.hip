@@ -9,8 +9,9 @@
 // Design (bf16 / fp8 caches, the matrix-core kernel):
 //  * one workgroup of NW waves per (slot, kv head).  The slot's keys are cut into 16-key chunks (a
 //    chunk never straddles a page: pages hold 16, 64 or 128 tokens and slots start on tile
-//    boundaries); wave w takes the slot's tiles w, w+NW, ... whole, so every streaming wave carries
-//    one tile and long slots get proportionally more bandwidth; the NW states merge in LDS at the end.
+//    boundaries); wave w takes units w, w+NW, ... of consecutive chunks, the unit being the plan's
+//    largest slot split NW ways, so every streaming wave carries one unit and a small slot runs
+//    fewer waves, leaving bandwidth to the large ones; the NW states merge in LDS at the end.
 //  * all query rows of the group -- G heads x L verify tokens, M = G*L <= 64 -- form the columns
 //    of 16-wide MFMA blocks, so each K/V byte is read from HBM once per (slot, kv head) whatever L is.
 //  * each chunk's K and V (16 x D each) are fetched with 16-byte coalesced loads two chunks ahead into
@@ -72,6 +73,82 @@ __device__ __forceinline__ bool slot_info(const DecodeArgs& a, int slot, SlotInf
     si.k_lo = static_cast<int>(min(lo, static_cast<long long>(S)));
     si.k_hi = static_cast<int>(max(hi, static_cast<long long>(si.k_lo)));
     return true;
+}
+
+// ---------------------------------------------------------------------------------------------
+// planning in place: the plan of a batch of at most kInlinePlanSeqs requests, evaluated by every
+// workgroup with one request per thread, so the decode needs no separate planning launch.  The
+// workgroup keeps its own slot's entry; kv head 0's workgroups store the entries, workgroup 0 the
+// per-request ranges and the slot counts, so the buffers end up as the plan kernel writes them.
+// ---------------------------------------------------------------------------------------------
+template <int NW>
+__device__ void plan_in_place(const DecodeArgs& a, int slot, int g, int4& wk, int2& nwk) {
+    static_assert(NW * 64 == kInlinePlanSeqs, "one request per thread");
+    __shared__ long long s_total[NW];
+    __shared__ int s_nonempty[NW], s_slots[NW], s_below[NW], s_largest[NW];
+    __shared__ int4 s_entry;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int r = tid;
+    const bool real = r < a.num_seqs;
+    const int len = real ? max(a.context_lens[r], 0) : 0;
+
+    // W = sum S_b and B' = #{S_b > 0}
+    const long long wsum = wave_sum_ll(len);
+    const int wne = __popcll(__builtin_amdgcn_ballot_w64(len > 0));
+    if (lane == 0) {
+        s_total[wave] = wsum;
+        s_nonempty[wave] = wne;
+    }
+    __syncthreads();
+    long long total = 0;
+    int nonempty = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        total += s_total[w];
+        nonempty += s_nonempty[w];
+    }
+
+    // this request's partitions, their exclusive scan, and the largest partition in tiles
+    const int parts = plan_parts(len, static_cast<long long>(a.plan_cap) - nonempty, total, a.tile_tokens,
+                                 a.max_partitions);
+    const int tiles = plan_tiles(len, a.tile_tokens);
+    const int incl = wave_incl_scan(parts, lane);
+    int big = parts > 0 ? (tiles + parts - 1) / parts : 0;     // a floor/ceil split's largest part
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) big = max(big, __shfl_xor(big, o, 64));
+    if (lane == 63) s_slots[wave] = incl;
+    if (lane == 0) s_largest[wave] = big;
+    __syncthreads();
+    int before = 0, used = 0, largest = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        before += w < wave ? s_slots[w] : 0;
+        used += s_slots[w];
+        largest = max(largest, s_largest[w]);
+    }
+    const int first = before + incl - parts;
+
+    // the requests whose first slot is <= slot are a prefix; its last one owns the slot
+    const int below = __popcll(__builtin_amdgcn_ballot_w64(real && first <= slot));
+    if (lane == 0) s_below[wave] = below;
+    if (blockIdx.x == 0 && real) a.plan_reduce_out[r] = make_int2(first, parts);
+    __syncthreads();
+    int owner = -1;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) owner += s_below[w];
+    if (slot < used && r == owner) {
+        const int2 t = plan_tile_range(slot - first, tiles, parts);
+        s_entry = make_int4(r, t.x, t.y, len);
+    }
+    __syncthreads();
+    wk = slot < used ? s_entry : make_int4(-1, 0, 0, 0);
+    nwk = make_int2(used, largest);
+    if (tid == 0) {
+        if (g == 0) a.plan_work_out[slot] = wk;
+        if (blockIdx.x == 0) *reinterpret_cast<int2*>(a.plan_num_work_out) = nwk;
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -205,8 +282,14 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
     // ---- slot geometry.  Dependent loads are kept to three levels: the work entry; then the
     // request's length, cumulative query lengths and (speculatively, over the plan's tile range)
     // this wave's page ids; then queries and K/V. ----
-    const int4 wk = a.work_info[slot];
-    const int2 nwk = *reinterpret_cast<const int2*>(a.num_work);   // (used slots, largest slot in tiles)
+    int4 wk;
+    int2 nwk;                                      // (used slots, largest slot in tiles)
+    if (a.plan_inline) {
+        plan_in_place<C::NW>(a, slot, g, wk, nwk);
+    } else {
+        wk = a.work_info[slot];
+        nwk = *reinterpret_cast<const int2*>(a.num_work);
+    }
     const int used = nwk.x;
     const int b = wk.x;
     if (slot >= used || b < 0 || b >= a.num_seqs) return;

@@ -98,6 +98,60 @@ __device__ __forceinline__ float2 load_f2_coherent(const float* p) {
 // Wait until this wave's outstanding memory operations are acknowledged (stores included).
 __device__ __forceinline__ void wait_memory_acks() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// ---------------------------------------------------------------------------------------------
+// the planner's rule, shared by the plan kernel and the decode that plans in place (ROCm/ATOM PR
+// #2366 section 1: partitions proportional to the request's length under the budget; section 3:
+// ceiling; review item 2: contiguous tile ranges).  Integer-only, so every evaluation is identical.
+// ---------------------------------------------------------------------------------------------
+
+__device__ __forceinline__ long long wave_sum_ll(long long v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        int lo = __shfl_xor(static_cast<int>(v & 0xffffffffll), o, 64);
+        int hi = __shfl_xor(static_cast<int>(v >> 32), o, 64);
+        v += (static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo);
+    }
+    return v;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int t = __shfl_up(v, o, 64);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+// Tiles of a request of s tokens.
+__device__ __forceinline__ int plan_tiles(long long s, int tile_tokens) {
+    return s > 0 ? static_cast<int>((s + tile_tokens - 1) / tile_tokens) : 0;
+}
+
+// Partitions of a request of s tokens: none when empty, else min(P, tiles, 1 + floor(extra * s / W))
+// with extra = capacity - (non-empty requests) and W the batch's total length.
+__device__ __forceinline__ int plan_parts(long long s, long long extra, long long total, int tile_tokens,
+                                          int max_partitions) {
+    if (s <= 0) return 0;
+    long long p = 1 + (extra * s) / total;
+    const long long tiles = plan_tiles(s, tile_tokens);
+    if (p > tiles) p = tiles;
+    if (p > max_partitions) p = max_partitions;
+    return static_cast<int>(p);
+}
+
+// Tile range [floor(j * tiles / parts), floor((j + 1) * tiles / parts)) of partition j.
+__device__ __forceinline__ int2 plan_tile_range(int j, int tiles, int parts) {
+    const unsigned t = static_cast<unsigned>(tiles);
+    if (static_cast<unsigned long long>(parts) * t < (1ull << 32)) {
+        // (j + 1) * tiles <= parts * tiles fits 32 bits: exact unsigned division
+        return make_int2(static_cast<int>((static_cast<unsigned>(j) * t) / static_cast<unsigned>(parts)),
+                         static_cast<int>((static_cast<unsigned>(j + 1) * t) / static_cast<unsigned>(parts)));
+    }
+    return make_int2(static_cast<int>((static_cast<long long>(j) * t) / parts),
+                     static_cast<int>((static_cast<long long>(j + 1) * t) / parts));
+}
+
 // Workspace layout (see pa_workspace_bytes): acc region then (m, l) region, each 256-byte aligned.
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -166,6 +220,14 @@ struct DecodeArgs {
     int* ws_counters;           // arrival counters of the fused merge
     const int2* reduce_info;    // (first slot, partitions) per request; needed when out is set
     void* out;                  // nullable: when set, the merge runs inside the decode launch
+    // planning in place (num_seqs <= kInlinePlanSeqs): every workgroup evaluates the planner's rule
+    // itself; the plan is also stored to these buffers for the merge and the caller
+    int plan_inline;
+    int plan_cap;               // the capacity formula's value (not the buffer's capacity)
+    int max_partitions;
+    int4* plan_work_out;
+    int2* plan_reduce_out;
+    int32_t* plan_num_work_out;
     int out_bf16;
     int num_rows, num_q_heads, num_kv_heads, group;   // group = Hq / Hkv
     int num_blocks, block_size, max_blocks, num_seqs;
@@ -182,6 +244,9 @@ struct MergeArgs {
     void* out;
     int num_rows, num_q_heads, num_seqs, max_q_len, capacity;
 };
+
+// Requests a decode workgroup can plan for in place: one per thread of its 4 waves.
+constexpr int kInlinePlanSeqs = PA_INLINE_PLAN_SEQS;
 
 hipError_t launch_plan(const int32_t* context_lens, int num_seqs, int cap_formula, int capacity,
                        int max_partitions, int tile_tokens, int32_t* work_info, int32_t* reduce_info,

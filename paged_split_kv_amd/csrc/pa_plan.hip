@@ -19,25 +19,6 @@ namespace {
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / 64;
 
-__device__ __forceinline__ long long wave_sum_ll(long long v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        int lo = __shfl_xor(static_cast<int>(v & 0xffffffffll), o, 64);
-        int hi = __shfl_xor(static_cast<int>(v >> 32), o, 64);
-        v += (static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo);
-    }
-    return v;
-}
-
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int t = __shfl_up(v, o, 64);
-        if (lane >= o) v += t;
-    }
-    return v;
-}
-
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int32_t* __restrict__ context_lens, int num_seqs, int cap_formula, int capacity,
     int max_partitions, int tile_tokens, int4* __restrict__ work_info,
@@ -81,15 +62,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int b1 = min(b0 + per, num_seqs);
     int local = 0;
     for (int b = b0; b < b1; ++b) {
-        const long long s = max(context_lens[b], 0);
-        int parts = 0;
-        if (s > 0) {
-            const long long tiles = (s + tile_tokens - 1) / tile_tokens;
-            long long p = 1 + (extra * s) / total;
-            if (p > tiles) p = tiles;
-            if (p > max_partitions) p = max_partitions;
-            parts = static_cast<int>(p);
-        }
+        const int parts = plan_parts(max(context_lens[b], 0), extra, total, tile_tokens, max_partitions);
         first[b] = parts;
         local += parts;
     }
@@ -125,18 +98,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
             const int j = s - first[b];
             const int parts = first[b + 1] - first[b];
             const int len = max(context_lens[b], 0);
-            const unsigned tiles = static_cast<unsigned>((static_cast<long long>(len) + tile_tokens - 1) / tile_tokens);
-            int tb, te;
-            if (static_cast<unsigned long long>(parts) * tiles < (1ull << 32)) {
-                // (j + 1) * tiles <= parts * tiles fits 32 bits: exact unsigned division
-                tb = static_cast<int>((static_cast<unsigned>(j) * tiles) / static_cast<unsigned>(parts));
-                te = static_cast<int>((static_cast<unsigned>(j + 1) * tiles) / static_cast<unsigned>(parts));
-            } else {
-                tb = static_cast<int>((static_cast<long long>(j) * tiles) / parts);
-                te = static_cast<int>((static_cast<long long>(j + 1) * tiles) / parts);
-            }
-            work_info[s] = make_int4(b, tb, te, len);
-            largest = max(largest, te - tb);
+            const int2 r = plan_tile_range(j, plan_tiles(len, tile_tokens), parts);
+            work_info[s] = make_int4(b, r.x, r.y, len);
+            largest = max(largest, r.y - r.x);
         } else {
             work_info[s] = make_int4(-1, 0, 0, 0);
         }

@@ -1,8 +1,8 @@
-"""One decode step on the device: pa_plan -> pa_decode -> pa_merge on one stream.
+"""One decode step on the device: pa_plan -> pa_decode -> pa_merge on one stream, or the same step
+as one pa_attention call (the decode plans in place: two launches).
 
 ``DecodeStep`` owns the plan buffers, the workspace and the output for one batch geometry, so a
-timed loop issues exactly the three library calls and allocates nothing.  All arithmetic happens in
-libpa.so.
+timed loop issues only library calls and allocates nothing.  All arithmetic happens in libpa.so.
 """
 from __future__ import annotations
 
@@ -65,14 +65,30 @@ class DecodeStep:
                     reduce_info=self.reduce_info if merge else None,
                     out=self.out if merge else None, stream=stream)
 
+    def attention(self, q, k_cache, v_cache, kv_dtype, block_tables, context_lens, *, scale,
+                  cu_query_lens=None, k_scale=1.0, v_scale=1.0, stream=None) -> torch.Tensor:
+        """pa_attention: plan, decode and merge into self.out; the plan buffers are refreshed."""
+        p = self.plan_cfg
+        B.pa_attention(q, k_cache, v_cache, kv_dtype, block_tables, context_lens, self.work_info,
+                       self.reduce_info, self.num_work, self.workspace, self.out, scale=scale,
+                       cu_count=p.cu_count, budget_mult=p.budget_mult, max_partitions=p.max_partitions,
+                       tile_tokens=p.tile_tokens, cu_query_lens=cu_query_lens, max_q_len=self.max_q_len,
+                       k_scale=k_scale, v_scale=v_scale, stream=stream)
+        return self.out
+
     def merge(self, cu_query_lens=None, stream=None) -> torch.Tensor:
         B.pa_merge(self.out, self.reduce_info, self.workspace, capacity=self.capacity,
                    cu_query_lens=cu_query_lens, max_q_len=self.max_q_len, stream=stream)
         return self.out
 
-    def run_case(self, case, stream=None, replan: bool = True, fused: bool = True) -> torch.Tensor:
+    def run_case(self, case, stream=None, replan: bool = True, fused: bool = True,
+                 whole: bool = False) -> torch.Tensor:
         """Plan, decode and merge one Case.  fused=True merges inside pa_decode (two launches per
-        step); fused=False calls pa_merge separately."""
+        step); fused=False calls pa_merge separately; whole=True makes the one pa_attention call."""
+        if whole:
+            return self.attention(case.q, case.k_cache, case.v_cache, case.kv_dtype, case.block_tables,
+                                  case.context_lens, scale=case.scale, cu_query_lens=case.cu_query_lens,
+                                  k_scale=case.k_scale, v_scale=case.v_scale, stream=stream)
         if replan:
             self.plan(case.context_lens, stream)
         self.decode(case.q, case.k_cache, case.v_cache, case.kv_dtype, case.block_tables,
@@ -83,6 +99,7 @@ class DecodeStep:
         return self.merge(case.cu_query_lens, stream)
 
 
-def run_case(case, plan: Optional[PlanConfig] = None, fused: bool = True) -> torch.Tensor:
+def run_case(case, plan: Optional[PlanConfig] = None, fused: bool = True,
+             whole: bool = False) -> torch.Tensor:
     """Plan, decode and merge one workload Case; returns the output tensor (device)."""
-    return DecodeStep.for_case(case, plan).run_case(case, fused=fused)
+    return DecodeStep.for_case(case, plan).run_case(case, fused=fused, whole=whole)

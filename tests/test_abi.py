@@ -155,3 +155,39 @@ def test_binding_refuses_host_tensors():
     ctx = torch.tensor([1, 2], dtype=torch.int32)
     with pytest.raises(ValueError):
         B.pa_plan(ctx, 1, cu_count=256)
+
+
+def _attention_status(**kw):
+    a = dict(_GOOD)
+    a.update(dict(out=512, cuc=256, mult=2, P=256))
+    a.update(kw)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return B.load().pa_attention(vp(a["q"]), a["qd"], a["R"], a["Hq"], a["D"], vp(a["k"]), vp(a["v"]),
+                                 a["kvd"], a["nb"], a["Hkv"], a["bs"], vp(a["bt"]), a["mb"], vp(a["ctx"]),
+                                 a["Bn"], vp(a["cu"]), a["ql"], a["scale"], a["ks"], a["vs"], a["cuc"],
+                                 a["mult"], a["P"], a["T"], a["cap"], vp(a["work"]), vp(a["red"]),
+                                 vp(a["nw"]), vp(a["ws"]), a["wsb"], vp(a["out"]), a["od"], None)
+
+
+def test_attention_argument_checks():
+    # the union of the three calls' checks, all before any launch
+    assert _attention_status(cap=255) == B.PA_CAPACITY                 # plan: below the formula (256)
+    assert _attention_status(P=0) == B.PA_INVALID_ARG
+    assert _attention_status(cuc=0) == B.PA_INVALID_ARG
+    assert _attention_status(nw=260) == B.PA_INVALID_ARG               # num_work pair misaligned
+    assert _attention_status(red=None) == B.PA_INVALID_ARG
+    assert _attention_status(Bn=B.PA_MAX_SEQS + 1, cap=1 << 22) == B.PA_UNSUPPORTED
+    assert _attention_status(D=96) == B.PA_UNSUPPORTED                 # decode checks
+    assert _attention_status(bs=32) == B.PA_UNSUPPORTED
+    assert _attention_status(T=200) == B.PA_UNSUPPORTED
+    assert _attention_status(qd=B.PA_FP8_E4M3) == B.PA_INVALID_ARG
+    assert _attention_status(ws=None) == B.PA_INVALID_ARG
+    assert _attention_status(wsb=1000) == B.PA_CAPACITY
+    assert _attention_status(out=None) == B.PA_INVALID_ARG             # merge checks
+    assert _attention_status(out=520) == B.PA_INVALID_ARG
+    assert _attention_status(od=B.PA_F32) == B.PA_INVALID_ARG
+    assert _attention_status(ql=2) == B.PA_INVALID_ARG
+
+
+def test_merge_refuses_misaligned_out():
+    assert _merge_status(out=264) == B.PA_INVALID_ARG

@@ -1,0 +1,151 @@
+"""pa_attention -- plan, decode and merge in one call, the decode planning in place -- against the
+three-call path (bitwise) and the fp64 oracle.
+
+The in-place plan must be the planner's plan bit for bit (ROCm/ATOM PR #2366 section 1, review items 2
+and 3): every workgroup evaluates the same integer rule, and the stored buffers are compared with the
+oracle's plan on whole buffers, sentinels and the largest-slot word included.  Batches above the
+in-place limit, and fp32 caches, take the three-launch route and must give the same results.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_split_kv_amd import binding as B
+from paged_split_kv_amd import workloads as W
+from paged_split_kv_amd.runner import DecodeStep, PlanConfig
+from _util import announce, assert_close, oracle_direct, to_f64, tolerance_kind
+from test_gpu_decode import SMALL, _partial_bytes, _small_case, _zero_rows
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _poison(step):
+    step.out.fill_(float("nan"))
+    step.workspace[:_partial_bytes(step)].fill_(0xFF)
+    step.work_info.fill_(0x5A5A5A5A)
+    step.reduce_info.fill_(-7)
+    step.num_work.fill_(-9)
+
+
+def _oracle_plan(ctx, hkv, cfg, capacity):
+    return oracle.plan(np.asarray(ctx), hkv, cfg.cu_count, cfg.budget_mult, cfg.max_partitions,
+                       cfg.tile_tokens, capacity, with_largest=True)
+
+
+def _check_plan(step, ctx, hkv, cfg):
+    ow, orr, on, olarge = _oracle_plan(ctx, hkv, cfg, step.capacity)
+    assert step.num_work.cpu().numpy().tolist() == [on, olarge]
+    assert np.array_equal(step.reduce_info.cpu().numpy(), orr)
+    assert np.array_equal(step.work_info.cpu().numpy(), ow)
+
+
+def _both_routes(case, cfg):
+    three = DecodeStep.for_case(case, cfg)
+    _poison(three)
+    ref = three.run_case(case, fused=False).clone()
+    whole = DecodeStep.for_case(case, cfg)
+    _poison(whole)
+    got = whole.run_case(case, whole=True)
+    torch.cuda.synchronize()
+    return got, ref, whole
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=[s[0] for s in SMALL])
+def test_small_cases(spec):
+    case, P, T = _small_case(spec, seed=12)
+    announce(f"attention {spec[0]}")
+    cfg = PlanConfig(cu_count=256, max_partitions=P, tile_tokens=T)
+    got, ref, step = _both_routes(case, cfg)
+    assert torch.equal(got, ref), "pa_attention differs from pa_plan + pa_decode + pa_merge"
+    _check_plan(step, case.context_lens.cpu().numpy(), case.num_kv_heads, cfg)
+    g = to_f64(got)
+    assert_close(g, oracle_direct(case), tolerance_kind(case), spec[0])
+    assert (g[_zero_rows(case)] == 0.0).all()
+
+
+@pytest.mark.parametrize("name", ["verify_bf16", "fp8_kv", "long_bf16"])
+def test_full_size_workloads(name):
+    announce(f"attention full {name}")
+    case = W.make_config(name, device=DEV)
+    cfg = PlanConfig(cu_count=256)
+    got, ref, step = _both_routes(case, cfg)
+    assert torch.equal(got, ref)
+    _check_plan(step, case.context_lens.cpu().numpy(), case.num_kv_heads, cfg)
+    assert_close(to_f64(got), oracle_direct(case), tolerance_kind(case), name)
+
+
+def test_skewed_max_step():
+    steps = W.skewed_step_set()
+    idx = W.skewed_named_steps(steps)["max_tokens"]
+    announce(f"attention skewed max step #{idx}")
+    case = W.make_config("skewed_bf16", device=DEV, step=idx)
+    cfg = PlanConfig(cu_count=256)
+    got, ref, step = _both_routes(case, cfg)
+    assert torch.equal(got, ref)
+    _check_plan(step, steps[idx], 2, cfg)
+    assert_close(to_f64(got), oracle_direct(case), "bf16", "skewed max")
+
+
+def _one_page_case(ctx, hkv, seed):
+    """Every block-table entry names page 0 of a tiny cache: any length stays in bounds, so the
+    plan can be exercised at any size; the output is checked against the three-call path only."""
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    Bn, hq, d, bs = len(ctx), 2 * hkv, 64, 16
+    k = torch.randn((2, hkv, bs, d), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((2, hkv, bs, d), generator=g, device=DEV).to(torch.bfloat16)
+    q = torch.randn((Bn, hq, d), generator=g, device=DEV).to(torch.bfloat16)
+    mb = max(1, -(-int(max(ctx, default=1)) // bs))
+    bt = torch.zeros((Bn, mb), dtype=torch.int32, device=DEV)
+    lens = torch.as_tensor(np.asarray(ctx, dtype=np.int32), device=DEV)
+    return q, k, v, bt, lens
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_plan_in_place_fuzz(seed):
+    rng = np.random.default_rng(900 + seed)
+    Bn = int(rng.choice([1, 2, 31, 63, 64, 65, 128, 200, 255, 256, 257, 300]))
+    hkv = int(rng.choice([1, 2, 4]))
+    P = int(rng.choice([1, 8, 256]))
+    T = int(rng.choice([16, 64, 256]))
+    mult = int(rng.choice([1, 2, 3]))
+    kind = seed % 3
+    if kind == 0:
+        ctx = rng.integers(0, 40000, size=Bn)
+    elif kind == 1:
+        ctx = np.where(rng.random(Bn) < 0.4, 0, rng.integers(1, 3000, size=Bn))
+    else:
+        ctx = np.clip(np.rint(np.exp(rng.normal(7.0, 1.5, size=Bn))), 0, 60000).astype(np.int64)
+    announce(f"plan in place fuzz seed {seed} B={Bn} Hkv={hkv} P={P} T={T} x{mult}")
+    q, k, v, bt, lens = _one_page_case(ctx, hkv, seed)
+    cfg = PlanConfig(cu_count=256, budget_mult=mult, max_partitions=P, tile_tokens=T)
+    mk = lambda: DecodeStep(num_seqs=Bn, num_rows=Bn, num_q_heads=2 * hkv, num_kv_heads=hkv, head_dim=64,
+                            max_q_len=1, out_dtype=torch.bfloat16, device=DEV, plan=cfg)
+    three, whole = mk(), mk()
+    for s in (three, whole):
+        _poison(s)
+    three.plan(lens)
+    three.decode(q, k, v, "bf16", bt, lens, scale=0.125)
+    three.merge()
+    whole.attention(q, k, v, "bf16", bt, lens, scale=0.125)
+    torch.cuda.synchronize()
+    _check_plan(whole, ctx, hkv, cfg)
+    assert torch.equal(whole.out, three.out)
+
+
+def test_all_empty_and_empty_batch():
+    for ctx in ([0, 0, 0], []):
+        announce(f"attention empty {ctx}")
+        q, k, v, bt, lens = _one_page_case(ctx or [0], 1, 0)
+        n = len(ctx)
+        q, bt, lens = q[:n], bt[:n], lens[:n]
+        step = DecodeStep(num_seqs=n, num_rows=max(n, 2), num_q_heads=2, num_kv_heads=1, head_dim=64,
+                          max_q_len=1, out_dtype=torch.bfloat16, device=DEV, plan=PlanConfig(cu_count=256))
+        _poison(step)
+        qq = torch.zeros((max(n, 2), 2, 64), dtype=torch.bfloat16, device=DEV)
+        step.attention(qq, k, v, "bf16", bt, lens, scale=0.125)
+        torch.cuda.synchronize()
+        assert (step.out == 0).all()
+        _check_plan(step, ctx, 1, PlanConfig(cu_count=256))

@@ -29,8 +29,9 @@ def _oracle_at(case, lens):
                                    case.scale, case.k_scale, case.v_scale)
 
 
-@pytest.mark.parametrize("fused", [False, True], ids=["separate_merge", "fused_merge"])
-def test_graph_replays_draft_passes(fused):
+@pytest.mark.parametrize("mode", ["separate_merge", "fused_merge", "attention"])
+def test_graph_replays_draft_passes(mode):
+    fused = mode == "fused_merge"
     final = [1300, 40, 2, 5000, 777, 256]
     q_lens = [2, 1, 2, 3, 1, 2]
     # pages exist for the final lengths; the graph starts PASSES tokens earlier
@@ -46,11 +47,15 @@ def test_graph_replays_draft_passes(fused):
     def passes():
         for p in range(PASSES):
             lens.add_(1)                                   # the draft step advances every length
-            step.plan(lens)                                # refresh the plan in place
-            step.decode(case.q, case.k_cache, case.v_cache, case.kv_dtype, case.block_tables, lens,
-                        scale=case.scale, cu_query_lens=case.cu_query_lens, merge=fused)
-            if not fused:
-                step.merge(case.cu_query_lens)
+            if mode == "attention":                        # plans in place inside the decode launch
+                step.attention(case.q, case.k_cache, case.v_cache, case.kv_dtype, case.block_tables, lens,
+                               scale=case.scale, cu_query_lens=case.cu_query_lens)
+            else:
+                step.plan(lens)                            # refresh the plan in place
+                step.decode(case.q, case.k_cache, case.v_cache, case.kv_dtype, case.block_tables, lens,
+                            scale=case.scale, cu_query_lens=case.cu_query_lens, merge=fused)
+                if not fused:
+                    step.merge(case.cu_query_lens)
             outs[p].copy_(step.out)
 
     # warm up eagerly (the recorded path must be the planned one), then capture
@@ -70,7 +75,7 @@ def test_graph_replays_draft_passes(fused):
                          kv_dtype="bf16", q_dtype="bf16", seed=32, q_lens=[1, 2], device=DEV)
     other_step = DecodeStep.for_case(other, PlanConfig(cu_count=256))
     for rep in range(4):
-        announce(f"graph replay {rep} fused={fused}")
+        announce(f"graph replay {rep} {mode}")
         lens.copy_(torch.from_numpy(start.astype(np.int32)))
         for o in outs:
             o.fill_(float("nan"))
@@ -80,8 +85,8 @@ def test_graph_replays_draft_passes(fused):
         for p in range(PASSES):
             assert_close(to_f64(outs[p]), refs[p], "bf16", f"replay {rep} pass {p}")
         assert int(lens.cpu().numpy().sum()) == int(np.sum(final))
-        ow, orr, on = oracle.plan(final, 2, 256)
-        assert int(step.num_work[0].item()) == on
+        ow, orr, on, olarge = oracle.plan(final, 2, 256, with_largest=True)
+        assert step.num_work.cpu().numpy().tolist() == [on, olarge]
         assert np.array_equal(step.work_info.cpu().numpy(), ow)
         assert np.array_equal(step.reduce_info.cpu().numpy(), orr)
         # eager work between replays, on the same device and stream
