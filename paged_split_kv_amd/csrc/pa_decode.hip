@@ -81,9 +81,48 @@ __device__ __forceinline__ bool slot_info(const DecodeArgs& a, int slot, SlotInf
 // workgroup keeps its own slot's entry; kv head 0's workgroups store the entries, workgroup 0 the
 // per-request ranges and the slot counts, so the buffers end up as the plan kernel writes them.
 // ---------------------------------------------------------------------------------------------
+// Up to 64 requests: every wave evaluates the whole plan on its own, with no barrier.
+__device__ __forceinline__ void plan_in_wave(const DecodeArgs& a, int slot, int g, int4& wk, int2& nwk) {
+    const int lane = threadIdx.x & 63;
+    const bool real = lane < a.num_seqs;
+    const int len = real ? max(a.context_lens[lane], 0) : 0;
+    const long long total = wave_sum_ll(len);
+    const int nonempty = __popcll(__builtin_amdgcn_ballot_w64(len > 0));
+    const int parts = plan_parts(len, static_cast<long long>(a.plan_cap) - nonempty, total, a.tile_tokens,
+                                 a.max_partitions);
+    const int tiles = plan_tiles(len, a.tile_tokens);
+    const int incl = wave_incl_scan(parts, lane);
+    const int first = incl - parts;
+    const int used = __builtin_amdgcn_readlane(incl, 63);
+    int big = parts > 0 ? (tiles + parts - 1) / parts : 0;      // a floor/ceil split's largest part
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) big = max(big, __shfl_xor(big, o, 64));
+    // the requests whose first slot is <= slot are a prefix; its last one owns the slot
+    const int owner = __popcll(__builtin_amdgcn_ballot_w64(real && first <= slot)) - 1;
+    wk = make_int4(-1, 0, 0, 0);
+    if (slot < used) {
+        const int o = max(owner, 0);
+        const int2 t = plan_tile_range(slot - __builtin_amdgcn_readlane(first, o),
+                                       __builtin_amdgcn_readlane(tiles, o), __builtin_amdgcn_readlane(parts, o));
+        wk = make_int4(o, t.x, t.y, __builtin_amdgcn_readlane(len, o));
+    }
+    nwk = make_int2(used, big);
+    if (threadIdx.x < 64) {
+        if (blockIdx.x == 0 && real) a.plan_reduce_out[lane] = make_int2(first, parts);
+        if (lane == 0) {
+            if (g == 0) a.plan_work_out[slot] = wk;
+            if (blockIdx.x == 0) *reinterpret_cast<int2*>(a.plan_num_work_out) = nwk;
+        }
+    }
+}
+
 template <int NW>
 __device__ void plan_in_place(const DecodeArgs& a, int slot, int g, int4& wk, int2& nwk) {
     static_assert(NW * 64 == kInlinePlanSeqs, "one request per thread");
+    if (a.num_seqs <= 64) {
+        plan_in_wave(a, slot, g, wk, nwk);
+        return;
+    }
     __shared__ long long s_total[NW];
     __shared__ int s_nonempty[NW], s_slots[NW], s_below[NW], s_largest[NW];
     __shared__ int4 s_entry;

@@ -123,18 +123,27 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
     return v;
 }
 
-// Tiles of a request of s tokens.
-__device__ __forceinline__ int plan_tiles(long long s, int tile_tokens) {
-    return s > 0 ? static_cast<int>((s + tile_tokens - 1) / tile_tokens) : 0;
+// Tiles of a request of s tokens (s + tile_tokens - 1 < 2^32, so 32-bit unsigned division is exact).
+__device__ __forceinline__ int plan_tiles(int s, int tile_tokens) {
+    return s > 0 ? static_cast<int>((static_cast<unsigned>(s) + static_cast<unsigned>(tile_tokens) - 1u) /
+                                    static_cast<unsigned>(tile_tokens))
+                 : 0;
 }
 
 // Partitions of a request of s tokens: none when empty, else min(P, tiles, 1 + floor(extra * s / W))
-// with extra = capacity - (non-empty requests) and W the batch's total length.
-__device__ __forceinline__ int plan_parts(long long s, long long extra, long long total, int tile_tokens,
+// with extra = capacity - (non-empty requests) >= 0 and W the batch's total length.  The quotient
+// takes the 32-bit unsigned division when both operands fit, the 64-bit one otherwise.
+__device__ __forceinline__ int plan_parts(int s, long long extra, long long total, int tile_tokens,
                                           int max_partitions) {
     if (s <= 0) return 0;
-    long long p = 1 + (extra * s) / total;
-    const long long tiles = plan_tiles(s, tile_tokens);
+    const unsigned long long num = static_cast<unsigned long long>(extra) * static_cast<unsigned>(s);
+    long long q;
+    if ((num >> 32) == 0 && (static_cast<unsigned long long>(total) >> 32) == 0)
+        q = static_cast<unsigned>(num) / static_cast<unsigned>(total);
+    else
+        q = static_cast<long long>(num / static_cast<unsigned long long>(total));
+    long long p = 1 + q;
+    const int tiles = plan_tiles(s, tile_tokens);
     if (p > tiles) p = tiles;
     if (p > max_partitions) p = max_partitions;
     return static_cast<int>(p);
