@@ -8,7 +8,8 @@ with gcc into ``liboracle.so`` beside this file.  This module only marshals nump
 
 Functions:
   plan_capacity, plan    -- O1, the length-proportional planner (integer, bit-exact contract)
-  attention_direct       -- O2, softmax attention of every row over its visible keys
+  attention_direct       -- O2, softmax attention of every row over its visible keys (optionally
+                            limited to the last `window` of them)
   attention_split        -- O3, the same computed per plan slot and merged by log-sum-exp
   attention_rows         -- O2 for selected (row, head) pairs of a full-size problem
   decode_values          -- element decoding of the storage types (bf16 bits, e4m3fn codes)
@@ -61,9 +62,10 @@ def _load():
         c_int = ctypes.c_int
         dbl = ctypes.c_double
         lib.orc_plan_capacity.argtypes = [c_int, c_int, c_int, c_int, c_int, i32p]
-        lib.orc_plan.argtypes = [vp, c_int, c_int, c_int, c_int, c_int, c_int, c_int, vp, vp, vp]
+        lib.orc_plan.argtypes = [vp, vp, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int, vp, vp,
+                                 vp]
         prob = [vp, c_int, c_int, c_int, c_int, vp, vp, c_int, c_int, c_int, c_int, vp, c_int, vp,
-                c_int, vp, dbl, dbl, dbl]
+                c_int, vp, dbl, dbl, dbl, c_int]
         lib.orc_attention_direct.argtypes = prob + [vp, c_int]
         lib.orc_attention_split.argtypes = prob + [vp, vp, c_int, vp, c_int]
         lib.orc_attention_rows.argtypes = prob + [vp, vp, c_int, vp]
@@ -103,19 +105,23 @@ def plan_capacity(num_seqs: int, num_kv_heads: int, cu_count: int = 256, budget_
 
 def plan(context_lens, num_kv_heads: int, cu_count: int = 256, budget_mult: int = 2,
          max_partitions: int = 256, tile_tokens: int = 256, capacity: Optional[int] = None,
-         with_largest: bool = False):
+         with_largest: bool = False, cu_query_lens=None, window: int = 0):
     """Returns (work_info int32 [capacity, 4], reduce_info int32 [B, 2], num_work) and, with
-    with_largest, also the tile count of the largest slot."""
+    with_largest, also the tile count of the largest slot.  cu_query_lens and window only matter
+    together: with a window the plan covers each request's windowed key range."""
     ctx = _i32(context_lens)
     B = int(ctx.shape[0])
+    cu = None if cu_query_lens is None else _i32(cu_query_lens)
+    if cu is not None and cu.shape[0] != B + 1:
+        raise OracleError("cu_query_lens shape")
     cap = plan_capacity(B, num_kv_heads, cu_count, budget_mult, max_partitions)
     if capacity is None:
         capacity = cap
     work = np.zeros((max(capacity, 0), 4), dtype=np.int32)
     red = np.zeros((B, 2), dtype=np.int32)
     nw = np.zeros(2, dtype=np.int32)
-    st = _load().orc_plan(_ptr(ctx), B, num_kv_heads, cu_count, budget_mult, max_partitions,
-                          tile_tokens, capacity, _ptr(work), _ptr(red), _ptr(nw))
+    st = _load().orc_plan(_ptr(ctx), _ptr(cu), B, num_kv_heads, cu_count, budget_mult, max_partitions,
+                          tile_tokens, int(window), capacity, _ptr(work), _ptr(red), _ptr(nw))
     if st != OK:
         raise OracleError("invalid planner arguments")
     if with_largest:
@@ -128,7 +134,7 @@ def plan(context_lens, num_kv_heads: int, cu_count: int = 256, budget_mult: int 
 # ---------------------------------------------------------------------------------------------
 
 def _problem(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables, context_lens, cu_query_lens,
-             scale, k_scale, v_scale):
+             scale, k_scale, v_scale, window=0):
     q = np.ascontiguousarray(q, dtype=_STORAGE[q_dtype])
     k = np.ascontiguousarray(k_cache, dtype=_STORAGE[kv_dtype])
     v = np.ascontiguousarray(v_cache, dtype=_STORAGE[kv_dtype])
@@ -147,15 +153,15 @@ def _problem(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables, context_lens,
     keep = (q, k, v, bt, ctx, cu)
     args = [_ptr(q), DTYPE_CODES[q_dtype], R, Hq, D, _ptr(k), _ptr(v), DTYPE_CODES[kv_dtype], nb, Hkv,
             bs, _ptr(bt), int(bt.shape[1]), _ptr(ctx), B, _ptr(cu), float(scale), float(k_scale),
-            float(v_scale)]
+            float(v_scale), int(window)]
     return args, keep, (R, Hq, D)
 
 
 def attention_direct(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables, context_lens,
                      cu_query_lens, scale, k_scale=1.0, v_scale=1.0,
-                     threads: Optional[int] = None) -> np.ndarray:
+                     threads: Optional[int] = None, window: int = 0) -> np.ndarray:
     args, keep, (R, Hq, D) = _problem(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables,
-                                      context_lens, cu_query_lens, scale, k_scale, v_scale)
+                                      context_lens, cu_query_lens, scale, k_scale, v_scale, window)
     out = np.empty((R, Hq, D), dtype=np.float64)
     st = _load().orc_attention_direct(*args, _ptr(out), threads or default_threads())
     if st != OK:
@@ -165,9 +171,9 @@ def attention_direct(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables, conte
 
 def attention_split(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables, context_lens,
                     cu_query_lens, scale, work_info, reduce_info, tile_tokens, k_scale=1.0,
-                    v_scale=1.0, threads: Optional[int] = None) -> np.ndarray:
+                    v_scale=1.0, threads: Optional[int] = None, window: int = 0) -> np.ndarray:
     args, keep, (R, Hq, D) = _problem(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables,
-                                      context_lens, cu_query_lens, scale, k_scale, v_scale)
+                                      context_lens, cu_query_lens, scale, k_scale, v_scale, window)
     work = _i32(work_info)
     red = _i32(reduce_info)
     out = np.empty((R, Hq, D), dtype=np.float64)
@@ -179,9 +185,10 @@ def attention_split(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables, contex
 
 
 def attention_rows(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables, context_lens,
-                   cu_query_lens, scale, rows, heads, k_scale=1.0, v_scale=1.0) -> np.ndarray:
+                   cu_query_lens, scale, rows, heads, k_scale=1.0, v_scale=1.0,
+                   window: int = 0) -> np.ndarray:
     args, keep, (R, Hq, D) = _problem(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables,
-                                      context_lens, cu_query_lens, scale, k_scale, v_scale)
+                                      context_lens, cu_query_lens, scale, k_scale, v_scale, window)
     rows = _i32(rows)
     heads = _i32(heads)
     out = np.empty((rows.shape[0], D), dtype=np.float64)
@@ -205,4 +212,5 @@ def run_case(case, threads: Optional[int] = None) -> np.ndarray:
     h = case.host()
     return attention_direct(h["q"], case.q_dtype, h["k_cache"], h["v_cache"], case.kv_dtype,
                             h["block_tables"], h["context_lens"], h["cu_query_lens"], case.scale,
-                            case.k_scale, case.v_scale, threads=threads)
+                            case.k_scale, case.v_scale, threads=threads,
+                            window=getattr(case, "window", 0))

@@ -16,7 +16,8 @@
  *   [ATOM-2514] ROCm/ATOM PR #2514 "Fix(attention): adapt the FlyDSL paged decode to aiter #5809
  *               (explicit work plans)": Motivation and Design (2 x CU budget on every call).
  *   [RDNA-29]   opengfx1030/vllm-rdna PR #29 (mixed and MTP-verify batches): Change, item 1
- *               "Kernel: per-token causal decode".
+ *               "Kernel: per-token causal decode" (the sliding window applies per token), and the
+ *               Test Plan's window cases.
  */
 #include <math.h>
 #include <pthread.h>
@@ -105,25 +106,40 @@ int orc_plan_capacity(int num_seqs, int num_kv_heads, int cu_count, int budget_m
     return ORC_OK;
 }
 
+/* Key range a request reads: [lo_b, S_b).  Without a window, lo_b = 0.  With a window of W keys
+ * (each token sees the last W of its visible keys, [RDNA-29] Change 1: the window applies per
+ * token), the union over the request's L_b tokens starts at the first token's window:
+ * lo_b = max(0, S_b - (L_b - 1) - W). */
+static int64_t orc_read_start(int64_t S, int L, int window) {
+    if (window <= 0) return 0;
+    int64_t lo = S - (int64_t)(L - 1) - window;
+    return lo > 0 ? lo : 0;
+}
+
 /* Work plan ([ATOM-2366] sections 1 and 3: each request receives a partition count proportional to
  * its real context length, under the workgroup budget, clamped only at max_partitions; work
- * entries carry begin/end tiles and the request's context length, [ATOM-2366] review item 2).
+ * entries carry begin/end tiles and the request's context length, [ATOM-2366] review item 2;
+ * review "window logic": the plan must cover the key range the kernel reads under a window).
  *
  * Reading of the apportionment, which the pages leave open:
- *   tiles_b = ceil(S_b / T); requests with S_b = 0 get no partition;
+ *   the request reads keys [lo_b, S_b) (orc_read_start) and its tiles are the 256-token-aligned
+ *   tiles that range touches: [floor(lo_b / T), ceil(S_b / T)), tiles_b of them;
+ *   its length is E_b = S_b - lo_b (= S_b without a window); requests with E_b = 0 get no partition;
  *   every non-empty request gets one partition, and the capacity left over (C - B') is shared in
- *   proportion to S_b, rounded down:  parts_b = min(P, tiles_b, 1 + floor((C - B') S_b / W)),
- *   W = sum S_b;  any remainder is left unused.
+ *   proportion to E_b, rounded down:  parts_b = min(P, tiles_b, 1 + floor((C - B') E_b / W)),
+ *   W = sum E_b;  any remainder is left unused.
  * Slots are filled request by request; partition j of request b spans tiles
- * [floor(j tiles_b / parts_b), floor((j+1) tiles_b / parts_b)).  Unused slots hold (-1, 0, 0, 0).
+ * [t0_b + floor(j tiles_b / parts_b), t0_b + floor((j+1) tiles_b / parts_b)), t0_b = floor(lo_b / T).
+ * Unused slots hold (-1, 0, 0, 0).
  * work_info[slot] = (request, tile_begin, tile_end, S_b); reduce_info[b] = (first_slot, parts_b);
  * num_work = (used slots, tiles of the largest slot).
+ * cu (nullable) gives the query lengths L_b; it only matters with a window.
  */
-int orc_plan(const int32_t* context_lens, int num_seqs, int num_kv_heads, int cu_count,
-             int budget_mult, int max_partitions, int tile_tokens, int capacity,
-             int32_t* work_info, int32_t* reduce_info, int32_t* num_work) {
+int orc_plan(const int32_t* context_lens, const int32_t* cu, int num_seqs, int num_kv_heads,
+             int cu_count, int budget_mult, int max_partitions, int tile_tokens, int window,
+             int capacity, int32_t* work_info, int32_t* reduce_info, int32_t* num_work) {
     int32_t cap = 0;
-    if (tile_tokens < 1) return ORC_INVALID;
+    if (tile_tokens < 1 || window < 0) return ORC_INVALID;
     if (orc_plan_capacity(num_seqs, num_kv_heads, cu_count, budget_mult, max_partitions, &cap))
         return ORC_INVALID;
     if (capacity < cap) return ORC_INVALID;
@@ -133,8 +149,10 @@ int orc_plan(const int32_t* context_lens, int num_seqs, int num_kv_heads, int cu
     int64_t total = 0;        /* W */
     int64_t nonempty = 0;     /* B' */
     for (int b = 0; b < num_seqs; ++b) {
-        total += context_lens[b];
-        if (context_lens[b] > 0) nonempty += 1;
+        int L = cu ? cu[b + 1] - cu[b] : 1;
+        int64_t len = context_lens[b] - orc_read_start(context_lens[b], L, window);
+        total += len;
+        if (len > 0) nonempty += 1;
     }
     int64_t extra = (int64_t)cap - nonempty;
 
@@ -142,10 +160,14 @@ int orc_plan(const int32_t* context_lens, int num_seqs, int num_kv_heads, int cu
     int32_t largest = 0;
     for (int b = 0; b < num_seqs; ++b) {
         int64_t s = context_lens[b];
+        int L = cu ? cu[b + 1] - cu[b] : 1;
+        int64_t lo = orc_read_start(s, L, window);
+        int64_t len = s - lo;
+        int64_t t0 = lo / tile_tokens;
         int64_t parts = 0;
-        int64_t tiles = orc_ceil_div(s, tile_tokens);
-        if (s > 0) {
-            parts = 1 + (extra * s) / total;
+        int64_t tiles = len > 0 ? orc_ceil_div(s, tile_tokens) - t0 : 0;
+        if (len > 0) {
+            parts = 1 + (extra * len) / total;
             if (parts > tiles) parts = tiles;
             if (parts > max_partitions) parts = max_partitions;
         }
@@ -154,8 +176,8 @@ int orc_plan(const int32_t* context_lens, int num_seqs, int num_kv_heads, int cu
         for (int64_t j = 0; j < parts; ++j) {
             int32_t* w = work_info + 4 * (slot + j);
             w[0] = b;
-            w[1] = (int32_t)((j * tiles) / parts);
-            w[2] = (int32_t)(((j + 1) * tiles) / parts);
+            w[1] = (int32_t)(t0 + (j * tiles) / parts);
+            w[2] = (int32_t)(t0 + ((j + 1) * tiles) / parts);
             w[3] = (int32_t)s;
             if (w[2] - w[1] > largest) largest = w[2] - w[1];
         }
@@ -184,6 +206,7 @@ typedef struct {
     const int32_t* context_lens; int num_seqs;
     const int32_t* cu; /* nullable */
     double scale, k_scale, v_scale;
+    int window;        /* 0: none; W > 0: each token sees its last W visible keys */
 } orc_problem;
 
 /* Element (block, kv head, slot, d) of a paged cache laid out [num_blocks, Hkv, bs, D]. */
@@ -209,9 +232,16 @@ static void orc_rows_of(const orc_problem* p, int b, int* first_row, int* qlen) 
     }
 }
 
-/* Keys visible to token i of a request with L query tokens and KV length S:
+/* Keys visible to token i of a request with L query tokens and KV length S: the first
  * S - (L - 1 - i), the causal range of [RDNA-29] Change 1. */
 static int64_t orc_visible(int64_t S, int L, int i) { return S - (int64_t)(L - 1 - i); }
+
+/* Start of token i's range: with a window of W keys the token sees [n - W, n) of its n visible
+ * keys ([RDNA-29] Change 1: the sliding window applies per token); without one, [0, n). */
+static int64_t orc_window_start(const orc_problem* p, int64_t n) {
+    if (p->window <= 0) return 0;
+    return n - p->window > 0 ? n - p->window : 0;
+}
 
 /* softmax-weighted sum over key positions [lo, hi) for one (row, head):
  * returns the partial (m, l, acc[D]) with m = max score, l = sum exp(s - m), acc = sum exp(s-m) v.
@@ -276,7 +306,7 @@ static void orc_task_direct(orc_job* J, int b, int g, double* qv, double* scores
             double* o = J->out + ((int64_t)(row0 + i) * p->num_q_heads + h) * D;
             if (n <= 0) { for (int d = 0; d < D; ++d) o[d] = 0.0; continue; }
             double m, l;
-            orc_partial(p, b, row0 + i, h, 0, n, qv, scores, &m, &l, acc);
+            orc_partial(p, b, row0 + i, h, orc_window_start(p, n), n, qv, scores, &m, &l, acc);
             for (int d = 0; d < D; ++d) o[d] = acc[d] / l;
         }
     }
@@ -306,6 +336,7 @@ static void orc_task_split(orc_job* J, int b, int g, double* qv, double* scores,
                 int64_t hi = (int64_t)w[2] * J->tile_tokens;
                 if (hi > w[3]) hi = w[3];
                 if (hi > n) hi = n;
+                if (lo < orc_window_start(p, n)) lo = orc_window_start(p, n);
                 orc_partial(p, b, row0 + i, h, lo, hi, qv, scores, &pm[j], &pl[j], pacc + (int64_t)j * D);
             }
             double M = -INFINITY;
@@ -346,6 +377,7 @@ static void* orc_worker(void* arg) {
 }
 
 static int orc_check(const orc_problem* p) {
+    if (p->window < 0) return ORC_INVALID;
     if (p->num_q_heads < 1 || p->num_kv_heads < 1 || p->num_q_heads % p->num_kv_heads) return ORC_INVALID;
     if (p->head_dim < 1 || p->block_size < 1 || p->num_seqs < 0 || p->num_rows < 0) return ORC_INVALID;
     int rows_used = p->cu ? p->cu[p->num_seqs] : p->num_seqs;
@@ -389,12 +421,12 @@ static int orc_run(orc_problem* p, int mode, const int32_t* work, const int32_t*
     const void *q, int q_dtype, int num_rows, int num_q_heads, int head_dim, const void *k,      \
         const void *v, int kv_dtype, int num_blocks, int num_kv_heads, int block_size,           \
         const int32_t *block_tables, int max_blocks, const int32_t *context_lens, int num_seqs,  \
-        const int32_t *cu, double scale, double k_scale, double v_scale
+        const int32_t *cu, double scale, double k_scale, double v_scale, int window
 
 #define ORC_FILL(p)                                                                               \
     orc_problem p = {q, q_dtype, num_rows, num_q_heads, head_dim, k, v, kv_dtype, num_blocks,     \
                      num_kv_heads, block_size, block_tables, max_blocks, context_lens, num_seqs,  \
-                     cu, scale, k_scale, v_scale}
+                     cu, scale, k_scale, v_scale, window}
 
 /* O2: direct softmax attention of every row over its visible keys, read through the block table. */
 int orc_attention_direct(ORC_PROBLEM_ARGS, double* out, int nthreads) {
@@ -439,7 +471,7 @@ int orc_attention_rows(ORC_PROBLEM_ARGS, const int32_t* rows, const int32_t* hea
         int64_t n = orc_visible(context_lens[owner], L, tok);
         if (n <= 0) continue;
         double m, l;
-        orc_partial(&p, owner, r, h, 0, n, qv, scores, &m, &l, o);
+        orc_partial(&p, owner, r, h, orc_window_start(&p, n), n, qv, scores, &m, &l, o);
         for (int d = 0; d < D; ++d) o[d] /= l;
     }
     free(qv); free(scores);

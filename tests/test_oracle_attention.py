@@ -281,3 +281,109 @@ def test_rejects_out_of_range_pages():
     pb["bt"][0, 1] = pb["kc"].shape[0]
     with pytest.raises(oracle.OracleError):
         _direct(pb, 0.25)
+
+
+# ---------------------------------------------------------------------------------------------
+# sliding window: token i with n visible keys sees [max(0, n - W), n) (opengfx1030/vllm-rdna PR #29,
+# Change 1: the sliding window applies per token; Test Plan: windows 0, 1, 3, 50)
+# ---------------------------------------------------------------------------------------------
+
+def _sdpa_window_reference(pb, Hq, scale, W):
+    """torch SDPA in float64 on the dense K/V with an explicit band mask n - W <= p < n."""
+    q = pb["q"]
+    R, _, D = q.shape
+    out = np.zeros((R, Hq, D))
+    for b, s in enumerate(pb["ctx"]):
+        r0, L = (b, 1) if pb["cu"] is None else (int(pb["cu"][b]), int(pb["cu"][b + 1] - pb["cu"][b]))
+        if L == 0 or s == 0:
+            continue
+        qq = torch.from_numpy(q[r0:r0 + L].astype(np.float64)).permute(1, 0, 2)[None]
+        kk = torch.from_numpy(pb["kd"][b].astype(np.float64)).permute(1, 0, 2)[None]
+        vv = torch.from_numpy(pb["vd"][b].astype(np.float64)).permute(1, 0, 2)[None]
+        n = int(s) - (L - 1 - torch.arange(L))[:, None]
+        p = torch.arange(int(s))[None, :]
+        mask = (p < n) & (p >= n - W)
+        visible = mask.any(dim=1).numpy()
+        mask[~mask.any(dim=1)] = True          # rows with no key: computed, then zeroed below
+        o = F.scaled_dot_product_attention(qq, kk, vv, attn_mask=mask, scale=scale, enable_gqa=True)
+        o = o[0].permute(1, 0, 2).numpy()
+        o[~visible] = 0.0
+        out[r0:r0 + L] = o
+    return out
+
+
+WINDOW_CASES = [
+    # (ctx, qlens, Hq, Hkv, D, bs, pad_rows, W)
+    ([1, 17, 100, 300], None, 4, 1, 64, 16, 0, 1),
+    ([37, 5, 64, 129], [3, 1, 2, 4], 8, 2, 32, 16, 2, 3),
+    ([2, 0, 7, 90, 3], [3, 2, 1, 3, 0], 6, 1, 16, 64, 3, 50),
+    ([513, 260], [2, 3], 12, 4, 128, 128, 1, 50),
+    ([700, 33], [4, 2], 4, 2, 64, 16, 0, 256),
+]
+
+
+@pytest.mark.parametrize("case", range(len(WINDOW_CASES)))
+def test_window_direct_matches_library_sdpa(case):
+    ctx, qlens, Hq, Hkv, D, bs, pad, W = WINDOW_CASES[case]
+    rng = np.random.default_rng(40 + case)
+    pb = _problem(rng, ctx, qlens, Hq, Hkv, D, bs, pad)
+    scale = 1.0 / math.sqrt(D)
+    got = _direct(pb, scale, window=W)
+    ref = _sdpa_window_reference(pb, Hq, scale, W)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-10)
+
+
+def test_window_of_one_returns_the_last_visible_value_row():
+    rng = np.random.default_rng(41)
+    pb = _problem(rng, [9, 33, 1], [2, 3, 1], 4, 2, 16, 16)
+    out = _direct(pb, 0.25, window=1)
+    for b, s in enumerate(pb["ctx"]):
+        r0, L = int(pb["cu"][b]), int(pb["cu"][b + 1] - pb["cu"][b])
+        for i in range(L):
+            n = int(s) - (L - 1 - i)
+            for h in range(4):
+                assert (out[r0 + i, h] == pb["vd"][b][n - 1, h // 2].astype(np.float64)).all()
+
+
+def test_window_at_least_the_context_changes_nothing():
+    rng = np.random.default_rng(42)
+    pb = _problem(rng, [37, 5, 64, 129], [3, 1, 2, 4], 8, 2, 32, 16, 2)
+    full = _direct(pb, 0.2)
+    for W in (129, 130, 10_000):
+        assert np.array_equal(_direct(pb, 0.2, window=W), full)
+
+
+def test_window_range_per_token():
+    rng = np.random.default_rng(43)
+    ctx, L, W = 60, 3, 7
+    pb = _problem(rng, [ctx], [L], 4, 1, 16, 16)
+    ref = _direct(pb, 0.25, window=W)
+    for i in range(L):
+        n = ctx - (L - 1 - i)
+        for pos, inside in ((n - W - 1, False), (n - W, True)):
+            kd = [k.copy() for k in pb["kd"]]
+            vd = [v.copy() for v in pb["vd"]]
+            kd[0][pos] += 3.0
+            vd[0][pos] -= 5.0
+            pb2 = dict(pb, kd=kd, vd=vd)
+            pb2["kc"], pb2["vc"], pb2["bt"] = _paged_from_dense(kd, vd, 16, np.random.default_rng(98))
+            got = _direct(pb2, 0.25, window=W)
+            changed = np.abs(got[i] - ref[i]).max() > 1e-6
+            assert changed == inside, (i, pos, inside)
+
+
+@pytest.mark.parametrize("case", range(len(WINDOW_CASES)))
+@pytest.mark.parametrize("T,P,cu_count,mult", [(16, 1, 256, 2), (64, 8, 7, 3), (256, 256, 256, 2),
+                                               (16, 256, 64, 1)])
+def test_window_split_equals_direct(case, T, P, cu_count, mult):
+    ctx, qlens, Hq, Hkv, D, bs, pad, W = WINDOW_CASES[case]
+    if T % bs:
+        pytest.skip("tile not a multiple of the page")
+    rng = np.random.default_rng(50 + case)
+    pb = _problem(rng, ctx, qlens, Hq, Hkv, D, bs, pad)
+    scale = 1.0 / math.sqrt(D)
+    work, red, nw = oracle.plan(pb["ctx"], Hkv, cu_count, mult, P, T, cu_query_lens=pb["cu"], window=W)
+    split = oracle.attention_split(pb["q"], "f32", pb["kc"], pb["vc"], "f32", pb["bt"], pb["ctx"],
+                                   pb["cu"], scale, work, red, T, window=W)
+    direct = _direct(pb, scale, window=W)
+    np.testing.assert_allclose(split, direct, rtol=0, atol=1e-10)

@@ -205,3 +205,75 @@ def test_rejects_bad_arguments():
         oracle.plan([5], 0)
     with pytest.raises(oracle.OracleError):
         oracle.plan([5], 1, tile_tokens=0)
+
+
+# ---------------------------------------------------------------------------------------------
+# with a sliding window the plan covers each request's windowed key range (ROCm/ATOM PR #2366
+# review, the window logic: plan and kernel must agree on the range once windows are allowed)
+# ---------------------------------------------------------------------------------------------
+
+def _read_range(s, L, W):
+    lo = max(0, s - (L - 1) - W) if W > 0 else 0
+    return lo, s
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_window_plan_covers_the_windowed_range(seed):
+    rng = np.random.default_rng(3000 + seed)
+    B = int(rng.choice([1, 3, 16, 40, 200]))
+    W = int(rng.choice([1, 3, 50, 700, 5000]))
+    T = int(rng.choice([16, 64, 256]))
+    P = int(rng.choice([1, 8, 256]))
+    ctx = np.where(rng.random(B) < 0.2, 0, rng.integers(1, 40000, size=B))
+    ql = rng.integers(1, 5, size=B)
+    cu = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+    work, red, nw, largest = oracle.plan(ctx, 2, 256, 2, P, T, with_largest=True, cu_query_lens=cu, window=W)
+    C = oracle.plan_capacity(B, 2, 256, 2, P)
+    lens = []
+    for b in range(B):
+        lo, hi = _read_range(int(ctx[b]), int(ql[b]), W)
+        lens.append(hi - lo)
+        first, parts = int(red[b, 0]), int(red[b, 1])
+        if hi - lo == 0:
+            assert parts == 0
+            continue
+        t0, t1 = lo // T, -(-hi // T)
+        assert 1 <= parts <= min(P, t1 - t0)
+        covered = t0
+        for j in range(parts):
+            w = work[first + j].tolist()
+            assert w[0] == b and w[3] == ctx[b] and w[1] == covered and w[2] > w[1]
+            covered = w[2]
+        assert covered == t1
+    assert red[:, 1].sum() == nw <= C
+    # partition counts by search, weighted by the windowed lengths
+    tot = sum(lens)
+    extra = C - sum(1 for x in lens if x > 0)
+    for b in range(B):
+        if lens[b] == 0:
+            continue
+        k = 0
+        while (k + 1) * tot <= extra * lens[b]:
+            k += 1
+        lo, hi = _read_range(int(ctx[b]), int(ql[b]), W)
+        assert red[b, 1] == min(P, -(-hi // T) - lo // T, 1 + k)
+    assert largest == max([int(w[2] - w[1]) for w in work[:nw]], default=0)
+
+
+def test_window_zero_or_wide_equals_the_plain_plan():
+    rng = np.random.default_rng(77)
+    ctx = rng.integers(0, 100000, size=50)
+    ql = rng.integers(1, 4, size=50)
+    cu = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+    plain = oracle.plan(ctx, 2, with_largest=True)
+    for W in (0, 200000):
+        got = oracle.plan(ctx, 2, with_largest=True, cu_query_lens=cu, window=W)
+        assert all(np.array_equal(a, b) for a, b in zip(got, plain))
+
+
+def test_window_plan_hand_worked():
+    # S = 1000, L = 2, W = 300: keys [699, 1000) -> tiles [2, 4) at T = 256; a lone request at Hkv 1
+    # has C = 512 slots, so parts = min(256, 2, 1 + 511) = 2: tiles [2, 3) and [3, 4)
+    work, red, nw = oracle.plan([1000], 1, cu_query_lens=[0, 2], window=300)
+    assert nw == 2 and red.tolist() == [[0, 2]]
+    assert work[:2].tolist() == [[0, 2, 3, 1000], [0, 3, 4, 1000]]
