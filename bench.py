@@ -54,7 +54,7 @@ def counter_traffic():
     return c.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(pool, budget_s: float, max_steps: int):
+def cpu_baseline(pool, budget_s: float, max_steps: int, window: int = 0):
     """The CPU oracle (direct fp64 attention over the gathered pages) on a bounded sample of steps."""
     import oracle
 
@@ -80,9 +80,10 @@ def cpu_baseline(pool, budget_s: float, max_steps: int):
         q = pool.q[i].cpu().view(torch.int16).numpy().view(np.uint16)
         t0 = time.perf_counter()
         oracle.attention_direct(q, "bf16", k, v, "bf16", remap, ctx.astype(np.int32), None, pool.scale,
-                                threads=threads)
+                                threads=threads, window=window)
         spent += time.perf_counter() - t0
-        done_bytes += int(ctx.sum()) * k.shape[1] * 2 * k.shape[3] * 2
+        keys = np.minimum(ctx, window) if window > 0 else ctx
+        done_bytes += int(keys.sum()) * k.shape[1] * 2 * k.shape[3] * 2
         n += 1
         if spent >= budget_s:
             break
@@ -103,6 +104,9 @@ def main():
     ap.add_argument("--graph", action="store_true", help="also time a HIP-graph replay of the steps")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a 1 GiB device copy first (reference kernel for the HBM counters)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window in keys per query token (0 = none); the bytes counted are the "
+                         "windowed ranges")
     ap.add_argument("--workload", choices=("skewed", "sparse"), default="skewed",
                     help="skewed: the 32-request agentic batch (default, the headline metric); "
                          "sparse: 16 near-uniform top-k requests with a partition cap of 8")
@@ -142,7 +146,9 @@ def main():
     step = DecodeStep(num_seqs=B_, num_rows=B_, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
                       max_q_len=1, out_dtype=torch.bfloat16, device=dev,
                       plan=PlanConfig(cu_count=cu_count, max_partitions=max_parts))
-    kv_bytes = pool.steps.sum(axis=1) * Hkv * 2 * D * 2                 # per step
+    win = args.window
+    keys = np.minimum(pool.steps, win) if win > 0 else pool.steps        # one query token per request
+    kv_bytes = keys.sum(axis=1) * Hkv * 2 * D * 2                         # per step
     stream = torch.cuda.current_stream()
 
     def run(i, ev=None, mode="attention"):
@@ -153,15 +159,15 @@ def main():
         ctx = pool.context_lens[i]
         if mode == "attention":
             step.attention(pool.q[i], pool.k_cache, pool.v_cache, "bf16", pool.block_tables[i], ctx,
-                           scale=pool.scale)
+                           scale=pool.scale, sliding_window=win)
             return
         if ev is not None:
             ev[0].record(stream)
-        step.plan(ctx)
+        step.plan(ctx, sliding_window=win)
         if ev is not None:
             ev[1].record(stream)
         step.decode(pool.q[i], pool.k_cache, pool.v_cache, "bf16", pool.block_tables[i], ctx,
-                    scale=pool.scale, merge=mode == "fused")
+                    scale=pool.scale, merge=mode == "fused", sliding_window=win)
         if ev is not None:
             ev[2].record(stream)
         if mode == "three":
@@ -219,14 +225,14 @@ def main():
     plans = []
     for i in range(nsteps):
         w, r, n = B.pa_plan(pool.context_lens[i], Hkv, cu_count=cu_count, max_partitions=max_parts,
-                            capacity=step.capacity)
+                            capacity=step.capacity, sliding_window=win)
         plans.append((w, n))
     torch.cuda.synchronize()
 
     def decode_only(i):
         i %= nsteps
         B.pa_decode(pool.q[i], pool.k_cache, pool.v_cache, "bf16", pool.block_tables[i], pool.context_lens[i],
-                    plans[i][0], plans[i][1], step.workspace, scale=pool.scale)
+                    plans[i][0], plans[i][1], step.workspace, scale=pool.scale, sliding_window=win)
 
     for i in range(8):
         decode_only(i)
@@ -271,10 +277,14 @@ def main():
     gbps = bytes_done / (plain_ms * 1e-3) / 1e9
     dec_gbps = float(kv_bytes.mean()) / (decode_ms * 1e-3) / 1e9
     traffic = counter_traffic()
-    if args.workload == "skewed":
+    if args.workload == "skewed" and win == 0:
         metric = METRIC
         workload = ("skewed 32-request bf16 decode, Hq 16 / Hkv 2, D 128, page 16, 128 stratified steps "
                     "over a 4 GiB pool")
+    elif args.workload == "skewed":
+        metric = f"µs/step + achieved KV-read HBM GB/s (% peak), skewed 32-req bf16 decode, window {win}"
+        workload = (f"skewed 32-request bf16 decode with a {win}-key sliding window, Hq 16 / Hkv 2, D 128, "
+                    "page 16, 128 stratified steps over a 4 GiB pool; bytes = windowed keys")
     else:
         metric = "µs/step + achieved KV-read HBM GB/s (% peak), sparse top-k 16-req bf16 decode, cap 8"
         workload = ("sparse top-k bf16 decode: 16 requests of 2048 selected + 1..256 local tokens, "
@@ -292,8 +302,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": workload,
+        "config": {"workload": workload, "sliding_window": win,
                    "num_seqs": B_, "q_len": 1, "mean_tokens_per_step": round(float(pool.steps.sum(1).mean()), 1),
+                   "mean_keys_read_per_step": round(float(keys.sum(1).mean()), 1),
                    "planner": {"budget": "2 x CU", "cu_count": cu_count, "max_partitions": max_parts,
                                "tile_tokens": 256}},
         "us_per_step": round(us_step, 2),
@@ -310,7 +321,8 @@ def main():
         "timed_wall_s": round(wall, 3),
         "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic if args.workload == "skewed" else None, "kernel": "pa_decode",
+                     "traffic": traffic if args.workload == "skewed" and win == 0 else None,
+                     "kernel": "pa_decode",
                      "duration_us": round(decode_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": round(float(kv_bytes.mean()), 1)},
         "hip_graph": graph,
@@ -318,7 +330,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(pool, args.cpu_seconds, nsteps)
+        result["cpu_baseline"] = cpu_baseline(pool, args.cpu_seconds, nsteps, win)
     print(json.dumps(result), flush=True)
 
 

@@ -10,7 +10,9 @@
  *              "adapt the FlyDSL paged decode to aiter #5809 (explicit work plans)", Design).
  *   pa_decode  split-KV grouped-query decode over a block-table KV cache: one partial softmax state per
  *              (plan slot, query token, query head).  Query token i of a request with L query tokens
- *              and KV length S sees keys [0, S - (L - 1 - i)) (opengfx1030/vllm-rdna PR #29, Change 1).
+ *              and KV length S sees keys [0, n), n = S - (L - 1 - i), or with a sliding window of W
+ *              keys [max(0, n - W), n): the window applies per token (opengfx1030/vllm-rdna PR #29,
+ *              Change 1).
  *   pa_merge   log-sum-exp merge of a request's partials into the output rows; rows past the last
  *              cumulative query length and rows with no visible key are written as exact zeros
  *              (same vllm-rdna page, Change 1; ATOM #2366 review, "Claims checked and not upheld").
@@ -99,29 +101,36 @@ size_t pa_workspace_bytes(int32_t capacity, int32_t max_q_len, int32_t num_q_hea
 
 /*
  * Build the work plan on the device from context_lens (device, [num_seqs]).
- *   tile_tokens   partition granularity in tokens (256 in the pages' deployment)
- *   capacity      length of work_info; must be >= pa_plan_capacity(...) for the same arguments
- * Apportionment: every request with S_b > 0 gets
- *   min(max_partitions, ceil(S_b / tile_tokens), 1 + floor((C - B') S_b / W))
- * partitions, C = the capacity formula, B' = number of requests with S_b > 0, W = sum S_b (64-bit);
- * requests with S_b = 0 get none.  Partition j of request b covers tiles
- * [floor(j tiles_b / parts_b), floor((j + 1) tiles_b / parts_b)).  Every slot of work_info is
+ *   cu_query_lens   [num_seqs + 1] or NULL; read only with a sliding window (query lengths L_b)
+ *   tile_tokens     partition granularity in tokens (256 in the pages' deployment)
+ *   sliding_window  0 = none; W > 0: the plan covers only the keys the decode reads under a window
+ *                   of W keys per query token (ROCm/ATOM PR #2366 review: plan and kernel must agree
+ *                   on the window)
+ *   capacity        length of work_info; must be >= pa_plan_capacity(...) for the same arguments
+ * Request b reads keys [lo_b, S_b): lo_b = 0 without a window, else max(0, S_b - (L_b - 1) - W).
+ * Its tiles are those the range touches, [t0_b, t1_b) = [floor(lo_b / T), ceil(S_b / T)), and its
+ * length E_b = S_b - lo_b.  Apportionment: every request with E_b > 0 gets
+ *   min(max_partitions, t1_b - t0_b, 1 + floor((C - B') E_b / W))
+ * partitions, C = the capacity formula, B' = number of requests with E_b > 0, W = sum E_b (64-bit);
+ * the others get none.  Partition j of request b covers tiles
+ * t0_b + [floor(j tiles_b / parts_b), floor((j + 1) tiles_b / parts_b)), tiles_b = t1_b - t0_b.
+ * Without a window this is the plain rule over [0, S_b).  Every slot of work_info is
  * rewritten (unused ones to (-1, 0, 0, 0)), so a plan never carries data from an earlier call.
  * num_work receives the number of used slots and the tile count of the largest slot.
  * Negative S_b (a precondition violation) are planned as 0.
  * Errors: PA_INVALID_ARG (null pointers, num_seqs < 0, arguments < 1), PA_UNSUPPORTED
  * (num_seqs > PA_MAX_SEQS), PA_CAPACITY (capacity too small), PA_HIP_ERROR (launch failure).
  */
-pa_status pa_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
-                  int32_t cu_count, int32_t budget_mult, int32_t max_partitions,
-                  int32_t tile_tokens, int32_t capacity, int32_t* work_info, int32_t* reduce_info,
-                  int32_t* num_work, void* stream);
+pa_status pa_plan(const int32_t* context_lens, const int32_t* cu_query_lens, int32_t num_seqs,
+                  int32_t num_kv_heads, int32_t cu_count, int32_t budget_mult, int32_t max_partitions,
+                  int32_t tile_tokens, int32_t sliding_window, int32_t capacity, int32_t* work_info,
+                  int32_t* reduce_info, int32_t* num_work, void* stream);
 
 /*
  * Split-KV decode: for every used plan slot w = (b, tile_begin, tile_end, .) and kv head g, one
  * workgroup computes, for each query token i of request b and each query head h of group g, the
  * softmax state of the keys [tile_begin x T, min(tile_end x T, S_b)) intersected with the token's
- * visible range [0, S_b - (L_b - 1 - i)):
+ * visible range [lo_i, n_i), n_i = S_b - (L_b - 1 - i), lo_i = 0 or, with a window, max(0, n_i - W):
  *   m = max score, l = sum exp(score - m), acc = sum exp(score - m) v,   score = scale x k_scale x (q . k)
  * (V is multiplied by v_scale), stored unnormalised in the workspace; a slot/token with no visible
  * key stores l = 0, acc = 0.  S_b is context_lens[b]; the plan must have been built from the same
@@ -133,6 +142,8 @@ pa_status pa_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_
  *   context_lens               [num_seqs]
  *   cu_query_lens              [num_seqs + 1] or NULL (then row b is request b's only token)
  *   max_q_len                  upper bound on every request's query length (1 when cu is NULL)
+ *   sliding_window             0 = none; W > 0: token i sees only keys [max(0, n_i - W), n_i); the plan
+ *                              must have been built with the same window
  *   scale, k_scale, v_scale    softmax scale (typically 1/sqrt(head_dim)) and per-tensor dequant scales
  *   work_info, reduce_info,    the plan from pa_plan (capacity slots); reduce_info is only read when
  *   num_work                   out is given and may then not be NULL
@@ -156,10 +167,10 @@ pa_status pa_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t n
                     int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
                     const int32_t* block_tables, int32_t max_blocks_per_seq,
                     const int32_t* context_lens, int32_t num_seqs, const int32_t* cu_query_lens,
-                    int32_t max_q_len, float scale, float k_scale, float v_scale,
-                    const int32_t* work_info, const int32_t* reduce_info, const int32_t* num_work,
-                    int32_t capacity, int32_t tile_tokens, void* workspace, size_t workspace_bytes,
-                    void* out, pa_dtype out_dtype, void* stream);
+                    int32_t max_q_len, int32_t sliding_window, float scale, float k_scale,
+                    float v_scale, const int32_t* work_info, const int32_t* reduce_info,
+                    const int32_t* num_work, int32_t capacity, int32_t tile_tokens, void* workspace,
+                    size_t workspace_bytes, void* out, pa_dtype out_dtype, void* stream);
 
 /*
  * Log-sum-exp merge.  For output row r and head h: the owning request b is found by binary search
@@ -180,7 +191,8 @@ pa_status pa_merge(int32_t num_rows, int32_t num_q_heads, int32_t head_dim, int3
  * by pa_decode (out = NULL) and pa_merge with the same arguments: work_info, reduce_info and num_work
  * receive the plan bit for bit as pa_plan writes it, the workspace the same partial states, and out
  * the same rows.  Arguments are those of the three calls (cu_count, budget_mult, max_partitions as
- * for pa_plan; capacity as for pa_plan and pa_decode); the plan buffers are outputs here.
+ * for pa_plan; capacity and sliding_window as for pa_plan and pa_decode); the plan buffers are
+ * outputs here.
  * With num_seqs <= PA_INLINE_PLAN_SEQS and a bf16 or fp8 cache, the decode launch evaluates the
  * planner's rule itself (every workgroup over all requests, one request per thread) and stores the
  * plan, so the step is two launches (decode, merge); otherwise it is the three launches.  The
@@ -192,8 +204,8 @@ pa_status pa_attention(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_
                        int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
                        const int32_t* block_tables, int32_t max_blocks_per_seq,
                        const int32_t* context_lens, int32_t num_seqs, const int32_t* cu_query_lens,
-                       int32_t max_q_len, float scale, float k_scale, float v_scale,
-                       int32_t cu_count, int32_t budget_mult, int32_t max_partitions,
+                       int32_t max_q_len, int32_t sliding_window, float scale, float k_scale,
+                       float v_scale, int32_t cu_count, int32_t budget_mult, int32_t max_partitions,
                        int32_t tile_tokens, int32_t capacity, int32_t* work_info,
                        int32_t* reduce_info, int32_t* num_work, void* workspace,
                        size_t workspace_bytes, void* out, pa_dtype out_dtype, void* stream);

@@ -56,17 +56,17 @@ def load(path: str = LIB_PATH):
     lib.pa_plan_capacity.restype = ctypes.c_int
     lib.pa_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.pa_workspace_bytes.restype = ctypes.c_size_t
-    lib.pa_plan.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]
+    lib.pa_plan.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]
     lib.pa_plan.restype = ctypes.c_int
     lib.pa_decode.argtypes = [vp, ctypes.c_int, i32, i32, i32, vp, vp, ctypes.c_int, i32, i32, i32,
-                              vp, i32, vp, i32, vp, i32, f32, f32, f32, vp, vp, vp, i32, i32, vp,
+                              vp, i32, vp, i32, vp, i32, i32, f32, f32, f32, vp, vp, vp, i32, i32, vp,
                               ctypes.c_size_t, vp, ctypes.c_int, vp]
     lib.pa_decode.restype = ctypes.c_int
     lib.pa_merge.argtypes = [i32, i32, i32, i32, vp, i32, vp, i32, vp, ctypes.c_size_t, vp,
                              ctypes.c_int, vp]
     lib.pa_merge.restype = ctypes.c_int
     lib.pa_attention.argtypes = [vp, ctypes.c_int, i32, i32, i32, vp, vp, ctypes.c_int, i32, i32, i32,
-                                 vp, i32, vp, i32, vp, i32, f32, f32, f32, i32, i32, i32, i32, i32,
+                                 vp, i32, vp, i32, vp, i32, i32, f32, f32, f32, i32, i32, i32, i32, i32,
                                  vp, vp, vp, vp, ctypes.c_size_t, vp, ctypes.c_int, vp]
     lib.pa_attention.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
@@ -135,14 +135,19 @@ def pa_device_cu_count(device: Optional[int] = None) -> int:
 def pa_plan(context_lens: torch.Tensor, num_kv_heads: int, *, cu_count: int, budget_mult: int = 2,
             max_partitions: int = 256, tile_tokens: int = 256, capacity: Optional[int] = None,
             work_info: Optional[torch.Tensor] = None, reduce_info: Optional[torch.Tensor] = None,
-            num_work: Optional[torch.Tensor] = None, stream=None
-            ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+            num_work: Optional[torch.Tensor] = None, cu_query_lens: Optional[torch.Tensor] = None,
+            sliding_window: int = 0, stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Plan on the device.  Returns (work_info [capacity, 4], reduce_info [B, 2], num_work [2] =
     (used slots, tiles of the largest slot)), all int32 on the device of context_lens; passed-in
-    buffers are refilled in place."""
+    buffers are refilled in place.  With a sliding window the plan covers the windowed key ranges
+    (cu_query_lens gives the query lengths)."""
     _need(context_lens, "context_lens", torch.int32)
     dev = context_lens.device
     B = int(context_lens.shape[0])
+    if cu_query_lens is not None:
+        _need(cu_query_lens, "cu_query_lens", torch.int32, dev)
+        if cu_query_lens.shape[0] != B + 1:
+            raise ValueError("cu_query_lens must be [num_seqs + 1]")
     if capacity is None:
         capacity = pa_plan_capacity(B, num_kv_heads, cu_count, budget_mult, max_partitions)
     if work_info is None:
@@ -156,9 +161,9 @@ def pa_plan(context_lens: torch.Tensor, num_kv_heads: int, *, cu_count: int, bud
     _need(num_work, "num_work", torch.int32, dev)
     if work_info.numel() < 4 * capacity or reduce_info.numel() < 2 * B or num_work.numel() < 2:
         raise ValueError("plan buffers smaller than capacity / num_seqs / 2")
-    _check(load().pa_plan(_ptr(context_lens), B, num_kv_heads, cu_count, budget_mult, max_partitions,
-                          tile_tokens, capacity, _ptr(work_info), _ptr(reduce_info), _ptr(num_work),
-                          _stream(stream)), "pa_plan")
+    _check(load().pa_plan(_ptr(context_lens), _ptr(cu_query_lens), B, num_kv_heads, cu_count, budget_mult,
+                          max_partitions, tile_tokens, sliding_window, capacity, _ptr(work_info),
+                          _ptr(reduce_info), _ptr(num_work), _stream(stream)), "pa_plan")
     return work_info, reduce_info, num_work
 
 
@@ -168,7 +173,7 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_
               cu_query_lens: Optional[torch.Tensor] = None, max_q_len: int = 1,
               k_scale: float = 1.0, v_scale: float = 1.0, tile_tokens: int = 256,
               reduce_info: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-              stream=None) -> None:
+              sliding_window: int = 0, stream=None) -> None:
     """Split-KV decode into the workspace (see include/pa.h).  kv_dtype is "f32", "bf16" or
     "fp8" (uint8 tensors holding OCP e4m3fn codes).  With ``out`` (and ``reduce_info``) the merge
     runs in the same call; the workspace must then have been allocated zero-filled."""
@@ -206,7 +211,7 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_
     _check(load().pa_decode(_ptr(q), PA_F32 if q.dtype == torch.float32 else PA_BF16, R, Hq, D,
                             _ptr(k_cache), _ptr(v_cache), _DTYPE_OF_NAME[kv_dtype], nb, Hkv, bs,
                             _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), B,
-                            _ptr(cu_query_lens), max_q_len, scale, k_scale, v_scale,
+                            _ptr(cu_query_lens), max_q_len, sliding_window, scale, k_scale, v_scale,
                             _ptr(work_info), _ptr(reduce_info), _ptr(num_work), capacity, tile_tokens,
                             _ptr(workspace), workspace.numel(), _ptr(out),
                             PA_F32 if q.dtype == torch.float32 else PA_BF16, _stream(stream)),
@@ -238,7 +243,8 @@ def pa_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
                  out: torch.Tensor, *, scale: float, cu_count: int, budget_mult: int = 2,
                  max_partitions: int = 256, tile_tokens: int = 256,
                  cu_query_lens: Optional[torch.Tensor] = None, max_q_len: int = 1,
-                 k_scale: float = 1.0, v_scale: float = 1.0, stream=None) -> None:
+                 k_scale: float = 1.0, v_scale: float = 1.0, sliding_window: int = 0,
+                 stream=None) -> None:
     """Plan, decode and merge in one call (see include/pa.h); the plan buffers are outputs."""
     dev = q.device
     if q.dtype not in (torch.float32, torch.bfloat16):
@@ -272,7 +278,8 @@ def pa_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
     qd = PA_F32 if q.dtype == torch.float32 else PA_BF16
     _check(load().pa_attention(_ptr(q), qd, R, Hq, D, _ptr(k_cache), _ptr(v_cache), _DTYPE_OF_NAME[kv_dtype],
                                nb, Hkv, bs, _ptr(block_tables), int(block_tables.shape[1]),
-                               _ptr(context_lens), B, _ptr(cu_query_lens), max_q_len, scale, k_scale,
-                               v_scale, cu_count, budget_mult, max_partitions, tile_tokens, capacity,
+                               _ptr(context_lens), B, _ptr(cu_query_lens), max_q_len, sliding_window,
+                               scale, k_scale, v_scale, cu_count, budget_mult, max_partitions,
+                               tile_tokens, capacity,
                                _ptr(work_info), _ptr(reduce_info), _ptr(num_work), _ptr(workspace),
                                workspace.numel(), _ptr(out), qd, _stream(stream)), "pa_attention")

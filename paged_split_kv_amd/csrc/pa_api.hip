@@ -36,9 +36,9 @@ namespace {
 
 pa_status check_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
                      int32_t cu_count, int32_t budget_mult, int32_t max_partitions, int32_t tile_tokens,
-                     int32_t capacity, const int32_t* work_info, const int32_t* reduce_info,
-                     const int32_t* num_work, int32_t* cap) {
-    if (num_seqs < 0 || tile_tokens < 1 || capacity < 0) return PA_INVALID_ARG;
+                     int32_t sliding_window, int32_t capacity, const int32_t* work_info,
+                     const int32_t* reduce_info, const int32_t* num_work, int32_t* cap) {
+    if (num_seqs < 0 || tile_tokens < 1 || capacity < 0 || sliding_window < 0) return PA_INVALID_ARG;
     if (!num_work || (num_seqs > 0 && (!context_lens || !reduce_info)) || (capacity > 0 && !work_info))
         return PA_INVALID_ARG;
     if ((work_info && !aligned(work_info, 16)) || (reduce_info && !aligned(reduce_info, 8)) ||
@@ -58,13 +58,14 @@ pa_status prepare_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int3
                          int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
                          const int32_t* block_tables, int32_t max_blocks_per_seq,
                          const int32_t* context_lens, int32_t num_seqs, const int32_t* cu_query_lens,
-                         int32_t max_q_len, float scale, float k_scale, float v_scale,
-                         const int32_t* work_info, const int32_t* reduce_info, const int32_t* num_work,
-                         int32_t capacity, int32_t tile_tokens, void* workspace, size_t workspace_bytes,
-                         void* out, pa_dtype out_dtype, pa::DecodeArgs* args, bool* nothing) {
+                         int32_t max_q_len, int32_t sliding_window, float scale, float k_scale,
+                         float v_scale, const int32_t* work_info, const int32_t* reduce_info,
+                         const int32_t* num_work, int32_t capacity, int32_t tile_tokens, void* workspace,
+                         size_t workspace_bytes, void* out, pa_dtype out_dtype, pa::DecodeArgs* args,
+                         bool* nothing) {
     if (num_rows < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_blocks < 0 || num_seqs < 0 ||
         max_blocks_per_seq < 0 || max_q_len < 1 || capacity < 0 || tile_tokens < 1 || head_dim < 1 ||
-        block_size < 1)
+        block_size < 1 || sliding_window < 0)
         return PA_INVALID_ARG;
     if (q_dtype != PA_F32 && q_dtype != PA_BF16) return PA_INVALID_ARG;
     if (kv_dtype != PA_F32 && kv_dtype != PA_BF16 && kv_dtype != PA_FP8_E4M3) return PA_INVALID_ARG;
@@ -126,6 +127,7 @@ pa_status prepare_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int3
     a.tile_tokens = tile_tokens;
     a.score_scale_log2 = scale * k_scale * pa::kLog2e;
     a.v_scale = v_scale;
+    a.window = sliding_window;
     return PA_OK;
 }
 
@@ -183,17 +185,18 @@ size_t pa_workspace_bytes(int32_t capacity, int32_t max_q_len, int32_t num_q_hea
            pa::workspace_counter_bytes(capacity, num_q_heads);
 }
 
-pa_status pa_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
-                  int32_t cu_count, int32_t budget_mult, int32_t max_partitions,
-                  int32_t tile_tokens, int32_t capacity, int32_t* work_info, int32_t* reduce_info,
-                  int32_t* num_work, void* stream) {
+pa_status pa_plan(const int32_t* context_lens, const int32_t* cu_query_lens, int32_t num_seqs,
+                  int32_t num_kv_heads, int32_t cu_count, int32_t budget_mult, int32_t max_partitions,
+                  int32_t tile_tokens, int32_t sliding_window, int32_t capacity, int32_t* work_info,
+                  int32_t* reduce_info, int32_t* num_work, void* stream) {
     int32_t cap = 0;
     const pa_status st = check_plan(context_lens, num_seqs, num_kv_heads, cu_count, budget_mult,
-                                    max_partitions, tile_tokens, capacity, work_info, reduce_info,
-                                    num_work, &cap);
+                                    max_partitions, tile_tokens, sliding_window, capacity, work_info,
+                                    reduce_info, num_work, &cap);
     if (st != PA_OK) return st;
-    return from_hip(pa::launch_plan(context_lens, num_seqs, cap, capacity, max_partitions, tile_tokens,
-                                    work_info, reduce_info, num_work, pa::as_stream(stream)));
+    return from_hip(pa::launch_plan(context_lens, cu_query_lens, num_seqs, cap, capacity, max_partitions,
+                                    tile_tokens, sliding_window, work_info, reduce_info, num_work,
+                                    pa::as_stream(stream)));
 }
 
 pa_status pa_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t num_q_heads,
@@ -201,18 +204,18 @@ pa_status pa_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t n
                     int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
                     const int32_t* block_tables, int32_t max_blocks_per_seq,
                     const int32_t* context_lens, int32_t num_seqs, const int32_t* cu_query_lens,
-                    int32_t max_q_len, float scale, float k_scale, float v_scale,
-                    const int32_t* work_info, const int32_t* reduce_info, const int32_t* num_work,
-                    int32_t capacity, int32_t tile_tokens, void* workspace, size_t workspace_bytes,
-                    void* out, pa_dtype out_dtype, void* stream) {
+                    int32_t max_q_len, int32_t sliding_window, float scale, float k_scale,
+                    float v_scale, const int32_t* work_info, const int32_t* reduce_info,
+                    const int32_t* num_work, int32_t capacity, int32_t tile_tokens, void* workspace,
+                    size_t workspace_bytes, void* out, pa_dtype out_dtype, void* stream) {
     pa::DecodeArgs a;
     bool nothing = false;
     const pa_status st = prepare_decode(q, q_dtype, num_rows, num_q_heads, head_dim, k_cache, v_cache,
                                         kv_dtype, num_blocks, num_kv_heads, block_size, block_tables,
                                         max_blocks_per_seq, context_lens, num_seqs, cu_query_lens,
-                                        max_q_len, scale, k_scale, v_scale, work_info, reduce_info,
-                                        num_work, capacity, tile_tokens, workspace, workspace_bytes, out,
-                                        out_dtype, &a, &nothing);
+                                        max_q_len, sliding_window, scale, k_scale, v_scale, work_info,
+                                        reduce_info, num_work, capacity, tile_tokens, workspace,
+                                        workspace_bytes, out, out_dtype, &a, &nothing);
     if (st != PA_OK) return st;
     if (nothing) {
         if (!out || num_rows == 0) return PA_OK;
@@ -240,24 +243,24 @@ pa_status pa_attention(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_
                        int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
                        const int32_t* block_tables, int32_t max_blocks_per_seq,
                        const int32_t* context_lens, int32_t num_seqs, const int32_t* cu_query_lens,
-                       int32_t max_q_len, float scale, float k_scale, float v_scale,
-                       int32_t cu_count, int32_t budget_mult, int32_t max_partitions,
+                       int32_t max_q_len, int32_t sliding_window, float scale, float k_scale,
+                       float v_scale, int32_t cu_count, int32_t budget_mult, int32_t max_partitions,
                        int32_t tile_tokens, int32_t capacity, int32_t* work_info,
                        int32_t* reduce_info, int32_t* num_work, void* workspace,
                        size_t workspace_bytes, void* out, pa_dtype out_dtype, void* stream) {
     // every check of the three calls first, so a failure launches nothing
     int32_t cap = 0;
     pa_status st = check_plan(context_lens, num_seqs, num_kv_heads, cu_count, budget_mult,
-                              max_partitions, tile_tokens, capacity, work_info, reduce_info, num_work,
-                              &cap);
+                              max_partitions, tile_tokens, sliding_window, capacity, work_info,
+                              reduce_info, num_work, &cap);
     if (st != PA_OK) return st;
     pa::DecodeArgs d;
     bool nothing = false;
     st = prepare_decode(q, q_dtype, num_rows, num_q_heads, head_dim, k_cache, v_cache, kv_dtype,
                         num_blocks, num_kv_heads, block_size, block_tables, max_blocks_per_seq,
-                        context_lens, num_seqs, cu_query_lens, max_q_len, scale, k_scale, v_scale,
-                        work_info, reduce_info, num_work, capacity, tile_tokens, workspace,
-                        workspace_bytes, nullptr, q_dtype, &d, &nothing);
+                        context_lens, num_seqs, cu_query_lens, max_q_len, sliding_window, scale,
+                        k_scale, v_scale, work_info, reduce_info, num_work, capacity, tile_tokens,
+                        workspace, workspace_bytes, nullptr, q_dtype, &d, &nothing);
     if (st != PA_OK) return st;
     if (out_dtype != q_dtype) return PA_INVALID_ARG;
     pa::MergeArgs m;
@@ -275,8 +278,8 @@ pa_status pa_attention(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_
         d.plan_reduce_out = reinterpret_cast<int2*>(reduce_info);
         d.plan_num_work_out = num_work;
     } else {
-        st = from_hip(pa::launch_plan(context_lens, num_seqs, cap, capacity, max_partitions, tile_tokens,
-                                      work_info, reduce_info, num_work, s));
+        st = from_hip(pa::launch_plan(context_lens, cu_query_lens, num_seqs, cap, capacity, max_partitions,
+                                      tile_tokens, sliding_window, work_info, reduce_info, num_work, s));
         if (st != PA_OK) return st;
     }
     if (!nothing) {

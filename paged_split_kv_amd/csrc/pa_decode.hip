@@ -85,12 +85,14 @@ __device__ __forceinline__ bool slot_info(const DecodeArgs& a, int slot, SlotInf
 __device__ __forceinline__ void plan_in_wave(const DecodeArgs& a, int slot, int g, int4& wk, int2& nwk) {
     const int lane = threadIdx.x & 63;
     const bool real = lane < a.num_seqs;
-    const int len = real ? max(a.context_lens[lane], 0) : 0;
+    const int S = real ? max(a.context_lens[lane], 0) : 0;
+    const PlanRange pr = plan_range(S, real && a.window > 0 ? plan_q_len(a.cu, lane) : 1, a.window, a.tile_tokens);
+    const int len = pr.len;
+    const int tiles = pr.tiles;
     const long long total = wave_sum_ll(len);
     const int nonempty = __popcll(__builtin_amdgcn_ballot_w64(len > 0));
-    const int parts = plan_parts(len, static_cast<long long>(a.plan_cap) - nonempty, total, a.tile_tokens,
+    const int parts = plan_parts(len, tiles, static_cast<long long>(a.plan_cap) - nonempty, total,
                                  a.max_partitions);
-    const int tiles = plan_tiles(len, a.tile_tokens);
     const int incl = wave_incl_scan(parts, lane);
     const int first = incl - parts;
     const int used = __builtin_amdgcn_readlane(incl, 63);
@@ -104,7 +106,8 @@ __device__ __forceinline__ void plan_in_wave(const DecodeArgs& a, int slot, int 
         const int o = max(owner, 0);
         const int2 t = plan_tile_range(slot - __builtin_amdgcn_readlane(first, o),
                                        __builtin_amdgcn_readlane(tiles, o), __builtin_amdgcn_readlane(parts, o));
-        wk = make_int4(o, t.x, t.y, __builtin_amdgcn_readlane(len, o));
+        const int t0 = __builtin_amdgcn_readlane(pr.t0, o);
+        wk = make_int4(o, t0 + t.x, t0 + t.y, __builtin_amdgcn_readlane(S, o));
     }
     nwk = make_int2(used, big);
     if (threadIdx.x < 64) {
@@ -131,9 +134,12 @@ __device__ void plan_in_place(const DecodeArgs& a, int slot, int g, int4& wk, in
     const int wave = tid >> 6;
     const int r = tid;
     const bool real = r < a.num_seqs;
-    const int len = real ? max(a.context_lens[r], 0) : 0;
+    const int S = real ? max(a.context_lens[r], 0) : 0;
+    const PlanRange pr = plan_range(S, real && a.window > 0 ? plan_q_len(a.cu, r) : 1, a.window, a.tile_tokens);
+    const int len = pr.len;
+    const int tiles = pr.tiles;
 
-    // W = sum S_b and B' = #{S_b > 0}
+    // W = sum of the lengths read and B' = #{requests reading any key}
     const long long wsum = wave_sum_ll(len);
     const int wne = __popcll(__builtin_amdgcn_ballot_w64(len > 0));
     if (lane == 0) {
@@ -150,9 +156,8 @@ __device__ void plan_in_place(const DecodeArgs& a, int slot, int g, int4& wk, in
     }
 
     // this request's partitions, their exclusive scan, and the largest partition in tiles
-    const int parts = plan_parts(len, static_cast<long long>(a.plan_cap) - nonempty, total, a.tile_tokens,
+    const int parts = plan_parts(len, tiles, static_cast<long long>(a.plan_cap) - nonempty, total,
                                  a.max_partitions);
-    const int tiles = plan_tiles(len, a.tile_tokens);
     const int incl = wave_incl_scan(parts, lane);
     int big = parts > 0 ? (tiles + parts - 1) / parts : 0;     // a floor/ceil split's largest part
 #pragma unroll
@@ -179,7 +184,7 @@ __device__ void plan_in_place(const DecodeArgs& a, int slot, int g, int4& wk, in
     for (int w = 0; w < NW; ++w) owner += s_below[w];
     if (slot < used && r == owner) {
         const int2 t = plan_tile_range(slot - first, tiles, parts);
-        s_entry = make_int4(r, t.x, t.y, len);
+        s_entry = make_int4(r, pr.t0 + t.x, pr.t0 + t.y, S);
     }
     __syncthreads();
     wk = slot < used ? s_entry : make_int4(-1, 0, 0, 0);
@@ -392,7 +397,8 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
 
     // ---- query operands (B of S^T = K.Q^T): qop[cb][s] = q[row][32s + 8*grp .. +8] as bf16 ----
     bf16x8_t qop[NCB][C::KSTEPS];
-    int nvis[NCB];                                // keys visible to this lane's query row
+    int nvis[NCB];                                // keys visible to this lane's query row: [nlo, nvis)
+    int nlo[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
         const int n = 16 * cb + col;
@@ -400,6 +406,7 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
         const int i = valid ? n / G : 0;
         const int h = g * G + (valid ? n - i * G : 0);
         nvis[cb] = valid ? si.S - (si.L - 1 - i) : 0;
+        nlo[cb] = a.window > 0 ? max(nvis[cb] - a.window, 0) : 0;
         const size_t qoff = (static_cast<size_t>(si.row0 + i) * a.num_q_heads + h) * D;
 #pragma unroll
         for (int s = 0; s < C::KSTEPS; ++s) {
@@ -564,11 +571,13 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
                     sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[s], qop[cb][s], sacc, 0, 0, 0);
                 // lane holds keys key0 + 4*grp + j for query row 16cb + col
                 const int lim = min(nv, nvis[cb] - key0);
+                const int low = nlo[cb] - key0;           // window start relative to the chunk
                 float x[4];
                 float mt = -INFINITY;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    x[j] = (4 * grp + j) < lim ? sacc[j] * a.score_scale_log2 : -INFINITY;
+                    const int kj = 4 * grp + j;
+                    x[j] = (kj < lim && kj >= low) ? sacc[j] * a.score_scale_log2 : -INFINITY;
                     mt = fmaxf(mt, x[j]);
                 }
                 mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
@@ -731,7 +740,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeArgs a) {
         const int i = n / G;
         const int h = g * G + (n - i * G);
         const int nv = si.S - (si.L - 1 - i);
-        const int lo = si.k_lo;
+        const int lo = a.window > 0 ? max(si.k_lo, nv - a.window) : si.k_lo;
         const int hi = min(si.k_hi, nv);
         const size_t qoff = (static_cast<size_t>(si.row0 + i) * a.num_q_heads + h) * D;
         compiler_fence();

@@ -123,30 +123,54 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
     return v;
 }
 
-// Tiles of a request of s tokens (s + tile_tokens - 1 < 2^32, so 32-bit unsigned division is exact).
-__device__ __forceinline__ int plan_tiles(int s, int tile_tokens) {
-    return s > 0 ? static_cast<int>((static_cast<unsigned>(s) + static_cast<unsigned>(tile_tokens) - 1u) /
-                                    static_cast<unsigned>(tile_tokens))
-                 : 0;
+// The key range a request reads and the tiles it spans.  Without a window the range is [0, S);
+// with a window of W keys per token (the window applies per token) it is the union of the
+// tokens' ranges, [max(0, S - (L - 1) - W), S).  The tiles are those the range touches,
+// [floor(lo / T), ceil(S / T)); len = S - lo weighs the request in the apportionment.
+struct PlanRange {
+    int len;      // keys read
+    int t0;       // first tile
+    int tiles;    // tiles spanned (0 when len = 0)
+};
+
+__device__ __forceinline__ PlanRange plan_range(int s, int q_len, int window, int tile_tokens) {
+    PlanRange r;
+    long long lo = 0;
+    if (window > 0) {
+        lo = static_cast<long long>(s) - (static_cast<long long>(q_len) - 1) - window;
+        lo = lo < 0 ? 0 : (lo > s ? s : lo);
+    }
+    const unsigned t = static_cast<unsigned>(tile_tokens);
+    r.len = s - static_cast<int>(lo);
+    r.t0 = static_cast<int>(static_cast<unsigned>(lo) / t);
+    // s + T - 1 < 2^32, so the 32-bit unsigned division is exact
+    r.tiles = r.len > 0 ? static_cast<int>((static_cast<unsigned>(s) + t - 1u) / t) - r.t0 : 0;
+    return r;
 }
 
-// Partitions of a request of s tokens: none when empty, else min(P, tiles, 1 + floor(extra * s / W))
-// with extra = capacity - (non-empty requests) >= 0 and W the batch's total length.  The quotient
-// takes the 32-bit unsigned division when both operands fit, the 64-bit one otherwise.
-__device__ __forceinline__ int plan_parts(int s, long long extra, long long total, int tile_tokens,
+// Partitions of a request reading `len` keys over `tiles` tiles: none when empty, else
+// min(P, tiles, 1 + floor(extra * len / W)) with extra = capacity - (non-empty requests) >= 0 and W
+// the batch's total.  The quotient takes the 32-bit unsigned division when both operands fit.
+__device__ __forceinline__ int plan_parts(int len, int tiles, long long extra, long long total,
                                           int max_partitions) {
-    if (s <= 0) return 0;
-    const unsigned long long num = static_cast<unsigned long long>(extra) * static_cast<unsigned>(s);
+    if (len <= 0) return 0;
+    const unsigned long long num = static_cast<unsigned long long>(extra) * static_cast<unsigned>(len);
     long long q;
     if ((num >> 32) == 0 && (static_cast<unsigned long long>(total) >> 32) == 0)
         q = static_cast<unsigned>(num) / static_cast<unsigned>(total);
     else
         q = static_cast<long long>(num / static_cast<unsigned long long>(total));
     long long p = 1 + q;
-    const int tiles = plan_tiles(s, tile_tokens);
     if (p > tiles) p = tiles;
     if (p > max_partitions) p = max_partitions;
     return static_cast<int>(p);
+}
+
+// Query length of request b (1 without cumulative lengths); a decreasing pair counts as 0.
+__device__ __forceinline__ int plan_q_len(const int32_t* cu, int b) {
+    if (!cu) return 1;
+    const int L = cu[b + 1] - cu[b];
+    return L < 0 ? 0 : L;
 }
 
 // Tile range [floor(j * tiles / parts), floor((j + 1) * tiles / parts)) of partition j.
@@ -229,6 +253,7 @@ struct DecodeArgs {
     int* ws_counters;           // arrival counters of the fused merge
     const int2* reduce_info;    // (first slot, partitions) per request; needed when out is set
     void* out;                  // nullable: when set, the merge runs inside the decode launch
+    int window;                 // 0: none; W > 0: each query token sees its last W visible keys
     // planning in place (num_seqs <= kInlinePlanSeqs): every workgroup evaluates the planner's rule
     // itself; the plan is also stored to these buffers for the merge and the caller
     int plan_inline;
@@ -257,9 +282,9 @@ struct MergeArgs {
 // Requests a decode workgroup can plan for in place: one per thread of its 4 waves.
 constexpr int kInlinePlanSeqs = PA_INLINE_PLAN_SEQS;
 
-hipError_t launch_plan(const int32_t* context_lens, int num_seqs, int cap_formula, int capacity,
-                       int max_partitions, int tile_tokens, int32_t* work_info, int32_t* reduce_info,
-                       int32_t* num_work, hipStream_t stream);
+hipError_t launch_plan(const int32_t* context_lens, const int32_t* cu, int num_seqs,
+                       int cap_formula, int capacity, int max_partitions, int tile_tokens, int window,
+                       int32_t* work_info, int32_t* reduce_info, int32_t* num_work, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, pa_dtype kv_dtype, bool q_f32,
                          hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int head_dim, bool out_bf16, hipStream_t stream);

@@ -3,8 +3,9 @@
 // What it computes is stated in ROCm/ATOM PR #2366 "[MiniMax-M3] Route the paged decode to aiter's
 // FlyDSL kernel with work planner" (section 1: a partition count proportional to each request's real
 // context length under a 2 x CU workgroup budget; section 3: ceiling 256; review item 2: work entries
-// hold begin/end tiles and the request's length; review item 3: the capacity formula).  The rounding of
-// the shares is this library's reading, documented in pa.h.
+// hold begin/end tiles and the request's length; review item 3: the capacity formula; review, window
+// logic: under a sliding window the plan covers the range the kernel reads).  The rounding of the
+// shares is this library's reading, documented in pa.h.
 //
 // One workgroup of 1024 threads does the whole plan: a reduction for the total length and the number
 // of non-empty requests, the per-request counts, an exclusive scan into LDS, and then one thread per
@@ -20,9 +21,9 @@ constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / 64;
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
-    const int32_t* __restrict__ context_lens, int num_seqs, int cap_formula, int capacity,
-    int max_partitions, int tile_tokens, int4* __restrict__ work_info,
-    int2* __restrict__ reduce_info, int32_t* __restrict__ num_work) {
+    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ cu, int num_seqs,
+    int cap_formula, int capacity, int max_partitions, int tile_tokens, int window,
+    int4* __restrict__ work_info, int2* __restrict__ reduce_info, int32_t* __restrict__ num_work) {
     __shared__ int32_t first[PA_MAX_SEQS + 1];
     __shared__ long long red_total[kPlanWaves];
     __shared__ int red_count[kPlanWaves];
@@ -33,13 +34,18 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int lane = tid & 63;
     const int wave = tid >> 6;
 
-    // --- W = sum S_b and B' = #{S_b > 0} ---
+    // the key range request b reads: all of [0, S_b), or its window's union
+    auto range_of = [&](int b) -> PlanRange {
+        return plan_range(max(context_lens[b], 0), window > 0 ? plan_q_len(cu, b) : 1, window, tile_tokens);
+    };
+
+    // --- W = sum of the lengths read and B' = #{requests reading any key} ---
     long long total = 0;
     int nonempty = 0;
     for (int b = tid; b < num_seqs; b += kPlanThreads) {
-        const int s = max(context_lens[b], 0);
-        total += s;
-        nonempty += (s > 0);
+        const int len = range_of(b).len;
+        total += len;
+        nonempty += (len > 0);
     }
     total = wave_sum_ll(total);
     for (int o = 32; o >= 1; o >>= 1) nonempty += __shfl_xor(nonempty, o, 64);
@@ -62,7 +68,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int b1 = min(b0 + per, num_seqs);
     int local = 0;
     for (int b = b0; b < b1; ++b) {
-        const int parts = plan_parts(max(context_lens[b], 0), extra, total, tile_tokens, max_partitions);
+        const PlanRange r = range_of(b);
+        const int parts = plan_parts(r.len, r.tiles, extra, total, max_partitions);
         first[b] = parts;
         local += parts;
     }
@@ -97,9 +104,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
             const int b = lo;
             const int j = s - first[b];
             const int parts = first[b + 1] - first[b];
-            const int len = max(context_lens[b], 0);
-            const int2 r = plan_tile_range(j, plan_tiles(len, tile_tokens), parts);
-            work_info[s] = make_int4(b, r.x, r.y, len);
+            const PlanRange pr = range_of(b);
+            const int2 r = plan_tile_range(j, pr.tiles, parts);
+            work_info[s] = make_int4(b, pr.t0 + r.x, pr.t0 + r.y, max(context_lens[b], 0));
             largest = max(largest, r.y - r.x);
         } else {
             work_info[s] = make_int4(-1, 0, 0, 0);
@@ -116,11 +123,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
 
 }  // namespace
 
-hipError_t launch_plan(const int32_t* context_lens, int num_seqs, int cap_formula, int capacity,
-                       int max_partitions, int tile_tokens, int32_t* work_info, int32_t* reduce_info,
-                       int32_t* num_work, hipStream_t stream) {
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, context_lens, num_seqs,
-                       cap_formula, capacity, max_partitions, tile_tokens,
+hipError_t launch_plan(const int32_t* context_lens, const int32_t* cu, int num_seqs, int cap_formula,
+                       int capacity, int max_partitions, int tile_tokens, int window,
+                       int32_t* work_info, int32_t* reduce_info, int32_t* num_work, hipStream_t stream) {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, context_lens, cu, num_seqs,
+                       cap_formula, capacity, max_partitions, tile_tokens, window,
                        reinterpret_cast<int4*>(work_info), reinterpret_cast<int2*>(reduce_info),
                        num_work);
     return hipGetLastError();

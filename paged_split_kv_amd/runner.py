@@ -48,32 +48,35 @@ class DecodeStep:
                    num_kv_heads=case.num_kv_heads, head_dim=case.head_dim, max_q_len=case.max_q_len,
                    out_dtype=case.q.dtype, device=case.q.device, plan=plan)
 
-    def plan(self, context_lens: torch.Tensor, stream=None) -> None:
+    def plan(self, context_lens: torch.Tensor, stream=None, cu_query_lens=None,
+             sliding_window: int = 0) -> None:
         p = self.plan_cfg
         B.pa_plan(context_lens, self.num_kv_heads, cu_count=p.cu_count, budget_mult=p.budget_mult,
                   max_partitions=p.max_partitions, tile_tokens=p.tile_tokens, capacity=self.capacity,
                   work_info=self.work_info, reduce_info=self.reduce_info, num_work=self.num_work,
-                  stream=stream)
+                  cu_query_lens=cu_query_lens, sliding_window=sliding_window, stream=stream)
 
     def decode(self, q, k_cache, v_cache, kv_dtype, block_tables, context_lens, *, scale,
-               cu_query_lens=None, k_scale=1.0, v_scale=1.0, merge: bool = False, stream=None) -> None:
+               cu_query_lens=None, k_scale=1.0, v_scale=1.0, merge: bool = False,
+               sliding_window: int = 0, stream=None) -> None:
         """pa_decode; with merge=True the log-sum-exp merge into self.out runs in the same call."""
         B.pa_decode(q, k_cache, v_cache, kv_dtype, block_tables, context_lens, self.work_info,
                     self.num_work, self.workspace, scale=scale, cu_query_lens=cu_query_lens,
                     max_q_len=self.max_q_len, k_scale=k_scale, v_scale=v_scale,
                     tile_tokens=self.plan_cfg.tile_tokens,
                     reduce_info=self.reduce_info if merge else None,
-                    out=self.out if merge else None, stream=stream)
+                    out=self.out if merge else None, sliding_window=sliding_window, stream=stream)
 
     def attention(self, q, k_cache, v_cache, kv_dtype, block_tables, context_lens, *, scale,
-                  cu_query_lens=None, k_scale=1.0, v_scale=1.0, stream=None) -> torch.Tensor:
+                  cu_query_lens=None, k_scale=1.0, v_scale=1.0, sliding_window: int = 0,
+                  stream=None) -> torch.Tensor:
         """pa_attention: plan, decode and merge into self.out; the plan buffers are refreshed."""
         p = self.plan_cfg
         B.pa_attention(q, k_cache, v_cache, kv_dtype, block_tables, context_lens, self.work_info,
                        self.reduce_info, self.num_work, self.workspace, self.out, scale=scale,
                        cu_count=p.cu_count, budget_mult=p.budget_mult, max_partitions=p.max_partitions,
                        tile_tokens=p.tile_tokens, cu_query_lens=cu_query_lens, max_q_len=self.max_q_len,
-                       k_scale=k_scale, v_scale=v_scale, stream=stream)
+                       k_scale=k_scale, v_scale=v_scale, sliding_window=sliding_window, stream=stream)
         return self.out
 
     def merge(self, cu_query_lens=None, stream=None) -> torch.Tensor:
@@ -85,15 +88,18 @@ class DecodeStep:
                  whole: bool = False) -> torch.Tensor:
         """Plan, decode and merge one Case.  fused=True merges inside pa_decode (two launches per
         step); fused=False calls pa_merge separately; whole=True makes the one pa_attention call."""
+        w = case.window
         if whole:
             return self.attention(case.q, case.k_cache, case.v_cache, case.kv_dtype, case.block_tables,
                                   case.context_lens, scale=case.scale, cu_query_lens=case.cu_query_lens,
-                                  k_scale=case.k_scale, v_scale=case.v_scale, stream=stream)
+                                  k_scale=case.k_scale, v_scale=case.v_scale, sliding_window=w,
+                                  stream=stream)
         if replan:
-            self.plan(case.context_lens, stream)
+            self.plan(case.context_lens, stream, cu_query_lens=case.cu_query_lens, sliding_window=w)
         self.decode(case.q, case.k_cache, case.v_cache, case.kv_dtype, case.block_tables,
                     case.context_lens, scale=case.scale, cu_query_lens=case.cu_query_lens,
-                    k_scale=case.k_scale, v_scale=case.v_scale, merge=fused, stream=stream)
+                    k_scale=case.k_scale, v_scale=case.v_scale, merge=fused, sliding_window=w,
+                    stream=stream)
         if fused:
             return self.out
         return self.merge(case.cu_query_lens, stream)

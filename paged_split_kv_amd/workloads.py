@@ -60,6 +60,7 @@ class Case:
     scale: float
     k_scale: float = 1.0
     v_scale: float = 1.0
+    window: int = 0                 # sliding window in keys per query token; 0 = none
     meta: Dict = field(default_factory=dict)
 
     @property

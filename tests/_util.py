@@ -38,10 +38,12 @@ def assert_close(got: np.ndarray, ref: np.ndarray, kind: str, what: str = "") ->
                              f"({kind}: atol {atol}, rtol {rtol}); max err {err.max():.3e}; first {idx}")
 
 
-def oracle_plan_of(case, cu_count, budget_mult=2, max_partitions=256, tile_tokens=256, capacity=None):
+def oracle_plan_of(case, cu_count, budget_mult=2, max_partitions=256, tile_tokens=256, capacity=None,
+                   with_largest=False):
     ctx = case.context_lens.cpu().numpy()
+    cu = None if case.cu_query_lens is None else case.cu_query_lens.cpu().numpy()
     return oracle.plan(ctx, case.num_kv_heads, cu_count, budget_mult, max_partitions, tile_tokens,
-                       capacity)
+                       capacity, with_largest=with_largest, cu_query_lens=cu, window=case.window)
 
 
 def oracle_direct(case) -> np.ndarray:

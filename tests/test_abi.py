@@ -60,11 +60,11 @@ def test_workspace_bytes():
 
 
 def _plan_status(**kw):
-    a = dict(ctx=ctypes.c_void_p(16), B=4, hkv=1, cu=256, mult=2, P=256, T=256, cap=512,
+    a = dict(ctx=ctypes.c_void_p(16), cuq=None, B=4, hkv=1, cu=256, mult=2, P=256, T=256, win=0, cap=512,
              work=ctypes.c_void_p(256), red=ctypes.c_void_p(256), nw=ctypes.c_void_p(256))
     a.update(kw)
-    return B.load().pa_plan(a["ctx"], a["B"], a["hkv"], a["cu"], a["mult"], a["P"], a["T"], a["cap"],
-                            a["work"], a["red"], a["nw"], None)
+    return B.load().pa_plan(a["ctx"], a["cuq"], a["B"], a["hkv"], a["cu"], a["mult"], a["P"], a["T"],
+                            a["win"], a["cap"], a["work"], a["red"], a["nw"], None)
 
 
 def test_plan_argument_checks():
@@ -82,10 +82,11 @@ def test_plan_argument_checks():
     assert _plan_status(work=ctypes.c_void_p(8)) == B.PA_INVALID_ARG       # misaligned int4 entries
     assert _plan_status(nw=ctypes.c_void_p(260)) == B.PA_INVALID_ARG       # num_work pair misaligned
     assert _plan_status(B=B.PA_MAX_SEQS + 1, cap=1 << 22) == B.PA_UNSUPPORTED
+    assert _plan_status(win=-1) == B.PA_INVALID_ARG
 
 
 _GOOD = dict(q=256, qd=B.PA_BF16, R=4, Hq=16, D=128, k=256, v=256, kvd=B.PA_BF16, nb=10, Hkv=2, bs=16,
-             bt=256, mb=4, ctx=256, Bn=4, cu=None, ql=1, scale=0.1, ks=1.0, vs=1.0, work=256, red=256,
+             bt=256, mb=4, ctx=256, Bn=4, cu=None, ql=1, win=0, scale=0.1, ks=1.0, vs=1.0, work=256, red=256,
              nw=256, cap=256, T=256, ws=256, wsb=1 << 30, out=None, od=B.PA_BF16)
 
 
@@ -95,7 +96,7 @@ def _decode_status(**kw):
     vp = lambda x: None if x is None else ctypes.c_void_p(x)
     return B.load().pa_decode(vp(a["q"]), a["qd"], a["R"], a["Hq"], a["D"], vp(a["k"]), vp(a["v"]),
                               a["kvd"], a["nb"], a["Hkv"], a["bs"], vp(a["bt"]), a["mb"], vp(a["ctx"]),
-                              a["Bn"], vp(a["cu"]), a["ql"], a["scale"], a["ks"], a["vs"], vp(a["work"]),
+                              a["Bn"], vp(a["cu"]), a["ql"], a["win"], a["scale"], a["ks"], a["vs"], vp(a["work"]),
                               vp(a["red"]), vp(a["nw"]), a["cap"], a["T"], vp(a["ws"]), a["wsb"],
                               vp(a["out"]), a["od"], None)
 
@@ -121,6 +122,7 @@ def test_decode_argument_checks():
     assert _decode_status(wsb=1000) == B.PA_CAPACITY
     assert _decode_status(scale=float("nan")) == B.PA_INVALID_ARG
     assert _decode_status(Bn=-1) == B.PA_INVALID_ARG
+    assert _decode_status(win=-5) == B.PA_INVALID_ARG
     assert _decode_status(out=512, od=B.PA_F32) == B.PA_INVALID_ARG    # merged output dtype != q dtype
     assert _decode_status(out=512, red=None, D=96) == B.PA_UNSUPPORTED
     assert _decode_status(out=512, red=None) == B.PA_INVALID_ARG       # merging needs reduce_info
@@ -164,7 +166,7 @@ def _attention_status(**kw):
     vp = lambda x: None if x is None else ctypes.c_void_p(x)
     return B.load().pa_attention(vp(a["q"]), a["qd"], a["R"], a["Hq"], a["D"], vp(a["k"]), vp(a["v"]),
                                  a["kvd"], a["nb"], a["Hkv"], a["bs"], vp(a["bt"]), a["mb"], vp(a["ctx"]),
-                                 a["Bn"], vp(a["cu"]), a["ql"], a["scale"], a["ks"], a["vs"], a["cuc"],
+                                 a["Bn"], vp(a["cu"]), a["ql"], a["win"], a["scale"], a["ks"], a["vs"], a["cuc"],
                                  a["mult"], a["P"], a["T"], a["cap"], vp(a["work"]), vp(a["red"]),
                                  vp(a["nw"]), vp(a["ws"]), a["wsb"], vp(a["out"]), a["od"], None)
 
@@ -187,6 +189,7 @@ def test_attention_argument_checks():
     assert _attention_status(out=520) == B.PA_INVALID_ARG
     assert _attention_status(od=B.PA_F32) == B.PA_INVALID_ARG
     assert _attention_status(ql=2) == B.PA_INVALID_ARG
+    assert _attention_status(win=-1) == B.PA_INVALID_ARG
 
 
 def test_merge_refuses_misaligned_out():
