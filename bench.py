@@ -107,9 +107,10 @@ def main():
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window in keys per query token (0 = none); the bytes counted are the "
                          "windowed ranges")
-    ap.add_argument("--workload", choices=("skewed", "sparse"), default="skewed",
+    ap.add_argument("--workload", choices=("skewed", "sparse", "long", "verify", "fp8"), default="skewed",
                     help="skewed: the 32-request agentic batch (default, the headline metric); "
-                         "sparse: 16 near-uniform top-k requests with a partition cap of 8")
+                         "sparse: 16 near-uniform top-k requests with a partition cap of 8; "
+                         "long / verify / fp8: the other full-size configurations, reported beside it")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -131,47 +132,73 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    print(f"[bench] building the 4 GiB page pool and the {args.workload} steps", file=sys.stderr, flush=True)
-    if args.workload == "skewed":
-        pool = W.skewed_pool(dev)
-        max_parts = 256
-    else:
-        pool = W.skewed_pool(dev, steps=W.sparse_lengths(64, 16, seed=11))
-        max_parts = 8
-    nsteps = pool.steps.shape[0]
-    B_ = pool.steps.shape[1]
-    Hq, D = pool.q.shape[2], pool.q.shape[3]
-    Hkv = pool.k_cache.shape[1]
-    cu_count = B.pa_device_cu_count(0)
-    step = DecodeStep(num_seqs=B_, num_rows=B_, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
-                      max_q_len=1, out_dtype=torch.bfloat16, device=dev,
-                      plan=PlanConfig(cu_count=cu_count, max_partitions=max_parts))
     win = args.window
-    keys = np.minimum(pool.steps, win) if win > 0 else pool.steps        # one query token per request
-    kv_bytes = keys.sum(axis=1) * Hkv * 2 * D * 2                         # per step
+    cu_count = B.pa_device_cu_count(0)
+    pool = None
+    if args.workload in ("skewed", "sparse"):
+        print(f"[bench] building the 4 GiB page pool and the {args.workload} steps", file=sys.stderr, flush=True)
+        if args.workload == "skewed":
+            pool = W.skewed_pool(dev)
+            max_parts = 256
+        else:
+            pool = W.skewed_pool(dev, steps=W.sparse_lengths(64, 16, seed=11))
+            max_parts = 8
+        batches = [W.Case(f"{args.workload}_{i}", pool.q[i], pool.k_cache, pool.v_cache, "bf16",
+                          pool.block_tables[i], pool.context_lens[i], None, 1, pool.scale)
+                   for i in range(pool.steps.shape[0])]
+        lens = [pool.steps[i] for i in range(len(batches))]
+        qlens = [np.ones_like(x) for x in lens]
+    else:
+        # one named configuration; independent copies (own pages and values) are rotated so that
+        # consecutive steps do not find each other's pages in the 256 MB last-level cache
+        name = {"long": "long_bf16", "verify": "verify_bf16", "fp8": "fp8_kv"}[args.workload]
+        first = W.make_config(name, device=dev)
+        copies = max(1, min(8, -(-(640 << 20) // first.kv_bytes())))
+        print(f"[bench] building {copies} copies of {name}", file=sys.stderr, flush=True)
+        batches = [first] + [W.make_config(name, device=dev, seed=1000 + c) for c in range(1, copies)]
+        max_parts = 256
+        lens = [c.context_lens.cpu().numpy() for c in batches]
+        qlens = [np.ones_like(x) if c.cu_query_lens is None else np.diff(c.cu_query_lens.cpu().numpy())
+                 for c, x in zip(batches, lens)]
+    for c in batches:
+        c.window = win
+    nsteps = len(batches)
+    c0 = batches[0]
+    B_, Hq, D, Hkv = c0.num_seqs, c0.num_q_heads, c0.head_dim, c0.num_kv_heads
+    step = DecodeStep.for_case(c0, PlanConfig(cu_count=cu_count, max_partitions=max_parts))
+    elem = {"f32": 4, "bf16": 2, "fp8": 1}[c0.kv_dtype]
+
+    def keys_read(S, L):
+        """Keys a request reads: all S, or with a window the union of its tokens' windows."""
+        return S - (np.maximum(0, S - (L - 1) - win) if win > 0 else 0)
+
+    keys = np.array([keys_read(np.asarray(x, np.int64), np.asarray(l, np.int64)).sum()
+                     for x, l in zip(lens, qlens)])
+    kv_bytes = keys * Hkv * 2 * D * elem                                    # per step
     stream = torch.cuda.current_stream()
 
     def run(i, ev=None, mode="attention"):
         """One step over batch i.  attention: one pa_attention call (the decode plans in place, then
         the merge: two launches).  three: pa_plan, pa_decode writing partial states, pa_merge.
         fused: pa_plan, then pa_decode with the merge inside its launch."""
-        i %= nsteps
-        ctx = pool.context_lens[i]
+        c = batches[i % nsteps]
         if mode == "attention":
-            step.attention(pool.q[i], pool.k_cache, pool.v_cache, "bf16", pool.block_tables[i], ctx,
-                           scale=pool.scale, sliding_window=win)
+            step.attention(c.q, c.k_cache, c.v_cache, c.kv_dtype, c.block_tables, c.context_lens,
+                           scale=c.scale, cu_query_lens=c.cu_query_lens, k_scale=c.k_scale,
+                           v_scale=c.v_scale, sliding_window=win)
             return
         if ev is not None:
             ev[0].record(stream)
-        step.plan(ctx, sliding_window=win)
+        step.plan(c.context_lens, cu_query_lens=c.cu_query_lens, sliding_window=win)
         if ev is not None:
             ev[1].record(stream)
-        step.decode(pool.q[i], pool.k_cache, pool.v_cache, "bf16", pool.block_tables[i], ctx,
-                    scale=pool.scale, merge=mode == "fused", sliding_window=win)
+        step.decode(c.q, c.k_cache, c.v_cache, c.kv_dtype, c.block_tables, c.context_lens, scale=c.scale,
+                    cu_query_lens=c.cu_query_lens, k_scale=c.k_scale, v_scale=c.v_scale,
+                    merge=mode == "fused", sliding_window=win)
         if ev is not None:
             ev[2].record(stream)
         if mode == "three":
-            step.merge()
+            step.merge(c.cu_query_lens)
         if ev is not None:
             ev[3].record(stream)
 
@@ -223,16 +250,18 @@ def main():
     # the decode kernel alone: launches back to back over the batches, each with its own plan made
     # beforehand, so consecutive launches read different pages and no event sits between them
     plans = []
-    for i in range(nsteps):
-        w, r, n = B.pa_plan(pool.context_lens[i], Hkv, cu_count=cu_count, max_partitions=max_parts,
-                            capacity=step.capacity, sliding_window=win)
+    for c in batches:
+        w, r, n = B.pa_plan(c.context_lens, Hkv, cu_count=cu_count, max_partitions=max_parts,
+                            capacity=step.capacity, cu_query_lens=c.cu_query_lens, sliding_window=win)
         plans.append((w, n))
     torch.cuda.synchronize()
 
     def decode_only(i):
-        i %= nsteps
-        B.pa_decode(pool.q[i], pool.k_cache, pool.v_cache, "bf16", pool.block_tables[i], pool.context_lens[i],
-                    plans[i][0], plans[i][1], step.workspace, scale=pool.scale, sliding_window=win)
+        c = batches[i % nsteps]
+        w, n = plans[i % nsteps]
+        B.pa_decode(c.q, c.k_cache, c.v_cache, c.kv_dtype, c.block_tables, c.context_lens, w, n, step.workspace,
+                    scale=c.scale, cu_query_lens=c.cu_query_lens, max_q_len=c.max_q_len, k_scale=c.k_scale,
+                    v_scale=c.v_scale, sliding_window=win)
 
     for i in range(8):
         decode_only(i)
@@ -285,10 +314,18 @@ def main():
         metric = f"µs/step + achieved KV-read HBM GB/s (% peak), skewed 32-req bf16 decode, window {win}"
         workload = (f"skewed 32-request bf16 decode with a {win}-key sliding window, Hq 16 / Hkv 2, D 128, "
                     "page 16, 128 stratified steps over a 4 GiB pool; bytes = windowed keys")
-    else:
+    elif args.workload == "sparse":
         metric = "µs/step + achieved KV-read HBM GB/s (% peak), sparse top-k 16-req bf16 decode, cap 8"
         workload = ("sparse top-k bf16 decode: 16 requests of 2048 selected + 1..256 local tokens, "
                     "Hq 16 / Hkv 2, D 128, page 16, 64 steps over a 4 GiB pool, partition cap 8")
+    else:
+        desc = {"long": "one 131072-token bf16 request, Hq 16 / Hkv 2, D 128, page 64",
+                "verify": "8 verify requests of 3 tokens + 7 single-token requests at 16384 tokens, bf16, "
+                          "Hq 6 / Hkv 1, D 256, page 16, 2 padding rows",
+                "fp8": "256 requests of 128..65536 tokens (log-normal), fp8 e4m3fn K/V with per-tensor "
+                       "scales, bf16 q, Hq 16 / Hkv 2, D 128, page 16"}[args.workload]
+        metric = f"µs/step + achieved KV-read HBM GB/s (% peak), {args.workload} workload"
+        workload = f"{desc}; {nsteps} independent copies rotated" + (f"; window {win}" if win else "")
     result = {
         "metric": metric,
         "value": round(gbps, 1),
@@ -300,11 +337,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": c0.kv_dtype if c0.kv_dtype != "fp8" else "fp8 KV, bf16 MFMA",
         "data": "synthetic",
         "config": {"workload": workload, "sliding_window": win,
-                   "num_seqs": B_, "q_len": 1, "mean_tokens_per_step": round(float(pool.steps.sum(1).mean()), 1),
-                   "mean_keys_read_per_step": round(float(keys.sum(1).mean()), 1),
+                   "num_seqs": B_, "max_q_len": c0.max_q_len,
+                   "mean_tokens_per_step": round(float(np.mean([x.sum() for x in lens])), 1),
+                   "mean_keys_read_per_step": round(float(keys.mean()), 1),
                    "planner": {"budget": "2 x CU", "cu_count": cu_count, "max_partitions": max_parts,
                                "tile_tokens": 256}},
         "us_per_step": round(us_step, 2),
@@ -328,7 +366,7 @@ def main():
         "hip_graph": graph,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and pool is not None:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(pool, args.cpu_seconds, nsteps, win)
     print(json.dumps(result), flush=True)

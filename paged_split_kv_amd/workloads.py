@@ -266,29 +266,33 @@ def fp8_context_lens(batch: int = 256, seed: int = 4) -> np.ndarray:
     return np.clip(np.rint(np.exp(mu + 1.27 * z)), 128, 65536).astype(np.int64)
 
 
-def make_config(name: str, device="cpu", step: Optional[int] = None) -> Case:
-    """The five named workloads at full size."""
+def make_config(name: str, device="cpu", step: Optional[int] = None, seed: Optional[int] = None) -> Case:
+    """The five named workloads at full size.  ``seed`` replaces the workload's own value seed (for
+    independent copies of the same shape)."""
+    def sd(own: int) -> int:
+        return own if seed is None else seed
+
     if name == "tiny_fp32":
         return build_case(name, [1, 17, 100, 300], num_q_heads=4, num_kv_heads=1, head_dim=64,
-                          block_size=16, kv_dtype="f32", q_dtype="f32", seed=0, device=device)
+                          block_size=16, kv_dtype="f32", q_dtype="f32", seed=sd(0), device=device)
     if name == "skewed_bf16":
         steps = skewed_step_set()
         idx = skewed_named_steps(steps)["p50"] if step is None else step
         c = build_case(name, steps[idx].tolist(), num_q_heads=16, num_kv_heads=2, head_dim=128,
-                       block_size=16, kv_dtype="bf16", q_dtype="bf16", seed=100 + idx,
+                       block_size=16, kv_dtype="bf16", q_dtype="bf16", seed=sd(100 + idx),
                        device=device)
         c.meta["step"] = idx
         return c
     if name == "long_bf16":
         return build_case(name, [131072], num_q_heads=16, num_kv_heads=2, head_dim=128,
-                          block_size=64, kv_dtype="bf16", q_dtype="bf16", seed=2, device=device)
+                          block_size=64, kv_dtype="bf16", q_dtype="bf16", seed=sd(2), device=device)
     if name == "verify_bf16":
         return build_case(name, [16384] * 15, num_q_heads=6, num_kv_heads=1, head_dim=256,
-                          block_size=16, kv_dtype="bf16", q_dtype="bf16", seed=3,
+                          block_size=16, kv_dtype="bf16", q_dtype="bf16", seed=sd(3),
                           q_lens=[3] * 8 + [1] * 7, pad_rows=2, device=device)
     if name == "fp8_kv":
         return build_case(name, fp8_context_lens().tolist(), num_q_heads=16, num_kv_heads=2,
-                          head_dim=128, block_size=16, kv_dtype="fp8", q_dtype="bf16", seed=4,
+                          head_dim=128, block_size=16, kv_dtype="fp8", q_dtype="bf16", seed=sd(4),
                           device=device)
     raise KeyError(name)
 
