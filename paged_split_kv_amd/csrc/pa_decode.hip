@@ -40,6 +40,12 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
+// Word 3 of a raw buffer resource on gfx9 parts (32-bit data format, no swizzle): loads past the
+// resource's byte count return zero without touching memory.
+constexpr int kRawBufferWord3 = 0x00020000;
+// Cache-policy operand of a buffer load that marks it non-temporal (the nt bit on gfx950).
+constexpr int kLoadNonTemporal = 2;
+
 // Request geometry of slot work item: first row, query length (clamped), KV length.
 struct SlotInfo {
     int b, row0, L, S;
@@ -292,8 +298,11 @@ struct Mfma {
     // Waves per SIMD the register budget is cut for: 2 (two workgroups per CU, 256 registers per lane)
     // where operands and accumulators fit, else 1 (512 registers) rather than spilling.
     static constexpr int WAVES = (D == 64 || (D == 128 && NCB == 1)) ? 2 : 1;
-    // chunks in flight per wave
-    static constexpr int PF = D == 64 ? 4 : (D == 128 ? 3 : (NCB == 1 ? 2 : 1));
+    // chunks in flight per wave: as many as the registers hold without spilling (scratch traffic would
+    // itself be waited for in order and stall the pipeline); an fp8 chunk takes half the registers
+    static constexpr int PF_BF16 = D == 64 ? (NCB <= 2 ? 4 : 3) : (D == 128 ? (NCB == 1 ? 2 : (NCB == 2 ? 3 : 2)) : (NCB == 1 ? 2 : 1));
+    static constexpr int PF_FP8 = D == 64 ? (NCB <= 2 ? 8 : 6) : (D == 128 ? (NCB == 1 ? 4 : (NCB == 2 ? 4 : 2)) : (NCB == 1 ? 4 : 1));
+    static constexpr int PF = KV8 ? PF_FP8 : PF_BF16;
 };
 
 // Byte offset of 16-byte column c of row r in a per-wave bf16 LDS tile (XOR swizzle on the column).
@@ -313,7 +322,9 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // wave-uniform by construction; said so, so that everything derived from it (chunk indices,
+    // page ids, buffer resources) stays in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int work_groups = a.capacity * a.num_kv_heads;
     if (static_cast<int>(blockIdx.x) >= work_groups) {
         // merge launched with the decode: trailing workgroups write the rows no slot owns as zeros
@@ -334,6 +345,9 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
         wk = a.work_info[slot];
         nwk = *reinterpret_cast<const int2*>(a.num_work);
     }
+    wk = make_int4(__builtin_amdgcn_readfirstlane(wk.x), __builtin_amdgcn_readfirstlane(wk.y),
+                   __builtin_amdgcn_readfirstlane(wk.z), __builtin_amdgcn_readfirstlane(wk.w));
+    nwk = make_int2(__builtin_amdgcn_readfirstlane(nwk.x), __builtin_amdgcn_readfirstlane(nwk.y));
     const int used = nwk.x;
     const int b = wk.x;
     if (slot >= used || b < 0 || b >= a.num_seqs) return;
@@ -357,28 +371,33 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
         return (wave + C::NW * j) * unit + (k - j * unit);
     };
 
-    // Page ids of this wave's chunks, one per lane (lane = chunk ordinal - base), refreshed every 64.
-    int pages = -1;
-    int pages_base = 0;
-    auto load_pages = [&](int base) {
-        const int my_c = chunk_of(base + lane);
-        int blk = -1;
-        if (my_c < plan_chunks) {
-            blk = bt_row[(plan_lo + 16 * my_c) / a.block_size];
-            if (blk < 0 || blk >= a.num_blocks) blk = -1;
-        }
-        pages = blk;
-        pages_base = base;
+    // Every memory instruction of the streaming loop is issued unconditionally, so each iteration
+    // issues the same number of vector loads and the compiler can wait for exactly the chunk it
+    // stages (vmcnt counts in order) rather than for every load in flight.  Loads that have nothing
+    // to fetch go through buffer resources with no records: they return zeros and touch no memory.
+    // Page ids are fetched 2 x PF chunks ahead, each just before the K/V loads PF chunks ahead, so
+    // waiting for chunk k's K/V also covers the page id needed to issue chunk k + PF.
+    const __amdgpu_buffer_rsrc_t bt_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int*>(bt_row), 0, a.max_blocks * 4, kRawBufferWord3);
+    auto page_load = [&](int k) -> int {       // page id of the wave's k-th chunk; 0 past the plan
+        const int c = chunk_of(k);
+        const unsigned off = c < plan_chunks ? static_cast<unsigned>((plan_lo + 16 * c) / a.block_size) * 4u
+                                             : 0xfffffff0u;
+        return __builtin_amdgcn_raw_buffer_load_b32(bt_rsrc, off, 0, 0);
     };
-    load_pages(0);
+    int pfirst[C::PF], pnext[C::PF];
+#pragma unroll
+    for (int st = 0; st < C::PF; ++st) pfirst[st] = page_load(st);
+#pragma unroll
+    for (int st = 0; st < C::PF; ++st) pnext[st] = page_load(st + C::PF);
 
     SlotInfo si;
     {
-        const int S = max(a.context_lens[b], 0);
+        const int S = __builtin_amdgcn_readfirstlane(max(a.context_lens[b], 0));
         int row0 = b, L = 1;
         if (a.cu) {
-            row0 = a.cu[b];
-            L = a.cu[b + 1] - row0;
+            row0 = __builtin_amdgcn_readfirstlane(a.cu[b]);
+            L = __builtin_amdgcn_readfirstlane(a.cu[b + 1]) - row0;
         }
         L = min(max(L, 0), a.max_q_len);
         if (row0 < 0 || row0 >= a.num_rows) L = 0;
@@ -450,31 +469,33 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
     int my_chunks = (full_units > wave ? (full_units - wave + C::NW - 1) / C::NW : 0) * unit;
     if (rem > 0 && full_units % C::NW == wave) my_chunks += rem;
 
-    auto chunk_block = [&](int k) -> int {
-        const int base = k & ~63;
-        if (base != pages_base) load_pages(base);
-        return __builtin_amdgcn_readlane(pages, k - base);
-    };
-
     u32x4_t kreg[C::PF][C::NLD], vreg[C::PF][C::NLD];
     int nvalid_st[C::PF];
-    auto issue = [&](int st, int k) {
+    // K and V of the wave's k-th chunk from page `page`: 16 rows of GRB bytes each, one 16-byte
+    // load per lane and step, non-temporal.  A chunk past the wave's work, past the context or on an
+    // invalid page loads zeros (no records) and stages as an empty chunk.
+    auto issue = [&](int st, int k, int page) {
         const int c = chunk_of(k);
         const int key0 = si.k_lo + 16 * c;
-        const int blk = chunk_block(k);
-        const int nv = blk < 0 ? 0 : min(16, si.k_hi - key0);
+        const int blk = __builtin_amdgcn_readfirstlane(page);
+        const bool live = k < my_chunks && blk >= 0 && blk < a.num_blocks;
+        const int nv = live ? max(min(16, si.k_hi - key0), 0) : 0;
         nvalid_st[st] = nv;
-        if (nv > 0) {
-            const int off = key0 % a.block_size;
-            const size_t base = (static_cast<size_t>(blk) * a.num_kv_heads + g) * head_stride +
-                                static_cast<size_t>(off) * C::GRB;
-            const u32x4_t* kp = reinterpret_cast<const u32x4_t*>(a.k_cache + base);
-            const u32x4_t* vp = reinterpret_cast<const u32x4_t*>(a.v_cache + base);
+        const int off = key0 % a.block_size;
+        const size_t base = nv > 0 ? (static_cast<size_t>(blk) * a.num_kv_heads + g) * head_stride +
+                                         static_cast<size_t>(off) * C::GRB
+                                   : 0;
+        const int records = nv > 0 ? 16 * C::GRB : 0;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(a.k_cache + base), 0, records, kRawBufferWord3);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(a.v_cache + base), 0, records, kRawBufferWord3);
 #pragma unroll
-            for (int it = 0; it < C::NLD; ++it) {
-                kreg[st][it] = __builtin_nontemporal_load(kp + it * 64 + lane);
-                vreg[st][it] = __builtin_nontemporal_load(vp + it * 64 + lane);
-            }
+        for (int it = 0; it < C::NLD; ++it) {
+            kreg[st][it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                           rk, (it * 64 + lane) * 16, 0, kLoadNonTemporal));
+            vreg[st][it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                           rv, (it * 64 + lane) * 16, 0, kLoadNonTemporal));
         }
     };
 
@@ -527,14 +548,14 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
     const int tr_d0 = 4 * (lane & 3);
 
 #pragma unroll
-    for (int st = 0; st < C::PF; ++st)
-        if (st < my_chunks) issue(st, st);
+    for (int st = 0; st < C::PF; ++st) issue(st, st, pfirst[st]);
 
-    for (int k0 = 0; k0 < my_chunks; k0 += C::PF) {
+    // whole rounds of PF chunks; the padding chunks past my_chunks are empty and fetch nothing
+    const int rounds = (my_chunks + C::PF - 1) / C::PF;
+    for (int k0 = 0; k0 < rounds * C::PF; k0 += C::PF) {
 #pragma unroll
         for (int st = 0; st < C::PF; ++st) {
             const int k = k0 + st;
-            if (k >= my_chunks) break;
             const int key0 = si.k_lo + 16 * chunk_of(k);
             const int nv = nvalid_st[st];
 
@@ -542,7 +563,9 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
             if (nv == 16) stage(st, 16, true);     // uniform: only a slot's ragged last chunk is partial
             else stage(st, nv, false);
             compiler_fence();
-            if (k + C::PF < my_chunks) issue(st, k + C::PF);
+            const int page = pnext[st];            // fetched before chunk k's K/V: already here
+            pnext[st] = page_load(k + 2 * C::PF);
+            issue(st, k + C::PF, page);
 
             // K operands (A of S^T): row = col, d = 32s + 8*grp .. +8
             bf16x8_t kop[C::KSTEPS];

@@ -14,13 +14,15 @@ namespace pa {
 
 namespace {
 
-// One workgroup of 256 threads per (row, head).  Thread t owns the 16-byte column dc = t % (D/4) of
+// One workgroup of NT threads per (row, head).  Thread t owns the 16-byte column dc = t % (D/4) of
 // the head dimension and the partials j = pg, pg + NPG, ... with pg = t / (D/4); it folds them into a
 // running (max, sum, acc) with independent loads, then the NPG states of a column are combined in LDS.
-template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
+// NT = 1024 when there are few (row, head) pairs: a request split into hundreds of partials is then
+// read by 4x the threads, in one round of loads instead of four.
+template <int D, bool OUT_BF16, int NT>
+__global__ __launch_bounds__(NT) void merge_kernel(const MergeArgs a) {
     constexpr int NDC = D / 4;          // float4 columns
-    constexpr int NPG = 256 / NDC;      // partial groups
+    constexpr int NPG = NT / NDC;       // partial groups
     __shared__ float4 s_acc[NPG][NDC];
     __shared__ float s_m[NPG];
     __shared__ float s_l[NPG];
@@ -100,8 +102,15 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
 
 template <int D>
 hipError_t launch_merge_d(const MergeArgs& a, bool out_bf16, dim3 grid, hipStream_t stream) {
-    if (out_bf16) hipLaunchKernelGGL((merge_kernel<D, true>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((merge_kernel<D, false>), grid, dim3(256), 0, stream, a);
+    // fewer (row, head) pairs than compute units: wide workgroups, so each pair's loads go out at once
+    const bool wide = grid.x < 256;
+    if (out_bf16) {
+        if (wide) hipLaunchKernelGGL((merge_kernel<D, true, 1024>), grid, dim3(1024), 0, stream, a);
+        else hipLaunchKernelGGL((merge_kernel<D, true, 256>), grid, dim3(256), 0, stream, a);
+    } else {
+        if (wide) hipLaunchKernelGGL((merge_kernel<D, false, 1024>), grid, dim3(1024), 0, stream, a);
+        else hipLaunchKernelGGL((merge_kernel<D, false, 256>), grid, dim3(256), 0, stream, a);
+    }
     return hipGetLastError();
 }
 
