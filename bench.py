@@ -94,6 +94,86 @@ def cpu_baseline(pool, budget_s: float, max_steps: int, window: int = 0):
                       f"{budget_s:.0f} s), fp64 direct attention over the gathered pages, {spent:.1f} s"}
 
 
+def bench_mixed(args, batches, cu_count):
+    """The decode-first split of a mixed batch: pa_attention over the decode requests, then
+    pa_prefill over the prompt, per step; the parts are also timed alone."""
+    from paged_split_kv_amd import binding as B
+    from paged_split_kv_amd.runner import MixedStep, PlanConfig
+
+    stream = torch.cuda.current_stream()
+    steps = [MixedStep(c, 1, PlanConfig(cu_count=cu_count), concurrent=True) for c in batches]
+    m_side = [m.side for m in steps]
+    for m in steps:
+        m.side = None                  # the timed step runs on one stream
+    n = len(batches)
+    K = args.steps
+
+    def part(i, which):
+        c, m = batches[i % n], steps[i % n]
+        if which == "step":
+            m.run(c, stream)
+            return
+        if which == "two_streams":
+            m.side = m_side[i % n]
+            m.run(c, stream)
+            m.side = None
+            return
+        if which == "decode" and m.dec is not None:
+            m.dec.attention(c.q[:m.ndt], c.k_cache, c.v_cache, c.kv_dtype, c.block_tables[:m.nd],
+                            c.context_lens[:m.nd], scale=c.scale, cu_query_lens=c.cu_query_lens[:m.nd + 1],
+                            sliding_window=c.window)
+        if which == "prefill":
+            B.pa_prefill(c.q, c.k_cache, c.v_cache, c.kv_dtype, c.block_tables[m.nd:], c.context_lens[m.nd:],
+                         c.cu_query_lens[m.nd:], m.out, scale=c.scale, sliding_window=c.window)
+
+    def timed(which, warm):
+        for i in range(warm):
+            part(i, which)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(K):
+            part(i, which)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / K
+
+    step_ms = timed("step", args.warmup)
+    two_ms = timed("two_streams", 8)
+    dec_ms = timed("decode", 8)
+    pre_ms = timed("prefill", 8)
+    c0, m0 = batches[0], steps[0]
+    elem = {"f32": 4, "bf16": 2, "fp8": 1}[c0.kv_dtype]
+    per_key = c0.num_kv_heads * 2 * c0.head_dim * elem
+    lens = c0.context_lens.cpu().numpy().astype(np.int64)
+    dec_bytes = float(lens[:m0.nd].sum() * per_key)
+    all_bytes = float(lens.sum() * per_key)
+    gbps = all_bytes / (step_ms * 1e-3) / 1e9
+    dec_gbps = dec_bytes / (dec_ms * 1e-3) / 1e9
+    return {
+        "metric": "µs/step + achieved KV-read HBM GB/s (% peak), mixed batch through the decode-first split",
+        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"7 decodes at 16384 tokens + a new 100-token prompt, decodes first, Hq 12 / Hkv 2, "
+                               f"D 256, page 16, bf16; {n} independent copies rotated",
+                   "num_decodes": m0.nd, "decode_rows": m0.ndt, "threshold": 1,
+                   "planner": {"budget": "2 x CU", "cu_count": cu_count, "max_partitions": 256, "tile_tokens": 256}},
+        "us_per_step": round(step_ms * 1e3, 2),
+        "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 1),
+        "step": "pa_split_decode_first on the host; pa_prefill over the prompt, then pa_attention over the "
+                "decodes, on one stream",
+        "decode_part_us": round(dec_ms * 1e3, 2), "prefill_part_us": round(pre_ms * 1e3, 2),
+        "two_streams_us_per_step": round(two_ms * 1e3, 2),
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "pa_attention over the decode part (decode + merge launches)",
+                     "duration_us": round(dec_ms * 1e3, 2), "algorithmic_bytes_per_launch": round(dec_bytes, 1)},
+        "cpu_baseline": None,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -107,10 +187,12 @@ def main():
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window in keys per query token (0 = none); the bytes counted are the "
                          "windowed ranges")
-    ap.add_argument("--workload", choices=("skewed", "sparse", "long", "verify", "fp8"), default="skewed",
+    ap.add_argument("--workload", choices=("skewed", "sparse", "long", "verify", "fp8", "mixed"),
+                    default="skewed",
                     help="skewed: the 32-request agentic batch (default, the headline metric); "
                          "sparse: 16 near-uniform top-k requests with a partition cap of 8; "
-                         "long / verify / fp8: the other full-size configurations, reported beside it")
+                         "long / verify / fp8: the other full-size configurations, reported beside it; "
+                         "mixed: 7 decodes at 16k + a 100-token prompt through the decode-first split")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -120,7 +202,7 @@ def main():
 
     from paged_split_kv_amd import binding as B
     from paged_split_kv_amd import workloads as W
-    from paged_split_kv_amd.runner import DecodeStep, PlanConfig
+    from paged_split_kv_amd.runner import DecodeStep, MixedStep, PlanConfig
 
     B.load()
     dev = torch.device("cuda:0")
@@ -151,17 +233,25 @@ def main():
     else:
         # one named configuration; independent copies (own pages and values) are rotated so that
         # consecutive steps do not find each other's pages in the 256 MB last-level cache
-        name = {"long": "long_bf16", "verify": "verify_bf16", "fp8": "fp8_kv"}[args.workload]
-        first = W.make_config(name, device=dev)
+        if args.workload == "mixed":
+            name = "mixed_7x16k_prompt100"
+            make = lambda sd: W.make_mixed_case(device=dev, seed=sd)
+        else:
+            name = {"long": "long_bf16", "verify": "verify_bf16", "fp8": "fp8_kv"}[args.workload]
+            make = lambda sd: W.make_config(name, device=dev, seed=sd)
+        first = make(None) if args.workload != "mixed" else make(5)
         copies = max(1, min(8, -(-(640 << 20) // first.kv_bytes())))
         print(f"[bench] building {copies} copies of {name}", file=sys.stderr, flush=True)
-        batches = [first] + [W.make_config(name, device=dev, seed=1000 + c) for c in range(1, copies)]
+        batches = [first] + [make(1000 + c) for c in range(1, copies)]
         max_parts = 256
         lens = [c.context_lens.cpu().numpy() for c in batches]
         qlens = [np.ones_like(x) if c.cu_query_lens is None else np.diff(c.cu_query_lens.cpu().numpy())
                  for c, x in zip(batches, lens)]
     for c in batches:
         c.window = win
+    if args.workload == "mixed":
+        print(json.dumps(bench_mixed(args, batches, cu_count)), flush=True)
+        return
     nsteps = len(batches)
     c0 = batches[0]
     B_, Hq, D, Hkv = c0.num_seqs, c0.num_q_heads, c0.head_dim, c0.num_kv_heads

@@ -210,6 +210,39 @@ pa_status pa_attention(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_
                        int32_t* reduce_info, int32_t* num_work, void* workspace,
                        size_t workspace_bytes, void* out, pa_dtype out_dtype, void* stream);
 
+/*
+ * Prefill rows: attention of every query token of the given requests over its visible keys, written
+ * normalised to out (no plan, no workspace).  For the decode-first split of mixed batches
+ * (opengfx1030/vllm-rdna PR #29, Change 2: decode and verify rows go to the split-KV decode, the rest
+ * to a prefill kernel on the rebased remainder): the caller passes the prefill requests' slices,
+ *   context_lens + nd, block_tables + nd rows, cu_query_lens + nd (absolute row numbers: row r of q
+ *   and out is query token r - cu[b] of request b),
+ * with q and out the whole batch's arrays and num_rows its row count.  Rows [cu[0], cu[num_seqs])
+ * get attention, rows [cu[num_seqs], num_rows) zeros, rows before cu[0] are not touched.
+ * Token i of a request with L tokens and S keys sees [0, S - (L - 1 - i)) (or its last
+ * sliding_window keys), as in pa_decode; rows with no visible key are zeros.
+ * Each workgroup takes a block of query tokens of one request and one kv head (up to 64 query rows
+ * of the group: block = 64 / G tokens for head_dim <= 128, 16 / G for 256) and streams all the
+ * keys the block sees, split over its waves.  K/V of bf16 or fp8 caches only (PA_UNSUPPORTED for
+ * f32).  cu_query_lens is required.  Other checks as pa_decode.
+ */
+pa_status pa_prefill(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t num_q_heads,
+                     int32_t head_dim, const void* k_cache, const void* v_cache, pa_dtype kv_dtype,
+                     int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t num_seqs, const int32_t* cu_query_lens,
+                     int32_t sliding_window, float scale, float k_scale, float v_scale, void* out,
+                     pa_dtype out_dtype, void* stream);
+
+/*
+ * The decode-first split of a batch whose requests are ordered decodes first (opengfx1030/vllm-rdna
+ * PR #29, Change 2, the builder's split): the leading requests with at most `threshold` query tokens
+ * (1 + speculative tokens) are the decode part.  HOST array cu_query_lens_host [num_seqs + 1];
+ * writes the number of decode requests and their rows (cu[nd] - cu[0]).  Pure host arithmetic.
+ */
+pa_status pa_split_decode_first(const int32_t* cu_query_lens_host, int32_t num_seqs, int32_t threshold,
+                                int32_t* num_decodes, int32_t* num_decode_tokens);
+
 /* Static, human-readable name of a status code. */
 const char* pa_status_string(pa_status status);
 

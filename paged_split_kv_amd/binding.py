@@ -28,7 +28,8 @@ _DTYPE_OF_NAME = {"f32": PA_F32, "bf16": PA_BF16, "fp8": PA_FP8_E4M3}
 _TORCH_OF_NAME = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
 
 SYMBOLS = ("pa_plan_capacity", "pa_workspace_bytes", "pa_plan", "pa_decode", "pa_merge",
-           "pa_attention", "pa_status_string", "pa_device_cu_count")
+           "pa_attention", "pa_prefill", "pa_split_decode_first", "pa_status_string",
+           "pa_device_cu_count")
 
 
 class PaError(RuntimeError):
@@ -69,6 +70,12 @@ def load(path: str = LIB_PATH):
                                  vp, i32, vp, i32, vp, i32, i32, f32, f32, f32, i32, i32, i32, i32, i32,
                                  vp, vp, vp, vp, ctypes.c_size_t, vp, ctypes.c_int, vp]
     lib.pa_attention.restype = ctypes.c_int
+    lib.pa_prefill.argtypes = [vp, ctypes.c_int, i32, i32, i32, vp, vp, ctypes.c_int, i32, i32, i32, vp, i32,
+                               vp, i32, vp, i32, f32, f32, f32, vp, ctypes.c_int, vp]
+    lib.pa_prefill.restype = ctypes.c_int
+    lib.pa_split_decode_first.argtypes = [ctypes.POINTER(i32), i32, i32, ctypes.POINTER(i32),
+                                          ctypes.POINTER(i32)]
+    lib.pa_split_decode_first.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_device_cu_count.argtypes = [i32, ctypes.POINTER(i32)]
@@ -283,3 +290,46 @@ def pa_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
                                tile_tokens, capacity,
                                _ptr(work_info), _ptr(reduce_info), _ptr(num_work), _ptr(workspace),
                                workspace.numel(), _ptr(out), qd, _stream(stream)), "pa_attention")
+
+
+def pa_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_dtype: str,
+               block_tables: torch.Tensor, context_lens: torch.Tensor, cu_query_lens: torch.Tensor,
+               out: torch.Tensor, *, scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
+               sliding_window: int = 0, stream=None) -> None:
+    """Prefill rows of the given requests into out (see include/pa.h).  q and out are the whole
+    batch's [R, Hq, D] arrays; cu_query_lens holds absolute row numbers (a slice of the batch's)."""
+    dev = q.device
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("q must be float32 or bfloat16")
+    _need(q, "q", q.dtype)
+    _need(out, "out", q.dtype, dev)
+    _need(k_cache, "k_cache", _TORCH_OF_NAME[kv_dtype], dev)
+    _need(v_cache, "v_cache", _TORCH_OF_NAME[kv_dtype], dev)
+    _need(block_tables, "block_tables", torch.int32, dev)
+    _need(context_lens, "context_lens", torch.int32, dev)
+    _need(cu_query_lens, "cu_query_lens", torch.int32, dev)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have the shape of q")
+    R, Hq, D = q.shape
+    nb, Hkv, bs, D2 = k_cache.shape
+    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shapes do not match q")
+    B = int(context_lens.shape[0])
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or cu_query_lens.shape[0] != B + 1:
+        raise ValueError("block_tables must be [num_seqs, max_blocks], cu_query_lens [num_seqs + 1]")
+    qd = PA_F32 if q.dtype == torch.float32 else PA_BF16
+    _check(load().pa_prefill(_ptr(q), qd, R, Hq, D, _ptr(k_cache), _ptr(v_cache), _DTYPE_OF_NAME[kv_dtype], nb,
+                             Hkv, bs, _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), B,
+                             _ptr(cu_query_lens), sliding_window, scale, k_scale, v_scale, _ptr(out), qd,
+                             _stream(stream)), "pa_prefill")
+
+
+def pa_split_decode_first(cu_query_lens_host, threshold: int) -> Tuple[int, int]:
+    """(decode requests, decode rows) of a decode-first batch, from HOST cumulative query lengths."""
+    import numpy as np
+    cu = np.ascontiguousarray(np.asarray(cu_query_lens_host, dtype=np.int32))
+    nd = ctypes.c_int32(0)
+    ndt = ctypes.c_int32(0)
+    _check(load().pa_split_decode_first(cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(cu.shape[0]) - 1,
+                                        threshold, ctypes.byref(nd), ctypes.byref(ndt)), "pa_split_decode_first")
+    return int(nd.value), int(ndt.value)

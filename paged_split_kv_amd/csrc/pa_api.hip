@@ -290,6 +290,75 @@ pa_status pa_attention(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_
     return from_hip(pa::launch_merge(m, head_dim, out_dtype == PA_BF16, s));
 }
 
+pa_status pa_prefill(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t num_q_heads,
+                     int32_t head_dim, const void* k_cache, const void* v_cache, pa_dtype kv_dtype,
+                     int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t num_seqs, const int32_t* cu_query_lens,
+                     int32_t sliding_window, float scale, float k_scale, float v_scale, void* out,
+                     pa_dtype out_dtype, void* stream) {
+    if (num_rows < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_blocks < 0 || num_seqs < 0 ||
+        max_blocks_per_seq < 0 || head_dim < 1 || block_size < 1 || sliding_window < 0)
+        return PA_INVALID_ARG;
+    if (q_dtype != PA_F32 && q_dtype != PA_BF16) return PA_INVALID_ARG;
+    if (kv_dtype != PA_F32 && kv_dtype != PA_BF16 && kv_dtype != PA_FP8_E4M3) return PA_INVALID_ARG;
+    if (out_dtype != q_dtype || num_q_heads % num_kv_heads != 0) return PA_INVALID_ARG;
+    if (!(scale == scale) || !(k_scale == k_scale) || !(v_scale == v_scale)) return PA_INVALID_ARG;
+    if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PA_UNSUPPORTED;
+    if (kv_dtype == PA_F32) return PA_UNSUPPORTED;
+    const int group = num_q_heads / num_kv_heads;
+    if (group > PA_MAX_GROUP_ROWS) return PA_UNSUPPORTED;
+    if (!cu_query_lens || (num_rows > 0 && (!q || !out))) return PA_INVALID_ARG;
+    if (num_seqs > 0 && (!k_cache || !v_cache || !block_tables || !context_lens)) return PA_INVALID_ARG;
+    if ((q && !aligned(q, 16)) || (out && !aligned(out, 16)) || (k_cache && !aligned(k_cache, 16)) ||
+        (v_cache && !aligned(v_cache, 16)))
+        return PA_INVALID_ARG;
+    if ((long long)num_rows * num_q_heads > (long long)INT_MAX) return PA_UNSUPPORTED;
+    if (num_rows == 0) return PA_OK;
+
+    const int lb = pa::prefill_block_tokens(head_dim, group);
+    // blocks of all requests together: sum ceil(L_b / lb) <= num_rows / lb + num_seqs
+    const long long blocks = (num_rows + lb - 1) / lb + (long long)num_seqs;
+    if (blocks * num_kv_heads > (long long)INT_MAX / 2) return PA_UNSUPPORTED;
+    pa::DecodeArgs a{};
+    a.q = q;
+    a.k_cache = static_cast<const uint8_t*>(k_cache);
+    a.v_cache = static_cast<const uint8_t*>(v_cache);
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.cu = cu_query_lens;
+    a.out = out;
+    a.out_bf16 = out_dtype == PA_BF16 ? 1 : 0;
+    a.num_rows = num_rows;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = group;
+    a.num_blocks = num_blocks;
+    a.block_size = block_size;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_seqs = num_seqs;
+    a.max_q_len = lb;
+    a.capacity = static_cast<int>(blocks);
+    a.tile_tokens = 256;
+    a.score_scale_log2 = scale * k_scale * pa::kLog2e;
+    a.v_scale = v_scale;
+    a.window = sliding_window;
+    a.prefill = 1;
+    a.block_tokens = lb;
+    return from_hip(pa::launch_prefill(a, head_dim, kv_dtype, q_dtype == PA_F32, pa::as_stream(stream)));
+}
+
+pa_status pa_split_decode_first(const int32_t* cu_query_lens_host, int32_t num_seqs, int32_t threshold,
+                                int32_t* num_decodes, int32_t* num_decode_tokens) {
+    if (num_seqs < 0 || threshold < 1 || !num_decodes || !num_decode_tokens) return PA_INVALID_ARG;
+    if (num_seqs > 0 && !cu_query_lens_host) return PA_INVALID_ARG;
+    int32_t nd = 0;
+    while (nd < num_seqs && cu_query_lens_host[nd + 1] - cu_query_lens_host[nd] <= threshold) ++nd;
+    *num_decodes = nd;
+    *num_decode_tokens = num_seqs > 0 ? cu_query_lens_host[nd] - cu_query_lens_host[0] : 0;
+    return PA_OK;
+}
+
 const char* pa_status_string(pa_status status) {
     switch (status) {
         case PA_OK: return "ok";

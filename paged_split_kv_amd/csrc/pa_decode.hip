@@ -202,6 +202,53 @@ __device__ void plan_in_place(const DecodeArgs& a, int slot, int g, int4& wk, in
 }
 
 // ---------------------------------------------------------------------------------------------
+// prefill blocks: request b's query tokens [i0, i1), block_tokens at a time.  Every wave scans the
+// cumulative query lengths 64 requests at a time and finds the request holding block qb; no barrier.
+// ---------------------------------------------------------------------------------------------
+struct PrefillBlock {
+    int b, i0, i1;
+};
+
+__device__ __forceinline__ bool find_prefill_block(const DecodeArgs& a, int qb, PrefillBlock& out) {
+    const int lane = threadIdx.x & 63;
+    const int Lb = a.block_tokens;
+    int before = 0;                                  // blocks of the requests already scanned
+    for (int c0 = 0; c0 < a.num_seqs; c0 += 64) {
+        const int r = c0 + lane;
+        int L = 0;
+        if (r < a.num_seqs) L = max(a.cu[r + 1] - a.cu[r], 0);
+        const int n = (L + Lb - 1) / Lb;
+        const int incl = wave_incl_scan(n, lane);
+        const int total = __builtin_amdgcn_readlane(incl, 63);
+        if (qb < before + total) {
+            // the owner is the first request whose blocks end past qb
+            const unsigned long long m = __builtin_amdgcn_ballot_w64(r < a.num_seqs && before + incl > qb);
+            const int o = __builtin_ctzll(m);
+            const int first = before + __builtin_amdgcn_readlane(incl, o) - __builtin_amdgcn_readlane(n, o);
+            const int j = qb - first;
+            out.b = c0 + o;
+            out.i0 = j * Lb;
+            out.i1 = min(__builtin_amdgcn_readlane(L, o), out.i0 + Lb);
+            return true;
+        }
+        before += total;
+    }
+    return false;
+}
+
+// Zero a row past the last prefill request's rows (rows before cu[0] belong to other calls).
+template <int D>
+__device__ __forceinline__ void zero_prefill_tail_row(const DecodeArgs& a, int r, int lane) {
+    if (r >= a.num_rows || r < a.cu[a.num_seqs]) return;
+    const size_t base = static_cast<size_t>(r) * a.num_q_heads * D;
+    const int n4 = a.num_q_heads * D / 4;
+    for (int e = lane; e < n4; e += 64) {
+        if (a.out_bf16) *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + base + 4 * e) = make_uint2(0u, 0u);
+        else *reinterpret_cast<float4*>(static_cast<float*>(a.out) + base + 4 * e) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
 // merge inside the decode launch
 // ---------------------------------------------------------------------------------------------
 
@@ -327,8 +374,11 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int work_groups = a.capacity * a.num_kv_heads;
     if (static_cast<int>(blockIdx.x) >= work_groups) {
-        // merge launched with the decode: trailing workgroups write the rows no slot owns as zeros
-        zero_unowned_row<D>(a, (blockIdx.x - work_groups) * C::NW + wave, lane);
+        // merge launched with the decode (or a prefill): trailing workgroups write the rows no slot
+        // owns as zeros
+        const int r = (blockIdx.x - work_groups) * C::NW + wave;
+        if (a.prefill) zero_prefill_tail_row<D>(a, r, lane);
+        else zero_unowned_row<D>(a, r, lane);
         return;
     }
     const int slot = blockIdx.x / a.num_kv_heads;
@@ -339,23 +389,48 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
     // this wave's page ids; then queries and K/V. ----
     int4 wk;
     int2 nwk;                                      // (used slots, largest slot in tiles)
-    if (a.plan_inline) {
-        plan_in_place<C::NW>(a, slot, g, wk, nwk);
+    SlotInfo si;                                   // filled here in prefill mode, after the pages otherwise
+    long long key_lo, key_hi;                      // the keys this workgroup covers, before clipping
+    if (a.prefill) {
+        // one block of query tokens: all keys its tokens see, from the first token's window start
+        PrefillBlock pb;
+        if (!find_prefill_block(a, slot, pb)) return;
+        const int b0 = __builtin_amdgcn_readfirstlane(pb.b);
+        const int i0 = __builtin_amdgcn_readfirstlane(pb.i0);
+        const int i1 = __builtin_amdgcn_readfirstlane(pb.i1);
+        const int Sb = __builtin_amdgcn_readfirstlane(max(a.context_lens[b0], 0));
+        const int c0 = __builtin_amdgcn_readfirstlane(a.cu[b0]);
+        const int Lr = __builtin_amdgcn_readfirstlane(a.cu[b0 + 1]) - c0;
+        si.b = b0;
+        si.row0 = c0 + i0;
+        si.L = i1 - i0;
+        si.S = Sb - (Lr - i1);                     // keys visible to the block's last token
+        if (si.row0 < 0 || si.row0 >= a.num_rows) si.L = 0;
+        else si.L = min(si.L, a.num_rows - si.row0);
+        key_hi = max(si.S, 0);
+        key_lo = a.window > 0 ? max(0LL, (key_hi - (si.L - 1) - a.window)) & ~15LL : 0;
+        wk = make_int4(b0, 0, 0, Sb);
+        nwk = make_int2(0, 0);
     } else {
-        wk = a.work_info[slot];
-        nwk = *reinterpret_cast<const int2*>(a.num_work);
+        if (a.plan_inline) {
+            plan_in_place<C::NW>(a, slot, g, wk, nwk);
+        } else {
+            wk = a.work_info[slot];
+            nwk = *reinterpret_cast<const int2*>(a.num_work);
+        }
+        wk = make_int4(__builtin_amdgcn_readfirstlane(wk.x), __builtin_amdgcn_readfirstlane(wk.y),
+                       __builtin_amdgcn_readfirstlane(wk.z), __builtin_amdgcn_readfirstlane(wk.w));
+        nwk = make_int2(__builtin_amdgcn_readfirstlane(nwk.x), __builtin_amdgcn_readfirstlane(nwk.y));
+        if (slot >= nwk.x) return;
+        key_lo = static_cast<long long>(max(wk.y, 0)) * a.tile_tokens;
+        key_hi = static_cast<long long>(max(wk.z, 0)) * a.tile_tokens;
     }
-    wk = make_int4(__builtin_amdgcn_readfirstlane(wk.x), __builtin_amdgcn_readfirstlane(wk.y),
-                   __builtin_amdgcn_readfirstlane(wk.z), __builtin_amdgcn_readfirstlane(wk.w));
-    nwk = make_int2(__builtin_amdgcn_readfirstlane(nwk.x), __builtin_amdgcn_readfirstlane(nwk.y));
-    const int used = nwk.x;
     const int b = wk.x;
-    if (slot >= used || b < 0 || b >= a.num_seqs) return;
+    if (b < 0 || b >= a.num_seqs) return;
     const int* bt_row = a.block_tables + static_cast<size_t>(b) * a.max_blocks;
     const long long reach = static_cast<long long>(a.max_blocks) * a.block_size;
-    const int plan_lo = static_cast<int>(min(static_cast<long long>(max(wk.y, 0)) * a.tile_tokens, reach));
-    const int plan_hi = static_cast<int>(max(min(static_cast<long long>(max(wk.z, 0)) * a.tile_tokens, reach),
-                                             static_cast<long long>(plan_lo)));
+    const int plan_lo = static_cast<int>(min(key_lo, reach));
+    const int plan_hi = static_cast<int>(max(min(key_hi, reach), static_cast<long long>(plan_lo)));
     const int plan_chunks = (plan_hi - plan_lo + 15) >> 4;
 
     // Chunks are dealt to waves in units of `unit` consecutive chunks: wave w owns units w, w + NW, ...
@@ -363,9 +438,10 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
     // over the NW waves, so that slot's waves and every other wave with a full unit carry the same
     // load and finish together, while a smaller slot runs fewer streaming waves and leaves more of the
     // bandwidth to the big ones.  Any unit >= 1 covers every chunk of every slot exactly once.
+    // (A prefill block is its own slot: its chunks are split evenly over the waves.)
     const int cpt = a.tile_tokens >> 4;          // 16-key chunks per tile
-    const int unit = static_cast<int>(min(max(1LL, (static_cast<long long>(max(nwk.y, 1)) * cpt + C::NW - 1) /
-                                                       C::NW), 1LL << 30));
+    const long long unit_chunks = a.prefill ? plan_chunks : static_cast<long long>(max(nwk.y, 1)) * cpt;
+    const int unit = static_cast<int>(min(max(1LL, (unit_chunks + C::NW - 1) / C::NW), 1LL << 30));
     auto chunk_of = [&](int k) -> int {
         const int j = k / unit;
         return (wave + C::NW * j) * unit + (k - j * unit);
@@ -391,8 +467,7 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
 #pragma unroll
     for (int st = 0; st < C::PF; ++st) pnext[st] = page_load(st + C::PF);
 
-    SlotInfo si;
-    {
+    if (!a.prefill) {
         const int S = __builtin_amdgcn_readfirstlane(max(a.context_lens[b], 0));
         int row0 = b, L = 1;
         if (a.cu) {
@@ -406,9 +481,9 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
         si.row0 = row0;
         si.L = L;
         si.S = S;
-        si.k_hi = min(plan_hi, S);
-        si.k_lo = min(plan_lo, si.k_hi);
     }
+    si.k_hi = min(plan_hi, max(si.S, 0));
+    si.k_lo = min(plan_lo, si.k_hi);
     const int G = a.group;
     const int M = G * si.L;                       // valid query rows (<= ROWS)
     const int col = lane & 15;                    // MFMA column = query row within a block
@@ -681,7 +756,8 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
     // ---- write the slot's states: rows n < M, token i = n / G, head g*G + n % G ----
     constexpr int D4 = D / 4;
     const size_t slot_base = static_cast<size_t>(slot) * a.max_q_len;
-    const bool single = a.out != nullptr && a.reduce_info[b].y == 1;
+    // a prefill block, or a request with one partition, holds its rows' whole softmax state
+    const bool single = a.prefill || (a.out != nullptr && a.reduce_info[b].y == 1);
     for (int e = tid; e < (single ? 0 : M * D4); e += 64 * C::NW) {
         const int n = e / D4;
         const int d4 = e - n * D4;
@@ -703,8 +779,8 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
     if (a.out == nullptr) return;
 
     // ---- merge in the same launch: the last workgroup of (request, kv head) to finish merges ----
-    if (a.reduce_info[b].y == 1) {
-        // a request with one partition: this workgroup holds the whole softmax state
+    if (single) {
+        // a prefill block or a request with one partition: this workgroup holds the whole state
         for (int e = tid; e < M * D4; e += 64 * C::NW) {
             const int n = e / D4;
             const int d4 = e - n * D4;
@@ -865,6 +941,26 @@ hipError_t launch_d(const DecodeArgs& a, pa_dtype kv, int ncb, bool qf32, dim3 g
 }
 
 }  // namespace
+
+int prefill_block_tokens(int head_dim, int group) {
+    // rows per workgroup: 64 (four 16-row matrix blocks) where the operands fit in registers, one
+    // block for head_dim 256, more only when a single token's heads need them
+    int rows = head_dim <= 128 ? 64 : 16;
+    while (rows < group && rows < PA_MAX_GROUP_ROWS) rows *= 2;
+    return group > 0 ? (rows / group > 0 ? rows / group : 1) : 1;
+}
+
+hipError_t launch_prefill(const DecodeArgs& a, int head_dim, pa_dtype kv_dtype, bool q_f32,
+                          hipStream_t stream) {
+    const int rows = a.group * a.block_tokens;
+    const int ncb = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+    const dim3 grid(static_cast<unsigned>(a.capacity) * static_cast<unsigned>(a.num_kv_heads));
+    switch (head_dim) {
+        case 64: return launch_d<64>(a, kv_dtype, ncb, q_f32, grid, stream);
+        case 128: return launch_d<128>(a, kv_dtype, ncb, q_f32, grid, stream);
+        default: return launch_d<256>(a, kv_dtype, ncb, q_f32, grid, stream);
+    }
+}
 
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, pa_dtype kv_dtype, bool q_f32,
                          hipStream_t stream) {

@@ -254,6 +254,10 @@ struct DecodeArgs {
     const int2* reduce_info;    // (first slot, partitions) per request; needed when out is set
     void* out;                  // nullable: when set, the merge runs inside the decode launch
     int window;                 // 0: none; W > 0: each query token sees its last W visible keys
+    // prefill mode: each workgroup takes a block of up to block_tokens query tokens of one request
+    // (all its visible keys, one partition) and writes the normalised rows to out directly
+    int prefill;
+    int block_tokens;
     // planning in place (num_seqs <= kInlinePlanSeqs): every workgroup evaluates the planner's rule
     // itself; the plan is also stored to these buffers for the merge and the caller
     int plan_inline;
@@ -288,5 +292,9 @@ hipError_t launch_plan(const int32_t* context_lens, const int32_t* cu, int num_s
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, pa_dtype kv_dtype, bool q_f32,
                          hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int head_dim, bool out_bf16, hipStream_t stream);
+// Query tokens per prefill workgroup for a group of G query heads per kv head (G * tokens rows).
+int prefill_block_tokens(int head_dim, int group);
+hipError_t launch_prefill(const DecodeArgs& a, int head_dim, pa_dtype kv_dtype, bool q_f32,
+                          hipStream_t stream);
 
 }  // namespace pa

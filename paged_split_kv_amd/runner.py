@@ -109,3 +109,50 @@ def run_case(case, plan: Optional[PlanConfig] = None, fused: bool = True,
              whole: bool = False) -> torch.Tensor:
     """Plan, decode and merge one workload Case; returns the output tensor (device)."""
     return DecodeStep.for_case(case, plan).run_case(case, fused=fused, whole=whole)
+
+
+class MixedStep:
+    """The decode-first split of a mixed batch (requests ordered decodes first): the leading requests
+    with at most `threshold` query tokens go through pa_attention (split-KV decode, rows written to a
+    view of the output), the rest through pa_prefill on the same stream.  The split is taken from a
+    host copy of the cumulative query lengths, as a batch builder holds them; buffers are made once.
+    With concurrent=True the two parts, which read the same inputs and write disjoint rows, run on
+    two streams (the prefill on a second stream of default priority) and join before returning."""
+
+    def __init__(self, case, threshold: int, plan: Optional[PlanConfig] = None, concurrent: bool = False):
+        self.threshold = threshold
+        self.side = torch.cuda.Stream(device=case.q.device) if concurrent else None
+        self.nd, self.ndt = B.pa_split_decode_first(case.cu_query_lens.cpu().numpy(), threshold)
+        self.out = torch.empty_like(case.q)
+        self.dec = None
+        if self.nd > 0:
+            self.dec = DecodeStep(num_seqs=self.nd, num_rows=self.ndt, num_q_heads=case.num_q_heads,
+                                  num_kv_heads=case.num_kv_heads, head_dim=case.head_dim,
+                                  max_q_len=threshold, out_dtype=case.q.dtype, device=case.q.device,
+                                  plan=plan)
+            self.dec.out = self.out[:self.ndt]
+
+    def run(self, case, stream=None) -> torch.Tensor:
+        nd, ndt = self.nd, self.ndt
+        main = stream if stream is not None else torch.cuda.current_stream(case.q.device)
+        pre = main
+        if self.side is not None and self.dec is not None:
+            self.side.wait_stream(main)
+            pre = self.side
+        B.pa_prefill(case.q, case.k_cache, case.v_cache, case.kv_dtype, case.block_tables[nd:],
+                     case.context_lens[nd:], case.cu_query_lens[nd:], self.out, scale=case.scale,
+                     k_scale=case.k_scale, v_scale=case.v_scale, sliding_window=case.window, stream=pre)
+        if self.dec is not None:
+            self.dec.attention(case.q[:ndt], case.k_cache, case.v_cache, case.kv_dtype, case.block_tables[:nd],
+                               case.context_lens[:nd], scale=case.scale,
+                               cu_query_lens=case.cu_query_lens[:nd + 1], k_scale=case.k_scale,
+                               v_scale=case.v_scale, sliding_window=case.window, stream=main)
+        if pre is not main:
+            main.wait_stream(pre)
+        return self.out
+
+
+def mixed_step(case, threshold: int, plan: Optional[PlanConfig] = None, stream=None,
+               concurrent: bool = False) -> torch.Tensor:
+    """One decode-first split step of a mixed batch (see MixedStep)."""
+    return MixedStep(case, threshold, plan, concurrent).run(case, stream)

@@ -300,6 +300,15 @@ def make_config(name: str, device="cpu", step: Optional[int] = None, seed: Optio
 CONFIG_NAMES: List[str] = ["tiny_fp32", "skewed_bf16", "long_bf16", "verify_bf16", "fp8_kv"]
 
 
+def make_mixed_case(device="cpu", seed: int = 5) -> Case:
+    """A mixed batch, decodes first: 7 decodes at 16384 tokens and a new 100-token prompt, at the
+    per-rank shapes of TP=2 (12 query heads, 2 kv heads, head_dim 256), bf16 (opengfx1030/vllm-rdna
+    PR #29, Problem table, second row)."""
+    return build_case("mixed_7x16k_prompt100", [16384] * 7 + [100], num_q_heads=12, num_kv_heads=2,
+                      head_dim=256, block_size=16, kv_dtype="bf16", q_dtype="bf16", seed=seed,
+                      q_lens=[1] * 7 + [100], device=device)
+
+
 # ----------------------------------------------------------------------------------------------
 # sparse / top-k layers: every request reads a fixed-size selection of pages, so lengths are
 # near-uniform (ROCm/ATOM PR #2366 section 3: sparse sites read a fixed top-k window; PR #2514

@@ -194,3 +194,43 @@ def test_attention_argument_checks():
 
 def test_merge_refuses_misaligned_out():
     assert _merge_status(out=264) == B.PA_INVALID_ARG
+
+
+def _prefill_status(**kw):
+    a = dict(_GOOD)
+    a.update(dict(cu=256, out=512))
+    a.update(kw)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return B.load().pa_prefill(vp(a["q"]), a["qd"], a["R"], a["Hq"], a["D"], vp(a["k"]), vp(a["v"]), a["kvd"],
+                               a["nb"], a["Hkv"], a["bs"], vp(a["bt"]), a["mb"], vp(a["ctx"]), a["Bn"],
+                               vp(a["cu"]), a["win"], a["scale"], a["ks"], a["vs"], vp(a["out"]), a["od"], None)
+
+
+def test_prefill_argument_checks():
+    assert _prefill_status(cu=None) == B.PA_INVALID_ARG             # the query lengths are required
+    assert _prefill_status(kvd=B.PA_F32) == B.PA_UNSUPPORTED        # matrix-core path only
+    assert _prefill_status(D=96) == B.PA_UNSUPPORTED
+    assert _prefill_status(bs=32) == B.PA_UNSUPPORTED
+    assert _prefill_status(Hq=15) == B.PA_INVALID_ARG
+    assert _prefill_status(od=B.PA_F32) == B.PA_INVALID_ARG
+    assert _prefill_status(out=None) == B.PA_INVALID_ARG
+    assert _prefill_status(out=520) == B.PA_INVALID_ARG
+    assert _prefill_status(win=-1) == B.PA_INVALID_ARG
+    assert _prefill_status(scale=float("nan")) == B.PA_INVALID_ARG
+    assert _prefill_status(R=0) == B.PA_OK                         # nothing to write: no launch
+
+
+def test_split_decode_first_on_the_host():
+    # 7 decodes then a 100-token prompt (opengfx1030/vllm-rdna PR #29 table: 7 decodes + a new prompt)
+    cu = [0, 1, 2, 3, 4, 5, 6, 7, 107]
+    assert B.pa_split_decode_first(cu, 1) == (7, 7)
+    # verify rows of 3 (1 + 2 speculative tokens) first, then two prefill chunks
+    cu = [0, 3, 6, 9, 209, 259]
+    assert B.pa_split_decode_first(cu, 3) == (3, 9)
+    assert B.pa_split_decode_first(cu, 1) == (0, 0)
+    assert B.pa_split_decode_first(cu, 1000) == (5, 259)
+    assert B.pa_split_decode_first([0], 1) == (0, 0)
+    # a decode after a prefill is not moved: the split is the leading run only
+    assert B.pa_split_decode_first([0, 1, 50, 51], 1) == (1, 1)
+    with pytest.raises(B.PaError):
+        B.pa_split_decode_first([0, 1], 0)

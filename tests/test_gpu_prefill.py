@@ -1,0 +1,105 @@
+"""Prefill rows and the decode-first split of mixed batches, against the fp64 oracle.
+
+The decode-first split (opengfx1030/vllm-rdna PR #29, Change 2): requests are ordered decodes first;
+the leading requests with at most 1 + k query tokens take the split-KV decode, the rest a prefill
+kernel on the rebased remainder, both writing slices of the layer output.  Token i of a request with
+L tokens and S keys sees S - (L - 1 - i) keys (Change 1), the window applying per token.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_split_kv_amd import binding as B
+from paged_split_kv_amd import workloads as W
+from paged_split_kv_amd.runner import PlanConfig, mixed_step
+from _util import announce, assert_close, oracle_direct, to_f64, tolerance_kind
+from test_gpu_decode import _zero_rows
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+# (name, ctx, q_lens, Hq, Hkv, D, bs, kv, q, pad, window)
+PREFILL = [
+    ("bf16_d128_prompts", [100, 300, 64, 9], [100, 300, 64, 9], 16, 2, 128, 16, "bf16", "bf16", 2, 0),
+    ("bf16_d128_chunk_behind_prefix", [1300, 5000], [200, 77], 16, 2, 128, 16, "bf16", "bf16", 0, 0),
+    ("bf16_d256_g6", [100, 700], [100, 33], 12, 2, 256, 16, "bf16", "bf16", 1, 0),
+    ("bf16_d64_g4_bs64", [520, 70], [250, 70], 8, 2, 64, 64, "bf16", "bf16", 0, 0),
+    ("fp8_d128", [400, 2100], [150, 100], 16, 2, 128, 16, "fp8", "bf16", 0, 0),
+    ("bf16_window50", [300, 1000], [120, 64], 16, 2, 128, 16, "bf16", "bf16", 1, 50),
+    ("fp8_d256_window32", [900], [96], 12, 2, 256, 16, "fp8", "bf16", 0, 32),
+    ("qf32_tokens_without_keys", [10, 40], [30, 40], 8, 1, 128, 16, "bf16", "f32", 2, 0),
+]
+
+
+def _case(spec, seed):
+    name, ctx, ql, Hq, Hkv, D, bs, kv, qd, pad, win = spec
+    c = W.build_case(name, ctx, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs, kv_dtype=kv,
+                     q_dtype=qd, seed=seed, q_lens=ql, pad_rows=pad, device=DEV)
+    c.window = win
+    return c
+
+
+@pytest.mark.parametrize("spec", PREFILL, ids=[p[0] for p in PREFILL])
+def test_prefill_matches_oracle(spec):
+    case = _case(spec, seed=41)
+    announce(f"prefill {spec[0]}")
+    out = torch.full_like(case.q, float("nan"))
+    B.pa_prefill(case.q, case.k_cache, case.v_cache, case.kv_dtype, case.block_tables, case.context_lens,
+                 case.cu_query_lens, out, scale=case.scale, k_scale=case.k_scale, v_scale=case.v_scale,
+                 sliding_window=case.window)
+    torch.cuda.synchronize()
+    got = to_f64(out)
+    assert_close(got, oracle_direct(case), tolerance_kind(case), spec[0])
+    assert (got[_zero_rows(case)] == 0.0).all()
+
+
+def test_prefill_leaves_rows_before_its_first_request_alone():
+    case = _case(PREFILL[0], seed=42)
+    # treat requests 1.. as the prefill part: rows [cu[1], R) are written, rows before stay poisoned
+    out = torch.full_like(case.q, float("nan"))
+    B.pa_prefill(case.q, case.k_cache, case.v_cache, case.kv_dtype, case.block_tables[1:], case.context_lens[1:],
+                 case.cu_query_lens[1:], out, scale=case.scale)
+    torch.cuda.synchronize()
+    c1 = int(case.cu_query_lens[1].item())
+    got = to_f64(out)
+    assert np.isnan(got[:c1]).all()
+    assert_close(got[c1:], oracle_direct(case)[c1:], "bf16", "prefill part")
+
+
+# (name, ctx, q_lens, Hq, Hkv, D, bs, kv, q, pad, window, threshold)
+MIXED = [
+    # 7 decodes + a new 100-token prompt, TP=2 shapes (H 12/2, D 256) as on the vllm-rdna page
+    ("seven_decodes_and_a_prompt", [2000] * 7 + [100], [1] * 7 + [100], 12, 2, 256, 16, "bf16", "bf16", 1, 0, 1),
+    # MTP verify rows (1 + 2 speculative tokens), then two prefill chunks
+    ("verify_then_chunks", [3000, 900, 17, 1500, 260], [3, 3, 3, 200, 60], 16, 2, 128, 16, "bf16", "bf16", 2, 0, 3),
+    ("fp8_mixed_window", [5000, 40, 700], [1, 1, 300], 16, 2, 128, 16, "fp8", "bf16", 0, 64, 1),
+    ("all_decode", [700, 33, 1], [1, 1, 1], 16, 2, 128, 16, "bf16", "bf16", 1, 0, 1),
+    ("all_prefill", [700, 333], [70, 33], 16, 2, 128, 16, "bf16", "bf16", 1, 0, 1),
+]
+
+
+@pytest.mark.parametrize("concurrent", [False, True], ids=["one_stream", "two_streams"])
+@pytest.mark.parametrize("spec", MIXED, ids=[m[0] for m in MIXED])
+def test_mixed_batch_decode_first_split(spec, concurrent):
+    *base, threshold = spec
+    case = _case(tuple(base), seed=43)
+    announce(f"mixed {spec[0]} threshold {threshold} concurrent {concurrent}")
+    out = mixed_step(case, threshold, PlanConfig(cu_count=256), concurrent=concurrent)
+    torch.cuda.synchronize()
+    got = to_f64(out)
+    assert_close(got, oracle_direct(case), tolerance_kind(case), spec[0])
+    assert (got[_zero_rows(case)] == 0.0).all()
+
+
+def test_seven_decodes_at_16k_and_a_prompt_full_size():
+    """The vllm-rdna table's second scenario at its sizes: 7 decodes at 16384 tokens and a new
+    100-token prompt, TP=2 per rank (H 12/2), D 256."""
+    case = W.build_case("mixed_16k", [16384] * 7 + [100], num_q_heads=12, num_kv_heads=2, head_dim=256,
+                        block_size=16, kv_dtype="bf16", q_dtype="bf16", seed=44, q_lens=[1] * 7 + [100],
+                        device=DEV)
+    announce("mixed 7 x 16k + 100-token prompt")
+    out = mixed_step(case, 1, PlanConfig(cu_count=256))
+    torch.cuda.synchronize()
+    assert_close(to_f64(out), oracle_direct(case), "bf16", "mixed full size")
