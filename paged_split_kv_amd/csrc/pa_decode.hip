@@ -336,7 +336,15 @@ struct Mfma {
     static constexpr int KSTEPS = D / 32;              // k-steps of the S^T product
     static constexpr int DT = D / 16;                  // 16-wide d tiles of the P.V product
     static constexpr int NW = 4;                       // waves per workgroup
-    static constexpr int WAVE_LDS = 2 * 16 * LRB;      // K then V chunk, per wave
+    // chunks in flight per wave: as many as the registers hold without spilling (scratch traffic would
+    // itself be waited for in order and stall the pipeline); an fp8 chunk takes half the registers
+    static constexpr int PF_BF16 = D == 64 ? (NCB <= 2 ? 4 : 3) : (D == 128 ? (NCB == 1 ? 2 : (NCB == 2 ? 3 : 2)) : (NCB == 1 ? 2 : 1));
+    static constexpr int PF_FP8 = D == 64 ? (NCB <= 2 ? 8 : 6) : (D == 128 ? (NCB == 1 ? 4 : (NCB == 2 ? 4 : 2)) : (NCB == 1 ? 4 : 1));
+    static constexpr int PF = KV8 ? PF_FP8 : PF_BF16;
+    // chunks per compute step: two where the registers allow, so each step runs two independent
+    // score chains and one softmax pass over 32 keys (the per-chunk latency of a lone wave drops)
+    static constexpr int CG = (D <= 128 && NCB == 1 && PF % 2 == 0) ? 2 : 1;
+    static constexpr int WAVE_LDS = CG * 2 * 16 * LRB; // K then V of each chunk of a step, per wave
     static constexpr int STAGE_LDS = NW * WAVE_LDS;
     static constexpr int ROWS = 16 * NCB;              // query rows per workgroup (padded)
     static constexpr int APITCH = D + 4;               // fp32 pitch of the LDS merge buffer
@@ -345,11 +353,7 @@ struct Mfma {
     // Waves per SIMD the register budget is cut for: 2 (two workgroups per CU, 256 registers per lane)
     // where operands and accumulators fit, else 1 (512 registers) rather than spilling.
     static constexpr int WAVES = (D == 64 || (D == 128 && NCB == 1)) ? 2 : 1;
-    // chunks in flight per wave: as many as the registers hold without spilling (scratch traffic would
-    // itself be waited for in order and stall the pipeline); an fp8 chunk takes half the registers
-    static constexpr int PF_BF16 = D == 64 ? (NCB <= 2 ? 4 : 3) : (D == 128 ? (NCB == 1 ? 2 : (NCB == 2 ? 3 : 2)) : (NCB == 1 ? 2 : 1));
-    static constexpr int PF_FP8 = D == 64 ? (NCB <= 2 ? 8 : 6) : (D == 128 ? (NCB == 1 ? 4 : (NCB == 2 ? 4 : 2)) : (NCB == 1 ? 4 : 1));
-    static constexpr int PF = KV8 ? PF_FP8 : PF_BF16;
+
 };
 
 // Byte offset of 16-byte column c of row r in a per-wave bf16 LDS tile (XOR swizzle on the column).
@@ -535,8 +539,7 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
     const int nkeys = si.k_hi - si.k_lo;
     const int nchunks = nkeys > 0 ? (nkeys + 15) >> 4 : 0;
     const size_t head_stride = static_cast<size_t>(a.block_size) * C::GRB;   // HBM bytes per (block, kv head)
-    uint8_t* klds = lds + wave * C::WAVE_LDS;
-    uint8_t* vlds = klds + 16 * C::LRB;
+    uint8_t* const wlds = lds + wave * C::WAVE_LDS;   // chunk c of a step: K at c * 32 rows, then V
 
     // this wave's number of chunks: its full units, plus the ragged last unit if it owns it
     const int full_units = nchunks / unit;
@@ -575,7 +578,9 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
     };
 
     // Write a staged chunk into the wave's LDS tiles as bf16 rows; rows >= nv are zero.
-    auto stage = [&](int st, int nv, bool full) {
+    auto stage = [&](int st, int nv, bool full, int cbuf) {
+        uint8_t* const klds = wlds + cbuf * 2 * 16 * C::LRB;
+        uint8_t* const vlds = klds + 16 * C::LRB;
 #pragma unroll
         for (int it = 0; it < C::NLD; ++it) {
             const int f = it * 64 + lane;
@@ -626,57 +631,75 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
     for (int st = 0; st < C::PF; ++st) issue(st, st, pfirst[st]);
 
     // whole rounds of PF chunks; the padding chunks past my_chunks are empty and fetch nothing
+    constexpr int CG = C::CG;
     const int rounds = (my_chunks + C::PF - 1) / C::PF;
     for (int k0 = 0; k0 < rounds * C::PF; k0 += C::PF) {
 #pragma unroll
-        for (int st = 0; st < C::PF; ++st) {
-            const int k = k0 + st;
-            const int key0 = si.k_lo + 16 * chunk_of(k);
-            const int nv = nvalid_st[st];
-
-            compiler_fence();
-            if (nv == 16) stage(st, 16, true);     // uniform: only a slot's ragged last chunk is partial
-            else stage(st, nv, false);
-            compiler_fence();
-            const int page = pnext[st];            // fetched before chunk k's K/V: already here
-            pnext[st] = page_load(k + 2 * C::PF);
-            issue(st, k + C::PF, page);
-
-            // K operands (A of S^T): row = col, d = 32s + 8*grp .. +8
-            bf16x8_t kop[C::KSTEPS];
+        for (int sg = 0; sg < C::PF; sg += CG) {
+            // stage the step's CG chunks, each followed by the loads PF chunks ahead
+            int key0[CG], nvc[CG];
 #pragma unroll
-            for (int s = 0; s < C::KSTEPS; ++s)
-                kop[s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
-                                                          klds + lds_col<C::LRB, C::SWM>(col, 4 * s + grp)));
-            // V^T operands (A of O^T = V^T.P^T): d = 16t + col, keys 4*grp + j, via transposed reads
-            short4_t vop[C::DT];
+            for (int c = 0; c < CG; ++c) {
+                const int st = sg + c;
+                const int k = k0 + st;
+                key0[c] = si.k_lo + 16 * chunk_of(k);
+                nvc[c] = nvalid_st[st];
+                compiler_fence();
+                if (nvc[c] == 16) stage(st, 16, true, c);   // uniform: only a ragged last chunk is partial
+                else stage(st, nvc[c], false, c);
+                compiler_fence();
+                const int page = pnext[st];            // fetched before chunk k's K/V: already here
+                pnext[st] = page_load(k + 2 * C::PF);
+                issue(st, k + C::PF, page);
+            }
+
+            // K operands (A of S^T): row = col, d = 32s + 8*grp .. +8; V^T operands (A of
+            // O^T = V^T.P^T): d = 16t + col, keys 4*grp + j, via transposed reads
+            bf16x8_t kop[CG][C::KSTEPS];
+            short4_t vop[CG][C::DT];
 #pragma unroll
-            for (int t = 0; t < C::DT; ++t) {
-                const int d0 = 16 * t + tr_d0;
-                const int off = lds_col<C::LRB, C::SWM>(tr_row, d0 >> 3) + ((d0 & 7) << 1);
-                typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-                typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
-                const bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(vlds + off));
-                vop[t] = __builtin_bit_cast(short4_t, v);
+            for (int c = 0; c < CG; ++c) {
+                const uint8_t* klds = wlds + c * 2 * 16 * C::LRB;
+                const uint8_t* vlds = klds + 16 * C::LRB;
+#pragma unroll
+                for (int s = 0; s < C::KSTEPS; ++s)
+                    kop[c][s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
+                                                                 klds + lds_col<C::LRB, C::SWM>(col, 4 * s + grp)));
+#pragma unroll
+                for (int t = 0; t < C::DT; ++t) {
+                    const int d0 = 16 * t + tr_d0;
+                    const int off = lds_col<C::LRB, C::SWM>(tr_row, d0 >> 3) + ((d0 & 7) << 1);
+                    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+                    typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+                    const bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(vlds + off));
+                    vop[c][t] = __builtin_bit_cast(short4_t, v);
+                }
             }
             compiler_fence();
 
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
-                float4_t sacc = {0.f, 0.f, 0.f, 0.f};
+                float4_t sacc[CG];
 #pragma unroll
-                for (int s = 0; s < C::KSTEPS; ++s)
-                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[s], qop[cb][s], sacc, 0, 0, 0);
-                // lane holds keys key0 + 4*grp + j for query row 16cb + col
-                const int lim = min(nv, nvis[cb] - key0);
-                const int low = nlo[cb] - key0;           // window start relative to the chunk
-                float x[4];
+                for (int c = 0; c < CG; ++c) {
+                    sacc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < C::KSTEPS; ++s)
+                        sacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[c][s], qop[cb][s], sacc[c], 0, 0, 0);
+                }
+                // lane holds keys key0[c] + 4*grp + j of each chunk for query row 16cb + col
+                float x[CG][4];
                 float mt = -INFINITY;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int kj = 4 * grp + j;
-                    x[j] = (kj < lim && kj >= low) ? sacc[j] * a.score_scale_log2 : -INFINITY;
-                    mt = fmaxf(mt, x[j]);
+                for (int c = 0; c < CG; ++c) {
+                    const int lim = min(nvc[c], nvis[cb] - key0[c]);
+                    const int low = nlo[cb] - key0[c];    // window start relative to the chunk
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int kj = 4 * grp + j;
+                        x[c][j] = (kj < lim && kj >= low) ? sacc[c][j] * a.score_scale_log2 : -INFINITY;
+                        mt = fmaxf(mt, x[c][j]);
+                    }
                 }
                 mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
                 mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
@@ -692,17 +715,20 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
                     m_run[cb] = mnew;
                 }
                 const float mref = m_run[cb] == -INFINITY ? 0.f : m_run[cb];
-                float p[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    p[j] = __builtin_amdgcn_exp2f(x[j] - mref);
-                    l_run[cb] += p[j];
+                for (int c = 0; c < CG; ++c) {
+                    float p[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        p[j] = __builtin_amdgcn_exp2f(x[c][j] - mref);
+                        l_run[cb] += p[j];
+                    }
+                    u32x2_t pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+                    const short4_t pop = __builtin_bit_cast(short4_t, pk);
+#pragma unroll
+                    for (int t = 0; t < C::DT; ++t)
+                        acc[cb][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop[c][t], pop, acc[cb][t], 0, 0, 0);
                 }
-                u32x2_t pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
-                const short4_t pop = __builtin_bit_cast(short4_t, pk);
-#pragma unroll
-                for (int t = 0; t < C::DT; ++t)
-                    acc[cb][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop[t], pop, acc[cb][t], 0, 0, 0);
             }
         }
     }
