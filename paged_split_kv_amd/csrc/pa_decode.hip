@@ -446,10 +446,16 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
     const int cpt = a.tile_tokens >> 4;          // 16-key chunks per tile
     const long long unit_chunks = a.prefill ? plan_chunks : static_cast<long long>(max(nwk.y, 1)) * cpt;
     const int unit = static_cast<int>(min(max(1LL, (unit_chunks + C::NW - 1) / C::NW), 1LL << 30));
+    // Every slot of the plan (and every prefill block) spans at most NW units, so a wave's live
+    // chunks are all in its first unit: k < unit takes no division.  Past that (only the empty
+    // padding chunks, or a plan whose largest-slot word understates a slot) the general form applies.
     auto chunk_of = [&](int k) -> int {
+        if (k < unit) return wave * unit + k;
         const int j = k / unit;
         return (wave + C::NW * j) * unit + (k - j * unit);
     };
+    // pages hold 16, 64 or 128 tokens: key -> (page ordinal, row) by shift and mask
+    const int page_shift = __builtin_ctz(a.block_size);
 
     // Every memory instruction of the streaming loop is issued unconditionally, so each iteration
     // issues the same number of vector loads and the compiler can wait for exactly the chunk it
@@ -461,7 +467,7 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
         __builtin_amdgcn_make_buffer_rsrc(const_cast<int*>(bt_row), 0, a.max_blocks * 4, kRawBufferWord3);
     auto page_load = [&](int k) -> int {       // page id of the wave's k-th chunk; 0 past the plan
         const int c = chunk_of(k);
-        const unsigned off = c < plan_chunks ? static_cast<unsigned>((plan_lo + 16 * c) / a.block_size) * 4u
+        const unsigned off = c < plan_chunks ? static_cast<unsigned>((plan_lo + 16 * c) >> page_shift) * 4u
                                              : 0xfffffff0u;
         return __builtin_amdgcn_raw_buffer_load_b32(bt_rsrc, off, 0, 0);
     };
@@ -559,7 +565,7 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
         const bool live = k < my_chunks && blk >= 0 && blk < a.num_blocks;
         const int nv = live ? max(min(16, si.k_hi - key0), 0) : 0;
         nvalid_st[st] = nv;
-        const int off = key0 % a.block_size;
+        const int off = key0 & (a.block_size - 1);
         const size_t base = nv > 0 ? (static_cast<size_t>(blk) * a.num_kv_heads + g) * head_stride +
                                          static_cast<size_t>(off) * C::GRB
                                    : 0;
