@@ -721,6 +721,7 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
                     m_run[cb] = mnew;
                 }
                 const float mref = m_run[cb] == -INFINITY ? 0.f : m_run[cb];
+                uint32_t pk[CG][2];
 #pragma unroll
                 for (int c = 0; c < CG; ++c) {
                     float p[4];
@@ -729,11 +730,29 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
                         p[j] = __builtin_amdgcn_exp2f(x[c][j] - mref);
                         l_run[cb] += p[j];
                     }
-                    u32x2_t pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
-                    const short4_t pop = __builtin_bit_cast(short4_t, pk);
+                    pk[c][0] = pack_bf16x2(p[0], p[1]);
+                    pk[c][1] = pack_bf16x2(p[2], p[3]);
+                }
+                if constexpr (CG == 2) {
+                    // one K = 32 product per d tile over both chunks: the contraction index 8*grp + jj
+                    // stands for key 4*grp + jj of the first chunk (jj < 4) or of the second (jj >= 4),
+                    // which is exactly what this lane holds of P and of the transposed V reads
+                    const u32x4_t pc = {pk[0][0], pk[0][1], pk[1][0], pk[1][1]};
+                    const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pc);
+#pragma unroll
+                    for (int t = 0; t < C::DT; ++t) {
+                        const u32x2_t va = __builtin_bit_cast(u32x2_t, vop[0][t]);
+                        const u32x2_t vb = __builtin_bit_cast(u32x2_t, vop[1][t]);
+                        const u32x4_t vc = {va[0], va[1], vb[0], vb[1]};
+                        acc[cb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vc), pop,
+                                                                             acc[cb][t], 0, 0, 0);
+                    }
+                } else {
+                    const u32x2_t pc = {pk[0][0], pk[0][1]};
+                    const short4_t pop = __builtin_bit_cast(short4_t, pc);
 #pragma unroll
                     for (int t = 0; t < C::DT; ++t)
-                        acc[cb][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop[c][t], pop, acc[cb][t], 0, 0, 0);
+                        acc[cb][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop[0][t], pop, acc[cb][t], 0, 0, 0);
                 }
             }
         }
