@@ -38,25 +38,37 @@ class OracleError(RuntimeError):
     pass
 
 
+def compile_source(src: str, lib_path: str) -> str:
+    """gcc with strict IEEE (no fast-math, no contraction): `src` -> shared library `lib_path`."""
+    tmp = lib_path + f".tmp{os.getpid()}"
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-ffp-contract=off",
+           "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, lib_path)
+    return lib_path
+
+
 def build(force: bool = False) -> str:
-    """Compile the oracle with gcc (strict IEEE: no fast-math, no contraction)."""
+    """Compile the oracle (pa_oracle.c -> liboracle.so) when missing or older than its source."""
     if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-        tmp = _LIB_PATH + f".tmp{os.getpid()}"
-        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-ffp-contract=off",
-               "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
-        subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB_PATH)
+        compile_source(_SRC, _LIB_PATH)
     return _LIB_PATH
 
 
 _lib = None
 
+# A test that plants a mistake in a copy of pa_oracle.c builds that copy elsewhere and names the
+# library here, so the pin tests run against it in a child process.
+_OVERRIDE_ENV = "PA_ORACLE_LIB"
+
 
 def _load():
     global _lib
     if _lib is None:
-        build()
-        lib = ctypes.CDLL(_LIB_PATH)
+        path = os.environ.get(_OVERRIDE_ENV)
+        if not path:
+            path = build()
+        lib = ctypes.CDLL(path)
         i32p = ctypes.POINTER(ctypes.c_int32)
         vp = ctypes.c_void_p
         c_int = ctypes.c_int

@@ -171,6 +171,7 @@ int orc_plan(const int32_t* context_lens, const int32_t* cu, int num_seqs, int n
             if (parts > tiles) parts = tiles;
             if (parts > max_partitions) parts = max_partitions;
         }
+        if (slot + parts > capacity) return ORC_INVALID; /* never writes past the caller's buffer */
         reduce_info[2 * b + 0] = (int32_t)slot;
         reduce_info[2 * b + 1] = (int32_t)parts;
         for (int64_t j = 0; j < parts; ++j) {
