@@ -25,6 +25,8 @@
 //  * fp8 (OCP e4m3fn) codes are widened exactly to bf16 in registers; k_scale folds into the score
 //    scale and v_scale into the final state.  Probabilities are rounded to bf16 for P.V.
 // The fp32-cache kernel is plain vector code (fp32 throughout) with the same outputs.
+#include <type_traits>
+
 #include "pa_device.h"
 
 namespace pa {
@@ -336,23 +338,37 @@ struct Mfma {
     static constexpr int KSTEPS = D / 32;              // k-steps of the S^T product
     static constexpr int DT = D / 16;                  // 16-wide d tiles of the P.V product
     static constexpr int NW = 4;                       // waves per workgroup
+    // head_dim 256: the NW waves split the head dimension and walk the slot's chunks together (DS).
+    // Each wave reads its SL columns of K straight into matrix-core operand registers and stages
+    // only its V columns in LDS; the partial scores are summed across the waves through LDS.  The
+    // per-wave state is then a quarter of the full one, so deep prefetch fits the registers.
+    static constexpr bool DS = D == 256;
+    static constexpr int SL = D / NW;                  // head-dimension columns per wave (DS)
+    static constexpr int KSW = SL / 32;                // k-steps of the partial S^T product (DS)
+    static constexpr int DTW = SL / 16;                // d tiles of the P.V product per wave (DS)
+    static constexpr int VGC = SL * ESZ / 16;          // 16-byte HBM columns of a wave's V row slice
+    static constexpr int VLD = 16 * VGC / 64;          // 16-byte V loads per lane per chunk (DS)
+    static constexpr int VLRB = SL * 2;                // LDS bytes per V row slice (bf16)
+    static constexpr int VSWM = (VLRB / 16 < 16 ? VLRB / 16 : 16) - 1;
+    static constexpr int PFD = KV8 ? (NCB <= 2 ? 8 : 2) : (NCB == 1 ? 8 : (NCB == 2 ? 6 : 3));   // chunks in flight per wave (DS)
+    static constexpr int XBUF = 2 * NCB * NW * 64 * 16;  // partial-score exchange, two parities (DS)
     // chunks in flight per wave: as many as the registers hold without spilling (scratch traffic would
     // itself be waited for in order and stall the pipeline); an fp8 chunk takes half the registers
     static constexpr int PF_BF16 = D == 64 ? (NCB <= 2 ? 4 : 3) : (D == 128 ? (NCB == 1 ? 2 : (NCB == 2 ? 3 : 2)) : (NCB == 1 ? 2 : 1));
     static constexpr int PF_FP8 = D == 64 ? (NCB <= 2 ? 8 : 6) : (D == 128 ? (NCB == 1 ? 4 : (NCB == 2 ? 4 : 2)) : (NCB == 1 ? 4 : 1));
-    static constexpr int PF = KV8 ? PF_FP8 : PF_BF16;
+    static constexpr int PF = DS ? PFD : (KV8 ? PF_FP8 : PF_BF16);
     // chunks per compute step: two where the registers allow, so each step runs two independent
     // score chains and one softmax pass over 32 keys (the per-chunk latency of a lone wave drops)
     static constexpr int CG = (D <= 128 && NCB == 1 && PF % 2 == 0) ? 2 : 1;
     static constexpr int WAVE_LDS = CG * 2 * 16 * LRB; // K then V of each chunk of a step, per wave
-    static constexpr int STAGE_LDS = NW * WAVE_LDS;
+    static constexpr int STAGE_LDS = DS ? NW * 16 * VLRB + XBUF : NW * WAVE_LDS;
     static constexpr int ROWS = 16 * NCB;              // query rows per workgroup (padded)
     static constexpr int APITCH = D + 4;               // fp32 pitch of the LDS merge buffer
     static constexpr int MERGE_LDS = (NW * ROWS + 2 * ROWS + ROWS * APITCH) * 4;
     static constexpr int LDS = STAGE_LDS > MERGE_LDS ? STAGE_LDS : MERGE_LDS;
     // Waves per SIMD the register budget is cut for: 2 (two workgroups per CU, 256 registers per lane)
     // where operands and accumulators fit, else 1 (512 registers) rather than spilling.
-    static constexpr int WAVES = (D == 64 || (D == 128 && NCB == 1)) ? 2 : 1;
+    static constexpr int WAVES = (D == 64 || (D == 128 && NCB == 1) || DS) ? 2 : 1;
 
 };
 
@@ -364,6 +380,25 @@ __device__ __forceinline__ int lds_col(int r, int c) {
 
 // Rescale threshold of the running maximum, in base-2 units: probabilities stay below 2^8.
 constexpr float kRescaleSlack = 8.0f;
+
+// Max and sum over the lanes l, l ^ 16, l ^ 32 and l ^ 48 (one query row's four lane groups) with
+// gfx950's row swaps: permlane16_swap exchanges the odd 16-lane rows of its first operand with the
+// even rows of its second, permlane32_swap the upper half of the first with the lower half of the
+// second, so with both operands x each lane ends up holding x of itself and of its partner, one in
+// each result.  Vector ALU only, no LDS round trip; every lane of the four gets the same value.
+__device__ __forceinline__ float max_over_row_groups(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float sum_over_row_groups(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 template <int D, int NCB, bool KV8, bool QF32>
 __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::WAVES)) void decode_mfma_kernel(const DecodeArgs a) {
@@ -450,6 +485,7 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
     // chunks are all in its first unit: k < unit takes no division.  Past that (only the empty
     // padding chunks, or a plan whose largest-slot word understates a slot) the general form applies.
     auto chunk_of = [&](int k) -> int {
+        if constexpr (C::DS) return k;            // every wave walks every chunk (its own columns)
         if (k < unit) return wave * unit + k;
         const int j = k / unit;
         return (wave + C::NW * j) * unit + (k - j * unit);
@@ -500,7 +536,10 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
     const int grp = lane >> 4;                    // 4 lane groups
 
     // ---- query operands (B of S^T = K.Q^T): qop[cb][s] = q[row][32s + 8*grp .. +8] as bf16 ----
-    bf16x8_t qop[NCB][C::KSTEPS];
+    constexpr int NKS = C::DS ? C::KSW : C::KSTEPS;   // k-steps of this wave's S^T product
+    constexpr int NDT = C::DS ? C::DTW : C::DT;       // d tiles of this wave's O^T
+    const int dcol0 = C::DS ? wave * C::SL : 0;       // this wave's first head-dimension column
+    bf16x8_t qop[NCB][NKS];
     int nvis[NCB];                                // keys visible to this lane's query row: [nlo, nvis)
     int nlo[NCB];
 #pragma unroll
@@ -513,8 +552,8 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
         nlo[cb] = a.window > 0 ? max(nvis[cb] - a.window, 0) : 0;
         const size_t qoff = (static_cast<size_t>(si.row0 + i) * a.num_q_heads + h) * D;
 #pragma unroll
-        for (int s = 0; s < C::KSTEPS; ++s) {
-            const int d0 = 32 * s + 8 * grp;
+        for (int s = 0; s < NKS; ++s) {
+            const int d0 = dcol0 + 32 * s + 8 * grp;
             u32x4_t v = {0u, 0u, 0u, 0u};
             if (valid) {
                 if constexpr (QF32) {
@@ -533,13 +572,13 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
     }
 
     float m_run[NCB], l_run[NCB];                 // running reference max (base 2) and lane-partial sum
-    float4_t acc[NCB][C::DT];                     // O^T tile: lane holds d = 16t + 4*grp + j, row = col
+    float4_t acc[NCB][NDT];                       // O^T tile: lane holds d = dcol0 + 16t + 4*grp + j, row = col
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
         m_run[cb] = -INFINITY;
         l_run[cb] = 0.f;
 #pragma unroll
-        for (int t = 0; t < C::DT; ++t) acc[cb][t] = float4_t{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < NDT; ++t) acc[cb][t] = float4_t{0.f, 0.f, 0.f, 0.f};
     }
 
     const int nkeys = si.k_hi - si.k_lo;
@@ -552,6 +591,196 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
     const int rem = nchunks - full_units * unit;
     int my_chunks = (full_units > wave ? (full_units - wave + C::NW - 1) / C::NW : 0) * unit;
     if (rem > 0 && full_units % C::NW == wave) my_chunks += rem;
+    if constexpr (C::DS) my_chunks = nchunks;
+
+    float* const mbuf = reinterpret_cast<float*>(lds);     // [NW][ROWS]  (after the stream)
+    float* const lbuf = mbuf + C::NW * C::ROWS;             // [ROWS]
+    float* const Mbuf = lbuf + C::ROWS;                     // [ROWS]
+    float* const abuf = Mbuf + C::ROWS;                     // [ROWS][APITCH]
+    if constexpr (C::DS) {
+        // ---- head-split stream: every wave takes every chunk, SL columns of it ----
+        constexpr int PF = C::PF;
+        using kload_t = typename std::conditional<KV8, u32x2_t, u32x4_t>::type;
+        kload_t kreg[PF][C::KSW];
+        u32x4_t vreg[PF][C::VLD];
+        int nvalid_st[PF];
+        // K columns in operand order (lane: key row lane & 15, columns dcol0 + 32s + 8*(lane >> 4)
+        // .. + 8) and this wave's V columns (16-byte pieces, row-major), non-temporal; a chunk past
+        // the slot, the context or on an invalid page loads zeros (no records)
+        auto issue = [&](int st, int k, int page) {
+            const int key0 = si.k_lo + 16 * k;
+            const int blk = __builtin_amdgcn_readfirstlane(page);
+            const bool live = k < nchunks && blk >= 0 && blk < a.num_blocks;
+            const int nv = live ? max(min(16, si.k_hi - key0), 0) : 0;
+            nvalid_st[st] = nv;
+            const int off = key0 & (a.block_size - 1);
+            const size_t base = nv > 0 ? (static_cast<size_t>(blk) * a.num_kv_heads + g) * head_stride +
+                                             static_cast<size_t>(off) * C::GRB
+                                       : 0;
+            const int records = nv > 0 ? 16 * C::GRB : 0;
+            const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint8_t*>(a.k_cache + base), 0, records, kRawBufferWord3);
+            const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint8_t*>(a.v_cache + base), 0, records, kRawBufferWord3);
+#pragma unroll
+            for (int ks = 0; ks < C::KSW; ++ks) {
+                const int o = col * C::GRB + (dcol0 + 32 * ks + 8 * grp) * C::ESZ;
+                if constexpr (KV8)
+                    kreg[st][ks] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rk, o, 0, kLoadNonTemporal));
+                else
+                    kreg[st][ks] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, kLoadNonTemporal));
+            }
+#pragma unroll
+            for (int it = 0; it < C::VLD; ++it) {
+                const int f = it * 64 + lane;
+                const int r = f / C::VGC;
+                const int c = f - r * C::VGC;
+                vreg[st][it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                               rv, r * C::GRB + dcol0 * C::ESZ + 16 * c, 0, kLoadNonTemporal));
+            }
+        };
+        uint8_t* const vlds = lds + wave * 16 * C::VLRB;
+        float4_t* const xbuf = reinterpret_cast<float4_t*>(lds + C::NW * 16 * C::VLRB);  // [2][NCB][NW][64]
+        const int tr_row = 4 * grp + ((lane >> 2) & 3);
+        const int tr_d0 = 4 * (lane & 3);
+
+#pragma unroll
+        for (int st = 0; st < PF; ++st) issue(st, st, pfirst[st]);
+        const int rounds = (nchunks + PF - 1) / PF;     // the same for every wave: one barrier per chunk
+        for (int k0 = 0; k0 < rounds * PF; k0 += PF) {
+#pragma unroll
+            for (int st = 0; st < PF; ++st) {
+                const int k = k0 + st;
+                const int key0 = si.k_lo + 16 * k;
+                const int nv = nvalid_st[st];
+                compiler_fence();
+                // V columns to LDS as bf16 rows (rows >= nv zero), K columns to operands
+#pragma unroll
+                for (int it = 0; it < C::VLD; ++it) {
+                    const int f = it * 64 + lane;
+                    const int r = f / C::VGC;
+                    const int c = f - r * C::VGC;
+                    u32x4_t vv = vreg[st][it];
+                    if (nv < 16) {
+                        const u32x4_t z = {0u, 0u, 0u, 0u};
+                        vv = r < nv ? vv : z;
+                    }
+                    if constexpr (!KV8) {
+                        *reinterpret_cast<u32x4_t*>(vlds + lds_col<C::VLRB, C::VSWM>(r, c)) = vv;
+                    } else {
+                        u32x4_t lo, hi;
+#pragma unroll
+                        for (int w = 0; w < 2; ++w) {
+                            lo[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vv[w], 1.0f, false));
+                            lo[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vv[w], 1.0f, true));
+                            hi[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vv[w + 2], 1.0f, false));
+                            hi[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vv[w + 2], 1.0f, true));
+                        }
+                        *reinterpret_cast<u32x4_t*>(vlds + lds_col<C::VLRB, C::VSWM>(r, 2 * c)) = lo;
+                        *reinterpret_cast<u32x4_t*>(vlds + lds_col<C::VLRB, C::VSWM>(r, 2 * c + 1)) = hi;
+                    }
+                }
+                bf16x8_t kop[C::KSW];
+#pragma unroll
+                for (int ks = 0; ks < C::KSW; ++ks) {
+                    if constexpr (KV8) {
+                        const u32x2_t w = kreg[st][ks];
+                        const u32x4_t e = {
+                            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false)),
+                            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true)),
+                            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false)),
+                            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true))};
+                        kop[ks] = __builtin_bit_cast(bf16x8_t, e);
+                    } else {
+                        kop[ks] = __builtin_bit_cast(bf16x8_t, kreg[st][ks]);
+                    }
+                }
+                compiler_fence();
+                const int page = pnext[st];
+                pnext[st] = page_load(k + 2 * PF);
+                issue(st, k + PF, page);
+
+                // partial S^T over this wave's columns, summed across the waves in a fixed order
+                float4_t* const xb = xbuf + (k & 1) * NCB * C::NW * 64;
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    float4_t sp = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < C::KSW; ++ks)
+                        sp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks], qop[cb][ks], sp, 0, 0, 0);
+                    xb[(cb * C::NW + wave) * 64 + lane] = sp;
+                }
+                short4_t vop[C::DTW];
+#pragma unroll
+                for (int t = 0; t < C::DTW; ++t) {
+                    const int d0 = 16 * t + tr_d0;
+                    const int off = lds_col<C::VLRB, C::VSWM>(tr_row, d0 >> 3) + ((d0 & 7) << 1);
+                    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+                    typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+                    const bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(vlds + off));
+                    vop[t] = __builtin_bit_cast(short4_t, v);
+                }
+                __syncthreads();
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    float4_t sc = xb[(cb * C::NW) * 64 + lane];
+#pragma unroll
+                    for (int w = 1; w < C::NW; ++w) sc += xb[(cb * C::NW + w) * 64 + lane];
+                    // lane holds keys key0 + 4*grp + j for query row 16cb + col (same in every wave)
+                    const int lim = min(nv, nvis[cb] - key0);
+                    const int low = nlo[cb] - key0;
+                    float x[4];
+                    float mt = -INFINITY;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int kj = 4 * grp + j;
+                        x[j] = (kj < lim && kj >= low) ? sc[j] * a.score_scale_log2 : -INFINITY;
+                        mt = fmaxf(mt, x[j]);
+                    }
+                    mt = max_over_row_groups(mt);
+                    const bool grow = mt > m_run[cb] + kRescaleSlack;
+                    if (__builtin_amdgcn_ballot_w64(grow)) {
+                        const float mnew = grow ? mt : m_run[cb];
+                        const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[cb] - mnew);
+                        l_run[cb] *= alpha;
+#pragma unroll
+                        for (int t = 0; t < NDT; ++t) acc[cb][t] *= alpha;
+                        m_run[cb] = mnew;
+                    }
+                    const float mref = m_run[cb] == -INFINITY ? 0.f : m_run[cb];
+                    float p[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        p[j] = __builtin_amdgcn_exp2f(x[j] - mref);
+                        l_run[cb] += p[j];
+                    }
+                    const u32x2_t pc = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+                    const short4_t pop = __builtin_bit_cast(short4_t, pc);
+#pragma unroll
+                    for (int t = 0; t < C::DTW; ++t)
+                        acc[cb][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop[t], pop, acc[cb][t], 0, 0, 0);
+                }
+            }
+        }
+        // every wave holds the same (m, l); each puts its columns of acc in the LDS state
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            l_run[cb] = sum_over_row_groups(l_run[cb]);
+        }
+        __syncthreads();   // staging and exchange buffers are free from here on
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            const int n = 16 * cb + col;
+#pragma unroll
+            for (int t = 0; t < C::DTW; ++t)
+                *reinterpret_cast<float4_t*>(abuf + n * C::APITCH + dcol0 + 16 * t + 4 * grp) = acc[cb][t];
+            if (wave == 0 && grp == 0) {
+                Mbuf[n] = m_run[cb];
+                lbuf[n] = l_run[cb];
+            }
+        }
+        __syncthreads();
+    } else {
 
     u32x4_t kreg[C::PF][C::NLD], vreg[C::PF][C::NLD];
     int nvalid_st[C::PF];
@@ -707,8 +936,7 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
                         mt = fmaxf(mt, x[c][j]);
                     }
                 }
-                mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-                mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+                mt = max_over_row_groups(mt);
                 // lazy rescale: move the reference only when the row max passes it by the slack
                 const bool grow = mt > m_run[cb] + kRescaleSlack;
                 if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -761,14 +989,9 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
     // ---- merge the wave states in LDS ----
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-        l_run[cb] += __shfl_xor(l_run[cb], 16, 64);
-        l_run[cb] += __shfl_xor(l_run[cb], 32, 64);
+        l_run[cb] = sum_over_row_groups(l_run[cb]);
     }
     __syncthreads();   // staging buffers are free from here on
-    float* mbuf = reinterpret_cast<float*>(lds);           // [NW][ROWS]
-    float* lbuf = mbuf + C::NW * C::ROWS;                   // [ROWS]
-    float* Mbuf = lbuf + C::ROWS;                           // [ROWS]
-    float* abuf = Mbuf + C::ROWS;                           // [ROWS][APITCH]
     if (grp == 0) {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) mbuf[wave * C::ROWS + 16 * cb + col] = m_run[cb];
@@ -802,6 +1025,7 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
             }
         }
         __syncthreads();
+    }
     }
 
     // ---- write the slot's states: rows n < M, token i = n / G, head g*G + n % G ----

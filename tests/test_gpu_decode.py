@@ -40,6 +40,12 @@ SMALL = [
     # wave that owns it while the last token does (regression: such rows must stay (-inf, 0, 0))
     ("bf16_short_last_tile", [257, 513, 258, 769], [3, 3, 2, 4], 8, 2, 128, 16, "bf16", "bf16", 1, 1, 256),
     ("fp8_short_last_tile", [257, 1025], [3, 4], 8, 2, 64, 16, "fp8", "bf16", 0, 1, 256),
+    # head_dim 256 (the waves split the head dimension): four 16-row blocks, fp32 queries, one-chunk
+    # slots, and a last tile shorter than the query length
+    ("bf16_d256_64rows", [2100, 40, 700], [6, 1, 6], 6, 1, 256, 16, "bf16", "bf16", 1, 64, 64),
+    ("fp8_d256_40rows", [900, 3000, 1], [5, 2, 1], 8, 1, 256, 64, "fp8", "bf16", 0, 256, 128),
+    ("qf32_d256_tiny_tiles", [17, 1, 300, 4097], None, 6, 1, 256, 16, "bf16", "f32", 0, 4, 16),
+    ("bf16_d256_short_last_tile", [257, 513], [3, 2], 6, 2, 256, 16, "bf16", "bf16", 0, 1, 256),
 ]
 
 
