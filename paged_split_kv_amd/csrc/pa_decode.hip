@@ -361,7 +361,7 @@ struct Mfma {
     // score chains and one softmax pass over 32 keys (the per-chunk latency of a lone wave drops)
     static constexpr int CG = (D <= 128 && NCB == 1 && PF % 2 == 0) ? 2 : 1;
     static constexpr int WAVE_LDS = CG * 2 * 16 * LRB; // K then V of each chunk of a step, per wave
-    static constexpr int STAGE_LDS = DS ? NW * 16 * VLRB + XBUF : NW * WAVE_LDS;
+    static constexpr int STAGE_LDS = DS ? NW * 2 * 16 * VLRB + XBUF : NW * WAVE_LDS;
     static constexpr int ROWS = 16 * NCB;              // query rows per workgroup (padded)
     static constexpr int APITCH = D + 4;               // fp32 pitch of the LDS merge buffer
     static constexpr int MERGE_LDS = (NW * ROWS + 2 * ROWS + ROWS * APITCH) * 4;
@@ -639,129 +639,153 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
                                                                rv, r * C::GRB + dcol0 * C::ESZ + 16 * c, 0, kLoadNonTemporal));
             }
         };
-        uint8_t* const vlds = lds + wave * 16 * C::VLRB;
-        float4_t* const xbuf = reinterpret_cast<float4_t*>(lds + C::NW * 16 * C::VLRB);  // [2][NCB][NW][64]
+        // two V tiles per wave (chunk parity), then the partial-score exchange [2][NCB][NW][64]
+        uint8_t* const vlds0 = lds + wave * 2 * 16 * C::VLRB;
+        float4_t* const xbuf = reinterpret_cast<float4_t*>(lds + C::NW * 2 * 16 * C::VLRB);
         const int tr_row = 4 * grp + ((lane >> 2) & 3);
         const int tr_d0 = 4 * (lane & 3);
 
+        // Stage A of chunk k (slot st of the load ring): V columns to LDS tile k & 1 as bf16 rows
+        // (rows >= nv zero), K columns to operands, the loads PF chunks ahead, then the partial S^T
+        // over this wave's columns into exchange buffer k & 1.
+        auto stage_a = [&](int st, int k) {
+            const int nv = nvalid_st[st];
+            uint8_t* const vlds = vlds0 + (k & 1) * 16 * C::VLRB;
+            compiler_fence();
+#pragma unroll
+            for (int it = 0; it < C::VLD; ++it) {
+                const int f = it * 64 + lane;
+                const int r = f / C::VGC;
+                const int c = f - r * C::VGC;
+                u32x4_t vv = vreg[st][it];
+                if (nv < 16) {
+                    const u32x4_t z = {0u, 0u, 0u, 0u};
+                    vv = r < nv ? vv : z;
+                }
+                if constexpr (!KV8) {
+                    *reinterpret_cast<u32x4_t*>(vlds + lds_col<C::VLRB, C::VSWM>(r, c)) = vv;
+                } else {
+                    u32x4_t lo, hi;
+#pragma unroll
+                    for (int w = 0; w < 2; ++w) {
+                        lo[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vv[w], 1.0f, false));
+                        lo[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vv[w], 1.0f, true));
+                        hi[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vv[w + 2], 1.0f, false));
+                        hi[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vv[w + 2], 1.0f, true));
+                    }
+                    *reinterpret_cast<u32x4_t*>(vlds + lds_col<C::VLRB, C::VSWM>(r, 2 * c)) = lo;
+                    *reinterpret_cast<u32x4_t*>(vlds + lds_col<C::VLRB, C::VSWM>(r, 2 * c + 1)) = hi;
+                }
+            }
+            bf16x8_t kop[C::KSW];
+#pragma unroll
+            for (int ks = 0; ks < C::KSW; ++ks) {
+                if constexpr (KV8) {
+                    const u32x2_t w = kreg[st][ks];
+                    const u32x4_t e = {
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true))};
+                    kop[ks] = __builtin_bit_cast(bf16x8_t, e);
+                } else {
+                    kop[ks] = __builtin_bit_cast(bf16x8_t, kreg[st][ks]);
+                }
+            }
+            compiler_fence();
+            const int page = pnext[st];
+            pnext[st] = page_load(k + 2 * PF);
+            issue(st, k + PF, page);
+            float4_t* const xb = xbuf + (k & 1) * NCB * C::NW * 64;
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                if (cb > 0 && 16 * cb >= M) break;     // a block past the request's rows: nothing
+                float4_t sp = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < C::KSW; ++ks)
+                    sp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks], qop[cb][ks], sp, 0, 0, 0);
+                xb[(cb * C::NW + wave) * 64 + lane] = sp;
+            }
+        };
+
+        // Stage B of chunk k (its keys from key0, nv of them): the summed scores (fixed wave order,
+        // so every wave sees the same values), the online softmax, and P.V over this wave's columns.
+        auto stage_b = [&](int k, int key0, int nv) {
+            const uint8_t* const vlds = vlds0 + (k & 1) * 16 * C::VLRB;
+            short4_t vop[C::DTW];
+#pragma unroll
+            for (int t = 0; t < C::DTW; ++t) {
+                const int d0 = 16 * t + tr_d0;
+                const int off = lds_col<C::VLRB, C::VSWM>(tr_row, d0 >> 3) + ((d0 & 7) << 1);
+                typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+                typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+                const bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(vlds + off));
+                vop[t] = __builtin_bit_cast(short4_t, v);
+            }
+            const float4_t* const xb = xbuf + (k & 1) * NCB * C::NW * 64;
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                if (cb > 0 && 16 * cb >= M) break;
+                float4_t sc = xb[(cb * C::NW) * 64 + lane];
+#pragma unroll
+                for (int w = 1; w < C::NW; ++w) sc += xb[(cb * C::NW + w) * 64 + lane];
+                // lane holds keys key0 + 4*grp + j for query row 16cb + col
+                const int lim = min(nv, nvis[cb] - key0);
+                const int low = nlo[cb] - key0;
+                float x[4];
+                float mt = -INFINITY;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int kj = 4 * grp + j;
+                    x[j] = (kj < lim && kj >= low) ? sc[j] * a.score_scale_log2 : -INFINITY;
+                    mt = fmaxf(mt, x[j]);
+                }
+                mt = max_over_row_groups(mt);
+                const bool grow = mt > m_run[cb] + kRescaleSlack;
+                if (__builtin_amdgcn_ballot_w64(grow)) {
+                    const float mnew = grow ? mt : m_run[cb];
+                    const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[cb] - mnew);
+                    l_run[cb] *= alpha;
+#pragma unroll
+                    for (int t = 0; t < NDT; ++t) acc[cb][t] *= alpha;
+                    m_run[cb] = mnew;
+                }
+                const float mref = m_run[cb] == -INFINITY ? 0.f : m_run[cb];
+                float p[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    p[j] = __builtin_amdgcn_exp2f(x[j] - mref);
+                    l_run[cb] += p[j];
+                }
+                const u32x2_t pc = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+                const short4_t pop = __builtin_bit_cast(short4_t, pc);
+#pragma unroll
+                for (int t = 0; t < C::DTW; ++t)
+                    acc[cb][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop[t], pop, acc[cb][t], 0, 0, 0);
+            }
+        };
+
 #pragma unroll
         for (int st = 0; st < PF; ++st) issue(st, st, pfirst[st]);
-        const int rounds = (nchunks + PF - 1) / PF;     // the same for every wave: one barrier per chunk
+        // Software pipeline over the chunks: iteration k runs stage A of chunk k, then stage B of
+        // chunk k - 1 (whose partial scores every wave wrote before the previous barrier), then one
+        // barrier.  Stage A of chunk k overwrites tile and exchange buffer k & 1, last read by stage
+        // B of chunk k - 2 before that barrier.  The trip count is the same for every wave.
+        const int rounds = (nchunks + PF - 1) / PF;
+        int key0_prev = 0, nv_prev = 0;
         for (int k0 = 0; k0 < rounds * PF; k0 += PF) {
 #pragma unroll
             for (int st = 0; st < PF; ++st) {
                 const int k = k0 + st;
-                const int key0 = si.k_lo + 16 * k;
                 const int nv = nvalid_st[st];
-                compiler_fence();
-                // V columns to LDS as bf16 rows (rows >= nv zero), K columns to operands
-#pragma unroll
-                for (int it = 0; it < C::VLD; ++it) {
-                    const int f = it * 64 + lane;
-                    const int r = f / C::VGC;
-                    const int c = f - r * C::VGC;
-                    u32x4_t vv = vreg[st][it];
-                    if (nv < 16) {
-                        const u32x4_t z = {0u, 0u, 0u, 0u};
-                        vv = r < nv ? vv : z;
-                    }
-                    if constexpr (!KV8) {
-                        *reinterpret_cast<u32x4_t*>(vlds + lds_col<C::VLRB, C::VSWM>(r, c)) = vv;
-                    } else {
-                        u32x4_t lo, hi;
-#pragma unroll
-                        for (int w = 0; w < 2; ++w) {
-                            lo[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vv[w], 1.0f, false));
-                            lo[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vv[w], 1.0f, true));
-                            hi[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vv[w + 2], 1.0f, false));
-                            hi[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vv[w + 2], 1.0f, true));
-                        }
-                        *reinterpret_cast<u32x4_t*>(vlds + lds_col<C::VLRB, C::VSWM>(r, 2 * c)) = lo;
-                        *reinterpret_cast<u32x4_t*>(vlds + lds_col<C::VLRB, C::VSWM>(r, 2 * c + 1)) = hi;
-                    }
-                }
-                bf16x8_t kop[C::KSW];
-#pragma unroll
-                for (int ks = 0; ks < C::KSW; ++ks) {
-                    if constexpr (KV8) {
-                        const u32x2_t w = kreg[st][ks];
-                        const u32x4_t e = {
-                            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false)),
-                            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true)),
-                            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false)),
-                            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true))};
-                        kop[ks] = __builtin_bit_cast(bf16x8_t, e);
-                    } else {
-                        kop[ks] = __builtin_bit_cast(bf16x8_t, kreg[st][ks]);
-                    }
-                }
-                compiler_fence();
-                const int page = pnext[st];
-                pnext[st] = page_load(k + 2 * PF);
-                issue(st, k + PF, page);
-
-                // partial S^T over this wave's columns, summed across the waves in a fixed order
-                float4_t* const xb = xbuf + (k & 1) * NCB * C::NW * 64;
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) {
-                    float4_t sp = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < C::KSW; ++ks)
-                        sp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks], qop[cb][ks], sp, 0, 0, 0);
-                    xb[(cb * C::NW + wave) * 64 + lane] = sp;
-                }
-                short4_t vop[C::DTW];
-#pragma unroll
-                for (int t = 0; t < C::DTW; ++t) {
-                    const int d0 = 16 * t + tr_d0;
-                    const int off = lds_col<C::VLRB, C::VSWM>(tr_row, d0 >> 3) + ((d0 & 7) << 1);
-                    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-                    typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
-                    const bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(vlds + off));
-                    vop[t] = __builtin_bit_cast(short4_t, v);
-                }
+                stage_a(st, k);
+                if (k > 0 && k - 1 < nchunks) stage_b(k - 1, key0_prev, nv_prev);
+                key0_prev = si.k_lo + 16 * k;
+                nv_prev = nv;
                 __syncthreads();
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) {
-                    float4_t sc = xb[(cb * C::NW) * 64 + lane];
-#pragma unroll
-                    for (int w = 1; w < C::NW; ++w) sc += xb[(cb * C::NW + w) * 64 + lane];
-                    // lane holds keys key0 + 4*grp + j for query row 16cb + col (same in every wave)
-                    const int lim = min(nv, nvis[cb] - key0);
-                    const int low = nlo[cb] - key0;
-                    float x[4];
-                    float mt = -INFINITY;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int kj = 4 * grp + j;
-                        x[j] = (kj < lim && kj >= low) ? sc[j] * a.score_scale_log2 : -INFINITY;
-                        mt = fmaxf(mt, x[j]);
-                    }
-                    mt = max_over_row_groups(mt);
-                    const bool grow = mt > m_run[cb] + kRescaleSlack;
-                    if (__builtin_amdgcn_ballot_w64(grow)) {
-                        const float mnew = grow ? mt : m_run[cb];
-                        const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[cb] - mnew);
-                        l_run[cb] *= alpha;
-#pragma unroll
-                        for (int t = 0; t < NDT; ++t) acc[cb][t] *= alpha;
-                        m_run[cb] = mnew;
-                    }
-                    const float mref = m_run[cb] == -INFINITY ? 0.f : m_run[cb];
-                    float p[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        p[j] = __builtin_amdgcn_exp2f(x[j] - mref);
-                        l_run[cb] += p[j];
-                    }
-                    const u32x2_t pc = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
-                    const short4_t pop = __builtin_bit_cast(short4_t, pc);
-#pragma unroll
-                    for (int t = 0; t < C::DTW; ++t)
-                        acc[cb][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop[t], pop, acc[cb][t], 0, 0, 0);
-                }
             }
         }
+        if (rounds > 0 && rounds * PF - 1 < nchunks) stage_b(rounds * PF - 1, key0_prev, nv_prev);
         // every wave holds the same (m, l); each puts its columns of acc in the LDS state
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
@@ -914,6 +938,7 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
 
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
+                if (cb > 0 && 16 * cb >= M) break;     // a block past the request's rows: nothing
                 float4_t sacc[CG];
 #pragma unroll
                 for (int c = 0; c < CG; ++c) {
