@@ -338,19 +338,23 @@ struct Mfma {
     static constexpr int KSTEPS = D / 32;              // k-steps of the S^T product
     static constexpr int DT = D / 16;                  // 16-wide d tiles of the P.V product
     static constexpr int NW = 4;                       // waves per workgroup
-    // head_dim 256: the NW waves split the head dimension and walk the slot's chunks together (DS).
-    // Each wave reads its SL columns of K straight into matrix-core operand registers and stages
-    // only its V columns in LDS; the partial scores are summed across the waves through LDS.  The
-    // per-wave state is then a quarter of the full one, so deep prefetch fits the registers.
+    // head_dim 256 (DS): the waves work in groups of SPLIT that split the head dimension, each group
+    // walking its own stream of the slot's chunks (chunks s, s + NS, ...).  A wave reads its SL
+    // columns of K straight into matrix-core operand registers and stages only its V columns in
+    // LDS; the group's partial scores are summed through LDS.  The per-wave state is 1/SPLIT of the
+    // full one, so operands, accumulators and a deep prefetch fit the registers of two workgroups
+    // per CU, while only SPLIT waves repeat each chunk's softmax.
     static constexpr bool DS = D == 256;
-    static constexpr int SL = D / NW;                  // head-dimension columns per wave (DS)
+    static constexpr int SPLIT = NCB >= 4 ? 4 : 2;     // waves sharing a chunk (DS)
+    static constexpr int NS = NW / SPLIT;              // chunk streams per workgroup (DS)
+    static constexpr int SL = D / SPLIT;               // head-dimension columns per wave (DS)
     static constexpr int KSW = SL / 32;                // k-steps of the partial S^T product (DS)
     static constexpr int DTW = SL / 16;                // d tiles of the P.V product per wave (DS)
     static constexpr int VGC = SL * ESZ / 16;          // 16-byte HBM columns of a wave's V row slice
     static constexpr int VLD = 16 * VGC / 64;          // 16-byte V loads per lane per chunk (DS)
     static constexpr int VLRB = SL * 2;                // LDS bytes per V row slice (bf16)
     static constexpr int VSWM = (VLRB / 16 < 16 ? VLRB / 16 : 16) - 1;
-    static constexpr int PFD = KV8 ? (NCB <= 2 ? 8 : 2) : (NCB == 1 ? 8 : (NCB == 2 ? 6 : 3));   // chunks in flight per wave (DS)
+    static constexpr int PFD = KV8 ? (NCB == 1 ? 6 : (NCB == 2 ? 4 : 2)) : (NCB == 1 ? 3 : (NCB == 2 ? 2 : 3));   // chunks in flight per wave (DS)
     static constexpr int XBUF = 2 * NCB * NW * 64 * 16;  // partial-score exchange, two parities (DS)
     // chunks in flight per wave: as many as the registers hold without spilling (scratch traffic would
     // itself be waited for in order and stall the pipeline); an fp8 chunk takes half the registers
@@ -485,7 +489,7 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
     // chunks are all in its first unit: k < unit takes no division.  Past that (only the empty
     // padding chunks, or a plan whose largest-slot word understates a slot) the general form applies.
     auto chunk_of = [&](int k) -> int {
-        if constexpr (C::DS) return k;            // every wave walks every chunk (its own columns)
+        if constexpr (C::DS) return k * C::NS + wave / C::SPLIT;   // the wave group's stream
         if (k < unit) return wave * unit + k;
         const int j = k / unit;
         return (wave + C::NW * j) * unit + (k - j * unit);
@@ -538,7 +542,7 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
     // ---- query operands (B of S^T = K.Q^T): qop[cb][s] = q[row][32s + 8*grp .. +8] as bf16 ----
     constexpr int NKS = C::DS ? C::KSW : C::KSTEPS;   // k-steps of this wave's S^T product
     constexpr int NDT = C::DS ? C::DTW : C::DT;       // d tiles of this wave's O^T
-    const int dcol0 = C::DS ? wave * C::SL : 0;       // this wave's first head-dimension column
+    const int dcol0 = C::DS ? (wave % C::SPLIT) * C::SL : 0;   // this wave's first head-dimension column
     bf16x8_t qop[NCB][NKS];
     int nvis[NCB];                                // keys visible to this lane's query row: [nlo, nvis)
     int nlo[NCB];
@@ -591,7 +595,7 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
     const int rem = nchunks - full_units * unit;
     int my_chunks = (full_units > wave ? (full_units - wave + C::NW - 1) / C::NW : 0) * unit;
     if (rem > 0 && full_units % C::NW == wave) my_chunks += rem;
-    if constexpr (C::DS) my_chunks = nchunks;
+    if constexpr (C::DS) my_chunks = (nchunks - wave / C::SPLIT + C::NS - 1) / C::NS;   // its stream's
 
     float* const mbuf = reinterpret_cast<float*>(lds);     // [NW][ROWS]  (after the stream)
     float* const lbuf = mbuf + C::NW * C::ROWS;             // [ROWS]
@@ -608,9 +612,9 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
         // .. + 8) and this wave's V columns (16-byte pieces, row-major), non-temporal; a chunk past
         // the slot, the context or on an invalid page loads zeros (no records)
         auto issue = [&](int st, int k, int page) {
-            const int key0 = si.k_lo + 16 * k;
+            const int key0 = si.k_lo + 16 * chunk_of(k);
             const int blk = __builtin_amdgcn_readfirstlane(page);
-            const bool live = k < nchunks && blk >= 0 && blk < a.num_blocks;
+            const bool live = k < my_chunks && blk >= 0 && blk < a.num_blocks;
             const int nv = live ? max(min(16, si.k_hi - key0), 0) : 0;
             nvalid_st[st] = nv;
             const int off = key0 & (a.block_size - 1);
@@ -726,9 +730,10 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
                 if (cb > 0 && 16 * cb >= M) break;
-                float4_t sc = xb[(cb * C::NW) * 64 + lane];
+                const int w0 = cb * C::NW + (wave / C::SPLIT) * C::SPLIT;   // the group's first wave
+                float4_t sc = xb[w0 * 64 + lane];
 #pragma unroll
-                for (int w = 1; w < C::NW; ++w) sc += xb[(cb * C::NW + w) * 64 + lane];
+                for (int w = 1; w < C::SPLIT; ++w) sc += xb[(w0 + w) * 64 + lane];
                 // lane holds keys key0 + 4*grp + j for query row 16cb + col
                 const int lim = min(nv, nvis[cb] - key0);
                 const int low = nlo[cb] - key0;
@@ -771,7 +776,8 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
         // chunk k - 1 (whose partial scores every wave wrote before the previous barrier), then one
         // barrier.  Stage A of chunk k overwrites tile and exchange buffer k & 1, last read by stage
         // B of chunk k - 2 before that barrier.  The trip count is the same for every wave.
-        const int rounds = (nchunks + PF - 1) / PF;
+        // rounds of the longest stream (stream 0's), so every wave meets every barrier
+        const int rounds = ((nchunks + C::NS - 1) / C::NS + PF - 1) / PF;
         int key0_prev = 0, nv_prev = 0;
         for (int k0 = 0; k0 < rounds * PF; k0 += PF) {
 #pragma unroll
@@ -779,31 +785,53 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
                 const int k = k0 + st;
                 const int nv = nvalid_st[st];
                 stage_a(st, k);
-                if (k > 0 && k - 1 < nchunks) stage_b(k - 1, key0_prev, nv_prev);
-                key0_prev = si.k_lo + 16 * k;
+                if (k > 0 && k - 1 < my_chunks) stage_b(k - 1, key0_prev, nv_prev);
+                key0_prev = si.k_lo + 16 * chunk_of(k);
                 nv_prev = nv;
                 __syncthreads();
             }
         }
-        if (rounds > 0 && rounds * PF - 1 < nchunks) stage_b(rounds * PF - 1, key0_prev, nv_prev);
-        // every wave holds the same (m, l); each puts its columns of acc in the LDS state
+        if (rounds > 0 && rounds * PF - 1 < my_chunks) stage_b(rounds * PF - 1, key0_prev, nv_prev);
+        // the waves of a group hold the same (m, l); the NS group states merge in LDS, each wave
+        // adding its columns of acc
+        const int stream = wave / C::SPLIT;
+        const bool lead = wave % C::SPLIT == 0;
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-            l_run[cb] = sum_over_row_groups(l_run[cb]);
-        }
+        for (int cb = 0; cb < NCB; ++cb) l_run[cb] = sum_over_row_groups(l_run[cb]);
         __syncthreads();   // staging and exchange buffers are free from here on
+        if (lead && grp == 0) {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) mbuf[stream * C::ROWS + 16 * cb + col] = m_run[cb];
+        }
+        __syncthreads();
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
             const int n = 16 * cb + col;
+            float Mx = -INFINITY;
 #pragma unroll
-            for (int t = 0; t < C::DTW; ++t)
-                *reinterpret_cast<float4_t*>(abuf + n * C::APITCH + dcol0 + 16 * t + 4 * grp) = acc[cb][t];
-            if (wave == 0 && grp == 0) {
-                Mbuf[n] = m_run[cb];
-                lbuf[n] = l_run[cb];
-            }
+            for (int q = 0; q < C::NS; ++q) Mx = fmaxf(Mx, mbuf[q * C::ROWS + n]);
+            const float f = __builtin_amdgcn_exp2f(m_run[cb] - (Mx == -INFINITY ? 0.f : Mx));
+            l_run[cb] *= f;
+#pragma unroll
+            for (int t = 0; t < C::DTW; ++t) acc[cb][t] *= f;
+            if (wave == 0 && grp == 0) Mbuf[n] = Mx;
         }
-        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < C::NS; ++q) {
+            if (stream == q) {
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    const int n = 16 * cb + col;
+#pragma unroll
+                    for (int t = 0; t < C::DTW; ++t) {
+                        float4_t* dst = reinterpret_cast<float4_t*>(abuf + n * C::APITCH + dcol0 + 16 * t + 4 * grp);
+                        *dst = (q == 0) ? acc[cb][t] : (*dst + acc[cb][t]);
+                    }
+                    if (lead && grp == 0) lbuf[n] = (q == 0) ? l_run[cb] : (lbuf[n] + l_run[cb]);
+                }
+            }
+            __syncthreads();
+        }
     } else {
 
     u32x4_t kreg[C::PF][C::NLD], vreg[C::PF][C::NLD];
