@@ -129,7 +129,7 @@ __device__ __forceinline__ void plan_in_wave(const DecodeArgs& a, int slot, int 
 
 template <int NW>
 __device__ void plan_in_place(const DecodeArgs& a, int slot, int g, int4& wk, int2& nwk) {
-    static_assert(NW * 64 == kInlinePlanSeqs, "one request per thread");
+    static_assert(NW * 64 >= kInlinePlanSeqs, "one request per thread");
     if (a.num_seqs <= 64) {
         plan_in_wave(a, slot, g, wk, nwk);
         return;
@@ -326,7 +326,7 @@ __device__ __forceinline__ void zero_unowned_row(const DecodeArgs& a, int r, int
 // ---------------------------------------------------------------------------------------------
 // matrix-core kernel (bf16 or fp8 caches)
 // ---------------------------------------------------------------------------------------------
-template <int D, int NCB, bool KV8>
+template <int D, int NCB, bool KV8, int NWAVES = 4>
 struct Mfma {
     static constexpr int ESZ = KV8 ? 1 : 2;            // bytes per cache element in HBM
     static constexpr int GRB = D * ESZ;                // HBM bytes per cache row (one token, one kv head)
@@ -337,7 +337,12 @@ struct Mfma {
     static constexpr int SWM = (LCPR < 16 ? LCPR : 16) - 1;  // XOR swizzle mask on the column
     static constexpr int KSTEPS = D / 32;              // k-steps of the S^T product
     static constexpr int DT = D / 16;                  // 16-wide d tiles of the P.V product
-    static constexpr int NW = 4;                       // waves per workgroup
+    static constexpr int NW = NWAVES;                  // waves per workgroup
+    // Chunk dealing: by default a wave takes units of the plan's largest slot split NW ways (small
+    // slots run fewer, fully loaded waves).  The 8-wave form, used when every request is one slot
+    // (slot sizes then follow the request lengths), splits each slot evenly over its waves instead,
+    // so short slots still run every wave and the longest gets twice the waves of a 4-wave group.
+    static constexpr bool EVEN = NW > 4;
     // head_dim 256 (DS): the waves work in groups of SPLIT that split the head dimension, each group
     // walking its own stream of the slot's chunks (chunks s, s + NS, ...).  A wave reads its SL
     // columns of K straight into matrix-core operand registers and stages only its V columns in
@@ -404,9 +409,9 @@ __device__ __forceinline__ float sum_over_row_groups(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <int D, int NCB, bool KV8, bool QF32>
-__global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::WAVES)) void decode_mfma_kernel(const DecodeArgs a) {
-    using C = Mfma<D, NCB, KV8>;
+template <int D, int NCB, bool KV8, bool QF32, int NWAVES>
+__global__ __launch_bounds__((64 * NWAVES), (Mfma<D, NCB, KV8, NWAVES>::WAVES)) void decode_mfma_kernel(const DecodeArgs a) {
+    using C = Mfma<D, NCB, KV8, NWAVES>;
     __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS];
     __shared__ int s_last;
 
@@ -483,7 +488,7 @@ __global__ __launch_bounds__((64 * Mfma<D, NCB, KV8>::NW), (Mfma<D, NCB, KV8>::W
     // bandwidth to the big ones.  Any unit >= 1 covers every chunk of every slot exactly once.
     // (A prefill block is its own slot: its chunks are split evenly over the waves.)
     const int cpt = a.tile_tokens >> 4;          // 16-key chunks per tile
-    const long long unit_chunks = a.prefill ? plan_chunks : static_cast<long long>(max(nwk.y, 1)) * cpt;
+    const long long unit_chunks = (a.prefill || C::EVEN) ? plan_chunks : static_cast<long long>(max(nwk.y, 1)) * cpt;
     const int unit = static_cast<int>(min(max(1LL, (unit_chunks + C::NW - 1) / C::NW), 1LL << 30));
     // Every slot of the plan (and every prefill block) spans at most NW units, so a wave's live
     // chunks are all in its first unit: k < unit takes no division.  Past that (only the empty
@@ -1227,18 +1232,23 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeArgs a) {
     }
 }
 
-template <int D, int NCB, bool KV8>
+template <int D, int NCB, bool KV8, int NW = 4>
 hipError_t launch_mfma_q(const DecodeArgs& a, bool qf32, dim3 grid, hipStream_t stream) {
-    constexpr int NW = Mfma<D, NCB, KV8>::NW;
     const dim3 block(64 * NW);
     if (a.out) grid.x += (a.num_rows + NW - 1) / NW;   // one wave per row for the zero fill
-    if (qf32) hipLaunchKernelGGL((decode_mfma_kernel<D, NCB, KV8, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((decode_mfma_kernel<D, NCB, KV8, false>), grid, block, 0, stream, a);
+    if (qf32) hipLaunchKernelGGL((decode_mfma_kernel<D, NCB, KV8, true, NW>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((decode_mfma_kernel<D, NCB, KV8, false, NW>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
 template <int D, bool KV8>
 hipError_t launch_mfma_ncb(const DecodeArgs& a, int ncb, bool qf32, dim3 grid, hipStream_t stream) {
+    // every request one slot (the capacity is the batch): slot sizes follow the request lengths
+    // and the longest requests set the time, so eight waves share each slot evenly
+    const bool one_slot_each = !a.prefill && (a.plan_inline ? a.plan_cap : a.capacity) <= a.num_seqs;
+    if constexpr (D <= 128) {
+        if (ncb == 1 && one_slot_each) return launch_mfma_q<D, 1, KV8, 8>(a, qf32, grid, stream);
+    }
     if (ncb == 1) return launch_mfma_q<D, 1, KV8>(a, qf32, grid, stream);
     if (ncb == 2) return launch_mfma_q<D, 2, KV8>(a, qf32, grid, stream);
     return launch_mfma_q<D, 4, KV8>(a, qf32, grid, stream);

@@ -102,6 +102,25 @@ def test_small_cases_match_oracle(spec, fused):
     assert (np.abs(got[~z]).sum(axis=(1, 2)) > 0).all()
 
 
+ONE_SLOT = [s for s in SMALL if s[7] != "f32" and s[5] <= 128
+            and s[3] // s[4] * max(s[2] or [1]) <= 16]
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["fused_merge", "separate_merge"])
+@pytest.mark.parametrize("spec", ONE_SLOT, ids=[s[0] for s in ONE_SLOT])
+def test_one_slot_per_request(spec, fused):
+    """A budget of at most one workgroup per request (cu_count 1): the capacity is the batch, every
+    request is one slot, and the decode runs its eight-wave form with slots split evenly."""
+    case, P, T = _small_case(spec, seed=12)
+    announce(f"one slot per request {spec[0]} fused={fused}")
+    out, step = _run(case, P, T, cu_count=1, fused=fused)
+    assert step.capacity == case.num_seqs
+    got = to_f64(out)
+    assert_close(got, oracle_direct(case), tolerance_kind(case), spec[0])
+    z = _zero_rows(case)
+    assert (got[z] == 0.0).all()
+
+
 @pytest.mark.parametrize("name", ["tiny_fp32", "long_bf16", "verify_bf16", "fp8_kv"])
 def test_full_size_workloads(name):
     announce(f"full {name}")
