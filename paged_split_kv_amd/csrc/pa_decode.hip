@@ -97,16 +97,14 @@ __device__ __forceinline__ void plan_in_wave(const DecodeArgs& a, int slot, int 
     const PlanRange pr = plan_range(S, real && a.window > 0 ? plan_q_len(a.cu, lane) : 1, a.window, a.tile_tokens);
     const int len = pr.len;
     const int tiles = pr.tiles;
-    const long long total = wave_sum_ll(len);
+    const long long total = wave_sum_nonneg(len);
     const int nonempty = __popcll(__builtin_amdgcn_ballot_w64(len > 0));
     const int parts = plan_parts(len, tiles, static_cast<long long>(a.plan_cap) - nonempty, total,
                                  a.max_partitions);
     const int incl = wave_incl_scan(parts, lane);
     const int first = incl - parts;
     const int used = __builtin_amdgcn_readlane(incl, 63);
-    int big = parts > 0 ? (tiles + parts - 1) / parts : 0;      // a floor/ceil split's largest part
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) big = max(big, __shfl_xor(big, o, 64));
+    const int big = wave_max_nonneg(parts > 0 ? (tiles + parts - 1) / parts : 0);   // largest part
     // the requests whose first slot is <= slot are a prefix; its last one owns the slot
     const int owner = __popcll(__builtin_amdgcn_ballot_w64(real && first <= slot)) - 1;
     wk = make_int4(-1, 0, 0, 0);
@@ -148,7 +146,7 @@ __device__ void plan_in_place(const DecodeArgs& a, int slot, int g, int4& wk, in
     const int tiles = pr.tiles;
 
     // W = sum of the lengths read and B' = #{requests reading any key}
-    const long long wsum = wave_sum_ll(len);
+    const long long wsum = wave_sum_nonneg(len);
     const int wne = __popcll(__builtin_amdgcn_ballot_w64(len > 0));
     if (lane == 0) {
         s_total[wave] = wsum;
@@ -167,9 +165,7 @@ __device__ void plan_in_place(const DecodeArgs& a, int slot, int g, int4& wk, in
     const int parts = plan_parts(len, tiles, static_cast<long long>(a.plan_cap) - nonempty, total,
                                  a.max_partitions);
     const int incl = wave_incl_scan(parts, lane);
-    int big = parts > 0 ? (tiles + parts - 1) / parts : 0;     // a floor/ceil split's largest part
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) big = max(big, __shfl_xor(big, o, 64));
+    const int big = wave_max_nonneg(parts > 0 ? (tiles + parts - 1) / parts : 0);   // largest part
     if (lane == 63) s_slots[wave] = incl;
     if (lane == 0) s_largest[wave] = big;
     __syncthreads();

@@ -114,13 +114,44 @@ __device__ __forceinline__ long long wave_sum_ll(long long v) {
     return v;
 }
 
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int t = __shfl_up(v, o, 64);
-        if (lane >= o) v += t;
-    }
+// Cross-lane steps through DPP (the vector ALU's lane-shifted operand; no LDS round trip).  Lanes
+// with no source lane, or outside the row mask, read `ident`.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_read(int v, int ident) {
+    return __builtin_amdgcn_update_dpp(ident, v, CTRL, ROW_MASK, 0xf, false);
+}
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+// Inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 within each 16-lane row, then the
+// last lane of row 0 (and of row 2) is added to row 1 (row 3), then lane 31 to rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int v, int /*lane*/) {
+    v += dpp_read<kDppRowShr1, 0xf>(v, 0);
+    v += dpp_read<kDppRowShr2, 0xf>(v, 0);
+    v += dpp_read<kDppRowShr4, 0xf>(v, 0);
+    v += dpp_read<kDppRowShr8, 0xf>(v, 0);
+    v += dpp_read<kDppRowBcast15, 0xa>(v, 0);
+    v += dpp_read<kDppRowBcast31, 0xc>(v, 0);
     return v;
+}
+
+// Maximum over the 64 lanes of non-negative values (the same prefix pattern with max), uniform.
+__device__ __forceinline__ int wave_max_nonneg(int v) {
+    v = max(v, dpp_read<kDppRowShr1, 0xf>(v, 0));
+    v = max(v, dpp_read<kDppRowShr2, 0xf>(v, 0));
+    v = max(v, dpp_read<kDppRowShr4, 0xf>(v, 0));
+    v = max(v, dpp_read<kDppRowShr8, 0xf>(v, 0));
+    v = max(v, dpp_read<kDppRowBcast15, 0xa>(v, 0));
+    v = max(v, dpp_read<kDppRowBcast31, 0xc>(v, 0));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+// Sum over the 64 lanes of values in [0, 2^31), exact in 64 bits: the low and high 16-bit halves
+// are summed separately (each total stays below 2^22), uniform.
+__device__ __forceinline__ long long wave_sum_nonneg(int v) {
+    const int lo = __builtin_amdgcn_readlane(wave_incl_scan(v & 0xffff, 0), 63);
+    const int hi = __builtin_amdgcn_readlane(wave_incl_scan(static_cast<int>(static_cast<unsigned>(v) >> 16), 0), 63);
+    return (static_cast<long long>(hi) << 16) + lo;
 }
 
 // The key range a request reads and the tiles it spans.  Without a window the range is [0, S);
