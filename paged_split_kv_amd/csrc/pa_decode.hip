@@ -371,6 +371,10 @@ struct Mfma {
     static constexpr int APITCH = D + 4;               // fp32 pitch of the LDS merge buffer
     static constexpr int MERGE_LDS = (NW * ROWS + 2 * ROWS + ROWS * APITCH) * 4;
     static constexpr int LDS = STAGE_LDS > MERGE_LDS ? STAGE_LDS : MERGE_LDS;
+    // Per-wave designs whose state (ROWS x D accumulators, then m and l per row) fits the wave's
+    // own staging tile park it there and merge the NW states per element while storing: one
+    // barrier instead of a barrier per wave.
+    static constexpr bool PARK = !DS && (ROWS * APITCH + 2 * ROWS) * 4 <= WAVE_LDS;
     // Waves per SIMD the register budget is cut for: 2 (two workgroups per CU, 256 registers per lane)
     // where operands and accumulators fit, else 1 (512 registers) rather than spilling.
     static constexpr int WAVES = (D == 64 || (D == 128 && NCB == 1) || DS) ? 2 : 1;
@@ -1045,6 +1049,23 @@ __global__ __launch_bounds__((64 * NWAVES), (Mfma<D, NCB, KV8, NWAVES>::WAVES)) 
     for (int cb = 0; cb < NCB; ++cb) {
         l_run[cb] = sum_over_row_groups(l_run[cb]);
     }
+    if constexpr (C::PARK) {
+        // the wave's own tile: no other wave reads it, and this wave's reads of it are done (LDS
+        // operations of a wave complete in order)
+        float* const ws = reinterpret_cast<float*>(wlds);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            const int n = 16 * cb + col;
+#pragma unroll
+            for (int t = 0; t < C::DT; ++t)
+                *reinterpret_cast<float4_t*>(ws + n * C::APITCH + 16 * t + 4 * grp) = acc[cb][t];
+            if (grp == 0) {
+                ws[C::ROWS * C::APITCH + n] = m_run[cb];
+                ws[C::ROWS * C::APITCH + C::ROWS + n] = l_run[cb];
+            }
+        }
+        __syncthreads();
+    } else {
     __syncthreads();   // staging buffers are free from here on
     if (grp == 0) {
 #pragma unroll
@@ -1081,6 +1102,37 @@ __global__ __launch_bounds__((64 * NWAVES), (Mfma<D, NCB, KV8, NWAVES>::WAVES)) 
         __syncthreads();
     }
     }
+    }
+
+    // merged state of row n, columns 4*d4 .. +4: from the LDS state, or from the NW parked states
+    // (max of the wave maxima, each wave rescaled to it, summed in wave order)
+    auto state_at = [&](int n, int d4, float& m, float& l) -> float4_t {
+        if constexpr (C::PARK) {
+            float mw[C::NW];
+            float Mx = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < C::NW; ++w) {
+                mw[w] = reinterpret_cast<const float*>(lds + w * C::WAVE_LDS)[C::ROWS * C::APITCH + n];
+                Mx = fmaxf(Mx, mw[w]);
+            }
+            const float mref = Mx == -INFINITY ? 0.f : Mx;
+            float4_t v = float4_t{0.f, 0.f, 0.f, 0.f};
+            l = 0.f;
+#pragma unroll
+            for (int w = 0; w < C::NW; ++w) {
+                const float* ws = reinterpret_cast<const float*>(lds + w * C::WAVE_LDS);
+                const float f = __builtin_amdgcn_exp2f(mw[w] - mref);
+                v += f * *reinterpret_cast<const float4_t*>(ws + n * C::APITCH + 4 * d4);
+                l += f * ws[C::ROWS * C::APITCH + C::ROWS + n];
+            }
+            m = Mx;
+            return v;
+        } else {
+            m = Mbuf[n];
+            l = lbuf[n];
+            return *reinterpret_cast<const float4_t*>(abuf + n * C::APITCH + 4 * d4);
+        }
+    };
 
     // ---- write the slot's states: rows n < M, token i = n / G, head g*G + n % G ----
     constexpr int D4 = D / 4;
@@ -1093,16 +1145,17 @@ __global__ __launch_bounds__((64 * NWAVES), (Mfma<D, NCB, KV8, NWAVES>::WAVES)) 
         const int i = n / G;
         const int h = g * G + (n - i * G);
         const size_t st = (slot_base + i) * a.num_q_heads + h;
-        float4_t v = *reinterpret_cast<const float4_t*>(abuf + n * C::APITCH + 4 * d4);
+        float mn, ln;
+        float4_t v = state_at(n, d4, mn, ln);
         v *= a.v_scale;
         if (a.out == nullptr) {
             *reinterpret_cast<float4_t*>(a.ws_acc + st * D + 4 * d4) = v;
-            if (d4 == 0) *reinterpret_cast<float2*>(a.ws_ml + st * 2) = make_float2(Mbuf[n], lbuf[n]);
+            if (d4 == 0) *reinterpret_cast<float2*>(a.ws_ml + st * 2) = make_float2(mn, ln);
         } else {
             // merged in this launch by another workgroup: write through to memory
             store_f2_coherent(a.ws_acc + st * D + 4 * d4, v[0], v[1]);
             store_f2_coherent(a.ws_acc + st * D + 4 * d4 + 2, v[2], v[3]);
-            if (d4 == 0) store_f2_coherent(a.ws_ml + st * 2, Mbuf[n], lbuf[n]);
+            if (d4 == 0) store_f2_coherent(a.ws_ml + st * 2, mn, ln);
         }
     }
     if (a.out == nullptr) return;
@@ -1115,9 +1168,10 @@ __global__ __launch_bounds__((64 * NWAVES), (Mfma<D, NCB, KV8, NWAVES>::WAVES)) 
             const int d4 = e - n * D4;
             const int i = n / G;
             const int h = g * G + (n - i * G);
-            const float l = lbuf[n];
+            float mn, l;
+            const float4_t sv = state_at(n, d4, mn, l);
             const float inv = l > 0.f ? a.v_scale / l : 0.f;
-            const float4_t v = *reinterpret_cast<const float4_t*>(abuf + n * C::APITCH + 4 * d4) * inv;
+            const float4_t v = sv * inv;
             const size_t o = (static_cast<size_t>(si.row0 + i) * a.num_q_heads + h) * D + 4 * d4;
             if (a.out_bf16) {
                 uint2 w;

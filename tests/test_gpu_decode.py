@@ -106,14 +106,21 @@ ONE_SLOT = [s for s in SMALL if s[7] != "f32" and s[5] <= 128
             and s[3] // s[4] * max(s[2] or [1]) <= 16]
 
 
-@pytest.mark.parametrize("fused", [True, False], ids=["fused_merge", "separate_merge"])
+@pytest.mark.parametrize("mode", ["fused_merge", "separate_merge", "attention"])
 @pytest.mark.parametrize("spec", ONE_SLOT, ids=[s[0] for s in ONE_SLOT])
-def test_one_slot_per_request(spec, fused):
+def test_one_slot_per_request(spec, mode):
     """A budget of at most one workgroup per request (cu_count 1): the capacity is the batch, every
-    request is one slot, and the decode runs its eight-wave form with slots split evenly."""
+    request is one slot, and the decode runs its eight-wave form with slots split evenly (planned
+    by pa_plan, or in place by pa_attention)."""
     case, P, T = _small_case(spec, seed=12)
-    announce(f"one slot per request {spec[0]} fused={fused}")
-    out, step = _run(case, P, T, cu_count=1, fused=fused)
+    announce(f"one slot per request {spec[0]} {mode}")
+    if mode == "attention":
+        step = DecodeStep.for_case(case, PlanConfig(cu_count=1, max_partitions=P, tile_tokens=T))
+        step.out.fill_(float("nan"))
+        out = step.run_case(case, whole=True)
+        torch.cuda.synchronize()
+    else:
+        out, step = _run(case, P, T, cu_count=1, fused=(mode == "fused_merge"))
     assert step.capacity == case.num_seqs
     got = to_f64(out)
     assert_close(got, oracle_direct(case), tolerance_kind(case), spec[0])
