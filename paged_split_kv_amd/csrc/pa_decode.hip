@@ -7,21 +7,26 @@
 // goes to the workspace; pa_merge combines a request's slots.
 //
 // Design (bf16 / fp8 caches, the matrix-core kernel):
-//  * one workgroup of NW waves per (slot, kv head).  The slot's keys are cut into 16-key chunks (a
-//    chunk never straddles a page: pages hold 16, 64 or 128 tokens and slots start on tile
-//    boundaries); wave w takes units w, w+NW, ... of consecutive chunks, the unit being the plan's
-//    largest slot split NW ways, so every streaming wave carries one unit and a small slot runs
-//    fewer waves, leaving bandwidth to the large ones; the NW states merge in LDS at the end.
+//  * one workgroup of NW waves (4; 8 when every request is one slot) per (slot, kv head).  The
+//    slot's keys are cut into 16-key chunks (a chunk never straddles a page: pages hold 16, 64 or
+//    128 tokens and slots start on tile boundaries); wave w takes units w, w+NW, ... of consecutive
+//    chunks, the unit being the plan's largest slot split NW ways (each slot split evenly in the
+//    8-wave form), so every streaming wave carries one unit and a small slot runs fewer waves,
+//    leaving bandwidth to the large ones; the NW states merge in LDS at the end.
 //  * all query rows of the group -- G heads x L verify tokens, M = G*L <= 64 -- form the columns
 //    of 16-wide MFMA blocks, so each K/V byte is read from HBM once per (slot, kv head) whatever L is.
-//  * each chunk's K and V (16 x D each) are fetched with 16-byte coalesced loads two chunks ahead into
-//    registers, written to a per-wave LDS buffer with an XOR swizzle on the 16-byte column, and read
-//    back in matrix-core operand order.  Rows past the slot's last key are written as zeros, so
-//    whatever a page holds past the context (even NaN) never reaches the products.
+//  * each chunk's K and V (16 x D each) are fetched PF chunks ahead into registers with 16-byte
+//    coalesced non-temporal buffer loads, written to a per-wave LDS buffer with an XOR swizzle on
+//    the 16-byte column, and read back in matrix-core operand order.  Rows past the slot's last key
+//    are written as zeros, so whatever a page holds past the context (even NaN) never reaches the
+//    products.
 //  * S^T = K . Q^T on v_mfma_f32_16x16x32_bf16: output lane l holds query row (l & 15) and keys
-//    4*(l >> 4) + j, so the per-row softmax max needs only 2 cross-lane steps and the probabilities
-//    are already in the B-operand order of O^T = V^T . P^T on v_mfma_f32_16x16x16_bf16, whose
-//    output lane again holds query row (l & 15): the per-row rescale factors stay in-lane.
+//    4*(l >> 4) + j, so the per-row softmax max needs only 2 cross-lane steps (gfx950 row swaps)
+//    and the probabilities are already in the B-operand order of O^T = V^T . P^T (16x16x16, or
+//    16x16x32 over two chunks at once), whose output lane again holds query row (l & 15): the
+//    per-row rescale factors stay in-lane.
+//  * head_dim 256 instead splits the head dimension across groups of two waves (four at four row
+//    blocks; see Mfma::DS), so two workgroups per CU fit without spilling.
 //  * fp8 (OCP e4m3fn) codes are widened exactly to bf16 in registers; k_scale folds into the score
 //    scale and v_scale into the final state.  Probabilities are rounded to bf16 for P.V.
 // The fp32-cache kernel is plain vector code (fp32 throughout) with the same outputs.
@@ -359,8 +364,9 @@ struct Mfma {
     static constexpr int XBUF = 2 * NCB * NW * 64 * 16;  // partial-score exchange, two parities (DS)
     // chunks in flight per wave: as many as the registers hold without spilling (scratch traffic would
     // itself be waited for in order and stall the pipeline); an fp8 chunk takes half the registers
-    static constexpr int PF_BF16 = D == 64 ? (NCB <= 2 ? 4 : 3) : (D == 128 ? (NCB == 1 ? 2 : (NCB == 2 ? 3 : 2)) : (NCB == 1 ? 2 : 1));
-    static constexpr int PF_FP8 = D == 64 ? (NCB <= 2 ? 8 : 6) : (D == 128 ? (NCB == 1 ? 4 : (NCB == 2 ? 4 : 2)) : (NCB == 1 ? 4 : 1));
+    // (head_dim 64 and 128; head_dim 256 uses PFD)
+    static constexpr int PF_BF16 = D == 64 ? (NCB <= 2 ? 4 : 3) : (NCB == 1 ? 2 : (NCB == 2 ? 3 : 2));
+    static constexpr int PF_FP8 = D == 64 ? (NCB <= 2 ? 8 : 6) : (NCB <= 2 ? 4 : 2);
     static constexpr int PF = DS ? PFD : (KV8 ? PF_FP8 : PF_BF16);
     // chunks per compute step: two where the registers allow, so each step runs two independent
     // score chains and one softmax pass over 32 keys (the per-chunk latency of a lone wave drops)
