@@ -95,8 +95,9 @@ def cpu_baseline(pool, budget_s: float, max_steps: int, window: int = 0):
 
 
 def bench_mixed(args, batches, cu_count):
-    """The decode-first split of a mixed batch: pa_attention over the decode requests, then
-    pa_prefill over the prompt, per step; the parts are also timed alone."""
+    """The decode-first split of a mixed batch: one pa_attention_mixed call per step (decode and
+    prompt in one launch, then the merge); the two-call form (pa_prefill, then pa_attention), the
+    same on two streams, and the parts alone are timed beside it."""
     from paged_split_kv_amd import binding as B
     from paged_split_kv_amd.runner import MixedStep, PlanConfig
 
@@ -104,13 +105,18 @@ def bench_mixed(args, batches, cu_count):
     steps = [MixedStep(c, 1, PlanConfig(cu_count=cu_count), concurrent=True) for c in batches]
     m_side = [m.side for m in steps]
     for m in steps:
-        m.side = None                  # the timed step runs on one stream
+        m.side = None                  # the two-call forms run on one stream unless timed otherwise
     n = len(batches)
     K = args.steps
 
     def part(i, which):
         c, m = batches[i % n], steps[i % n]
         if which == "step":
+            m.one_call = True
+            m.run(c, stream)
+            m.one_call = False
+            return
+        if which == "two_calls":
             m.run(c, stream)
             return
         if which == "two_streams":
@@ -140,6 +146,7 @@ def bench_mixed(args, batches, cu_count):
         return a.elapsed_time(b) / K
 
     step_ms = timed("step", args.warmup)
+    two_calls_ms = timed("two_calls", 8)
     two_ms = timed("two_streams", 8)
     dec_ms = timed("decode", 8)
     pre_ms = timed("prefill", 8)
@@ -162,9 +169,10 @@ def bench_mixed(args, batches, cu_count):
                    "planner": {"budget": "2 x CU", "cu_count": cu_count, "max_partitions": 256, "tile_tokens": 256}},
         "us_per_step": round(step_ms * 1e3, 2),
         "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 1),
-        "step": "pa_split_decode_first on the host; pa_prefill over the prompt, then pa_attention over the "
-                "decodes, on one stream",
+        "step": "pa_split_decode_first on the host; pa_attention_mixed: the decodes (planned in place) and "
+                "the prompt's query blocks in one launch, then pa_merge",
         "decode_part_us": round(dec_ms * 1e3, 2), "prefill_part_us": round(pre_ms * 1e3, 2),
+        "two_calls_us_per_step": round(two_calls_ms * 1e3, 2),
         "two_streams_us_per_step": round(two_ms * 1e3, 2),
         "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,

@@ -235,6 +235,38 @@ pa_status pa_prefill(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t 
                      pa_dtype out_dtype, void* stream);
 
 /*
+ * A mixed batch whose requests are ordered decodes first, in one call (opengfx1030/vllm-rdna PR #29,
+ * Change 2: decode and verify rows to the split-KV decode, the rest to the prefill kernel).
+ * Requests [0, num_decodes) are the decode part: each has at most max_q_len query tokens, their rows
+ * are [0, num_decode_rows) (num_decode_rows = cu[num_decodes], as pa_split_decode_first reports it),
+ * and they are planned, decoded and merged exactly as pa_attention does with num_seqs = num_decodes
+ * and num_rows = num_decode_rows: the plan buffers (sized for num_decodes requests), the workspace and
+ * out rows [0, num_decode_rows) receive the same values.  Requests [num_decodes, num_seqs) are
+ * prompts, computed as pa_prefill computes them from the slices context_lens + num_decodes,
+ * block_tables + num_decodes rows and cu_query_lens + num_decodes: out rows [num_decode_rows,
+ * cu[num_seqs]) get their attention, rows [cu[num_seqs], num_rows) zeros.
+ * Where the decode part is planned in place and the prompts' query blocks fit the decode's query
+ * rows per workgroup (or can be cut to fit while there are at most 64 prompt rows), the decode and
+ * the prompts share one launch (decode workgroups first, the prompts' after them) followed by the
+ * merge: two launches for the whole batch; otherwise the parts are launched apart.  Prompt query
+ * blocks may then hold fewer tokens than pa_prefill's, which changes only how the work is cut.
+ * cu_query_lens is required.  Errors: those of pa_attention on the decode part and of pa_prefill
+ * on the prompts, plus PA_INVALID_ARG for num_decodes outside [0, num_seqs] or num_decode_rows
+ * outside [0, num_rows]; all before any launch.
+ */
+pa_status pa_attention_mixed(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t num_q_heads,
+                             int32_t head_dim, const void* k_cache, const void* v_cache,
+                             pa_dtype kv_dtype, int32_t num_blocks, int32_t num_kv_heads,
+                             int32_t block_size, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                             const int32_t* cu_query_lens, int32_t num_decodes, int32_t num_decode_rows,
+                             int32_t max_q_len, int32_t sliding_window, float scale, float k_scale,
+                             float v_scale, int32_t cu_count, int32_t budget_mult, int32_t max_partitions,
+                             int32_t tile_tokens, int32_t capacity, int32_t* work_info,
+                             int32_t* reduce_info, int32_t* num_work, void* workspace,
+                             size_t workspace_bytes, void* out, pa_dtype out_dtype, void* stream);
+
+/*
  * The decode-first split of a batch whose requests are ordered decodes first (opengfx1030/vllm-rdna
  * PR #29, Change 2, the builder's split): the leading requests with at most `threshold` query tokens
  * (1 + speculative tokens) are the decode part.  HOST array cu_query_lens_host [num_seqs + 1];

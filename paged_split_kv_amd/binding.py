@@ -28,7 +28,7 @@ _DTYPE_OF_NAME = {"f32": PA_F32, "bf16": PA_BF16, "fp8": PA_FP8_E4M3}
 _TORCH_OF_NAME = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
 
 SYMBOLS = ("pa_plan_capacity", "pa_workspace_bytes", "pa_plan", "pa_decode", "pa_merge",
-           "pa_attention", "pa_prefill", "pa_split_decode_first", "pa_status_string",
+           "pa_attention", "pa_prefill", "pa_attention_mixed", "pa_split_decode_first", "pa_status_string",
            "pa_device_cu_count")
 
 
@@ -73,6 +73,10 @@ def load(path: str = LIB_PATH):
     lib.pa_prefill.argtypes = [vp, ctypes.c_int, i32, i32, i32, vp, vp, ctypes.c_int, i32, i32, i32, vp, i32,
                                vp, i32, vp, i32, f32, f32, f32, vp, ctypes.c_int, vp]
     lib.pa_prefill.restype = ctypes.c_int
+    lib.pa_attention_mixed.argtypes = [vp, ctypes.c_int, i32, i32, i32, vp, vp, ctypes.c_int, i32, i32, i32,
+                                       vp, i32, vp, i32, vp, i32, i32, i32, i32, f32, f32, f32, i32, i32,
+                                       i32, i32, i32, vp, vp, vp, vp, ctypes.c_size_t, vp, ctypes.c_int, vp]
+    lib.pa_attention_mixed.restype = ctypes.c_int
     lib.pa_split_decode_first.argtypes = [ctypes.POINTER(i32), i32, i32, ctypes.POINTER(i32),
                                           ctypes.POINTER(i32)]
     lib.pa_split_decode_first.restype = ctypes.c_int
@@ -290,6 +294,54 @@ def pa_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
                                tile_tokens, capacity,
                                _ptr(work_info), _ptr(reduce_info), _ptr(num_work), _ptr(workspace),
                                workspace.numel(), _ptr(out), qd, _stream(stream)), "pa_attention")
+
+
+def pa_attention_mixed(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_dtype: str,
+                       block_tables: torch.Tensor, context_lens: torch.Tensor, cu_query_lens: torch.Tensor,
+                       num_decodes: int, num_decode_rows: int, work_info: torch.Tensor,
+                       reduce_info: torch.Tensor, num_work: torch.Tensor, workspace: torch.Tensor,
+                       out: torch.Tensor, *, scale: float, cu_count: int, budget_mult: int = 2,
+                       max_partitions: int = 256, tile_tokens: int = 256, max_q_len: int = 1,
+                       k_scale: float = 1.0, v_scale: float = 1.0, sliding_window: int = 0,
+                       stream=None) -> None:
+    """A decodes-first mixed batch in one call (see include/pa.h): the plan buffers are sized for the
+    num_decodes decode requests; out receives every row."""
+    dev = q.device
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("q must be float32 or bfloat16")
+    _need(q, "q", q.dtype)
+    _need(k_cache, "k_cache", _TORCH_OF_NAME[kv_dtype], dev)
+    _need(v_cache, "v_cache", _TORCH_OF_NAME[kv_dtype], dev)
+    _need(block_tables, "block_tables", torch.int32, dev)
+    _need(context_lens, "context_lens", torch.int32, dev)
+    _need(cu_query_lens, "cu_query_lens", torch.int32, dev)
+    _need(work_info, "work_info", torch.int32, dev)
+    _need(reduce_info, "reduce_info", torch.int32, dev)
+    _need(num_work, "num_work", torch.int32, dev)
+    _need(workspace, "workspace", torch.uint8, dev)
+    _need(out, "out", q.dtype, dev)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have the shape of q")
+    R, Hq, D = q.shape
+    nb, Hkv, bs, D2 = k_cache.shape
+    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shapes do not match q")
+    B = int(context_lens.shape[0])
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs, max_blocks]")
+    if cu_query_lens.shape[0] != B + 1:
+        raise ValueError("cu_query_lens must be [num_seqs + 1]")
+    if reduce_info.numel() < 2 * num_decodes or num_work.numel() < 2:
+        raise ValueError("plan buffers smaller than num_decodes / 2")
+    qd = PA_F32 if q.dtype == torch.float32 else PA_BF16
+    _check(load().pa_attention_mixed(_ptr(q), qd, R, Hq, D, _ptr(k_cache), _ptr(v_cache),
+                                     _DTYPE_OF_NAME[kv_dtype], nb, Hkv, bs, _ptr(block_tables),
+                                     int(block_tables.shape[1]), _ptr(context_lens), B, _ptr(cu_query_lens),
+                                     num_decodes, num_decode_rows, max_q_len, sliding_window, scale, k_scale,
+                                     v_scale, cu_count, budget_mult, max_partitions, tile_tokens,
+                                     int(work_info.shape[0]), _ptr(work_info), _ptr(reduce_info),
+                                     _ptr(num_work), _ptr(workspace), workspace.numel(), _ptr(out), qd,
+                                     _stream(stream)), "pa_attention_mixed")
 
 
 def pa_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_dtype: str,

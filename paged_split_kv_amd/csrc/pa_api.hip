@@ -168,6 +168,70 @@ pa_status prepare_merge(int32_t num_rows, int32_t num_q_heads, int32_t head_dim,
 
 }  // namespace
 
+namespace {
+
+// Checks of pa_prefill; on success fills the kernel arguments.  block_tokens 0 takes the kernel's own
+// block size (prefill_block_tokens).
+pa_status prepare_prefill(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t num_q_heads,
+                          int32_t head_dim, const void* k_cache, const void* v_cache, pa_dtype kv_dtype,
+                          int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t num_seqs, const int32_t* cu_query_lens,
+                          int32_t sliding_window, float scale, float k_scale, float v_scale, void* out,
+                          pa_dtype out_dtype, int block_tokens, pa::DecodeArgs* args) {
+    if (num_rows < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_blocks < 0 || num_seqs < 0 ||
+        max_blocks_per_seq < 0 || head_dim < 1 || block_size < 1 || sliding_window < 0)
+        return PA_INVALID_ARG;
+    if (q_dtype != PA_F32 && q_dtype != PA_BF16) return PA_INVALID_ARG;
+    if (kv_dtype != PA_F32 && kv_dtype != PA_BF16 && kv_dtype != PA_FP8_E4M3) return PA_INVALID_ARG;
+    if (out_dtype != q_dtype || num_q_heads % num_kv_heads != 0) return PA_INVALID_ARG;
+    if (!(scale == scale) || !(k_scale == k_scale) || !(v_scale == v_scale)) return PA_INVALID_ARG;
+    if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PA_UNSUPPORTED;
+    if (kv_dtype == PA_F32) return PA_UNSUPPORTED;
+    const int group = num_q_heads / num_kv_heads;
+    if (group > PA_MAX_GROUP_ROWS) return PA_UNSUPPORTED;
+    if (!cu_query_lens || (num_rows > 0 && (!q || !out))) return PA_INVALID_ARG;
+    if (num_seqs > 0 && (!k_cache || !v_cache || !block_tables || !context_lens)) return PA_INVALID_ARG;
+    if ((q && !aligned(q, 16)) || (out && !aligned(out, 16)) || (k_cache && !aligned(k_cache, 16)) ||
+        (v_cache && !aligned(v_cache, 16)))
+        return PA_INVALID_ARG;
+    if ((long long)num_rows * num_q_heads > (long long)INT_MAX) return PA_UNSUPPORTED;
+
+    const int lb = block_tokens > 0 ? block_tokens : pa::prefill_block_tokens(head_dim, group);
+    // blocks of all requests together: sum ceil(L_b / lb) <= num_rows / lb + num_seqs
+    const long long blocks = (num_rows + lb - 1) / lb + (long long)num_seqs;
+    if (blocks * num_kv_heads > (long long)INT_MAX / 2) return PA_UNSUPPORTED;
+    pa::DecodeArgs& a = *args;
+    a = pa::DecodeArgs{};
+    a.q = q;
+    a.k_cache = static_cast<const uint8_t*>(k_cache);
+    a.v_cache = static_cast<const uint8_t*>(v_cache);
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.cu = cu_query_lens;
+    a.out = out;
+    a.out_bf16 = out_dtype == PA_BF16 ? 1 : 0;
+    a.num_rows = num_rows;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = group;
+    a.num_blocks = num_blocks;
+    a.block_size = block_size;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_seqs = num_seqs;
+    a.max_q_len = lb;
+    a.capacity = static_cast<int>(blocks);
+    a.tile_tokens = 256;
+    a.score_scale_log2 = scale * k_scale * pa::kLog2e;
+    a.v_scale = v_scale;
+    a.window = sliding_window;
+    a.prefill = 1;
+    a.block_tokens = lb;
+    return PA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 pa_status pa_plan_capacity(int32_t num_seqs, int32_t num_kv_heads, int32_t cu_count,
@@ -297,55 +361,113 @@ pa_status pa_prefill(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t 
                      const int32_t* context_lens, int32_t num_seqs, const int32_t* cu_query_lens,
                      int32_t sliding_window, float scale, float k_scale, float v_scale, void* out,
                      pa_dtype out_dtype, void* stream) {
-    if (num_rows < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_blocks < 0 || num_seqs < 0 ||
-        max_blocks_per_seq < 0 || head_dim < 1 || block_size < 1 || sliding_window < 0)
-        return PA_INVALID_ARG;
-    if (q_dtype != PA_F32 && q_dtype != PA_BF16) return PA_INVALID_ARG;
-    if (kv_dtype != PA_F32 && kv_dtype != PA_BF16 && kv_dtype != PA_FP8_E4M3) return PA_INVALID_ARG;
-    if (out_dtype != q_dtype || num_q_heads % num_kv_heads != 0) return PA_INVALID_ARG;
-    if (!(scale == scale) || !(k_scale == k_scale) || !(v_scale == v_scale)) return PA_INVALID_ARG;
-    if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PA_UNSUPPORTED;
-    if (kv_dtype == PA_F32) return PA_UNSUPPORTED;
-    const int group = num_q_heads / num_kv_heads;
-    if (group > PA_MAX_GROUP_ROWS) return PA_UNSUPPORTED;
-    if (!cu_query_lens || (num_rows > 0 && (!q || !out))) return PA_INVALID_ARG;
-    if (num_seqs > 0 && (!k_cache || !v_cache || !block_tables || !context_lens)) return PA_INVALID_ARG;
-    if ((q && !aligned(q, 16)) || (out && !aligned(out, 16)) || (k_cache && !aligned(k_cache, 16)) ||
-        (v_cache && !aligned(v_cache, 16)))
-        return PA_INVALID_ARG;
-    if ((long long)num_rows * num_q_heads > (long long)INT_MAX) return PA_UNSUPPORTED;
-    if (num_rows == 0) return PA_OK;
-
-    const int lb = pa::prefill_block_tokens(head_dim, group);
-    // blocks of all requests together: sum ceil(L_b / lb) <= num_rows / lb + num_seqs
-    const long long blocks = (num_rows + lb - 1) / lb + (long long)num_seqs;
-    if (blocks * num_kv_heads > (long long)INT_MAX / 2) return PA_UNSUPPORTED;
-    pa::DecodeArgs a{};
-    a.q = q;
-    a.k_cache = static_cast<const uint8_t*>(k_cache);
-    a.v_cache = static_cast<const uint8_t*>(v_cache);
-    a.block_tables = block_tables;
-    a.context_lens = context_lens;
-    a.cu = cu_query_lens;
-    a.out = out;
-    a.out_bf16 = out_dtype == PA_BF16 ? 1 : 0;
-    a.num_rows = num_rows;
-    a.num_q_heads = num_q_heads;
-    a.num_kv_heads = num_kv_heads;
-    a.group = group;
-    a.num_blocks = num_blocks;
-    a.block_size = block_size;
-    a.max_blocks = max_blocks_per_seq;
-    a.num_seqs = num_seqs;
-    a.max_q_len = lb;
-    a.capacity = static_cast<int>(blocks);
-    a.tile_tokens = 256;
-    a.score_scale_log2 = scale * k_scale * pa::kLog2e;
-    a.v_scale = v_scale;
-    a.window = sliding_window;
-    a.prefill = 1;
-    a.block_tokens = lb;
+    pa::DecodeArgs a;
+    const pa_status st = prepare_prefill(q, q_dtype, num_rows, num_q_heads, head_dim, k_cache, v_cache,
+                                         kv_dtype, num_blocks, num_kv_heads, block_size, block_tables,
+                                         max_blocks_per_seq, context_lens, num_seqs, cu_query_lens,
+                                         sliding_window, scale, k_scale, v_scale, out, out_dtype, 0, &a);
+    if (st != PA_OK || num_rows == 0) return st;
     return from_hip(pa::launch_prefill(a, head_dim, kv_dtype, q_dtype == PA_F32, pa::as_stream(stream)));
+}
+
+pa_status pa_attention_mixed(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t num_q_heads,
+                             int32_t head_dim, const void* k_cache, const void* v_cache,
+                             pa_dtype kv_dtype, int32_t num_blocks, int32_t num_kv_heads,
+                             int32_t block_size, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                             const int32_t* cu_query_lens, int32_t num_decodes, int32_t num_decode_rows,
+                             int32_t max_q_len, int32_t sliding_window, float scale, float k_scale,
+                             float v_scale, int32_t cu_count, int32_t budget_mult, int32_t max_partitions,
+                             int32_t tile_tokens, int32_t capacity, int32_t* work_info,
+                             int32_t* reduce_info, int32_t* num_work, void* workspace,
+                             size_t workspace_bytes, void* out, pa_dtype out_dtype, void* stream) {
+    if (num_seqs < 0 || num_decodes < 0 || num_decodes > num_seqs || num_rows < 0 ||
+        num_decode_rows < 0 || num_decode_rows > num_rows || max_blocks_per_seq < 0)
+        return PA_INVALID_ARG;
+    if (!cu_query_lens) return PA_INVALID_ARG;
+    // all requests are decodes, or none is: one of the two entry points alone
+    if (num_decodes == num_seqs)
+        return pa_attention(q, q_dtype, num_rows, num_q_heads, head_dim, k_cache, v_cache, kv_dtype,
+                            num_blocks, num_kv_heads, block_size, block_tables, max_blocks_per_seq,
+                            context_lens, num_seqs, cu_query_lens, max_q_len, sliding_window, scale,
+                            k_scale, v_scale, cu_count, budget_mult, max_partitions, tile_tokens, capacity,
+                            work_info, reduce_info, num_work, workspace, workspace_bytes, out, out_dtype,
+                            stream);
+    if (num_decodes == 0)
+        return pa_prefill(q, q_dtype, num_rows, num_q_heads, head_dim, k_cache, v_cache, kv_dtype,
+                          num_blocks, num_kv_heads, block_size, block_tables, max_blocks_per_seq,
+                          context_lens, num_seqs, cu_query_lens, sliding_window, scale, k_scale, v_scale,
+                          out, out_dtype, stream);
+
+    // the decode part: requests [0, num_decodes), rows [0, num_decode_rows), planned in place
+    int32_t cap = 0;
+    pa_status st = check_plan(context_lens, num_decodes, num_kv_heads, cu_count, budget_mult,
+                              max_partitions, tile_tokens, sliding_window, capacity, work_info,
+                              reduce_info, num_work, &cap);
+    if (st != PA_OK) return st;
+    pa::DecodeArgs d;
+    bool nothing = false;
+    st = prepare_decode(q, q_dtype, num_decode_rows, num_q_heads, head_dim, k_cache, v_cache, kv_dtype,
+                        num_blocks, num_kv_heads, block_size, block_tables, max_blocks_per_seq,
+                        context_lens, num_decodes, cu_query_lens, max_q_len, sliding_window, scale,
+                        k_scale, v_scale, work_info, reduce_info, num_work, capacity, tile_tokens,
+                        workspace, workspace_bytes, nullptr, q_dtype, &d, &nothing);
+    if (st != PA_OK) return st;
+    if (out_dtype != q_dtype) return PA_INVALID_ARG;
+    pa::MergeArgs m;
+    st = prepare_merge(num_decode_rows, num_q_heads, head_dim, num_decodes, cu_query_lens, max_q_len,
+                       reduce_info, capacity, workspace, workspace_bytes, out, out_dtype, &m);
+    if (st != PA_OK) return st;
+
+    // the prompts: requests [num_decodes, num_seqs), absolute rows of q and out (rows past the last
+    // cumulative length are written as zeros)
+    const int group = num_q_heads / num_kv_heads;
+    const int ncb_dec = pa::column_blocks(group * max_q_len);
+    const int lb_own = pa::prefill_block_tokens(head_dim, group);
+    // one launch when the prompts' query blocks fit the decode's column blocks, or can be cut to fit
+    // while few (at most 64 prompt rows: smaller blocks each read all their keys again)
+    int lb = 0;
+    if (pa::column_blocks(group * lb_own) == ncb_dec) lb = lb_own;
+    else if (num_rows - num_decode_rows <= 64 && 16 * ncb_dec >= group) lb = 16 * ncb_dec / group;
+    const bool in_place = !nothing && kv_dtype != PA_F32 && num_decodes <= PA_INLINE_PLAN_SEQS;
+    const bool fused = in_place && lb > 0 && pa::mixed_launch_supported(head_dim, kv_dtype, ncb_dec);
+    const size_t bt_off = (size_t)num_decodes * (size_t)max_blocks_per_seq;
+    pa::DecodeArgs p;
+    st = prepare_prefill(q, q_dtype, num_rows, num_q_heads, head_dim, k_cache, v_cache, kv_dtype,
+                         num_blocks, num_kv_heads, block_size, block_tables ? block_tables + bt_off : nullptr,
+                         max_blocks_per_seq, context_lens + num_decodes, num_seqs - num_decodes,
+                         cu_query_lens + num_decodes, sliding_window, scale, k_scale, v_scale, out, out_dtype,
+                         fused ? lb : 0, &p);
+    if (st != PA_OK) return st;
+
+    hipStream_t s = pa::as_stream(stream);
+    if (in_place) {
+        d.plan_inline = 1;
+        d.plan_cap = cap;
+        d.max_partitions = max_partitions;
+        d.plan_work_out = reinterpret_cast<int4*>(work_info);
+        d.plan_reduce_out = reinterpret_cast<int2*>(reduce_info);
+        d.plan_num_work_out = num_work;
+    } else {
+        st = from_hip(pa::launch_plan(context_lens, cu_query_lens, num_decodes, cap, capacity, max_partitions,
+                                      tile_tokens, sliding_window, work_info, reduce_info, num_work, s));
+        if (st != PA_OK) return st;
+    }
+    if (fused) {
+        st = from_hip(pa::launch_mixed(d, p, head_dim, kv_dtype, q_dtype == PA_F32, ncb_dec, s));
+        if (st != PA_OK) return st;
+    } else {
+        if (!nothing) {
+            st = from_hip(pa::launch_decode(d, head_dim, kv_dtype, q_dtype == PA_F32, s));
+            if (st != PA_OK) return st;
+        }
+        if (num_rows > 0) {
+            st = from_hip(pa::launch_prefill(p, head_dim, kv_dtype, q_dtype == PA_F32, s));
+            if (st != PA_OK) return st;
+        }
+    }
+    if (num_decode_rows == 0) return PA_OK;
+    return from_hip(pa::launch_merge(m, head_dim, out_dtype == PA_BF16, s));
 }
 
 pa_status pa_split_decode_first(const int32_t* cu_query_lens_host, int32_t num_seqs, int32_t threshold,

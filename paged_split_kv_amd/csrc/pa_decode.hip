@@ -30,6 +30,7 @@
 //  * fp8 (OCP e4m3fn) codes are widened exactly to bf16 in registers; k_scale folds into the score
 //    scale and v_scale into the final state.  Probabilities are rounded to bf16 for P.V.
 // The fp32-cache kernel is plain vector code (fp32 throughout) with the same outputs.
+#include <climits>
 #include <type_traits>
 
 #include "pa_device.h"
@@ -415,9 +416,15 @@ __device__ __forceinline__ float sum_over_row_groups(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <int D, int NCB, bool KV8, bool QF32, int NWAVES>
-__global__ __launch_bounds__((64 * NWAVES), (Mfma<D, NCB, KV8, NWAVES>::WAVES)) void decode_mfma_kernel(const DecodeArgs a) {
+// MIXED: the launch holds two parts (see LaunchArgs); otherwise every workgroup runs part[0].
+template <int D, int NCB, bool KV8, bool QF32, int NWAVES, bool MIXED>
+__global__ __launch_bounds__((64 * NWAVES), (Mfma<D, NCB, KV8, NWAVES>::WAVES)) void decode_mfma_kernel(const LaunchArgs L) {
     using C = Mfma<D, NCB, KV8, NWAVES>;
+    const bool second = MIXED && static_cast<int>(blockIdx.x) >= L.split;
+    // a copy (the fields become scalar selects): through a pointer chosen at run time the compiler
+    // could no longer treat the arguments as invariant and reloaded them in the loop
+    const DecodeArgs a = second ? L.part[1] : L.part[0];
+    const int bid = static_cast<int>(blockIdx.x) - (second ? L.split : 0);
     __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS];
     __shared__ int s_last;
 
@@ -427,16 +434,16 @@ __global__ __launch_bounds__((64 * NWAVES), (Mfma<D, NCB, KV8, NWAVES>::WAVES)) 
     // page ids, buffer resources) stays in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int work_groups = a.capacity * a.num_kv_heads;
-    if (static_cast<int>(blockIdx.x) >= work_groups) {
+    if (bid >= work_groups) {
         // merge launched with the decode (or a prefill): trailing workgroups write the rows no slot
         // owns as zeros
-        const int r = (blockIdx.x - work_groups) * C::NW + wave;
+        const int r = (bid - work_groups) * C::NW + wave;
         if (a.prefill) zero_prefill_tail_row<D>(a, r, lane);
         else zero_unowned_row<D>(a, r, lane);
         return;
     }
-    const int slot = blockIdx.x / a.num_kv_heads;
-    const int g = blockIdx.x - slot * a.num_kv_heads;
+    const int slot = bid / a.num_kv_heads;
+    const int g = bid - slot * a.num_kv_heads;
 
     // ---- slot geometry.  Dependent loads are kept to three levels: the work entry; then the
     // request's length, cumulative query lengths and (speculatively, over the plan's tile range)
@@ -1288,13 +1295,48 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeArgs a) {
     }
 }
 
+// Workgroups of one part: its slots (or query blocks) times kv heads, and with an output a trailing
+// workgroup per NW rows for the zero fill.
+template <int NW>
+unsigned part_workgroups(const DecodeArgs& a) {
+    unsigned n = static_cast<unsigned>(a.capacity) * static_cast<unsigned>(a.num_kv_heads);
+    if (a.out) n += static_cast<unsigned>((a.num_rows + NW - 1) / NW);
+    return n;
+}
+
 template <int D, int NCB, bool KV8, int NW = 4>
 hipError_t launch_mfma_q(const DecodeArgs& a, bool qf32, dim3 grid, hipStream_t stream) {
+    (void)grid;
+    LaunchArgs L;
+    L.part[0] = a;
+    L.part[1] = a;
+    L.split = INT_MAX;
+    const dim3 g(part_workgroups<NW>(a));
     const dim3 block(64 * NW);
-    if (a.out) grid.x += (a.num_rows + NW - 1) / NW;   // one wave per row for the zero fill
-    if (qf32) hipLaunchKernelGGL((decode_mfma_kernel<D, NCB, KV8, true, NW>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((decode_mfma_kernel<D, NCB, KV8, false, NW>), grid, block, 0, stream, a);
+    if (qf32) hipLaunchKernelGGL((decode_mfma_kernel<D, NCB, KV8, true, NW, false>), g, block, 0, stream, L);
+    else hipLaunchKernelGGL((decode_mfma_kernel<D, NCB, KV8, false, NW, false>), g, block, 0, stream, L);
     return hipGetLastError();
+}
+
+template <int D, int NCB, bool KV8>
+hipError_t launch_mixed_q(const DecodeArgs& dec, const DecodeArgs& pre, bool qf32, hipStream_t stream) {
+    constexpr int NW = 4;
+    LaunchArgs L;
+    L.part[0] = dec;
+    L.part[1] = pre;
+    L.split = static_cast<int>(part_workgroups<NW>(dec));
+    const dim3 g(static_cast<unsigned>(L.split) + part_workgroups<NW>(pre));
+    const dim3 block(64 * NW);
+    if (qf32) hipLaunchKernelGGL((decode_mfma_kernel<D, NCB, KV8, true, NW, true>), g, block, 0, stream, L);
+    else hipLaunchKernelGGL((decode_mfma_kernel<D, NCB, KV8, false, NW, true>), g, block, 0, stream, L);
+    return hipGetLastError();
+}
+
+template <int D, bool KV8>
+hipError_t launch_mixed_ncb(const DecodeArgs& dec, const DecodeArgs& pre, int ncb, bool qf32, hipStream_t stream) {
+    if (ncb == 1) return launch_mixed_q<D, 1, KV8>(dec, pre, qf32, stream);
+    if (ncb == 2) return launch_mixed_q<D, 2, KV8>(dec, pre, qf32, stream);
+    return launch_mixed_q<D, 4, KV8>(dec, pre, qf32, stream);
 }
 
 template <int D, bool KV8>
@@ -1346,8 +1388,7 @@ int prefill_block_tokens(int head_dim, int group) {
 
 hipError_t launch_prefill(const DecodeArgs& a, int head_dim, pa_dtype kv_dtype, bool q_f32,
                           hipStream_t stream) {
-    const int rows = a.group * a.block_tokens;
-    const int ncb = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+    const int ncb = column_blocks(a.group * a.block_tokens);
     const dim3 grid(static_cast<unsigned>(a.capacity) * static_cast<unsigned>(a.num_kv_heads));
     switch (head_dim) {
         case 64: return launch_d<64>(a, kv_dtype, ncb, q_f32, grid, stream);
@@ -1356,10 +1397,28 @@ hipError_t launch_prefill(const DecodeArgs& a, int head_dim, pa_dtype kv_dtype, 
     }
 }
 
+bool mixed_launch_supported(int head_dim, pa_dtype kv_dtype, int ncb) {
+    return (head_dim == 64 || head_dim == 128 || head_dim == 256) &&
+           (kv_dtype == PA_BF16 || kv_dtype == PA_FP8_E4M3) && ncb >= 1 && ncb <= 4 && ncb != 3;
+}
+
+hipError_t launch_mixed(const DecodeArgs& dec, const DecodeArgs& pre, int head_dim, pa_dtype kv_dtype,
+                        bool q_f32, int ncb, hipStream_t stream) {
+    if (!mixed_launch_supported(head_dim, kv_dtype, ncb)) return hipErrorInvalidValue;
+    const bool kv8 = kv_dtype == PA_FP8_E4M3;
+    switch (head_dim) {
+        case 64: return kv8 ? launch_mixed_ncb<64, true>(dec, pre, ncb, q_f32, stream)
+                            : launch_mixed_ncb<64, false>(dec, pre, ncb, q_f32, stream);
+        case 128: return kv8 ? launch_mixed_ncb<128, true>(dec, pre, ncb, q_f32, stream)
+                             : launch_mixed_ncb<128, false>(dec, pre, ncb, q_f32, stream);
+        default: return kv8 ? launch_mixed_ncb<256, true>(dec, pre, ncb, q_f32, stream)
+                            : launch_mixed_ncb<256, false>(dec, pre, ncb, q_f32, stream);
+    }
+}
+
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, pa_dtype kv_dtype, bool q_f32,
                          hipStream_t stream) {
-    const int rows = a.group * a.max_q_len;
-    const int ncb = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+    const int ncb = column_blocks(a.group * a.max_q_len);
     const dim3 grid(static_cast<unsigned>(a.capacity) * static_cast<unsigned>(a.num_kv_heads));
     if (grid.x == 0) return hipSuccess;
     switch (head_dim) {

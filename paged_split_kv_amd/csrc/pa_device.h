@@ -305,6 +305,14 @@ struct DecodeArgs {
     float v_scale;
 };
 
+// A decode launch: workgroups [0, split) run part[0], workgroups [split, grid) run part[1] with
+// workgroup indices counted from split.  A plain launch sets split past the grid; a mixed batch's
+// launch runs its decode requests (in-place plan) as part[0] and its prompts' query blocks as part[1].
+struct LaunchArgs {
+    DecodeArgs part[2];
+    int split;
+};
+
 struct MergeArgs {
     const int32_t* cu;          // nullable
     const int2* reduce_info;
@@ -325,6 +333,14 @@ hipError_t launch_decode(const DecodeArgs& a, int head_dim, pa_dtype kv_dtype, b
 hipError_t launch_merge(const MergeArgs& a, int head_dim, bool out_bf16, hipStream_t stream);
 // Query tokens per prefill workgroup for a group of G query heads per kv head (G * tokens rows).
 int prefill_block_tokens(int head_dim, int group);
+// Column blocks (16 query rows each) of a decode launch over `rows` query rows per workgroup.
+inline int column_blocks(int rows) { return rows <= 16 ? 1 : (rows <= 32 ? 2 : 4); }
+// One launch for a mixed batch: the decode part (in-place plan) and the prompts' query blocks, both
+// with `ncb` column blocks; false when the kernel has no form for that shape (the caller then
+// launches the parts apart).
+bool mixed_launch_supported(int head_dim, pa_dtype kv_dtype, int ncb);
+hipError_t launch_mixed(const DecodeArgs& dec, const DecodeArgs& pre, int head_dim, pa_dtype kv_dtype,
+                        bool q_f32, int ncb, hipStream_t stream);
 hipError_t launch_prefill(const DecodeArgs& a, int head_dim, pa_dtype kv_dtype, bool q_f32,
                           hipStream_t stream);
 

@@ -117,10 +117,14 @@ class MixedStep:
     view of the output), the rest through pa_prefill on the same stream.  The split is taken from a
     host copy of the cumulative query lengths, as a batch builder holds them; buffers are made once.
     With concurrent=True the two parts, which read the same inputs and write disjoint rows, run on
-    two streams (the prefill on a second stream of default priority) and join before returning."""
+    two streams (the prefill on a second stream of default priority) and join before returning.
+    With one_call=True the step is one pa_attention_mixed call (decode and prompts share a launch
+    where they fit one, then the merge)."""
 
-    def __init__(self, case, threshold: int, plan: Optional[PlanConfig] = None, concurrent: bool = False):
+    def __init__(self, case, threshold: int, plan: Optional[PlanConfig] = None, concurrent: bool = False,
+                 one_call: bool = False):
         self.threshold = threshold
+        self.one_call = one_call
         self.side = torch.cuda.Stream(device=case.q.device) if concurrent else None
         self.nd, self.ndt = B.pa_split_decode_first(case.cu_query_lens.cpu().numpy(), threshold)
         self.out = torch.empty_like(case.q)
@@ -135,6 +139,15 @@ class MixedStep:
     def run(self, case, stream=None) -> torch.Tensor:
         nd, ndt = self.nd, self.ndt
         main = stream if stream is not None else torch.cuda.current_stream(case.q.device)
+        if self.one_call and self.dec is not None:
+            d, p = self.dec, self.dec.plan_cfg
+            B.pa_attention_mixed(case.q, case.k_cache, case.v_cache, case.kv_dtype, case.block_tables,
+                                 case.context_lens, case.cu_query_lens, nd, ndt, d.work_info, d.reduce_info,
+                                 d.num_work, d.workspace, self.out, scale=case.scale, cu_count=p.cu_count,
+                                 budget_mult=p.budget_mult, max_partitions=p.max_partitions,
+                                 tile_tokens=p.tile_tokens, max_q_len=self.threshold, k_scale=case.k_scale,
+                                 v_scale=case.v_scale, sliding_window=case.window, stream=main)
+            return self.out
         pre = main
         if self.side is not None and self.dec is not None:
             self.side.wait_stream(main)
@@ -153,6 +166,6 @@ class MixedStep:
 
 
 def mixed_step(case, threshold: int, plan: Optional[PlanConfig] = None, stream=None,
-               concurrent: bool = False) -> torch.Tensor:
+               concurrent: bool = False, one_call: bool = False) -> torch.Tensor:
     """One decode-first split step of a mixed batch (see MixedStep)."""
-    return MixedStep(case, threshold, plan, concurrent).run(case, stream)
+    return MixedStep(case, threshold, plan, concurrent, one_call).run(case, stream)

@@ -220,6 +220,34 @@ def test_prefill_argument_checks():
     assert _prefill_status(R=0) == B.PA_OK                         # nothing to write: no launch
 
 
+def _mixed_status(**kw):
+    a = dict(_GOOD)
+    a.update(dict(cu=256, out=512, cuc=256, mult=2, P=256, nd=2, ndt=2))
+    a.update(kw)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return B.load().pa_attention_mixed(vp(a["q"]), a["qd"], a["R"], a["Hq"], a["D"], vp(a["k"]), vp(a["v"]),
+                                       a["kvd"], a["nb"], a["Hkv"], a["bs"], vp(a["bt"]), a["mb"], vp(a["ctx"]),
+                                       a["Bn"], vp(a["cu"]), a["nd"], a["ndt"], a["ql"], a["win"], a["scale"],
+                                       a["ks"], a["vs"], a["cuc"], a["mult"], a["P"], a["T"], a["cap"],
+                                       vp(a["work"]), vp(a["red"]), vp(a["nw"]), vp(a["ws"]), a["wsb"],
+                                       vp(a["out"]), a["od"], None)
+
+
+def test_mixed_attention_argument_checks():
+    # the split itself, then the decode part's checks (plan, decode, merge), then the prompts'
+    assert _mixed_status(nd=5) == B.PA_INVALID_ARG                  # more decodes than requests
+    assert _mixed_status(nd=-1) == B.PA_INVALID_ARG
+    assert _mixed_status(ndt=5) == B.PA_INVALID_ARG                 # decode rows past the rows
+    assert _mixed_status(cu=None) == B.PA_INVALID_ARG
+    assert _mixed_status(cap=255) == B.PA_CAPACITY                  # formula for 2 requests: 256
+    assert _mixed_status(D=96) == B.PA_UNSUPPORTED
+    assert _mixed_status(od=B.PA_F32) == B.PA_INVALID_ARG
+    assert _mixed_status(out=None) == B.PA_INVALID_ARG
+    assert _mixed_status(out=520) == B.PA_INVALID_ARG
+    assert _mixed_status(kvd=B.PA_F32) == B.PA_UNSUPPORTED          # the prompts need bf16 / fp8
+    assert _mixed_status(win=-1) == B.PA_INVALID_ARG
+
+
 def test_split_decode_first_on_the_host():
     # 7 decodes then a 100-token prompt (opengfx1030/vllm-rdna PR #29 table: 7 decodes + a new prompt)
     cu = [0, 1, 2, 3, 4, 5, 6, 7, 107]

@@ -77,29 +77,35 @@ MIXED = [
     ("fp8_mixed_window", [5000, 40, 700], [1, 1, 300], 16, 2, 128, 16, "fp8", "bf16", 0, 64, 1),
     ("all_decode", [700, 33, 1], [1, 1, 1], 16, 2, 128, 16, "bf16", "bf16", 1, 0, 1),
     ("all_prefill", [700, 333], [70, 33], 16, 2, 128, 16, "bf16", "bf16", 1, 0, 1),
+    # short prompts after decodes: in one call the prompts' query blocks are cut to the decode's
+    # 16 query rows per workgroup and share its launch
+    ("short_prompts_d128", [900, 4000, 50, 30], [1, 1, 20, 9], 16, 2, 128, 16, "bf16", "bf16", 1, 0, 1),
+    ("short_prompts_fp8_window", [900, 4000, 50, 30], [1, 1, 20, 9], 8, 1, 64, 16, "fp8", "bf16", 0, 16, 1),
 ]
 
 
-@pytest.mark.parametrize("concurrent", [False, True], ids=["one_stream", "two_streams"])
+@pytest.mark.parametrize("mode", ["one_stream", "two_streams", "one_call"])
 @pytest.mark.parametrize("spec", MIXED, ids=[m[0] for m in MIXED])
-def test_mixed_batch_decode_first_split(spec, concurrent):
+def test_mixed_batch_decode_first_split(spec, mode):
     *base, threshold = spec
     case = _case(tuple(base), seed=43)
-    announce(f"mixed {spec[0]} threshold {threshold} concurrent {concurrent}")
-    out = mixed_step(case, threshold, PlanConfig(cu_count=256), concurrent=concurrent)
+    announce(f"mixed {spec[0]} threshold {threshold} {mode}")
+    out = mixed_step(case, threshold, PlanConfig(cu_count=256), concurrent=(mode == "two_streams"),
+                     one_call=(mode == "one_call"))
     torch.cuda.synchronize()
     got = to_f64(out)
     assert_close(got, oracle_direct(case), tolerance_kind(case), spec[0])
     assert (got[_zero_rows(case)] == 0.0).all()
 
 
-def test_seven_decodes_at_16k_and_a_prompt_full_size():
+@pytest.mark.parametrize("one_call", [False, True], ids=["two_calls", "one_call"])
+def test_seven_decodes_at_16k_and_a_prompt_full_size(one_call):
     """The vllm-rdna table's second scenario at its sizes: 7 decodes at 16384 tokens and a new
     100-token prompt, TP=2 per rank (H 12/2), D 256."""
     case = W.build_case("mixed_16k", [16384] * 7 + [100], num_q_heads=12, num_kv_heads=2, head_dim=256,
                         block_size=16, kv_dtype="bf16", q_dtype="bf16", seed=44, q_lens=[1] * 7 + [100],
                         device=DEV)
-    announce("mixed 7 x 16k + 100-token prompt")
-    out = mixed_step(case, 1, PlanConfig(cu_count=256))
+    announce(f"mixed 7 x 16k + 100-token prompt one_call={one_call}")
+    out = mixed_step(case, 1, PlanConfig(cu_count=256), one_call=one_call)
     torch.cuda.synchronize()
     assert_close(to_f64(out), oracle_direct(case), "bf16", "mixed full size")
