@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from paged_split_kv_amd import workloads as W
-from paged_split_kv_amd.runner import DecodeStep, PlanConfig
+from paged_split_kv_amd.runner import DecodeStep, MixedStep, PlanConfig
 from _util import announce, assert_close, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -93,3 +93,46 @@ def test_graph_replays_draft_passes(mode):
         o = other_step.run_case(other, fused=True)
         torch.cuda.synchronize()
         assert_close(to_f64(o), oracle.run_case(other), "bf16", f"eager between replays {rep}")
+
+
+def test_graph_replays_mixed_batch_one_call():
+    """pa_attention_mixed inside a graph: decodes and a prompt share one launch, then the merge.
+    Three passes advance every length by one; each replay is checked against the oracle."""
+    final = [1300, 40, 5000, 777, 300]
+    q_lens = [1, 1, 1, 1, 9]
+    case = W.build_case("graph_mixed", final, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                        kv_dtype="bf16", q_dtype="bf16", seed=33, q_lens=q_lens, pad_rows=1, device=DEV,
+                        poison_tail=False)
+    start = np.asarray(final) - PASSES
+    lens = torch.from_numpy(start.astype(np.int32)).to(DEV)
+    case.context_lens = lens
+    step = MixedStep(case, 1, PlanConfig(cu_count=256), one_call=True)
+    outs = [torch.empty_like(step.out) for _ in range(PASSES)]
+
+    def passes():
+        for p in range(PASSES):
+            lens.add_(1)
+            step.run(case)
+            outs[p].copy_(step.out)
+
+    passes()
+    torch.cuda.synchronize()
+    lens.copy_(torch.from_numpy(start.astype(np.int32)))
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            passes()
+    torch.cuda.synchronize()
+    refs = [_oracle_at(case, start + p + 1) for p in range(PASSES)]
+    for rep in range(3):
+        announce(f"mixed graph replay {rep}")
+        lens.copy_(torch.from_numpy(start.astype(np.int32)))
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for p in range(PASSES):
+            assert_close(to_f64(outs[p]), refs[p], "bf16", f"mixed replay {rep} pass {p}")
