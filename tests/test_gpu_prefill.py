@@ -109,3 +109,19 @@ def test_seven_decodes_at_16k_and_a_prompt_full_size(one_call):
     out = mixed_step(case, 1, PlanConfig(cu_count=256), one_call=one_call)
     torch.cuda.synchronize()
     assert_close(to_f64(out), oracle_direct(case), "bf16", "mixed full size")
+
+
+def test_one_call_with_more_decodes_than_plan_in_place():
+    """300 single-token decodes and two prompts: the decode part is beyond the in-place plan's 256
+    requests, so pa_attention_mixed plans with the plan kernel and launches the parts apart."""
+    rng = np.random.default_rng(45)
+    ctx = list(rng.integers(1, 600, size=300)) + [200, 90]
+    ql = [1] * 300 + [40, 90]
+    case = W.build_case("many_decodes", ctx, num_q_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
+                        kv_dtype="bf16", q_dtype="bf16", seed=46, q_lens=ql, pad_rows=2, device=DEV)
+    announce("mixed one call, 300 decodes + 2 prompts")
+    out = mixed_step(case, 1, PlanConfig(cu_count=256), one_call=True)
+    torch.cuda.synchronize()
+    got = to_f64(out)
+    assert_close(got, oracle_direct(case), "bf16", "many decodes")
+    assert (got[_zero_rows(case)] == 0.0).all()
