@@ -18,7 +18,9 @@
  *              (same vllm-rdna page, Change 1; ATOM #2366 review, "Claims checked and not upheld").
  *
  * pa_attention runs the same three steps with one launch fewer: the decode plans in place (for
- * batches of up to PA_INLINE_PLAN_SEQS requests) and stores the plan it used.
+ * batches of up to PA_INLINE_PLAN_SEQS requests) and stores the plan it used.  pa_prefill computes
+ * prompt rows of a mixed batch (no plan, no workspace), and pa_attention_mixed a whole decodes-first
+ * mixed batch, the decodes and the prompts sharing one launch where they fit it.
  *
  * Conventions shared by every entry point:
  *   - All array arguments are DEVICE pointers (memory of the current HIP device), except where a
