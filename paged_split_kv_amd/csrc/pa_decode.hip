@@ -277,22 +277,30 @@ __device__ __forceinline__ void merge_request_rows(const DecodeArgs& a, int b, i
         const size_t st0 = (static_cast<size_t>(first) * a.max_q_len + i) * a.num_q_heads + h;
         float m = -INFINITY, l = 0.f;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-        for (int j = 0; j < parts; ++j) {
-            const size_t st = st0 + static_cast<size_t>(j) * step;
-            const float2 ml = load_f2_coherent(a.ws_ml + st * 2);
-            const float2 v01 = load_f2_coherent(a.ws_acc + st * D + 4 * dc);
-            const float2 v23 = load_f2_coherent(a.ws_acc + st * D + 4 * dc + 2);
-            if (ml.y > 0.f) {
-                const float mn = fmaxf(m, ml.x);
+        // U partials in flight: all loads issued before any is used (indices past the last partial
+        // repeat it and are dropped); empty partials are dropped by selects, not branches
+        constexpr int U = 4;
+        for (int j0 = 0; j0 < parts; j0 += U) {
+            float2 ml[U], v01[U], v23[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const size_t st = st0 + static_cast<size_t>(min(j0 + u, parts - 1)) * step;
+                ml[u] = load_f2_coherent(a.ws_ml + st * 2);
+                v01[u] = load_f2_coherent(a.ws_acc + st * D + 4 * dc);
+                v23[u] = load_f2_coherent(a.ws_acc + st * D + 4 * dc + 2);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const bool use = j0 + u < parts && ml[u].y > 0.f;
+                const float mn = fmaxf(m, ml[u].x);
                 const float fo = __builtin_amdgcn_exp2f(m - mn);
-                const float fn = __builtin_amdgcn_exp2f(ml.x - mn);
-                l = l * fo + ml.y * fn;
-                acc.x = acc.x * fo + v01.x * fn;
-                acc.y = acc.y * fo + v01.y * fn;
-                acc.z = acc.z * fo + v23.x * fn;
-                acc.w = acc.w * fo + v23.y * fn;
-                m = mn;
+                const float fn = __builtin_amdgcn_exp2f(ml[u].x - mn);
+                l = use ? l * fo + ml[u].y * fn : l;
+                acc.x = use ? acc.x * fo + v01[u].x * fn : acc.x;
+                acc.y = use ? acc.y * fo + v01[u].y * fn : acc.y;
+                acc.z = use ? acc.z * fo + v23[u].x * fn : acc.z;
+                acc.w = use ? acc.w * fo + v23[u].y * fn : acc.w;
+                m = use ? mn : m;
             }
         }
         const float inv = l > 0.f ? 1.f / l : 0.f;

@@ -43,21 +43,31 @@ __global__ __launch_bounds__(NT) void merge_kernel(const MergeArgs a) {
         const int parts = max(min(ri.y, a.capacity - first), 0);
         const size_t step = static_cast<size_t>(a.max_q_len) * a.num_q_heads;       // states per slot
         const size_t st0 = (static_cast<size_t>(first) * a.max_q_len + i) * a.num_q_heads + h;
-#pragma unroll 8
-        for (int j = pg; j < parts; j += NPG) {
-            const size_t st = st0 + static_cast<size_t>(j) * step;
-            const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + st * 2);
-            const float4 v = *reinterpret_cast<const float4*>(a.ws_acc + st * D + 4 * dc);
-            if (ml.y > 0.f) {
-                const float mn = fmaxf(m, ml.x);
+        // U partials in flight per thread: every load is issued before any is used (indices past
+        // the last partial repeat it and are dropped), so a thread waits for memory once per batch
+        // rather than twice per partial; empty partials (l = 0) are dropped by selects, not branches
+        constexpr int U = NT >= 1024 ? 8 : 4;
+        for (int j0 = pg; j0 < parts; j0 += U * NPG) {
+            float2 ml[U];
+            float4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const size_t st = st0 + static_cast<size_t>(min(j0 + u * NPG, parts - 1)) * step;
+                ml[u] = *reinterpret_cast<const float2*>(a.ws_ml + st * 2);
+                v[u] = *reinterpret_cast<const float4*>(a.ws_acc + st * D + 4 * dc);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const bool use = j0 + u * NPG < parts && ml[u].y > 0.f;
+                const float mn = fmaxf(m, ml[u].x);
                 const float fo = __builtin_amdgcn_exp2f(m - mn);      // 0 while m = -inf
-                const float fn = __builtin_amdgcn_exp2f(ml.x - mn);
-                l = l * fo + ml.y * fn;
-                acc.x = acc.x * fo + v.x * fn;
-                acc.y = acc.y * fo + v.y * fn;
-                acc.z = acc.z * fo + v.z * fn;
-                acc.w = acc.w * fo + v.w * fn;
-                m = mn;
+                const float fn = __builtin_amdgcn_exp2f(ml[u].x - mn);
+                l = use ? l * fo + ml[u].y * fn : l;
+                acc.x = use ? acc.x * fo + v[u].x * fn : acc.x;
+                acc.y = use ? acc.y * fo + v[u].y * fn : acc.y;
+                acc.z = use ? acc.z * fo + v[u].z * fn : acc.z;
+                acc.w = use ? acc.w * fo + v[u].w * fn : acc.w;
+                m = use ? mn : m;
             }
         }
     }
