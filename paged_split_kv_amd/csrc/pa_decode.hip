@@ -601,6 +601,11 @@ __global__ __launch_bounds__((64 * NWAVES), (Mfma<D, NCB, KV8, NWAVES>::WAVES)) 
         }
     }
 
+    // bounds over the workgroup's rows: the first token sees the fewest keys, the last token's window
+    // starts latest; a step whose keys all lie in [nlo_hi, nvis_lo) needs no mask (rows past the
+    // request's own rows take unmasked scores then, but they are never written)
+    const int nvis_lo = si.S - (si.L - 1);
+    const int nlo_hi = a.window > 0 ? max(si.S - a.window, 0) : 0;
     float m_run[NCB], l_run[NCB];                 // running reference max (base 2) and lane-partial sum
     float4_t acc[NCB][NDT];                       // O^T tile: lane holds d = dcol0 + 16t + 4*grp + j, row = col
 #pragma unroll
@@ -1004,15 +1009,29 @@ __global__ __launch_bounds__((64 * NWAVES), (Mfma<D, NCB, KV8, NWAVES>::WAVES)) 
                 // lane holds keys key0[c] + 4*grp + j of each chunk for query row 16cb + col
                 float x[CG][4];
                 float mt = -INFINITY;
+                bool whole = true;                       // every key of the step visible to every row
 #pragma unroll
-                for (int c = 0; c < CG; ++c) {
-                    const int lim = min(nvc[c], nvis[cb] - key0[c]);
-                    const int low = nlo[cb] - key0[c];    // window start relative to the chunk
+                for (int c = 0; c < CG; ++c)
+                    whole = whole && nvc[c] == 16 && key0[c] + 16 <= nvis_lo && key0[c] >= nlo_hi;
+                if (whole) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int kj = 4 * grp + j;
-                        x[c][j] = (kj < lim && kj >= low) ? sacc[c][j] * a.score_scale_log2 : -INFINITY;
-                        mt = fmaxf(mt, x[c][j]);
+                    for (int c = 0; c < CG; ++c)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            x[c][j] = sacc[c][j] * a.score_scale_log2;
+                            mt = fmaxf(mt, x[c][j]);
+                        }
+                } else {
+#pragma unroll
+                    for (int c = 0; c < CG; ++c) {
+                        const int lim = min(nvc[c], nvis[cb] - key0[c]);
+                        const int low = nlo[cb] - key0[c];    // window start relative to the chunk
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int kj = 4 * grp + j;
+                            x[c][j] = (kj < lim && kj >= low) ? sacc[c][j] * a.score_scale_log2 : -INFINITY;
+                            mt = fmaxf(mt, x[c][j]);
+                        }
                     }
                 }
                 mt = max_over_row_groups(mt);
