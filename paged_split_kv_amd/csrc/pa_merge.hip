@@ -14,24 +14,28 @@ namespace pa {
 
 namespace {
 
-// One workgroup of NT threads per (row, head).  Thread t owns the 16-byte column dc = t % (D/4) of
-// the head dimension and the partials j = pg, pg + NPG, ... with pg = t / (D/4); it folds them into a
-// running (max, sum, acc) with independent loads, then the NPG states of a column are combined in LDS.
-// NT = 1024 when there are few (row, head) pairs: a request split into hundreds of partials is then
-// read by 4x the threads, in one round of loads instead of four.
-template <int D, bool OUT_BF16, int NT>
+// One workgroup of NT threads per (row, head) and column part: the head dimension is split into CS
+// parts of D / CS columns, each its own workgroup (every part reads all partials' (m, l) and its own
+// columns of acc; the parts write disjoint columns).  Thread t owns the 16-byte column dc = t % NDC of
+// its part and the partials j = pg, pg + NPG, ... with pg = t / NDC; it folds them into a running
+// (max, sum, acc) with independent loads, then the NPG states of a column are combined in LDS.
+// CS = 4 when there are fewer (row, head) pairs than compute units: a request split into hundreds of
+// partials is then read by four workgroups on four compute units.
+template <int D, bool OUT_BF16, int NT, int CS>
 __global__ __launch_bounds__(NT) void merge_kernel(const MergeArgs a) {
-    constexpr int NDC = D / 4;          // float4 columns
+    constexpr int NDC = D / 4 / CS;     // float4 columns of this part
     constexpr int NPG = NT / NDC;       // partial groups
     __shared__ float4 s_acc[NPG][NDC];
     __shared__ float s_m[NPG];
     __shared__ float s_l[NPG];
 
     const int tid = threadIdx.x;
-    const int dc = tid % NDC;
+    const int pair = blockIdx.x / CS;
+    const int part = blockIdx.x - pair * CS;
+    const int dc = tid % NDC + part * NDC;       // float4 column within the head dimension
     const int pg = tid / NDC;
-    const int r = blockIdx.x / a.num_q_heads;
-    const int h = blockIdx.x - r * a.num_q_heads;
+    const int r = pair / a.num_q_heads;
+    const int h = pair - r * a.num_q_heads;
 
     int i;
     const int b = owner_of_row(a.cu, a.num_seqs, a.max_q_len, r, i);
@@ -46,7 +50,7 @@ __global__ __launch_bounds__(NT) void merge_kernel(const MergeArgs a) {
         // U partials in flight per thread: every load is issued before any is used (indices past
         // the last partial repeat it and are dropped), so a thread waits for memory once per batch
         // rather than twice per partial; empty partials (l = 0) are dropped by selects, not branches
-        constexpr int U = NT >= 1024 ? 8 : 4;
+        constexpr int U = NPG >= 32 ? 8 : 4;
         for (int j0 = pg; j0 < parts; j0 += U * NPG) {
             float2 ml[U];
             float4 v[U];
@@ -71,8 +75,8 @@ __global__ __launch_bounds__(NT) void merge_kernel(const MergeArgs a) {
             }
         }
     }
-    s_acc[pg][dc] = acc;
-    if (dc == 0) {
+    s_acc[pg][tid % NDC] = acc;
+    if (tid % NDC == 0) {
         s_m[pg] = m;
         s_l[pg] = l;
     }
@@ -88,7 +92,7 @@ __global__ __launch_bounds__(NT) void merge_kernel(const MergeArgs a) {
         for (int k = 0; k < NPG; ++k) {
             if (!(s_l[k] > 0.f)) continue;
             const float f = __builtin_amdgcn_exp2f(s_m[k] - Mx);
-            const float4 v = s_acc[k][dc];
+            const float4 v = s_acc[k][tid % NDC];
             den += f * s_l[k];
             num.x += f * v.x;
             num.y += f * v.y;
@@ -112,14 +116,14 @@ __global__ __launch_bounds__(NT) void merge_kernel(const MergeArgs a) {
 
 template <int D>
 hipError_t launch_merge_d(const MergeArgs& a, bool out_bf16, dim3 grid, hipStream_t stream) {
-    // fewer (row, head) pairs than compute units: wide workgroups, so each pair's loads go out at once
-    const bool wide = grid.x < 256;
-    if (out_bf16) {
-        if (wide) hipLaunchKernelGGL((merge_kernel<D, true, 1024>), grid, dim3(1024), 0, stream, a);
-        else hipLaunchKernelGGL((merge_kernel<D, true, 256>), grid, dim3(256), 0, stream, a);
+    // fewer (row, head) pairs than compute units: each pair's columns split over four workgroups
+    if (grid.x < 256) {
+        const dim3 g4(grid.x * 4);
+        if (out_bf16) hipLaunchKernelGGL((merge_kernel<D, true, 256, 4>), g4, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((merge_kernel<D, false, 256, 4>), g4, dim3(256), 0, stream, a);
     } else {
-        if (wide) hipLaunchKernelGGL((merge_kernel<D, false, 1024>), grid, dim3(1024), 0, stream, a);
-        else hipLaunchKernelGGL((merge_kernel<D, false, 256>), grid, dim3(256), 0, stream, a);
+        if (out_bf16) hipLaunchKernelGGL((merge_kernel<D, true, 256, 1>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((merge_kernel<D, false, 256, 1>), grid, dim3(256), 0, stream, a);
     }
     return hipGetLastError();
 }
