@@ -93,10 +93,14 @@ pa_status pa_plan_capacity(int32_t num_seqs, int32_t num_kv_heads, int32_t cu_co
                            int32_t budget_mult, int32_t max_partitions, int32_t* capacity_out);
 
 /*
- * Bytes of workspace pa_decode and pa_merge use for a plan of `capacity` slots: fp32 partial outputs
- * [capacity, max_q_len, num_q_heads, head_dim], fp32 (max, sum) pairs [capacity, max_q_len,
- * num_q_heads, 2], and int32 arrival counters [capacity x num_q_heads] for the merge pa_decode can run
- * in the same launch; each region 256-byte aligned.
+ * Bytes of workspace pa_decode, pa_merge and pa_attention use for a plan of `capacity` slots, in
+ * this order, each region 256-byte aligned:
+ *   fp32 partial outputs [capacity, max_q_len, num_q_heads, head_dim], fp32 (max, sum) pairs
+ *   [capacity, max_q_len, num_q_heads, 2], and int32 arrival counters [capacity x num_q_heads] for
+ *   the merge pa_decode can run in the same launch;
+ *   then (capacity > 0) pa_attention's shared-slot region, used when every request is one slot (see
+ *   there): partials and pairs as above for 3 x capacity pieces, then int32 (first piece, pieces)
+ *   pairs [PA_INLINE_PLAN_SEQS].
  * Returns 0 if any argument is < 1 (capacity may be 0) or the size overflows.
  */
 size_t pa_workspace_bytes(int32_t capacity, int32_t max_q_len, int32_t num_q_heads, int32_t head_dim);
@@ -192,13 +196,23 @@ pa_status pa_merge(int32_t num_rows, int32_t num_q_heads, int32_t head_dim, int3
  * The whole step -- plan, decode, merge -- on one stream, with results identical to pa_plan followed
  * by pa_decode (out = NULL) and pa_merge with the same arguments: work_info, reduce_info and num_work
  * receive the plan bit for bit as pa_plan writes it, the workspace the same partial states, and out
- * the same rows.  Arguments are those of the three calls (cu_count, budget_mult, max_partitions as
- * for pa_plan; capacity and sliding_window as for pa_plan and pa_decode); the plan buffers are
- * outputs here.
+ * the same rows (except with shared slots, below).  Arguments are those of the three calls
+ * (cu_count, budget_mult, max_partitions as for pa_plan; capacity and sliding_window as for pa_plan
+ * and pa_decode); the plan buffers are outputs here.
  * With num_seqs <= PA_INLINE_PLAN_SEQS and a bf16 or fp8 cache, the decode launch evaluates the
  * planner's rule itself (every workgroup over all requests, one request per thread) and stores the
  * plan, so the step is two launches (decode, merge); otherwise it is the three launches.  The
  * single-launch merge of pa_decode is not used here, so the workspace needs no zero fill.
+ * Shared slots: when that in-place plan gives every request one slot (the capacity formula's value
+ * is at most num_seqs), head_dim <= 128, G x max_q_len <= 16 and workspace_bytes covers the
+ * shared-slot region (pa_workspace_bytes does), slot sizes follow the request lengths and one
+ * workgroup per slot would leave the longest request to a single workgroup.  The decode then cuts
+ * every slot of request b into X_b pieces of at most p tiles, p = ceil((sum of slot tiles + slots)
+ * / (2 x capacity formula)), X_b = ceil(ceil(tiles_b / parts_b) / p), piece k of a slot of n tiles
+ * taking its tiles [floor(k n / X_b), floor((k + 1) n / X_b)); each piece is one workgroup, its
+ * states go to the shared-slot region, and the merge folds each request's pieces.  The plan
+ * buffers are still the planner's, bit for bit; out agrees with the three calls within the
+ * attention tolerance (the same keys, folded in another grouping) instead of bit for bit.
  * Errors: the union of pa_plan's, pa_decode's and pa_merge's checks, before any launch.
  */
 pa_status pa_attention(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t num_q_heads,

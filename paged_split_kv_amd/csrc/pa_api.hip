@@ -166,6 +166,33 @@ pa_status prepare_merge(int32_t num_rows, int32_t num_q_heads, int32_t head_dim,
     return PA_OK;
 }
 
+// Shared slots: with every request one slot (the capacity formula gives the batch no more slots than
+// requests) slot sizes follow the request lengths, and the longest request alone would set the time.
+// When the decode runs its one-row-block form (head_dim <= 128, G x L <= 16) and the workspace holds
+// the piece layout, the in-place plan also cuts each slot into pieces, one workgroup each, whose
+// states the merge folds per request like slots.  The plan buffers are written as without pieces.
+void share_slots(pa::DecodeArgs& d, pa::MergeArgs& m, int head_dim, int capacity, void* workspace,
+                 size_t workspace_bytes) {
+    if (head_dim > 128 || pa::column_blocks(d.group * d.max_q_len) != 1 || d.plan_cap > d.num_seqs) return;
+    const int states = capacity > pa::piece_bound(d.plan_cap) ? capacity : pa::piece_bound(d.plan_cap);
+    const size_t base = pa::workspace_acc_bytes(capacity, d.max_q_len, d.num_q_heads, head_dim) +
+                        pa::workspace_ml_bytes(capacity, d.max_q_len, d.num_q_heads) +
+                        pa::workspace_counter_bytes(capacity, d.num_q_heads);
+    if (workspace_bytes < base + pa::workspace_piece_bytes(states, d.max_q_len, d.num_q_heads, head_dim)) return;
+    uint8_t* ws = static_cast<uint8_t*>(workspace) + base;
+    const size_t acc = pa::workspace_acc_bytes(states, d.max_q_len, d.num_q_heads, head_dim);
+    const size_t ml = pa::workspace_ml_bytes(states, d.max_q_len, d.num_q_heads);
+    d.pieces = pa::kPieceFactor;
+    d.capacity = states;
+    d.ws_acc = reinterpret_cast<float*>(ws);
+    d.ws_ml = reinterpret_cast<float*>(ws + acc);
+    d.piece_reduce_out = reinterpret_cast<int2*>(ws + acc + ml);
+    m.reduce_info = d.piece_reduce_out;
+    m.ws_acc = d.ws_acc;
+    m.ws_ml = d.ws_ml;
+    m.capacity = states;
+}
+
 }  // namespace
 
 namespace {
@@ -244,9 +271,13 @@ size_t pa_workspace_bytes(int32_t capacity, int32_t max_q_len, int32_t num_q_hea
     if (capacity < 0 || max_q_len < 1 || num_q_heads < 1 || head_dim < 1) return 0;
     const unsigned long long states = (unsigned long long)capacity * max_q_len * num_q_heads;
     if (states > (1ull << 40)) return 0;
-    return pa::workspace_acc_bytes(capacity, max_q_len, num_q_heads, head_dim) +
-           pa::workspace_ml_bytes(capacity, max_q_len, num_q_heads) +
-           pa::workspace_counter_bytes(capacity, num_q_heads);
+    const size_t slots = pa::workspace_acc_bytes(capacity, max_q_len, num_q_heads, head_dim) +
+                         pa::workspace_ml_bytes(capacity, max_q_len, num_q_heads) +
+                         pa::workspace_counter_bytes(capacity, num_q_heads);
+    if (capacity == 0) return slots;
+    // then pa_attention's shared-slot region (up to three times as many piece states), apart from the
+    // counters so that the fused merge's zero counters survive it
+    return slots + pa::workspace_piece_bytes(pa::piece_bound(capacity), max_q_len, num_q_heads, head_dim);
 }
 
 pa_status pa_plan(const int32_t* context_lens, const int32_t* cu_query_lens, int32_t num_seqs,
@@ -338,9 +369,11 @@ pa_status pa_attention(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_
         d.plan_inline = 1;
         d.plan_cap = cap;
         d.max_partitions = max_partitions;
+        d.plan_slots = capacity;
         d.plan_work_out = reinterpret_cast<int4*>(work_info);
         d.plan_reduce_out = reinterpret_cast<int2*>(reduce_info);
         d.plan_num_work_out = num_work;
+        share_slots(d, m, head_dim, capacity, workspace, workspace_bytes);
     } else {
         st = from_hip(pa::launch_plan(context_lens, cu_query_lens, num_seqs, cap, capacity, max_partitions,
                                       tile_tokens, sliding_window, work_info, reduce_info, num_work, s));
@@ -445,6 +478,7 @@ pa_status pa_attention_mixed(const void* q, pa_dtype q_dtype, int32_t num_rows, 
         d.plan_inline = 1;
         d.plan_cap = cap;
         d.max_partitions = max_partitions;
+        d.plan_slots = capacity;
         d.plan_work_out = reinterpret_cast<int4*>(work_info);
         d.plan_reduce_out = reinterpret_cast<int2*>(reduce_info);
         d.plan_num_work_out = num_work;

@@ -13,6 +13,10 @@
 //    chunks, the unit being the plan's largest slot split NW ways (each slot split evenly in the
 //    8-wave form), so every streaming wave carries one unit and a small slot runs fewer waves,
 //    leaving bandwidth to the large ones; the NW states merge in LDS at the end.
+//  * when every request is one slot, pa_attention's in-place plan can also cut the slots into pieces
+//    of about half the mean slot, one workgroup each (shared slots, see piece_size): the states are
+//    then per piece, the merge folds a request's pieces, and the unit is the piece-size bound split
+//    four ways.
 //  * all query rows of the group -- G heads x L verify tokens, M = G*L <= 64 -- form the columns
 //    of 16-wide MFMA blocks, so each K/V byte is read from HBM once per (slot, kv head) whatever L is.
 //  * each chunk's K and V (16 x D each) are fetched PF chunks ahead into registers with 16-byte
@@ -95,6 +99,32 @@ __device__ __forceinline__ bool slot_info(const DecodeArgs& a, int slot, SlotInf
 // workgroup keeps its own slot's entry; kv head 0's workgroups store the entries, workgroup 0 the
 // per-request ranges and the slot counts, so the buffers end up as the plan kernel writes them.
 // ---------------------------------------------------------------------------------------------
+// Shared slots.  When the capacity leaves every request one slot, slot sizes follow the request
+// lengths and one workgroup per slot leaves the longest request to a single workgroup.  Pieces of at
+// most `per` tiles, per = ceil((sum of the slots' tiles + slots) / (factor x cap)), cut every slot of
+// a request into the same number of pieces, ceil(largest slot / per), so the pieces of all slots
+// together number at most factor x cap + cap.  Piece k of X of a slot of n tiles covers its tiles
+// [floor(k n / X), floor((k + 1) n / X)), the plan's own split rule one level down.
+__device__ __forceinline__ long long piece_size(long long tiles_total, int slots, int factor, int cap) {
+    const long long den = static_cast<long long>(factor) * max(cap, 1);
+    return max(1LL, (tiles_total + slots + den - 1) / den);
+}
+
+__device__ __forceinline__ int pieces_per_slot(int tiles, int parts, long long per) {
+    if (parts <= 0) return 0;
+    const long long largest = (tiles + parts - 1) / parts;
+    return static_cast<int>((largest + per - 1) / per);
+}
+
+// Tiles, relative to the request's first tile, of its piece `off` (slot off / X, piece off % X).
+__device__ __forceinline__ int2 piece_tile_range(int off, int X, int tiles, int parts) {
+    const int j = off / X;
+    const int k = off - j * X;
+    const int2 t = plan_tile_range(j, tiles, parts);
+    const int2 u = plan_tile_range(k, t.y - t.x, X);
+    return make_int2(t.x + u.x, t.x + u.y);
+}
+
 // Up to 64 requests: every wave evaluates the whole plan on its own, with no barrier.
 __device__ __forceinline__ void plan_in_wave(const DecodeArgs& a, int slot, int g, int4& wk, int2& nwk) {
     const int lane = threadIdx.x & 63;
@@ -125,10 +155,29 @@ __device__ __forceinline__ void plan_in_wave(const DecodeArgs& a, int slot, int 
     if (threadIdx.x < 64) {
         if (blockIdx.x == 0 && real) a.plan_reduce_out[lane] = make_int2(first, parts);
         if (lane == 0) {
-            if (g == 0) a.plan_work_out[slot] = wk;
+            if (g == 0 && slot < a.plan_slots) a.plan_work_out[slot] = wk;
             if (blockIdx.x == 0) *reinterpret_cast<int2*>(a.plan_num_work_out) = nwk;
         }
     }
+    if (!a.pieces) return;
+    // shared slots: this workgroup streams piece `slot` instead (see piece_size)
+    const long long per = piece_size(wave_sum_nonneg(tiles), used, a.pieces, a.plan_cap);
+    const int X = pieces_per_slot(tiles, parts, per);
+    const int np = parts * X;
+    const int pincl = wave_incl_scan(np, lane);
+    const int pfirst = pincl - np;
+    const int pused = __builtin_amdgcn_readlane(pincl, 63);
+    if (threadIdx.x < 64 && blockIdx.x == 0 && real) a.piece_reduce_out[lane] = make_int2(pfirst, np);
+    const int po = __popcll(__builtin_amdgcn_ballot_w64(real && pfirst <= slot)) - 1;
+    wk = make_int4(-1, 0, 0, 0);
+    if (slot < pused) {
+        const int o = max(po, 0);
+        const int2 t = piece_tile_range(slot - __builtin_amdgcn_readlane(pfirst, o), __builtin_amdgcn_readlane(X, o),
+                                        __builtin_amdgcn_readlane(tiles, o), __builtin_amdgcn_readlane(parts, o));
+        const int t0 = __builtin_amdgcn_readlane(pr.t0, o);
+        wk = make_int4(o, t0 + t.x, t0 + t.y, __builtin_amdgcn_readlane(S, o));
+    }
+    nwk = make_int2(pused, static_cast<int>(min(per, static_cast<long long>(INT_MAX))));   // pieces <= per tiles
 }
 
 template <int NW>
@@ -138,9 +187,9 @@ __device__ void plan_in_place(const DecodeArgs& a, int slot, int g, int4& wk, in
         plan_in_wave(a, slot, g, wk, nwk);
         return;
     }
-    __shared__ long long s_total[NW];
-    __shared__ int s_nonempty[NW], s_slots[NW], s_below[NW], s_largest[NW];
-    __shared__ int4 s_entry;
+    __shared__ long long s_total[NW], s_tiles[NW];
+    __shared__ int s_nonempty[NW], s_slots[NW], s_below[NW], s_largest[NW], s_pieces[NW], s_pbelow[NW];
+    __shared__ int4 s_entry, s_pentry;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -154,17 +203,20 @@ __device__ void plan_in_place(const DecodeArgs& a, int slot, int g, int4& wk, in
     // W = sum of the lengths read and B' = #{requests reading any key}
     const long long wsum = wave_sum_nonneg(len);
     const int wne = __popcll(__builtin_amdgcn_ballot_w64(len > 0));
+    const long long wtiles = a.pieces ? wave_sum_nonneg(tiles) : 0;
     if (lane == 0) {
         s_total[wave] = wsum;
         s_nonempty[wave] = wne;
+        s_tiles[wave] = wtiles;
     }
     __syncthreads();
-    long long total = 0;
+    long long total = 0, tiles_total = 0;
     int nonempty = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
         total += s_total[w];
         nonempty += s_nonempty[w];
+        tiles_total += s_tiles[w];
     }
 
     // this request's partitions, their exclusive scan, and the largest partition in tiles
@@ -184,25 +236,58 @@ __device__ void plan_in_place(const DecodeArgs& a, int slot, int g, int4& wk, in
     }
     const int first = before + incl - parts;
 
+    // shared slots: this request's pieces and their scan within the wave
+    int X = 0, np = 0, pincl = 0;
+    const long long per = a.pieces ? piece_size(tiles_total, used, a.pieces, a.plan_cap) : 1;
+    if (a.pieces) {
+        X = pieces_per_slot(tiles, parts, per);
+        np = parts * X;
+        pincl = wave_incl_scan(np, lane);
+    }
+
     // the requests whose first slot is <= slot are a prefix; its last one owns the slot
     const int below = __popcll(__builtin_amdgcn_ballot_w64(real && first <= slot));
     if (lane == 0) s_below[wave] = below;
+    if (lane == 63) s_pieces[wave] = pincl;
     if (blockIdx.x == 0 && real) a.plan_reduce_out[r] = make_int2(first, parts);
     __syncthreads();
-    int owner = -1;
+    int owner = -1, pbefore = 0, pused = 0;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) owner += s_below[w];
+    for (int w = 0; w < NW; ++w) {
+        owner += s_below[w];
+        pbefore += w < wave ? s_pieces[w] : 0;
+        pused += s_pieces[w];
+    }
     if (slot < used && r == owner) {
         const int2 t = plan_tile_range(slot - first, tiles, parts);
         s_entry = make_int4(r, pr.t0 + t.x, pr.t0 + t.y, S);
+    }
+    const int pfirst = pbefore + pincl - np;
+    if (a.pieces) {
+        const int pbelow = __popcll(__builtin_amdgcn_ballot_w64(real && pfirst <= slot));
+        if (lane == 0) s_pbelow[wave] = pbelow;
+        if (blockIdx.x == 0 && real) a.piece_reduce_out[r] = make_int2(pfirst, np);
     }
     __syncthreads();
     wk = slot < used ? s_entry : make_int4(-1, 0, 0, 0);
     nwk = make_int2(used, largest);
     if (tid == 0) {
-        if (g == 0) a.plan_work_out[slot] = wk;
+        if (g == 0 && slot < a.plan_slots) a.plan_work_out[slot] = wk;
         if (blockIdx.x == 0) *reinterpret_cast<int2*>(a.plan_num_work_out) = nwk;
     }
+    if (!a.pieces) return;
+    // shared slots: this workgroup streams piece `slot` of the last request whose first piece is
+    // <= slot
+    int powner = -1;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) powner += s_pbelow[w];
+    if (slot < pused && r == powner) {
+        const int2 t = piece_tile_range(slot - pfirst, X, tiles, parts);
+        s_pentry = make_int4(r, pr.t0 + t.x, pr.t0 + t.y, S);
+    }
+    __syncthreads();
+    wk = slot < pused ? s_pentry : make_int4(-1, 0, 0, 0);
+    nwk = make_int2(pused, static_cast<int>(min(per, static_cast<long long>(INT_MAX))));   // pieces <= per tiles
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1369,10 +1454,12 @@ hipError_t launch_mixed_ncb(const DecodeArgs& dec, const DecodeArgs& pre, int nc
 template <int D, bool KV8>
 hipError_t launch_mfma_ncb(const DecodeArgs& a, int ncb, bool qf32, dim3 grid, hipStream_t stream) {
     // every request one slot (the capacity is the batch): slot sizes follow the request lengths
-    // and the longest requests set the time, so eight waves share each slot evenly
+    // and the longest requests set the time, so eight waves share each slot evenly -- unless the
+    // slots are shared (cut into pieces of about half the mean slot, see piece_size), which the
+    // four-wave form streams faster (measured: fp8 workload step 171 against 175 us)
     const bool one_slot_each = !a.prefill && (a.plan_inline ? a.plan_cap : a.capacity) <= a.num_seqs;
     if constexpr (D <= 128) {
-        if (ncb == 1 && one_slot_each) return launch_mfma_q<D, 1, KV8, 8>(a, qf32, grid, stream);
+        if (ncb == 1 && one_slot_each && !a.pieces) return launch_mfma_q<D, 1, KV8, 8>(a, qf32, grid, stream);
     }
     if (ncb == 1) return launch_mfma_q<D, 1, KV8>(a, qf32, grid, stream);
     if (ncb == 2) return launch_mfma_q<D, 2, KV8>(a, qf32, grid, stream);

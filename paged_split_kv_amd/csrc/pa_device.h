@@ -297,6 +297,14 @@ struct DecodeArgs {
     int4* plan_work_out;
     int2* plan_reduce_out;
     int32_t* plan_num_work_out;
+    // shared slots (planning in place only): pieces > 0 cuts every slot into pieces of at most
+    // ceil((tiles of all slots + slots) / (pieces * plan_cap)) tiles, one workgroup each; workgroup p
+    // streams piece p and writes its state as state p (capacity is then the piece count's bound), and
+    // (first piece, pieces) per request go to piece_reduce_out for the merge.  plan_slots is the
+    // length of plan_work_out.
+    int pieces;
+    int plan_slots;
+    int2* piece_reduce_out;
     int out_bf16;
     int num_rows, num_q_heads, num_kv_heads, group;   // group = Hq / Hkv
     int num_blocks, block_size, max_blocks, num_seqs;
@@ -324,6 +332,17 @@ struct MergeArgs {
 
 // Requests a decode workgroup can plan for in place: one per thread of its 4 waves.
 constexpr int kInlinePlanSeqs = PA_INLINE_PLAN_SEQS;
+
+// Shared slots: pieces per slot are sized so that all slots together make at most kPieceFactor x
+// plan_cap + plan_cap pieces.
+constexpr int kPieceFactor = 2;
+inline int piece_bound(int plan_cap) { return (kPieceFactor + 1) * plan_cap; }
+// Workspace bytes of the shared-slot layout for `states` piece states: acc, (m, l), then the
+// per-request (first piece, pieces) pairs.
+inline size_t workspace_piece_bytes(int states, int max_q_len, int hq, int d) {
+    return workspace_acc_bytes(states, max_q_len, hq, d) + workspace_ml_bytes(states, max_q_len, hq) +
+           align256(static_cast<size_t>(kInlinePlanSeqs) * 2 * sizeof(int32_t));
+}
 
 hipError_t launch_plan(const int32_t* context_lens, const int32_t* cu, int num_seqs,
                        int cap_formula, int capacity, int max_partitions, int tile_tokens, int window,

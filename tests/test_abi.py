@@ -48,11 +48,14 @@ def test_capacity_matches_oracle(seed):
 
 
 def test_workspace_bytes():
-    # fp32 partials [C, Lmax, Hq, D], (m, l) pairs [C, Lmax, Hq, 2] and int32 counters [C * Hq],
-    # each rounded up to 256 bytes
+    # fp32 partials [C, Lmax, Hq, D], (m, l) pairs [C, Lmax, Hq, 2] and int32 counters [C * Hq], then
+    # (C > 0) the shared-slot region: partials and (m, l) pairs of 3 C pieces and 256 int32 pairs;
+    # each region rounded up to 256 bytes
     def expect(c, l, h, d):
         up = lambda x: (x + 255) // 256 * 256
-        return up(c * l * h * d * 4) + up(c * l * h * 2 * 4) + up(c * h * 4)
+        slots = up(c * l * h * d * 4) + up(c * l * h * 2 * 4) + up(c * h * 4)
+        pieces = up(3 * c * l * h * d * 4) + up(3 * c * l * h * 2 * 4) + up(256 * 2 * 4)
+        return slots + pieces if c > 0 else slots
     for args in [(512, 1, 4, 64), (256, 1, 16, 128), (512, 3, 6, 256), (1, 1, 1, 64), (0, 1, 1, 64)]:
         assert B.pa_workspace_bytes(*args) == expect(*args)
     assert B.pa_workspace_bytes(10, 0, 1, 64) == 0

@@ -42,15 +42,32 @@ def _check_plan(step, ctx, hkv, cfg):
     assert np.array_equal(step.work_info.cpu().numpy(), ow)
 
 
+def _poison_pieces(step):
+    """NaN pattern in the shared-slot region too (it follows the slot partials and the counters)."""
+    up = lambda x: (x + 255) // 256 * 256
+    start = _partial_bytes(step) + up(step.capacity * step.out.shape[1] * 4)
+    step.workspace[start:].fill_(0xFF)
+
+
 def _both_routes(case, cfg):
     three = DecodeStep.for_case(case, cfg)
     _poison(three)
     ref = three.run_case(case, fused=False).clone()
     whole = DecodeStep.for_case(case, cfg)
     _poison(whole)
+    _poison_pieces(whole)
     got = whole.run_case(case, whole=True)
     torch.cuda.synchronize()
     return got, ref, whole
+
+
+def _assert_same_as_three(got, ref, step, kv, what=""):
+    """Bit for bit, except where pa_attention shares slots between workgroups: the pieces' states
+    are folded in another order, so the two routes agree within the attention tolerance."""
+    if step.shares_slots(kv, got.shape[1], got.shape[2]):
+        assert_close(to_f64(got), to_f64(ref), "fp8" if kv == "fp8" else "bf16", what)
+    else:
+        assert torch.equal(got, ref), f"{what}: pa_attention differs from pa_plan + pa_decode + pa_merge"
 
 
 @pytest.mark.parametrize("spec", SMALL, ids=[s[0] for s in SMALL])
@@ -59,7 +76,7 @@ def test_small_cases(spec):
     announce(f"attention {spec[0]}")
     cfg = PlanConfig(cu_count=256, max_partitions=P, tile_tokens=T)
     got, ref, step = _both_routes(case, cfg)
-    assert torch.equal(got, ref), "pa_attention differs from pa_plan + pa_decode + pa_merge"
+    _assert_same_as_three(got, ref, step, case.kv_dtype, spec[0])
     _check_plan(step, case.context_lens.cpu().numpy(), case.num_kv_heads, cfg)
     g = to_f64(got)
     assert_close(g, oracle_direct(case), tolerance_kind(case), spec[0])
@@ -72,7 +89,7 @@ def test_full_size_workloads(name):
     case = W.make_config(name, device=DEV)
     cfg = PlanConfig(cu_count=256)
     got, ref, step = _both_routes(case, cfg)
-    assert torch.equal(got, ref)
+    _assert_same_as_three(got, ref, step, case.kv_dtype, name)
     _check_plan(step, case.context_lens.cpu().numpy(), case.num_kv_heads, cfg)
     assert_close(to_f64(got), oracle_direct(case), tolerance_kind(case), name)
 
@@ -84,9 +101,53 @@ def test_skewed_max_step():
     case = W.make_config("skewed_bf16", device=DEV, step=idx)
     cfg = PlanConfig(cu_count=256)
     got, ref, step = _both_routes(case, cfg)
-    assert torch.equal(got, ref)
+    _assert_same_as_three(got, ref, step, case.kv_dtype, "skewed max")
     _check_plan(step, steps[idx], 2, cfg)
     assert_close(to_f64(got), oracle_direct(case), "bf16", "skewed max")
+
+
+SHARED = [
+    # (name, context lens, query lens, Hq, Hkv, D, page, kv, cu_count, tile): each batch has at least
+    # 2 x cu_count / Hkv requests, so the capacity is the batch and pa_attention shares slots
+    # up to 64 requests (the plan in one wave); empty requests leave spare slots, so the long
+    # requests get several slots, each cut into the same number of pieces (some of them empty)
+    ("wave_plan_bf16", [0] * 6 + [16, 600, 33, 5000, 1, 9000, 250, 20000] * 4 + [77, 3, 1500, 40, 0, 0],
+     None, 8, 1, 128, 16, "bf16", 8, 256),
+    # more than 64 requests (the plan across waves), fp8, log-normal lengths
+    ("threads_plan_fp8", "lognormal200", None, 16, 2, 128, 16, "fp8", 100, 256),
+    # verify rows (G x L = 8 rows), head_dim 64, 16-token tiles
+    ("verify_d64_tiles16", "lognormal70", "q2", 4, 1, 64, 16, "bf16", 16, 16),
+]
+
+
+def _shared_case(spec, seed):
+    name, ctx, ql, hq, hkv, d, bs, kv, cu_count, T = spec
+    rng = np.random.default_rng(seed)
+    if isinstance(ctx, str):
+        n = int(ctx[len("lognormal"):])
+        ctx = np.clip(np.rint(np.exp(rng.normal(6.5, 1.4, size=n))), 1, 30000).astype(int)
+        ctx[rng.random(n) < 0.1] = 0
+        ctx = ctx.tolist()
+    q_lens = None if ql is None else rng.integers(1, int(ql[1:]) + 1, size=len(ctx)).tolist()
+    case = W.build_case(name, ctx, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs,
+                        kv_dtype=kv, q_dtype="bf16", seed=seed, q_lens=q_lens, pad_rows=1, device=DEV)
+    return case, PlanConfig(cu_count=cu_count, tile_tokens=T)
+
+
+@pytest.mark.parametrize("spec", SHARED, ids=[s[0] for s in SHARED])
+def test_shared_slots_match_oracle(spec):
+    """Every request one slot: pa_attention cuts the slots into pieces streamed by workgroups of
+    their own and merges the pieces per request.  Output against the oracle, the stored plan
+    against the oracle's plan, exact zeros where rows have no keys."""
+    case, cfg = _shared_case(spec, seed=31)
+    announce(f"shared slots {spec[0]}")
+    got, ref, step = _both_routes(case, cfg)
+    assert step.shares_slots(case.kv_dtype, case.num_q_heads, case.head_dim)
+    _check_plan(step, case.context_lens.cpu().numpy(), case.num_kv_heads, cfg)
+    g = to_f64(got)
+    assert_close(g, oracle_direct(case), tolerance_kind(case), spec[0])
+    assert (g[_zero_rows(case)] == 0.0).all()
+    _assert_same_as_three(got, ref, step, case.kv_dtype, spec[0])
 
 
 def _one_page_case(ctx, hkv, seed):
@@ -132,7 +193,7 @@ def test_plan_in_place_fuzz(seed):
     whole.attention(q, k, v, "bf16", bt, lens, scale=0.125)
     torch.cuda.synchronize()
     _check_plan(whole, ctx, hkv, cfg)
-    assert torch.equal(whole.out, three.out)
+    _assert_same_as_three(whole.out, three.out, whole, "bf16", f"fuzz seed {seed}")
 
 
 def test_all_empty_and_empty_batch():
