@@ -117,6 +117,10 @@ SHARED = [
     ("threads_plan_fp8", "lognormal200", None, 16, 2, 128, 16, "fp8", 100, 256),
     # verify rows (G x L = 8 rows), head_dim 64, 16-token tiles
     ("verify_d64_tiles16", "lognormal70", "q2", 4, 1, 64, 16, "bf16", 16, 16),
+    # one request, one slot (capacity 1): its pieces are the only parallelism
+    ("single_request", [100000], None, 4, 2, 128, 64, "bf16", 1, 256),
+    # mostly empty requests: the spare slots go to five long ones, ~9 slots each, then pieces
+    ("mostly_empty", [0] * 45 + [30000, 7000, 65000, 12000, 300], None, 8, 1, 128, 16, "fp8", 8, 256),
 ]
 
 

@@ -29,9 +29,12 @@ def _oracle_at(case, lens):
                                    case.scale, case.k_scale, case.v_scale)
 
 
-@pytest.mark.parametrize("mode", ["separate_merge", "fused_merge", "attention"])
+@pytest.mark.parametrize("mode", ["separate_merge", "fused_merge", "attention", "attention_shared_slots"])
 def test_graph_replays_draft_passes(mode):
+    """attention_shared_slots: a budget of 2 compute units leaves every request one slot, so
+    pa_attention cuts the slots into pieces; the piece table is rewritten on every replay."""
     fused = mode == "fused_merge"
+    cu_count = 2 if mode == "attention_shared_slots" else 256
     final = [1300, 40, 2, 5000, 777, 256]
     q_lens = [2, 1, 2, 3, 1, 2]
     # pages exist for the final lengths; the graph starts PASSES tokens earlier
@@ -41,13 +44,14 @@ def test_graph_replays_draft_passes(mode):
     start = np.asarray(final) - PASSES
     lens = torch.from_numpy(start.astype(np.int32)).to(DEV)
     case.context_lens = lens
-    step = DecodeStep.for_case(case, PlanConfig(cu_count=256))
+    step = DecodeStep.for_case(case, PlanConfig(cu_count=cu_count))
+    assert step.shares_slots(case.kv_dtype, case.num_q_heads, case.head_dim) == (mode == "attention_shared_slots")
     outs = [torch.empty_like(step.out) for _ in range(PASSES)]
 
     def passes():
         for p in range(PASSES):
             lens.add_(1)                                   # the draft step advances every length
-            if mode == "attention":                        # plans in place inside the decode launch
+            if mode.startswith("attention"):               # plans in place inside the decode launch
                 step.attention(case.q, case.k_cache, case.v_cache, case.kv_dtype, case.block_tables, lens,
                                scale=case.scale, cu_query_lens=case.cu_query_lens)
             else:
@@ -85,7 +89,7 @@ def test_graph_replays_draft_passes(mode):
         for p in range(PASSES):
             assert_close(to_f64(outs[p]), refs[p], "bf16", f"replay {rep} pass {p}")
         assert int(lens.cpu().numpy().sum()) == int(np.sum(final))
-        ow, orr, on, olarge = oracle.plan(final, 2, 256, with_largest=True)
+        ow, orr, on, olarge = oracle.plan(final, 2, cu_count, with_largest=True)
         assert step.num_work.cpu().numpy().tolist() == [on, olarge]
         assert np.array_equal(step.work_info.cpu().numpy(), ow)
         assert np.array_equal(step.reduce_info.cpu().numpy(), orr)
