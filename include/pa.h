@@ -98,9 +98,10 @@ pa_status pa_plan_capacity(int32_t num_seqs, int32_t num_kv_heads, int32_t cu_co
  *   fp32 partial outputs [capacity, max_q_len, num_q_heads, head_dim], fp32 (max, sum) pairs
  *   [capacity, max_q_len, num_q_heads, 2], and int32 arrival counters [capacity x num_q_heads] for
  *   the merge pa_decode can run in the same launch;
- *   then (capacity > 0) pa_attention's shared-slot region, used when every request is one slot (see
- *   there): partials and pairs as above for 3 x capacity pieces, then int32 (first piece, pieces)
- *   pairs [PA_INLINE_PLAN_SEQS].
+ *   then (capacity > 0) the shared-slot region, used when every request is one slot (see
+ *   pa_decode): partials and pairs as above for 3 x capacity pieces, then int32 (first piece,
+ *   pieces) pairs [PA_INLINE_PLAN_SEQS].  A workspace without this region (workspace_bytes short of
+ *   it) works, without shared slots.
  * Returns 0 if any argument is < 1 (capacity may be 0) or the size overflows.
  */
 size_t pa_workspace_bytes(int32_t capacity, int32_t max_q_len, int32_t num_q_heads, int32_t head_dim);
@@ -167,6 +168,15 @@ pa_status pa_plan(const int32_t* context_lens, const int32_t* cu_query_lens, int
  * KV types bf16 and fp8 run on the matrix cores in bf16 (fp8 codes widen exactly to bf16; q is
  * rounded to bf16; probabilities are rounded to bf16 for the P.V product; accumulation is fp32).
  * KV type f32 runs in fp32 on the vector ALUs (with out, the merge is a second launch).
+ * Shared slots: when 0 < capacity <= num_seqs <= PA_INLINE_PLAN_SEQS (every request at most one
+ * slot once the plan fills the capacity), head_dim <= 128, out is NULL and workspace_bytes covers
+ * the shared-slot region (pa_workspace_bytes does), slot sizes follow the request lengths and one
+ * workgroup per slot would leave the longest request to one workgroup.  The decode then cuts every
+ * used slot of n tiles into X = max(1, ceil(n / p)) pieces, p = ceil((sum of the used slots' tiles +
+ * used slots) / (2 x used slots)), piece k taking the slot's tiles [floor(k n / X),
+ * floor((k + 1) n / X)); each piece is one workgroup, pieces are numbered slot by slot, and their
+ * states go to the shared-slot region with each request's (first piece, pieces).  pa_merge decides
+ * the same way from its own arguments (capacity, num_seqs, head_dim, workspace_bytes).
  */
 pa_status pa_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t num_q_heads,
                     int32_t head_dim, const void* k_cache, const void* v_cache, pa_dtype kv_dtype,
@@ -186,6 +196,10 @@ pa_status pa_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t n
  * partitions, and rows whose partials are all empty are written as +0.0.  Every element of out
  * ([num_rows, num_q_heads, head_dim]) is written.
  * out_dtype must equal the q dtype given to pa_decode (PA_F32 or PA_BF16).
+ * Under pa_decode's shared-slot condition (0 < capacity <= num_seqs <= PA_INLINE_PLAN_SEQS,
+ * head_dim <= 128, workspace_bytes covering the region) a request's partials are its pieces (in slot
+ * order) rather than its slots; same formula.  The workspace must hold what pa_decode (out = NULL)
+ * wrote with the same capacity, max_q_len, num_q_heads, head_dim and workspace_bytes.
  */
 pa_status pa_merge(int32_t num_rows, int32_t num_q_heads, int32_t head_dim, int32_t num_seqs,
                    const int32_t* cu_query_lens, int32_t max_q_len, const int32_t* reduce_info,
@@ -196,23 +210,15 @@ pa_status pa_merge(int32_t num_rows, int32_t num_q_heads, int32_t head_dim, int3
  * The whole step -- plan, decode, merge -- on one stream, with results identical to pa_plan followed
  * by pa_decode (out = NULL) and pa_merge with the same arguments: work_info, reduce_info and num_work
  * receive the plan bit for bit as pa_plan writes it, the workspace the same partial states, and out
- * the same rows (except with shared slots, below).  Arguments are those of the three calls
+ * the same rows, when capacity is pa_plan_capacity's value.  Arguments are those of the three calls
  * (cu_count, budget_mult, max_partitions as for pa_plan; capacity and sliding_window as for pa_plan
  * and pa_decode); the plan buffers are outputs here.
  * With num_seqs <= PA_INLINE_PLAN_SEQS and a bf16 or fp8 cache, the decode launch evaluates the
  * planner's rule itself (every workgroup over all requests, one request per thread) and stores the
  * plan, so the step is two launches (decode, merge); otherwise it is the three launches.  The
  * single-launch merge of pa_decode is not used here, so the workspace needs no zero fill.
- * Shared slots: when that in-place plan gives every request one slot (the capacity formula's value
- * is at most num_seqs), head_dim <= 128, G x max_q_len <= 16 and workspace_bytes covers the
- * shared-slot region (pa_workspace_bytes does), slot sizes follow the request lengths and one
- * workgroup per slot would leave the longest request to a single workgroup.  The decode then cuts
- * every slot of request b into X_b pieces of at most p tiles, p = ceil((sum of slot tiles + slots)
- * / (2 x capacity formula)), X_b = ceil(ceil(tiles_b / parts_b) / p), piece k of a slot of n tiles
- * taking its tiles [floor(k n / X_b), floor((k + 1) n / X_b)); each piece is one workgroup, its
- * states go to the shared-slot region, and the merge folds each request's pieces.  The plan
- * buffers are still the planner's, bit for bit; out agrees with the three calls within the
- * attention tolerance (the same keys, folded in another grouping) instead of bit for bit.
+ * Shared slots as in pa_decode, with the capacity formula's value in place of capacity when the
+ * plan is made in place (the two agree when capacity is pa_plan_capacity's value).
  * Errors: the union of pa_plan's, pa_decode's and pa_merge's checks, before any launch.
  */
 pa_status pa_attention(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t num_q_heads,

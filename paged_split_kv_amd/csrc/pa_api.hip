@@ -111,6 +111,7 @@ pa_status prepare_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int3
     a.ws_ml = workspace ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + acc_bytes) : nullptr;
     a.ws_counters = workspace ? reinterpret_cast<int*>(static_cast<uint8_t*>(workspace) + acc_bytes + ml_bytes)
                               : nullptr;
+
     a.reduce_info = reinterpret_cast<const int2*>(reduce_info);
     a.out = out;
     a.out_bf16 = out_dtype == PA_BF16 ? 1 : 0;
@@ -166,31 +167,36 @@ pa_status prepare_merge(int32_t num_rows, int32_t num_q_heads, int32_t head_dim,
     return PA_OK;
 }
 
-// Shared slots: with every request one slot (the capacity formula gives the batch no more slots than
-// requests) slot sizes follow the request lengths, and the longest request alone would set the time.
-// When the decode runs its one-row-block form (head_dim <= 128, G x L <= 16) and the workspace holds
-// the piece layout, the in-place plan also cuts each slot into pieces, one workgroup each, whose
-// states the merge folds per request like slots.  The plan buffers are written as without pieces.
-void share_slots(pa::DecodeArgs& d, pa::MergeArgs& m, int head_dim, int capacity, void* workspace,
-                 size_t workspace_bytes) {
-    if (head_dim > 128 || pa::column_blocks(d.group * d.max_q_len) != 1 || d.plan_cap > d.num_seqs) return;
-    const int states = capacity > pa::piece_bound(d.plan_cap) ? capacity : pa::piece_bound(d.plan_cap);
-    const size_t base = pa::workspace_acc_bytes(capacity, d.max_q_len, d.num_q_heads, head_dim) +
-                        pa::workspace_ml_bytes(capacity, d.max_q_len, d.num_q_heads) +
-                        pa::workspace_counter_bytes(capacity, d.num_q_heads);
-    if (workspace_bytes < base + pa::workspace_piece_bytes(states, d.max_q_len, d.num_q_heads, head_dim)) return;
-    uint8_t* ws = static_cast<uint8_t*>(workspace) + base;
-    const size_t acc = pa::workspace_acc_bytes(states, d.max_q_len, d.num_q_heads, head_dim);
-    const size_t ml = pa::workspace_ml_bytes(states, d.max_q_len, d.num_q_heads);
+// Shared slots: with every request one slot (capacity <= batch) slot sizes follow the request
+// lengths, and the longest request alone would set the time.  When the decode writes partial states
+// (no merge in its launch), head_dim <= 128, the batch is at most PA_INLINE_PLAN_SEQS requests and the
+// workspace holds the shared-slot region, the decode cuts each slot into pieces, one workgroup each,
+// and the merge folds a request's pieces like slots.  `one_slot_cap` is the capacity that decides
+// "one slot each": the plan's capacity for pa_decode, the capacity formula's value for pa_attention's
+// in-place plan.  pa_merge decides with its own arguments (pa::shares_slots), which are the same.
+bool share_slots(pa::DecodeArgs& d, int head_dim, int one_slot_cap, void* workspace, size_t workspace_bytes) {
+    if (d.out || d.prefill ||
+        !pa::shares_slots(one_slot_cap, d.num_seqs, head_dim, d.capacity, d.max_q_len, d.num_q_heads, workspace_bytes))
+        return false;
+    const pa::SharedRegion r = pa::shared_region(d.capacity, d.max_q_len, d.num_q_heads, head_dim);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
     d.pieces = pa::kPieceFactor;
-    d.capacity = states;
-    d.ws_acc = reinterpret_cast<float*>(ws);
-    d.ws_ml = reinterpret_cast<float*>(ws + acc);
-    d.piece_reduce_out = reinterpret_cast<int2*>(ws + acc + ml);
-    m.reduce_info = d.piece_reduce_out;
-    m.ws_acc = d.ws_acc;
-    m.ws_ml = d.ws_ml;
-    m.capacity = states;
+    d.plan_slots = d.capacity;
+    d.capacity = pa::piece_bound(d.capacity);
+    d.ws_acc = reinterpret_cast<float*>(ws + r.acc);
+    d.ws_ml = reinterpret_cast<float*>(ws + r.ml);
+    d.piece_reduce_out = reinterpret_cast<int2*>(ws + r.reduce);
+    return true;
+}
+
+// The merge of shared slots: each request's pieces, from the shared-slot region.
+void merge_pieces(pa::MergeArgs& m, int head_dim, const void* workspace) {
+    const pa::SharedRegion r = pa::shared_region(m.capacity, m.max_q_len, m.num_q_heads, head_dim);
+    const uint8_t* ws = static_cast<const uint8_t*>(workspace);
+    m.reduce_info = reinterpret_cast<const int2*>(ws + r.reduce);
+    m.ws_acc = reinterpret_cast<const float*>(ws + r.acc);
+    m.ws_ml = reinterpret_cast<const float*>(ws + r.ml);
+    m.capacity = pa::piece_bound(m.capacity);
 }
 
 }  // namespace
@@ -275,9 +281,9 @@ size_t pa_workspace_bytes(int32_t capacity, int32_t max_q_len, int32_t num_q_hea
                          pa::workspace_ml_bytes(capacity, max_q_len, num_q_heads) +
                          pa::workspace_counter_bytes(capacity, num_q_heads);
     if (capacity == 0) return slots;
-    // then pa_attention's shared-slot region (up to three times as many piece states), apart from the
-    // counters so that the fused merge's zero counters survive it
-    return slots + pa::workspace_piece_bytes(pa::piece_bound(capacity), max_q_len, num_q_heads, head_dim);
+    // then the shared-slot region (up to three times as many piece states), apart from the counters
+    // so that the fused merge's zero counters survive it
+    return pa::shared_region(capacity, max_q_len, num_q_heads, head_dim).end;
 }
 
 pa_status pa_plan(const int32_t* context_lens, const int32_t* cu_query_lens, int32_t num_seqs,
@@ -318,6 +324,7 @@ pa_status pa_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t n
         return pa_merge(num_rows, num_q_heads, head_dim, 0, nullptr, 1, nullptr, 0, nullptr, 0, out,
                         out_dtype, stream);
     }
+    share_slots(a, head_dim, capacity, workspace, workspace_bytes);
     return from_hip(pa::launch_decode(a, head_dim, kv_dtype, q_dtype == PA_F32, pa::as_stream(stream)));
 }
 
@@ -330,6 +337,10 @@ pa_status pa_merge(int32_t num_rows, int32_t num_q_heads, int32_t head_dim, int3
                                        max_q_len, reduce_info, capacity, workspace, workspace_bytes, out,
                                        out_dtype, &a);
     if (st != PA_OK || num_rows == 0) return st;
+    // pieces where pa_decode, given the same arguments, shared the slots
+    if (a.num_seqs > 0 &&
+        pa::shares_slots(capacity, num_seqs, head_dim, capacity, max_q_len, num_q_heads, workspace_bytes))
+        merge_pieces(a, head_dim, workspace);
     return from_hip(pa::launch_merge(a, head_dim, out_dtype == PA_BF16, pa::as_stream(stream)));
 }
 
@@ -373,8 +384,10 @@ pa_status pa_attention(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_
         d.plan_work_out = reinterpret_cast<int4*>(work_info);
         d.plan_reduce_out = reinterpret_cast<int2*>(reduce_info);
         d.plan_num_work_out = num_work;
-        share_slots(d, m, head_dim, capacity, workspace, workspace_bytes);
+        if (share_slots(d, head_dim, cap, workspace, workspace_bytes)) merge_pieces(m, head_dim, workspace);
     } else {
+        if (!nothing && share_slots(d, head_dim, capacity, workspace, workspace_bytes))
+            merge_pieces(m, head_dim, workspace);
         st = from_hip(pa::launch_plan(context_lens, cu_query_lens, num_seqs, cap, capacity, max_partitions,
                                       tile_tokens, sliding_window, work_info, reduce_info, num_work, s));
         if (st != PA_OK) return st;

@@ -64,12 +64,10 @@ struct SlotInfo {
     int k_lo, k_hi;   // key range of the slot
 };
 
-__device__ __forceinline__ bool slot_info(const DecodeArgs& a, int slot, SlotInfo& si) {
-    // the slot's work entry and the used-slot count are independent loads
-    const int4 w = a.work_info[slot];
-    const int used = *a.num_work;
+// From work entry w = (b, tile_begin, tile_end, .); `live` says the entry is among the used ones.
+__device__ __forceinline__ bool entry_info(const DecodeArgs& a, int4 w, bool live, SlotInfo& si) {
     const int b = w.x;
-    if (slot >= used || b < 0 || b >= a.num_seqs) return false;
+    if (!live || b < 0 || b >= a.num_seqs) return false;
     const int S = max(a.context_lens[b], 0);
     int row0 = b, L = 1;
     if (a.cu) {
@@ -93,6 +91,13 @@ __device__ __forceinline__ bool slot_info(const DecodeArgs& a, int slot, SlotInf
     return true;
 }
 
+__device__ __forceinline__ bool slot_info(const DecodeArgs& a, int slot, SlotInfo& si) {
+    // the slot's work entry and the used-slot count are independent loads
+    const int4 w = a.work_info[slot];
+    const int used = *a.num_work;
+    return entry_info(a, w, slot < used, si);
+}
+
 // ---------------------------------------------------------------------------------------------
 // planning in place: the plan of a batch of at most kInlinePlanSeqs requests, evaluated by every
 // workgroup with one request per thread, so the decode needs no separate planning launch.  The
@@ -100,29 +105,118 @@ __device__ __forceinline__ bool slot_info(const DecodeArgs& a, int slot, SlotInf
 // per-request ranges and the slot counts, so the buffers end up as the plan kernel writes them.
 // ---------------------------------------------------------------------------------------------
 // Shared slots.  When the capacity leaves every request one slot, slot sizes follow the request
-// lengths and one workgroup per slot leaves the longest request to a single workgroup.  Pieces of at
-// most `per` tiles, per = ceil((sum of the slots' tiles + slots) / (factor x cap)), cut every slot of
-// a request into the same number of pieces, ceil(largest slot / per), so the pieces of all slots
-// together number at most factor x cap + cap.  Piece k of X of a slot of n tiles covers its tiles
-// [floor(k n / X), floor((k + 1) n / X)), the plan's own split rule one level down.
-__device__ __forceinline__ long long piece_size(long long tiles_total, int slots, int factor, int cap) {
-    const long long den = static_cast<long long>(factor) * max(cap, 1);
-    return max(1LL, (tiles_total + slots + den - 1) / den);
+// lengths and one workgroup per slot leaves the longest request to a single workgroup.  Then every
+// slot of n tiles is cut into X = max(1, ceil(n / per)) pieces, per = ceil((sum of the slots' tiles +
+// slots) / (factor x slots)), so a plan of `used` slots makes at most factor x used + used pieces;
+// piece k covers the slot's tiles [floor(k n / X), floor((k + 1) n / X)), the plan's own split rule
+// one level down.  Pieces are numbered slot by slot, in slot order, so a request's pieces are
+// consecutive; the in-place plan and a plan read from work_info give the same pieces.
+__device__ __forceinline__ long long piece_size(long long tiles_total, int used, int factor) {
+    const long long den = static_cast<long long>(factor) * max(used, 1);
+    return max(1LL, (tiles_total + used + den - 1) / den);
 }
 
-__device__ __forceinline__ int pieces_per_slot(int tiles, int parts, long long per) {
+__device__ __forceinline__ int pieces_of(int n, long long per) {
+    return max(1, static_cast<int>((n + per - 1) / per));
+}
+
+// A request's slots hold q = floor(tiles / parts) or q + 1 tiles; pieces of all its slots.
+__device__ __forceinline__ int request_pieces(int tiles, int parts, long long per) {
     if (parts <= 0) return 0;
-    const long long largest = (tiles + parts - 1) / parts;
-    return static_cast<int>((largest + per - 1) / per);
+    const int q = tiles / parts;
+    const int big = tiles - q * parts;             // slots of q + 1 tiles
+    return (parts - big) * pieces_of(q, per) + big * pieces_of(q + 1, per);
 }
 
-// Tiles, relative to the request's first tile, of its piece `off` (slot off / X, piece off % X).
-__device__ __forceinline__ int2 piece_tile_range(int off, int X, int tiles, int parts) {
-    const int j = off / X;
-    const int k = off - j * X;
-    const int2 t = plan_tile_range(j, tiles, parts);
-    const int2 u = plan_tile_range(k, t.y - t.x, X);
+// Tiles, relative to the request's first tile, of the request's piece `off`: its slot j is the last
+// one whose earlier slots hold at most `off` pieces (slots before j: j of q tiles at least, and
+// floor(j tiles / parts) - j q of them with q + 1), found by bisection.
+__device__ __forceinline__ int2 request_piece_tiles(int off, int tiles, int parts, long long per) {
+    const int q = tiles / parts;
+    const int xq = pieces_of(q, per);
+    const int xb = pieces_of(q + 1, per);
+    auto before = [&](int j) -> int {              // pieces of slots 0 .. j-1
+        const int nb = plan_tile_range(j, tiles, parts).x - j * q;
+        return j * xq + nb * (xb - xq);
+    };
+    int lo = 0, hi = parts - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (before(mid) <= off) lo = mid;
+        else hi = mid - 1;
+    }
+    const int2 t = plan_tile_range(lo, tiles, parts);
+    const int n = t.y - t.x;
+    const int2 u = plan_tile_range(off - before(lo), n, pieces_of(n, per));
     return make_int2(t.x + u.x, t.x + u.y);
+}
+
+// Shared slots over a plan read from work_info (at most kInlinePlanSeqs slots, one per thread):
+// workgroup p's piece, the piece count and bound, and (workgroup 0) the requests' piece ranges.
+template <int NW>
+__device__ void pieces_from_plan(const DecodeArgs& a, int p, int4& wk, int2& nwk) {
+    static_assert(NW * 64 >= kInlinePlanSeqs, "one slot per thread");
+    __shared__ long long s_tiles[NW];
+    __shared__ int s_count[NW], s_below[NW];
+    __shared__ int s_pfirst[kInlinePlanSeqs + 1];
+    __shared__ int s_req[kInlinePlanSeqs];
+    __shared__ int2 s_range[kInlinePlanSeqs];
+    __shared__ int4 s_pentry;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const bool lead = blockIdx.x == 0;             // writes the requests' piece ranges
+    const int used = min(max(__builtin_amdgcn_readfirstlane(a.num_work[0]), 0), a.plan_slots);
+    const int4 e = tid < used ? a.work_info[tid] : make_int4(-1, 0, 0, 0);
+    const int n = tid < used ? max(e.z - e.y, 0) : 0;
+    const long long wt = wave_sum_nonneg(n);
+    if (lane == 0) s_tiles[wave] = wt;
+    if (lead && tid < kInlinePlanSeqs) {
+        s_req[tid] = e.x;
+        s_range[tid] = make_int2(0, 0);            // requests without slots: no pieces
+    }
+    __syncthreads();
+    long long total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) total += s_tiles[w];
+    const long long per = piece_size(total, used, a.pieces);
+    const int X = tid < used ? pieces_of(n, per) : 0;
+    const int incl = wave_incl_scan(X, lane);
+    if (lane == 63) s_count[wave] = incl;
+    __syncthreads();
+    int before = 0, pused = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        before += w < wave ? s_count[w] : 0;
+        pused += s_count[w];
+    }
+    const int pfirst = before + incl - X;          // = pused past the last slot
+    if (tid < kInlinePlanSeqs) s_pfirst[tid] = pfirst;
+    if (tid == 0) s_pfirst[kInlinePlanSeqs] = pused;
+    const int below = __popcll(__builtin_amdgcn_ballot_w64(tid < used && pfirst <= p));
+    if (lane == 0) s_below[wave] = below;
+    __syncthreads();
+    int owner = -1;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) owner += s_below[w];
+    if (p < pused && tid == owner) {
+        const int2 u = plan_tile_range(p - pfirst, n, X);
+        s_pentry = make_int4(e.x, e.y + u.x, e.y + u.y, e.w);
+    }
+    if (lead && tid < used) {
+        // a request's slots are consecutive: the first of them records the request's pieces,
+        // [its first piece, the first piece past the request's last slot)
+        const int b = e.x;
+        if (b >= 0 && b < a.num_seqs && (tid == 0 || s_req[tid - 1] != b)) {
+            int k = tid + 1;
+            while (k < used && s_req[k] == b) ++k;
+            s_range[b] = make_int2(pfirst, s_pfirst[k] - pfirst);
+        }
+    }
+    __syncthreads();
+    if (lead && tid < a.num_seqs) a.piece_reduce_out[tid] = s_range[tid];
+    wk = p < pused ? s_pentry : make_int4(-1, 0, 0, 0);
+    nwk = make_int2(pused, static_cast<int>(min(per, static_cast<long long>(INT_MAX))));   // pieces <= per tiles
 }
 
 // Up to 64 requests: every wave evaluates the whole plan on its own, with no barrier.
@@ -161,9 +255,8 @@ __device__ __forceinline__ void plan_in_wave(const DecodeArgs& a, int slot, int 
     }
     if (!a.pieces) return;
     // shared slots: this workgroup streams piece `slot` instead (see piece_size)
-    const long long per = piece_size(wave_sum_nonneg(tiles), used, a.pieces, a.plan_cap);
-    const int X = pieces_per_slot(tiles, parts, per);
-    const int np = parts * X;
+    const long long per = piece_size(wave_sum_nonneg(tiles), used, a.pieces);
+    const int np = request_pieces(tiles, parts, per);
     const int pincl = wave_incl_scan(np, lane);
     const int pfirst = pincl - np;
     const int pused = __builtin_amdgcn_readlane(pincl, 63);
@@ -172,8 +265,8 @@ __device__ __forceinline__ void plan_in_wave(const DecodeArgs& a, int slot, int 
     wk = make_int4(-1, 0, 0, 0);
     if (slot < pused) {
         const int o = max(po, 0);
-        const int2 t = piece_tile_range(slot - __builtin_amdgcn_readlane(pfirst, o), __builtin_amdgcn_readlane(X, o),
-                                        __builtin_amdgcn_readlane(tiles, o), __builtin_amdgcn_readlane(parts, o));
+        const int2 t = request_piece_tiles(slot - __builtin_amdgcn_readlane(pfirst, o),
+                                           __builtin_amdgcn_readlane(tiles, o), __builtin_amdgcn_readlane(parts, o), per);
         const int t0 = __builtin_amdgcn_readlane(pr.t0, o);
         wk = make_int4(o, t0 + t.x, t0 + t.y, __builtin_amdgcn_readlane(S, o));
     }
@@ -237,11 +330,10 @@ __device__ void plan_in_place(const DecodeArgs& a, int slot, int g, int4& wk, in
     const int first = before + incl - parts;
 
     // shared slots: this request's pieces and their scan within the wave
-    int X = 0, np = 0, pincl = 0;
-    const long long per = a.pieces ? piece_size(tiles_total, used, a.pieces, a.plan_cap) : 1;
+    int np = 0, pincl = 0;
+    const long long per = a.pieces ? piece_size(tiles_total, used, a.pieces) : 1;
     if (a.pieces) {
-        X = pieces_per_slot(tiles, parts, per);
-        np = parts * X;
+        np = request_pieces(tiles, parts, per);
         pincl = wave_incl_scan(np, lane);
     }
 
@@ -282,7 +374,7 @@ __device__ void plan_in_place(const DecodeArgs& a, int slot, int g, int4& wk, in
 #pragma unroll
     for (int w = 0; w < NW; ++w) powner += s_pbelow[w];
     if (slot < pused && r == powner) {
-        const int2 t = piece_tile_range(slot - pfirst, X, tiles, parts);
+        const int2 t = request_piece_tiles(slot - pfirst, tiles, parts, per);
         s_pentry = make_int4(r, pr.t0 + t.x, pr.t0 + t.y, S);
     }
     __syncthreads();
@@ -568,6 +660,8 @@ __global__ __launch_bounds__((64 * NWAVES), (Mfma<D, NCB, KV8, NWAVES>::WAVES)) 
     } else {
         if (a.plan_inline) {
             plan_in_place<C::NW>(a, slot, g, wk, nwk);
+        } else if (a.pieces) {
+            pieces_from_plan<C::NW>(a, slot, wk, nwk);
         } else {
             wk = a.work_info[slot];
             nwk = *reinterpret_cast<const int2*>(a.num_work);
@@ -1335,7 +1429,15 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeArgs a) {
     const int slot = blockIdx.x / a.num_kv_heads;
     const int g = blockIdx.x - slot * a.num_kv_heads;
     SlotInfo si;
-    if (!slot_info(a, slot, si)) return;
+    if (a.pieces) {
+        // shared slots: this workgroup's piece (slot is then the piece index)
+        int4 wk;
+        int2 nwk;
+        pieces_from_plan<4>(a, slot, wk, nwk);
+        if (!entry_info(a, wk, slot < nwk.x, si)) return;
+    } else if (!slot_info(a, slot, si)) {
+        return;
+    }
     const int G = a.group;
     const int M = G * si.L;
     constexpr int E = D / 64;
@@ -1473,7 +1575,7 @@ hipError_t launch_d(const DecodeArgs& a, pa_dtype kv, int ncb, bool qf32, dim3 g
         else hipLaunchKernelGGL((decode_f32_kernel<D, false>), grid, dim3(256), 0, stream, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || !a.out) return e;
-        MergeArgs m;                                  // fp32 caches: the merge is a second launch
+        MergeArgs m{};                                // fp32 caches: the merge is a second launch
         m.cu = a.cu;
         m.reduce_info = a.reduce_info;
         m.ws_acc = a.ws_acc;

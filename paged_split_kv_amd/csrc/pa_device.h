@@ -297,11 +297,11 @@ struct DecodeArgs {
     int4* plan_work_out;
     int2* plan_reduce_out;
     int32_t* plan_num_work_out;
-    // shared slots (planning in place only): pieces > 0 cuts every slot into pieces of at most
-    // ceil((tiles of all slots + slots) / (pieces * plan_cap)) tiles, one workgroup each; workgroup p
-    // streams piece p and writes its state as state p (capacity is then the piece count's bound), and
-    // (first piece, pieces) per request go to piece_reduce_out for the merge.  plan_slots is the
-    // length of plan_work_out.
+    // shared slots: pieces != 0 cuts every slot into pieces (see piece_size), one workgroup each;
+    // workgroup p streams piece p and writes its state as state p of the shared-slot region (ws_acc
+    // and ws_ml then point there and capacity is the piece count's bound), and (first piece, pieces)
+    // per request go to piece_reduce_out for the merge.  plan_slots is the plan's slot count (the
+    // length of work_info).
     int pieces;
     int plan_slots;
     int2* piece_reduce_out;
@@ -333,15 +333,36 @@ struct MergeArgs {
 // Requests a decode workgroup can plan for in place: one per thread of its 4 waves.
 constexpr int kInlinePlanSeqs = PA_INLINE_PLAN_SEQS;
 
-// Shared slots: pieces per slot are sized so that all slots together make at most kPieceFactor x
-// plan_cap + plan_cap pieces.
+// Shared slots: pieces are sized so that a plan of `used` slots makes at most kPieceFactor x used +
+// used pieces (see piece_size), so 3 x capacity piece states always suffice.
 constexpr int kPieceFactor = 2;
-inline int piece_bound(int plan_cap) { return (kPieceFactor + 1) * plan_cap; }
-// Workspace bytes of the shared-slot layout for `states` piece states: acc, (m, l), then the
-// per-request (first piece, pieces) pairs.
-inline size_t workspace_piece_bytes(int states, int max_q_len, int hq, int d) {
-    return workspace_acc_bytes(states, max_q_len, hq, d) + workspace_ml_bytes(states, max_q_len, hq) +
-           align256(static_cast<size_t>(kInlinePlanSeqs) * 2 * sizeof(int32_t));
+inline int piece_bound(int capacity) { return (kPieceFactor + 1) * capacity; }
+
+// The shared-slot region, after the slot layout's counters: the piece states' acc and (m, l) for
+// piece_bound(capacity) pieces, then the per-request (first piece, pieces) pairs for up to
+// kInlinePlanSeqs requests.  Byte offsets from the workspace's start.
+struct SharedRegion {
+    size_t acc, ml, reduce, end;
+};
+inline SharedRegion shared_region(int capacity, int max_q_len, int hq, int d) {
+    SharedRegion r;
+    const int states = piece_bound(capacity);
+    r.acc = workspace_acc_bytes(capacity, max_q_len, hq, d) + workspace_ml_bytes(capacity, max_q_len, hq) +
+            workspace_counter_bytes(capacity, hq);
+    r.ml = r.acc + workspace_acc_bytes(states, max_q_len, hq, d);
+    r.reduce = r.ml + workspace_ml_bytes(states, max_q_len, hq);
+    r.end = r.reduce + align256(static_cast<size_t>(kInlinePlanSeqs) * 2 * sizeof(int32_t));
+    return r;
+}
+
+// Whether a decode writes pieces rather than slot states: a pure function of arguments that pa_decode,
+// pa_merge and pa_attention all receive, so each decides alike.  `one_slot_cap` is the plan capacity
+// that makes every request at most one slot (<= num_seqs); the batch fits the per-request table; the
+// workspace holds the region.
+inline bool shares_slots(int one_slot_cap, int num_seqs, int head_dim, int capacity, int max_q_len, int hq,
+                         size_t workspace_bytes) {
+    return one_slot_cap > 0 && one_slot_cap <= num_seqs && num_seqs <= kInlinePlanSeqs && head_dim <= 128 &&
+           workspace_bytes >= shared_region(capacity, max_q_len, hq, head_dim).end;
 }
 
 hipError_t launch_plan(const int32_t* context_lens, const int32_t* cu, int num_seqs,

@@ -43,13 +43,10 @@ class DecodeStep:
         self.out = torch.empty((num_rows, num_q_heads, head_dim), dtype=out_dtype, device=self.device)
 
     def shares_slots(self, kv_dtype: str, num_q_heads: int, head_dim: int) -> bool:
-        """Whether ``attention`` streams slots with several workgroups each: the in-place plan gives
-        every request one slot (capacity <= batch) and the decode runs its one-row-block form
-        (head_dim <= 128, G x max_q_len <= 16).  Its output then matches the three-call path within
-        the attention tolerance rather than bit for bit; the plan buffers still match exactly."""
-        rows = (num_q_heads // self.num_kv_heads) * self.max_q_len
-        return (kv_dtype != "f32" and 0 < self.num_seqs <= B.PA_INLINE_PLAN_SEQS and self.capacity > 0
-                and self.capacity <= self.num_seqs and head_dim <= 128 and rows <= 16)
+        """Whether the decode (``decode`` without the merge, or ``attention``) streams slots with
+        several workgroups each: the plan gives every request one slot (capacity <= batch <= 256),
+        head_dim <= 128, and the workspace (sized by pa_workspace_bytes) holds the region."""
+        return 0 < self.capacity <= self.num_seqs <= B.PA_INLINE_PLAN_SEQS and head_dim <= 128
 
     @classmethod
     def for_case(cls, case, plan: Optional[PlanConfig] = None) -> "DecodeStep":

@@ -43,7 +43,8 @@ def _check_plan(step, ctx, hkv, cfg):
 
 
 def _poison_pieces(step):
-    """NaN pattern in the shared-slot region too (it follows the slot partials and the counters)."""
+    """NaN pattern in the shared-slot region too (it follows the slot partials and the counters;
+    its mode word is written by every decode launch)."""
     up = lambda x: (x + 255) // 256 * 256
     start = _partial_bytes(step) + up(step.capacity * step.out.shape[1] * 4)
     step.workspace[start:].fill_(0xFF)
@@ -52,6 +53,7 @@ def _poison_pieces(step):
 def _both_routes(case, cfg):
     three = DecodeStep.for_case(case, cfg)
     _poison(three)
+    _poison_pieces(three)
     ref = three.run_case(case, fused=False).clone()
     whole = DecodeStep.for_case(case, cfg)
     _poison(whole)
@@ -61,13 +63,9 @@ def _both_routes(case, cfg):
     return got, ref, whole
 
 
-def _assert_same_as_three(got, ref, step, kv, what=""):
-    """Bit for bit, except where pa_attention shares slots between workgroups: the pieces' states
-    are folded in another order, so the two routes agree within the attention tolerance."""
-    if step.shares_slots(kv, got.shape[1], got.shape[2]):
-        assert_close(to_f64(got), to_f64(ref), "fp8" if kv == "fp8" else "bf16", what)
-    else:
-        assert torch.equal(got, ref), f"{what}: pa_attention differs from pa_plan + pa_decode + pa_merge"
+def _assert_same_as_three(got, ref, what=""):
+    """Bit for bit: with shared slots both routes cut the slots into the same pieces."""
+    assert torch.equal(got, ref), f"{what}: pa_attention differs from pa_plan + pa_decode + pa_merge"
 
 
 @pytest.mark.parametrize("spec", SMALL, ids=[s[0] for s in SMALL])
@@ -76,7 +74,7 @@ def test_small_cases(spec):
     announce(f"attention {spec[0]}")
     cfg = PlanConfig(cu_count=256, max_partitions=P, tile_tokens=T)
     got, ref, step = _both_routes(case, cfg)
-    _assert_same_as_three(got, ref, step, case.kv_dtype, spec[0])
+    _assert_same_as_three(got, ref, spec[0])
     _check_plan(step, case.context_lens.cpu().numpy(), case.num_kv_heads, cfg)
     g = to_f64(got)
     assert_close(g, oracle_direct(case), tolerance_kind(case), spec[0])
@@ -89,7 +87,7 @@ def test_full_size_workloads(name):
     case = W.make_config(name, device=DEV)
     cfg = PlanConfig(cu_count=256)
     got, ref, step = _both_routes(case, cfg)
-    _assert_same_as_three(got, ref, step, case.kv_dtype, name)
+    _assert_same_as_three(got, ref, name)
     _check_plan(step, case.context_lens.cpu().numpy(), case.num_kv_heads, cfg)
     assert_close(to_f64(got), oracle_direct(case), tolerance_kind(case), name)
 
@@ -101,14 +99,14 @@ def test_skewed_max_step():
     case = W.make_config("skewed_bf16", device=DEV, step=idx)
     cfg = PlanConfig(cu_count=256)
     got, ref, step = _both_routes(case, cfg)
-    _assert_same_as_three(got, ref, step, case.kv_dtype, "skewed max")
+    _assert_same_as_three(got, ref, "skewed max")
     _check_plan(step, steps[idx], 2, cfg)
     assert_close(to_f64(got), oracle_direct(case), "bf16", "skewed max")
 
 
 SHARED = [
-    # (name, context lens, query lens, Hq, Hkv, D, page, kv, cu_count, tile): each batch has at least
-    # 2 x cu_count / Hkv requests, so the capacity is the batch and pa_attention shares slots
+    # (name, context lens, query lens, Hq, Hkv, D, page, kv, cu_count, tile[, q dtype]): each batch
+    # has at least 2 x cu_count / Hkv requests, so the capacity is the batch and the slots are shared
     # up to 64 requests (the plan in one wave); empty requests leave spare slots, so the long
     # requests get several slots, each cut into the same number of pieces (some of them empty)
     ("wave_plan_bf16", [0] * 6 + [16, 600, 33, 5000, 1, 9000, 250, 20000] * 4 + [77, 3, 1500, 40, 0, 0],
@@ -121,11 +119,16 @@ SHARED = [
     ("single_request", [100000], None, 4, 2, 128, 64, "bf16", 1, 256),
     # mostly empty requests: the spare slots go to five long ones, ~9 slots each, then pieces
     ("mostly_empty", [0] * 45 + [30000, 7000, 65000, 12000, 300], None, 8, 1, 128, 16, "fp8", 8, 256),
+    # two 16-row blocks (G x L = 32): the four-wave form with two column blocks
+    ("two_row_blocks", "lognormal90", "q2", 16, 1, 128, 16, "bf16", 32, 256),
+    # fp32 cache and queries: the vector kernel takes its piece from the same rule
+    ("fp32_cache", "lognormal80", None, 8, 2, 64, 16, "f32", 64, 64, "f32"),
 ]
 
 
 def _shared_case(spec, seed):
-    name, ctx, ql, hq, hkv, d, bs, kv, cu_count, T = spec
+    name, ctx, ql, hq, hkv, d, bs, kv, cu_count, T = spec[:10]
+    qd = spec[10] if len(spec) > 10 else "bf16"
     rng = np.random.default_rng(seed)
     if isinstance(ctx, str):
         n = int(ctx[len("lognormal"):])
@@ -134,15 +137,16 @@ def _shared_case(spec, seed):
         ctx = ctx.tolist()
     q_lens = None if ql is None else rng.integers(1, int(ql[1:]) + 1, size=len(ctx)).tolist()
     case = W.build_case(name, ctx, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs,
-                        kv_dtype=kv, q_dtype="bf16", seed=seed, q_lens=q_lens, pad_rows=1, device=DEV)
+                        kv_dtype=kv, q_dtype=qd, seed=seed, q_lens=q_lens, pad_rows=1, device=DEV)
     return case, PlanConfig(cu_count=cu_count, tile_tokens=T)
 
 
 @pytest.mark.parametrize("spec", SHARED, ids=[s[0] for s in SHARED])
 def test_shared_slots_match_oracle(spec):
-    """Every request one slot: pa_attention cuts the slots into pieces streamed by workgroups of
-    their own and merges the pieces per request.  Output against the oracle, the stored plan
-    against the oracle's plan, exact zeros where rows have no keys."""
+    """Every request one slot: the decode cuts the slots into pieces streamed by workgroups of their
+    own and the merge folds the pieces per request, in pa_attention and in pa_plan + pa_decode +
+    pa_merge alike (bit for bit).  Output against the oracle, the stored plan against the oracle's
+    plan, exact zeros where rows have no keys."""
     case, cfg = _shared_case(spec, seed=31)
     announce(f"shared slots {spec[0]}")
     got, ref, step = _both_routes(case, cfg)
@@ -151,7 +155,7 @@ def test_shared_slots_match_oracle(spec):
     g = to_f64(got)
     assert_close(g, oracle_direct(case), tolerance_kind(case), spec[0])
     assert (g[_zero_rows(case)] == 0.0).all()
-    _assert_same_as_three(got, ref, step, case.kv_dtype, spec[0])
+    _assert_same_as_three(got, ref, spec[0])
 
 
 def _one_page_case(ctx, hkv, seed):
@@ -197,7 +201,7 @@ def test_plan_in_place_fuzz(seed):
     whole.attention(q, k, v, "bf16", bt, lens, scale=0.125)
     torch.cuda.synchronize()
     _check_plan(whole, ctx, hkv, cfg)
-    _assert_same_as_three(whole.out, three.out, whole, "bf16", f"fuzz seed {seed}")
+    _assert_same_as_three(whole.out, three.out, f"fuzz seed {seed}")
 
 
 def test_all_empty_and_empty_batch():

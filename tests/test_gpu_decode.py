@@ -102,16 +102,16 @@ def test_small_cases_match_oracle(spec, fused):
     assert (np.abs(got[~z]).sum(axis=(1, 2)) > 0).all()
 
 
-ONE_SLOT = [s for s in SMALL if s[7] != "f32" and s[5] <= 128
-            and s[3] // s[4] * max(s[2] or [1]) <= 16]
+ONE_SLOT = [s for s in SMALL if s[5] <= 128]
 
 
 @pytest.mark.parametrize("mode", ["fused_merge", "separate_merge", "attention"])
 @pytest.mark.parametrize("spec", ONE_SLOT, ids=[s[0] for s in ONE_SLOT])
 def test_one_slot_per_request(spec, mode):
     """A budget of at most one workgroup per request (cu_count 1): the capacity is the batch, every
-    request is one slot, and the decode runs its eight-wave form with slots split evenly (planned
-    by pa_plan, or in place by pa_attention)."""
+    request is one slot.  Without out the decode shares the slots (pieces, folded by pa_merge);
+    with out it merges in its launch, in the eight-wave form with slots split evenly where that
+    applies (G x L <= 16, head_dim <= 128, bf16 or fp8)."""
     case, P, T = _small_case(spec, seed=12)
     announce(f"one slot per request {spec[0]} {mode}")
     if mode == "attention":
@@ -183,6 +183,30 @@ def test_fused_calls_back_to_back_reuse_the_workspace():
             out = step.run_case(case, fused=True)
             torch.cuda.synchronize()
             assert_close(to_f64(out), oracle_direct(case), "bf16", f"back-to-back {rep} {k}")
+    nbytes = _partial_bytes(step)
+    counters = (step.capacity * step.out.shape[1] * 4 + 255) // 256 * 256
+    assert int(step.workspace[nbytes:nbytes + counters].view(torch.int32).abs().sum().item()) == 0
+
+
+def test_workspace_switches_between_pieces_and_slots():
+    """One workspace, one plan capacity (every request one slot), bf16 and fp32 caches: pa_decode
+    without out cuts the slots into pieces (the shared-slot region), pa_decode with out keeps slot
+    states and merges in its launch with the arrival counters; alternating the two must leave both
+    right and the counters zero."""
+    ctx = [1, 17, 100, 3000, 5000]
+    cases = [W.build_case(f"switch_{kv}", ctx, num_q_heads=4, num_kv_heads=1, head_dim=64, block_size=16,
+                          kv_dtype=kv, q_dtype="f32", seed=41, device=DEV) for kv in ("bf16", "f32")]
+    step = DecodeStep.for_case(cases[0], PlanConfig(cu_count=1, tile_tokens=16))
+    assert step.capacity == len(ctx) and step.shares_slots("bf16", 4, 64)
+    refs = [oracle_direct(c) for c in cases]
+    for rep in range(2):
+        for fused in (False, True):
+            for case, ref in zip(cases, refs):
+                announce(f"pieces/slots switch {rep} fused={fused} {case.kv_dtype}")
+                step.out.fill_(float("nan"))
+                out = step.run_case(case, fused=fused)
+                torch.cuda.synchronize()
+                assert_close(to_f64(out), ref, tolerance_kind(case), f"switch {rep} {fused} {case.kv_dtype}")
     nbytes = _partial_bytes(step)
     counters = (step.capacity * step.out.shape[1] * 4 + 255) // 256 * 256
     assert int(step.workspace[nbytes:nbytes + counters].view(torch.int32).abs().sum().item()) == 0
