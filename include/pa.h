@@ -164,7 +164,8 @@ pa_status pa_plan(const int32_t* context_lens, const int32_t* cu_query_lens, int
  *                              workspace zero-filled) and every completed call leaves them zero.
  *                              Calls that share a workspace must not overlap.
  * Supported: head_dim in {64, 128, 256}; block_size in {16, 64, 128};
- * (num_q_heads / num_kv_heads) x max_q_len <= PA_MAX_GROUP_ROWS.
+ * (num_q_heads / num_kv_heads) x max_q_len <= PA_MAX_GROUP_ROWS; max_blocks_per_seq x block_size
+ * <= 2^31 - 257 (key positions are 32-bit).  Anything else returns PA_UNSUPPORTED.
  * KV types bf16 and fp8 run on the matrix cores in bf16 (fp8 codes widen exactly to bf16; q is
  * rounded to bf16; probabilities are rounded to bf16 for the P.V product; accumulation is fp32).
  * KV type f32 runs in fp32 on the vector ALUs (with out, the merge is a second launch).

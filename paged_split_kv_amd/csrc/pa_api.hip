@@ -13,6 +13,12 @@ bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) %
 bool supported_head_dim(int d) { return d == 64 || d == 128 || d == 256; }
 bool supported_block_size(int bs) { return bs == 16 || bs == 64 || bs == 128; }
 
+// The kernels address a request's keys and its block-table row with 32-bit integers: every key a
+// block table can reach (max_blocks_per_seq x block_size, with a chunk of slack) must fit.
+bool table_reach_fits(int32_t max_blocks_per_seq, int32_t block_size) {
+    return (long long)max_blocks_per_seq * block_size <= (long long)INT_MAX - 256;
+}
+
 pa_status capacity_formula(int32_t num_seqs, int32_t num_kv_heads, int32_t cu_count,
                            int32_t budget_mult, int32_t max_partitions, int32_t* out) {
     if (num_seqs < 0 || num_kv_heads < 1 || cu_count < 1 || budget_mult < 1 || max_partitions < 1)
@@ -73,6 +79,7 @@ pa_status prepare_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int3
     if (!cu_query_lens && (max_q_len != 1 || num_rows < num_seqs)) return PA_INVALID_ARG;
     if (!(scale == scale) || !(k_scale == k_scale) || !(v_scale == v_scale)) return PA_INVALID_ARG;
     if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PA_UNSUPPORTED;
+    if (!table_reach_fits(max_blocks_per_seq, block_size)) return PA_UNSUPPORTED;
     if (tile_tokens % block_size != 0) return PA_UNSUPPORTED;
     const int group = num_q_heads / num_kv_heads;
     if ((long long)group * max_q_len > PA_MAX_GROUP_ROWS) return PA_UNSUPPORTED;
@@ -220,6 +227,7 @@ pa_status prepare_prefill(const void* q, pa_dtype q_dtype, int32_t num_rows, int
     if (out_dtype != q_dtype || num_q_heads % num_kv_heads != 0) return PA_INVALID_ARG;
     if (!(scale == scale) || !(k_scale == k_scale) || !(v_scale == v_scale)) return PA_INVALID_ARG;
     if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PA_UNSUPPORTED;
+    if (!table_reach_fits(max_blocks_per_seq, block_size)) return PA_UNSUPPORTED;
     if (kv_dtype == PA_F32) return PA_UNSUPPORTED;
     const int group = num_q_heads / num_kv_heads;
     if (group > PA_MAX_GROUP_ROWS) return PA_UNSUPPORTED;

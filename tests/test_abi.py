@@ -111,6 +111,7 @@ def test_decode_argument_checks():
     assert _decode_status(D=96) == B.PA_UNSUPPORTED
     assert _decode_status(D=512) == B.PA_UNSUPPORTED
     assert _decode_status(bs=32) == B.PA_UNSUPPORTED
+    assert _decode_status(mb=1 << 27) == B.PA_UNSUPPORTED              # keys a table reaches exceed int32
     assert _decode_status(T=200) == B.PA_UNSUPPORTED                   # tile not a multiple of bs
     assert _decode_status(Hq=32, Hkv=1, cu=256, ql=3) == B.PA_UNSUPPORTED   # 96 rows per group
     assert _decode_status(ql=2) == B.PA_INVALID_ARG                    # no cu but max_q_len 2
@@ -214,6 +215,7 @@ def test_prefill_argument_checks():
     assert _prefill_status(kvd=B.PA_F32) == B.PA_UNSUPPORTED        # matrix-core path only
     assert _prefill_status(D=96) == B.PA_UNSUPPORTED
     assert _prefill_status(bs=32) == B.PA_UNSUPPORTED
+    assert _prefill_status(mb=1 << 27) == B.PA_UNSUPPORTED           # keys a table reaches exceed int32
     assert _prefill_status(Hq=15) == B.PA_INVALID_ARG
     assert _prefill_status(od=B.PA_F32) == B.PA_INVALID_ARG
     assert _prefill_status(out=None) == B.PA_INVALID_ARG
