@@ -14,20 +14,38 @@ namespace pa {
 
 namespace {
 
+// (m, l, acc) <- the log-sum-exp merge of two states (m in base-2 units; an empty state has m = -inf
+// and l = 0 and contributes nothing; two empty states stay empty).
+__device__ __forceinline__ void fold_state(float& m, float& l, float4& acc, float m2, float l2, const float4& a2) {
+    const float mn = fmaxf(m, m2);
+    const bool none = mn == -INFINITY;
+    const float f1 = none ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+    const float f2 = none ? 0.f : __builtin_amdgcn_exp2f(m2 - mn);
+    l = l * f1 + l2 * f2;
+    acc.x = acc.x * f1 + a2.x * f2;
+    acc.y = acc.y * f1 + a2.y * f2;
+    acc.z = acc.z * f1 + a2.z * f2;
+    acc.w = acc.w * f1 + a2.w * f2;
+    m = mn;
+}
+
 // One workgroup of NT threads per (row, head) and column part: the head dimension is split into CS
 // parts of D / CS columns, each its own workgroup (every part reads all partials' (m, l) and its own
 // columns of acc; the parts write disjoint columns).  Thread t owns the 16-byte column dc = t % NDC of
 // its part and the partials j = pg, pg + NPG, ... with pg = t / NDC; it folds them into a running
-// (max, sum, acc) with independent loads, then the NPG states of a column are combined in LDS.
+// (max, sum, acc) with independent loads, then the NPG states of a column are combined in a fixed
+// tree (lanes of a wave, then the waves through LDS).
 // CS = 4 when there are fewer (row, head) pairs than compute units: a request split into hundreds of
 // partials is then read by four workgroups on four compute units.
 template <int D, bool OUT_BF16, int NT, int CS>
 __global__ __launch_bounds__(NT) void merge_kernel(const MergeArgs a) {
     constexpr int NDC = D / 4 / CS;     // float4 columns of this part
     constexpr int NPG = NT / NDC;       // partial groups
-    __shared__ float4 s_acc[NPG][NDC];
-    __shared__ float s_m[NPG];
-    __shared__ float s_l[NPG];
+    constexpr int NW = NT / 64;         // waves
+    static_assert(NDC <= 64 && 64 % NDC == 0, "a wave holds whole partial groups");
+    __shared__ float4 s_acc[NW][NDC];
+    __shared__ float s_m[NW][NDC];
+    __shared__ float s_l[NW][NDC];
 
     const int tid = threadIdx.x;
     const int pair = blockIdx.x / CS;
@@ -75,31 +93,36 @@ __global__ __launch_bounds__(NT) void merge_kernel(const MergeArgs a) {
             }
         }
     }
-    s_acc[pg][tid % NDC] = acc;
-    if (tid % NDC == 0) {
-        s_m[pg] = m;
-        s_l[pg] = l;
+    // Fold the NPG group states of each column in a fixed tree: group pg sits in lanes of wave
+    // pg / (64 / NDC), so the first steps pair lanes NDC, 2 NDC, ... apart inside the wave, then one
+    // thread per column folds the waves' states through LDS.
+#pragma unroll
+    for (int d = NDC; d < 64; d <<= 1) {
+        const float m2 = __shfl_xor(m, d, 64);
+        const float l2 = __shfl_xor(l, d, 64);
+        float4 a2;
+        a2.x = __shfl_xor(acc.x, d, 64);
+        a2.y = __shfl_xor(acc.y, d, 64);
+        a2.z = __shfl_xor(acc.z, d, 64);
+        a2.w = __shfl_xor(acc.w, d, 64);
+        fold_state(m, l, acc, m2, l2, a2);
+    }
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    if (lane < NDC) {
+        s_acc[wave][lane] = acc;
+        s_m[wave][lane] = m;
+        s_l[wave][lane] = l;
     }
     __syncthreads();
-    if (pg != 0) return;
-    float Mx = -INFINITY;
+    if (tid >= NDC) return;
+    m = s_m[0][tid];
+    l = s_l[0][tid];
+    acc = s_acc[0][tid];
 #pragma unroll
-    for (int k = 0; k < NPG; ++k) Mx = fmaxf(Mx, s_l[k] > 0.f ? s_m[k] : -INFINITY);
-    float den = 0.f;
-    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (Mx != -INFINITY) {
-#pragma unroll
-        for (int k = 0; k < NPG; ++k) {
-            if (!(s_l[k] > 0.f)) continue;
-            const float f = __builtin_amdgcn_exp2f(s_m[k] - Mx);
-            const float4 v = s_acc[k][tid % NDC];
-            den += f * s_l[k];
-            num.x += f * v.x;
-            num.y += f * v.y;
-            num.z += f * v.z;
-            num.w += f * v.w;
-        }
-    }
+    for (int w = 1; w < NW; ++w) fold_state(m, l, acc, s_m[w][tid], s_l[w][tid], s_acc[w][tid]);
+    const float den = l;
+    const float4 num = acc;
     const float inv = den > 0.f ? 1.f / den : 0.f;
     const float4 o = den > 0.f ? make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv)
                                : make_float4(0.f, 0.f, 0.f, 0.f);
