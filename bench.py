@@ -190,6 +190,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--graph", action="store_true", help="also time a HIP-graph replay of the steps")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the per-step timing with the last-level cache evicted between steps")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a 1 GiB device copy first (reference kernel for the HBM counters)")
     ap.add_argument("--window", type=int, default=0,
@@ -400,6 +402,36 @@ def main():
         graph = {"us_per_step": round(g_ms * 1e3, 2),
                  "kv_gbps": round(float(kv_bytes.mean()) / (g_ms * 1e-3) / 1e9, 1)}
 
+    # one step per batch with events around it, each after a 512 MB write that evicts the 256 MB
+    # last-level cache (outside the events), and the same without the write
+    cold = None
+    if args.workload == "skewed" and not args.no_cold:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+        def per_step(evict):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(nsteps)]
+            for i in range(nsteps):
+                if evict:
+                    scratch.fill_(i & 0xff)
+                evs[i][0].record(stream)
+                run(i)
+                evs[i][1].record(stream)
+            torch.cuda.synchronize()
+            return np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+
+        per_step(True)                                # warm-up of the pattern
+        t_cold, t_warm = per_step(True), per_step(False)
+        del scratch
+        cold = {"steps": nsteps,
+                "evicted_us_mean": round(float(t_cold.mean()), 2),
+                "evicted_us_p50": round(float(np.median(t_cold)), 2),
+                "evicted_us_p90": round(float(np.quantile(t_cold, 0.9)), 2),
+                "evicted_kv_gbps": round(float(kv_bytes.mean()) / (float(t_cold.mean()) * 1e-6) / 1e9, 1),
+                "not_evicted_us_mean": round(float(t_warm.mean()), 2),
+                "note": "pa_attention per step between its own events; 512 MB written before each "
+                        "evicted step, outside its events"}
+
     us_step = plain_ms * 1e3 / K
     gbps = bytes_done / (plain_ms * 1e-3) / 1e9
     dec_gbps = float(kv_bytes.mean()) / (decode_ms * 1e-3) / 1e9
@@ -462,6 +494,7 @@ def main():
                      "duration_us": round(decode_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": round(float(kv_bytes.mean()), 1)},
         "hip_graph": graph,
+        "cold_cache": cold,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline and pool is not None:
