@@ -1,6 +1,6 @@
 """Benchmark of the paged split-KV decode step on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--graph]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--graph] [--no-cold]
 
 Workload: the skewed 32-request bf16 decode (Hq 16 / Hkv 2, D 128, pages of 16 tokens).  128 decode
 steps whose in-batch max/min context ratio follows the agentic trace (p50 ~2.5, p90 ~21); every step
@@ -8,7 +8,8 @@ draws its pages at random from a 4 GiB K/V pool, so the 256 MB last-level cache 
 data across steps.  One timed step = one pa_attention call over one batch (plan, decode and merge; the
 decode launch plans in place, so two launches), inputs resident in HBM.  value = KV bytes read / step
 time (GB/s).  The three-call form (pa_plan + pa_decode + pa_merge) and the form with the merge inside
-the decode launch are timed too and reported beside it.
+the decode launch are timed too and reported beside it, and so is each step between its own events
+with the 256 MB last-level cache evicted before it (a 512 MB write outside the events) and without.
 
 The roofline object is for the decode kernel: algorithmic bytes (sum of context lengths x Hkv x 2 x D
 x 2 bytes per launch, averaged over the batches) over its average launch duration, measured with HIP
