@@ -10,6 +10,8 @@ decode launch plans in place, so two launches), inputs resident in HBM.  value =
 time (GB/s).  The three-call form (pa_plan + pa_decode + pa_merge) and the form with the merge inside
 the decode launch are timed too and reported beside it, and so is each step between its own events
 with the 256 MB last-level cache evicted before it (a 512 MB write outside the events) and without.
+A 1 GiB device copy gives the box's measured copy ceiling beside the 8 TB/s peak, and the CPU oracle
+is timed on a bounded sample of every workload (cpu_baseline).
 
 The roofline object is for the decode kernel: algorithmic bytes (sum of context lengths x Hkv x 2 x D
 x 2 bytes per launch, averaged over the batches) over its average launch duration, measured with HIP
@@ -88,11 +90,58 @@ def cpu_baseline(pool, budget_s: float, max_steps: int, window: int = 0):
         n += 1
         if spent >= budget_s:
             break
-    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": threads,
+    # the oracle splits the work into (request, kv head) tasks: no more threads than tasks are busy
+    used = min(threads, len(pool.steps[0]) * pool.k_cache.shape[1])
+    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": used,
             "kind": "oracle",
             "us_per_step": round(spent / n * 1e6, 1),
             "sample": f"{n} of the {len(pool.steps)} steps (seeded random order, stopped after "
                       f"{budget_s:.0f} s), fp64 direct attention over the gathered pages, {spent:.1f} s"}
+
+
+def cpu_baseline_case(case, budget_s: float, kv_bytes: float):
+    """The CPU oracle (direct fp64 attention) on one full-size configuration, repeated while the
+    budget lasts (at least once); the host copy of the case is made before the clock starts."""
+    import oracle
+
+    threads = oracle.default_threads()
+    h = case.host()
+    spent, n = 0.0, 0
+    while n == 0 or spent < budget_s:
+        t0 = time.perf_counter()
+        oracle.attention_direct(h["q"], case.q_dtype, h["k_cache"], h["v_cache"], case.kv_dtype,
+                                h["block_tables"], h["context_lens"], h["cu_query_lens"], case.scale,
+                                case.k_scale, case.v_scale, threads=threads, window=case.window)
+        spent += time.perf_counter() - t0
+        n += 1
+    used = min(threads, case.num_seqs * case.num_kv_heads)   # busy threads: one (request, kv head) task each
+    return {"value": round(kv_bytes * n / spent / 1e9, 4), "unit": "GB/s", "cores": used,
+            "kind": "oracle", "us_per_step": round(spent / n * 1e6, 1),
+            "sample": f"{n} run(s) of the whole configuration (one batch), fp64 direct attention over the "
+                      f"gathered pages, {spent:.1f} s"}
+
+
+def copy_ceiling(dev) -> dict:
+    """A device-to-device copy of 1 GiB (torch's copy kernel), best of 10: read + written bytes over
+    time, the box's measured streaming ceiling beside the 8 TB/s published peak."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(10):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b))
+    del src, dst
+    return {"gbps": round(2 * n / (best * 1e-3) / 1e9, 1), "bytes_moved": 2 * n,
+            "kernel": "torch copy_, 1 GiB device to device, best of 10"}
 
 
 def bench_mixed(args, batches, cu_count):
@@ -152,6 +201,7 @@ def bench_mixed(args, batches, cu_count):
     dec_ms = timed("decode", 8)
     pre_ms = timed("prefill", 8)
     c0, m0 = batches[0], steps[0]
+    ceil = copy_ceiling(stream.device)
     elem = {"f32": 4, "bf16": 2, "fp8": 1}[c0.kv_dtype]
     per_key = c0.num_kv_heads * 2 * c0.head_dim * elem
     lens = c0.context_lens.cpu().numpy().astype(np.int64)
@@ -179,7 +229,9 @@ def bench_mixed(args, batches, cu_count):
                      "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel": "pa_attention over the decode part (decode + merge launches)",
                      "duration_us": round(dec_ms * 1e3, 2), "algorithmic_bytes_per_launch": round(dec_bytes, 1)},
-        "cpu_baseline": None,
+        "copy_ceiling": ceil,
+        "pct_of_copy_ceiling": {"step": round(100.0 * gbps / ceil["gbps"], 1)},
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_case(c0, args.cpu_seconds, all_bytes),
     }
 
 
@@ -498,9 +550,16 @@ def main():
         "cold_cache": cold,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline and pool is not None:
+    ceil = copy_ceiling(dev)
+    result["copy_ceiling"] = ceil
+    result["pct_of_copy_ceiling"] = {"step": round(100.0 * gbps / ceil["gbps"], 1),
+                                     "decode_kernel": round(100.0 * dec_gbps / ceil["gbps"], 1)}
+    if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(pool, args.cpu_seconds, nsteps, win)
+        if pool is not None:
+            result["cpu_baseline"] = cpu_baseline(pool, args.cpu_seconds, nsteps, win)
+        else:
+            result["cpu_baseline"] = cpu_baseline_case(c0, min(args.cpu_seconds, 10.0), float(kv_bytes[0]))
     print(json.dumps(result), flush=True)
 
 
