@@ -36,6 +36,14 @@ SMALL = [
     ("f32_d128_verify", [500, 31, 2], [3, 2, 2], 8, 2, 128, 64, "f32", "f32", 1, 8, 64),
     ("f32_d256_qbf16", [700, 90], [1, 2], 4, 2, 256, 16, "f32", "bf16", 0, 256, 256),
     ("bf16_many_slots", [4096, 4096, 100, 5000], None, 8, 1, 128, 16, "bf16", "bf16", 0, 256, 16),
+    # one query head per kv head (G = 1: one-row blocks), verify rows included
+    ("bf16_g1_verify", [900, 2, 300], [1, 2, 3], 8, 8, 128, 16, "bf16", "bf16", 1, 256, 256),
+    # fp8 at head_dim 64 on 128-token pages, tile 256 = two pages
+    ("fp8_d64_bs128", [5000, 129, 700], None, 8, 2, 64, 128, "fp8", "bf16", 0, 256, 256),
+    # the largest row block: 32 query heads per kv head x 2 tokens = 64 rows
+    ("bf16_g32_64rows", [1200, 64], [2, 1], 32, 1, 128, 16, "bf16", "bf16", 1, 256, 256),
+    # eight kv heads at head_dim 256 (G = 2)
+    ("bf16_hkv8_d256", [800, 3000], [2, 1], 16, 8, 256, 16, "bf16", "bf16", 0, 256, 256),
     # last tile holds fewer keys than the request has query tokens: early tokens see nothing in the
     # wave that owns it while the last token does (regression: such rows must stay (-inf, 0, 0))
     ("bf16_short_last_tile", [257, 513, 258, 769], [3, 3, 2, 4], 8, 2, 128, 16, "bf16", "bf16", 1, 1, 256),
