@@ -218,3 +218,28 @@ def test_all_empty_and_empty_batch():
         torch.cuda.synchronize()
         assert (step.out == 0).all()
         _check_plan(step, ctx, 1, PlanConfig(cu_count=256))
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_batch_beyond_plan_in_place(kv):
+    """600 requests: past the in-place plan's limit (pa_attention then launches the plan kernel) and
+    past the shared-slot table, so every request is one slot streamed by the eight-wave form.
+    Lengths are log-normal with zeros and verify rows; both routes against the oracle."""
+    rng = np.random.default_rng(31)
+    Bn = 600
+    ctx = np.clip(np.rint(np.exp(rng.normal(5.5, 1.2, size=Bn))), 1, 6000).astype(np.int64)
+    ctx[rng.random(Bn) < 0.05] = 0
+    ql = rng.integers(1, 3, size=Bn)
+    ctx = np.maximum(ctx, np.where(ctx > 0, ql, 0))
+    announce(f"attention {Bn} requests {kv}")
+    case = W.build_case(f"beyond_in_place_{kv}", ctx.tolist(), num_q_heads=8, num_kv_heads=2, head_dim=128,
+                        block_size=16, kv_dtype=kv, q_dtype="bf16", seed=77, q_lens=ql.tolist(), pad_rows=3,
+                        device=DEV)
+    cfg = PlanConfig(cu_count=256)
+    got, ref, step = _both_routes(case, cfg)
+    assert step.capacity == Bn                   # one slot per request
+    _assert_same_as_three(got, ref, f"{Bn} requests")
+    _check_plan(step, ctx, case.num_kv_heads, cfg)
+    g = to_f64(got)
+    assert_close(g, oracle_direct(case), tolerance_kind(case), f"{Bn} requests {kv}")
+    assert (g[_zero_rows(case)] == 0.0).all()
