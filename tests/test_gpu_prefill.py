@@ -30,6 +30,10 @@ PREFILL = [
     ("bf16_window50", [300, 1000], [120, 64], 16, 2, 128, 16, "bf16", "bf16", 1, 50),
     ("fp8_d256_window32", [900], [96], 12, 2, 256, 16, "fp8", "bf16", 0, 32),
     ("qf32_tokens_without_keys", [10, 40], [30, 40], 8, 1, 128, 16, "bf16", "f32", 2, 0),
+    # one query head per kv head: 64 tokens per block
+    ("bf16_g1_prompts", [333, 90], [200, 90], 4, 4, 128, 16, "bf16", "bf16", 1, 0),
+    # 32 query heads per kv head: 2 tokens per 64-row block, with a window
+    ("bf16_g32_window", [700, 129], [41, 7], 32, 1, 64, 16, "bf16", "bf16", 0, 100),
 ]
 
 
