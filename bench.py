@@ -259,7 +259,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the decode path has no multi-GPU mode (see DESIGN.md)",
+        print("bench.py measures one GPU: the decode path has no multi-GPU mode (it would shard by kv "
+              "head, each GPU running the same op on its share of the heads)",
               file=sys.stderr)
         sys.exit(2)
 
