@@ -144,6 +144,11 @@ hipError_t launch_merge_d(const MergeArgs& a, bool out_bf16, dim3 grid, hipStrea
         const dim3 g4(grid.x * 4);
         if (out_bf16) hipLaunchKernelGGL((merge_kernel<D, true, 256, 4>), g4, dim3(256), 0, stream, a);
         else hipLaunchKernelGGL((merge_kernel<D, false, 256, 4>), g4, dim3(256), 0, stream, a);
+    } else if (grid.x >= 2048) {
+        // many pairs (large batches, typically with few partials each): one wave per pair, so the
+        // launch fits the compute units in one round instead of queueing 256-thread workgroups
+        if (out_bf16) hipLaunchKernelGGL((merge_kernel<D, true, 64, 1>), grid, dim3(64), 0, stream, a);
+        else hipLaunchKernelGGL((merge_kernel<D, false, 64, 1>), grid, dim3(64), 0, stream, a);
     } else {
         if (out_bf16) hipLaunchKernelGGL((merge_kernel<D, true, 256, 1>), grid, dim3(256), 0, stream, a);
         else hipLaunchKernelGGL((merge_kernel<D, false, 256, 1>), grid, dim3(256), 0, stream, a);
