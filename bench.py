@@ -1,22 +1,32 @@
 """Benchmark of the paged split-KV decode step on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--graph] [--no-cold]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME] [--window W]
+                    [--no-graph] [--no-cold] [--no-cpu-baseline] [--cpu-seconds S] [--step-only]
 
-Workload: the skewed 32-request bf16 decode (Hq 16 / Hkv 2, D 128, pages of 16 tokens).  128 decode
-steps whose in-batch max/min context ratio follows the agentic trace (p50 ~2.5, p90 ~21); every step
-draws its pages at random from a 4 GiB K/V pool, so the 256 MB last-level cache cannot hold a step's
-data across steps.  One timed step = one pa_attention call over one batch (plan, decode and merge; the
-decode launch plans in place, so two launches), inputs resident in HBM.  value = KV bytes read / step
-time (GB/s).  The three-call form (pa_plan + pa_decode + pa_merge) and the form with the merge inside
-the decode launch are timed too and reported beside it, and so is each step between its own events
-with the 256 MB last-level cache evicted before it (a 512 MB write outside the events) and without.
-A 1 GiB device copy gives the box's measured copy ceiling beside the 8 TB/s peak, and the CPU oracle
-is timed on a bounded sample of every workload (cpu_baseline).
+Default workload: the skewed 32-request bf16 decode (Hq 16 / Hkv 2, D 128, pages of 16 tokens): 128
+decode steps whose in-batch max/min context ratio follows the agentic trace (p50 ~2.5, p90 ~21), every
+step drawing its pages at random from a 4 GiB K/V pool so that the 256 MB last-level cache cannot
+carry a step's data to the next.  Inputs are resident in HBM.
 
-The roofline object is for the decode kernel: algorithmic bytes (sum of context lengths x Hkv x 2 x D
-x 2 bytes per launch, averaged over the batches) over its average launch duration, measured with HIP
-events on the launch stream around K pa_decode launches issued back to back over the batches, each
-with its own plan made beforehand.
+One timed step = pa_decode + pa_merge for one attention layer, with the step's plan made once
+beforehand (the pages build the plan once per forward and share it across layers: ROCm/ATOM PR #2366,
+section 3, "Plan lifetime vs cudagraph").  The K timed steps sample the whole step set: whole passes
+over all 128 steps in one seeded order, and for the remainder r < 128 the r steps at the set's
+quantiles (j + 1/2) / r, so any K is a stratified sample (step_order).  value = KV bytes of exactly
+the timed steps / their time (GB/s); ms_per_step = time / K.
+
+Reported beside it: the same step over whole passes of all 128 steps (full_set); a HIP-graph replay
+of it; pa_plan alone (the per-forward refresh); the one-call pa_attention (plan in place, two
+launches) and the three-call form; per-kernel times with events around each launch; each step once
+with the 256 MB last-level cache evicted before it; the decode kernel alone back to back (roofline);
+the read-only ceilings of the same device (pa_probe_read: a contiguous read; pa_probe_gather: exactly
+the decode's K/V bytes over the same plans, with the decode's launch shape, no arithmetic); and the
+CPU oracle on a bounded sample plus one timing per named configuration (cpu_baseline).
+
+The roofline object is for the decode kernel: algorithmic bytes per launch (context length x Hkv x 2 x
+D x element size summed over the batch, averaged over exactly the launches timed) over the mean
+launch duration, measured with HIP events on the launch stream around K launches issued back to back
+over the same step order as the headline.
 """
 from __future__ import annotations
 
@@ -35,76 +45,151 @@ import torch  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "µs/step + achieved KV-read HBM GB/s (% peak), skewed 32-req bf16 decode"
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_skewed_bf16_counters.json")
 DECODE_SRC = os.path.join(ROOT, "paged_split_kv_amd", "csrc", "pa_decode.hip")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_{workload}_counters.json")
 
 
-def decode_source_sha() -> str:
-    with open(DECODE_SRC, "rb") as f:
+# ------------------------------------------------------------------------------------------------
+# step order and the headline arithmetic (host only; tested on the CPU)
+# ------------------------------------------------------------------------------------------------
+
+def step_order(K: int, nsteps: int, seed: int = 0) -> np.ndarray:
+    """Indices of the K timed steps into a step set of nsteps (the skewed set is sorted by ratio):
+    K // nsteps whole passes over every step in one seeded random order, then for the remainder r the
+    r steps at the quantiles (j + 1/2) / r of the set, in a seeded random order."""
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(nsteps)
+    full, r = divmod(int(K), int(nsteps))
+    parts = [perm] * full
+    if r:
+        strat = np.floor((np.arange(r) + 0.5) * nsteps / r).astype(np.int64)
+        parts.append(rng.permutation(strat))
+    return np.concatenate(parts).astype(np.int64) if parts else np.zeros(0, np.int64)
+
+
+def rate(bytes_per_step: np.ndarray, order: np.ndarray, total_ms: float) -> dict:
+    """Throughput of a timed run over `order`: bytes of exactly those steps over the total time."""
+    K = len(order)
+    done = float(np.asarray(bytes_per_step, dtype=np.float64)[order].sum())
+    ms = total_ms / K
+    gbps = done / (total_ms * 1e-3) / 1e9
+    return {"steps": K, "distinct_steps": int(len(np.unique(order))), "bytes": done,
+            "mean_bytes": done / K, "ms_per_step": ms, "us_per_step": ms * 1e3, "gbps": gbps,
+            "pct_peak": 100.0 * gbps / HBM_PEAK_GBPS}
+
+
+def source_sha(path: str) -> str:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def counter_traffic():
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary, if it was taken on
-    the current decode source; else None."""
+def counter_traffic(workload: str):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary of this workload, if
+    it was taken on the current decode source; else None."""
     try:
-        with open(COUNTERS_FILE) as f:
+        with open(COUNTERS_FILE.format(workload=workload)) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
-    if c.get("decode_source_sha") != decode_source_sha():
+    if c.get("decode_source_sha") != source_sha(DECODE_SRC):
         return None
     return c.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(pool, budget_s: float, max_steps: int, window: int = 0):
-    """The CPU oracle (direct fp64 attention over the gathered pages) on a bounded sample of steps."""
+# ------------------------------------------------------------------------------------------------
+# timing helpers
+# ------------------------------------------------------------------------------------------------
+
+def timed(calls, stream, warm_calls=()) -> float:
+    """Run the warm-up calls, then the calls between two events on `stream`, synchronised on both
+    sides; returns the elapsed milliseconds."""
+    for f in warm_calls:
+        f()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for f in calls:
+        f()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b)
+
+
+def read_ceiling(dev, cu_count: int) -> dict:
+    """pa_probe_read over a 2 GiB buffer, best of 10: the device's practical streaming read rate."""
+    from paged_split_kv_amd import probe as P
+
+    n = 2 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    wgs = 2 * cu_count
+    sink = P.sink_for(4 * wgs, dev)
+    stream = torch.cuda.current_stream()
+    best = float("inf")
+    for _ in range(3):
+        P.pa_probe_read(src, wgs, sink)
+    for _ in range(10):
+        best = min(best, timed([lambda: P.pa_probe_read(src, wgs, sink)], stream))
+    del src
+    gbps = n / (best * 1e-3) / 1e9
+    return {"gbps": round(gbps, 1), "pct_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 1), "bytes": n,
+            "kernel": f"pa_probe_read: contiguous 2 GiB, {wgs} workgroups x 256 threads, 16-byte "
+                      "non-temporal loads; best of 10"}
+
+
+# ------------------------------------------------------------------------------------------------
+# CPU oracle timings
+# ------------------------------------------------------------------------------------------------
+
+def _pool_step_host(pool, i):
+    """Host arrays of skewed/sparse step i (pages gathered from the pool, block table renumbered)."""
+    ctx = pool.steps[i]
+    bs = pool.block_size
+    pages = (ctx + bs - 1) // bs
+    bt = pool.block_tables[i].cpu().numpy()
+    used = np.concatenate([bt[b, :pages[b]] for b in range(len(ctx))])
+    idx = torch.from_numpy(used.astype(np.int64)).to(pool.k_cache.device)
+    k = pool.k_cache.index_select(0, idx).cpu().view(torch.int16).numpy().view(np.uint16)
+    v = pool.v_cache.index_select(0, idx).cpu().view(torch.int16).numpy().view(np.uint16)
+    remap = np.full(bt.shape, -1, dtype=np.int32)
+    pos = 0
+    for b in range(len(ctx)):
+        remap[b, :pages[b]] = np.arange(pos, pos + pages[b], dtype=np.int32)
+        pos += pages[b]
+    q = pool.q[i].cpu().view(torch.int16).numpy().view(np.uint16)
+    return q, k, v, remap, ctx.astype(np.int32)
+
+
+def cpu_baseline_pool(pool, budget_s: float, window: int = 0) -> dict:
+    """The CPU oracle (direct fp64 attention over the gathered pages) on a bounded sample of the
+    pool's steps, in seeded random order, until the budget is spent."""
     import oracle
 
     threads = oracle.default_threads()
-    done_bytes = 0
-    spent = 0.0
-    n = 0
-    picks = np.random.default_rng(0).permutation(len(pool.steps))
-    for i in picks[:max_steps]:
-        ctx = pool.steps[i]
-        bs = pool.block_size
-        pages = (ctx + bs - 1) // bs
-        bt = pool.block_tables[i].cpu().numpy()
-        used = np.concatenate([bt[b, :pages[b]] for b in range(len(ctx))])
-        idx = torch.from_numpy(used.astype(np.int64)).to(pool.k_cache.device)
-        k = pool.k_cache.index_select(0, idx).cpu().view(torch.int16).numpy().view(np.uint16)
-        v = pool.v_cache.index_select(0, idx).cpu().view(torch.int16).numpy().view(np.uint16)
-        remap = np.full(bt.shape, -1, dtype=np.int32)
-        pos = 0
-        for b in range(len(ctx)):
-            remap[b, :pages[b]] = np.arange(pos, pos + pages[b], dtype=np.int32)
-            pos += pages[b]
-        q = pool.q[i].cpu().view(torch.int16).numpy().view(np.uint16)
+    done_bytes, spent, n = 0, 0.0, 0
+    for i in np.random.default_rng(0).permutation(len(pool.steps)):
+        q, k, v, remap, ctx = _pool_step_host(pool, i)
         t0 = time.perf_counter()
-        oracle.attention_direct(q, "bf16", k, v, "bf16", remap, ctx.astype(np.int32), None, pool.scale,
-                                threads=threads, window=window)
+        oracle.attention_direct(q, "bf16", k, v, "bf16", remap, ctx, None, pool.scale, threads=threads,
+                                window=window)
         spent += time.perf_counter() - t0
         keys = np.minimum(ctx, window) if window > 0 else ctx
-        done_bytes += int(keys.sum()) * k.shape[1] * 2 * k.shape[3] * 2
+        done_bytes += int(keys.astype(np.int64).sum()) * k.shape[1] * 2 * k.shape[3] * 2
         n += 1
         if spent >= budget_s:
             break
-    # the oracle splits the work into (request, kv head) tasks: no more threads than tasks are busy
     used = min(threads, len(pool.steps[0]) * pool.k_cache.shape[1])
-    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": used,
-            "kind": "oracle",
+    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": used, "kind": "oracle",
             "us_per_step": round(spent / n * 1e6, 1),
             "sample": f"{n} of the {len(pool.steps)} steps (seeded random order, stopped after "
-                      f"{budget_s:.0f} s), fp64 direct attention over the gathered pages, {spent:.1f} s"}
+                      f"{budget_s:.0f} s of oracle time), fp64 direct attention over the gathered pages, "
+                      f"{spent:.1f} s"}
 
 
-def cpu_baseline_case(case, budget_s: float, kv_bytes: float):
-    """The CPU oracle (direct fp64 attention) on one full-size configuration, repeated while the
-    budget lasts (at least once); the host copy of the case is made before the clock starts."""
+def _oracle_case_us(case, threads, budget_s: float = 1.0):
     import oracle
 
-    threads = oracle.default_threads()
     h = case.host()
     spent, n = 0.0, 0
     while n == 0 or spent < budget_s:
@@ -114,35 +199,51 @@ def cpu_baseline_case(case, budget_s: float, kv_bytes: float):
                                 case.k_scale, case.v_scale, threads=threads, window=case.window)
         spent += time.perf_counter() - t0
         n += 1
-    used = min(threads, case.num_seqs * case.num_kv_heads)   # busy threads: one (request, kv head) task each
-    return {"value": round(kv_bytes * n / spent / 1e9, 4), "unit": "GB/s", "cores": used,
-            "kind": "oracle", "us_per_step": round(spent / n * 1e6, 1),
-            "sample": f"{n} run(s) of the whole configuration (one batch), fp64 direct attention over the "
-                      f"gathered pages, {spent:.1f} s"}
+    return spent / n * 1e6, min(threads, case.num_seqs * case.num_kv_heads), n
 
 
-def copy_ceiling(dev) -> dict:
-    """A device-to-device copy of 1 GiB (torch's copy kernel), best of 10: read + written bytes over
-    time, the box's measured streaming ceiling beside the 8 TB/s published peak."""
-    n = 1 << 30
-    src = torch.empty(n, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    best = float("inf")
-    for _ in range(10):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        dst.copy_(src)
-        b.record()
-        torch.cuda.synchronize()
-        best = min(best, a.elapsed_time(b))
-    del src, dst
-    return {"gbps": round(2 * n / (best * 1e-3) / 1e9, 1), "bytes_moved": 2 * n,
-            "kernel": "torch copy_, 1 GiB device to device, best of 10"}
+def cpu_oracle_per_config(dev, pool=None) -> dict:
+    """The oracle's µs per step on every named configuration: tiny; the skewed steps nearest the p50
+    and p90 ratio and the step with most tokens; long; verify; fp8 (each run once, or repeated for
+    about a second when fast)."""
+    import oracle
+    from paged_split_kv_amd import workloads as W
 
+    threads = oracle.default_threads()
+    out = {}
+    cases = [("tiny_fp32", None)]
+    steps = W.skewed_step_set()
+    for tag, idx in W.skewed_named_steps(steps).items():
+        cases.append((f"skewed_{tag}", idx))
+    cases += [("long_bf16", None), ("verify_bf16", None), ("fp8_kv", None)]
+    for name, idx in cases:
+        if name.startswith("skewed"):
+            c = W.make_config("skewed_bf16", device=dev, step=idx)
+        else:
+            c = W.make_config(name, device=dev)
+        us, busy, runs = _oracle_case_us(c, threads)
+        out[name] = {"us_per_step": round(us, 1), "runs": runs, "kv_bytes": c.kv_bytes(), "busy_threads": busy,
+                     "kv_gbps": round(c.kv_bytes() / (us * 1e-6) / 1e9, 3)}
+        del c
+    return out
+
+
+def cpu_baseline_case(case, budget_s: float, kv_bytes: float) -> dict:
+    """The CPU oracle on one full-size configuration, repeated while the budget lasts (at least once);
+    the host copy of the case is made before the clock starts."""
+    import oracle
+
+    threads = oracle.default_threads()
+    us, busy, n = _oracle_case_us(case, threads, budget_s)
+    return {"value": round(kv_bytes / (us * 1e-6) / 1e9, 4), "unit": "GB/s", "cores": busy, "kind": "oracle",
+            "us_per_step": round(us, 1),
+            "sample": f"the whole configuration (one batch) {n} time(s), fp64 direct attention over the "
+                      f"gathered pages"}
+
+
+# ------------------------------------------------------------------------------------------------
+# mixed batches
+# ------------------------------------------------------------------------------------------------
 
 def bench_mixed(args, batches, cu_count):
     """The decode-first split of a mixed batch: one pa_attention_mixed call per step (decode and
@@ -155,85 +256,130 @@ def bench_mixed(args, batches, cu_count):
     steps = [MixedStep(c, 1, PlanConfig(cu_count=cu_count), concurrent=True) for c in batches]
     m_side = [m.side for m in steps]
     for m in steps:
-        m.side = None                  # the two-call forms run on one stream unless timed otherwise
+        m.side = None
     n = len(batches)
     K = args.steps
+    order = np.arange(K) % n
 
     def part(i, which):
-        c, m = batches[i % n], steps[i % n]
+        c, m = batches[i], steps[i]
         if which == "step":
             m.one_call = True
             m.run(c, stream)
             m.one_call = False
-            return
-        if which == "two_calls":
+        elif which == "two_calls":
             m.run(c, stream)
-            return
-        if which == "two_streams":
-            m.side = m_side[i % n]
+        elif which == "two_streams":
+            m.side = m_side[i]
             m.run(c, stream)
             m.side = None
-            return
-        if which == "decode" and m.dec is not None:
+        elif which == "decode" and m.dec is not None:
             m.dec.attention(c.q[:m.ndt], c.k_cache, c.v_cache, c.kv_dtype, c.block_tables[:m.nd],
                             c.context_lens[:m.nd], scale=c.scale, cu_query_lens=c.cu_query_lens[:m.nd + 1],
                             sliding_window=c.window)
-        if which == "prefill":
+        elif which == "prefill":
             B.pa_prefill(c.q, c.k_cache, c.v_cache, c.kv_dtype, c.block_tables[m.nd:], c.context_lens[m.nd:],
                          c.cu_query_lens[m.nd:], m.out, scale=c.scale, sliding_window=c.window)
 
-    def timed(which, warm):
-        for i in range(warm):
-            part(i, which)
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record(stream)
-        for i in range(K):
-            part(i, which)
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / K
+    def run(which, warm):
+        return timed([lambda i=i: part(i, which) for i in order], stream,
+                     [lambda i=i: part(i % n, which) for i in range(warm)])
 
-    step_ms = timed("step", args.warmup)
-    two_calls_ms = timed("two_calls", 8)
-    two_ms = timed("two_streams", 8)
-    dec_ms = timed("decode", 8)
-    pre_ms = timed("prefill", 8)
+    step_ms = run("step", args.warmup)
     c0, m0 = batches[0], steps[0]
-    ceil = copy_ceiling(stream.device)
     elem = {"f32": 4, "bf16": 2, "fp8": 1}[c0.kv_dtype]
     per_key = c0.num_kv_heads * 2 * c0.head_dim * elem
     lens = c0.context_lens.cpu().numpy().astype(np.int64)
-    dec_bytes = float(lens[:m0.nd].sum() * per_key)
-    all_bytes = float(lens.sum() * per_key)
-    gbps = all_bytes / (step_ms * 1e-3) / 1e9
-    dec_gbps = dec_bytes / (dec_ms * 1e-3) / 1e9
+    all_bytes = np.full(n, float(lens.sum() * per_key))
+    if args.step_only:
+        head = rate(all_bytes, order, step_ms)
+        return {"metric": "µs/step, mixed batch through the decode-first split (one pa_attention_mixed call)",
+                "value": round(head["gbps"], 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+                "ms_per_step": round(head["ms_per_step"], 6), "us_per_step": round(head["us_per_step"], 2),
+                "all_kv_bytes_per_step": float(all_bytes[0]),
+                "decode_kv_bytes_per_step": float(lens[:m0.nd].sum() * per_key)}
+    two_calls_ms = run("two_calls", 8)
+    two_ms = run("two_streams", 8)
+    dec_ms = run("decode", 8)
+    pre_ms = run("prefill", 8)
+    dec_bytes = np.full(n, float(lens[:m0.nd].sum() * per_key))
+    head = rate(all_bytes, order, step_ms)
+    dec = rate(dec_bytes, order, dec_ms)
     return {
         "metric": "µs/step + achieved KV-read HBM GB/s (% peak), mixed batch through the decode-first split",
-        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
-        "ms_per_step": round(step_ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
+        "value": round(head["gbps"], 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"7 decodes at 16384 tokens + a new 100-token prompt, decodes first, Hq 12 / Hkv 2, "
                                f"D 256, page 16, bf16; {n} independent copies rotated",
                    "num_decodes": m0.nd, "decode_rows": m0.ndt, "threshold": 1,
                    "planner": {"budget": "2 x CU", "cu_count": cu_count, "max_partitions": 256, "tile_tokens": 256}},
-        "us_per_step": round(step_ms * 1e3, 2),
-        "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 1),
+        "us_per_step": round(head["us_per_step"], 2), "pct_hbm_peak": round(head["pct_peak"], 1),
         "step": "pa_split_decode_first on the host; pa_attention_mixed: the decodes (planned in place) and "
                 "the prompt's query blocks in one launch, then pa_merge",
-        "decode_part_us": round(dec_ms * 1e3, 2), "prefill_part_us": round(pre_ms * 1e3, 2),
-        "two_calls_us_per_step": round(two_calls_ms * 1e3, 2),
-        "two_streams_us_per_step": round(two_ms * 1e3, 2),
-        "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+        "decode_part_us": round(dec["us_per_step"], 2), "prefill_part_us": round(pre_ms * 1e3 / K, 2),
+        "two_calls_us_per_step": round(two_calls_ms * 1e3 / K, 2),
+        "two_streams_us_per_step": round(two_ms * 1e3 / K, 2),
+        "roofline": {"bound": "hbm", "achieved": round(dec["gbps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(dec["gbps"] / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel": "pa_attention over the decode part (decode + merge launches)",
-                     "duration_us": round(dec_ms * 1e3, 2), "algorithmic_bytes_per_launch": round(dec_bytes, 1)},
-        "copy_ceiling": ceil,
-        "pct_of_copy_ceiling": {"step": round(100.0 * gbps / ceil["gbps"], 1)},
-        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_case(c0, args.cpu_seconds, all_bytes),
+                     "duration_us": round(dec["us_per_step"], 2),
+                     "algorithmic_bytes_per_launch": round(dec["mean_bytes"], 1)},
+        "read_ceiling": read_ceiling(stream.device, cu_count),
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_case(c0, args.cpu_seconds,
+                                                                             float(all_bytes[0])),
     }
 
+
+def bench_prefill(args, batches, cu_count):
+    """A prompt chunk behind a long prefix through pa_prefill alone: every query token of the chunk
+    reads all the keys it sees.  Bytes counted: the request's K/V once (the algorithmic bytes); the
+    rocprofv3 FETCH_SIZE of the same command gives the re-read factor of the query blocks."""
+    from paged_split_kv_amd import binding as B
+
+    stream = torch.cuda.current_stream()
+    n = len(batches)
+    K = args.steps
+    order = np.arange(K) % n
+    outs = [torch.empty_like(c.q) for c in batches]
+
+    def call(i):
+        c = batches[i]
+        B.pa_prefill(c.q, c.k_cache, c.v_cache, c.kv_dtype, c.block_tables, c.context_lens, c.cu_query_lens,
+                     outs[i], scale=c.scale, sliding_window=c.window)
+
+    ms = timed([lambda i=i: call(i) for i in order], stream, [lambda i=i: call(i % n) for i in range(args.warmup)])
+    c0 = batches[0]
+    kv = np.array([float(c.kv_bytes()) for c in batches])
+    r = rate(kv, order, ms)
+    G = c0.num_q_heads // c0.num_kv_heads
+    from paged_split_kv_amd.binding import PA_MAX_GROUP_ROWS  # noqa: F401
+    result = {
+        "metric": "µs/step + achieved KV-read HBM GB/s (% peak), prompt chunk behind a long prefix (pa_prefill)",
+        "value": round(r["gbps"], 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"one request: a {int(np.diff(c0.cu_query_lens.cpu().numpy())[0])}-token prompt chunk "
+                               f"behind a {int(c0.context_lens[0].item()) - int(np.diff(c0.cu_query_lens.cpu().numpy())[0])}"
+                               f"-token prefix, Hq {c0.num_q_heads} / Hkv {c0.num_kv_heads}, D {c0.head_dim}, page "
+                               f"{c0.block_size}, bf16; {n} independent copies rotated",
+                   "group": G},
+        "us_per_step": round(r["us_per_step"], 2), "pct_hbm_peak": round(r["pct_peak"], 1),
+        "step": "pa_prefill over the chunk's query blocks",
+        "roofline": {"bound": "hbm", "achieved": round(r["gbps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(r["gbps"] / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "pa_prefill",
+                     "duration_us": round(r["us_per_step"], 3),
+                     "algorithmic_bytes_per_launch": round(r["mean_bytes"], 1),
+                     "note": "algorithmic bytes count the request's K/V once"},
+    }
+    if not args.step_only:
+        result["read_ceiling"] = read_ceiling(stream.device, cu_count)
+    return result
+
+
+# ------------------------------------------------------------------------------------------------
+# the decode workloads
+# ------------------------------------------------------------------------------------------------
 
 def main():
     ap = argparse.ArgumentParser()
@@ -242,20 +388,25 @@ def main():
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--graph", action="store_true", help="also time a HIP-graph replay of the steps")
+    ap.add_argument("--graph", dest="graph", action="store_true", default=True,
+                    help="time a HIP-graph replay of the step set too (the default)")
+    ap.add_argument("--no-graph", dest="graph", action="store_false", help="skip the HIP-graph replay")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the per-step timing with the last-level cache evicted between steps")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time only the headline step (for profiler runs: warm-up, then K steps)")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="run a 1 GiB device copy first (reference kernel for the HBM counters)")
+                    help="run a 1 GiB device copy first (the reference kernel for the HBM counters)")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window in keys per query token (0 = none); the bytes counted are the "
                          "windowed ranges")
-    ap.add_argument("--workload", choices=("skewed", "sparse", "long", "verify", "fp8", "mixed"),
+    ap.add_argument("--workload", choices=("skewed", "sparse", "long", "verify", "fp8", "mixed", "prefill"),
                     default="skewed",
                     help="skewed: the 32-request agentic batch (default, the headline metric); "
                          "sparse: 16 near-uniform top-k requests with a partition cap of 8; "
                          "long / verify / fp8: the other full-size configurations, reported beside it; "
-                         "mixed: 7 decodes at 16k + a 100-token prompt through the decode-first split")
+                         "mixed: 7 decodes at 16k + a 100-token prompt through the decode-first split; "
+                         "prefill: a 512-token prompt chunk behind a 16384-token prefix through pa_prefill")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -265,10 +416,12 @@ def main():
         sys.exit(2)
 
     from paged_split_kv_amd import binding as B
+    from paged_split_kv_amd import probe as P
     from paged_split_kv_amd import workloads as W
-    from paged_split_kv_amd.runner import DecodeStep, MixedStep, PlanConfig
+    from paged_split_kv_amd.runner import DecodeStep, PlanConfig
 
     B.load()
+    P.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.calibrate_copy:
@@ -281,6 +434,7 @@ def main():
     win = args.window
     cu_count = B.pa_device_cu_count(0)
     pool = None
+    T = 256
     if args.workload in ("skewed", "sparse"):
         print(f"[bench] building the 4 GiB page pool and the {args.workload} steps", file=sys.stderr, flush=True)
         if args.workload == "skewed":
@@ -289,8 +443,9 @@ def main():
         else:
             pool = W.skewed_pool(dev, steps=W.sparse_lengths(64, 16, seed=11))
             max_parts = 8
-        batches = [W.Case(f"{args.workload}_{i}", pool.q[i], pool.k_cache, pool.v_cache, "bf16",
-                          pool.block_tables[i], pool.context_lens[i], None, 1, pool.scale)
+        batches = [W.Case(name=f"{args.workload}_{i}", q=pool.q[i], k_cache=pool.k_cache, v_cache=pool.v_cache,
+                          kv_dtype="bf16", block_tables=pool.block_tables[i], context_lens=pool.context_lens[i],
+                          cu_query_lens=None, max_q_len=1, scale=pool.scale)
                    for i in range(pool.steps.shape[0])]
         lens = [pool.steps[i] for i in range(len(batches))]
         qlens = [np.ones_like(x) for x in lens]
@@ -298,14 +453,17 @@ def main():
         # one named configuration; independent copies (own pages and values) are rotated so that
         # consecutive steps do not find each other's pages in the 256 MB last-level cache
         if args.workload == "mixed":
-            name = "mixed_7x16k_prompt100"
             make = lambda sd: W.make_mixed_case(device=dev, seed=sd)
+            first = make(5)
+        elif args.workload == "prefill":
+            make = lambda sd: W.make_prefill_chunk_case(device=dev, seed=sd)
+            first = make(6)
         else:
             name = {"long": "long_bf16", "verify": "verify_bf16", "fp8": "fp8_kv"}[args.workload]
             make = lambda sd: W.make_config(name, device=dev, seed=sd)
-        first = make(None) if args.workload != "mixed" else make(5)
+            first = make(None)
         copies = max(1, min(8, -(-(640 << 20) // first.kv_bytes())))
-        print(f"[bench] building {copies} copies of {name}", file=sys.stderr, flush=True)
+        print(f"[bench] building {copies} copies of the {args.workload} workload", file=sys.stderr, flush=True)
         batches = [first] + [make(1000 + c) for c in range(1, copies)]
         max_parts = 256
         lens = [c.context_lens.cpu().numpy() for c in batches]
@@ -316,10 +474,14 @@ def main():
     if args.workload == "mixed":
         print(json.dumps(bench_mixed(args, batches, cu_count)), flush=True)
         return
+    if args.workload == "prefill":
+        print(json.dumps(bench_prefill(args, batches, cu_count)), flush=True)
+        return
     nsteps = len(batches)
     c0 = batches[0]
     B_, Hq, D, Hkv = c0.num_seqs, c0.num_q_heads, c0.head_dim, c0.num_kv_heads
-    step = DecodeStep.for_case(c0, PlanConfig(cu_count=cu_count, max_partitions=max_parts))
+    cfg = PlanConfig(cu_count=cu_count, max_partitions=max_parts, tile_tokens=T)
+    step = DecodeStep.for_case(c0, cfg)
     elem = {"f32": 4, "bf16": 2, "fp8": 1}[c0.kv_dtype]
 
     def keys_read(S, L):
@@ -328,168 +490,44 @@ def main():
 
     keys = np.array([keys_read(np.asarray(x, np.int64), np.asarray(l, np.int64)).sum()
                      for x, l in zip(lens, qlens)])
-    kv_bytes = keys * Hkv * 2 * D * elem                                    # per step
+    kv_bytes = (keys * Hkv * 2 * D * elem).astype(np.float64)          # per step
     stream = torch.cuda.current_stream()
-
-    def run(i, ev=None, mode="attention"):
-        """One step over batch i.  attention: one pa_attention call (the decode plans in place, then
-        the merge: two launches).  three: pa_plan, pa_decode writing partial states, pa_merge.
-        fused: pa_plan, then pa_decode with the merge inside its launch."""
-        c = batches[i % nsteps]
-        if mode == "attention":
-            step.attention(c.q, c.k_cache, c.v_cache, c.kv_dtype, c.block_tables, c.context_lens,
-                           scale=c.scale, cu_query_lens=c.cu_query_lens, k_scale=c.k_scale,
-                           v_scale=c.v_scale, sliding_window=win)
-            return
-        if ev is not None:
-            ev[0].record(stream)
-        step.plan(c.context_lens, cu_query_lens=c.cu_query_lens, sliding_window=win)
-        if ev is not None:
-            ev[1].record(stream)
-        step.decode(c.q, c.k_cache, c.v_cache, c.kv_dtype, c.block_tables, c.context_lens, scale=c.scale,
-                    cu_query_lens=c.cu_query_lens, k_scale=c.k_scale, v_scale=c.v_scale,
-                    merge=mode == "fused", sliding_window=win)
-        if ev is not None:
-            ev[2].record(stream)
-        if mode == "three":
-            step.merge(c.cu_query_lens)
-        if ev is not None:
-            ev[3].record(stream)
-
-    def timed(mode, warm=8):
-        for i in range(warm):
-            run(i, mode=mode)
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record(stream)
-        for i in range(K):
-            run(i, mode=mode)
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b)
-
     K = args.steps
-    for i in range(args.warmup):
-        run(i)
-    torch.cuda.synchronize()
+    order = step_order(K, nsteps)
+    full_order = step_order(4 * nsteps, nsteps, seed=1)                # four whole passes
 
-    # the timed region: K steps of the whole path, synchronised on both sides
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    for i in range(K):
-        run(i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    plain_ms = start.elapsed_time(end)
-    bytes_done = float(sum(kv_bytes[i % nsteps] for i in range(K)))
-
-    # per-kernel durations: the three-call form of the same steps with events around each launch
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
-    for i in range(8):
-        run(i, mode="three")
-    torch.cuda.synchronize()
-    for i in range(K):
-        run(i, evs[i], mode="three")
-    torch.cuda.synchronize()
-    plan_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    mrg_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
-    step_ms = plan_ms + dec_ms + mrg_ms
-
-    # the decode kernel alone: launches back to back over the batches, each with its own plan made
-    # beforehand, so consecutive launches read different pages and no event sits between them
+    # every step's plan, made once beforehand (as a forward shares one plan across its layers)
     plans = []
     for c in batches:
-        w, r, n = B.pa_plan(c.context_lens, Hkv, cu_count=cu_count, max_partitions=max_parts,
+        w, r, n = B.pa_plan(c.context_lens, Hkv, cu_count=cu_count, max_partitions=max_parts, tile_tokens=T,
                             capacity=step.capacity, cu_query_lens=c.cu_query_lens, sliding_window=win)
-        plans.append((w, n))
+        plans.append((w, r, n))
     torch.cuda.synchronize()
+    ws, out = step.workspace, step.out
 
-    def decode_only(i):
-        c = batches[i % nsteps]
-        w, n = plans[i % nsteps]
-        B.pa_decode(c.q, c.k_cache, c.v_cache, c.kv_dtype, c.block_tables, c.context_lens, w, n, step.workspace,
-                    scale=c.scale, cu_query_lens=c.cu_query_lens, max_q_len=c.max_q_len, k_scale=c.k_scale,
-                    v_scale=c.v_scale, sliding_window=win)
+    def dec_call(i, prepare=True):
+        c, (w, r, n) = batches[i], plans[i]
+        return B.pa_decode(c.q, c.k_cache, c.v_cache, c.kv_dtype, c.block_tables, c.context_lens, w, n, ws,
+                           scale=c.scale, cu_query_lens=c.cu_query_lens, max_q_len=c.max_q_len, k_scale=c.k_scale,
+                           v_scale=c.v_scale, tile_tokens=T, sliding_window=win, prepare=prepare)
 
-    for i in range(8):
-        decode_only(i)
-    da = torch.cuda.Event(enable_timing=True)
-    db = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    da.record(stream)
-    for i in range(K):
-        decode_only(i)
-    db.record(stream)
-    torch.cuda.synchronize()
-    decode_ms = da.elapsed_time(db) / K
+    def mrg_call(i, prepare=True):
+        c, (w, r, n) = batches[i], plans[i]
+        return B.pa_merge(out, r, ws, capacity=step.capacity, cu_query_lens=c.cu_query_lens,
+                          max_q_len=c.max_q_len, prepare=prepare)
 
-    three_ms = timed("three")          # pa_plan + pa_decode + pa_merge, no events in between
-    fused_ms = timed("fused")          # pa_plan + pa_decode with the merge in its launch
+    dec_p = [dec_call(i) for i in range(nsteps)]
+    mrg_p = [mrg_call(i) for i in range(nsteps)]
 
-    graph = None
-    if args.graph:
-        g = torch.cuda.CUDAGraph()
-        cap = torch.cuda.Stream()
-        cap.wait_stream(stream)
-        with torch.cuda.stream(cap):
-            with torch.cuda.graph(g, stream=cap):
-                for i in range(nsteps):
-                    run(i)
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        gs = torch.cuda.Event(enable_timing=True)
-        ge = torch.cuda.Event(enable_timing=True)
-        reps = max(1, K // nsteps)
-        gs.record(stream)
-        for _ in range(reps):
-            g.replay()
-        ge.record(stream)
-        torch.cuda.synchronize()
-        g_ms = gs.elapsed_time(ge) / (reps * nsteps)
-        graph = {"us_per_step": round(g_ms * 1e3, 2),
-                 "kv_gbps": round(float(kv_bytes.mean()) / (g_ms * 1e-3) / 1e9, 1)}
+    def headline(i):
+        dec_p[i]()
+        mrg_p[i]()
 
-    # one step per batch with events around it, each after a 512 MB write that evicts the 256 MB
-    # last-level cache (outside the events), and the same without the write
-    cold = None
-    if args.workload == "skewed" and not args.no_cold:
-        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-
-        def per_step(evict):
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(nsteps)]
-            for i in range(nsteps):
-                if evict:
-                    scratch.fill_(i & 0xff)
-                evs[i][0].record(stream)
-                run(i)
-                evs[i][1].record(stream)
-            torch.cuda.synchronize()
-            return np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
-
-        per_step(True)                                # warm-up of the pattern
-        t_cold, t_warm = per_step(True), per_step(False)
-        del scratch
-        cold = {"steps": nsteps,
-                "evicted_us_mean": round(float(t_cold.mean()), 2),
-                "evicted_us_p50": round(float(np.median(t_cold)), 2),
-                "evicted_us_p90": round(float(np.quantile(t_cold, 0.9)), 2),
-                "evicted_kv_gbps": round(float(kv_bytes.mean()) / (float(t_cold.mean()) * 1e-6) / 1e9, 1),
-                "not_evicted_us_mean": round(float(t_warm.mean()), 2),
-                "note": "pa_attention per step between its own events; 512 MB written before each "
-                        "evicted step, outside its events"}
-
-    us_step = plain_ms * 1e3 / K
-    gbps = bytes_done / (plain_ms * 1e-3) / 1e9
-    dec_gbps = float(kv_bytes.mean()) / (decode_ms * 1e-3) / 1e9
-    traffic = counter_traffic()
+    warm = [lambda i=i: headline(i % nsteps) for i in range(args.warmup)]
+    t0 = time.perf_counter()
+    head_ms = timed([lambda i=i: headline(i) for i in order], stream, warm)
+    wall = time.perf_counter() - t0
+    head = rate(kv_bytes, order, head_ms)
     if args.workload == "skewed" and win == 0:
         metric = METRIC
         workload = ("skewed 32-request bf16 decode, Hq 16 / Hkv 2, D 128, page 16, 128 stratified steps "
@@ -512,55 +550,177 @@ def main():
         workload = f"{desc}; {nsteps} independent copies rotated" + (f"; window {win}" if win else "")
     result = {
         "metric": metric,
-        "value": round(gbps, 1),
+        "value": round(head["gbps"], 1),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": round(plain_ms / K, 5),
+        "ms_per_step": round(head["ms_per_step"], 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": c0.kv_dtype if c0.kv_dtype != "fp8" else "fp8 KV, bf16 MFMA",
         "data": "synthetic",
-        "config": {"workload": workload, "sliding_window": win,
-                   "num_seqs": B_, "max_q_len": c0.max_q_len,
-                   "mean_tokens_per_step": round(float(np.mean([x.sum() for x in lens])), 1),
+        "config": {"workload": workload, "sliding_window": win, "num_seqs": B_, "max_q_len": c0.max_q_len,
+                   "timed_steps": {"count": K, "distinct": head["distinct_steps"], "of": nsteps,
+                                   "rule": "whole passes over every step in a seeded order, then the "
+                                           "remainder at the set's quantiles (j + 1/2) / r",
+                                   "mean_kv_bytes": round(head["mean_bytes"], 1),
+                                   "set_mean_kv_bytes": round(float(kv_bytes.mean()), 1)},
                    "mean_keys_read_per_step": round(float(keys.mean()), 1),
                    "planner": {"budget": "2 x CU", "cu_count": cu_count, "max_partitions": max_parts,
-                               "tile_tokens": 256}},
-        "us_per_step": round(us_step, 2),
-        "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 1),
-        "step": "pa_attention: the decode launch plans in place, then pa_merge",
-        "three_call_us_per_step": round(three_ms * 1e3 / K, 2),
-        "merge_in_decode_launch_us_per_step": round(fused_ms * 1e3 / K, 2),
-        "evented_three_call_us_p50": round(float(np.median(step_ms)) * 1e3, 2),
-        "evented_three_call_us_p90": round(float(np.quantile(step_ms, 0.9)) * 1e3, 2),
-        "kernel_us": {"pa_decode_back_to_back": round(decode_ms * 1e3, 2),
-                      "evented": {"pa_plan": round(float(plan_ms.mean()) * 1e3, 2),
-                                  "pa_decode": round(float(dec_ms.mean()) * 1e3, 2),
-                                  "pa_merge": round(float(mrg_ms.mean()) * 1e3, 2)}},
+                               "tile_tokens": T, "capacity": step.capacity}},
+        "us_per_step": round(head["us_per_step"], 2),
+        "pct_hbm_peak": round(head["pct_peak"], 1),
+        "step": "pa_decode + pa_merge (two launches), each step's plan made once beforehand",
         "timed_wall_s": round(wall, 3),
-        "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic if args.workload == "skewed" and win == 0 else None,
+    }
+    if args.step_only:
+        print(json.dumps(result), flush=True)
+        return
+
+    # the decode kernel alone, back to back over the same order (the roofline kernel)
+    dec_ms = timed([lambda i=i: dec_p[i]() for i in order], stream, [lambda: dec_p[0]()] * 8)
+    dec = rate(kv_bytes, order, dec_ms)
+    # the decode-shaped gather over the same plans and order: the same K/V bytes, no arithmetic
+    sink = P.sink_for(4 * step.capacity * Hkv, dev)
+    gat_p = [P.pa_probe_gather(c.k_cache, c.v_cache, c.kv_dtype, c.block_tables, c.context_lens, w, n, sink,
+                               tile_tokens=T, prepare=True) for c, (w, r, n) in zip(batches, plans)]
+    gat_ms = timed([lambda i=i: gat_p[i]() for i in order], stream, [lambda: gat_p[0]()] * 8)
+    gat = rate(kv_bytes, order, gat_ms)
+    # the headline step over four whole passes of the set
+    full = rate(kv_bytes, full_order, timed([lambda i=i: headline(i) for i in full_order], stream))
+    # the plan alone (its per-forward refresh), the one-call and three-call forms, same order
+    plan_p = [B.pa_plan(c.context_lens, Hkv, cu_count=cu_count, max_partitions=max_parts, tile_tokens=T,
+                        capacity=step.capacity, work_info=step.work_info, reduce_info=step.reduce_info,
+                        num_work=step.num_work, cu_query_lens=c.cu_query_lens, sliding_window=win, prepare=True)
+              for c in batches]
+    plan_ms = timed([lambda i=i: plan_p[i]() for i in order], stream, [lambda: plan_p[0]()] * 8)
+    att_p = [B.pa_attention(c.q, c.k_cache, c.v_cache, c.kv_dtype, c.block_tables, c.context_lens, step.work_info,
+                            step.reduce_info, step.num_work, ws, out, scale=c.scale, cu_count=cu_count,
+                            max_partitions=max_parts, tile_tokens=T, cu_query_lens=c.cu_query_lens,
+                            max_q_len=c.max_q_len, k_scale=c.k_scale, v_scale=c.v_scale, sliding_window=win,
+                            prepare=True) for c in batches]
+    att_ms = timed([lambda i=i: att_p[i]() for i in order], stream, [lambda: att_p[0]()] * 8)
+    dec_s = [B.pa_decode(c.q, c.k_cache, c.v_cache, c.kv_dtype, c.block_tables, c.context_lens, step.work_info,
+                         step.num_work, ws, scale=c.scale, cu_query_lens=c.cu_query_lens, max_q_len=c.max_q_len,
+                         k_scale=c.k_scale, v_scale=c.v_scale, tile_tokens=T, sliding_window=win, prepare=True)
+             for c in batches]
+    mrg_s = [B.pa_merge(out, step.reduce_info, ws, capacity=step.capacity, cu_query_lens=c.cu_query_lens,
+                        max_q_len=c.max_q_len, prepare=True) for c in batches]
+
+    def three(i):
+        plan_p[i]()
+        dec_s[i]()
+        mrg_s[i]()
+
+    three_ms = timed([lambda i=i: three(i) for i in order], stream, [lambda: three(0)] * 8)
+
+    # per-kernel durations with events around each launch of the headline step
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(len(order))]
+    torch.cuda.synchronize()
+    for e, i in zip(evs, order):
+        e[0].record(stream)
+        dec_p[i]()
+        e[1].record(stream)
+        mrg_p[i]()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    ev_dec = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
+    ev_mrg = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
+
+    graph = None
+    if args.graph:
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(nsteps):
+                    dec_call(i, prepare=False)
+                    mrg_call(i, prepare=False)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        reps = 4
+        g_ms = timed([g.replay] * reps, stream)
+        gr = rate(kv_bytes, np.tile(np.arange(nsteps), reps), g_ms)
+        graph = {"us_per_step": round(gr["us_per_step"], 2), "kv_gbps": round(gr["gbps"], 1),
+                 "pct_peak": round(gr["pct_peak"], 1),
+                 "replayed": f"{reps} replays of one graph holding all {nsteps} steps (decode + merge each)"}
+
+    cold = None
+    if args.workload == "skewed" and not args.no_cold:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+        def per_step(evict):
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(nsteps)]
+            for i in range(nsteps):
+                if evict:
+                    scratch.fill_(i & 0xff)
+                ev[i][0].record(stream)
+                headline(i)
+                ev[i][1].record(stream)
+            torch.cuda.synchronize()
+            return np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
+
+        per_step(True)
+        t_cold, t_warm = per_step(True), per_step(False)
+        del scratch
+        cold = {"steps": nsteps,
+                "evicted_us_mean": round(float(t_cold.mean()), 2),
+                "evicted_us_p50": round(float(np.median(t_cold)), 2),
+                "evicted_us_p90": round(float(np.quantile(t_cold, 0.9)), 2),
+                "evicted_kv_gbps": round(float(kv_bytes.sum()) / (float(t_cold.sum()) * 1e-6) / 1e9, 1),
+                "not_evicted_us_mean": round(float(t_warm.mean()), 2),
+                "note": "each step (decode + merge) between its own events; 512 MB written before each "
+                        "evicted step, outside its events"}
+
+    traffic = counter_traffic(args.workload) if win == 0 else None
+    rc = read_ceiling(dev, cu_count)
+    result.update({
+        "full_set": {"steps": full["steps"], "distinct": full["distinct_steps"],
+                     "us_per_step": round(full["us_per_step"], 2), "kv_gbps": round(full["gbps"], 1),
+                     "pct_peak": round(full["pct_peak"], 1),
+                     "note": "the headline step over four whole passes of every step, seeded order"},
+        "pa_plan_us": round(plan_ms * 1e3 / K, 2),
+        "plan_decode_merge_us_per_step": round(three_ms * 1e3 / K, 2),
+        "pa_attention_us_per_step": round(att_ms * 1e3 / K, 2),
+        "kernel_us": {"pa_decode_back_to_back": round(dec["us_per_step"], 2),
+                      "decode_shaped_gather_back_to_back": round(gat["us_per_step"], 2),
+                      "evented": {"pa_decode": round(float(ev_dec.mean()), 2),
+                                  "pa_merge": round(float(ev_mrg.mean()), 2),
+                                  "step_p50": round(float(np.median(ev_dec + ev_mrg)), 2),
+                                  "step_p90": round(float(np.quantile(ev_dec + ev_mrg, 0.9)), 2)}},
+        "roofline": {"bound": "hbm", "achieved": round(dec["gbps"], 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(dec["gbps"] / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
                      "kernel": "pa_decode",
-                     "duration_us": round(decode_ms * 1e3, 2),
-                     "algorithmic_bytes_per_launch": round(float(kv_bytes.mean()), 1)},
+                     "duration_us": round(dec["us_per_step"], 3),
+                     "algorithmic_bytes_per_launch": round(dec["mean_bytes"], 1),
+                     "launches": K},
+        "ceilings": {"read": rc,
+                     "decode_shaped_gather": {"gbps": round(gat["gbps"], 1), "pct_peak": round(gat["pct_peak"], 1),
+                                              "us_per_launch": round(gat["us_per_step"], 2),
+                                              "kernel": "pa_probe_gather: the decode's K/V bytes over the same "
+                                                        "plans and step order, its launch shape, no arithmetic"},
+                     "decode_pct_of_gather": round(100.0 * dec["gbps"] / gat["gbps"], 1),
+                     "decode_pct_of_read": round(100.0 * dec["gbps"] / rc["gbps"], 1),
+                     "step_pct_of_read": round(100.0 * head["gbps"] / rc["gbps"], 1)},
         "hip_graph": graph,
         "cold_cache": cold,
         "cpu_baseline": None,
-    }
-    ceil = copy_ceiling(dev)
-    result["copy_ceiling"] = ceil
-    result["pct_of_copy_ceiling"] = {"step": round(100.0 * gbps / ceil["gbps"], 1),
-                                     "decode_kernel": round(100.0 * dec_gbps / ceil["gbps"], 1)}
+    })
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         if pool is not None:
-            result["cpu_baseline"] = cpu_baseline(pool, args.cpu_seconds, nsteps, win)
+            cb = cpu_baseline_pool(pool, args.cpu_seconds, win)
         else:
-            result["cpu_baseline"] = cpu_baseline_case(c0, min(args.cpu_seconds, 10.0), float(kv_bytes[0]))
+            cb = cpu_baseline_case(c0, min(args.cpu_seconds, 10.0), float(kv_bytes[0]))
+        if args.workload == "skewed" and win == 0:
+            cb["per_config"] = cpu_oracle_per_config(dev)
+        result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)
 
 

@@ -50,7 +50,7 @@
  *   reduce_info    [num_seqs, 2]  (first_slot, num_partitions)
  *   num_work       [2]            (number of used slots, tiles in the largest slot); 8-byte aligned
  *   workspace      pa_workspace_bytes(...) bytes: fp32 partials written by pa_decode and read by
- *                  pa_merge, plus the counters of the merge pa_decode can run in the same launch
+ *                  pa_merge
  *
  * Query head h reads kv head h / (num_q_heads / num_kv_heads).
  */
@@ -95,9 +95,8 @@ pa_status pa_plan_capacity(int32_t num_seqs, int32_t num_kv_heads, int32_t cu_co
 /*
  * Bytes of workspace pa_decode, pa_merge and pa_attention use for a plan of `capacity` slots, in
  * this order, each region 256-byte aligned:
- *   fp32 partial outputs [capacity, max_q_len, num_q_heads, head_dim], fp32 (max, sum) pairs
- *   [capacity, max_q_len, num_q_heads, 2], and int32 arrival counters [capacity x num_q_heads] for
- *   the merge pa_decode can run in the same launch;
+ *   fp32 partial outputs [capacity, max_q_len, num_q_heads, head_dim] and fp32 (max, sum) pairs
+ *   [capacity, max_q_len, num_q_heads, 2];
  *   then (capacity > 0) the shared-slot region, used when every request is one slot (see
  *   pa_decode): partials and pairs as above for 3 x capacity pieces, then int32 (first piece,
  *   pieces) pairs [PA_INLINE_PLAN_SEQS].  A workspace without this region (workspace_bytes short of
@@ -155,22 +154,22 @@ pa_status pa_plan(const int32_t* context_lens, const int32_t* cu_query_lens, int
  *   work_info, reduce_info,    the plan from pa_plan (capacity slots); reduce_info is only read when
  *   num_work                   out is given and may then not be NULL
  *   tile_tokens                the plan's tile size; a multiple of block_size
- *   workspace                  >= pa_workspace_bytes(capacity, max_q_len, num_q_heads, head_dim)
+ *   workspace                  pa_workspace_bytes(capacity, max_q_len, num_q_heads, head_dim) bytes;
+ *                              at least the slot states (that size without the shared-slot region,
+ *                              PA_CAPACITY below it), in which case slots are not shared
  *   out, out_dtype             NULL: write the partial states only (pa_merge combines them later).
- *                              Non-NULL: also merge, in the same launch, exactly as pa_merge would
- *                              (out_dtype must equal q_dtype).  The last workgroup of each (request,
- *                              kv head) to finish merges it, counted by the workspace's arrival
- *                              counters: they must be zero before the first such call (allocate the
- *                              workspace zero-filled) and every completed call leaves them zero.
- *                              Calls that share a workspace must not overlap.
+ *                              Non-NULL: also merge, exactly as pa_merge with the same arguments
+ *                              (out_dtype must equal q_dtype): the call is then the decode launch
+ *                              followed by the merge launch on the same stream, and the merge's
+ *                              checks run with the decode's, before either launch.
  * Supported: head_dim in {64, 128, 256}; block_size in {16, 64, 128};
  * (num_q_heads / num_kv_heads) x max_q_len <= PA_MAX_GROUP_ROWS; max_blocks_per_seq x block_size
  * <= 2^31 - 257 (key positions are 32-bit).  Anything else returns PA_UNSUPPORTED.
  * KV types bf16 and fp8 run on the matrix cores in bf16 (fp8 codes widen exactly to bf16; q is
  * rounded to bf16; probabilities are rounded to bf16 for the P.V product; accumulation is fp32).
- * KV type f32 runs in fp32 on the vector ALUs (with out, the merge is a second launch).
+ * KV type f32 runs in fp32 on the vector ALUs.
  * Shared slots: when 0 < capacity <= num_seqs <= PA_INLINE_PLAN_SEQS (every request at most one
- * slot once the plan fills the capacity), head_dim <= 128, out is NULL and workspace_bytes covers
+ * slot once the plan fills the capacity), head_dim <= 128 and workspace_bytes covers
  * the shared-slot region (pa_workspace_bytes does), slot sizes follow the request lengths and one
  * workgroup per slot would leave the longest request to one workgroup.  The decode then cuts every
  * used slot of n tiles into X = max(1, ceil(n / p)) pieces, p = ceil((sum of the used slots' tiles +
@@ -216,8 +215,7 @@ pa_status pa_merge(int32_t num_rows, int32_t num_q_heads, int32_t head_dim, int3
  * and pa_decode); the plan buffers are outputs here.
  * With num_seqs <= PA_INLINE_PLAN_SEQS and a bf16 or fp8 cache, the decode launch evaluates the
  * planner's rule itself (every workgroup over all requests, one request per thread) and stores the
- * plan, so the step is two launches (decode, merge); otherwise it is the three launches.  The
- * single-launch merge of pa_decode is not used here, so the workspace needs no zero fill.
+ * plan, so the step is two launches (decode, merge); otherwise it is the three launches.
  * Shared slots as in pa_decode, with the capacity formula's value in place of capacity when the
  * plan is made in place (the two agree when capacity is pa_plan_capacity's value).
  * Errors: the union of pa_plan's, pa_decode's and pa_merge's checks, before any launch.

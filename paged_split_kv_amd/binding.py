@@ -97,6 +97,27 @@ def _check(status: int, where: str) -> None:
         raise PaError(status, where)
 
 
+class Prepared:
+    """One C entry point with its arguments already marshalled (pointers, sizes and the stream as
+    they were when it was prepared): calling it issues the same call again.  For timed loops, where
+    re-checking and re-marshalling every argument would add host time per launch."""
+
+    def __init__(self, fn, args, where: str):
+        self.fn = fn
+        self.args = args
+        self.where = where
+
+    def __call__(self) -> None:
+        _check(self.fn(*self.args), self.where)
+
+
+def _issue(fn, args, where: str, prepare: bool):
+    if prepare:
+        return Prepared(fn, args, where)
+    _check(fn(*args), where)
+    return None
+
+
 def _ptr(t: Optional[torch.Tensor]):
     if t is None:
         return None
@@ -147,11 +168,12 @@ def pa_plan(context_lens: torch.Tensor, num_kv_heads: int, *, cu_count: int, bud
             max_partitions: int = 256, tile_tokens: int = 256, capacity: Optional[int] = None,
             work_info: Optional[torch.Tensor] = None, reduce_info: Optional[torch.Tensor] = None,
             num_work: Optional[torch.Tensor] = None, cu_query_lens: Optional[torch.Tensor] = None,
-            sliding_window: int = 0, stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+            sliding_window: int = 0, stream=None, prepare: bool = False):
     """Plan on the device.  Returns (work_info [capacity, 4], reduce_info [B, 2], num_work [2] =
     (used slots, tiles of the largest slot)), all int32 on the device of context_lens; passed-in
     buffers are refilled in place.  With a sliding window the plan covers the windowed key ranges
-    (cu_query_lens gives the query lengths)."""
+    (cu_query_lens gives the query lengths).  With prepare=True nothing is launched and a Prepared
+    call is returned instead."""
     _need(context_lens, "context_lens", torch.int32)
     dev = context_lens.device
     B = int(context_lens.shape[0])
@@ -172,10 +194,11 @@ def pa_plan(context_lens: torch.Tensor, num_kv_heads: int, *, cu_count: int, bud
     _need(num_work, "num_work", torch.int32, dev)
     if work_info.numel() < 4 * capacity or reduce_info.numel() < 2 * B or num_work.numel() < 2:
         raise ValueError("plan buffers smaller than capacity / num_seqs / 2")
-    _check(load().pa_plan(_ptr(context_lens), _ptr(cu_query_lens), B, num_kv_heads, cu_count, budget_mult,
-                          max_partitions, tile_tokens, sliding_window, capacity, _ptr(work_info),
-                          _ptr(reduce_info), _ptr(num_work), _stream(stream)), "pa_plan")
-    return work_info, reduce_info, num_work
+    args = (_ptr(context_lens), _ptr(cu_query_lens), B, num_kv_heads, cu_count, budget_mult, max_partitions,
+            tile_tokens, sliding_window, capacity, _ptr(work_info), _ptr(reduce_info), _ptr(num_work),
+            _stream(stream))
+    prepared = _issue(load().pa_plan, args, "pa_plan", prepare)
+    return prepared if prepare else (work_info, reduce_info, num_work)
 
 
 def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_dtype: str,
@@ -184,10 +207,10 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_
               cu_query_lens: Optional[torch.Tensor] = None, max_q_len: int = 1,
               k_scale: float = 1.0, v_scale: float = 1.0, tile_tokens: int = 256,
               reduce_info: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-              sliding_window: int = 0, stream=None) -> None:
+              sliding_window: int = 0, stream=None, prepare: bool = False):
     """Split-KV decode into the workspace (see include/pa.h).  kv_dtype is "f32", "bf16" or
     "fp8" (uint8 tensors holding OCP e4m3fn codes).  With ``out`` (and ``reduce_info``) the merge
-    runs in the same call; the workspace must then have been allocated zero-filled."""
+    runs in the same call.  With prepare=True nothing is launched and a Prepared call is returned."""
     dev = q.device
     if q.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("q must be float32 or bfloat16")
@@ -219,19 +242,21 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_
     if cu_query_lens is not None and cu_query_lens.shape[0] != B + 1:
         raise ValueError("cu_query_lens must be [num_seqs + 1]")
     capacity = int(work_info.shape[0])
-    _check(load().pa_decode(_ptr(q), PA_F32 if q.dtype == torch.float32 else PA_BF16, R, Hq, D,
-                            _ptr(k_cache), _ptr(v_cache), _DTYPE_OF_NAME[kv_dtype], nb, Hkv, bs,
-                            _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), B,
-                            _ptr(cu_query_lens), max_q_len, sliding_window, scale, k_scale, v_scale,
-                            _ptr(work_info), _ptr(reduce_info), _ptr(num_work), capacity, tile_tokens,
-                            _ptr(workspace), workspace.numel(), _ptr(out),
-                            PA_F32 if q.dtype == torch.float32 else PA_BF16, _stream(stream)),
-           "pa_decode")
+    args = (_ptr(q), PA_F32 if q.dtype == torch.float32 else PA_BF16, R, Hq, D,
+            _ptr(k_cache), _ptr(v_cache), _DTYPE_OF_NAME[kv_dtype], nb, Hkv, bs,
+            _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), B,
+            _ptr(cu_query_lens), max_q_len, sliding_window, scale, k_scale, v_scale,
+            _ptr(work_info), _ptr(reduce_info), _ptr(num_work), capacity, tile_tokens,
+            _ptr(workspace), workspace.numel(), _ptr(out),
+            PA_F32 if q.dtype == torch.float32 else PA_BF16, _stream(stream))
+    return _issue(load().pa_decode, args, "pa_decode", prepare)
 
 
 def pa_merge(out: torch.Tensor, reduce_info: torch.Tensor, workspace: torch.Tensor, *, capacity: int,
-             cu_query_lens: Optional[torch.Tensor] = None, max_q_len: int = 1, stream=None) -> None:
-    """Log-sum-exp merge of the workspace into out ([R, Hq, D], float32 or bfloat16), in place."""
+             cu_query_lens: Optional[torch.Tensor] = None, max_q_len: int = 1, stream=None,
+             prepare: bool = False):
+    """Log-sum-exp merge of the workspace into out ([R, Hq, D], float32 or bfloat16), in place.  With
+    prepare=True nothing is launched and a Prepared call is returned."""
     dev = out.device
     if out.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("out must be float32 or bfloat16")
@@ -242,10 +267,10 @@ def pa_merge(out: torch.Tensor, reduce_info: torch.Tensor, workspace: torch.Tens
         _need(cu_query_lens, "cu_query_lens", torch.int32, dev)
     R, Hq, D = out.shape
     B = int(reduce_info.shape[0])
-    _check(load().pa_merge(R, Hq, D, B, _ptr(cu_query_lens), max_q_len, _ptr(reduce_info), capacity,
-                           _ptr(workspace), workspace.numel(), _ptr(out),
-                           PA_F32 if out.dtype == torch.float32 else PA_BF16, _stream(stream)),
-           "pa_merge")
+    args = (R, Hq, D, B, _ptr(cu_query_lens), max_q_len, _ptr(reduce_info), capacity,
+            _ptr(workspace), workspace.numel(), _ptr(out),
+            PA_F32 if out.dtype == torch.float32 else PA_BF16, _stream(stream))
+    return _issue(load().pa_merge, args, "pa_merge", prepare)
 
 
 def pa_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_dtype: str,
@@ -255,8 +280,9 @@ def pa_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
                  max_partitions: int = 256, tile_tokens: int = 256,
                  cu_query_lens: Optional[torch.Tensor] = None, max_q_len: int = 1,
                  k_scale: float = 1.0, v_scale: float = 1.0, sliding_window: int = 0,
-                 stream=None) -> None:
-    """Plan, decode and merge in one call (see include/pa.h); the plan buffers are outputs."""
+                 stream=None, prepare: bool = False):
+    """Plan, decode and merge in one call (see include/pa.h); the plan buffers are outputs.  With
+    prepare=True nothing is launched and a Prepared call is returned."""
     dev = q.device
     if q.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("q must be float32 or bfloat16")
@@ -287,13 +313,13 @@ def pa_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
     if reduce_info.numel() < 2 * B or num_work.numel() < 2:
         raise ValueError("plan buffers smaller than num_seqs / 2")
     qd = PA_F32 if q.dtype == torch.float32 else PA_BF16
-    _check(load().pa_attention(_ptr(q), qd, R, Hq, D, _ptr(k_cache), _ptr(v_cache), _DTYPE_OF_NAME[kv_dtype],
-                               nb, Hkv, bs, _ptr(block_tables), int(block_tables.shape[1]),
-                               _ptr(context_lens), B, _ptr(cu_query_lens), max_q_len, sliding_window,
-                               scale, k_scale, v_scale, cu_count, budget_mult, max_partitions,
-                               tile_tokens, capacity,
-                               _ptr(work_info), _ptr(reduce_info), _ptr(num_work), _ptr(workspace),
-                               workspace.numel(), _ptr(out), qd, _stream(stream)), "pa_attention")
+    args = (_ptr(q), qd, R, Hq, D, _ptr(k_cache), _ptr(v_cache), _DTYPE_OF_NAME[kv_dtype],
+            nb, Hkv, bs, _ptr(block_tables), int(block_tables.shape[1]),
+            _ptr(context_lens), B, _ptr(cu_query_lens), max_q_len, sliding_window,
+            scale, k_scale, v_scale, cu_count, budget_mult, max_partitions, tile_tokens, capacity,
+            _ptr(work_info), _ptr(reduce_info), _ptr(num_work), _ptr(workspace),
+            workspace.numel(), _ptr(out), qd, _stream(stream))
+    return _issue(load().pa_attention, args, "pa_attention", prepare)
 
 
 def pa_attention_mixed(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_dtype: str,

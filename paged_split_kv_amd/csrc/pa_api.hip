@@ -40,6 +40,20 @@ extern "C" size_t pa_workspace_bytes(int32_t capacity, int32_t max_q_len, int32_
 
 namespace {
 
+// Bytes of the slot states alone (partials and (m, l) pairs), the least workspace a decode and merge
+// need; 0 for invalid sizes.  pa_workspace_bytes adds the shared-slot region.
+size_t slot_state_bytes(int32_t capacity, int32_t max_q_len, int32_t num_q_heads, int32_t head_dim) {
+    if (capacity < 0 || max_q_len < 1 || num_q_heads < 1 || head_dim < 1) return 0;
+    const unsigned long long states = (unsigned long long)capacity * max_q_len * num_q_heads;
+    if (states > (1ull << 40)) return 0;
+    return pa::workspace_acc_bytes(capacity, max_q_len, num_q_heads, head_dim) +
+           pa::workspace_ml_bytes(capacity, max_q_len, num_q_heads);
+}
+
+}  // namespace
+
+namespace {
+
 pa_status check_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
                      int32_t cu_count, int32_t budget_mult, int32_t max_partitions, int32_t tile_tokens,
                      int32_t sliding_window, int32_t capacity, const int32_t* work_info,
@@ -98,7 +112,8 @@ pa_status prepare_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int3
         (work_info && !aligned(work_info, 16)) || (workspace && !aligned(workspace, 256)) ||
         (num_work && !aligned(num_work, 8)))
         return PA_INVALID_ARG;
-    const size_t need = pa_workspace_bytes(capacity, max_q_len, num_q_heads, head_dim);
+    // the slot states must fit; the shared-slot region is used only when it fits too
+    const size_t need = slot_state_bytes(capacity, max_q_len, num_q_heads, head_dim);
     if (capacity > 0 && (need == 0 || workspace_bytes < need)) return PA_CAPACITY;
     *nothing = capacity == 0 || num_seqs == 0;
 
@@ -114,13 +129,8 @@ pa_status prepare_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int3
     a.num_work = num_work;
     a.ws_acc = static_cast<float*>(workspace);
     const size_t acc_bytes = pa::workspace_acc_bytes(capacity, max_q_len, num_q_heads, head_dim);
-    const size_t ml_bytes = pa::workspace_ml_bytes(capacity, max_q_len, num_q_heads);
     a.ws_ml = workspace ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + acc_bytes) : nullptr;
-    a.ws_counters = workspace ? reinterpret_cast<int*>(static_cast<uint8_t*>(workspace) + acc_bytes + ml_bytes)
-                              : nullptr;
-
-    a.reduce_info = reinterpret_cast<const int2*>(reduce_info);
-    a.out = out;
+    a.out = nullptr;                  // the decode writes partial states; a merge launch writes out
     a.out_bf16 = out_dtype == PA_BF16 ? 1 : 0;
     a.num_rows = num_rows;
     a.num_q_heads = num_q_heads;
@@ -153,7 +163,8 @@ pa_status prepare_merge(int32_t num_rows, int32_t num_q_heads, int32_t head_dim,
     if ((reduce_info && !aligned(reduce_info, 8)) || (workspace && !aligned(workspace, 256)) ||
         (out && !aligned(out, 16)))
         return PA_INVALID_ARG;
-    const size_t need = pa_workspace_bytes(capacity, max_q_len, num_q_heads, head_dim);
+    // the slot states must fit; the shared-slot region is used only when it fits too
+    const size_t need = slot_state_bytes(capacity, max_q_len, num_q_heads, head_dim);
     if (capacity > 0 && (need == 0 || workspace_bytes < need)) return PA_CAPACITY;
     if ((long long)num_rows * num_q_heads > (long long)INT_MAX) return PA_UNSUPPORTED;
 
@@ -175,14 +186,13 @@ pa_status prepare_merge(int32_t num_rows, int32_t num_q_heads, int32_t head_dim,
 }
 
 // Shared slots: with every request one slot (capacity <= batch) slot sizes follow the request
-// lengths, and the longest request alone would set the time.  When the decode writes partial states
-// (no merge in its launch), head_dim <= 128, the batch is at most PA_INLINE_PLAN_SEQS requests and the
-// workspace holds the shared-slot region, the decode cuts each slot into pieces, one workgroup each,
-// and the merge folds a request's pieces like slots.  `one_slot_cap` is the capacity that decides
+// lengths, and the longest request alone would set the time.  When head_dim <= 128, the batch is at
+// most PA_INLINE_PLAN_SEQS requests and the workspace holds the shared-slot region, the decode cuts
+// each slot into pieces, one workgroup each, and the merge folds a request's pieces like slots.  `one_slot_cap` is the capacity that decides
 // "one slot each": the plan's capacity for pa_decode, the capacity formula's value for pa_attention's
 // in-place plan.  pa_merge decides with its own arguments (pa::shares_slots), which are the same.
 bool share_slots(pa::DecodeArgs& d, int head_dim, int one_slot_cap, void* workspace, size_t workspace_bytes) {
-    if (d.out || d.prefill ||
+    if (d.prefill ||
         !pa::shares_slots(one_slot_cap, d.num_seqs, head_dim, d.capacity, d.max_q_len, d.num_q_heads, workspace_bytes))
         return false;
     const pa::SharedRegion r = pa::shared_region(d.capacity, d.max_q_len, d.num_q_heads, head_dim);
@@ -282,15 +292,9 @@ pa_status pa_plan_capacity(int32_t num_seqs, int32_t num_kv_heads, int32_t cu_co
 }
 
 size_t pa_workspace_bytes(int32_t capacity, int32_t max_q_len, int32_t num_q_heads, int32_t head_dim) {
-    if (capacity < 0 || max_q_len < 1 || num_q_heads < 1 || head_dim < 1) return 0;
-    const unsigned long long states = (unsigned long long)capacity * max_q_len * num_q_heads;
-    if (states > (1ull << 40)) return 0;
-    const size_t slots = pa::workspace_acc_bytes(capacity, max_q_len, num_q_heads, head_dim) +
-                         pa::workspace_ml_bytes(capacity, max_q_len, num_q_heads) +
-                         pa::workspace_counter_bytes(capacity, num_q_heads);
-    if (capacity == 0) return slots;
-    // then the shared-slot region (up to three times as many piece states), apart from the counters
-    // so that the fused merge's zero counters survive it
+    const size_t slots = slot_state_bytes(capacity, max_q_len, num_q_heads, head_dim);
+    if (slots == 0 || capacity == 0) return slots;
+    // then the shared-slot region (up to three times as many piece states)
     return pa::shared_region(capacity, max_q_len, num_q_heads, head_dim).end;
 }
 
@@ -326,6 +330,13 @@ pa_status pa_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t n
                                         reduce_info, num_work, capacity, tile_tokens, workspace,
                                         workspace_bytes, out, out_dtype, &a, &nothing);
     if (st != PA_OK) return st;
+    if (out) {
+        // the merge's own checks too, so that a failure launches nothing
+        pa::MergeArgs m;
+        const pa_status sm = prepare_merge(num_rows, num_q_heads, head_dim, num_seqs, cu_query_lens, max_q_len,
+                                           reduce_info, capacity, workspace, workspace_bytes, out, out_dtype, &m);
+        if (sm != PA_OK) return sm;
+    }
     if (nothing) {
         if (!out || num_rows == 0) return PA_OK;
         // nothing to decode: the merge's contract still writes every row (all zero here)
@@ -333,7 +344,11 @@ pa_status pa_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t n
                         out_dtype, stream);
     }
     share_slots(a, head_dim, capacity, workspace, workspace_bytes);
-    return from_hip(pa::launch_decode(a, head_dim, kv_dtype, q_dtype == PA_F32, pa::as_stream(stream)));
+    const pa_status sd = from_hip(pa::launch_decode(a, head_dim, kv_dtype, q_dtype == PA_F32, pa::as_stream(stream)));
+    if (sd != PA_OK || !out || num_rows == 0) return sd;
+    // with out: the merge launch on the same stream, exactly as pa_merge with the same arguments
+    return pa_merge(num_rows, num_q_heads, head_dim, num_seqs, cu_query_lens, max_q_len, reduce_info, capacity,
+                    workspace, workspace_bytes, out, out_dtype, stream);
 }
 
 pa_status pa_merge(int32_t num_rows, int32_t num_q_heads, int32_t head_dim, int32_t num_seqs,

@@ -430,87 +430,6 @@ __device__ __forceinline__ void zero_prefill_tail_row(const DecodeArgs& a, int r
 }
 
 // ---------------------------------------------------------------------------------------------
-// merge inside the decode launch
-// ---------------------------------------------------------------------------------------------
-
-// Log-sum-exp merge of request b's partial states for the rows of kv head g (rows n < M: token n / G,
-// query head g*G + n % G) into out.  The states were written by other workgroups of this launch, so
-// they are read with device-coherent loads.  Thread t handles the 16-byte columns u = t, t + nthreads, ...
-// of the M x D/4 row-column grid and folds the request's partitions in order with a running max.
-template <int D>
-__device__ __forceinline__ void merge_request_rows(const DecodeArgs& a, int b, int g, int row0, int M,
-                                                   int nthreads) {
-    constexpr int NDC = D / 4;
-    const int2 ri = a.reduce_info[b];
-    const int first = max(ri.x, 0);
-    const int parts = max(min(ri.y, a.capacity - first), 0);
-    const int G = a.group;
-    const size_t step = static_cast<size_t>(a.max_q_len) * a.num_q_heads;
-    for (int u = threadIdx.x; u < M * NDC; u += nthreads) {
-        const int n = u / NDC;
-        const int dc = u - n * NDC;
-        const int i = n / G;
-        const int h = g * G + (n - i * G);
-        const size_t st0 = (static_cast<size_t>(first) * a.max_q_len + i) * a.num_q_heads + h;
-        float m = -INFINITY, l = 0.f;
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        // U partials in flight: all loads issued before any is used (indices past the last partial
-        // repeat it and are dropped); empty partials are dropped by selects, not branches
-        constexpr int U = 4;
-        for (int j0 = 0; j0 < parts; j0 += U) {
-            float2 ml[U], v01[U], v23[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const size_t st = st0 + static_cast<size_t>(min(j0 + u, parts - 1)) * step;
-                ml[u] = load_f2_coherent(a.ws_ml + st * 2);
-                v01[u] = load_f2_coherent(a.ws_acc + st * D + 4 * dc);
-                v23[u] = load_f2_coherent(a.ws_acc + st * D + 4 * dc + 2);
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const bool use = j0 + u < parts && ml[u].y > 0.f;
-                const float mn = fmaxf(m, ml[u].x);
-                const float fo = __builtin_amdgcn_exp2f(m - mn);
-                const float fn = __builtin_amdgcn_exp2f(ml[u].x - mn);
-                l = use ? l * fo + ml[u].y * fn : l;
-                acc.x = use ? acc.x * fo + v01[u].x * fn : acc.x;
-                acc.y = use ? acc.y * fo + v01[u].y * fn : acc.y;
-                acc.z = use ? acc.z * fo + v23[u].x * fn : acc.z;
-                acc.w = use ? acc.w * fo + v23[u].y * fn : acc.w;
-                m = use ? mn : m;
-            }
-        }
-        const float inv = l > 0.f ? 1.f / l : 0.f;
-        const size_t o = (static_cast<size_t>(row0 + i) * a.num_q_heads + h) * D + 4 * dc;
-        const float4 r = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-        if (a.out_bf16) {
-            uint2 w;
-            w.x = pack_bf16x2(r.x, r.y);
-            w.y = pack_bf16x2(r.z, r.w);
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + o) = w;
-        } else {
-            *reinterpret_cast<float4*>(static_cast<float*>(a.out) + o) = r;
-        }
-    }
-}
-
-// Write row r of out as zeros when no plan slot owns it: padding rows past the last cumulative
-// query length, rows of requests without partitions, and tokens past max_q_len.  One wave per row.
-template <int D>
-__device__ __forceinline__ void zero_unowned_row(const DecodeArgs& a, int r, int lane) {
-    if (r >= a.num_rows) return;
-    int i;
-    const int b = owner_of_row(a.cu, a.num_seqs, a.max_q_len, r, i);
-    if (b >= 0 && a.reduce_info[b].y > 0) return;
-    const size_t base = static_cast<size_t>(r) * a.num_q_heads * D;
-    const int n4 = a.num_q_heads * D / 4;
-    for (int e = lane; e < n4; e += 64) {
-        if (a.out_bf16) *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + base + 4 * e) = make_uint2(0u, 0u);
-        else *reinterpret_cast<float4*>(static_cast<float*>(a.out) + base + 4 * e) = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-}
-
-// ---------------------------------------------------------------------------------------------
 // matrix-core kernel (bf16 or fp8 caches)
 // ---------------------------------------------------------------------------------------------
 template <int D, int NCB, bool KV8, int NWAVES = 4>
@@ -611,7 +530,6 @@ __global__ __launch_bounds__((64 * NWAVES), (Mfma<D, NCB, KV8, NWAVES>::WAVES)) 
     const DecodeArgs a = second ? L.part[1] : L.part[0];
     const int bid = static_cast<int>(blockIdx.x) - (second ? L.split : 0);
     __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS];
-    __shared__ int s_last;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -620,11 +538,8 @@ __global__ __launch_bounds__((64 * NWAVES), (Mfma<D, NCB, KV8, NWAVES>::WAVES)) 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int work_groups = a.capacity * a.num_kv_heads;
     if (bid >= work_groups) {
-        // merge launched with the decode (or a prefill): trailing workgroups write the rows no slot
-        // owns as zeros
-        const int r = (bid - work_groups) * C::NW + wave;
-        if (a.prefill) zero_prefill_tail_row<D>(a, r, lane);
-        else zero_unowned_row<D>(a, r, lane);
+        // prefill: trailing workgroups write the rows past the last request as zeros
+        if (a.prefill) zero_prefill_tail_row<D>(a, (bid - work_groups) * C::NW + wave, lane);
         return;
     }
     const int slot = bid / a.num_kv_heads;
@@ -1355,66 +1270,42 @@ __global__ __launch_bounds__((64 * NWAVES), (Mfma<D, NCB, KV8, NWAVES>::WAVES)) 
 
     // ---- write the slot's states: rows n < M, token i = n / G, head g*G + n % G ----
     constexpr int D4 = D / 4;
-    const size_t slot_base = static_cast<size_t>(slot) * a.max_q_len;
-    // a prefill block, or a request with one partition, holds its rows' whole softmax state
-    const bool single = a.prefill || (a.out != nullptr && a.reduce_info[b].y == 1);
-    for (int e = tid; e < (single ? 0 : M * D4); e += 64 * C::NW) {
-        const int n = e / D4;
-        const int d4 = e - n * D4;
-        const int i = n / G;
-        const int h = g * G + (n - i * G);
-        const size_t st = (slot_base + i) * a.num_q_heads + h;
-        float mn, ln;
-        float4_t v = state_at(n, d4, mn, ln);
-        v *= a.v_scale;
-        if (a.out == nullptr) {
-            *reinterpret_cast<float4_t*>(a.ws_acc + st * D + 4 * d4) = v;
-            if (d4 == 0) *reinterpret_cast<float2*>(a.ws_ml + st * 2) = make_float2(mn, ln);
-        } else {
-            // merged in this launch by another workgroup: write through to memory
-            store_f2_coherent(a.ws_acc + st * D + 4 * d4, v[0], v[1]);
-            store_f2_coherent(a.ws_acc + st * D + 4 * d4 + 2, v[2], v[3]);
-            if (d4 == 0) store_f2_coherent(a.ws_ml + st * 2, mn, ln);
-        }
-    }
-    if (a.out == nullptr) return;
-
-    // ---- merge in the same launch: the last workgroup of (request, kv head) to finish merges ----
-    if (single) {
-        // a prefill block or a request with one partition: this workgroup holds the whole state
+    if (!a.prefill) {
+        const size_t slot_base = static_cast<size_t>(slot) * a.max_q_len;
         for (int e = tid; e < M * D4; e += 64 * C::NW) {
             const int n = e / D4;
             const int d4 = e - n * D4;
             const int i = n / G;
             const int h = g * G + (n - i * G);
-            float mn, l;
-            const float4_t sv = state_at(n, d4, mn, l);
-            const float inv = l > 0.f ? a.v_scale / l : 0.f;
-            const float4_t v = sv * inv;
-            const size_t o = (static_cast<size_t>(si.row0 + i) * a.num_q_heads + h) * D + 4 * d4;
-            if (a.out_bf16) {
-                uint2 w;
-                w.x = pack_bf16x2(v[0], v[1]);
-                w.y = pack_bf16x2(v[2], v[3]);
-                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + o) = w;
-            } else {
-                *reinterpret_cast<float4_t*>(static_cast<float*>(a.out) + o) = v;
-            }
+            const size_t st = (slot_base + i) * a.num_q_heads + h;
+            float mn, ln;
+            float4_t v = state_at(n, d4, mn, ln);
+            v *= a.v_scale;
+            *reinterpret_cast<float4_t*>(a.ws_acc + st * D + 4 * d4) = v;
+            if (d4 == 0) *reinterpret_cast<float2*>(a.ws_ml + st * 2) = make_float2(mn, ln);
         }
         return;
     }
-    wait_memory_acks();                               // this thread's states are in memory
-    __syncthreads();                                  // ... and every other thread's
-    int* counter = a.ws_counters + b * a.num_kv_heads + g;
-    if (tid == 0) {
-        const int parts = a.reduce_info[b].y;
-        const int seen = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (seen + 1 == parts) ? 1 : 0;
+    // a prefill block holds its rows' whole softmax state: the rows are written normalised
+    for (int e = tid; e < M * D4; e += 64 * C::NW) {
+        const int n = e / D4;
+        const int d4 = e - n * D4;
+        const int i = n / G;
+        const int h = g * G + (n - i * G);
+        float mn, l;
+        const float4_t sv = state_at(n, d4, mn, l);
+        const float inv = l > 0.f ? a.v_scale / l : 0.f;
+        const float4_t v = sv * inv;
+        const size_t o = (static_cast<size_t>(si.row0 + i) * a.num_q_heads + h) * D + 4 * d4;
+        if (a.out_bf16) {
+            uint2 w;
+            w.x = pack_bf16x2(v[0], v[1]);
+            w.y = pack_bf16x2(v[2], v[3]);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + o) = w;
+        } else {
+            *reinterpret_cast<float4_t*>(static_cast<float*>(a.out) + o) = v;
+        }
     }
-    __syncthreads();
-    if (!s_last) return;
-    merge_request_rows<D>(a, b, g, si.row0, M, 64 * C::NW);
-    if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1509,12 +1400,12 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeArgs a) {
     }
 }
 
-// Workgroups of one part: its slots (or query blocks) times kv heads, and with an output a trailing
-// workgroup per NW rows for the zero fill.
+// Workgroups of one part: its slots (or query blocks) times kv heads, and in prefill mode a trailing
+// workgroup per NW rows for the zero fill of the rows past the last request.
 template <int NW>
 unsigned part_workgroups(const DecodeArgs& a) {
     unsigned n = static_cast<unsigned>(a.capacity) * static_cast<unsigned>(a.num_kv_heads);
-    if (a.out) n += static_cast<unsigned>((a.num_rows + NW - 1) / NW);
+    if (a.prefill) n += static_cast<unsigned>((a.num_rows + NW - 1) / NW);
     return n;
 }
 
@@ -1573,20 +1464,7 @@ hipError_t launch_d(const DecodeArgs& a, pa_dtype kv, int ncb, bool qf32, dim3 g
     if (kv == PA_F32) {
         if (qf32) hipLaunchKernelGGL((decode_f32_kernel<D, true>), grid, dim3(256), 0, stream, a);
         else hipLaunchKernelGGL((decode_f32_kernel<D, false>), grid, dim3(256), 0, stream, a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess || !a.out) return e;
-        MergeArgs m{};                                // fp32 caches: the merge is a second launch
-        m.cu = a.cu;
-        m.reduce_info = a.reduce_info;
-        m.ws_acc = a.ws_acc;
-        m.ws_ml = a.ws_ml;
-        m.out = a.out;
-        m.num_rows = a.num_rows;
-        m.num_q_heads = a.num_q_heads;
-        m.num_seqs = a.num_seqs;
-        m.max_q_len = a.max_q_len;
-        m.capacity = a.capacity;
-        return launch_merge(m, D, a.out_bf16 != 0, stream);
+        return hipGetLastError();
     }
     if (kv == PA_BF16) return launch_mfma_ncb<D, false>(a, ncb, qf32, grid, stream);
     return launch_mfma_ncb<D, true>(a, ncb, qf32, grid, stream);

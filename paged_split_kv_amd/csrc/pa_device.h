@@ -78,26 +78,6 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Device-coherent 8-byte accesses (agent-scope relaxed atomics: per instruction they bypass the
-// per-XCD L2, writing through to memory or reading from it), used to hand partial states from one
-// workgroup to another inside a launch without writing back or invalidating whole caches.
-__device__ __forceinline__ void store_f2_coherent(float* p, float a, float b) {
-    const unsigned long long bits =
-        (static_cast<unsigned long long>(__float_as_uint(b)) << 32) | __float_as_uint(a);
-    __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), bits, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ float2 load_f2_coherent(const float* p) {
-    const unsigned long long bits = __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p),
-                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return make_float2(__uint_as_float(static_cast<unsigned>(bits)),
-                       __uint_as_float(static_cast<unsigned>(bits >> 32)));
-}
-
-// Wait until this wave's outstanding memory operations are acknowledged (stores included).
-__device__ __forceinline__ void wait_memory_acks() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 // ---------------------------------------------------------------------------------------------
 // the planner's rule, shared by the plan kernel and the decode that plans in place (ROCm/ATOM PR
 // #2366 section 1: partitions proportional to the request's length under the budget; section 3:
@@ -220,18 +200,13 @@ __device__ __forceinline__ int2 plan_tile_range(int j, int tiles, int parts) {
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 // Workspace regions: acc [capacity, max_q_len, num_q_heads, head_dim] fp32, then (m, l) pairs
-// [capacity, max_q_len, num_q_heads, 2] fp32 (m is the running max in base-2 units), then the arrival
-// counters of the fused merge [capacity * num_q_heads] int32 (one per (request, kv head) is used).
+// [capacity, max_q_len, num_q_heads, 2] fp32 (m is the running max in base-2 units).
 __host__ __device__ inline size_t workspace_acc_bytes(int capacity, int max_q_len, int hq, int d) {
     return align256(static_cast<size_t>(capacity) * max_q_len * hq * d * sizeof(float));
 }
 
 __host__ __device__ inline size_t workspace_ml_bytes(int capacity, int max_q_len, int hq) {
     return align256(static_cast<size_t>(capacity) * max_q_len * hq * 2 * sizeof(float));
-}
-
-__host__ __device__ inline size_t workspace_counter_bytes(int capacity, int hq) {
-    return align256(static_cast<size_t>(capacity) * hq * sizeof(int32_t));
 }
 
 // Owning request and token of output row r (-1 when the row is padding or otherwise unowned).
@@ -281,9 +256,7 @@ struct DecodeArgs {
     const int32_t* num_work;
     float* ws_acc;
     float* ws_ml;
-    int* ws_counters;           // arrival counters of the fused merge
-    const int2* reduce_info;    // (first slot, partitions) per request; needed when out is set
-    void* out;                  // nullable: when set, the merge runs inside the decode launch
+    void* out;                  // prefill mode only: the normalised rows are written here
     int window;                 // 0: none; W > 0: each query token sees its last W visible keys
     // prefill mode: each workgroup takes a block of up to block_tokens query tokens of one request
     // (all its visible keys, one partition) and writes the normalised rows to out directly
@@ -338,7 +311,7 @@ constexpr int kInlinePlanSeqs = PA_INLINE_PLAN_SEQS;
 constexpr int kPieceFactor = 2;
 inline int piece_bound(int capacity) { return (kPieceFactor + 1) * capacity; }
 
-// The shared-slot region, after the slot layout's counters: the piece states' acc and (m, l) for
+// The shared-slot region, after the slot states: the piece states' acc and (m, l) for
 // piece_bound(capacity) pieces, then the per-request (first piece, pieces) pairs for up to
 // kInlinePlanSeqs requests.  Byte offsets from the workspace's start.
 struct SharedRegion {
@@ -347,8 +320,7 @@ struct SharedRegion {
 inline SharedRegion shared_region(int capacity, int max_q_len, int hq, int d) {
     SharedRegion r;
     const int states = piece_bound(capacity);
-    r.acc = workspace_acc_bytes(capacity, max_q_len, hq, d) + workspace_ml_bytes(capacity, max_q_len, hq) +
-            workspace_counter_bytes(capacity, hq);
+    r.acc = workspace_acc_bytes(capacity, max_q_len, hq, d) + workspace_ml_bytes(capacity, max_q_len, hq);
     r.ml = r.acc + workspace_acc_bytes(states, max_q_len, hq, d);
     r.reduce = r.ml + workspace_ml_bytes(states, max_q_len, hq);
     r.end = r.reduce + align256(static_cast<size_t>(kInlinePlanSeqs) * 2 * sizeof(int32_t));

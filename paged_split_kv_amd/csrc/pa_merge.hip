@@ -137,16 +137,27 @@ __global__ __launch_bounds__(NT) void merge_kernel(const MergeArgs a) {
     }
 }
 
+// Compute units of the current device (the launch shapes below are chosen against it).
+int device_cu_count() {
+    int dev = 0, cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu < 1)
+        return 256;
+    return cu;
+}
+
 template <int D>
 hipError_t launch_merge_d(const MergeArgs& a, bool out_bf16, dim3 grid, hipStream_t stream) {
+    const unsigned cu = static_cast<unsigned>(device_cu_count());
     // fewer (row, head) pairs than compute units: each pair's columns split over four workgroups
-    if (grid.x < 256) {
+    if (grid.x < cu) {
         const dim3 g4(grid.x * 4);
         if (out_bf16) hipLaunchKernelGGL((merge_kernel<D, true, 256, 4>), g4, dim3(256), 0, stream, a);
         else hipLaunchKernelGGL((merge_kernel<D, false, 256, 4>), g4, dim3(256), 0, stream, a);
-    } else if (grid.x >= 2048) {
+    } else if (grid.x >= 8 * cu) {
         // many pairs (large batches, typically with few partials each): one wave per pair, so the
         // launch fits the compute units in one round instead of queueing 256-thread workgroups
+        // (eight 256-thread workgroups per compute unit would be two rounds at 32 resident waves)
         if (out_bf16) hipLaunchKernelGGL((merge_kernel<D, true, 64, 1>), grid, dim3(64), 0, stream, a);
         else hipLaunchKernelGGL((merge_kernel<D, false, 64, 1>), grid, dim3(64), 0, stream, a);
     } else {

@@ -38,8 +38,7 @@ class DecodeStep:
         self.reduce_info = torch.empty((num_seqs, 2), dtype=torch.int32, device=self.device)
         self.num_work = torch.empty((2,), dtype=torch.int32, device=self.device)
         nbytes = B.pa_workspace_bytes(self.capacity, max_q_len, num_q_heads, head_dim)
-        # zero-filled once: the fused merge's arrival counters start (and are left) at zero
-        self.workspace = torch.zeros((max(nbytes, 256),), dtype=torch.uint8, device=self.device)
+        self.workspace = torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=self.device)
         self.out = torch.empty((num_rows, num_q_heads, head_dim), dtype=out_dtype, device=self.device)
 
     def shares_slots(self, kv_dtype: str, num_q_heads: int, head_dim: int) -> bool:
@@ -65,7 +64,8 @@ class DecodeStep:
     def decode(self, q, k_cache, v_cache, kv_dtype, block_tables, context_lens, *, scale,
                cu_query_lens=None, k_scale=1.0, v_scale=1.0, merge: bool = False,
                sliding_window: int = 0, stream=None) -> None:
-        """pa_decode; with merge=True the log-sum-exp merge into self.out runs in the same call."""
+        """pa_decode; with merge=True the call also runs the log-sum-exp merge into self.out (the
+        merge launch follows the decode launch on the same stream)."""
         B.pa_decode(q, k_cache, v_cache, kv_dtype, block_tables, context_lens, self.work_info,
                     self.num_work, self.workspace, scale=scale, cu_query_lens=cu_query_lens,
                     max_q_len=self.max_q_len, k_scale=k_scale, v_scale=v_scale,
@@ -92,8 +92,9 @@ class DecodeStep:
 
     def run_case(self, case, stream=None, replan: bool = True, fused: bool = True,
                  whole: bool = False) -> torch.Tensor:
-        """Plan, decode and merge one Case.  fused=True merges inside pa_decode (two launches per
-        step); fused=False calls pa_merge separately; whole=True makes the one pa_attention call."""
+        """Plan, decode and merge one Case.  fused=True passes out to pa_decode, which then merges
+        in the same call; fused=False calls pa_merge separately; whole=True makes the one pa_attention
+        call."""
         w = case.window
         if whole:
             return self.attention(case.q, case.k_cache, case.v_cache, case.kv_dtype, case.block_tables,

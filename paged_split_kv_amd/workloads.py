@@ -104,9 +104,11 @@ class Case:
     def to(self, device) -> "Case":
         def mv(t):
             return None if t is None else t.to(device)
-        return Case(self.name, mv(self.q), mv(self.k_cache), mv(self.v_cache), self.kv_dtype,
-                    mv(self.block_tables), mv(self.context_lens), mv(self.cu_query_lens),
-                    self.max_q_len, self.scale, self.k_scale, self.v_scale, dict(self.meta))
+        return Case(name=self.name, q=mv(self.q), k_cache=mv(self.k_cache), v_cache=mv(self.v_cache),
+                    kv_dtype=self.kv_dtype, block_tables=mv(self.block_tables),
+                    context_lens=mv(self.context_lens), cu_query_lens=mv(self.cu_query_lens),
+                    max_q_len=self.max_q_len, scale=self.scale, k_scale=self.k_scale,
+                    v_scale=self.v_scale, window=self.window, meta=dict(self.meta))
 
     def host(self) -> Dict[str, np.ndarray]:
         """Host numpy views of the storage bytes (bf16 as uint16 bits, fp8 as uint8 codes)."""
@@ -307,6 +309,15 @@ def make_mixed_case(device="cpu", seed: int = 5) -> Case:
     return build_case("mixed_7x16k_prompt100", [16384] * 7 + [100], num_q_heads=12, num_kv_heads=2,
                       head_dim=256, block_size=16, kv_dtype="bf16", q_dtype="bf16", seed=seed,
                       q_lens=[1] * 7 + [100], device=device)
+
+
+def make_prefill_chunk_case(device="cpu", seed: int = 6, prefix: int = 16384, chunk: int = 512) -> Case:
+    """A prompt chunk behind a long prefix (chunked prefill): one request whose last `chunk` tokens are
+    new query rows over prefix + chunk keys, at the per-rank shapes of the mixed batch (12 query heads,
+    2 kv heads, head_dim 256), bf16 (opengfx1030/vllm-rdna PR #29, Change 2: prompt rows go to the
+    prefill kernel on the rebased remainder)."""
+    return build_case("prefill_chunk", [prefix + chunk], num_q_heads=12, num_kv_heads=2, head_dim=256,
+                      block_size=16, kv_dtype="bf16", q_dtype="bf16", seed=seed, q_lens=[chunk], device=device)
 
 
 # ----------------------------------------------------------------------------------------------

@@ -14,8 +14,8 @@ from paged_split_kv_amd import binding as B
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared_functions():
-    text = open(os.path.join(ROOT, "include", "pa.h")).read()
+def _declared_functions(header="pa.h"):
+    text = open(os.path.join(ROOT, "include", header)).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
 
@@ -26,6 +26,41 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(B.SYMBOLS)
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_probe_library_exports_every_declared_function():
+    from paged_split_kv_amd import probe as P
+    lib = P.load()
+    names = _declared_functions("pa_probe.h")
+    assert set(names) == set(P.SYMBOLS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_probe_argument_checks():
+    # refused before any launch: null pointers, misalignment, unsupported shapes
+    from paged_split_kv_amd import probe as P
+    lib = P.load()
+    v = ctypes.c_void_p
+    assert lib.pa_probe_read(None, 1024, 4, v(256), None) == B.PA_INVALID_ARG
+    assert lib.pa_probe_read(v(256), 1024, 0, v(256), None) == B.PA_INVALID_ARG
+    assert lib.pa_probe_read(v(258), 1024, 4, v(256), None) == B.PA_INVALID_ARG
+    assert lib.pa_probe_read(v(256), 0, 4, v(256), None) == B.PA_OK        # nothing to read
+    g = dict(k=v(256), v=v(512), dt=B.PA_BF16, nb=8, hkv=2, bs=16, d=128, bt=v(256), mb=4, ctx=v(256), ns=2,
+             wi=v(256), nw=v(256), cap=8, T=256, sink=v(256))
+
+    def gather(**kw):
+        a = dict(g)
+        a.update(kw)
+        return lib.pa_probe_gather(a["k"], a["v"], a["dt"], a["nb"], a["hkv"], a["bs"], a["d"], a["bt"], a["mb"],
+                                   a["ctx"], a["ns"], a["wi"], a["nw"], a["cap"], a["T"], a["sink"], None)
+    assert gather(k=None) == B.PA_INVALID_ARG
+    assert gather(wi=v(264)) == B.PA_INVALID_ARG
+    assert gather(d=96) == B.PA_UNSUPPORTED
+    assert gather(bs=32) == B.PA_UNSUPPORTED
+    assert gather(T=24) == B.PA_UNSUPPORTED
+    assert gather(dt=7) == B.PA_INVALID_ARG
+    assert gather(cap=0) == B.PA_OK                                            # no workgroup
 
 
 def test_status_strings():
@@ -48,12 +83,12 @@ def test_capacity_matches_oracle(seed):
 
 
 def test_workspace_bytes():
-    # fp32 partials [C, Lmax, Hq, D], (m, l) pairs [C, Lmax, Hq, 2] and int32 counters [C * Hq], then
-    # (C > 0) the shared-slot region: partials and (m, l) pairs of 3 C pieces and 256 int32 pairs;
-    # each region rounded up to 256 bytes
+    # fp32 partials [C, Lmax, Hq, D] and (m, l) pairs [C, Lmax, Hq, 2], then (C > 0) the shared-slot
+    # region: partials and (m, l) pairs of 3 C pieces and 256 int32 pairs; each region rounded up to
+    # 256 bytes
     def expect(c, l, h, d):
         up = lambda x: (x + 255) // 256 * 256
-        slots = up(c * l * h * d * 4) + up(c * l * h * 2 * 4) + up(c * h * 4)
+        slots = up(c * l * h * d * 4) + up(c * l * h * 2 * 4)
         pieces = up(3 * c * l * h * d * 4) + up(3 * c * l * h * 2 * 4) + up(256 * 2 * 4)
         return slots + pieces if c > 0 else slots
     for args in [(512, 1, 4, 64), (256, 1, 16, 128), (512, 3, 6, 256), (1, 1, 1, 64), (0, 1, 1, 64)]:

@@ -31,8 +31,55 @@ def test_distributed_launch_is_refused():
 def test_help_lists_the_workloads_and_options():
     r = _run(["--help"])
     assert r.returncode == 0
-    for opt in ("--steps", "--warmup", "--gpus", "--workload", "--window", "--graph", "--no-cold",
-                "--no-cpu-baseline"):
+    for opt in ("--steps", "--warmup", "--gpus", "--workload", "--window", "--graph", "--no-graph",
+                "--no-cold", "--no-cpu-baseline", "--step-only"):
         assert opt in r.stdout
-    for w in ("skewed", "sparse", "long", "verify", "fp8", "mixed"):
+    for w in ("skewed", "sparse", "long", "verify", "fp8", "mixed", "prefill"):
         assert w in r.stdout
+
+
+def _bench_module():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench_under_test", BENCH)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_step_order_samples_the_whole_set():
+    import numpy as np
+    bench = _bench_module()
+    n = 128
+    # fewer steps than the set: a stratified sample, the j-th smallest index at quantile (j + 1/2) / K
+    for K in (1, 5, 20, 100, 127):
+        order = bench.step_order(K, n)
+        assert len(order) == K and len(np.unique(order)) == K
+        target = (np.arange(K) + 0.5) * n / K
+        assert (np.abs(np.sort(order) - target) < 1.0).all(), K
+    # whole passes: every step equally often; a remainder adds a stratified sample
+    for K in (128, 512, 300):
+        order = bench.step_order(K, n)
+        counts = np.bincount(order, minlength=n)
+        assert len(order) == K
+        assert counts.min() >= K // n and counts.max() <= K // n + 1
+    # the same K gives the same order
+    assert (bench.step_order(20, n) == bench.step_order(20, n)).all()
+
+
+def test_rate_counts_exactly_the_timed_steps():
+    import numpy as np
+    bench = _bench_module()
+    rng = np.random.default_rng(3)
+    per_step = rng.uniform(50e6, 400e6, size=128)        # bytes of each step of the set, unequal
+    for K in (20, 128, 200):
+        order = bench.step_order(K, 128)
+        r = bench.rate(per_step, order, total_ms=K * 0.045)
+        assert abs(r["mean_bytes"] - per_step[order].mean()) <= 1e-6 * r["mean_bytes"]
+        # value x ms_per_step = mean bytes of the timed steps
+        assert abs(r["gbps"] * 1e9 * r["ms_per_step"] * 1e-3 - per_step[order].mean()) <= 1e-6 * r["mean_bytes"]
+        assert abs(r["pct_peak"] - 100 * r["gbps"] / bench.HBM_PEAK_GBPS) < 1e-9
+    # a stratified sample of 20 stays near the set's mean, where the first 20 of a sorted set would not
+    sorted_bytes = np.sort(per_step)
+    r20 = bench.rate(sorted_bytes, bench.step_order(20, 128), 1.0)
+    assert abs(r20["mean_bytes"] / sorted_bytes.mean() - 1) < 0.05
+    assert sorted_bytes[:20].mean() / sorted_bytes.mean() < 0.7

@@ -43,11 +43,8 @@ def _check_plan(step, ctx, hkv, cfg):
 
 
 def _poison_pieces(step):
-    """NaN pattern in the shared-slot region too (it follows the slot partials and the counters;
-    its mode word is written by every decode launch)."""
-    up = lambda x: (x + 255) // 256 * 256
-    start = _partial_bytes(step) + up(step.capacity * step.out.shape[1] * 4)
-    step.workspace[start:].fill_(0xFF)
+    """NaN pattern in the shared-slot region too (it follows the slot partials)."""
+    step.workspace[_partial_bytes(step):].fill_(0xFF)
 
 
 def _both_routes(case, cfg):

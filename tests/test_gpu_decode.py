@@ -64,7 +64,7 @@ def _small_case(spec, seed):
 
 
 def _partial_bytes(step):
-    """Bytes of the workspace's partial-state regions (the arrival counters follow them)."""
+    """Bytes of the workspace's slot partial-state regions (the shared-slot region follows them)."""
     up = lambda x: (x + 255) // 256 * 256
     c, l, h, d = step.capacity, step.max_q_len, step.out.shape[1], step.out.shape[2]
     return up(c * l * h * d * 4) + up(c * l * h * 2 * 4)
@@ -96,7 +96,7 @@ def _zero_rows(case):
     return zero
 
 
-@pytest.mark.parametrize("fused", [True, False], ids=["fused_merge", "separate_merge"])
+@pytest.mark.parametrize("fused", [True, False], ids=["merge_in_call", "separate_merge"])
 @pytest.mark.parametrize("spec", SMALL, ids=[s[0] for s in SMALL])
 def test_small_cases_match_oracle(spec, fused):
     case, P, T = _small_case(spec, seed=11)
@@ -113,13 +113,12 @@ def test_small_cases_match_oracle(spec, fused):
 ONE_SLOT = [s for s in SMALL if s[5] <= 128]
 
 
-@pytest.mark.parametrize("mode", ["fused_merge", "separate_merge", "attention"])
+@pytest.mark.parametrize("mode", ["merge_in_call", "separate_merge", "attention"])
 @pytest.mark.parametrize("spec", ONE_SLOT, ids=[s[0] for s in ONE_SLOT])
 def test_one_slot_per_request(spec, mode):
     """A budget of at most one workgroup per request (cu_count 1): the capacity is the batch, every
-    request is one slot.  Without out the decode shares the slots (pieces, folded by pa_merge);
-    with out it merges in its launch, in the eight-wave form with slots split evenly where that
-    applies (G x L <= 16, head_dim <= 128, bf16 or fp8)."""
+    request is one slot, and the decode shares the slots (pieces, folded by the merge) where that
+    applies (batch <= 256, head_dim <= 128), with or without out."""
     case, P, T = _small_case(spec, seed=12)
     announce(f"one slot per request {spec[0]} {mode}")
     if mode == "attention":
@@ -128,7 +127,7 @@ def test_one_slot_per_request(spec, mode):
         out = step.run_case(case, whole=True)
         torch.cuda.synchronize()
     else:
-        out, step = _run(case, P, T, cu_count=1, fused=(mode == "fused_merge"))
+        out, step = _run(case, P, T, cu_count=1, fused=(mode == "merge_in_call"))
     assert step.capacity == case.num_seqs
     got = to_f64(out)
     assert_close(got, oracle_direct(case), tolerance_kind(case), spec[0])
@@ -160,13 +159,47 @@ def test_skewed_steps(which):
     assert_close(to_f64(out), oracle_direct(case), "bf16", f"skewed {which}")
 
 
-@pytest.mark.parametrize("fused", [True, False], ids=["fused_merge", "separate_merge"])
+@pytest.mark.parametrize("fused", [True, False], ids=["merge_in_call", "separate_merge"])
 def test_sparse_topk_workload_with_cap_8(fused):
     announce(f"sparse top-k, cap 8, fused={fused}")
     case = W.make_sparse_case(device=DEV)
     out, step = _run(case, P=8, T=256, cu_count=256, fused=fused)
     assert (step.reduce_info[:, 1] <= 8).all()
     assert_close(to_f64(out), oracle_direct(case), "bf16", "sparse top-k")
+
+
+# The merge's launch shapes: with at least 8 x CU (row, head) pairs one 64-thread workgroup per pair
+# (no lane fold at head_dim 256, where a wave is exactly the 64 float4 columns); with fewer pairs than
+# compute units each pair's columns over four workgroups; in between one 256-thread workgroup per pair.
+MANY_PAIRS = [
+    # (name, requests, Hq, Hkv, D, kv, q dtype): 300 x 8 = 2400 pairs >= 2048
+    ("d256_bf16_2400pairs", 300, 8, 2, 256, "bf16", "bf16"),
+    ("d256_qf32_2400pairs", 300, 8, 2, 256, "bf16", "f32"),
+    ("d128_qf32_kvf32_2400pairs", 300, 8, 1, 128, "f32", "f32"),
+    ("d64_fp8_qf32_2400pairs", 300, 8, 4, 64, "fp8", "f32"),
+    ("d256_qf32_fewpairs", 20, 4, 1, 256, "bf16", "f32"),
+    ("d128_qf32_midpairs", 100, 8, 2, 128, "bf16", "f32"),
+]
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["merge_in_call", "separate_merge"])
+@pytest.mark.parametrize("spec", MANY_PAIRS, ids=[s[0] for s in MANY_PAIRS])
+def test_merge_launch_shapes(spec, fused):
+    name, n, hq, hkv, d, kv, qd = spec
+    rng = np.random.default_rng(31)
+    ctx = rng.integers(0, 700, size=n).tolist()
+    ctx[3] = 0                                    # an empty request: its rows are zeros
+    case = W.build_case(name, ctx, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=16,
+                        kv_dtype=kv, q_dtype=qd, seed=32, device=DEV)
+    announce(f"merge launch shape {name} fused={fused}")
+    # a large budget (planner argument only) and 16-token tiles, so that requests get several
+    # partitions and each merge folds several states
+    out, step = _run(case, P=256, T=16, cu_count=4096, fused=fused)
+    assert int(step.num_work[0].item()) > 2 * n
+    got = to_f64(out)
+    assert_close(got, oracle_direct(case), tolerance_kind(case), name)
+    z = _zero_rows(case)
+    assert z[3] and (got[z] == 0.0).all()
 
 
 def test_full_size_separate_merge_fp8():
@@ -176,9 +209,9 @@ def test_full_size_separate_merge_fp8():
     assert_close(to_f64(out), oracle_direct(case), "fp8", "fp8 separate merge")
 
 
-def test_fused_calls_back_to_back_reuse_the_workspace():
-    # one step object (one workspace) across several different batches: the arrival counters must
-    # return to zero after every call for the next merge to fire correctly
+def test_merging_calls_back_to_back_reuse_the_workspace():
+    # one step object (one workspace) across several different batches, pa_decode with out (the decode
+    # and the merge launch in one call): nothing of a call may leak into the next
     specs = [("a", [700, 33, 1, 2000], [2, 1, 1, 3], 8, 2, 128, 16, "bf16", "bf16", 2, 256, 256),
              ("b", [90, 5000, 12, 64], [1, 3, 2, 1], 8, 2, 128, 16, "bf16", "bf16", 2, 256, 256),
              ("c", [0, 300, 4096, 7], [2, 1, 3, 1], 8, 2, 128, 16, "bf16", "bf16", 2, 256, 256)]
@@ -191,16 +224,17 @@ def test_fused_calls_back_to_back_reuse_the_workspace():
             out = step.run_case(case, fused=True)
             torch.cuda.synchronize()
             assert_close(to_f64(out), oracle_direct(case), "bf16", f"back-to-back {rep} {k}")
-    nbytes = _partial_bytes(step)
-    counters = (step.capacity * step.out.shape[1] * 4 + 255) // 256 * 256
-    assert int(step.workspace[nbytes:nbytes + counters].view(torch.int32).abs().sum().item()) == 0
+            # the call with out is exactly the decode followed by pa_merge
+            got = out.clone()
+            sep = step.run_case(case, fused=False)
+            torch.cuda.synchronize()
+            assert torch.equal(got, sep), f"back-to-back {rep} {k}: pa_decode with out differs from pa_merge"
 
 
 def test_workspace_switches_between_pieces_and_slots():
-    """One workspace, one plan capacity (every request one slot), bf16 and fp32 caches: pa_decode
-    without out cuts the slots into pieces (the shared-slot region), pa_decode with out keeps slot
-    states and merges in its launch with the arrival counters; alternating the two must leave both
-    right and the counters zero."""
+    """One workspace, one plan capacity (every request one slot), bf16 and fp32 caches: the bf16
+    decode cuts the slots into pieces (the shared-slot region), the fp32 decode keeps slot states;
+    alternating them, with and without out, must leave every call right."""
     ctx = [1, 17, 100, 3000, 5000]
     cases = [W.build_case(f"switch_{kv}", ctx, num_q_heads=4, num_kv_heads=1, head_dim=64, block_size=16,
                           kv_dtype=kv, q_dtype="f32", seed=41, device=DEV) for kv in ("bf16", "f32")]
@@ -215,9 +249,30 @@ def test_workspace_switches_between_pieces_and_slots():
                 out = step.run_case(case, fused=fused)
                 torch.cuda.synchronize()
                 assert_close(to_f64(out), ref, tolerance_kind(case), f"switch {rep} {fused} {case.kv_dtype}")
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["merge_in_call", "separate_merge"])
+def test_workspace_of_slot_states_only(fused):
+    """A workspace that holds the slot states but not the shared-slot region is accepted; the decode
+    and the merge then both keep slot states (no pieces), and agree with the oracle.  A smaller one is
+    refused before any launch."""
+    ctx = [1, 17, 100, 3000, 5000, 640]
+    case = W.build_case("short_ws", ctx, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                        kv_dtype="bf16", q_dtype="bf16", seed=43, device=DEV)
+    step = DecodeStep.for_case(case, PlanConfig(cu_count=1, tile_tokens=16))
+    assert step.capacity == len(ctx)
     nbytes = _partial_bytes(step)
-    counters = (step.capacity * step.out.shape[1] * 4 + 255) // 256 * 256
-    assert int(step.workspace[nbytes:nbytes + counters].view(torch.int32).abs().sum().item()) == 0
+    assert nbytes < step.workspace.numel()
+    step.workspace = step.workspace[:nbytes]
+    announce(f"slot-state workspace ({nbytes} bytes) fused={fused}")
+    step.out.fill_(float("nan"))
+    out = step.run_case(case, fused=fused)
+    torch.cuda.synchronize()
+    assert_close(to_f64(out), oracle_direct(case), "bf16", "slot-state workspace")
+    step.workspace = step.workspace[:nbytes - 256]
+    with pytest.raises(B.PaError) as e:
+        step.run_case(case, fused=fused)
+    assert e.value.status == B.PA_CAPACITY
 
 
 def test_single_key_row_is_the_value_row_fp32():

@@ -29,11 +29,11 @@ def _oracle_at(case, lens):
                                    case.scale, case.k_scale, case.v_scale)
 
 
-@pytest.mark.parametrize("mode", ["separate_merge", "fused_merge", "attention", "attention_shared_slots"])
+@pytest.mark.parametrize("mode", ["separate_merge", "merge_in_call", "attention", "attention_shared_slots"])
 def test_graph_replays_draft_passes(mode):
     """attention_shared_slots: a budget of 2 compute units leaves every request one slot, so
     pa_attention cuts the slots into pieces; the piece table is rewritten on every replay."""
-    fused = mode == "fused_merge"
+    fused = mode == "merge_in_call"
     cu_count = 2 if mode == "attention_shared_slots" else 256
     final = [1300, 40, 2, 5000, 777, 256]
     q_lens = [2, 1, 2, 3, 1, 2]

@@ -56,7 +56,7 @@ def _check_plan(step, case, cfg):
     assert np.array_equal(step.work_info.cpu().numpy(), ow)
 
 
-@pytest.mark.parametrize("mode", ["separate", "fused", "attention"])
+@pytest.mark.parametrize("mode", ["separate", "merge_in_call", "attention"])
 @pytest.mark.parametrize("spec", CASES, ids=[c[0] for c in CASES])
 def test_window_cases_match_oracle(spec, mode):
     case, cfg = _case(spec, seed=21)
@@ -65,7 +65,7 @@ def test_window_cases_match_oracle(spec, mode):
     step.out.fill_(float("nan"))
     step.workspace[:_partial_bytes(step)].fill_(0xFF)
     step.work_info.fill_(0x5A5A5A5A)
-    out = step.run_case(case, fused=mode == "fused", whole=mode == "attention")
+    out = step.run_case(case, fused=mode == "merge_in_call", whole=mode == "attention")
     torch.cuda.synchronize()
     _check_plan(step, case, cfg)
     got = to_f64(out)
