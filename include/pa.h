@@ -82,6 +82,7 @@ typedef enum {
 #define PA_MAX_SEQS 8192           /* pa_plan keeps per-request prefix sums in LDS */
 #define PA_MAX_GROUP_ROWS 64       /* (num_q_heads / num_kv_heads) x max_q_len */
 #define PA_INLINE_PLAN_SEQS 256    /* largest batch pa_attention plans inside the decode launch */
+#define PA_NOALLOC_SCRATCH_BYTES (32u << 20)   /* the device array behind pa_attention_noalloc */
 
 /*
  * Number of plan slots a batch needs:
@@ -230,6 +231,33 @@ pa_status pa_attention(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_
                        int32_t tile_tokens, int32_t capacity, int32_t* work_info,
                        int32_t* reduce_info, int32_t* num_work, void* workspace,
                        size_t workspace_bytes, void* out, pa_dtype out_dtype, void* stream);
+
+/*
+ * pa_attention for callers that cannot allocate memory: code under HIP graph capture, serving loops
+ * and harnesses that forbid allocation.  Arguments are pa_attention's without the workspace; the
+ * partial states go instead to a static device array of PA_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every device it runs on until the process ends.  The call allocates nothing (no hipMalloc,
+ * hipFree or allocating library call).  The workspace it uses is pa_workspace_bytes(capacity,
+ * max_q_len, num_q_heads, head_dim) bytes of the array when that fits, else the slot states alone (no
+ * shared slots) when those fit; the results are pa_attention's with a workspace of that size.
+ * Beyond the array, PA_CAPACITY before anything else.
+ * The first call with a device current looks up that device's copy of the array (hipGetSymbolAddress)
+ * and keeps it; make that first call outside graph capture.  All calls on one device share its array
+ * and find it holding the last call's contents (nothing in it must start at zero): calls that
+ * overlap on one device (concurrent streams or threads) race and give wrong results.
+ * Errors: PA_CAPACITY (the states exceed the array), PA_UNSUPPORTED (device index >= 64),
+ * PA_HIP_ERROR (no current device or the lookup failed), then those of pa_attention.
+ */
+pa_status pa_attention_noalloc(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t num_q_heads,
+                               int32_t head_dim, const void* k_cache, const void* v_cache, pa_dtype kv_dtype,
+                               int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t num_seqs, const int32_t* cu_query_lens,
+                               int32_t max_q_len, int32_t sliding_window, float scale, float k_scale,
+                               float v_scale, int32_t cu_count, int32_t budget_mult, int32_t max_partitions,
+                               int32_t tile_tokens, int32_t capacity, int32_t* work_info,
+                               int32_t* reduce_info, int32_t* num_work, void* out, pa_dtype out_dtype,
+                               void* stream);
 
 /*
  * Prefill rows: attention of every query token of the given requests over its visible keys, written

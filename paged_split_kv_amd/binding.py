@@ -23,13 +23,14 @@ PA_OK, PA_INVALID_ARG, PA_UNSUPPORTED, PA_CAPACITY, PA_HIP_ERROR = 0, 1, 2, 3, 4
 PA_MAX_SEQS = 8192
 PA_MAX_GROUP_ROWS = 64
 PA_INLINE_PLAN_SEQS = 256
+PA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _DTYPE_OF_NAME = {"f32": PA_F32, "bf16": PA_BF16, "fp8": PA_FP8_E4M3}
 _TORCH_OF_NAME = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
 
 SYMBOLS = ("pa_plan_capacity", "pa_workspace_bytes", "pa_plan", "pa_decode", "pa_merge",
-           "pa_attention", "pa_prefill", "pa_attention_mixed", "pa_split_decode_first", "pa_status_string",
-           "pa_device_cu_count")
+           "pa_attention", "pa_attention_noalloc", "pa_prefill", "pa_attention_mixed", "pa_split_decode_first",
+           "pa_status_string", "pa_device_cu_count")
 
 
 class PaError(RuntimeError):
@@ -70,6 +71,10 @@ def load(path: str = LIB_PATH):
                                  vp, i32, vp, i32, vp, i32, i32, f32, f32, f32, i32, i32, i32, i32, i32,
                                  vp, vp, vp, vp, ctypes.c_size_t, vp, ctypes.c_int, vp]
     lib.pa_attention.restype = ctypes.c_int
+    lib.pa_attention_noalloc.argtypes = [vp, ctypes.c_int, i32, i32, i32, vp, vp, ctypes.c_int, i32, i32, i32,
+                                         vp, i32, vp, i32, vp, i32, i32, f32, f32, f32, i32, i32, i32, i32, i32,
+                                         vp, vp, vp, vp, ctypes.c_int, vp]
+    lib.pa_attention_noalloc.restype = ctypes.c_int
     lib.pa_prefill.argtypes = [vp, ctypes.c_int, i32, i32, i32, vp, vp, ctypes.c_int, i32, i32, i32, vp, i32,
                                vp, i32, vp, i32, f32, f32, f32, vp, ctypes.c_int, vp]
     lib.pa_prefill.restype = ctypes.c_int
@@ -320,6 +325,50 @@ def pa_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
             _ptr(work_info), _ptr(reduce_info), _ptr(num_work), _ptr(workspace),
             workspace.numel(), _ptr(out), qd, _stream(stream))
     return _issue(load().pa_attention, args, "pa_attention", prepare)
+
+
+def pa_attention_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_dtype: str,
+                         block_tables: torch.Tensor, context_lens: torch.Tensor, work_info: torch.Tensor,
+                         reduce_info: torch.Tensor, num_work: torch.Tensor, out: torch.Tensor, *, scale: float,
+                         cu_count: int, budget_mult: int = 2, max_partitions: int = 256, tile_tokens: int = 256,
+                         cu_query_lens: Optional[torch.Tensor] = None, max_q_len: int = 1, k_scale: float = 1.0,
+                         v_scale: float = 1.0, sliding_window: int = 0, stream=None, prepare: bool = False):
+    """pa_attention without a workspace argument: the library's per-device static array holds the
+    partial states (see include/pa.h).  Same checks as pa_attention otherwise."""
+    dev = q.device
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("q must be float32 or bfloat16")
+    _need(q, "q", q.dtype)
+    _need(k_cache, "k_cache", _TORCH_OF_NAME[kv_dtype], dev)
+    _need(v_cache, "v_cache", _TORCH_OF_NAME[kv_dtype], dev)
+    _need(block_tables, "block_tables", torch.int32, dev)
+    _need(context_lens, "context_lens", torch.int32, dev)
+    _need(work_info, "work_info", torch.int32, dev)
+    _need(reduce_info, "reduce_info", torch.int32, dev)
+    _need(num_work, "num_work", torch.int32, dev)
+    _need(out, "out", q.dtype, dev)
+    if cu_query_lens is not None:
+        _need(cu_query_lens, "cu_query_lens", torch.int32, dev)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have the shape of q")
+    R, Hq, D = q.shape
+    nb, Hkv, bs, D2 = k_cache.shape
+    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shapes do not match q")
+    B = int(context_lens.shape[0])
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs, max_blocks]")
+    if cu_query_lens is not None and cu_query_lens.shape[0] != B + 1:
+        raise ValueError("cu_query_lens must be [num_seqs + 1]")
+    if reduce_info.numel() < 2 * B or num_work.numel() < 2:
+        raise ValueError("plan buffers smaller than num_seqs / 2")
+    qd = PA_F32 if q.dtype == torch.float32 else PA_BF16
+    args = (_ptr(q), qd, R, Hq, D, _ptr(k_cache), _ptr(v_cache), _DTYPE_OF_NAME[kv_dtype],
+            nb, Hkv, bs, _ptr(block_tables), int(block_tables.shape[1]),
+            _ptr(context_lens), B, _ptr(cu_query_lens), max_q_len, sliding_window,
+            scale, k_scale, v_scale, cu_count, budget_mult, max_partitions, tile_tokens, int(work_info.shape[0]),
+            _ptr(work_info), _ptr(reduce_info), _ptr(num_work), _ptr(out), qd, _stream(stream))
+    return _issue(load().pa_attention_noalloc, args, "pa_attention_noalloc", prepare)
 
 
 def pa_attention_mixed(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_dtype: str,

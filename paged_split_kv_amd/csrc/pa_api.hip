@@ -4,7 +4,15 @@
 // synchronises or reads device memory.
 #include <limits.h>
 
+#include <mutex>
+
 #include "pa_device.h"
+
+// The workspace of pa_attention_noalloc: a static device array that every device the library runs
+// on holds until the process ends.  In host code the name `scratch` is a host-side stand-in, not a
+// device address; host code uses only the address hipGetSymbolAddress returns for the current
+// device (scratch_on_current_device).
+static __device__ __align__(256) uint8_t scratch[PA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -421,6 +429,58 @@ pa_status pa_attention(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_
     }
     if (num_rows == 0) return PA_OK;
     return from_hip(pa::launch_merge(m, head_dim, out_dtype == PA_BF16, s));
+}
+
+}  // extern "C"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` on each device, once looked up
+
+// The current device's copy of `scratch`: its address is looked up with hipGetSymbolAddress the first
+// time a call is made with that device current, checked, and kept for later calls.
+pa_status scratch_on_current_device(void** ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return PA_HIP_ERROR;
+    if (dev < 0 || dev >= kMaxDevices) return PA_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PA_HIP_ERROR;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_attention_noalloc(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t num_q_heads,
+                               int32_t head_dim, const void* k_cache, const void* v_cache, pa_dtype kv_dtype,
+                               int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t num_seqs, const int32_t* cu_query_lens,
+                               int32_t max_q_len, int32_t sliding_window, float scale, float k_scale,
+                               float v_scale, int32_t cu_count, int32_t budget_mult, int32_t max_partitions,
+                               int32_t tile_tokens, int32_t capacity, int32_t* work_info,
+                               int32_t* reduce_info, int32_t* num_work, void* out, pa_dtype out_dtype,
+                               void* stream) {
+    // the whole workspace when it fits the array, else the slot states alone (no shared slots)
+    size_t bytes = pa_workspace_bytes(capacity, max_q_len, num_q_heads, head_dim);
+    if (bytes > PA_NOALLOC_SCRATCH_BYTES) bytes = slot_state_bytes(capacity, max_q_len, num_q_heads, head_dim);
+    if (bytes > PA_NOALLOC_SCRATCH_BYTES) return PA_CAPACITY;
+    void* ws = nullptr;
+    const pa_status st = scratch_on_current_device(&ws);
+    if (st != PA_OK) return st;
+    return pa_attention(q, q_dtype, num_rows, num_q_heads, head_dim, k_cache, v_cache, kv_dtype, num_blocks,
+                        num_kv_heads, block_size, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                        cu_query_lens, max_q_len, sliding_window, scale, k_scale, v_scale, cu_count, budget_mult,
+                        max_partitions, tile_tokens, capacity, work_info, reduce_info, num_work, ws, bytes, out,
+                        out_dtype, stream);
 }
 
 pa_status pa_prefill(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t num_q_heads,

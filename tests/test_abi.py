@@ -28,6 +28,17 @@ def test_library_exports_every_declared_function():
         assert hasattr(lib, n), n
 
 
+def test_noalloc_refuses_states_beyond_its_array():
+    # the size check comes first: no device lookup and no launch for states beyond the static array
+    lib = B.load()
+    vp = ctypes.c_void_p
+    cap = B.pa_plan_capacity(8, 1, 1 << 20, 2, 256)
+    st = lib.pa_attention_noalloc(vp(256), B.PA_BF16, 32, 16, 256, vp(256), vp(256), B.PA_BF16, 64, 1, 16, vp(256),
+                                  4, vp(256), 8, vp(256), 4, 0, 0.0625, 1.0, 1.0, 1 << 20, 2, 256, 256, cap,
+                                  vp(256), vp(256), vp(256), vp(256), B.PA_BF16, None)
+    assert st == B.PA_CAPACITY
+
+
 def test_probe_library_exports_every_declared_function():
     from paged_split_kv_amd import probe as P
     lib = P.load()
