@@ -35,7 +35,6 @@
 //    scale and v_scale into the final state.  Probabilities are rounded to bf16 for P.V.
 // The fp32-cache kernel is plain vector code (fp32 throughout) with the same outputs.
 #include <climits>
-#include <type_traits>
 
 #include "pa_device.h"
 
@@ -450,9 +449,10 @@ struct Mfma {
     // so short slots still run every wave and the longest gets twice the waves of a 4-wave group.
     static constexpr bool EVEN = NW > 4;
     // head_dim 256 (DS): the waves work in groups of SPLIT that split the head dimension, each group
-    // walking its own stream of the slot's chunks (chunks s, s + NS, ...).  A wave reads its SL
-    // columns of K straight into matrix-core operand registers and stages only its V columns in
-    // LDS; the group's partial scores are summed through LDS.  The per-wave state is 1/SPLIT of the
+    // walking its own stream of the slot's chunks (chunks s, s + NS, ...).  A wave loads its SL
+    // columns of K and V row-major (coalesced 16-byte pieces), stages them in LDS (K in a tile it
+    // reads back at once in operand order, V in tiles of two parities for the transposed reads), and
+    // the group's partial scores are summed through LDS.  The per-wave state is 1/SPLIT of the
     // full one, so operands, accumulators and a deep prefetch fit the registers of two workgroups
     // per CU, while only SPLIT waves repeat each chunk's softmax.
     static constexpr bool DS = D == 256;
@@ -461,9 +461,9 @@ struct Mfma {
     static constexpr int SL = D / SPLIT;               // head-dimension columns per wave (DS)
     static constexpr int KSW = SL / 32;                // k-steps of the partial S^T product (DS)
     static constexpr int DTW = SL / 16;                // d tiles of the P.V product per wave (DS)
-    static constexpr int VGC = SL * ESZ / 16;          // 16-byte HBM columns of a wave's V row slice
-    static constexpr int VLD = 16 * VGC / 64;          // 16-byte V loads per lane per chunk (DS)
-    static constexpr int VLRB = SL * 2;                // LDS bytes per V row slice (bf16)
+    static constexpr int VGC = SL * ESZ / 16;          // 16-byte HBM columns of a wave's K or V row slice
+    static constexpr int VLD = 16 * VGC / 64;          // 16-byte K (and V) loads per lane per chunk (DS)
+    static constexpr int VLRB = SL * 2;                // LDS bytes per K or V row slice (bf16)
     static constexpr int VSWM = (VLRB / 16 < 16 ? VLRB / 16 : 16) - 1;
     static constexpr int PFD = KV8 ? (NCB == 1 ? 6 : (NCB == 2 ? 4 : 2)) : (NCB == 1 ? 3 : (NCB == 2 ? 2 : 3));   // chunks in flight per wave (DS)
     static constexpr int XBUF = 2 * NCB * NW * 64 * 16;  // partial-score exchange, two parities (DS)
@@ -477,7 +477,8 @@ struct Mfma {
     // score chains and one softmax pass over 32 keys (the per-chunk latency of a lone wave drops)
     static constexpr int CG = (D <= 128 && NCB == 1 && PF % 2 == 0) ? 2 : 1;
     static constexpr int WAVE_LDS = CG * 2 * 16 * LRB; // K then V of each chunk of a step, per wave
-    static constexpr int STAGE_LDS = DS ? NW * 2 * 16 * VLRB + XBUF : NW * WAVE_LDS;
+    // DS: per wave two V tiles (chunk parity) and one K tile, then the exchange
+    static constexpr int STAGE_LDS = DS ? NW * 3 * 16 * VLRB + XBUF : NW * WAVE_LDS;
     static constexpr int ROWS = 16 * NCB;              // query rows per workgroup (padded)
     static constexpr int APITCH = D + 4;               // fp32 pitch of the LDS merge buffer
     static constexpr int MERGE_LDS = (NW * ROWS + 2 * ROWS + ROWS * APITCH) * 4;
@@ -729,13 +730,10 @@ __global__ __launch_bounds__((64 * NWAVES), (Mfma<D, NCB, KV8, NWAVES>::WAVES)) 
     if constexpr (C::DS) {
         // ---- head-split stream: every wave takes every chunk, SL columns of it ----
         constexpr int PF = C::PF;
-        using kload_t = typename std::conditional<KV8, u32x2_t, u32x4_t>::type;
-        kload_t kreg[PF][C::KSW];
-        u32x4_t vreg[PF][C::VLD];
+        u32x4_t kreg[PF][C::VLD], vreg[PF][C::VLD];
         int nvalid_st[PF];
-        // K columns in operand order (lane: key row lane & 15, columns dcol0 + 32s + 8*(lane >> 4)
-        // .. + 8) and this wave's V columns (16-byte pieces, row-major), non-temporal; a chunk past
-        // the slot, the context or on an invalid page loads zeros (no records)
+        // this wave's K and V columns, 16-byte pieces, row-major, non-temporal; a chunk past the
+        // slot, the context or on an invalid page loads zeros (no records)
         auto issue = [&](int st, int k, int page) {
             const int key0 = si.k_lo + 16 * chunk_of(k);
             const int blk = __builtin_amdgcn_readfirstlane(page);
@@ -752,31 +750,29 @@ __global__ __launch_bounds__((64 * NWAVES), (Mfma<D, NCB, KV8, NWAVES>::WAVES)) 
             const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<uint8_t*>(a.v_cache + base), 0, records, kRawBufferWord3);
 #pragma unroll
-            for (int ks = 0; ks < C::KSW; ++ks) {
-                const int o = col * C::GRB + (dcol0 + 32 * ks + 8 * grp) * C::ESZ;
-                if constexpr (KV8)
-                    kreg[st][ks] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rk, o, 0, kLoadNonTemporal));
-                else
-                    kreg[st][ks] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, kLoadNonTemporal));
-            }
-#pragma unroll
             for (int it = 0; it < C::VLD; ++it) {
                 const int f = it * 64 + lane;
                 const int r = f / C::VGC;
                 const int c = f - r * C::VGC;
-                vreg[st][it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                               rv, r * C::GRB + dcol0 * C::ESZ + 16 * c, 0, kLoadNonTemporal));
+                const int o = r * C::GRB + dcol0 * C::ESZ + 16 * c;
+                kreg[st][it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, kLoadNonTemporal));
+                vreg[st][it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, kLoadNonTemporal));
             }
         };
-        // two V tiles per wave (chunk parity), then the partial-score exchange [2][NCB][NW][64]
+        // two V tiles per wave (chunk parity), then one K tile per wave, then the partial-score
+        // exchange [2][NCB][NW][64]
         uint8_t* const vlds0 = lds + wave * 2 * 16 * C::VLRB;
-        float4_t* const xbuf = reinterpret_cast<float4_t*>(lds + C::NW * 2 * 16 * C::VLRB);
+        uint8_t* const klds = lds + C::NW * 2 * 16 * C::VLRB + wave * 16 * C::VLRB;
+        float4_t* const xbuf = reinterpret_cast<float4_t*>(lds + C::NW * 3 * 16 * C::VLRB);
         const int tr_row = 4 * grp + ((lane >> 2) & 3);
         const int tr_d0 = 4 * (lane & 3);
 
-        // Stage A of chunk k (slot st of the load ring): V columns to LDS tile k & 1 as bf16 rows
-        // (rows >= nv zero), K columns to operands, the loads PF chunks ahead, then the partial S^T
-        // over this wave's columns into exchange buffer k & 1.
+        // Stage A of chunk k (slot st of the load ring): K columns to the wave's K tile and V columns to
+        // V tile k & 1, as bf16 rows (rows >= nv zero); K read back in operand order (lane: key row
+        // lane & 15, columns 32s + 8*(lane >> 4) .. + 8 of the wave's slice); the loads PF chunks
+        // ahead; then the partial S^T over this wave's columns into exchange buffer k & 1.  The K tile
+        // is written and read by this wave alone, and a wave's LDS operations complete in order, so
+        // the next chunk's K may reuse it.
         auto stage_a = [&](int st, int k) {
             const int nv = nvalid_st[st];
             uint8_t* const vlds = vlds0 + (k & 1) * 16 * C::VLRB;
@@ -786,41 +782,44 @@ __global__ __launch_bounds__((64 * NWAVES), (Mfma<D, NCB, KV8, NWAVES>::WAVES)) 
                 const int f = it * 64 + lane;
                 const int r = f / C::VGC;
                 const int c = f - r * C::VGC;
+                u32x4_t kv = kreg[st][it];
                 u32x4_t vv = vreg[st][it];
                 if (nv < 16) {
                     const u32x4_t z = {0u, 0u, 0u, 0u};
+                    kv = r < nv ? kv : z;
                     vv = r < nv ? vv : z;
                 }
                 if constexpr (!KV8) {
-                    *reinterpret_cast<u32x4_t*>(vlds + lds_col<C::VLRB, C::VSWM>(r, c)) = vv;
+                    const int off = lds_col<C::VLRB, C::VSWM>(r, c);
+                    *reinterpret_cast<u32x4_t*>(klds + off) = kv;
+                    *reinterpret_cast<u32x4_t*>(vlds + off) = vv;
                 } else {
-                    u32x4_t lo, hi;
+                    // 16 fp8 codes -> 16 bf16 values = two LDS columns (2c, 2c+1), widened exactly
+                    u32x4_t klo, khi, vlo, vhi;
 #pragma unroll
                     for (int w = 0; w < 2; ++w) {
-                        lo[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vv[w], 1.0f, false));
-                        lo[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vv[w], 1.0f, true));
-                        hi[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vv[w + 2], 1.0f, false));
-                        hi[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vv[w + 2], 1.0f, true));
+                        klo[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kv[w], 1.0f, false));
+                        klo[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kv[w], 1.0f, true));
+                        khi[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kv[w + 2], 1.0f, false));
+                        khi[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kv[w + 2], 1.0f, true));
+                        vlo[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vv[w], 1.0f, false));
+                        vlo[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vv[w], 1.0f, true));
+                        vhi[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vv[w + 2], 1.0f, false));
+                        vhi[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vv[w + 2], 1.0f, true));
                     }
-                    *reinterpret_cast<u32x4_t*>(vlds + lds_col<C::VLRB, C::VSWM>(r, 2 * c)) = lo;
-                    *reinterpret_cast<u32x4_t*>(vlds + lds_col<C::VLRB, C::VSWM>(r, 2 * c + 1)) = hi;
+                    const int o0 = lds_col<C::VLRB, C::VSWM>(r, 2 * c);
+                    const int o1 = lds_col<C::VLRB, C::VSWM>(r, 2 * c + 1);
+                    *reinterpret_cast<u32x4_t*>(klds + o0) = klo;
+                    *reinterpret_cast<u32x4_t*>(klds + o1) = khi;
+                    *reinterpret_cast<u32x4_t*>(vlds + o0) = vlo;
+                    *reinterpret_cast<u32x4_t*>(vlds + o1) = vhi;
                 }
             }
             bf16x8_t kop[C::KSW];
 #pragma unroll
-            for (int ks = 0; ks < C::KSW; ++ks) {
-                if constexpr (KV8) {
-                    const u32x2_t w = kreg[st][ks];
-                    const u32x4_t e = {
-                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false)),
-                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true)),
-                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false)),
-                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true))};
-                    kop[ks] = __builtin_bit_cast(bf16x8_t, e);
-                } else {
-                    kop[ks] = __builtin_bit_cast(bf16x8_t, kreg[st][ks]);
-                }
-            }
+            for (int ks = 0; ks < C::KSW; ++ks)
+                kop[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
+                                                           klds + lds_col<C::VLRB, C::VSWM>(col, 4 * ks + grp)));
             compiler_fence();
             const int page = pnext[st];
             pnext[st] = page_load(k + 2 * PF);
