@@ -334,7 +334,8 @@ def bench_mixed(args, batches, cu_count):
 def bench_prefill(args, batches, cu_count):
     """A prompt chunk behind a long prefix through pa_prefill alone: every query token of the chunk
     reads all the keys it sees.  Bytes counted: the request's K/V once (the algorithmic bytes); the
-    rocprofv3 FETCH_SIZE of the same command gives the re-read factor of the query blocks."""
+    rocprofv3 FETCH_SIZE of the same command gives the re-read factor of the query blocks.  One
+    workspace serves the rotated copies (calls on one stream do not overlap)."""
     from paged_split_kv_amd import binding as B
 
     stream = torch.cuda.current_stream()
@@ -342,18 +343,22 @@ def bench_prefill(args, batches, cu_count):
     K = args.steps
     order = np.arange(K) % n
     outs = [torch.empty_like(c.q) for c in batches]
-
-    def call(i):
-        c = batches[i]
-        B.pa_prefill(c.q, c.k_cache, c.v_cache, c.kv_dtype, c.block_tables, c.context_lens, c.cu_query_lens,
-                     outs[i], scale=c.scale, sliding_window=c.window)
-
-    ms = timed([lambda i=i: call(i) for i in order], stream, [lambda i=i: call(i % n) for i in range(args.warmup)])
     c0 = batches[0]
+    ws = torch.empty((B.pa_prefill_workspace_bytes(c0.num_rows, c0.num_seqs, c0.num_q_heads, c0.num_kv_heads,
+                                                   c0.head_dim, cu_count),), dtype=torch.uint8, device=c0.q.device)
+    calls = [B.pa_prefill(c.q, c.k_cache, c.v_cache, c.kv_dtype, c.block_tables, c.context_lens, c.cu_query_lens,
+                          outs[i], ws, scale=c.scale, cu_count=cu_count, sliding_window=c.window, prepare=True)
+             for i, c in enumerate(batches)]
+    ms = timed([lambda i=i: calls[i]() for i in order], stream, [lambda i=i: calls[i % n]() for i in range(args.warmup)])
+    single = None
+    if not args.step_only:
+        one = [B.pa_prefill(c.q, c.k_cache, c.v_cache, c.kv_dtype, c.block_tables, c.context_lens, c.cu_query_lens,
+                            outs[i], scale=c.scale, sliding_window=c.window, prepare=True)
+               for i, c in enumerate(batches)]
+        single = timed([lambda i=i: one[i]() for i in order], stream, [lambda: one[0]()] * 4) * 1e3 / K
     kv = np.array([float(c.kv_bytes()) for c in batches])
     r = rate(kv, order, ms)
     G = c0.num_q_heads // c0.num_kv_heads
-    from paged_split_kv_amd.binding import PA_MAX_GROUP_ROWS  # noqa: F401
     result = {
         "metric": "µs/step + achieved KV-read HBM GB/s (% peak), prompt chunk behind a long prefix (pa_prefill)",
         "value": round(r["gbps"], 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
@@ -365,7 +370,9 @@ def bench_prefill(args, batches, cu_count):
                                f"{c0.block_size}, bf16; {n} independent copies rotated",
                    "group": G},
         "us_per_step": round(r["us_per_step"], 2), "pct_hbm_peak": round(r["pct_peak"], 1),
-        "step": "pa_prefill over the chunk's query blocks",
+        "step": "pa_prefill, split form: the chunk's query blocks planned, decoded split-KV and merged "
+                "(four launches)",
+        "one_launch_form_us_per_step": None if single is None else round(single, 2),
         "roofline": {"bound": "hbm", "achieved": round(r["gbps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(r["gbps"] / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "pa_prefill",
                      "duration_us": round(r["us_per_step"], 3),

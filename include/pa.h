@@ -19,8 +19,9 @@
  *
  * pa_attention runs the same three steps with one launch fewer: the decode plans in place (for
  * batches of up to PA_INLINE_PLAN_SEQS requests) and stores the plan it used.  pa_prefill computes
- * prompt rows of a mixed batch (no plan, no workspace), and pa_attention_mixed a whole decodes-first
- * mixed batch, the decodes and the prompts sharing one launch where they fit it.
+ * prompt rows of a mixed batch (their query blocks planned, decoded and merged like requests), and
+ * pa_attention_mixed a whole decodes-first mixed batch, the decodes and the prompts sharing one launch
+ * where they fit it.
  *
  * Conventions shared by every entry point:
  *   - All array arguments are DEVICE pointers (memory of the current HIP device), except where a
@@ -261,27 +262,52 @@ pa_status pa_attention_noalloc(const void* q, pa_dtype q_dtype, int32_t num_rows
 
 /*
  * Prefill rows: attention of every query token of the given requests over its visible keys, written
- * normalised to out (no plan, no workspace).  For the decode-first split of mixed batches
- * (opengfx1030/vllm-rdna PR #29, Change 2: decode and verify rows go to the split-KV decode, the rest
- * to a prefill kernel on the rebased remainder): the caller passes the prefill requests' slices,
+ * normalised to out.  For the decode-first split of mixed batches (opengfx1030/vllm-rdna PR #29,
+ * Change 2: decode and verify rows go to the split-KV decode, the rest to a prefill kernel on the
+ * rebased remainder): the caller passes the prefill requests' slices,
  *   context_lens + nd, block_tables + nd rows, cu_query_lens + nd (absolute row numbers: row r of q
  *   and out is query token r - cu[b] of request b),
  * with q and out the whole batch's arrays and num_rows its row count.  Rows [cu[0], cu[num_seqs])
  * get attention, rows [cu[num_seqs], num_rows) zeros, rows before cu[0] are not touched.
  * Token i of a request with L tokens and S keys sees [0, S - (L - 1 - i)) (or its last
  * sliding_window keys), as in pa_decode; rows with no visible key are zeros.
- * Each workgroup takes a block of query tokens of one request and one kv head (up to 64 query rows
- * of the group: block = 64 / G tokens for head_dim <= 128, 16 / G for 256) and streams all the
- * keys the block sees, split over its waves.  K/V of bf16 or fp8 caches only (PA_UNSUPPORTED for
- * f32).  cu_query_lens is required.  Other checks as pa_decode.
+ * Two forms, chosen by the caller:
+ *   workspace NULL   each query block (64 / G tokens at head_dim <= 128, 16 / G at 256) is one
+ *                    workgroup that streams every key the block sees, in one launch: the form for
+ *                    short prompts, whose blocks see few keys.
+ *   workspace given  each request's query tokens are cut into blocks of T = 64 / G tokens (32 / G at
+ *                    head_dim 256), and the blocks are planned like requests -- the length-proportional
+ *                    rule of pa_plan over the blocks' key ranges, with budget 2 x cu_count, ceiling 256
+ *                    and 256-token tiles -- then decoded split-KV and merged: a block behind a long
+ *                    prefix reads its keys with several workgroups, and each K/V byte is read once per
+ *                    block of T tokens.  Four launches: the blocks, their plan, the decode, the merge.
+ *                    The workspace holds pa_prefill_workspace_bytes(num_rows, num_seqs, num_q_heads,
+ *                    num_kv_heads, head_dim, cu_count) bytes, 256-byte aligned, owned by the caller, with
+ *                    no initial contents needed; cu_count is the compute-unit count the budget is built
+ *                    from (pa_device_cu_count).
+ * Both forms compute the same rows up to rounding.
+ * K/V of bf16 or fp8 caches only (PA_UNSUPPORTED for f32).  cu_query_lens is required.  Errors: as
+ * pa_decode, plus, with a workspace, PA_INVALID_ARG (cu_count < 1, misaligned workspace),
+ * PA_UNSUPPORTED (more than PA_MAX_SEQS blocks), PA_CAPACITY (workspace too small).
  */
 pa_status pa_prefill(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t num_q_heads,
                      int32_t head_dim, const void* k_cache, const void* v_cache, pa_dtype kv_dtype,
                      int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
                      const int32_t* block_tables, int32_t max_blocks_per_seq,
                      const int32_t* context_lens, int32_t num_seqs, const int32_t* cu_query_lens,
-                     int32_t sliding_window, float scale, float k_scale, float v_scale, void* out,
-                     pa_dtype out_dtype, void* stream);
+                     int32_t sliding_window, float scale, float k_scale, float v_scale, int32_t cu_count,
+                     void* workspace, size_t workspace_bytes, void* out, pa_dtype out_dtype, void* stream);
+
+/*
+ * Bytes of workspace pa_prefill's split form needs for num_rows rows of num_seqs prompt requests: the
+ * query blocks' lengths, first rows and request indices (at most ceil(num_rows / T) + num_seqs blocks),
+ * their plan
+ * (work_info for the capacity formula over the blocks, reduce_info, num_work), and the fp32 partial
+ * states [capacity, T, num_q_heads, head_dim] plus (max, sum) pairs, each region 256-byte aligned.
+ * Returns 0 for invalid sizes or more than PA_MAX_SEQS blocks.  Pure host arithmetic.
+ */
+size_t pa_prefill_workspace_bytes(int32_t num_rows, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t cu_count);
 
 /*
  * A mixed batch whose requests are ordered decodes first, in one call (opengfx1030/vllm-rdna PR #29,
@@ -291,9 +317,12 @@ pa_status pa_prefill(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t 
  * and they are planned, decoded and merged exactly as pa_attention does with num_seqs = num_decodes
  * and num_rows = num_decode_rows: the plan buffers (sized for num_decodes requests), the workspace and
  * out rows [0, num_decode_rows) receive the same values.  Requests [num_decodes, num_seqs) are
- * prompts, computed as pa_prefill computes them from the slices context_lens + num_decodes,
+ * prompts, with the attention pa_prefill computes from the slices context_lens + num_decodes,
  * block_tables + num_decodes rows and cu_query_lens + num_decodes: out rows [num_decode_rows,
- * cu[num_seqs]) get their attention, rows [cu[num_seqs], num_rows) zeros.
+ * cu[num_seqs]) get their attention, rows [cu[num_seqs], num_rows) zeros.  Here each prompt query
+ * block (up to 64 / G tokens for head_dim <= 128, 16 / G for 256) is one workgroup that streams every
+ * key the block sees, with no workspace of its own: the form for short prompts beside decodes; long
+ * prompt chunks behind a prefix belong in pa_prefill.
  * Where the decode part is planned in place and the prompts' query blocks fit the decode's query
  * rows per workgroup (or can be cut to fit while there are at most 64 prompt rows), the decode and
  * the prompts share one launch (decode workgroups first, the prompts' after them) followed by the

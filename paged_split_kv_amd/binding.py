@@ -29,8 +29,8 @@ _DTYPE_OF_NAME = {"f32": PA_F32, "bf16": PA_BF16, "fp8": PA_FP8_E4M3}
 _TORCH_OF_NAME = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
 
 SYMBOLS = ("pa_plan_capacity", "pa_workspace_bytes", "pa_plan", "pa_decode", "pa_merge",
-           "pa_attention", "pa_attention_noalloc", "pa_prefill", "pa_attention_mixed", "pa_split_decode_first",
-           "pa_status_string", "pa_device_cu_count")
+           "pa_attention", "pa_attention_noalloc", "pa_prefill", "pa_prefill_workspace_bytes", "pa_attention_mixed",
+           "pa_split_decode_first", "pa_status_string", "pa_device_cu_count")
 
 
 class PaError(RuntimeError):
@@ -76,8 +76,10 @@ def load(path: str = LIB_PATH):
                                          vp, vp, vp, vp, ctypes.c_int, vp]
     lib.pa_attention_noalloc.restype = ctypes.c_int
     lib.pa_prefill.argtypes = [vp, ctypes.c_int, i32, i32, i32, vp, vp, ctypes.c_int, i32, i32, i32, vp, i32,
-                               vp, i32, vp, i32, f32, f32, f32, vp, ctypes.c_int, vp]
+                               vp, i32, vp, i32, f32, f32, f32, i32, vp, ctypes.c_size_t, vp, ctypes.c_int, vp]
     lib.pa_prefill.restype = ctypes.c_int
+    lib.pa_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.pa_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.pa_attention_mixed.argtypes = [vp, ctypes.c_int, i32, i32, i32, vp, vp, ctypes.c_int, i32, i32, i32,
                                        vp, i32, vp, i32, vp, i32, i32, i32, i32, f32, f32, f32, i32, i32,
                                        i32, i32, i32, vp, vp, vp, vp, ctypes.c_size_t, vp, ctypes.c_int, vp]
@@ -419,12 +421,20 @@ def pa_attention_mixed(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
                                      _stream(stream)), "pa_attention_mixed")
 
 
+def pa_prefill_workspace_bytes(num_rows: int, num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                               head_dim: int, cu_count: int) -> int:
+    return int(load().pa_prefill_workspace_bytes(num_rows, num_seqs, num_q_heads, num_kv_heads, head_dim, cu_count))
+
+
 def pa_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_dtype: str,
                block_tables: torch.Tensor, context_lens: torch.Tensor, cu_query_lens: torch.Tensor,
-               out: torch.Tensor, *, scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
-               sliding_window: int = 0, stream=None) -> None:
+               out: torch.Tensor, workspace: Optional[torch.Tensor] = None, *, scale: float, cu_count: int = 0,
+               k_scale: float = 1.0, v_scale: float = 1.0, sliding_window: int = 0, stream=None,
+               prepare: bool = False):
     """Prefill rows of the given requests into out (see include/pa.h).  q and out are the whole
-    batch's [R, Hq, D] arrays; cu_query_lens holds absolute row numbers (a slice of the batch's)."""
+    batch's [R, Hq, D] arrays; cu_query_lens holds absolute row numbers (a slice of the batch's).
+    Without a workspace the one-launch form runs; with one (a uint8 device tensor of
+    pa_prefill_workspace_bytes(...) bytes, and cu_count) the split form."""
     dev = q.device
     if q.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("q must be float32 or bfloat16")
@@ -435,6 +445,8 @@ def pa_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv
     _need(block_tables, "block_tables", torch.int32, dev)
     _need(context_lens, "context_lens", torch.int32, dev)
     _need(cu_query_lens, "cu_query_lens", torch.int32, dev)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, dev)
     if tuple(out.shape) != tuple(q.shape):
         raise ValueError("out must have the shape of q")
     R, Hq, D = q.shape
@@ -445,10 +457,11 @@ def pa_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv
     if block_tables.dim() != 2 or block_tables.shape[0] != B or cu_query_lens.shape[0] != B + 1:
         raise ValueError("block_tables must be [num_seqs, max_blocks], cu_query_lens [num_seqs + 1]")
     qd = PA_F32 if q.dtype == torch.float32 else PA_BF16
-    _check(load().pa_prefill(_ptr(q), qd, R, Hq, D, _ptr(k_cache), _ptr(v_cache), _DTYPE_OF_NAME[kv_dtype], nb,
-                             Hkv, bs, _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), B,
-                             _ptr(cu_query_lens), sliding_window, scale, k_scale, v_scale, _ptr(out), qd,
-                             _stream(stream)), "pa_prefill")
+    args = (_ptr(q), qd, R, Hq, D, _ptr(k_cache), _ptr(v_cache), _DTYPE_OF_NAME[kv_dtype], nb, Hkv, bs,
+            _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), B, _ptr(cu_query_lens),
+            sliding_window, scale, k_scale, v_scale, int(cu_count), _ptr(workspace),
+            0 if workspace is None else workspace.numel(), _ptr(out), qd, _stream(stream))
+    return _issue(load().pa_prefill, args, "pa_prefill", prepare)
 
 
 def pa_split_decode_first(cu_query_lens_host, threshold: int) -> Tuple[int, int]:

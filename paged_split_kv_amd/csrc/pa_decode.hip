@@ -591,7 +591,9 @@ __global__ __launch_bounds__((64 * NWAVES), (Mfma<D, NCB, KV8, NWAVES>::WAVES)) 
     }
     const int b = wk.x;
     if (b < 0 || b >= a.num_seqs) return;
-    const int* bt_row = a.block_tables + static_cast<size_t>(b) * a.max_blocks;
+    // query blocks of a prefill read their request's block-table row
+    const int bt_b = a.bt_index ? __builtin_amdgcn_readfirstlane(a.bt_index[b]) : b;
+    const int* bt_row = a.block_tables + static_cast<size_t>(bt_b) * a.max_blocks;
     const long long reach = static_cast<long long>(a.max_blocks) * a.block_size;
     const int plan_lo = static_cast<int>(min(key_lo, reach));
     const int plan_hi = static_cast<int>(max(min(key_hi, reach), static_cast<long long>(plan_lo)));

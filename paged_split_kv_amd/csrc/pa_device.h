@@ -256,6 +256,7 @@ struct DecodeArgs {
     const int32_t* num_work;
     float* ws_acc;
     float* ws_ml;
+    const int32_t* bt_index;    // nullable: request b's block-table row is bt_index[b] (query blocks)
     void* out;                  // prefill mode only: the normalised rows are written here
     int window;                 // 0: none; W > 0: each query token sees its last W visible keys
     // prefill mode: each workgroup takes a block of up to block_tokens query tokens of one request
@@ -299,6 +300,7 @@ struct MergeArgs {
     const int2* reduce_info;
     const float* ws_acc;
     const float* ws_ml;
+    const int32_t* row_floor;   // nullable: rows below *row_floor are left untouched
     void* out;
     int num_rows, num_q_heads, num_seqs, max_q_len, capacity;
 };
@@ -340,6 +342,9 @@ inline bool shares_slots(int one_slot_cap, int num_seqs, int head_dim, int capac
 hipError_t launch_plan(const int32_t* context_lens, const int32_t* cu, int num_seqs,
                        int cap_formula, int capacity, int max_partitions, int tile_tokens, int window,
                        int32_t* work_info, int32_t* reduce_info, int32_t* num_work, hipStream_t stream);
+hipError_t launch_prefill_blocks(const int32_t* context_lens, const int32_t* cu, int num_seqs, int block_tokens,
+                                 int max_blocks, int32_t* blk_ctx, int32_t* blk_cu, int32_t* blk_req,
+                                 hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, pa_dtype kv_dtype, bool q_f32,
                          hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int head_dim, bool out_bf16, hipStream_t stream);

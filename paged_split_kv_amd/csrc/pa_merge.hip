@@ -54,6 +54,7 @@ __global__ __launch_bounds__(NT) void merge_kernel(const MergeArgs a) {
     const int pg = tid / NDC;
     const int r = pair / a.num_q_heads;
     const int h = pair - r * a.num_q_heads;
+    if (a.row_floor && r < *a.row_floor) return;     // the whole workgroup: before any barrier
 
     int i;
     const int b = owner_of_row(a.cu, a.num_seqs, a.max_q_len, r, i);

@@ -121,7 +121,66 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     }
 }
 
+// Query blocks of a prefill batch as pseudo-requests for the planner, the decode and the merge: each
+// request's query tokens [0, L_b) are cut into blocks of block_tokens, numbered request by request.
+// Block j covering tokens [i0, i1) of request b gets
+//   blk_cu[j] = cu[b] + i0                (its first row; blk_cu[max_blocks] = cu[num_seqs]),
+//   blk_ctx[j] = S_b - (L_b - i1)         (the keys its last token sees, at least 0),
+//   blk_req[j] = b                        (the request's block-table row),
+// so that token i of the block sees blk_ctx[j] - (i1 - 1 - i) = S_b - (L_b - 1 - i) keys, the
+// request's own per-token causal range (opengfx1030/vllm-rdna PR #29, Change 1).  Slots past the last
+// block are empty blocks (blk_cu = cu[num_seqs], blk_ctx = 0, blk_req = 0).  Each thread takes a
+// contiguous run of requests; a scan over the threads gives each run's first block.
+__global__ __launch_bounds__(kPlanThreads) void prefill_blocks_kernel(
+    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ cu, int num_seqs, int block_tokens,
+    int max_blocks, int32_t* __restrict__ blk_ctx, int32_t* __restrict__ blk_cu, int32_t* __restrict__ blk_req) {
+    __shared__ int scan_carry[kPlanWaves];
+    __shared__ int s_total;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int per = (num_seqs + kPlanThreads - 1) / kPlanThreads;
+    const int b0 = min(tid * per, num_seqs);
+    const int b1 = min(b0 + per, num_seqs);
+    auto q_len = [&](int b) { return max(cu[b + 1] - cu[b], 0); };
+    int local = 0;
+    for (int b = b0; b < b1; ++b) local += (q_len(b) + block_tokens - 1) / block_tokens;
+    const int incl = wave_incl_scan(local, lane);
+    if (lane == 63) scan_carry[wave] = incl;
+    __syncthreads();
+    int j = incl - local;
+    for (int w = 0; w < wave; ++w) j += scan_carry[w];
+    if (tid == kPlanThreads - 1) s_total = j + local;
+    for (int b = b0; b < b1; ++b) {
+        const int L = q_len(b);
+        const int S = max(context_lens[b], 0);
+        const int row = cu[b];
+        for (int i0 = 0; i0 < L && j < max_blocks; i0 += block_tokens, ++j) {
+            const int i1 = min(L, i0 + block_tokens);
+            blk_cu[j] = row + i0;
+            blk_ctx[j] = max(S - (L - i1), 0);
+            blk_req[j] = b;
+        }
+    }
+    __syncthreads();
+    const int end = cu[num_seqs];
+    for (int e = max(s_total, 0) + tid; e < max_blocks; e += kPlanThreads) {
+        blk_cu[e] = end;
+        blk_ctx[e] = 0;
+        blk_req[e] = 0;
+    }
+    if (tid == 0) blk_cu[max_blocks] = end;
+}
+
 }  // namespace
+
+hipError_t launch_prefill_blocks(const int32_t* context_lens, const int32_t* cu, int num_seqs, int block_tokens,
+                                 int max_blocks, int32_t* blk_ctx, int32_t* blk_cu, int32_t* blk_req,
+                                 hipStream_t stream) {
+    hipLaunchKernelGGL(prefill_blocks_kernel, dim3(1), dim3(kPlanThreads), 0, stream, context_lens, cu, num_seqs,
+                       block_tokens, max_blocks, blk_ctx, blk_cu, blk_req);
+    return hipGetLastError();
+}
 
 hipError_t launch_plan(const int32_t* context_lens, const int32_t* cu, int num_seqs, int cap_formula,
                        int capacity, int max_partitions, int tile_tokens, int window,

@@ -121,7 +121,8 @@ def run_case(case, plan: Optional[PlanConfig] = None, fused: bool = True,
 class MixedStep:
     """The decode-first split of a mixed batch (requests ordered decodes first): the leading requests
     with at most `threshold` query tokens go through pa_attention (split-KV decode, rows written to a
-    view of the output), the rest through pa_prefill on the same stream.  The split is taken from a
+    view of the output), the rest through pa_prefill's one-launch form (short prompts) on the same
+    stream.  The split is taken from a
     host copy of the cumulative query lengths, as a batch builder holds them; buffers are made once.
     With concurrent=True the two parts, which read the same inputs and write disjoint rows, run on
     two streams (the prefill on a second stream of default priority) and join before returning.

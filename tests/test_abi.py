@@ -248,12 +248,32 @@ def test_merge_refuses_misaligned_out():
 
 def _prefill_status(**kw):
     a = dict(_GOOD)
-    a.update(dict(cu=256, out=512))
+    a.update(dict(cu=256, out=512, cuc=256, pws=1024, pwsb=1 << 30))
     a.update(kw)
     vp = lambda x: None if x is None else ctypes.c_void_p(x)
     return B.load().pa_prefill(vp(a["q"]), a["qd"], a["R"], a["Hq"], a["D"], vp(a["k"]), vp(a["v"]), a["kvd"],
                                a["nb"], a["Hkv"], a["bs"], vp(a["bt"]), a["mb"], vp(a["ctx"]), a["Bn"],
-                               vp(a["cu"]), a["win"], a["scale"], a["ks"], a["vs"], vp(a["out"]), a["od"], None)
+                               vp(a["cu"]), a["win"], a["scale"], a["ks"], a["vs"], a["cuc"], vp(a["pws"]),
+                               a["pwsb"], vp(a["out"]), a["od"], None)
+
+
+def test_prefill_workspace_bytes():
+    # blocks of T = 64 / G tokens (32 / G at head_dim 256), at most ceil(R / T) + B of them; capacity
+    # formula over the blocks
+    # (budget 2 x CU, ceiling 256); regions: lengths, first rows (+1), request indices, work_info,
+    # reduce_info, num_work, then the partial states [C, T, Hq, D] fp32 and (m, l) pairs, each 256-aligned
+    up = lambda x: (x + 255) // 256 * 256
+    for R, Bn, hq, hkv, d, cu in [(512, 1, 12, 2, 256, 256), (33, 4, 16, 2, 128, 256), (1000, 7, 8, 8, 64, 80),
+                                  (0, 0, 4, 1, 128, 256)]:
+        T = max(1, (32 if d == 256 else 64) // (hq // hkv))
+        nb = (R + T - 1) // T + Bn
+        cap = min(nb * 256, max(nb, -(-2 * cu // hkv)))
+        want = (up(4 * nb) + up(4 * (nb + 1)) + up(4 * nb) + up(16 * cap) + up(8 * nb) + up(8)
+                + up(cap * T * hq * d * 4) + up(cap * T * hq * 2 * 4))
+        assert B.pa_prefill_workspace_bytes(R, Bn, hq, hkv, d, cu) == want, (R, Bn, hq, hkv, d, cu)
+    assert B.pa_prefill_workspace_bytes(8192 * 64, 1, 64, 1, 128, 256) == 0          # more than 8192 blocks
+    assert B.pa_prefill_workspace_bytes(10, 1, 12, 5, 128, 256) == 0                  # heads not a multiple
+    assert B.pa_prefill_workspace_bytes(10, 1, 4, 1, 128, 0) == 0
 
 
 def test_prefill_argument_checks():
@@ -268,6 +288,10 @@ def test_prefill_argument_checks():
     assert _prefill_status(out=520) == B.PA_INVALID_ARG
     assert _prefill_status(win=-1) == B.PA_INVALID_ARG
     assert _prefill_status(scale=float("nan")) == B.PA_INVALID_ARG
+    assert _prefill_status(cuc=0) == B.PA_INVALID_ARG
+    assert _prefill_status(pws=None, R=0) == B.PA_OK                # the one-launch form: no workspace
+    assert _prefill_status(pws=1032) == B.PA_INVALID_ARG            # workspace 256-byte aligned
+    assert _prefill_status(pwsb=4096) == B.PA_CAPACITY
     assert _prefill_status(R=0) == B.PA_OK                         # nothing to write: no launch
 
 

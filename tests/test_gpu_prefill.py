@@ -37,6 +37,21 @@ PREFILL = [
 ]
 
 
+def _prefill(case, out, *, requests=slice(None), cu_count=256, split=True):
+    """pa_prefill over the given requests (a slice of the batch): the split form with its own workspace,
+    or the one-launch form."""
+    bt, ctx = case.block_tables[requests], case.context_lens[requests]
+    n = int(ctx.shape[0])
+    cu = case.cu_query_lens[requests.start or 0:(requests.start or 0) + n + 1]
+    ws = None
+    if split:
+        nbytes = B.pa_prefill_workspace_bytes(case.num_rows, n, case.num_q_heads, case.num_kv_heads, case.head_dim,
+                                              cu_count)
+        ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=DEV)     # no initial contents needed
+    B.pa_prefill(case.q, case.k_cache, case.v_cache, case.kv_dtype, bt, ctx, cu, out, ws, scale=case.scale,
+                 cu_count=cu_count, k_scale=case.k_scale, v_scale=case.v_scale, sliding_window=case.window)
+
+
 def _case(spec, seed):
     name, ctx, ql, Hq, Hkv, D, bs, kv, qd, pad, win = spec
     c = W.build_case(name, ctx, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs, kv_dtype=kv,
@@ -45,31 +60,78 @@ def _case(spec, seed):
     return c
 
 
+@pytest.mark.parametrize("split", [True, False], ids=["split", "one_launch"])
 @pytest.mark.parametrize("spec", PREFILL, ids=[p[0] for p in PREFILL])
-def test_prefill_matches_oracle(spec):
+def test_prefill_matches_oracle(spec, split):
     case = _case(spec, seed=41)
-    announce(f"prefill {spec[0]}")
+    announce(f"prefill {spec[0]} split={split}")
     out = torch.full_like(case.q, float("nan"))
-    B.pa_prefill(case.q, case.k_cache, case.v_cache, case.kv_dtype, case.block_tables, case.context_lens,
-                 case.cu_query_lens, out, scale=case.scale, k_scale=case.k_scale, v_scale=case.v_scale,
-                 sliding_window=case.window)
+    _prefill(case, out, split=split)
     torch.cuda.synchronize()
     got = to_f64(out)
     assert_close(got, oracle_direct(case), tolerance_kind(case), spec[0])
     assert (got[_zero_rows(case)] == 0.0).all()
 
 
-def test_prefill_leaves_rows_before_its_first_request_alone():
+@pytest.mark.parametrize("split", [True, False], ids=["split", "one_launch"])
+def test_prefill_leaves_rows_before_its_first_request_alone(split):
     case = _case(PREFILL[0], seed=42)
     # treat requests 1.. as the prefill part: rows [cu[1], R) are written, rows before stay poisoned
     out = torch.full_like(case.q, float("nan"))
-    B.pa_prefill(case.q, case.k_cache, case.v_cache, case.kv_dtype, case.block_tables[1:], case.context_lens[1:],
-                 case.cu_query_lens[1:], out, scale=case.scale)
+    _prefill(case, out, requests=slice(1, None), split=split)
     torch.cuda.synchronize()
     c1 = int(case.cu_query_lens[1].item())
     got = to_f64(out)
     assert np.isnan(got[:c1]).all()
     assert_close(got[c1:], oracle_direct(case)[c1:], "bf16", "prefill part")
+
+
+# prompt chunks behind long prefixes: several blocks per request, each block's keys split over several
+# workgroups by the plan; a small budget (cu_count) makes slots of many tiles, a large one many slots
+LONG_PREFIX = [
+    ("d256_g6_chunk_behind_3000", [3096], [96], 12, 2, 256, 16, "bf16", "bf16", 1, 0, 256),
+    ("d128_g8_two_chunks", [4100, 2600], [200, 130], 16, 2, 128, 16, "bf16", "bf16", 0, 0, 256),
+    ("d128_fp8_small_budget", [5000, 64], [150, 64], 16, 2, 128, 64, "fp8", "bf16", 2, 0, 8),
+    ("d64_g4_window", [6000], [300], 8, 2, 64, 16, "bf16", "bf16", 0, 500, 256),
+    ("d256_fp8_window", [3000, 700], [70, 40], 12, 2, 256, 16, "fp8", "bf16", 0, 1000, 64),
+    # more blocks than the budget's slots: every block one slot
+    ("d128_g16_many_blocks", [3000, 2000], [1100, 900], 16, 1, 128, 16, "bf16", "bf16", 0, 0, 64),
+    # a request whose query outnumbers its keys (precondition edge): early tokens see nothing
+    ("d128_tokens_without_keys", [40, 900], [100, 50], 8, 2, 128, 16, "bf16", "f32", 1, 0, 256),
+]
+
+
+@pytest.mark.parametrize("spec", LONG_PREFIX, ids=[p[0] for p in LONG_PREFIX])
+def test_prefill_chunks_behind_long_prefixes(spec):
+    case = _case(spec[:11], seed=44)
+    cu_count = spec[11]
+    announce(f"prefill behind a prefix {spec[0]}")
+    out = torch.full_like(case.q, float("nan"))
+    _prefill(case, out, cu_count=cu_count)
+    torch.cuda.synchronize()
+    got = to_f64(out)
+    assert_close(got, oracle_direct(case), tolerance_kind(case), spec[0])
+    assert (got[_zero_rows(case)] == 0.0).all()
+
+
+def test_prefill_chunk_of_the_bench_at_full_size():
+    """The 512-token chunk behind a 16384-token prefix (Hq 12 / Hkv 2, D 256) that bench.py times:
+    sampled rows against the oracle, computed one by one."""
+    case = W.make_prefill_chunk_case(device=DEV)
+    announce("prefill chunk 512 behind 16384, full size")
+    out = torch.full_like(case.q, float("nan"))
+    _prefill(case, out, cu_count=B.pa_device_cu_count(0))
+    torch.cuda.synchronize()
+    # block edges (5 tokens per block at G = 6, head_dim 256) and the chunk's ends, every head of each row
+    rows = np.repeat(np.array([0, 1, 4, 5, 6, 255, 256, 400, 509, 510, 511]), case.num_q_heads)
+    heads = np.tile(np.arange(case.num_q_heads), rows.shape[0] // case.num_q_heads)
+    h = case.host()
+    ref = oracle.attention_rows(h["q"], case.q_dtype, h["k_cache"], h["v_cache"], case.kv_dtype, h["block_tables"],
+                                h["context_lens"], h["cu_query_lens"], case.scale, rows, heads, case.k_scale,
+                                case.v_scale)
+    got = to_f64(out)
+    assert_close(got[rows, heads], ref, "bf16", "prefill chunk rows")
+    assert np.isfinite(got).all()
 
 
 # (name, ctx, q_lens, Hq, Hkv, D, bs, kv, q, pad, window, threshold)
