@@ -503,20 +503,25 @@ def main():
     order = step_order(K, nsteps)
     full_order = step_order(4 * nsteps, nsteps, seed=1)                # four whole passes
 
-    # every step's plan, made once beforehand (as a forward shares one plan across its layers)
-    plans = []
+    # every step's plan, made once beforehand (as a forward shares one plan across its layers), with
+    # the decode's dispatch order beside it
+    plans, disps = [], []
     for c in batches:
+        d = torch.empty((step.capacity, 4), dtype=torch.int32, device=dev)
         w, r, n = B.pa_plan(c.context_lens, Hkv, cu_count=cu_count, max_partitions=max_parts, tile_tokens=T,
-                            capacity=step.capacity, cu_query_lens=c.cu_query_lens, sliding_window=win)
+                            capacity=step.capacity, cu_query_lens=c.cu_query_lens, sliding_window=win,
+                            dispatch_info=d)
         plans.append((w, r, n))
+        disps.append(d)
     torch.cuda.synchronize()
     ws, out = step.workspace, step.out
 
-    def dec_call(i, prepare=True):
+    def dec_call(i, prepare=True, dispatch=True):
         c, (w, r, n) = batches[i], plans[i]
         return B.pa_decode(c.q, c.k_cache, c.v_cache, c.kv_dtype, c.block_tables, c.context_lens, w, n, ws,
                            scale=c.scale, cu_query_lens=c.cu_query_lens, max_q_len=c.max_q_len, k_scale=c.k_scale,
-                           v_scale=c.v_scale, tile_tokens=T, sliding_window=win, prepare=prepare)
+                           v_scale=c.v_scale, tile_tokens=T, sliding_window=win,
+                           dispatch_info=disps[i] if dispatch else None, prepare=prepare)
 
     def mrg_call(i, prepare=True):
         c, (w, r, n) = batches[i], plans[i]
@@ -579,16 +584,20 @@ def main():
                                "tile_tokens": T, "capacity": step.capacity}},
         "us_per_step": round(head["us_per_step"], 2),
         "pct_hbm_peak": round(head["pct_peak"], 1),
-        "step": "pa_decode + pa_merge (two launches), each step's plan made once beforehand",
+        "step": "pa_decode (in the plan's dispatch order) + pa_merge (two launches), each step's plan and "
+                "dispatch order made once beforehand",
         "timed_wall_s": round(wall, 3),
     }
     if args.step_only:
         print(json.dumps(result), flush=True)
         return
 
-    # the decode kernel alone, back to back over the same order (the roofline kernel)
+    # the decode kernel alone, back to back over the same order (the roofline kernel); and in slot
+    # order, without the plan's dispatch order
     dec_ms = timed([lambda i=i: dec_p[i]() for i in order], stream, [lambda: dec_p[0]()] * 8)
     dec = rate(kv_bytes, order, dec_ms)
+    dec_s = [dec_call(i, dispatch=False) for i in range(nsteps)]
+    dec_slot_ms = timed([lambda i=i: dec_s[i]() for i in order], stream, [lambda: dec_s[0]()] * 8)
     # the decode-shaped gather over the same plans and order: the same K/V bytes, no arithmetic
     sink = P.sink_for(4 * step.capacity * Hkv, dev)
     gat_p = [P.pa_probe_gather(c.k_cache, c.v_cache, c.kv_dtype, c.block_tables, c.context_lens, w, n, sink,
@@ -600,7 +609,8 @@ def main():
     # the plan alone (its per-forward refresh), the one-call and three-call forms, same order
     plan_p = [B.pa_plan(c.context_lens, Hkv, cu_count=cu_count, max_partitions=max_parts, tile_tokens=T,
                         capacity=step.capacity, work_info=step.work_info, reduce_info=step.reduce_info,
-                        num_work=step.num_work, cu_query_lens=c.cu_query_lens, sliding_window=win, prepare=True)
+                        num_work=step.num_work, cu_query_lens=c.cu_query_lens, sliding_window=win,
+                        dispatch_info=step.dispatch_info, prepare=True)
               for c in batches]
     plan_ms = timed([lambda i=i: plan_p[i]() for i in order], stream, [lambda: plan_p[0]()] * 8)
     att_p = [B.pa_attention(c.q, c.k_cache, c.v_cache, c.kv_dtype, c.block_tables, c.context_lens, step.work_info,
@@ -609,17 +619,18 @@ def main():
                             max_q_len=c.max_q_len, k_scale=c.k_scale, v_scale=c.v_scale, sliding_window=win,
                             prepare=True) for c in batches]
     att_ms = timed([lambda i=i: att_p[i]() for i in order], stream, [lambda: att_p[0]()] * 8)
-    dec_s = [B.pa_decode(c.q, c.k_cache, c.v_cache, c.kv_dtype, c.block_tables, c.context_lens, step.work_info,
+    dec_3 = [B.pa_decode(c.q, c.k_cache, c.v_cache, c.kv_dtype, c.block_tables, c.context_lens, step.work_info,
                          step.num_work, ws, scale=c.scale, cu_query_lens=c.cu_query_lens, max_q_len=c.max_q_len,
-                         k_scale=c.k_scale, v_scale=c.v_scale, tile_tokens=T, sliding_window=win, prepare=True)
+                         k_scale=c.k_scale, v_scale=c.v_scale, tile_tokens=T, sliding_window=win,
+                         dispatch_info=step.dispatch_info, prepare=True)
              for c in batches]
-    mrg_s = [B.pa_merge(out, step.reduce_info, ws, capacity=step.capacity, cu_query_lens=c.cu_query_lens,
+    mrg_3 = [B.pa_merge(out, step.reduce_info, ws, capacity=step.capacity, cu_query_lens=c.cu_query_lens,
                         max_q_len=c.max_q_len, prepare=True) for c in batches]
 
     def three(i):
         plan_p[i]()
-        dec_s[i]()
-        mrg_s[i]()
+        dec_3[i]()
+        mrg_3[i]()
 
     three_ms = timed([lambda i=i: three(i) for i in order], stream, [lambda: three(0)] * 8)
 
@@ -695,6 +706,7 @@ def main():
         "plan_decode_merge_us_per_step": round(three_ms * 1e3 / K, 2),
         "pa_attention_us_per_step": round(att_ms * 1e3 / K, 2),
         "kernel_us": {"pa_decode_back_to_back": round(dec["us_per_step"], 2),
+                      "pa_decode_in_slot_order": round(dec_slot_ms * 1e3 / K, 2),
                       "decode_shaped_gather_back_to_back": round(gat["us_per_step"], 2),
                       "evented": {"pa_decode": round(float(ev_dec.mean()), 2),
                                   "pa_merge": round(float(ev_mrg.mean()), 2),

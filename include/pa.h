@@ -125,6 +125,13 @@ size_t pa_workspace_bytes(int32_t capacity, int32_t max_q_len, int32_t num_q_hea
  * Without a window this is the plain rule over [0, S_b).  Every slot of work_info is
  * rewritten (unused ones to (-1, 0, 0, 0)), so a plan never carries data from an earlier call.
  * num_work receives the number of used slots and the tile count of the largest slot.
+ * dispatch_info (nullable, [capacity, 4], 16-byte aligned) receives, besides the plan, an order in
+ * which pa_decode can run the slots: the slots ranked by tile count (largest first, ties by slot
+ * index, unused slots last), rank r at position r when r < half = ceil(capacity / 2) and at position
+ * capacity + half - 1 - r otherwise, each entry (request, tile_begin, tile_end, slot).  Positions p
+ * and p + half hold ranks p and capacity - 1 - p, so where two workgroups share a compute unit a large
+ * slot pairs with a small one.  This is this library's scheduling, not part of the plan; plans of
+ * more than 2048 slots get the identity order.
  * Negative S_b (a precondition violation) are planned as 0.
  * Errors: PA_INVALID_ARG (null pointers, num_seqs < 0, arguments < 1), PA_UNSUPPORTED
  * (num_seqs > PA_MAX_SEQS), PA_CAPACITY (capacity too small), PA_HIP_ERROR (launch failure).
@@ -132,7 +139,7 @@ size_t pa_workspace_bytes(int32_t capacity, int32_t max_q_len, int32_t num_q_hea
 pa_status pa_plan(const int32_t* context_lens, const int32_t* cu_query_lens, int32_t num_seqs,
                   int32_t num_kv_heads, int32_t cu_count, int32_t budget_mult, int32_t max_partitions,
                   int32_t tile_tokens, int32_t sliding_window, int32_t capacity, int32_t* work_info,
-                  int32_t* reduce_info, int32_t* num_work, void* stream);
+                  int32_t* reduce_info, int32_t* num_work, int32_t* dispatch_info, void* stream);
 
 /*
  * Split-KV decode: for every used plan slot w = (b, tile_begin, tile_end, .) and kv head g, one
@@ -155,6 +162,10 @@ pa_status pa_plan(const int32_t* context_lens, const int32_t* cu_query_lens, int
  *   scale, k_scale, v_scale    softmax scale (typically 1/sqrt(head_dim)) and per-tensor dequant scales
  *   work_info, reduce_info,    the plan from pa_plan (capacity slots); reduce_info is only read when
  *   num_work                   out is given and may then not be NULL
+ *   dispatch_info              NULL, or pa_plan's dispatch order for the same plan: workgroup position
+ *                              p then runs the slot dispatch_info[p] names (word 3) instead of slot p;
+ *                              the states go to the same places either way (bf16 and fp8 caches; the
+ *                              f32 kernel and shared slots keep slot order)
  *   tile_tokens                the plan's tile size; a multiple of block_size
  *   workspace                  pa_workspace_bytes(capacity, max_q_len, num_q_heads, head_dim) bytes;
  *                              at least the slot states (that size without the shared-slot region,
@@ -187,8 +198,9 @@ pa_status pa_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t n
                     const int32_t* context_lens, int32_t num_seqs, const int32_t* cu_query_lens,
                     int32_t max_q_len, int32_t sliding_window, float scale, float k_scale,
                     float v_scale, const int32_t* work_info, const int32_t* reduce_info,
-                    const int32_t* num_work, int32_t capacity, int32_t tile_tokens, void* workspace,
-                    size_t workspace_bytes, void* out, pa_dtype out_dtype, void* stream);
+                    const int32_t* num_work, const int32_t* dispatch_info, int32_t capacity,
+                    int32_t tile_tokens, void* workspace, size_t workspace_bytes, void* out,
+                    pa_dtype out_dtype, void* stream);
 
 /*
  * Log-sum-exp merge.  For output row r and head h: the owning request b is found by binary search

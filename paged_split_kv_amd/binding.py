@@ -58,10 +58,10 @@ def load(path: str = LIB_PATH):
     lib.pa_plan_capacity.restype = ctypes.c_int
     lib.pa_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.pa_workspace_bytes.restype = ctypes.c_size_t
-    lib.pa_plan.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]
+    lib.pa_plan.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]
     lib.pa_plan.restype = ctypes.c_int
     lib.pa_decode.argtypes = [vp, ctypes.c_int, i32, i32, i32, vp, vp, ctypes.c_int, i32, i32, i32,
-                              vp, i32, vp, i32, vp, i32, i32, f32, f32, f32, vp, vp, vp, i32, i32, vp,
+                              vp, i32, vp, i32, vp, i32, i32, f32, f32, f32, vp, vp, vp, vp, i32, i32, vp,
                               ctypes.c_size_t, vp, ctypes.c_int, vp]
     lib.pa_decode.restype = ctypes.c_int
     lib.pa_merge.argtypes = [i32, i32, i32, i32, vp, i32, vp, i32, vp, ctypes.c_size_t, vp,
@@ -175,12 +175,14 @@ def pa_plan(context_lens: torch.Tensor, num_kv_heads: int, *, cu_count: int, bud
             max_partitions: int = 256, tile_tokens: int = 256, capacity: Optional[int] = None,
             work_info: Optional[torch.Tensor] = None, reduce_info: Optional[torch.Tensor] = None,
             num_work: Optional[torch.Tensor] = None, cu_query_lens: Optional[torch.Tensor] = None,
-            sliding_window: int = 0, stream=None, prepare: bool = False):
+            sliding_window: int = 0, dispatch_info: Optional[torch.Tensor] = None, stream=None,
+            prepare: bool = False):
     """Plan on the device.  Returns (work_info [capacity, 4], reduce_info [B, 2], num_work [2] =
     (used slots, tiles of the largest slot)), all int32 on the device of context_lens; passed-in
     buffers are refilled in place.  With a sliding window the plan covers the windowed key ranges
-    (cu_query_lens gives the query lengths).  With prepare=True nothing is launched and a Prepared
-    call is returned instead."""
+    (cu_query_lens gives the query lengths).  dispatch_info (int32 [capacity, 4]) also receives the
+    decode's dispatch order.  With prepare=True nothing is launched and a Prepared call is returned
+    instead."""
     _need(context_lens, "context_lens", torch.int32)
     dev = context_lens.device
     B = int(context_lens.shape[0])
@@ -201,9 +203,13 @@ def pa_plan(context_lens: torch.Tensor, num_kv_heads: int, *, cu_count: int, bud
     _need(num_work, "num_work", torch.int32, dev)
     if work_info.numel() < 4 * capacity or reduce_info.numel() < 2 * B or num_work.numel() < 2:
         raise ValueError("plan buffers smaller than capacity / num_seqs / 2")
+    if dispatch_info is not None:
+        _need(dispatch_info, "dispatch_info", torch.int32, dev)
+        if dispatch_info.numel() < 4 * capacity:
+            raise ValueError("dispatch_info smaller than capacity")
     args = (_ptr(context_lens), _ptr(cu_query_lens), B, num_kv_heads, cu_count, budget_mult, max_partitions,
             tile_tokens, sliding_window, capacity, _ptr(work_info), _ptr(reduce_info), _ptr(num_work),
-            _stream(stream))
+            _ptr(dispatch_info), _stream(stream))
     prepared = _issue(load().pa_plan, args, "pa_plan", prepare)
     return prepared if prepare else (work_info, reduce_info, num_work)
 
@@ -214,7 +220,8 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_
               cu_query_lens: Optional[torch.Tensor] = None, max_q_len: int = 1,
               k_scale: float = 1.0, v_scale: float = 1.0, tile_tokens: int = 256,
               reduce_info: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-              sliding_window: int = 0, stream=None, prepare: bool = False):
+              sliding_window: int = 0, dispatch_info: Optional[torch.Tensor] = None, stream=None,
+              prepare: bool = False):
     """Split-KV decode into the workspace (see include/pa.h).  kv_dtype is "f32", "bf16" or
     "fp8" (uint8 tensors holding OCP e4m3fn codes).  With ``out`` (and ``reduce_info``) the merge
     runs in the same call.  With prepare=True nothing is launched and a Prepared call is returned."""
@@ -239,6 +246,10 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_
             raise ValueError("reduce_info is required when out is given")
     if reduce_info is not None:
         _need(reduce_info, "reduce_info", torch.int32, dev)
+    if dispatch_info is not None:
+        _need(dispatch_info, "dispatch_info", torch.int32, dev)
+        if dispatch_info.numel() < work_info.numel():
+            raise ValueError("dispatch_info smaller than work_info")
     R, Hq, D = q.shape
     nb, Hkv, bs, D2 = k_cache.shape
     if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
@@ -253,7 +264,7 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_
             _ptr(k_cache), _ptr(v_cache), _DTYPE_OF_NAME[kv_dtype], nb, Hkv, bs,
             _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), B,
             _ptr(cu_query_lens), max_q_len, sliding_window, scale, k_scale, v_scale,
-            _ptr(work_info), _ptr(reduce_info), _ptr(num_work), capacity, tile_tokens,
+            _ptr(work_info), _ptr(reduce_info), _ptr(num_work), _ptr(dispatch_info), capacity, tile_tokens,
             _ptr(workspace), workspace.numel(), _ptr(out),
             PA_F32 if q.dtype == torch.float32 else PA_BF16, _stream(stream))
     return _issue(load().pa_decode, args, "pa_decode", prepare)

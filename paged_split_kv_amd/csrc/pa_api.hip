@@ -368,14 +368,15 @@ size_t pa_workspace_bytes(int32_t capacity, int32_t max_q_len, int32_t num_q_hea
 pa_status pa_plan(const int32_t* context_lens, const int32_t* cu_query_lens, int32_t num_seqs,
                   int32_t num_kv_heads, int32_t cu_count, int32_t budget_mult, int32_t max_partitions,
                   int32_t tile_tokens, int32_t sliding_window, int32_t capacity, int32_t* work_info,
-                  int32_t* reduce_info, int32_t* num_work, void* stream) {
+                  int32_t* reduce_info, int32_t* num_work, int32_t* dispatch_info, void* stream) {
     int32_t cap = 0;
     const pa_status st = check_plan(context_lens, num_seqs, num_kv_heads, cu_count, budget_mult,
                                     max_partitions, tile_tokens, sliding_window, capacity, work_info,
                                     reduce_info, num_work, &cap);
     if (st != PA_OK) return st;
+    if (dispatch_info && !aligned(dispatch_info, 16)) return PA_INVALID_ARG;
     return from_hip(pa::launch_plan(context_lens, cu_query_lens, num_seqs, cap, capacity, max_partitions,
-                                    tile_tokens, sliding_window, work_info, reduce_info, num_work,
+                                    tile_tokens, sliding_window, work_info, reduce_info, num_work, dispatch_info,
                                     pa::as_stream(stream)));
 }
 
@@ -386,8 +387,8 @@ pa_status pa_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t n
                     const int32_t* context_lens, int32_t num_seqs, const int32_t* cu_query_lens,
                     int32_t max_q_len, int32_t sliding_window, float scale, float k_scale,
                     float v_scale, const int32_t* work_info, const int32_t* reduce_info,
-                    const int32_t* num_work, int32_t capacity, int32_t tile_tokens, void* workspace,
-                    size_t workspace_bytes, void* out, pa_dtype out_dtype, void* stream) {
+                    const int32_t* num_work, const int32_t* dispatch_info, int32_t capacity, int32_t tile_tokens,
+                    void* workspace, size_t workspace_bytes, void* out, pa_dtype out_dtype, void* stream) {
     pa::DecodeArgs a;
     bool nothing = false;
     const pa_status st = prepare_decode(q, q_dtype, num_rows, num_q_heads, head_dim, k_cache, v_cache,
@@ -397,6 +398,8 @@ pa_status pa_decode(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t n
                                         reduce_info, num_work, capacity, tile_tokens, workspace,
                                         workspace_bytes, out, out_dtype, &a, &nothing);
     if (st != PA_OK) return st;
+    if (dispatch_info && !aligned(dispatch_info, 16)) return PA_INVALID_ARG;
+    a.dispatch_info = reinterpret_cast<const int4*>(dispatch_info);
     if (out) {
         // the merge's own checks too, so that a failure launches nothing
         pa::MergeArgs m;
@@ -479,7 +482,7 @@ pa_status pa_attention(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_
         if (!nothing && share_slots(d, head_dim, capacity, workspace, workspace_bytes))
             merge_pieces(m, head_dim, workspace);
         st = from_hip(pa::launch_plan(context_lens, cu_query_lens, num_seqs, cap, capacity, max_partitions,
-                                      tile_tokens, sliding_window, work_info, reduce_info, num_work, s));
+                                      tile_tokens, sliding_window, work_info, reduce_info, num_work, nullptr, s));
         if (st != PA_OK) return st;
     }
     if (!nothing) {
@@ -581,7 +584,7 @@ pa_status pa_prefill(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t 
                                             blk_ctx, blk_cu, blk_req, s));
     if (st != PA_OK) return st;
     st = from_hip(pa::launch_plan(blk_ctx, blk_cu, L.max_blocks, L.capacity, L.capacity, 256, 256, sliding_window,
-                                  work, reduce, num_work, s));
+                                  work, reduce, num_work, nullptr, s));
     if (st != PA_OK) return st;
 
     pa::DecodeArgs d = pa::DecodeArgs{};
@@ -716,7 +719,7 @@ pa_status pa_attention_mixed(const void* q, pa_dtype q_dtype, int32_t num_rows, 
         d.plan_num_work_out = num_work;
     } else {
         st = from_hip(pa::launch_plan(context_lens, cu_query_lens, num_decodes, cap, capacity, max_partitions,
-                                      tile_tokens, sliding_window, work_info, reduce_info, num_work, s));
+                                      tile_tokens, sliding_window, work_info, reduce_info, num_work, nullptr, s));
         if (st != PA_OK) return st;
     }
     if (fused) {

@@ -543,7 +543,9 @@ __global__ __launch_bounds__((64 * NWAVES), (Mfma<D, NCB, KV8, NWAVES>::WAVES)) 
         if (a.prefill) zero_prefill_tail_row<D>(a, (bid - work_groups) * C::NW + wave, lane);
         return;
     }
-    const int slot = bid / a.num_kv_heads;
+    // the workgroup's position among the plan's slots; its slot is the position itself, or with a
+    // dispatch order the slot that order puts there
+    int slot = bid / a.num_kv_heads;
     const int g = bid - slot * a.num_kv_heads;
 
     // ---- slot geometry.  Dependent loads are kept to three levels: the work entry; then the
@@ -579,11 +581,12 @@ __global__ __launch_bounds__((64 * NWAVES), (Mfma<D, NCB, KV8, NWAVES>::WAVES)) 
         } else if (a.pieces) {
             pieces_from_plan<C::NW>(a, slot, wk, nwk);
         } else {
-            wk = a.work_info[slot];
+            wk = a.dispatch_info ? a.dispatch_info[slot] : a.work_info[slot];
             nwk = *reinterpret_cast<const int2*>(a.num_work);
         }
         wk = make_int4(__builtin_amdgcn_readfirstlane(wk.x), __builtin_amdgcn_readfirstlane(wk.y),
                        __builtin_amdgcn_readfirstlane(wk.z), __builtin_amdgcn_readfirstlane(wk.w));
+        if (a.dispatch_info && !a.plan_inline && !a.pieces) slot = wk.w;   // word 3: the slot index
         nwk = make_int2(__builtin_amdgcn_readfirstlane(nwk.x), __builtin_amdgcn_readfirstlane(nwk.y));
         if (slot >= nwk.x) return;
         key_lo = static_cast<long long>(max(wk.y, 0)) * a.tile_tokens;

@@ -253,6 +253,8 @@ struct DecodeArgs {
     const int32_t* context_lens;
     const int32_t* cu;          // nullable
     const int4* work_info;
+    const int4* dispatch_info;  // nullable: workgroup position p runs dispatch_info[p] = (request,
+                                // tile_begin, tile_end, slot), the plan's slots in dispatch order
     const int32_t* num_work;
     float* ws_acc;
     float* ws_ml;
@@ -341,7 +343,10 @@ inline bool shares_slots(int one_slot_cap, int num_seqs, int head_dim, int capac
 
 hipError_t launch_plan(const int32_t* context_lens, const int32_t* cu, int num_seqs,
                        int cap_formula, int capacity, int max_partitions, int tile_tokens, int window,
-                       int32_t* work_info, int32_t* reduce_info, int32_t* num_work, hipStream_t stream);
+                       int32_t* work_info, int32_t* reduce_info, int32_t* num_work, int32_t* dispatch_info,
+                       hipStream_t stream);
+// Plans of at most this many slots get a balanced dispatch order; larger ones the identity.
+constexpr int kDispatchMaxSlots = 2048;
 hipError_t launch_prefill_blocks(const int32_t* context_lens, const int32_t* cu, int num_seqs, int block_tokens,
                                  int max_blocks, int32_t* blk_ctx, int32_t* blk_cu, int32_t* blk_req,
                                  hipStream_t stream);

@@ -11,6 +11,13 @@
 // of non-empty requests, the per-request counts, an exclusive scan into LDS, and then one thread per
 // slot fills work_info by binary-searching the scanned offsets.  Integer-only, 64-bit where
 // products can exceed 32 bits, so the result is bit-identical to any other exact evaluation.
+//
+// Optionally the same launch writes a dispatch order for the decode (this library's scheduling, not
+// part of the pages' plan): the slots ranked by tile count (largest first, ties by slot index, unused
+// slots last), rank r placed at position r when r < half = ceil(C / 2) and at position C + half - 1 - r
+// otherwise.  Positions p and p + half hold ranks p and C - 1 - p; with two workgroups per compute
+// unit (positions p and p + half share one when C x kv heads is twice the compute units) each unit
+// pairs a large slot with a small one, and the largest slots start in the first dispatch round.
 #include "pa_device.h"
 
 namespace pa {
@@ -23,8 +30,11 @@ constexpr int kPlanWaves = kPlanThreads / 64;
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ cu, int num_seqs,
     int cap_formula, int capacity, int max_partitions, int tile_tokens, int window,
-    int4* __restrict__ work_info, int2* __restrict__ reduce_info, int32_t* __restrict__ num_work) {
+    int4* __restrict__ work_info, int2* __restrict__ reduce_info, int32_t* __restrict__ num_work,
+    int4* __restrict__ dispatch_info) {
     __shared__ int32_t first[PA_MAX_SEQS + 1];
+    __shared__ int32_t s_tiles[kDispatchMaxSlots];
+    __shared__ int4 s_entry[kDispatchMaxSlots];
     __shared__ long long red_total[kPlanWaves];
     __shared__ int red_count[kPlanWaves];
     __shared__ int scan_carry[kPlanWaves];
@@ -91,8 +101,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
         reduce_info[b] = make_int2(first[b], first[b + 1] - first[b]);
 
     // --- one thread per slot ---
+    const bool ranked = dispatch_info && capacity <= kDispatchMaxSlots;
     int largest = 0;
     for (int s = tid; s < capacity; s += kPlanThreads) {
+        int4 e = make_int4(-1, 0, 0, 0);
+        int tiles = -1;                                   // unused slots rank after every used one
         if (s < used) {
             // last request whose first slot is <= s (it has at least one partition because s < used)
             int lo = 0, hi = num_seqs - 1;
@@ -106,10 +119,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
             const int parts = first[b + 1] - first[b];
             const PlanRange pr = range_of(b);
             const int2 r = plan_tile_range(j, pr.tiles, parts);
-            work_info[s] = make_int4(b, pr.t0 + r.x, pr.t0 + r.y, max(context_lens[b], 0));
-            largest = max(largest, r.y - r.x);
-        } else {
-            work_info[s] = make_int4(-1, 0, 0, 0);
+            e = make_int4(b, pr.t0 + r.x, pr.t0 + r.y, max(context_lens[b], 0));
+            tiles = r.y - r.x;
+            largest = max(largest, tiles);
+        }
+        work_info[s] = e;
+        if (ranked) {
+            s_tiles[s] = tiles;
+            s_entry[s] = e;
+        } else if (dispatch_info) {
+            dispatch_info[s] = make_int4(e.x, e.y, e.z, s);    // beyond the ranked size: identity order
         }
     }
     for (int o = 32; o >= 1; o >>= 1) largest = max(largest, __shfl_xor(largest, o, 64));
@@ -118,6 +137,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     if (tid == 0) {
         for (int w = 0; w < kPlanWaves; ++w) largest = max(largest, largest_of_wave[w]);
         *reinterpret_cast<int2*>(num_work) = make_int2(used, largest);
+    }
+    if (!ranked) return;
+    // rank of slot s: slots with more tiles, then slots with as many tiles and a lower index
+    const int half = (capacity + 1) / 2;
+    for (int s = tid; s < capacity; s += kPlanThreads) {
+        const int t = s_tiles[s];
+        int rank = 0;
+        for (int u = 0; u < capacity; ++u) {
+            const int tu = s_tiles[u];
+            rank += (tu > t) || (tu == t && u < s);
+        }
+        const int pos = rank < half ? rank : capacity + half - 1 - rank;
+        const int4 e = s_entry[s];
+        dispatch_info[pos] = make_int4(e.x, e.y, e.z, s);
     }
 }
 
@@ -184,11 +217,12 @@ hipError_t launch_prefill_blocks(const int32_t* context_lens, const int32_t* cu,
 
 hipError_t launch_plan(const int32_t* context_lens, const int32_t* cu, int num_seqs, int cap_formula,
                        int capacity, int max_partitions, int tile_tokens, int window,
-                       int32_t* work_info, int32_t* reduce_info, int32_t* num_work, hipStream_t stream) {
+                       int32_t* work_info, int32_t* reduce_info, int32_t* num_work, int32_t* dispatch_info,
+                       hipStream_t stream) {
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, context_lens, cu, num_seqs,
                        cap_formula, capacity, max_partitions, tile_tokens, window,
                        reinterpret_cast<int4*>(work_info), reinterpret_cast<int2*>(reduce_info),
-                       num_work);
+                       num_work, reinterpret_cast<int4*>(dispatch_info));
     return hipGetLastError();
 }
 

@@ -31,10 +31,13 @@ class DecodeStep:
         p = self.plan_cfg
         self.num_seqs = num_seqs
         self.num_kv_heads = num_kv_heads
+        self.use_dispatch = True          # decode() follows the plan's dispatch order
         self.max_q_len = max_q_len
         self.capacity = B.pa_plan_capacity(num_seqs, num_kv_heads, p.cu_count, p.budget_mult,
                                            p.max_partitions)
         self.work_info = torch.empty((self.capacity, 4), dtype=torch.int32, device=self.device)
+        # the decode's dispatch order, written by the plan beside it
+        self.dispatch_info = torch.empty((self.capacity, 4), dtype=torch.int32, device=self.device)
         self.reduce_info = torch.empty((num_seqs, 2), dtype=torch.int32, device=self.device)
         self.num_work = torch.empty((2,), dtype=torch.int32, device=self.device)
         nbytes = B.pa_workspace_bytes(self.capacity, max_q_len, num_q_heads, head_dim)
@@ -59,7 +62,8 @@ class DecodeStep:
         B.pa_plan(context_lens, self.num_kv_heads, cu_count=p.cu_count, budget_mult=p.budget_mult,
                   max_partitions=p.max_partitions, tile_tokens=p.tile_tokens, capacity=self.capacity,
                   work_info=self.work_info, reduce_info=self.reduce_info, num_work=self.num_work,
-                  cu_query_lens=cu_query_lens, sliding_window=sliding_window, stream=stream)
+                  cu_query_lens=cu_query_lens, sliding_window=sliding_window, dispatch_info=self.dispatch_info,
+                  stream=stream)
 
     def decode(self, q, k_cache, v_cache, kv_dtype, block_tables, context_lens, *, scale,
                cu_query_lens=None, k_scale=1.0, v_scale=1.0, merge: bool = False,
@@ -71,7 +75,8 @@ class DecodeStep:
                     max_q_len=self.max_q_len, k_scale=k_scale, v_scale=v_scale,
                     tile_tokens=self.plan_cfg.tile_tokens,
                     reduce_info=self.reduce_info if merge else None,
-                    out=self.out if merge else None, sliding_window=sliding_window, stream=stream)
+                    out=self.out if merge else None, sliding_window=sliding_window,
+                    dispatch_info=self.dispatch_info if self.use_dispatch else None, stream=stream)
 
     def attention(self, q, k_cache, v_cache, kv_dtype, block_tables, context_lens, *, scale,
                   cu_query_lens=None, k_scale=1.0, v_scale=1.0, sliding_window: int = 0,

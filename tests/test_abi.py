@@ -110,14 +110,15 @@ def test_workspace_bytes():
 
 def _plan_status(**kw):
     a = dict(ctx=ctypes.c_void_p(16), cuq=None, B=4, hkv=1, cu=256, mult=2, P=256, T=256, win=0, cap=512,
-             work=ctypes.c_void_p(256), red=ctypes.c_void_p(256), nw=ctypes.c_void_p(256))
+             work=ctypes.c_void_p(256), red=ctypes.c_void_p(256), nw=ctypes.c_void_p(256), disp=None)
     a.update(kw)
     return B.load().pa_plan(a["ctx"], a["cuq"], a["B"], a["hkv"], a["cu"], a["mult"], a["P"], a["T"],
-                            a["win"], a["cap"], a["work"], a["red"], a["nw"], None)
+                            a["win"], a["cap"], a["work"], a["red"], a["nw"], a["disp"], None)
 
 
 def test_plan_argument_checks():
     # (no valid call is made: every case below must be refused before a launch)
+    assert _plan_status(disp=ctypes.c_void_p(264)) == B.PA_INVALID_ARG   # dispatch order 16-byte aligned
     assert _plan_status(cap=511) == B.PA_CAPACITY
     assert _plan_status(B=-1) == B.PA_INVALID_ARG
     assert _plan_status(hkv=0) == B.PA_INVALID_ARG
@@ -146,11 +147,12 @@ def _decode_status(**kw):
     return B.load().pa_decode(vp(a["q"]), a["qd"], a["R"], a["Hq"], a["D"], vp(a["k"]), vp(a["v"]),
                               a["kvd"], a["nb"], a["Hkv"], a["bs"], vp(a["bt"]), a["mb"], vp(a["ctx"]),
                               a["Bn"], vp(a["cu"]), a["ql"], a["win"], a["scale"], a["ks"], a["vs"], vp(a["work"]),
-                              vp(a["red"]), vp(a["nw"]), a["cap"], a["T"], vp(a["ws"]), a["wsb"],
+                              vp(a["red"]), vp(a["nw"]), vp(a.get("disp")), a["cap"], a["T"], vp(a["ws"]), a["wsb"],
                               vp(a["out"]), a["od"], None)
 
 
 def test_decode_argument_checks():
+    assert _decode_status(disp=264) == B.PA_INVALID_ARG                 # dispatch order 16-byte aligned
     assert _decode_status(qd=B.PA_FP8_E4M3) == B.PA_INVALID_ARG        # q must be f32 or bf16
     assert _decode_status(kvd=7) == B.PA_INVALID_ARG
     assert _decode_status(Hq=15) == B.PA_INVALID_ARG                   # Hq % Hkv != 0

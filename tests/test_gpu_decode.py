@@ -202,6 +202,37 @@ def test_merge_launch_shapes(spec, fused):
     assert z[3] and (got[z] == 0.0).all()
 
 
+@pytest.mark.parametrize("name", ["skewed_p90", "verify_bf16", "long_bf16", "small_mixed_lengths"])
+def test_dispatch_order_changes_nothing(name):
+    """pa_decode following the plan's dispatch order writes every slot's state where slot order
+    writes it, bit for bit, and the merged rows are bitwise equal."""
+    if name == "skewed_p90":
+        steps = W.skewed_step_set()
+        case = W.make_config("skewed_bf16", device=DEV, step=W.skewed_named_steps(steps)["p90"])
+    elif name == "small_mixed_lengths":
+        case = W.build_case(name, [9000, 33, 700, 0, 4096, 1], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                            block_size=16, kv_dtype="bf16", q_dtype="bf16", seed=45, q_lens=[2, 1, 3, 1, 1, 1],
+                            pad_rows=1, device=DEV)
+    else:
+        case = W.make_config(name, device=DEV)
+    announce(f"dispatch order {name}")
+    outs, states = [], []
+    for use in (True, False):
+        step = DecodeStep.for_case(case, PlanConfig(cu_count=256))
+        step.use_dispatch = use
+        step.workspace.fill_(0xFF)
+        step.out.fill_(float("nan"))
+        step.run_case(case, fused=False)
+        torch.cuda.synchronize()
+        outs.append(step.out.clone())
+        states.append(step.workspace[:_partial_bytes(step)].clone())
+        disp = step.dispatch_info.cpu().numpy()
+    assert sorted(disp[:, 3].tolist()) == list(range(disp.shape[0]))       # a permutation of the slots
+    assert torch.equal(states[0], states[1]), f"{name}: slot states differ with the dispatch order"
+    assert torch.equal(outs[0], outs[1])
+    assert_close(to_f64(outs[0]), oracle_direct(case), tolerance_kind(case), name)
+
+
 def test_full_size_separate_merge_fp8():
     announce("full fp8_kv, separate merge")
     case = W.make_config("fp8_kv", device=DEV)
@@ -314,6 +345,7 @@ def test_slot_order_does_not_change_the_output():
     assert pos == nw
     step.work_info.copy_(torch.from_numpy(new_work))
     step.reduce_info.copy_(torch.from_numpy(new_red))
+    step.use_dispatch = False         # the dispatch order belongs to the plan pa_plan wrote, not this one
     step.out.fill_(float("nan"))
     out = step.run_case(case, replan=False)
     torch.cuda.synchronize()

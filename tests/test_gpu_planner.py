@@ -19,14 +19,38 @@ def _gpu_plan(ctx, hkv, cu, mult=2, P=256, T=256, capacity=None, poison=True):
     work = torch.empty((cap, 4), dtype=torch.int32, device=DEV)
     red = torch.empty((len(ctx), 2), dtype=torch.int32, device=DEV)
     nw = torch.empty((2,), dtype=torch.int32, device=DEV)
+    disp = torch.empty((cap, 4), dtype=torch.int32, device=DEV)
     if poison:
         work.fill_(0x5A5A5A5A)
         red.fill_(-7)
         nw.fill_(-9)
+        disp.fill_(0x3C3C3C3C)
     B.pa_plan(c, hkv, cu_count=cu, budget_mult=mult, max_partitions=P, tile_tokens=T, capacity=cap,
-              work_info=work, reduce_info=red, num_work=nw)
+              work_info=work, reduce_info=red, num_work=nw, dispatch_info=disp)
     torch.cuda.synchronize()
+    _gpu_plan.dispatch = disp.cpu().numpy()
     return work.cpu().numpy(), red.cpu().numpy(), nw.cpu().numpy().tolist()
+
+
+def expected_dispatch(work, used):
+    """The dispatch order from its definition: slots ranked by tile count, largest first, ties by
+    slot index, unused slots last; rank r at position r below half = ceil(C / 2), else at
+    C + half - 1 - r; entries (request, tile_begin, tile_end, slot).  Identity above 2048 slots."""
+    C = work.shape[0]
+    out = np.empty((C, 4), dtype=np.int32)
+    slots = np.arange(C)
+    if C > 2048:
+        out[:, :3] = work[:, :3]
+        out[:, 3] = slots
+        return out
+    tiles = np.where(slots < used, work[:, 2] - work[:, 1], -1)
+    order = sorted(range(C), key=lambda s: (-int(tiles[s]), s))
+    half = (C + 1) // 2
+    for r, s in enumerate(order):
+        p = r if r < half else C + half - 1 - r
+        out[p, :3] = work[s, :3]
+        out[p, 3] = s
+    return out
 
 
 def _compare(ctx, hkv, cu, mult=2, P=256, T=256, capacity=None):
@@ -35,6 +59,7 @@ def _compare(ctx, hkv, cu, mult=2, P=256, T=256, capacity=None):
     assert gn == [on, olarge]
     assert np.array_equal(gr, orr)
     assert np.array_equal(gw, ow)
+    assert np.array_equal(_gpu_plan.dispatch, expected_dispatch(np.asarray(ow).reshape(-1, 4), on))
 
 
 @pytest.mark.parametrize("name", W.CONFIG_NAMES)
