@@ -131,7 +131,7 @@ size_t pa_workspace_bytes(int32_t capacity, int32_t max_q_len, int32_t num_q_hea
  * capacity + half - 1 - r otherwise, each entry (request, tile_begin, tile_end, slot).  Positions p
  * and p + half hold ranks p and capacity - 1 - p, so where two workgroups share a compute unit a large
  * slot pairs with a small one.  This is this library's scheduling, not part of the plan; plans of
- * more than 2048 slots get the identity order.
+ * more than 1024 slots get the identity order.
  * Negative S_b (a precondition violation) are planned as 0.
  * Errors: PA_INVALID_ARG (null pointers, num_seqs < 0, arguments < 1), PA_UNSUPPORTED
  * (num_seqs > PA_MAX_SEQS), PA_CAPACITY (capacity too small), PA_HIP_ERROR (launch failure).

@@ -346,7 +346,7 @@ hipError_t launch_plan(const int32_t* context_lens, const int32_t* cu, int num_s
                        int32_t* work_info, int32_t* reduce_info, int32_t* num_work, int32_t* dispatch_info,
                        hipStream_t stream);
 // Plans of at most this many slots get a balanced dispatch order; larger ones the identity.
-constexpr int kDispatchMaxSlots = 2048;
+constexpr int kDispatchMaxSlots = 1024;
 hipError_t launch_prefill_blocks(const int32_t* context_lens, const int32_t* cu, int num_seqs, int block_tokens,
                                  int max_blocks, int32_t* blk_ctx, int32_t* blk_cu, int32_t* blk_req,
                                  hipStream_t stream);

@@ -15,7 +15,7 @@
 // Optionally the same launch writes a dispatch order for the decode (this library's scheduling, not
 // part of the pages' plan): the slots ranked by tile count (largest first, ties by slot index, unused
 // slots last), rank r placed at position r when r < half = ceil(C / 2) and at position C + half - 1 - r
-// otherwise.  Positions p and p + half hold ranks p and C - 1 - p; with two workgroups per compute
+// otherwise; plans of more than kDispatchMaxSlots slots keep the slot order.  Positions p and p + half hold ranks p and C - 1 - p; with two workgroups per compute
 // unit (positions p and p + half share one when C x kv heads is twice the compute units) each unit
 // pairs a large slot with a small one, and the largest slots start in the first dispatch round.
 #include "pa_device.h"
@@ -27,6 +27,16 @@ namespace {
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / 64;
 
+// A slot's dispatch key: larger for more tiles, then for a lower slot index (slots < 2048), distinct
+// for distinct slots.  Unused slots (tiles -1) key below every used one and padding (-2) below those.
+// Exact while tiles < kRankKeyTiles; the clamp keeps every key inside 31 bits.
+constexpr int kRankKeyTiles = (1 << 20) - 2;
+constexpr int kClosedMaxSeqs = kDispatchMaxSlots / 4;
+static_assert(kDispatchMaxSlots <= 2048, "slot indices take the key's low 11 bits");
+__device__ __forceinline__ int rank_key(int tiles, int slot) {
+    return ((min(tiles, kRankKeyTiles - 1) + 2) << 11) | (2047 - slot);
+}
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ cu, int num_seqs,
     int cap_formula, int capacity, int max_partitions, int tile_tokens, int window,
@@ -34,7 +44,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     int4* __restrict__ dispatch_info) {
     __shared__ int32_t first[PA_MAX_SEQS + 1];
     __shared__ int32_t s_tiles[kDispatchMaxSlots];
+    __shared__ __align__(16) int32_t s_aux[kDispatchMaxSlots];   // a slot's key, or its rank within its request
+    __shared__ int32_t s_rank[kDispatchMaxSlots];
     __shared__ int4 s_entry[kDispatchMaxSlots];
+    __shared__ int4 s_qrp[kClosedMaxSeqs];
     __shared__ long long red_total[kPlanWaves];
     __shared__ int red_count[kPlanWaves];
     __shared__ int scan_carry[kPlanWaves];
@@ -43,6 +56,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const bool ranked = dispatch_info && capacity > 0 && capacity <= kDispatchMaxSlots;
+    // ranks from the closed form (O(requests) per slot) when the batch is small against the slots
+    const bool closed = ranked && num_seqs <= kClosedMaxSeqs && 4 * num_seqs <= capacity;
 
     // the key range request b reads: all of [0, S_b), or its window's union
     auto range_of = [&](int b) -> PlanRange {
@@ -82,6 +98,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
         const int parts = plan_parts(r.len, r.tiles, extra, total, max_partitions);
         first[b] = parts;
         local += parts;
+        if (closed)     // (q, rem, parts): rem slots of q + 1 tiles, the others of q
+            s_qrp[b] = parts > 0 ? make_int4(r.tiles / parts, r.tiles % parts, parts, 0) : make_int4(0, 0, 0, 0);
     }
     const int incl = wave_incl_scan(local, lane);
     if (lane == 63) scan_carry[wave] = incl;
@@ -101,11 +119,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
         reduce_info[b] = make_int2(first[b], first[b + 1] - first[b]);
 
     // --- one thread per slot ---
-    const bool ranked = dispatch_info && capacity <= kDispatchMaxSlots;
+    const int cap4 = (capacity + 3) & ~3;                 // the keys are read four at a time
+    if (ranked)
+        for (int s = tid; s < cap4; s += kPlanThreads) {
+            s_rank[s] = 0;
+            if (s >= capacity) {                          // padding: below every slot, counts for none
+                s_tiles[s] = -2;
+                s_aux[s] = rank_key(-2, s);
+            }
+        }
     int largest = 0;
     for (int s = tid; s < capacity; s += kPlanThreads) {
         int4 e = make_int4(-1, 0, 0, 0);
         int tiles = -1;                                   // unused slots rank after every used one
+        int owner = num_seqs, within = s - used;          // (closed form) an unused slot's terms
         if (s < used) {
             // last request whose first slot is <= s (it has at least one partition because s < used)
             int lo = 0, hi = num_seqs - 1;
@@ -122,11 +149,19 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
             e = make_int4(b, pr.t0 + r.x, pr.t0 + r.y, max(context_lens[b], 0));
             tiles = r.y - r.x;
             largest = max(largest, tiles);
+            if (closed) {
+                // the request's slots before this one of the same size: r.x - j q of them hold q + 1
+                const int q = s_qrp[b].x;
+                const int big_before = r.x - j * q;
+                owner = b;
+                within = tiles == q + 1 ? big_before : j - big_before;
+            }
         }
         work_info[s] = e;
         if (ranked) {
             s_tiles[s] = tiles;
-            s_entry[s] = e;
+            s_aux[s] = closed ? within : rank_key(tiles, s);
+            s_entry[s] = make_int4(e.x, e.y, e.z, owner);
         } else if (dispatch_info) {
             dispatch_info[s] = make_int4(e.x, e.y, e.z, s);    // beyond the ranked size: identity order
         }
@@ -139,18 +174,74 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
         *reinterpret_cast<int2*>(num_work) = make_int2(used, largest);
     }
     if (!ranked) return;
-    // rank of slot s: slots with more tiles, then slots with as many tiles and a lower index
+    // rank of slot s: slots with more tiles, then slots with as many tiles and a lower index.  Each
+    // slot's terms are split over `split` threads; the parts meet in s_rank through integer adds, whose
+    // sum does not depend on their order.
+    const int split = max(1, min(kPlanThreads / capacity, 16));
+    if (closed) {
+        // Closed form.  Request b' holds rem' slots of q' + 1 tiles and parts' - rem' of q', so for a
+        // slot of t tiles owned by request b it contributes parts' slots with more tiles when q' > t,
+        // rem' when q' = t; and, when b' < b, parts' - rem' slots with as many tiles when q' = t,
+        // rem' when q' + 1 = t.  Add the owner's own earlier slots of t tiles.  An unused slot (t = -1,
+        // owner past the last request) gets every used slot plus the unused ones before it.
+        const int per_part = (num_seqs + split - 1) / split;
+        for (int w = tid; w < capacity * split; w += kPlanThreads) {
+            const int s = w / split;
+            const int part = w - s * split;
+            const int t = s_tiles[s];
+            const int owner = s_entry[s].w;
+            const int r0 = part * per_part;
+            const int r1 = min(r0 + per_part, num_seqs);
+            int count = part == 0 ? s_aux[s] : 0;
+            for (int b = r0; b < r1; ++b) {
+                const int4 v = s_qrp[b];
+                const int more = v.x > t ? v.z : (v.x == t ? v.y : 0);
+                const int same = v.x == t ? v.z - v.y : (v.x + 1 == t ? v.y : 0);
+                count += more + (b < owner ? same : 0);
+            }
+            if (count) atomicAdd(&s_rank[s], count);
+        }
+    } else {
+        // Pairwise: while every slot holds fewer than kRankKeyTiles tiles the order is that of the
+        // distinct keys rank_key(tiles, slot), one difference per pair (read four keys at a time from
+        // the padded array); otherwise the pairs are compared field by field.
+        int top = 0;
+        for (int w = 0; w < kPlanWaves; ++w) top = max(top, largest_of_wave[w]);
+        const bool keyed = top < kRankKeyTiles;
+        const int quads = cap4 / 4;
+        const int per_part = (quads + split - 1) / split;
+        for (int w = tid; w < capacity * split; w += kPlanThreads) {
+            const int s = w / split;
+            const int part = w - s * split;
+            const int q0 = part * per_part;
+            const int q1 = min(q0 + per_part, quads);
+            int count = 0;
+            if (keyed) {
+                const int k = s_aux[s];
+#pragma unroll 8
+                for (int q = q0; q < q1; ++q) {
+                    // keys lie in [0, 2^31): the differences cannot overflow; 1 exactly when key u > k
+                    const int4 ku = reinterpret_cast<const int4*>(s_aux)[q];
+                    count += min(max(ku.x - k, 0), 1) + min(max(ku.y - k, 0), 1) +
+                             min(max(ku.z - k, 0), 1) + min(max(ku.w - k, 0), 1);
+                }
+            } else {
+                const int t = s_tiles[s];
+                for (int u = 4 * q0; u < 4 * q1; ++u) {
+                    const int tu = s_tiles[u];
+                    count += (tu > t) || (tu == t && u < s);
+                }
+            }
+            if (count) atomicAdd(&s_rank[s], count);
+        }
+    }
+    __syncthreads();
     const int half = (capacity + 1) / 2;
     for (int s = tid; s < capacity; s += kPlanThreads) {
-        const int t = s_tiles[s];
-        int rank = 0;
-        for (int u = 0; u < capacity; ++u) {
-            const int tu = s_tiles[u];
-            rank += (tu > t) || (tu == t && u < s);
-        }
+        const int rank = s_rank[s];
         const int pos = rank < half ? rank : capacity + half - 1 - rank;
         const int4 e = s_entry[s];
-        dispatch_info[pos] = make_int4(e.x, e.y, e.z, s);
+        dispatch_info[pos] = make_int4(e.x, e.y, e.z, s);    // (request, tile_begin, tile_end, slot)
     }
 }
 

@@ -35,11 +35,11 @@ def _gpu_plan(ctx, hkv, cu, mult=2, P=256, T=256, capacity=None, poison=True):
 def expected_dispatch(work, used):
     """The dispatch order from its definition: slots ranked by tile count, largest first, ties by
     slot index, unused slots last; rank r at position r below half = ceil(C / 2), else at
-    C + half - 1 - r; entries (request, tile_begin, tile_end, slot).  Identity above 2048 slots."""
+    C + half - 1 - r; entries (request, tile_begin, tile_end, slot).  Identity above 1024 slots."""
     C = work.shape[0]
     out = np.empty((C, 4), dtype=np.int32)
     slots = np.arange(C)
-    if C > 2048:
+    if C > 1024:
         out[:, :3] = work[:, :3]
         out[:, 3] = slots
         return out
@@ -124,3 +124,22 @@ def test_replan_in_place_leaves_nothing_stale():
 def test_empty_and_all_zero_batches():
     _compare([0, 0, 0], 2, 256)
     _compare([0], 1, 256, capacity=600)
+
+
+@pytest.mark.parametrize("cap", [1, 3, 6, 65, 511, 513, 1023, 1024, 1025, 2048])
+def test_dispatch_order_at_capacity_edges(cap):
+    """Capacities around the four-slot reads and the thread splits of the ranking, with tied slot
+    sizes and unused slots; above 1024 slots the order is the identity."""
+    announce(f"dispatch order capacity {cap}")
+    rng = np.random.default_rng(cap)
+    if cap < 64:
+        ctx, P = [int(rng.integers(1, 5000))], 1
+    else:
+        ctx, P = rng.choice([768, 1280, 1000, 70000, 0, 256], size=40).tolist(), 256
+    _compare(ctx, 8, 256, 2, P, 256, cap)
+
+
+def test_dispatch_order_with_slots_beyond_the_packed_keys():
+    """Slots of a million tiles and more are ranked by comparing their fields, not by packed keys."""
+    announce("dispatch order, huge slots")
+    _compare([20_000_000, 17_000_000, 5, 20_000_000, 0, 16_777_216], 8, 256, 2, 1, 16)
