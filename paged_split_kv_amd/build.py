@@ -21,7 +21,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpa.so")
-SOURCES = ["pa_api.hip", "pa_plan.hip", "pa_decode.hip", "pa_merge.hip"]
+SOURCES = ["pa_api.hip", "pa_plan.hip", "pa_decode.hip", "pa_prefill.hip", "pa_merge.hip"]
 PROBE_LIB = os.path.join(PKG, "libpa_probe.so")
 PROBE_SOURCES = ["pa_probe.hip"]
 ARCH = "gfx950"

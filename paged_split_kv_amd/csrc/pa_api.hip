@@ -302,6 +302,10 @@ namespace {
 // Workspace regions, each 256-byte aligned: per-block lengths, first rows (max_blocks + 1) and
 // request indices; the plan over the blocks (work_info [capacity], reduce_info [max_blocks],
 // num_work [2]); the slot states of that plan.
+// Workgroup budget of the split prefill's plan over query blocks, in workgroups per compute unit: the
+// block kernel holds one workgroup per compute unit, so its slots run in one round.
+constexpr int kPrefillBudget = 1;
+
 struct PrefillLayout {
     int block_tokens, max_blocks, capacity;
     size_t blk_ctx, blk_cu, blk_req, work, reduce, num_work, states, end;
@@ -314,14 +318,14 @@ bool prefill_layout(int32_t num_rows, int32_t num_seqs, int32_t num_q_heads, int
         return false;
     const int group = num_q_heads / num_kv_heads;
     if (group > PA_MAX_GROUP_ROWS) return false;
-    L->block_tokens = (head_dim == 256 ? PA_MAX_GROUP_ROWS / 2 : PA_MAX_GROUP_ROWS) / group;
+    L->block_tokens = pa::prefill_tile_rows(head_dim) / group;
     if (L->block_tokens < 1) L->block_tokens = 1;
     // blocks: sum over requests of ceil(L_b / T) <= num_rows / T + num_seqs
     const long long nb = ((long long)num_rows + L->block_tokens - 1) / L->block_tokens + num_seqs;
     if (nb > PA_MAX_SEQS) return false;
     L->max_blocks = (int)nb;
     int32_t cap = 0;
-    if (capacity_formula(L->max_blocks, num_kv_heads, cu_count, 2, 256, &cap) != PA_OK) return false;
+    if (capacity_formula(L->max_blocks, num_kv_heads, cu_count, kPrefillBudget, 256, &cap) != PA_OK) return false;
     L->capacity = cap;
     size_t at = 0;
     auto region = [&](size_t bytes) {
@@ -615,7 +619,7 @@ pa_status pa_prefill(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t 
     d.score_scale_log2 = scale * k_scale * pa::kLog2e;
     d.v_scale = v_scale;
     d.window = sliding_window;
-    st = from_hip(pa::launch_decode(d, head_dim, kv_dtype, q_dtype == PA_F32, s));
+    st = from_hip(pa::launch_prefill_tiles(d, head_dim, kv_dtype, q_dtype == PA_F32, s));
     if (st != PA_OK) return st;
 
     pa::MergeArgs m = pa::MergeArgs{};

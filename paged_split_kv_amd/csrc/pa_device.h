@@ -365,5 +365,12 @@ hipError_t launch_mixed(const DecodeArgs& dec, const DecodeArgs& pre, int head_d
                         bool q_f32, int ncb, hipStream_t stream);
 hipError_t launch_prefill(const DecodeArgs& a, int head_dim, pa_dtype kv_dtype, bool q_f32,
                           hipStream_t stream);
+// Query rows (G heads x tokens) of one query block of the split prefill, per head_dim.
+int prefill_tile_rows(int head_dim);
+// The split prefill's query blocks: one workgroup per (plan slot, kv head) of a plan over the blocks
+// (a as for launch_decode with context_lens, cu and bt_index describing the blocks; max_q_len the
+// block's token bound), writing slot states like the decode.  bf16 or fp8 caches.
+hipError_t launch_prefill_tiles(const DecodeArgs& a, int head_dim, pa_dtype kv_dtype, bool q_f32,
+                                hipStream_t stream);
 
 }  // namespace pa

@@ -260,20 +260,20 @@ def _prefill_status(**kw):
 
 
 def test_prefill_workspace_bytes():
-    # blocks of T = 64 / G tokens (32 / G at head_dim 256), at most ceil(R / T) + B of them; capacity
-    # formula over the blocks
-    # (budget 2 x CU, ceiling 256); regions: lengths, first rows (+1), request indices, work_info,
-    # reduce_info, num_work, then the partial states [C, T, Hq, D] fp32 and (m, l) pairs, each 256-aligned
+    # blocks of T = 256 / G tokens (128 / G at head_dim 256), at most ceil(R / T) + B of them; capacity
+    # formula over the blocks (budget 1 x CU, ceiling 256); regions: lengths, first rows (+1), request
+    # indices, work_info, reduce_info, num_work, then the partial states [C, T, Hq, D] fp32 and (m, l)
+    # pairs, each 256-aligned
     up = lambda x: (x + 255) // 256 * 256
     for R, Bn, hq, hkv, d, cu in [(512, 1, 12, 2, 256, 256), (33, 4, 16, 2, 128, 256), (1000, 7, 8, 8, 64, 80),
                                   (0, 0, 4, 1, 128, 256)]:
-        T = max(1, (32 if d == 256 else 64) // (hq // hkv))
+        T = max(1, (128 if d == 256 else 256) // (hq // hkv))
         nb = (R + T - 1) // T + Bn
-        cap = min(nb * 256, max(nb, -(-2 * cu // hkv)))
+        cap = min(nb * 256, max(nb, -(-cu // hkv)))
         want = (up(4 * nb) + up(4 * (nb + 1)) + up(4 * nb) + up(16 * cap) + up(8 * nb) + up(8)
                 + up(cap * T * hq * d * 4) + up(cap * T * hq * 2 * 4))
         assert B.pa_prefill_workspace_bytes(R, Bn, hq, hkv, d, cu) == want, (R, Bn, hq, hkv, d, cu)
-    assert B.pa_prefill_workspace_bytes(8192 * 64, 1, 64, 1, 128, 256) == 0          # more than 8192 blocks
+    assert B.pa_prefill_workspace_bytes(8192 * 256, 1, 64, 1, 128, 256) == 0         # more than 8192 blocks
     assert B.pa_prefill_workspace_bytes(10, 1, 12, 5, 128, 256) == 0                  # heads not a multiple
     assert B.pa_prefill_workspace_bytes(10, 1, 4, 1, 128, 0) == 0
 

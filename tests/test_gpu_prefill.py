@@ -122,8 +122,8 @@ def test_prefill_chunk_of_the_bench_at_full_size():
     out = torch.full_like(case.q, float("nan"))
     _prefill(case, out, cu_count=B.pa_device_cu_count(0))
     torch.cuda.synchronize()
-    # block edges (5 tokens per block at G = 6, head_dim 256) and the chunk's ends, every head of each row
-    rows = np.repeat(np.array([0, 1, 4, 5, 6, 255, 256, 400, 509, 510, 511]), case.num_q_heads)
+    # block edges (21 tokens per block at G = 6, head_dim 256) and the chunk's ends, every head of each row
+    rows = np.repeat(np.array([0, 1, 20, 21, 22, 41, 42, 251, 252, 400, 503, 504, 510, 511]), case.num_q_heads)
     heads = np.tile(np.arange(case.num_q_heads), rows.shape[0] // case.num_q_heads)
     h = case.host()
     ref = oracle.attention_rows(h["q"], case.q_dtype, h["k_cache"], h["v_cache"], case.kv_dtype, h["block_tables"],
