@@ -263,7 +263,18 @@ __global__ __launch_bounds__(512, 2) void prefill_tile_kernel(const DecodeArgs a
         const uint8_t* const vt = kt + C::TILE;
         if (live_rb == 0) return;
         // S^T for the two 16-key halves: lane holds keys 16 kb + 4 grp + j of row block rb's row col
-        // (2 RB independent accumulation chains; blocks past the rows compute on zero queries)
+        // (2 RB independent accumulation chains; blocks past the rows compute on zero queries).  The K
+        // operands are read KP steps ahead of their products, so LDS latency overlaps the matrix cores.
+        constexpr int KP = C::KS < 4 ? C::KS : 4;
+        bf16x8_t kop[C::KS][2];
+        auto kread = [&](int s) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                kop[s][kb] = __builtin_bit_cast(
+                    bf16x8_t, *reinterpret_cast<const u32x4_t*>(kt + tile_col<C::LRB, C::SWM>(16 * kb + col, 4 * s + grp)));
+        };
+#pragma unroll
+        for (int s = 0; s < KP; ++s) kread(s);
         float4_t sc[2][C::RB];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -271,32 +282,50 @@ __global__ __launch_bounds__(512, 2) void prefill_tile_kernel(const DecodeArgs a
             for (int rb = 0; rb < C::RB; ++rb) sc[kb][rb] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < C::KS; ++s) {
-            bf16x8_t kop[2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                kop[kb] = __builtin_bit_cast(
-                    bf16x8_t, *reinterpret_cast<const u32x4_t*>(kt + tile_col<C::LRB, C::SWM>(16 * kb + col, 4 * s + grp)));
 #pragma unroll
             for (int rb = 0; rb < C::RB; ++rb)
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
-                    sc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kb], qop[rb][s], sc[kb][rb], 0, 0, 0);
+                    sc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[s][kb], qop[rb][s], sc[kb][rb], 0, 0, 0);
+            if (s + KP < C::KS) kread(s + KP);
         }
-        const int full = nv == C::KC && key0 + C::KC <= nvis_min && key0 >= nlo_max;
+        // V^T operands (A of O^T += V^T . P^T over the 32 keys): contraction index 8 grp + j is key
+        // 4 grp + j of the first half for j < 4 and key 16 + 4 grp + j - 4 of the second for j >= 4, as
+        // P's registers lie.  The first VP tiles are read before the softmax, which then hides them.
+        constexpr int VP = C::DT < 4 ? C::DT : 4;
+        bf16x8_t vop[C::DT];
+        auto vread = [&](int t) {
+            const int d0 = 16 * t + tr_d0;
+            const int o0 = tile_col<C::LRB, C::SWM>(tr_row, d0 >> 3) + ((d0 & 7) << 1);
+            const int o1 = tile_col<C::LRB, C::SWM>(16 + tr_row, d0 >> 3) + ((d0 & 7) << 1);
+            const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(vt + o0));
+            const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(vt + o1));
+            const u32x2_t a0 = __builtin_bit_cast(u32x2_t, v0);
+            const u32x2_t a1 = __builtin_bit_cast(u32x2_t, v1);
+            const u32x4_t vc = {a0[0], a0[1], a1[0], a1[1]};
+            vop[t] = __builtin_bit_cast(bf16x8_t, vc);
+        };
+#pragma unroll
+        for (int t = 0; t < VP; ++t) vread(t);
+        // the chunk lies inside every row's visible range: no mask (uniform)
+        const bool full = nv == C::KC && key0 + C::KC <= nvis_min && key0 >= nlo_max;
         bf16x8_t pop[C::RB];
 #pragma unroll
         for (int rb = 0; rb < C::RB; ++rb) {
             float x[8];
-            float mt = -INFINITY;
-            const int lim = min(nv, nvis[rb] - key0);
-            const int low = nlo[rb] - key0;
+            if (full) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int q = 16 * (j >> 2) + 4 * grp + (j & 3);
-                const int keep = full | ((q < lim) & (q >= low));
-                x[j] = keep ? sc[j >> 2][rb][j & 3] * a.score_scale_log2 : -INFINITY;
-                mt = fmaxf(mt, x[j]);
+                for (int j = 0; j < 8; ++j) x[j] = sc[j >> 2][rb][j & 3] * a.score_scale_log2;
+            } else {
+                const int lim = min(nv, nvis[rb] - key0);
+                const int low = nlo[rb] - key0;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int q = 16 * (j >> 2) + 4 * grp + (j & 3);
+                    x[j] = (q < lim && q >= low) ? sc[j >> 2][rb][j & 3] * a.score_scale_log2 : -INFINITY;
+                }
             }
+            float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
             mt = row_max4(mt);
             const bool grow = mt > m_run[rb] + kSlack;
             if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -318,22 +347,12 @@ __global__ __launch_bounds__(512, 2) void prefill_tile_kernel(const DecodeArgs a
                                 pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
             pop[rb] = __builtin_bit_cast(bf16x8_t, pc);
         }
-        // O^T += V^T . P^T over the 32 keys: contraction index 8 grp + j is key 4 grp + j of the first
-        // half for j < 4 and key 16 + 4 grp + j - 4 of the second for j >= 4, as P's registers lie
 #pragma unroll
         for (int t = 0; t < C::DT; ++t) {
-            const int d0 = 16 * t + tr_d0;
-            const int o0 = tile_col<C::LRB, C::SWM>(tr_row, d0 >> 3) + ((d0 & 7) << 1);
-            const int o1 = tile_col<C::LRB, C::SWM>(16 + tr_row, d0 >> 3) + ((d0 & 7) << 1);
-            const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(vt + o0));
-            const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(vt + o1));
-            const u32x2_t a0 = __builtin_bit_cast(u32x2_t, v0);
-            const u32x2_t a1 = __builtin_bit_cast(u32x2_t, v1);
-            const u32x4_t vc = {a0[0], a0[1], a1[0], a1[1]};
-            const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, vc);
 #pragma unroll
             for (int rb = 0; rb < C::RB; ++rb)
-                acc[rb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[rb], acc[rb][t], 0, 0, 0);
+                acc[rb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[t], pop[rb], acc[rb][t], 0, 0, 0);
+            if (t + VP < C::DT) vread(t + VP);
         }
     };
 
