@@ -44,8 +44,10 @@ import numpy as np  # noqa: E402
 import torch  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0      # dense bf16 matrix-core peak of the chip
 METRIC = "µs/step + achieved KV-read HBM GB/s (% peak), skewed 32-req bf16 decode"
 DECODE_SRC = os.path.join(ROOT, "paged_split_kv_amd", "csrc", "pa_decode.hip")
+PREFILL_SRC = os.path.join(ROOT, "paged_split_kv_amd", "csrc", "pa_prefill.hip")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_{workload}_counters.json")
 
 
@@ -84,8 +86,8 @@ def source_sha(path: str) -> str:
 
 
 def counter_traffic(workload: str):
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary of this workload, if
-    it was taken on the current decode source; else None."""
+    """HBM bytes per launch of the workload's main kernel from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel sources; else None."""
     try:
         with open(COUNTERS_FILE.format(workload=workload)) as f:
             c = json.load(f)
@@ -93,7 +95,25 @@ def counter_traffic(workload: str):
         return None
     if c.get("decode_source_sha") != source_sha(DECODE_SRC):
         return None
+    if workload == "prefill" and c.get("prefill_source_sha") != source_sha(PREFILL_SRC):
+        return None
     return c.get("traffic_bytes_per_launch")
+
+
+def attention_flops(context_lens, cu_query_lens, num_q_heads: int, head_dim: int, window: int = 0) -> float:
+    """Matrix-core flops of one attention call: every (query token, head) row multiplies each key it
+    sees twice (Q.K and P.V), 2 D flops each; token i of a request with L tokens and S keys sees
+    S - (L - 1 - i) keys, the last W of them under a window."""
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    cu = np.asarray(cu_query_lens, dtype=np.int64)
+    pairs = 0
+    for b in range(ctx.shape[0]):
+        L = int(cu[b + 1] - cu[b])
+        n = np.maximum(ctx[b] - (L - 1 - np.arange(L)), 0)
+        if window > 0:
+            n = np.minimum(n, window)
+        pairs += int(n.sum())
+    return 4.0 * head_dim * num_q_heads * pairs
 
 
 # ------------------------------------------------------------------------------------------------
@@ -359,6 +379,9 @@ def bench_prefill(args, batches, cu_count):
     kv = np.array([float(c.kv_bytes()) for c in batches])
     r = rate(kv, order, ms)
     G = c0.num_q_heads // c0.num_kv_heads
+    flops = np.array([attention_flops(c.context_lens.cpu().numpy(), c.cu_query_lens.cpu().numpy(), c.num_q_heads,
+                                      c.head_dim, c.window) for c in batches])
+    tflops = float(flops[order].sum()) / (ms * 1e-3) / 1e12
     result = {
         "metric": "µs/step + achieved KV-read HBM GB/s (% peak), prompt chunk behind a long prefix (pa_prefill)",
         "value": round(r["gbps"], 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
@@ -370,14 +393,20 @@ def bench_prefill(args, batches, cu_count):
                                f"{c0.block_size}, bf16; {n} independent copies rotated",
                    "group": G},
         "us_per_step": round(r["us_per_step"], 2), "pct_hbm_peak": round(r["pct_peak"], 1),
-        "step": "pa_prefill, split form: the chunk's query blocks planned, decoded split-KV and merged "
+        "step": "pa_prefill, split form: the chunk's query blocks cut and planned, each plan slot computed "
+                "by the query-block kernel (waves share each K/V chunk through LDS), the slots merged "
                 "(four launches)",
         "one_launch_form_us_per_step": None if single is None else round(single, 2),
-        "roofline": {"bound": "hbm", "achieved": round(r["gbps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(r["gbps"] / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "pa_prefill",
+        "tflops": round(tflops, 1),
+        # 512 query tokens against 16.9k keys are a dense contraction: the matrix cores bound it
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "traffic": counter_traffic("prefill"), "kernel": "pa_prefill (all four launches)",
                      "duration_us": round(r["us_per_step"], 3),
+                     "algorithmic_flops_per_launch": round(float(flops[order].mean()), 1),
                      "algorithmic_bytes_per_launch": round(r["mean_bytes"], 1),
-                     "note": "algorithmic bytes count the request's K/V once"},
+                     "note": "flops: 4 D per visible (query row, key) pair; bytes: the request's K/V once; "
+                             "traffic: FETCH + WRITE of the query-block kernel"},
     }
     if not args.step_only:
         result["read_ceiling"] = read_ceiling(stream.device, cu_count)

@@ -83,3 +83,25 @@ def test_rate_counts_exactly_the_timed_steps():
     r20 = bench.rate(sorted_bytes, bench.step_order(20, 128), 1.0)
     assert abs(r20["mean_bytes"] / sorted_bytes.mean() - 1) < 0.05
     assert sorted_bytes[:20].mean() / sorted_bytes.mean() < 0.7
+
+
+def test_attention_flops_counts_each_visible_pair():
+    """Matrix-core flops of the prefill bench: 4 D per visible (query row, key) pair, counted here by
+    brute force over the tokens of small requests, with and without a window."""
+    import numpy as np
+    bench = _bench_module()
+    rng = np.random.default_rng(5)
+    for _ in range(20):
+        B = int(rng.integers(1, 5))
+        L = rng.integers(0, 40, size=B)
+        S = L + rng.integers(0, 300, size=B)
+        cu = np.concatenate([[0], np.cumsum(L)])
+        hq, d = int(rng.choice([4, 12])), int(rng.choice([64, 256]))
+        for W in (0, 1, 17, 1000):
+            pairs = 0
+            for b in range(B):
+                for i in range(int(L[b])):
+                    n = int(S[b]) - (int(L[b]) - 1 - i)
+                    keys = range(max(n - W, 0) if W else 0, n)
+                    pairs += len(keys)
+            assert bench.attention_flops(S, cu, hq, d, W) == 4.0 * d * hq * pairs
