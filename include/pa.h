@@ -287,12 +287,15 @@ pa_status pa_attention_noalloc(const void* q, pa_dtype q_dtype, int32_t num_rows
  *   workspace NULL   each query block (64 / G tokens at head_dim <= 128, 16 / G at 256) is one
  *                    workgroup that streams every key the block sees, in one launch: the form for
  *                    short prompts, whose blocks see few keys.
- *   workspace given  each request's query tokens are cut into blocks of T = 64 / G tokens (32 / G at
- *                    head_dim 256), and the blocks are planned like requests -- the length-proportional
- *                    rule of pa_plan over the blocks' key ranges, with budget 2 x cu_count, ceiling 256
- *                    and 256-token tiles -- then decoded split-KV and merged: a block behind a long
- *                    prefix reads its keys with several workgroups, and each K/V byte is read once per
- *                    block of T tokens.  Four launches: the blocks, their plan, the decode, the merge.
+ *   workspace given  each request's query tokens are cut into blocks of T = 256 / G tokens (128 / G
+ *                    at head_dim 256), and the blocks are planned like requests -- the length-
+ *                    proportional rule of pa_plan over the blocks' key ranges, with budget 1 x
+ *                    cu_count, ceiling 256 and 256-token tiles.  Each plan slot (a block and a range of
+ *                    its keys) is then one workgroup whose eight waves share every 32-key K/V chunk
+ *                    through LDS, each wave holding 16 or 32 of the block's query rows; the slots'
+ *                    states are merged into the rows.  A block behind a long prefix reads its keys with
+ *                    several workgroups, and each K/V byte is read once per block of T tokens.  Four
+ *                    launches: the blocks, their plan, the block kernel, the merge.
  *                    The workspace holds pa_prefill_workspace_bytes(num_rows, num_seqs, num_q_heads,
  *                    num_kv_heads, head_dim, cu_count) bytes, 256-byte aligned, owned by the caller, with
  *                    no initial contents needed; cu_count is the compute-unit count the budget is built
@@ -312,10 +315,10 @@ pa_status pa_prefill(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t 
 
 /*
  * Bytes of workspace pa_prefill's split form needs for num_rows rows of num_seqs prompt requests: the
- * query blocks' lengths, first rows and request indices (at most ceil(num_rows / T) + num_seqs blocks),
- * their plan
- * (work_info for the capacity formula over the blocks, reduce_info, num_work), and the fp32 partial
- * states [capacity, T, num_q_heads, head_dim] plus (max, sum) pairs, each region 256-byte aligned.
+ * query blocks' lengths, first rows and request indices (at most ceil(num_rows / T) + num_seqs blocks,
+ * T as in pa_prefill), their plan (work_info for the capacity formula over the blocks, reduce_info,
+ * num_work), and the fp32 partial states [capacity, T, num_q_heads, head_dim] plus (max, sum) pairs,
+ * each region 256-byte aligned.
  * Returns 0 for invalid sizes or more than PA_MAX_SEQS blocks.  Pure host arithmetic.
  */
 size_t pa_prefill_workspace_bytes(int32_t num_rows, int32_t num_seqs, int32_t num_q_heads,
