@@ -34,6 +34,8 @@ typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(4))) int cint4;
 
 // Word 3 of a raw buffer resource (32-bit data format, no swizzle): loads past the byte count return
 // zero without touching memory.  Cache-policy operand 2 marks a load non-temporal.
@@ -58,10 +60,16 @@ struct Tile {
     static constexpr int LCPR = LRB / 16;              // 16-byte LDS columns per row
     static constexpr int SWM = (LCPR < 16 ? LCPR : 16) - 1;
     static constexpr int TILE = KC * LRB;              // one K or V tile
-    static constexpr int LDS = 4 * TILE;               // K and V of two chunks
+    // bf16 caches at head_dim >= 128 load chunks straight into LDS (no staging registers), NBUF
+    // chunks deep; fp8 (widened on the way) and head_dim 64 stage through registers, two deep
+    static constexpr bool DMA = !KV8 && D >= 128;
+    static constexpr int NBUF = DMA ? 4 : 2;           // LDS chunk buffers
+    static constexpr int NLD = DMA ? 2 * PIECES / NT : 0;   // direct loads per thread per chunk (K and V)
+    static constexpr int LDS = NBUF * 2 * TILE;        // K and V of NBUF chunks
     static constexpr int KS = D / 32;                  // k-steps of S^T
     static constexpr int DT = D / 16;                  // d tiles of O^T
     static_assert(NT % PPR == 0 || PIECES <= NT, "a wave's pieces lie in one half-chunk");
+    static_assert(!DMA || (PIECES % NT == 0 && PPR == LCPR), "direct loads: whole 1 KB runs per wave");
 };
 
 // Byte offset of 16-byte column c of row r of a bf16 tile (XOR swizzle on the column).
@@ -356,36 +364,116 @@ __global__ __launch_bounds__(512, 2) void prefill_tile_kernel(const DecodeArgs a
         }
     };
 
-    // ---- pipeline: LDS parity k & 1 holds chunk k; register set (k + 1) & 1 holds chunk k + 1 in
-    // flight.  Iteration k loads the page ids of chunk k + 3, issues chunk k + 2 into the free register
-    // set, computes chunk k, stages chunk k + 1 into the other parity (last read in iteration k - 1,
-    // before that iteration's barrier) and meets the barrier.  Every wave runs the same trip count. ----
-    int pg[2][2];                                      // page ids of chunks k + 2 and k + 3 (by parity)
-    {
-        const int p00 = page_load(0, 0), p01 = page_load(0, 1);
-        const int p10 = page_load(1, 0), p11 = page_load(1, 1);
-        pg[0][0] = page_load(2, 0);
-        pg[0][1] = page_load(2, 1);
-        issue(0, 0, p00, p01);
-        issue(1, 1, p10, p11);
-        pg[1][0] = page_load(3, 0);
-        pg[1][1] = page_load(3, 1);
-    }
-    stage(0, 0);
-    __syncthreads();
-    for (int k0 = 0; k0 < nchunks; k0 += 2) {
+    if constexpr (C::DMA) {
+        // ---- direct loads: chunk k goes to LDS buffer k % NBUF.  Lane l of a load instruction writes
+        // the 16 bytes at its buffer base + 16 l, so the lane fetches the piece whose swizzled place is
+        // there (the same layout stage() writes); a half-chunk's rows past the slot's last key, or on an
+        // invalid page, are past its resource's byte count and land as zeros.  Page ids come through
+        // scalar loads, so the vector-memory counter counts only the chunk loads: NLD per chunk. ----
+        // the block table is read-only here: through the constant address space a wave-uniform index
+        // is a scalar load
+        cint4* const cbt = (cint4*)(bt_row);
+        auto spage = [&](int k, int half) -> int {
+            const long long key = static_cast<long long>(k_lo) + C::KC * static_cast<long long>(k) + 16 * half;
+            if (key >= k_hi) return -1;                // past the slot: loads nothing
+            return cbt[__builtin_amdgcn_readfirstlane(static_cast<int>(key >> page_shift))];
+        };
+        auto dma = [&](int k, int page0, int page1) {
+            const int key0 = k_lo + C::KC * k;
+            const int nv = k < nchunks ? min(C::KC, k_hi - key0) : 0;
+            __amdgpu_buffer_rsrc_t rk[2], rv[2];
 #pragma unroll
-        for (int par = 0; par < 2; ++par) {
-            const int k = k0 + par;
-            if (par == 1 && k >= nchunks) break;       // uniform: every wave leaves here together
-            const int q0 = pg[par][0], q1 = pg[par][1];
-            pg[par][0] = page_load(k + 4, 0);
-            pg[par][1] = page_load(k + 4, 1);
-            const int nv = nv_of[par];
-            issue(par, k + 2, q0, q1);
-            compute(par, k_lo + C::KC * k, nv);
-            stage(par ^ 1, par ^ 1);
-            __syncthreads();
+            for (int h = 0; h < 2; ++h) {
+                // wave-uniform values, said so: the resources must stay in scalar registers
+                const int blk = __builtin_amdgcn_readfirstlane(h ? page1 : page0);
+                const int nvh = __builtin_amdgcn_readfirstlane(min(max(nv - 16 * h, 0), 16));
+                const bool ok = nvh > 0 && blk >= 0 && blk < a.num_blocks;
+                const int off = (key0 + 16 * h) & (a.block_size - 1);
+                const size_t base = ok ? (static_cast<size_t>(blk) * a.num_kv_heads + g) * head_stride +
+                                             static_cast<size_t>(off) * C::GRB
+                                       : 0;
+                const int records = __builtin_amdgcn_readfirstlane(ok ? nvh * C::GRB : 0);
+                rk[h] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.k_cache + base), 0, records, kRawWord3);
+                rv[h] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.v_cache + base), 0, records, kRawWord3);
+            }
+            uint8_t* const kt = lds + (k % C::NBUF) * 2 * C::TILE;
+            uint8_t* const vt = kt + C::TILE;
+#pragma unroll
+            for (int it = 0; it < C::PIECES / C::NT; ++it) {
+                const int p0 = it * C::NT + wave * 64;         // the wave's first place (uniform)
+                const int pos = p0 + lane;
+                const int r = pos / C::LCPR;
+                const int c = (pos - r * C::LCPR) ^ (r & C::SWM);   // the piece that belongs there
+                const int h = __builtin_amdgcn_readfirstlane(r >> 4);
+                const int vo = (r - 16 * h) * C::GRB + 16 * c;
+                // a branch on the (uniform) half keeps the resource in scalar registers
+                if (h) {
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk[1], (lds_void*)(kt + 16 * p0), 16, vo, 0, 0, kNonTemporal);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv[1], (lds_void*)(vt + 16 * p0), 16, vo, 0, 0, kNonTemporal);
+                } else {
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk[0], (lds_void*)(kt + 16 * p0), 16, vo, 0, 0, kNonTemporal);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv[0], (lds_void*)(vt + 16 * p0), 16, vo, 0, 0, kNonTemporal);
+                }
+            }
+        };
+        // The loop: iteration k waits for chunk k's loads (NBUF - 2 younger chunks may stay in flight)
+        // and meets the barrier, so every wave's part of chunk k is in LDS and every wave is done with
+        // chunk k - 1; it computes chunk k, then loads chunk k + NBUF - 1 into chunk k - 1's buffer.
+        // The barrier carries no memory fence (that would wait for every load in flight); the compiler
+        // fences keep LDS accesses on their side of it.
+        for (int j = 0; j < C::NBUF - 1; ++j) dma(j, spage(j, 0), spage(j, 1));
+        int np0 = spage(C::NBUF - 1, 0), np1 = spage(C::NBUF - 1, 1);
+        constexpr int kWaitChunk = (C::NBUF - 2) * C::NLD;     // loads younger than chunk k's
+        static_assert(kWaitChunk < 64, "vmcnt field");
+        for (int k = 0; k < nchunks; ++k) {
+            __builtin_amdgcn_s_waitcnt((kWaitChunk & 15) | (7 << 4) | (15 << 8) | ((kWaitChunk >> 4) << 14));
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            const int key0 = k_lo + C::KC * k;
+            compute(k % C::NBUF, key0, min(C::KC, k_hi - key0));
+            // after this chunk's reads: before a transposed LDS read the compiler waits for every direct
+            // load in flight (it cannot tell their buffers apart), so loads issued here have a whole
+            // iteration before that wait.  Waiting inside hand-written read blocks instead (so loads
+            // could go first) measured slower.
+            dma(k + C::NBUF - 1, np0, np1);
+            np0 = spage(k + C::NBUF, 0);
+            np1 = spage(k + C::NBUF, 1);
+        }
+        // the last loads (past the slot: zeros) land before the workgroup's LDS is released
+        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    } else {
+        // ---- pipeline: LDS parity k & 1 holds chunk k; register set (k + 1) & 1 holds chunk k + 1 in
+        // flight.  Iteration k loads the page ids of chunk k + 3, issues chunk k + 2 into the free register
+        // set, computes chunk k, stages chunk k + 1 into the other parity (last read in iteration k - 1,
+        // before that iteration's barrier) and meets the barrier.  Every wave runs the same trip count. ----
+        int pg[2][2];                                      // page ids of chunks k + 2 and k + 3 (by parity)
+        {
+            const int p00 = page_load(0, 0), p01 = page_load(0, 1);
+            const int p10 = page_load(1, 0), p11 = page_load(1, 1);
+            pg[0][0] = page_load(2, 0);
+            pg[0][1] = page_load(2, 1);
+            issue(0, 0, p00, p01);
+            issue(1, 1, p10, p11);
+            pg[1][0] = page_load(3, 0);
+            pg[1][1] = page_load(3, 1);
+        }
+        stage(0, 0);
+        __syncthreads();
+        for (int k0 = 0; k0 < nchunks; k0 += 2) {
+    #pragma unroll
+            for (int par = 0; par < 2; ++par) {
+                const int k = k0 + par;
+                if (par == 1 && k >= nchunks) break;       // uniform: every wave leaves here together
+                const int q0 = pg[par][0], q1 = pg[par][1];
+                pg[par][0] = page_load(k + 4, 0);
+                pg[par][1] = page_load(k + 4, 1);
+                const int nv = nv_of[par];
+                issue(par, k + 2, q0, q1);
+                compute(par, k_lo + C::KC * k, nv);
+                stage(par ^ 1, par ^ 1);
+                __syncthreads();
+            }
         }
     }
 
