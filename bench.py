@@ -100,6 +100,13 @@ def counter_traffic(workload: str):
     return c.get("traffic_bytes_per_launch")
 
 
+def traffic_gbps(traffic_bytes, duration_us):
+    """Counter-measured HBM GB/s of a launch: its FETCH + WRITE bytes over the measured duration."""
+    if traffic_bytes is None or duration_us <= 0:
+        return None
+    return round(traffic_bytes / (duration_us * 1e-6) / 1e9, 1)
+
+
 def attention_flops(context_lens, cu_query_lens, num_q_heads: int, head_dim: int, window: int = 0) -> float:
     """Matrix-core flops of one attention call: every (query token, head) row multiplies each key it
     sees twice (Q.K and P.V), 2 D flops each; token i of a request with L tokens and S keys sees
@@ -341,7 +348,8 @@ def bench_mixed(args, batches, cu_count):
         "two_calls_us_per_step": round(two_calls_ms * 1e3 / K, 2),
         "two_streams_us_per_step": round(two_ms * 1e3 / K, 2),
         "roofline": {"bound": "hbm", "achieved": round(dec["gbps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(dec["gbps"] / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(dec["gbps"] / HBM_PEAK_GBPS, 4), "traffic": counter_traffic("mixed"),
+                     "traffic_gbps": traffic_gbps(counter_traffic("mixed"), dec["us_per_step"]),
                      "kernel": "pa_attention over the decode part (decode + merge launches)",
                      "duration_us": round(dec["us_per_step"], 2),
                      "algorithmic_bytes_per_launch": round(dec["mean_bytes"], 1)},
@@ -401,7 +409,9 @@ def bench_prefill(args, batches, cu_count):
         # 512 query tokens against 16.9k keys are a dense contraction: the matrix cores bound it
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-                     "traffic": counter_traffic("prefill"), "kernel": "pa_prefill (all four launches)",
+                     "traffic": counter_traffic("prefill"),
+                     "traffic_gbps": traffic_gbps(counter_traffic("prefill"), r["us_per_step"]),
+                     "kernel": "pa_prefill (all four launches)",
                      "duration_us": round(r["us_per_step"], 3),
                      "algorithmic_flops_per_launch": round(float(flops[order].mean()), 1),
                      "algorithmic_bytes_per_launch": round(r["mean_bytes"], 1),
@@ -744,6 +754,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(dec["gbps"], 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(dec["gbps"] / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
+                     "traffic_gbps": traffic_gbps(traffic, dec["us_per_step"]),
                      "kernel": "pa_decode",
                      "duration_us": round(dec["us_per_step"], 3),
                      "algorithmic_bytes_per_launch": round(dec["mean_bytes"], 1),
