@@ -210,15 +210,30 @@ __host__ __device__ inline size_t workspace_ml_bytes(int capacity, int max_q_len
 }
 
 // Owning request and token of output row r (-1 when the row is padding or otherwise unowned).
-// With cumulative query lengths this is the last b with cu[b] <= r, found by a 64-way search in which
-// every lane of the wave loads one probe: one round of loads for up to 64 requests, two up to 4096.
-// All lanes of the wave must call it with the same r.
+// With cumulative query lengths this is the last b with cu[b] <= r.  Up to 63 requests, lane l of the
+// wave loads cu[l] for l <= num_seqs, and the range check, the owner (a ballot) and its bounds (lane
+// reads) follow from that one round of loads.  Beyond, a 64-way search in which every lane loads one
+// probe: one round of loads for up to 64 requests per level.  A cu that is not monotone (a violated
+// precondition) may give a wrong owner but never a token outside [0, max_q_len).  All lanes of the
+// wave must call it with the same r.
 __device__ __forceinline__ int owner_of_row(const int32_t* cu, int num_seqs, int max_q_len, int r, int& i) {
     i = 0;
     int b = -1;
     if (cu) {
-        if (num_seqs > 0 && r >= cu[0] && r < cu[num_seqs]) {
-            const int lane = threadIdx.x & 63;
+        const int lane = threadIdx.x & 63;
+        if (num_seqs > 0 && num_seqs < 64) {
+            const int v = lane <= num_seqs ? cu[lane] : 0x7fffffff;
+            const int first = __builtin_amdgcn_readlane(v, 0);
+            const int last = __builtin_amdgcn_readlane(v, num_seqs);
+            if (r >= first && r < last) {
+                const unsigned long long m = __builtin_amdgcn_ballot_w64(lane < num_seqs && v <= r);
+                b = __builtin_popcountll(m) - 1;            // >= 0: lane 0 holds first <= r
+                const int c0 = __builtin_amdgcn_readlane(v, b);
+                const int c1 = __builtin_amdgcn_readlane(v, b + 1);
+                i = r - c0;
+                if (i < 0 || i >= c1 - c0) b = -1;
+            }
+        } else if (num_seqs > 0 && r >= cu[0] && r < cu[num_seqs]) {
             int lo = 0, hi = num_seqs;                    // cu[lo] <= r; answer in [lo, hi)
             while (hi - lo > 1) {
                 const int step = (hi - lo + 63) >> 6;
@@ -226,18 +241,19 @@ __device__ __forceinline__ int owner_of_row(const int32_t* cu, int num_seqs, int
                 const int v = idx < hi ? cu[idx] : 0x7fffffff;
                 const unsigned long long m = __builtin_amdgcn_ballot_w64(v <= r);
                 const int k = __builtin_popcountll(m);     // probes are monotone: lanes 0..k-1 hold
-                const int nlo = lo + (k - 1) * step;
+                const int nlo = lo + max(k - 1, 0) * step;
                 hi = min(hi, nlo + step);
                 lo = nlo;
             }
             b = lo;
             i = r - cu[b];
-            if (i >= cu[b + 1] - cu[b]) b = -1;
+            if (i < 0 || i >= cu[b + 1] - cu[b]) b = -1;
         }
     } else if (r < num_seqs) {
         b = r;
     }
     if (i >= max_q_len) b = -1;
+    if (b < 0) i = 0;
     return b;
 }
 
