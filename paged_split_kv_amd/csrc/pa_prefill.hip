@@ -506,6 +506,9 @@ hipError_t launch_tiles_d(const DecodeArgs& a, bool q_f32, hipStream_t stream) {
 
 }  // namespace
 
+static_assert(Tile<64, false>::ROWS == Tile<128, false>::ROWS && Tile<64, true>::ROWS == Tile<128, true>::ROWS &&
+                  Tile<256, true>::ROWS == Tile<256, false>::ROWS,
+              "one block size per head_dim, whatever the cache dtype");
 int prefill_tile_rows(int head_dim) { return head_dim == 256 ? Tile<256, false>::ROWS : Tile<128, false>::ROWS; }
 
 hipError_t launch_prefill_tiles(const DecodeArgs& a, int head_dim, pa_dtype kv_dtype, bool q_f32, hipStream_t stream) {
