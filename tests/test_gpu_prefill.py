@@ -98,6 +98,9 @@ LONG_PREFIX = [
     ("d128_g16_many_blocks", [3000, 2000], [1100, 900], 16, 1, 128, 16, "bf16", "bf16", 0, 0, 64),
     # a request whose query outnumbers its keys (precondition edge): early tokens see nothing
     ("d128_tokens_without_keys", [40, 900], [100, 50], 8, 2, 128, 16, "bf16", "f32", 1, 0, 256),
+    # pages of 64 and 128 tokens on the direct-load path (both halves of a 32-key chunk in one page)
+    ("d256_bs64_bf16", [2500, 900], [120, 60], 12, 2, 256, 64, "bf16", "bf16", 1, 0, 256),
+    ("d128_bs128_bf16_window", [3000, 1000], [200, 33], 16, 2, 128, 128, "bf16", "bf16", 0, 300, 64),
 ]
 
 
