@@ -234,8 +234,8 @@ __global__ __launch_bounds__(512, 2) void prefill_tile_kernel(const DecodeArgs a
     };
     // register set st -> LDS tiles of parity p (rows at or past nv as zeros)
     auto stage = [&](int st, int p) {
-        uint8_t* const kt = lds + p * 2 * C::TILE;
-        uint8_t* const vt = kt + C::TILE;
+        uint8_t* const kt = lds + p * C::TILE;
+        uint8_t* const vt = lds + (C::NBUF + p) * C::TILE;
         const int nv = nv_of[st];
 #pragma unroll
         for (int it = 0; it < C::NL; ++it) {
@@ -268,8 +268,8 @@ __global__ __launch_bounds__(512, 2) void prefill_tile_kernel(const DecodeArgs a
     const int tr_row = 4 * grp + ((lane >> 2) & 3);
     const int tr_d0 = 4 * (lane & 3);
     auto compute = [&](int p, int key0, int nv) {
-        const uint8_t* const kt = lds + p * 2 * C::TILE;
-        const uint8_t* const vt = kt + C::TILE;
+        const uint8_t* const kt = lds + p * C::TILE;
+        const uint8_t* const vt = lds + (C::NBUF + p) * C::TILE;
         if (live_rb == 0) return;
         // S^T for the two 16-key halves: lane holds keys 16 kb + 4 grp + j of row block rb's row col
         // (2 RB independent accumulation chains; blocks past the rows compute on zero queries).  The K
@@ -397,8 +397,8 @@ __global__ __launch_bounds__(512, 2) void prefill_tile_kernel(const DecodeArgs a
                 rk[h] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.k_cache + base), 0, records, kRawWord3);
                 rv[h] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.v_cache + base), 0, records, kRawWord3);
             }
-            uint8_t* const kt = lds + (k % C::NBUF) * 2 * C::TILE;
-            uint8_t* const vt = kt + C::TILE;
+            uint8_t* const kt = lds + (k % C::NBUF) * C::TILE;
+            uint8_t* const vt = lds + (C::NBUF + k % C::NBUF) * C::TILE;
 #pragma unroll
             for (int it = 0; it < C::PIECES / C::NT; ++it) {
                 const int p0 = it * C::NT + wave * 64;         // the wave's first place (uniform)
@@ -426,20 +426,27 @@ __global__ __launch_bounds__(512, 2) void prefill_tile_kernel(const DecodeArgs a
         int np0 = spage(C::NBUF - 1, 0), np1 = spage(C::NBUF - 1, 1);
         constexpr int kWaitChunk = (C::NBUF - 2) * C::NLD;     // loads younger than chunk k's
         static_assert(kWaitChunk < 64, "vmcnt field");
-        for (int k = 0; k < nchunks; ++k) {
-            __builtin_amdgcn_s_waitcnt((kWaitChunk & 15) | (7 << 4) | (15 << 8) | ((kWaitChunk >> 4) << 14));
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
-            const int key0 = k_lo + C::KC * k;
-            compute(k % C::NBUF, key0, min(C::KC, k_hi - key0));
-            // after this chunk's reads: before a transposed LDS read the compiler waits for every direct
-            // load in flight (it cannot tell their buffers apart), so loads issued here have a whole
-            // iteration before that wait.  Waiting inside hand-written read blocks instead (so loads
-            // could go first) measured slower.
-            dma(k + C::NBUF - 1, np0, np1);
-            np0 = spage(k + C::NBUF, 0);
-            np1 = spage(k + C::NBUF, 1);
+        // unrolled NBUF times, so each buffer is a constant: the LDS reads then take their buffer in the
+        // instructions' offset field (K tiles in the first 64 KB, V tiles after them)
+        for (int k0 = 0; k0 < nchunks; k0 += C::NBUF) {
+#pragma unroll
+            for (int par = 0; par < C::NBUF; ++par) {
+                const int k = k0 + par;
+                if (k >= nchunks) break;               // uniform: every wave leaves here together
+                __builtin_amdgcn_s_waitcnt((kWaitChunk & 15) | (7 << 4) | (15 << 8) | ((kWaitChunk >> 4) << 14));
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+                const int key0 = k_lo + C::KC * k;
+                compute(par, key0, min(C::KC, k_hi - key0));
+                // after this chunk's reads: before a transposed LDS read the compiler waits for every
+                // direct load in flight (it cannot tell their buffers apart), so loads issued here have
+                // a whole iteration before that wait.  Waiting inside hand-written read blocks instead
+                // (so loads could go first) measured slower.
+                dma(k + C::NBUF - 1, np0, np1);
+                np0 = spage(k + C::NBUF, 0);
+                np1 = spage(k + C::NBUF, 1);
+            }
         }
         // the last loads (past the slot: zeros) land before the workgroup's LDS is released
         __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
