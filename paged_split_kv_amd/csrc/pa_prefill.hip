@@ -45,6 +45,26 @@ constexpr int kNonTemporal = 2;
 // Rescale threshold of the running maximum, in base-2 units: probabilities stay below 2^8.
 constexpr float kSlack = 8.0f;
 
+// One direct load: each lane reads 16 bytes at its offset in the (scalar) buffer resource and the
+// unit writes them to LDS at dst + 16 * lane, with zeros for lanes past the byte count.  The block
+// names no register as output (the data goes to LDS only), and it is hand-written so that the
+// compiler does not count it: otherwise it waits for every direct load in flight before each
+// transposed LDS read.  The caller waits with explicit vector-memory counts before reading the data.
+__device__ __forceinline__ void lds_load16(u32x4_t rsrc, const lds_void* dst, int voffset) {
+    const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<size_t>(dst));
+    asm volatile("buffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                 :
+                 : "{m0}"(m0), "v"(voffset), "s"(rsrc)
+                 : "memory");
+}
+
+// The four words of a raw buffer resource over [base, base + records).
+__device__ __forceinline__ u32x4_t raw_rsrc(const uint8_t* base, int records) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    return u32x4_t{static_cast<uint32_t>(p), static_cast<uint32_t>(p >> 32) & 0xffffu,
+                   static_cast<uint32_t>(records), static_cast<uint32_t>(kRawWord3)};
+}
+
 template <int D, bool KV8>
 struct Tile {
     static constexpr int NW = 8;                       // waves (two per SIMD)
@@ -382,7 +402,7 @@ __global__ __launch_bounds__(512, 2) void prefill_tile_kernel(const DecodeArgs a
         auto dma = [&](int k, int page0, int page1) {
             const int key0 = k_lo + C::KC * k;
             const int nv = k < nchunks ? min(C::KC, k_hi - key0) : 0;
-            __amdgpu_buffer_rsrc_t rk[2], rv[2];
+            u32x4_t rk[2], rv[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 // wave-uniform values, said so: the resources must stay in scalar registers
@@ -394,8 +414,8 @@ __global__ __launch_bounds__(512, 2) void prefill_tile_kernel(const DecodeArgs a
                                              static_cast<size_t>(off) * C::GRB
                                        : 0;
                 const int records = __builtin_amdgcn_readfirstlane(ok ? nvh * C::GRB : 0);
-                rk[h] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.k_cache + base), 0, records, kRawWord3);
-                rv[h] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.v_cache + base), 0, records, kRawWord3);
+                rk[h] = raw_rsrc(a.k_cache + base, records);
+                rv[h] = raw_rsrc(a.v_cache + base, records);
             }
             uint8_t* const kt = lds + (k % C::NBUF) * C::TILE;
             uint8_t* const vt = lds + (C::NBUF + k % C::NBUF) * C::TILE;
@@ -409,19 +429,23 @@ __global__ __launch_bounds__(512, 2) void prefill_tile_kernel(const DecodeArgs a
                 const int vo = (r - 16 * h) * C::GRB + 16 * c;
                 // a branch on the (uniform) half keeps the resource in scalar registers
                 if (h) {
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk[1], (lds_void*)(kt + 16 * p0), 16, vo, 0, 0, kNonTemporal);
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv[1], (lds_void*)(vt + 16 * p0), 16, vo, 0, 0, kNonTemporal);
+                    lds_load16(rk[1], (const lds_void*)(kt + 16 * p0), vo);
+                    lds_load16(rv[1], (const lds_void*)(vt + 16 * p0), vo);
                 } else {
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk[0], (lds_void*)(kt + 16 * p0), 16, vo, 0, 0, kNonTemporal);
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv[0], (lds_void*)(vt + 16 * p0), 16, vo, 0, 0, kNonTemporal);
+                    lds_load16(rk[0], (const lds_void*)(kt + 16 * p0), vo);
+                    lds_load16(rv[0], (const lds_void*)(vt + 16 * p0), vo);
                 }
             }
         };
         // The loop: iteration k waits for chunk k's loads (NBUF - 2 younger chunks may stay in flight)
         // and meets the barrier, so every wave's part of chunk k is in LDS and every wave is done with
-        // chunk k - 1; it computes chunk k, then loads chunk k + NBUF - 1 into chunk k - 1's buffer.
+        // chunk k - 1; it loads chunk k + NBUF - 1 into chunk k - 1's buffer, then computes chunk k.
         // The barrier carries no memory fence (that would wait for every load in flight); the compiler
         // fences keep LDS accesses on their side of it.
+        // The query loads land first: the compiler does not see the direct loads, so once it knows the
+        // query operands are in registers it adds no wait of its own for them inside the loop.
+        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+        asm volatile("" ::: "memory");
         for (int j = 0; j < C::NBUF - 1; ++j) dma(j, spage(j, 0), spage(j, 1));
         int np0 = spage(C::NBUF - 1, 0), np1 = spage(C::NBUF - 1, 1);
         constexpr int kWaitChunk = (C::NBUF - 2) * C::NLD;     // loads younger than chunk k's
@@ -437,13 +461,9 @@ __global__ __launch_bounds__(512, 2) void prefill_tile_kernel(const DecodeArgs a
                 asm volatile("" ::: "memory");
                 __builtin_amdgcn_s_barrier();
                 asm volatile("" ::: "memory");
+                dma(k + C::NBUF - 1, np0, np1);
                 const int key0 = k_lo + C::KC * k;
                 compute(par, key0, min(C::KC, k_hi - key0));
-                // after this chunk's reads: before a transposed LDS read the compiler waits for every
-                // direct load in flight (it cannot tell their buffers apart), so loads issued here have
-                // a whole iteration before that wait.  Waiting inside hand-written read blocks instead
-                // (so loads could go first) measured slower.
-                dma(k + C::NBUF - 1, np0, np1);
                 np0 = spage(k + C::NBUF, 0);
                 np1 = spage(k + C::NBUF, 1);
             }
