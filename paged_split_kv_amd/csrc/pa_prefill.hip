@@ -336,24 +336,26 @@ __global__ __launch_bounds__(512, 2) void prefill_tile_kernel(const DecodeArgs a
         };
 #pragma unroll
         for (int t = 0; t < VP; ++t) vread(t);
-        // the chunk lies inside every row's visible range: no mask (uniform)
-        const bool full = nv == C::KC && key0 + C::KC <= nvis_min && key0 >= nlo_max;
-        bf16x8_t pop[C::RB];
+        // a chunk inside every row's visible range takes no mask (uniform); otherwise the scores past a
+        // row's range become -inf in place, so both cases share one softmax
+        if (!(nv == C::KC && key0 + C::KC <= nvis_min && key0 >= nlo_max)) {
 #pragma unroll
-        for (int rb = 0; rb < C::RB; ++rb) {
-            float x[8];
-            if (full) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) x[j] = sc[j >> 2][rb][j & 3] * a.score_scale_log2;
-            } else {
+            for (int rb = 0; rb < C::RB; ++rb) {
                 const int lim = min(nv, nvis[rb] - key0);
                 const int low = nlo[rb] - key0;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int q = 16 * (j >> 2) + 4 * grp + (j & 3);
-                    x[j] = (q < lim && q >= low) ? sc[j >> 2][rb][j & 3] * a.score_scale_log2 : -INFINITY;
+                    if (!(q < lim && q >= low)) sc[j >> 2][rb][j & 3] = -INFINITY;
                 }
             }
+        }
+        bf16x8_t pop[C::RB];
+#pragma unroll
+        for (int rb = 0; rb < C::RB; ++rb) {
+            float x[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[j] = sc[j >> 2][rb][j & 3] * a.score_scale_log2;
             float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
             mt = row_max4(mt);
             const bool grow = mt > m_run[rb] + kSlack;
@@ -386,55 +388,56 @@ __global__ __launch_bounds__(512, 2) void prefill_tile_kernel(const DecodeArgs a
     };
 
     if constexpr (C::DMA) {
-        // ---- direct loads: chunk k goes to LDS buffer k % NBUF.  Lane l of a load instruction writes
-        // the 16 bytes at its buffer base + 16 l, so the lane fetches the piece whose swizzled place is
-        // there (the same layout stage() writes); a half-chunk's rows past the slot's last key, or on an
-        // invalid page, are past its resource's byte count and land as zeros.  Page ids come through
-        // scalar loads, so the vector-memory counter counts only the chunk loads: NLD per chunk. ----
+        // ---- direct loads: chunk k goes to LDS buffer k % NBUF.  The first NW / 2 waves load the first
+        // 16 keys of every chunk and the others the last 16, so a wave finds one page and builds one pair
+        // of resources per chunk.  Lane l of a load instruction writes the 16 bytes at its base + 16 l, so
+        // the lane fetches the piece whose swizzled place is there (the same layout stage() writes); rows
+        // past the slot's last key, or on an invalid page, are past the resource's byte count and land as
+        // zeros.  Page ids come through scalar loads, so the vector-memory counter counts only the chunk
+        // loads: NLD per chunk. ----
+        constexpr int HW = C::NW / 2;                  // waves per half-chunk
+        constexpr int WPOS = 16 * C::LCPR / HW;        // a wave's 16-byte places in a half of a tile
+        constexpr int ITS = WPOS / 64;                 // its loads per tile and chunk
+        static_assert(WPOS % 64 == 0 && 2 * ITS == C::NLD, "whole loads per wave");
+        const int half = wave / HW;                    // wave-uniform
+        const int p0w = 16 * C::LCPR * half + WPOS * (wave - HW * half);   // the wave's first place
+        int vo[ITS];                                   // per lane: its piece's offset in the half's rows
+#pragma unroll
+        for (int it = 0; it < ITS; ++it) {
+            const int pos = p0w + 64 * it + lane;
+            const int r = pos / C::LCPR;
+            const int c = (pos - r * C::LCPR) ^ (r & C::SWM);
+            vo[it] = (r - 16 * half) * C::GRB + 16 * c;
+        }
+        const uint8_t* const kg = a.k_cache + static_cast<size_t>(g) * head_stride;
+        const uint8_t* const vg = a.v_cache + static_cast<size_t>(g) * head_stride;
+        const size_t page_stride = static_cast<size_t>(a.num_kv_heads) * head_stride;
         // the block table is read-only here: through the constant address space a wave-uniform index
         // is a scalar load
         cint4* const cbt = (cint4*)(bt_row);
-        auto spage = [&](int k, int half) -> int {
-            const long long key = static_cast<long long>(k_lo) + C::KC * static_cast<long long>(k) + 16 * half;
-            if (key >= k_hi) return -1;                // past the slot: loads nothing
-            return cbt[__builtin_amdgcn_readfirstlane(static_cast<int>(key >> page_shift))];
+        // the page of this wave's half of chunk k, -1 past the slot (loads nothing)
+        auto spage = [&](int k) -> int {
+            if (k >= nchunks) return -1;
+            const int key = k_lo + C::KC * k + 16 * half;
+            if (key >= k_hi) return -1;
+            return cbt[key >> page_shift];
         };
-        auto dma = [&](int k, int page0, int page1) {
-            const int key0 = k_lo + C::KC * k;
-            const int nv = k < nchunks ? min(C::KC, k_hi - key0) : 0;
-            u32x4_t rk[2], rv[2];
+        auto dma = [&](int k, int page) {
+            const int key = k_lo + C::KC * k + 16 * half;
+            const int nvh = k < nchunks ? min(max(k_hi - key, 0), 16) : 0;
+            const bool ok = nvh > 0 && page >= 0 && page < a.num_blocks;
+            const size_t off = ok ? static_cast<size_t>(page) * page_stride +
+                                        static_cast<size_t>(key & (a.block_size - 1)) * C::GRB
+                                  : 0;
+            const int records = ok ? nvh * C::GRB : 0;
+            const u32x4_t rk = raw_rsrc(kg + off, records);
+            const u32x4_t rv = raw_rsrc(vg + off, records);
+            const uint8_t* const kt = lds + (k % C::NBUF) * C::TILE + 16 * p0w;
+            const uint8_t* const vt = lds + (C::NBUF + k % C::NBUF) * C::TILE + 16 * p0w;
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                // wave-uniform values, said so: the resources must stay in scalar registers
-                const int blk = __builtin_amdgcn_readfirstlane(h ? page1 : page0);
-                const int nvh = __builtin_amdgcn_readfirstlane(min(max(nv - 16 * h, 0), 16));
-                const bool ok = nvh > 0 && blk >= 0 && blk < a.num_blocks;
-                const int off = (key0 + 16 * h) & (a.block_size - 1);
-                const size_t base = ok ? (static_cast<size_t>(blk) * a.num_kv_heads + g) * head_stride +
-                                             static_cast<size_t>(off) * C::GRB
-                                       : 0;
-                const int records = __builtin_amdgcn_readfirstlane(ok ? nvh * C::GRB : 0);
-                rk[h] = raw_rsrc(a.k_cache + base, records);
-                rv[h] = raw_rsrc(a.v_cache + base, records);
-            }
-            uint8_t* const kt = lds + (k % C::NBUF) * C::TILE;
-            uint8_t* const vt = lds + (C::NBUF + k % C::NBUF) * C::TILE;
-#pragma unroll
-            for (int it = 0; it < C::PIECES / C::NT; ++it) {
-                const int p0 = it * C::NT + wave * 64;         // the wave's first place (uniform)
-                const int pos = p0 + lane;
-                const int r = pos / C::LCPR;
-                const int c = (pos - r * C::LCPR) ^ (r & C::SWM);   // the piece that belongs there
-                const int h = __builtin_amdgcn_readfirstlane(r >> 4);
-                const int vo = (r - 16 * h) * C::GRB + 16 * c;
-                // a branch on the (uniform) half keeps the resource in scalar registers
-                if (h) {
-                    lds_load16(rk[1], (const lds_void*)(kt + 16 * p0), vo);
-                    lds_load16(rv[1], (const lds_void*)(vt + 16 * p0), vo);
-                } else {
-                    lds_load16(rk[0], (const lds_void*)(kt + 16 * p0), vo);
-                    lds_load16(rv[0], (const lds_void*)(vt + 16 * p0), vo);
-                }
+            for (int it = 0; it < ITS; ++it) {
+                lds_load16(rk, (const lds_void*)(kt + 1024 * it), vo[it]);
+                lds_load16(rv, (const lds_void*)(vt + 1024 * it), vo[it]);
             }
         };
         // The loop: iteration k waits for chunk k's loads (NBUF - 2 younger chunks may stay in flight)
@@ -446,8 +449,8 @@ __global__ __launch_bounds__(512, 2) void prefill_tile_kernel(const DecodeArgs a
         // query operands are in registers it adds no wait of its own for them inside the loop.
         __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
         asm volatile("" ::: "memory");
-        for (int j = 0; j < C::NBUF - 1; ++j) dma(j, spage(j, 0), spage(j, 1));
-        int np0 = spage(C::NBUF - 1, 0), np1 = spage(C::NBUF - 1, 1);
+        for (int j = 0; j < C::NBUF - 1; ++j) dma(j, spage(j));
+        int np = spage(C::NBUF - 1);
         constexpr int kWaitChunk = (C::NBUF - 2) * C::NLD;     // loads younger than chunk k's
         static_assert(kWaitChunk < 64, "vmcnt field");
         // unrolled NBUF times, so each buffer is a constant: the LDS reads then take their buffer in the
@@ -461,11 +464,10 @@ __global__ __launch_bounds__(512, 2) void prefill_tile_kernel(const DecodeArgs a
                 asm volatile("" ::: "memory");
                 __builtin_amdgcn_s_barrier();
                 asm volatile("" ::: "memory");
-                dma(k + C::NBUF - 1, np0, np1);
+                dma(k + C::NBUF - 1, np);
                 const int key0 = k_lo + C::KC * k;
                 compute(par, key0, min(C::KC, k_hi - key0));
-                np0 = spage(k + C::NBUF, 0);
-                np1 = spage(k + C::NBUF, 1);
+                np = spage(k + C::NBUF);
             }
         }
         // the last loads (past the slot: zeros) land before the workgroup's LDS is released
