@@ -93,10 +93,25 @@ struct Tile {
     static_assert(!DMA || (PIECES % NT == 0 && PPR == LCPR), "direct loads: whole 1 KB runs per wave");
 };
 
-// Byte offset of 16-byte column c of row r of a bf16 tile (XOR swizzle on the column).
-template <int LRB, int SWM>
-__device__ __forceinline__ int tile_col(int r, int c) {
-    return r * LRB + ((c ^ (r & SWM)) << 4);
+// XOR swizzles of the 16-byte columns, one per tile (measured with the kernel's own read patterns;
+// rows of 256 bytes and up all start on the same bank):
+//  * K tiles are read 16 rows x one column per quarter wave (16-byte reads): r & 15 keeps those
+//    reads at the full LDS rate;
+//  * V tiles are read by the transposing 8-byte reads, each half wave taking 8 rows x two adjacent
+//    columns: r & 15 puts rows r and r ^ 1 on the same two columns, so with 16 columns a row the V
+//    XOR is even on rows 0-7 and odd on rows 8-15, which spreads them over 16 distinct columns.
+template <int SWM>
+__device__ __forceinline__ int kxor(int r) { return r & SWM; }
+template <int SWM>
+__device__ __forceinline__ int vxor(int r) {
+    if constexpr (SWM == 15) return ((r & 7) << 1) | ((r >> 3) & 1);
+    else return r & SWM;
+}
+
+// Byte offset of 16-byte column c of row r of a bf16 tile whose row r columns are XORed with x.
+template <int LRB>
+__device__ __forceinline__ int tile_col(int r, int c, int x) {
+    return r * LRB + ((c ^ x) << 4);
 }
 
 __device__ __forceinline__ float row_max4(float x) {
@@ -267,19 +282,17 @@ __global__ __launch_bounds__(512, 2) void prefill_tile_kernel(const DecodeArgs a
             const u32x4_t kv = r < nv ? kreg[st][it] : z;
             const u32x4_t vv = r < nv ? vreg[st][it] : z;
             if constexpr (!KV8) {
-                const int off = tile_col<C::LRB, C::SWM>(r, c);
-                *reinterpret_cast<u32x4_t*>(kt + off) = kv;
-                *reinterpret_cast<u32x4_t*>(vt + off) = vv;
+                *reinterpret_cast<u32x4_t*>(kt + tile_col<C::LRB>(r, c, kxor<C::SWM>(r))) = kv;
+                *reinterpret_cast<u32x4_t*>(vt + tile_col<C::LRB>(r, c, vxor<C::SWM>(r))) = vv;
             } else {
                 u32x4_t klo, khi, vlo, vhi;
                 widen_fp8(kv, klo, khi);
                 widen_fp8(vv, vlo, vhi);
-                const int o0 = tile_col<C::LRB, C::SWM>(r, 2 * c);
-                const int o1 = tile_col<C::LRB, C::SWM>(r, 2 * c + 1);
-                *reinterpret_cast<u32x4_t*>(kt + o0) = klo;
-                *reinterpret_cast<u32x4_t*>(kt + o1) = khi;
-                *reinterpret_cast<u32x4_t*>(vt + o0) = vlo;
-                *reinterpret_cast<u32x4_t*>(vt + o1) = vhi;
+                const int kx = kxor<C::SWM>(r), vx = vxor<C::SWM>(r);
+                *reinterpret_cast<u32x4_t*>(kt + tile_col<C::LRB>(r, 2 * c, kx)) = klo;
+                *reinterpret_cast<u32x4_t*>(kt + tile_col<C::LRB>(r, 2 * c + 1, kx)) = khi;
+                *reinterpret_cast<u32x4_t*>(vt + tile_col<C::LRB>(r, 2 * c, vx)) = vlo;
+                *reinterpret_cast<u32x4_t*>(vt + tile_col<C::LRB>(r, 2 * c + 1, vx)) = vhi;
             }
         }
     };
@@ -300,7 +313,7 @@ __global__ __launch_bounds__(512, 2) void prefill_tile_kernel(const DecodeArgs a
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
                 kop[s][kb] = __builtin_bit_cast(
-                    bf16x8_t, *reinterpret_cast<const u32x4_t*>(kt + tile_col<C::LRB, C::SWM>(16 * kb + col, 4 * s + grp)));
+                    bf16x8_t, *reinterpret_cast<const u32x4_t*>(kt + tile_col<C::LRB>(16 * kb + col, 4 * s + grp, kxor<C::SWM>(16 * kb + col))));
         };
 #pragma unroll
         for (int s = 0; s < KP; ++s) kread(s);
@@ -325,8 +338,8 @@ __global__ __launch_bounds__(512, 2) void prefill_tile_kernel(const DecodeArgs a
         bf16x8_t vop[C::DT];
         auto vread = [&](int t) {
             const int d0 = 16 * t + tr_d0;
-            const int o0 = tile_col<C::LRB, C::SWM>(tr_row, d0 >> 3) + ((d0 & 7) << 1);
-            const int o1 = tile_col<C::LRB, C::SWM>(16 + tr_row, d0 >> 3) + ((d0 & 7) << 1);
+            const int o0 = tile_col<C::LRB>(tr_row, d0 >> 3, vxor<C::SWM>(tr_row)) + ((d0 & 7) << 1);
+            const int o1 = tile_col<C::LRB>(16 + tr_row, d0 >> 3, vxor<C::SWM>(16 + tr_row)) + ((d0 & 7) << 1);
             const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(vt + o0));
             const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(vt + o1));
             const u32x2_t a0 = __builtin_bit_cast(u32x2_t, v0);
@@ -401,13 +414,14 @@ __global__ __launch_bounds__(512, 2) void prefill_tile_kernel(const DecodeArgs a
         static_assert(WPOS % 64 == 0 && 2 * ITS == C::NLD, "whole loads per wave");
         const int half = wave / HW;                    // wave-uniform
         const int p0w = 16 * C::LCPR * half + WPOS * (wave - HW * half);   // the wave's first place
-        int vo[ITS];                                   // per lane: its piece's offset in the half's rows
+        int ko[ITS], vo[ITS];                          // per lane: its pieces' offsets in the half's rows
 #pragma unroll
         for (int it = 0; it < ITS; ++it) {
             const int pos = p0w + 64 * it + lane;
             const int r = pos / C::LCPR;
-            const int c = (pos - r * C::LCPR) ^ (r & C::SWM);
-            vo[it] = (r - 16 * half) * C::GRB + 16 * c;
+            const int c = pos - r * C::LCPR;           // the place; the piece that belongs there:
+            ko[it] = (r - 16 * half) * C::GRB + 16 * (c ^ kxor<C::SWM>(r));
+            vo[it] = (r - 16 * half) * C::GRB + 16 * (c ^ vxor<C::SWM>(r));
         }
         const uint8_t* const kg = a.k_cache + static_cast<size_t>(g) * head_stride;
         const uint8_t* const vg = a.v_cache + static_cast<size_t>(g) * head_stride;
@@ -436,7 +450,7 @@ __global__ __launch_bounds__(512, 2) void prefill_tile_kernel(const DecodeArgs a
             const uint8_t* const vt = lds + (C::NBUF + k % C::NBUF) * C::TILE + 16 * p0w;
 #pragma unroll
             for (int it = 0; it < ITS; ++it) {
-                lds_load16(rk, (const lds_void*)(kt + 1024 * it), vo[it]);
+                lds_load16(rk, (const lds_void*)(kt + 1024 * it), ko[it]);
                 lds_load16(rv, (const lds_void*)(vt + 1024 * it), vo[it]);
             }
         };
