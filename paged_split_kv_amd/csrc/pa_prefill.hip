@@ -13,12 +13,13 @@
 //  * one workgroup of 8 waves (two per SIMD) per (slot, kv head); wave w owns RB blocks of 16 query
 //    rows (rows 16 RB w .. 16 RB (w+1) - 1 of the block) and all D columns of their accumulators,
 //    which with the query operands fit the 256 registers of a wave with no copies between register
-//    files; while one wave of a SIMD runs its softmax the other runs its products;
-//  * the slot's keys go in chunks of 32, loaded by all 512 threads (16-byte coalesced non-temporal
-//    loads) as bf16 rows into LDS tiles with an XOR swizzle on the 16-byte column: bf16 caches at
-//    head_dim >= 128 straight from HBM into a ring of four LDS chunk buffers, fp8 (widened on the
-//    way) and head_dim 64 through registers into two; every wave then reads the whole chunk, so each
-//    K/V byte is fetched once per workgroup and read from LDS by 8 waves;
+//    files;
+//  * the slot's keys go in chunks of 32, loaded with 16-byte coalesced non-temporal loads as bf16
+//    rows into LDS tiles, K and V each with an XOR swizzle of its own on the 16-byte column: bf16
+//    caches at head_dim >= 128 straight from HBM into a ring of four LDS chunk buffers (each half of
+//    the waves loading one 16-key half of every chunk), fp8 (widened on the way) and head_dim 64
+//    through registers into two; every wave then reads the whole chunk, so each K/V byte is fetched
+//    once per workgroup and read from LDS by 8 waves;
 //  * S^T = K . Q^T on v_mfma_f32_16x16x32_bf16 (keys as rows, query rows as columns), the online
 //    softmax in base 2 with lazy rescaling, and O^T = V^T . P^T on the same instruction over the 32
 //    keys (V^T from the LDS transpose read), as in the decode kernel;
