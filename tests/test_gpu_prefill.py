@@ -34,6 +34,10 @@ PREFILL = [
     ("bf16_g1_prompts", [333, 90], [200, 90], 4, 4, 128, 16, "bf16", "bf16", 1, 0),
     # 32 query heads per kv head: 2 tokens per 64-row block, with a window
     ("bf16_g32_window", [700, 129], [41, 7], 32, 1, 64, 16, "bf16", "bf16", 0, 100),
+    # the direct-load path at head_dim 256: fp32 queries under a window (chunks wholly before a row's
+    # window), and slots of fewer chunks than the ring holds (one to two 32-key chunks, ragged)
+    ("bf16_d256_qf32_window40", [500, 45], [200, 45], 12, 2, 256, 16, "bf16", "f32", 1, 40),
+    ("bf16_d256_short_slots", [20, 60, 3, 33], [20, 10, 3, 1], 8, 2, 256, 16, "bf16", "bf16", 0, 0),
 ]
 
 
