@@ -403,7 +403,7 @@ def bench_prefill(args, batches, cu_count):
         "us_per_step": round(r["us_per_step"], 2), "pct_hbm_peak": round(r["pct_peak"], 1),
         "step": "pa_prefill, split form: the chunk's query blocks cut and planned, each plan slot computed "
                 "by the query-block kernel (waves share each K/V chunk through LDS), the slots merged "
-                "(four launches)",
+                "(three launches)",
         "one_launch_form_us_per_step": None if single is None else round(single, 2),
         "tflops": round(tflops, 1),
         # 512 query tokens against 16.9k keys are a dense contraction: the matrix cores bound it
@@ -411,7 +411,7 @@ def bench_prefill(args, batches, cu_count):
                      "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
                      "traffic": counter_traffic("prefill"),
                      "traffic_gbps": traffic_gbps(counter_traffic("prefill"), r["us_per_step"]),
-                     "kernel": "pa_prefill (all four launches)",
+                     "kernel": "pa_prefill (all three launches)",
                      "duration_us": round(r["us_per_step"], 3),
                      "algorithmic_flops_per_launch": round(float(flops[order].mean()), 1),
                      "algorithmic_bytes_per_launch": round(r["mean_bytes"], 1),

@@ -584,11 +584,10 @@ pa_status pa_prefill(const void* q, pa_dtype q_dtype, int32_t num_rows, int32_t 
     int32_t* num_work = reinterpret_cast<int32_t*>(ws + L.num_work);
     float* states = reinterpret_cast<float*>(ws + L.states);
     const hipStream_t s = pa::as_stream(stream);
-    st = from_hip(pa::launch_prefill_blocks(context_lens, cu_query_lens, num_seqs, L.block_tokens, L.max_blocks,
-                                            blk_ctx, blk_cu, blk_req, s));
-    if (st != PA_OK) return st;
+    // one launch cuts the query blocks and plans them
+    const pa::PlanBlocks blocks{context_lens, cu_query_lens, num_seqs, L.block_tokens, blk_ctx, blk_cu, blk_req};
     st = from_hip(pa::launch_plan(blk_ctx, blk_cu, L.max_blocks, L.capacity, L.capacity, 256, 256, sliding_window,
-                                  work, reduce, num_work, nullptr, s));
+                                  work, reduce, num_work, nullptr, s, &blocks));
     if (st != PA_OK) return st;
 
     pa::DecodeArgs d = pa::DecodeArgs{};

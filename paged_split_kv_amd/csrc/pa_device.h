@@ -357,15 +357,20 @@ inline bool shares_slots(int one_slot_cap, int num_seqs, int head_dim, int capac
            workspace_bytes >= shared_region(capacity, max_q_len, hq, head_dim).end;
 }
 
+// A split prefill's requests, cut into query blocks by the plan launch itself before it plans them
+// (the planned sequences are then the blocks: num_seqs = max_blocks); see cut_blocks in pa_plan.hip.
+struct PlanBlocks {
+    const int32_t* ctx;       // the requests' context lengths [num_reqs] (null: no blocks to cut)
+    const int32_t* cu;        // their query rows [num_reqs + 1]
+    int num_reqs, block_tokens;
+    int32_t *blk_ctx, *blk_cu, *blk_req;   // per block [max_blocks] (blk_cu [max_blocks + 1])
+};
 hipError_t launch_plan(const int32_t* context_lens, const int32_t* cu, int num_seqs,
                        int cap_formula, int capacity, int max_partitions, int tile_tokens, int window,
                        int32_t* work_info, int32_t* reduce_info, int32_t* num_work, int32_t* dispatch_info,
-                       hipStream_t stream);
+                       hipStream_t stream, const PlanBlocks* blocks = nullptr);
 // Plans of at most this many slots get a balanced dispatch order; larger ones the identity.
 constexpr int kDispatchMaxSlots = 1024;
-hipError_t launch_prefill_blocks(const int32_t* context_lens, const int32_t* cu, int num_seqs, int block_tokens,
-                                 int max_blocks, int32_t* blk_ctx, int32_t* blk_cu, int32_t* blk_req,
-                                 hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, pa_dtype kv_dtype, bool q_f32,
                          hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int head_dim, bool out_bf16, hipStream_t stream);

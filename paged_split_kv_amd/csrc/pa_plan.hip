@@ -37,12 +37,70 @@ __device__ __forceinline__ int rank_key(int tiles, int slot) {
     return ((min(tiles, kRankKeyTiles - 1) + 2) << 11) | (2047 - slot);
 }
 
+// Query blocks of a prefill batch as pseudo-requests for the planner, the decode and the merge: each
+// request's query tokens [0, L_b) are cut into blocks of block_tokens, numbered request by request.
+// Block j covering tokens [i0, i1) of request b gets
+//   blk_cu[j] = cu[b] + i0                (its first row; blk_cu[max_blocks] = cu[num_seqs]),
+//   blk_ctx[j] = S_b - (L_b - i1)         (the keys its last token sees, at least 0),
+//   blk_req[j] = b                        (the request's block-table row),
+// so that token i of the block sees blk_ctx[j] - (i1 - 1 - i) = S_b - (L_b - 1 - i) keys, the
+// request's own per-token causal range (opengfx1030/vllm-rdna PR #29, Change 1).  Slots past the last
+// block are empty blocks (blk_cu = cu[num_seqs], blk_ctx = 0, blk_req = 0).  Each thread takes a
+// contiguous run of requests; a scan over the threads gives each run's first block.  The blocks'
+// lengths and token counts also go to the planner's LDS arrays (the caller meets the barrier after).
+__device__ void cut_blocks(const PlanBlocks& pb, int max_blocks, int32_t* s_len, int32_t* s_qlen) {
+    __shared__ int scan_carry[kPlanWaves];
+    __shared__ int s_total;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int32_t* const cu = pb.cu;
+    const int per = (pb.num_reqs + kPlanThreads - 1) / kPlanThreads;
+    const int b0 = min(tid * per, pb.num_reqs);
+    const int b1 = min(b0 + per, pb.num_reqs);
+    auto q_len = [&](int b) { return max(cu[b + 1] - cu[b], 0); };
+    int local = 0;
+    for (int b = b0; b < b1; ++b) local += (q_len(b) + pb.block_tokens - 1) / pb.block_tokens;
+    const int incl = wave_incl_scan(local, lane);
+    if (lane == 63) scan_carry[wave] = incl;
+    __syncthreads();
+    int j = incl - local;
+    for (int w = 0; w < wave; ++w) j += scan_carry[w];
+    if (tid == kPlanThreads - 1) s_total = j + local;
+    for (int b = b0; b < b1; ++b) {
+        const int L = q_len(b);
+        const int S = max(pb.ctx[b], 0);
+        const int row = cu[b];
+        for (int i0 = 0; i0 < L && j < max_blocks; i0 += pb.block_tokens, ++j) {
+            const int i1 = min(L, i0 + pb.block_tokens);
+            const int ctx = max(S - (L - i1), 0);
+            pb.blk_cu[j] = row + i0;
+            pb.blk_ctx[j] = ctx;
+            pb.blk_req[j] = b;
+            s_len[j] = ctx;
+            s_qlen[j] = i1 - i0;
+        }
+    }
+    __syncthreads();
+    const int end = cu[pb.num_reqs];
+    for (int e = max(s_total, 0) + tid; e < max_blocks; e += kPlanThreads) {
+        pb.blk_cu[e] = end;
+        pb.blk_ctx[e] = 0;
+        pb.blk_req[e] = 0;
+        s_len[e] = 0;
+        s_qlen[e] = 0;
+    }
+    if (tid == 0) pb.blk_cu[max_blocks] = end;
+}
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ cu, int num_seqs,
     int cap_formula, int capacity, int max_partitions, int tile_tokens, int window,
     int4* __restrict__ work_info, int2* __restrict__ reduce_info, int32_t* __restrict__ num_work,
-    int4* __restrict__ dispatch_info) {
+    int4* __restrict__ dispatch_info, const PlanBlocks blocks) {
     __shared__ int32_t first[PA_MAX_SEQS + 1];
+    __shared__ int32_t s_len[PA_MAX_SEQS];        // each planned sequence's length (>= 0) ...
+    __shared__ int32_t s_qlen[PA_MAX_SEQS];       // ... and query tokens, read from memory once
     __shared__ int32_t s_tiles[kDispatchMaxSlots];
     __shared__ __align__(16) int32_t s_aux[kDispatchMaxSlots];   // a slot's key, or its rank within its request
     __shared__ int32_t s_rank[kDispatchMaxSlots];
@@ -60,9 +118,19 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     // ranks from the closed form (O(requests) per slot) when the batch is small against the slots
     const bool closed = ranked && num_seqs <= kClosedMaxSeqs && 4 * num_seqs <= capacity;
 
+    if (blocks.ctx) {
+        cut_blocks(blocks, num_seqs, s_len, s_qlen);
+    } else {
+        for (int b = tid; b < num_seqs; b += kPlanThreads) {
+            s_len[b] = max(context_lens[b], 0);
+            s_qlen[b] = plan_q_len(cu, b);
+        }
+    }
+    __syncthreads();
+
     // the key range request b reads: all of [0, S_b), or its window's union
     auto range_of = [&](int b) -> PlanRange {
-        return plan_range(max(context_lens[b], 0), window > 0 ? plan_q_len(cu, b) : 1, window, tile_tokens);
+        return plan_range(s_len[b], window > 0 ? s_qlen[b] : 1, window, tile_tokens);
     };
 
     // --- W = sum of the lengths read and B' = #{requests reading any key} ---
@@ -146,7 +214,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
             const int parts = first[b + 1] - first[b];
             const PlanRange pr = range_of(b);
             const int2 r = plan_tile_range(j, pr.tiles, parts);
-            e = make_int4(b, pr.t0 + r.x, pr.t0 + r.y, max(context_lens[b], 0));
+            e = make_int4(b, pr.t0 + r.x, pr.t0 + r.y, s_len[b]);
             tiles = r.y - r.x;
             largest = max(largest, tiles);
             if (closed) {
@@ -245,75 +313,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     }
 }
 
-// Query blocks of a prefill batch as pseudo-requests for the planner, the decode and the merge: each
-// request's query tokens [0, L_b) are cut into blocks of block_tokens, numbered request by request.
-// Block j covering tokens [i0, i1) of request b gets
-//   blk_cu[j] = cu[b] + i0                (its first row; blk_cu[max_blocks] = cu[num_seqs]),
-//   blk_ctx[j] = S_b - (L_b - i1)         (the keys its last token sees, at least 0),
-//   blk_req[j] = b                        (the request's block-table row),
-// so that token i of the block sees blk_ctx[j] - (i1 - 1 - i) = S_b - (L_b - 1 - i) keys, the
-// request's own per-token causal range (opengfx1030/vllm-rdna PR #29, Change 1).  Slots past the last
-// block are empty blocks (blk_cu = cu[num_seqs], blk_ctx = 0, blk_req = 0).  Each thread takes a
-// contiguous run of requests; a scan over the threads gives each run's first block.
-__global__ __launch_bounds__(kPlanThreads) void prefill_blocks_kernel(
-    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ cu, int num_seqs, int block_tokens,
-    int max_blocks, int32_t* __restrict__ blk_ctx, int32_t* __restrict__ blk_cu, int32_t* __restrict__ blk_req) {
-    __shared__ int scan_carry[kPlanWaves];
-    __shared__ int s_total;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int per = (num_seqs + kPlanThreads - 1) / kPlanThreads;
-    const int b0 = min(tid * per, num_seqs);
-    const int b1 = min(b0 + per, num_seqs);
-    auto q_len = [&](int b) { return max(cu[b + 1] - cu[b], 0); };
-    int local = 0;
-    for (int b = b0; b < b1; ++b) local += (q_len(b) + block_tokens - 1) / block_tokens;
-    const int incl = wave_incl_scan(local, lane);
-    if (lane == 63) scan_carry[wave] = incl;
-    __syncthreads();
-    int j = incl - local;
-    for (int w = 0; w < wave; ++w) j += scan_carry[w];
-    if (tid == kPlanThreads - 1) s_total = j + local;
-    for (int b = b0; b < b1; ++b) {
-        const int L = q_len(b);
-        const int S = max(context_lens[b], 0);
-        const int row = cu[b];
-        for (int i0 = 0; i0 < L && j < max_blocks; i0 += block_tokens, ++j) {
-            const int i1 = min(L, i0 + block_tokens);
-            blk_cu[j] = row + i0;
-            blk_ctx[j] = max(S - (L - i1), 0);
-            blk_req[j] = b;
-        }
-    }
-    __syncthreads();
-    const int end = cu[num_seqs];
-    for (int e = max(s_total, 0) + tid; e < max_blocks; e += kPlanThreads) {
-        blk_cu[e] = end;
-        blk_ctx[e] = 0;
-        blk_req[e] = 0;
-    }
-    if (tid == 0) blk_cu[max_blocks] = end;
-}
-
 }  // namespace
-
-hipError_t launch_prefill_blocks(const int32_t* context_lens, const int32_t* cu, int num_seqs, int block_tokens,
-                                 int max_blocks, int32_t* blk_ctx, int32_t* blk_cu, int32_t* blk_req,
-                                 hipStream_t stream) {
-    hipLaunchKernelGGL(prefill_blocks_kernel, dim3(1), dim3(kPlanThreads), 0, stream, context_lens, cu, num_seqs,
-                       block_tokens, max_blocks, blk_ctx, blk_cu, blk_req);
-    return hipGetLastError();
-}
 
 hipError_t launch_plan(const int32_t* context_lens, const int32_t* cu, int num_seqs, int cap_formula,
                        int capacity, int max_partitions, int tile_tokens, int window,
                        int32_t* work_info, int32_t* reduce_info, int32_t* num_work, int32_t* dispatch_info,
-                       hipStream_t stream) {
+                       hipStream_t stream, const PlanBlocks* blocks) {
+    const PlanBlocks pb = blocks ? *blocks : PlanBlocks{};
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, context_lens, cu, num_seqs,
                        cap_formula, capacity, max_partitions, tile_tokens, window,
                        reinterpret_cast<int4*>(work_info), reinterpret_cast<int2*>(reduce_info),
-                       num_work, reinterpret_cast<int4*>(dispatch_info));
+                       num_work, reinterpret_cast<int4*>(dispatch_info), pb);
     return hipGetLastError();
 }
 
