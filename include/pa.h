@@ -294,8 +294,8 @@ pa_status pa_attention_noalloc(const void* q, pa_dtype q_dtype, int32_t num_rows
  *                    its keys) is then one workgroup whose eight waves share every 32-key K/V chunk
  *                    through LDS, each wave holding 16 or 32 of the block's query rows; the slots'
  *                    states are merged into the rows.  A block behind a long prefix reads its keys with
- *                    several workgroups, and each K/V byte is read once per block of T tokens.  Four
- *                    launches: the blocks, their plan, the block kernel, the merge.
+ *                    several workgroups, and each K/V byte is read once per block of T tokens.  Three
+ *                    launches: the blocks and their plan, the block kernel, the merge.
  *                    The workspace holds pa_prefill_workspace_bytes(num_rows, num_seqs, num_q_heads,
  *                    num_kv_heads, head_dim, cu_count) bytes, 256-byte aligned, owned by the caller, with
  *                    no initial contents needed; cu_count is the compute-unit count the budget is built
