@@ -105,6 +105,7 @@ LONG_PREFIX = [
     # pages of 64 and 128 tokens on the direct-load path (both halves of a 32-key chunk in one page)
     ("d256_bs64_bf16", [2500, 900], [120, 60], 12, 2, 256, 64, "bf16", "bf16", 1, 0, 256),
     ("d128_bs128_bf16_window", [3000, 1000], [200, 33], 16, 2, 128, 128, "bf16", "bf16", 0, 300, 64),
+    ("d256_bs128_bf16_qf32", [2100, 700], [90, 40], 12, 2, 256, 128, "bf16", "f32", 0, 0, 16),
 ]
 
 
