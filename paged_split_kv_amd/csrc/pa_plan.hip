@@ -7,10 +7,12 @@
 // logic: under a sliding window the plan covers the range the kernel reads).  The rounding of the
 // shares is this library's reading, documented in pa.h.
 //
-// One workgroup of 1024 threads does the whole plan: a reduction for the total length and the number
-// of non-empty requests, the per-request counts, an exclusive scan into LDS, and then one thread per
-// slot fills work_info by binary-searching the scanned offsets.  Integer-only, 64-bit where
-// products can exceed 32 bits, so the result is bit-identical to any other exact evaluation.
+// One workgroup of 1024 threads does the whole plan: the planned sequences' lengths are read once into
+// LDS, then a reduction for the total length and the number of non-empty requests, the per-request
+// counts, an exclusive scan into LDS, and one thread per slot fills work_info by binary-searching the
+// scanned offsets.  Integer-only, 64-bit where products can exceed 32 bits, so the result is
+// bit-identical to any other exact evaluation.  For the split prefill the same launch first cuts the
+// prompt requests into query blocks (cut_blocks) and plans the blocks.
 //
 // Optionally the same launch writes a dispatch order for the decode (this library's scheduling, not
 // part of the pages' plan): the slots ranked by tile count (largest first, ties by slot index, unused
