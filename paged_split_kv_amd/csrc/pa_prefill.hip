@@ -468,8 +468,9 @@ __global__ __launch_bounds__(512, 2) void prefill_tile_kernel(const DecodeArgs a
         int np = spage(C::NBUF - 1);
         constexpr int kWaitChunk = (C::NBUF - 2) * C::NLD;     // loads younger than chunk k's
         static_assert(kWaitChunk < 64, "vmcnt field");
-        // unrolled NBUF times, so each buffer is a constant: the LDS reads then take their buffer in the
-        // instructions' offset field (K tiles in the first 64 KB, V tiles after them)
+        // unrolled NBUF times, so each buffer is a constant: the K reads then take their buffer in the
+        // instructions' 16-bit offset field (K tiles in the first 64 KB); the V tiles lie past its
+        // reach, so their reads keep an address per buffer
         for (int k0 = 0; k0 < nchunks; k0 += C::NBUF) {
 #pragma unroll
             for (int par = 0; par < C::NBUF; ++par) {
