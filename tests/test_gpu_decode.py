@@ -54,6 +54,9 @@ SMALL = [
     ("fp8_d256_40rows", [900, 3000, 1], [5, 2, 1], 8, 1, 256, 64, "fp8", "bf16", 0, 256, 128),
     ("qf32_d256_tiny_tiles", [17, 1, 300, 4097], None, 6, 1, 256, 16, "bf16", "f32", 0, 4, 16),
     ("bf16_d256_short_last_tile", [257, 513], [3, 2], 6, 2, 256, 16, "bf16", "bf16", 0, 1, 256),
+    # 128-token pages with an fp32 cache; 64-token pages with fp8 at head_dim 128 and verify rows
+    ("f32_d128_bs128", [3000, 129, 128], None, 4, 1, 128, 128, "f32", "f32", 1, 256, 256),
+    ("fp8_d128_bs64_verify", [2000, 65, 700], [2, 1, 3], 16, 2, 128, 64, "fp8", "bf16", 1, 256, 128),
 ]
 
 
