@@ -20,7 +20,8 @@ of it; pa_plan alone (the per-forward refresh); the one-call pa_attention (plan 
 launches) and the three-call form; per-kernel times with events around each launch; each step once
 with the 256 MB last-level cache evicted before it; the decode kernel alone back to back (roofline);
 the read-only ceilings of the same device (pa_probe_read: a contiguous read; pa_probe_gather: exactly
-the decode's K/V bytes over the same plans, with the decode's launch shape, no arithmetic); and the
+the decode's K/V bytes over the same plans, with the decode's launch shape and dispatch order, no
+arithmetic; also timed in slot order); and the
 CPU oracle on a bounded sample plus one timing per named configuration (cpu_baseline).
 
 The roofline object is for the decode kernel: algorithmic bytes per launch (context length x Hkv x 2 x
@@ -637,12 +638,17 @@ def main():
     dec = rate(kv_bytes, order, dec_ms)
     dec_s = [dec_call(i, dispatch=False) for i in range(nsteps)]
     dec_slot_ms = timed([lambda i=i: dec_s[i]() for i in order], stream, [lambda: dec_s[0]()] * 8)
-    # the decode-shaped gather over the same plans and order: the same K/V bytes, no arithmetic
+    # the decode-shaped gather over the same plans and steps, its workgroups taking the slots in the
+    # decode's dispatch order (the entries carry the slot's request and tile range first): the same
+    # K/V bytes, no arithmetic; and the same gather in slot order
     sink = P.sink_for(4 * step.capacity * Hkv, dev)
-    gat_p = [P.pa_probe_gather(c.k_cache, c.v_cache, c.kv_dtype, c.block_tables, c.context_lens, w, n, sink,
-                               tile_tokens=T, prepare=True) for c, (w, r, n) in zip(batches, plans)]
+    gat_p = [P.pa_probe_gather(c.k_cache, c.v_cache, c.kv_dtype, c.block_tables, c.context_lens, d, n, sink,
+                               tile_tokens=T, prepare=True) for c, (w, r, n), d in zip(batches, plans, disps)]
     gat_ms = timed([lambda i=i: gat_p[i]() for i in order], stream, [lambda: gat_p[0]()] * 8)
     gat = rate(kv_bytes, order, gat_ms)
+    gat_s = [P.pa_probe_gather(c.k_cache, c.v_cache, c.kv_dtype, c.block_tables, c.context_lens, w, n, sink,
+                               tile_tokens=T, prepare=True) for c, (w, r, n) in zip(batches, plans)]
+    gat_slot_ms = timed([lambda i=i: gat_s[i]() for i in order], stream, [lambda: gat_s[0]()] * 8)
     # the headline step over four whole passes of the set
     full = rate(kv_bytes, full_order, timed([lambda i=i: headline(i) for i in full_order], stream))
     # the plan alone (its per-forward refresh), the one-call and three-call forms, same order
@@ -747,6 +753,7 @@ def main():
         "kernel_us": {"pa_decode_back_to_back": round(dec["us_per_step"], 2),
                       "pa_decode_in_slot_order": round(dec_slot_ms * 1e3 / K, 2),
                       "decode_shaped_gather_back_to_back": round(gat["us_per_step"], 2),
+                      "decode_shaped_gather_in_slot_order": round(gat_slot_ms * 1e3 / K, 2),
                       "evented": {"pa_decode": round(float(ev_dec.mean()), 2),
                                   "pa_merge": round(float(ev_mrg.mean()), 2),
                                   "step_p50": round(float(np.median(ev_dec + ev_mrg)), 2),
@@ -763,7 +770,8 @@ def main():
                      "decode_shaped_gather": {"gbps": round(gat["gbps"], 1), "pct_peak": round(gat["pct_peak"], 1),
                                               "us_per_launch": round(gat["us_per_step"], 2),
                                               "kernel": "pa_probe_gather: the decode's K/V bytes over the same "
-                                                        "plans and step order, its launch shape, no arithmetic"},
+                                                        "plans and step order, its launch shape and dispatch "
+                                                        "order, no arithmetic"},
                      "decode_pct_of_gather": round(100.0 * dec["gbps"] / gat["gbps"], 1),
                      "decode_pct_of_read": round(100.0 * dec["gbps"] / rc["gbps"], 1),
                      "step_pct_of_read": round(100.0 * head["gbps"] / rc["gbps"], 1)},

@@ -44,8 +44,11 @@ pa_status pa_probe_read(const void* src, size_t bytes, int32_t workgroups, uint3
 /*
  * Read the K/V bytes of a plan as described above.  Arguments mean what they mean for pa_decode
  * (include/pa.h): caches [num_blocks, num_kv_heads, block_size, head_dim] of kv_dtype,
- * block_tables [num_seqs, max_blocks_per_seq], context_lens [num_seqs], work_info [capacity, 4] and
- * num_work [2] from pa_plan.  Only the rows below S_b are read; slots past num_work[0] read nothing.
+ * block_tables [num_seqs, max_blocks_per_seq], context_lens [num_seqs], work_info [capacity, 4] from
+ * pa_plan -- or the decode's dispatch order (pa_plan's dispatch_info), whose entries also start with
+ * the request and the tile range, so workgroups take the slots in that order -- and num_work [2] from
+ * pa_plan (checked, not read).  Only the rows below S_b are read; an entry naming no request (the
+ * plan's sentinel for an unused slot) reads nothing.
  *   sink        device uint32 [4 x capacity x num_kv_heads], 4-byte aligned
  * Errors: PA_INVALID_ARG (null pointers, sizes < 1, misalignment, unknown kv_dtype),
  * PA_UNSUPPORTED (head_dim not 64/128/256, block_size not 16/64/128, tile_tokens not a multiple of

@@ -68,7 +68,6 @@ struct GatherArgs {
     const int32_t* block_tables;
     const int32_t* context_lens;
     const int4* work_info;
-    const int32_t* num_work;
     uint32_t* sink;
     int num_blocks, num_kv_heads, block_size, max_blocks, num_seqs, tile_tokens, row_bytes;
 };
@@ -82,10 +81,11 @@ __global__ __launch_bounds__(256) void probe_gather_kernel(const GatherArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int slot = blockIdx.x / a.num_kv_heads;
     const int g = blockIdx.x - slot * a.num_kv_heads;
+    // an unused slot's entry names no request (the plan's sentinel), in slot order and in the decode's
+    // dispatch order alike, where unused slots do not sit at the end
     const int4 w = a.work_info[slot];
-    const int used = *a.num_work;
     const int b = __builtin_amdgcn_readfirstlane(w.x);
-    if (slot >= used || b < 0 || b >= a.num_seqs) return;
+    if (b < 0 || b >= a.num_seqs) return;
     const int S = __builtin_amdgcn_readfirstlane(max(a.context_lens[b], 0));
     const long long reach = static_cast<long long>(a.max_blocks) * a.block_size;
     long long lo = static_cast<long long>(max(w.y, 0)) * a.tile_tokens;
@@ -195,7 +195,6 @@ pa_status pa_probe_gather(const void* k_cache, const void* v_cache, pa_dtype kv_
     a.block_tables = block_tables;
     a.context_lens = context_lens;
     a.work_info = reinterpret_cast<const int4*>(work_info);
-    a.num_work = num_work;
     a.sink = sink;
     a.num_blocks = num_blocks;
     a.num_kv_heads = num_kv_heads;
