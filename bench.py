@@ -276,42 +276,70 @@ def cpu_baseline_case(case, budget_s: float, kv_bytes: float) -> dict:
 def bench_mixed(args, batches, cu_count):
     """The decode-first split of a mixed batch: one pa_attention_mixed call per step (decode and
     prompt in one launch, then the merge); the two-call form (pa_prefill, then pa_attention), the
-    same on two streams, and the parts alone are timed beside it."""
+    same on two streams, and the parts alone are timed beside it.  Every timed call is marshalled
+    beforehand (prepare=True), so the loops measure the device, not the host's argument checks."""
     from paged_split_kv_amd import binding as B
     from paged_split_kv_amd.runner import MixedStep, PlanConfig
 
     stream = torch.cuda.current_stream()
-    steps = [MixedStep(c, 1, PlanConfig(cu_count=cu_count), concurrent=True) for c in batches]
-    m_side = [m.side for m in steps]
-    for m in steps:
-        m.side = None
+    side = torch.cuda.Stream(device=stream.device)         # default priority
+    steps = [MixedStep(c, 1, PlanConfig(cu_count=cu_count)) for c in batches]
+    one, dec, pre, pre_side, pre_split = [], [], [], [], []
+    c0 = batches[0]
+    ws_pre = torch.empty((B.pa_prefill_workspace_bytes(c0.num_rows, c0.num_seqs, c0.num_q_heads, c0.num_kv_heads,
+                                                       c0.head_dim, cu_count),), dtype=torch.uint8,
+                         device=stream.device)
+    for c, m in zip(batches, steps):
+        if m.dec is None:
+            raise ValueError("the mixed workload has decode requests")
+        d, p = m.dec, m.dec.plan_cfg
+        one.append(B.pa_attention_mixed(
+            c.q, c.k_cache, c.v_cache, c.kv_dtype, c.block_tables, c.context_lens, c.cu_query_lens, m.nd, m.ndt,
+            d.work_info, d.reduce_info, d.num_work, d.workspace, m.out, scale=c.scale, cu_count=p.cu_count,
+            budget_mult=p.budget_mult, max_partitions=p.max_partitions, tile_tokens=p.tile_tokens,
+            max_q_len=m.threshold, k_scale=c.k_scale, v_scale=c.v_scale, sliding_window=c.window, stream=stream,
+            prepare=True))
+        dec.append(B.pa_attention(
+            c.q[:m.ndt], c.k_cache, c.v_cache, c.kv_dtype, c.block_tables[:m.nd], c.context_lens[:m.nd],
+            d.work_info, d.reduce_info, d.num_work, d.workspace, d.out, scale=c.scale, cu_count=p.cu_count,
+            budget_mult=p.budget_mult, max_partitions=p.max_partitions, tile_tokens=p.tile_tokens,
+            cu_query_lens=c.cu_query_lens[:m.nd + 1], max_q_len=d.max_q_len, k_scale=c.k_scale,
+            v_scale=c.v_scale, sliding_window=c.window, stream=stream, prepare=True))
+        for s_, lst in ((stream, pre), (side, pre_side)):
+            lst.append(B.pa_prefill(c.q, c.k_cache, c.v_cache, c.kv_dtype, c.block_tables[m.nd:],
+                                    c.context_lens[m.nd:], c.cu_query_lens[m.nd:], m.out, scale=c.scale,
+                                    k_scale=c.k_scale, v_scale=c.v_scale, sliding_window=c.window, stream=s_,
+                                    prepare=True))
+        # the prompt alone in the split form (query blocks planned over a workspace)
+        pre_split.append(B.pa_prefill(c.q, c.k_cache, c.v_cache, c.kv_dtype, c.block_tables[m.nd:],
+                                      c.context_lens[m.nd:], c.cu_query_lens[m.nd:], m.out, ws_pre, scale=c.scale,
+                                      cu_count=cu_count, k_scale=c.k_scale, v_scale=c.v_scale,
+                                      sliding_window=c.window, stream=stream, prepare=True))
     n = len(batches)
     K = args.steps
     order = np.arange(K) % n
 
     def part(i, which):
-        c, m = batches[i], steps[i]
         if which == "step":
-            m.one_call = True
-            m.run(c, stream)
-            m.one_call = False
+            one[i]()
         elif which == "two_calls":
-            m.run(c, stream)
+            pre[i]()
+            dec[i]()
         elif which == "two_streams":
-            m.side = m_side[i]
-            m.run(c, stream)
-            m.side = None
-        elif which == "decode" and m.dec is not None:
-            m.dec.attention(c.q[:m.ndt], c.k_cache, c.v_cache, c.kv_dtype, c.block_tables[:m.nd],
-                            c.context_lens[:m.nd], scale=c.scale, cu_query_lens=c.cu_query_lens[:m.nd + 1],
-                            sliding_window=c.window)
+            side.wait_stream(stream)
+            pre_side[i]()
+            dec[i]()
+            stream.wait_stream(side)
+        elif which == "decode":
+            dec[i]()
         elif which == "prefill":
-            B.pa_prefill(c.q, c.k_cache, c.v_cache, c.kv_dtype, c.block_tables[m.nd:], c.context_lens[m.nd:],
-                         c.cu_query_lens[m.nd:], m.out, scale=c.scale, sliding_window=c.window)
+            pre[i]()
+        elif which == "prefill_split":
+            pre_split[i]()
 
     def run(which, warm):
         return timed([lambda i=i: part(i, which) for i in order], stream,
-                     [lambda i=i: part(i % n, which) for i in range(warm)])
+                      [lambda i=i: part(i % n, which) for i in range(warm)])
 
     step_ms = run("step", args.warmup)
     c0, m0 = batches[0], steps[0]
@@ -330,6 +358,7 @@ def bench_mixed(args, batches, cu_count):
     two_ms = run("two_streams", 8)
     dec_ms = run("decode", 8)
     pre_ms = run("prefill", 8)
+    pre_split_ms = run("prefill_split", 8)
     dec_bytes = np.full(n, float(lens[:m0.nd].sum() * per_key))
     head = rate(all_bytes, order, step_ms)
     dec = rate(dec_bytes, order, dec_ms)
@@ -346,6 +375,7 @@ def bench_mixed(args, batches, cu_count):
         "step": "pa_split_decode_first on the host; pa_attention_mixed: the decodes (planned in place) and "
                 "the prompt's query blocks in one launch, then pa_merge",
         "decode_part_us": round(dec["us_per_step"], 2), "prefill_part_us": round(pre_ms * 1e3 / K, 2),
+        "prefill_part_split_form_us": round(pre_split_ms * 1e3 / K, 2),
         "two_calls_us_per_step": round(two_calls_ms * 1e3 / K, 2),
         "two_streams_us_per_step": round(two_ms * 1e3 / K, 2),
         "roofline": {"bound": "hbm", "achieved": round(dec["gbps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -391,9 +391,10 @@ def pa_attention_mixed(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
                        out: torch.Tensor, *, scale: float, cu_count: int, budget_mult: int = 2,
                        max_partitions: int = 256, tile_tokens: int = 256, max_q_len: int = 1,
                        k_scale: float = 1.0, v_scale: float = 1.0, sliding_window: int = 0,
-                       stream=None) -> None:
+                       stream=None, prepare: bool = False):
     """A decodes-first mixed batch in one call (see include/pa.h): the plan buffers are sized for the
-    num_decodes decode requests; out receives every row."""
+    num_decodes decode requests; out receives every row.  With prepare=True nothing is launched and a
+    Prepared call is returned."""
     dev = q.device
     if q.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("q must be float32 or bfloat16")
@@ -422,14 +423,13 @@ def pa_attention_mixed(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
     if reduce_info.numel() < 2 * num_decodes or num_work.numel() < 2:
         raise ValueError("plan buffers smaller than num_decodes / 2")
     qd = PA_F32 if q.dtype == torch.float32 else PA_BF16
-    _check(load().pa_attention_mixed(_ptr(q), qd, R, Hq, D, _ptr(k_cache), _ptr(v_cache),
-                                     _DTYPE_OF_NAME[kv_dtype], nb, Hkv, bs, _ptr(block_tables),
-                                     int(block_tables.shape[1]), _ptr(context_lens), B, _ptr(cu_query_lens),
-                                     num_decodes, num_decode_rows, max_q_len, sliding_window, scale, k_scale,
-                                     v_scale, cu_count, budget_mult, max_partitions, tile_tokens,
-                                     int(work_info.shape[0]), _ptr(work_info), _ptr(reduce_info),
-                                     _ptr(num_work), _ptr(workspace), workspace.numel(), _ptr(out), qd,
-                                     _stream(stream)), "pa_attention_mixed")
+    args = (_ptr(q), qd, R, Hq, D, _ptr(k_cache), _ptr(v_cache), _DTYPE_OF_NAME[kv_dtype], nb, Hkv, bs,
+            _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), B, _ptr(cu_query_lens),
+            num_decodes, num_decode_rows, max_q_len, sliding_window, scale, k_scale, v_scale, cu_count,
+            budget_mult, max_partitions, tile_tokens, int(work_info.shape[0]), _ptr(work_info),
+            _ptr(reduce_info), _ptr(num_work), _ptr(workspace), workspace.numel(), _ptr(out), qd,
+            _stream(stream))
+    return _issue(load().pa_attention_mixed, args, "pa_attention_mixed", prepare)
 
 
 def pa_prefill_workspace_bytes(num_rows: int, num_seqs: int, num_q_heads: int, num_kv_heads: int,
