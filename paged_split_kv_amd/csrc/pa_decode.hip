@@ -10,9 +10,11 @@
 //  * one workgroup of NW waves (4; 8 when every request is one slot) per (slot, kv head).  The
 //    slot's keys are cut into 16-key chunks (a chunk never straddles a page: pages hold 16, 64 or
 //    128 tokens and slots start on tile boundaries); wave w takes units w, w+NW, ... of consecutive
-//    chunks, the unit being the plan's largest slot split NW ways (each slot split evenly in the
-//    8-wave form), so every streaming wave carries one unit and a small slot runs fewer waves,
-//    leaving bandwidth to the large ones; the NW states merge in LDS at the end.
+//    chunks.  When the plan's largest slot gives each of its waves at least kEvenDealChunks chunks
+//    (launches long enough to be bound by bandwidth), and in the 8-wave form, the unit is the slot
+//    itself split NW ways, so every slot streams on all its waves from the start; otherwise it is the
+//    largest slot split NW ways, so a small slot runs fewer, fully loaded waves and its loads do not
+//    delay the largest slot's in a latency-bound launch.  The NW states merge in LDS at the end.
 //  * when every request is one slot, pa_attention's in-place plan can also cut the slots into pieces
 //    of about half the mean slot, one workgroup each (shared slots, see piece_size): the states are
 //    then per piece, the merge folds a request's pieces, and the unit is the piece-size bound split
@@ -603,13 +605,19 @@ __global__ __launch_bounds__((64 * NWAVES), (Mfma<D, NCB, KV8, NWAVES>::WAVES)) 
     const int plan_chunks = (plan_hi - plan_lo + 15) >> 4;
 
     // Chunks are dealt to waves in units of `unit` consecutive chunks: wave w owns units w, w + NW, ...
-    // of the slot and its k-th chunk is chunk_of(k).  The unit is the largest slot of the plan split
-    // over the NW waves, so that slot's waves and every other wave with a full unit carry the same
-    // load and finish together, while a smaller slot runs fewer streaming waves and leaves more of the
-    // bandwidth to the big ones.  Any unit >= 1 covers every chunk of every slot exactly once.
-    // (A prefill block is its own slot: its chunks are split evenly over the waves.)
+    // of the slot and its k-th chunk is chunk_of(k).  Even dealing: the unit is this slot split over
+    // the NW waves, so every slot streams on all its waves from the start, which keeps the most loads
+    // in flight while the launch is bound by bandwidth.  Unit dealing: the unit is the plan's largest
+    // slot split over the NW waves, so that slot's waves and every other wave with a full unit carry
+    // the same load and finish together, while a smaller slot runs fewer streaming waves; in a short,
+    // latency-bound launch this keeps the small slots' loads from delaying the largest slot's.  The
+    // choice is uniform over the launch (from the plan's largest slot).  Any unit >= 1 covers every
+    // chunk of every slot exactly once.  (A prefill block is its own slot: its chunks are split
+    // evenly over the waves.)
     const int cpt = a.tile_tokens >> 4;          // 16-key chunks per tile
-    const long long unit_chunks = (a.prefill || C::EVEN) ? plan_chunks : static_cast<long long>(max(nwk.y, 1)) * cpt;
+    const long long largest_chunks = static_cast<long long>(max(nwk.y, 1)) * cpt;
+    const bool even = a.prefill || C::EVEN || largest_chunks >= static_cast<long long>(C::NW) * kEvenDealChunks;
+    const long long unit_chunks = even ? plan_chunks : largest_chunks;
     const int unit = static_cast<int>(min(max(1LL, (unit_chunks + C::NW - 1) / C::NW), 1LL << 30));
     // Every slot of the plan (and every prefill block) spans at most NW units, so a wave's live
     // chunks are all in its first unit: k < unit takes no division.  Past that (only the empty

@@ -331,6 +331,10 @@ constexpr int kInlinePlanSeqs = PA_INLINE_PLAN_SEQS;
 constexpr int kPieceFactor = 2;
 inline int piece_bound(int capacity) { return (kPieceFactor + 1) * capacity; }
 
+// The decode deals each slot's chunks evenly over its waves when the plan's largest slot gives every
+// wave at least this many 16-key chunks, and in units of the largest slot otherwise.
+constexpr int kEvenDealChunks = 12;
+
 // The shared-slot region, after the slot states: the piece states' acc and (m, l) for
 // piece_bound(capacity) pieces, then the per-request (first piece, pieces) pairs for up to
 // kInlinePlanSeqs requests.  Byte offsets from the workspace's start.
