@@ -17,8 +17,8 @@
 //    delay the largest slot's in a latency-bound launch.  The NW states merge in LDS at the end.
 //  * when every request is one slot, pa_attention's in-place plan can also cut the slots into pieces
 //    of about half the mean slot, one workgroup each (shared slots, see piece_size): the states are
-//    then per piece, the merge folds a request's pieces, and the unit is the piece-size bound split
-//    four ways.
+//    then per piece, the merge folds a request's pieces, and the piece-size bound stands for the
+//    largest slot in the choice of dealing.
 //  * all query rows of the group -- G heads x L verify tokens, M = G*L <= 64 -- form the columns
 //    of 16-wide MFMA blocks, so each K/V byte is read from HBM once per (slot, kv head) whatever L is.
 //  * each chunk's K and V (16 x D each) are fetched PF chunks ahead into registers with 16-byte
