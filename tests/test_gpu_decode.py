@@ -138,6 +138,38 @@ def test_one_slot_per_request(spec, mode):
     assert (got[z] == 0.0).all()
 
 
+# The decode deals a slot's chunks evenly over its waves when the plan's largest slot holds at least
+# 48 16-key chunks (12 per wave), and in units of the largest slot below that.  With at most two
+# partitions per request (P = 2) the longest request's halves are the largest slots: 48 chunks at the
+# boundary, 47 or 32 just below it; short requests leave some waves without chunks under either rule.
+DEALING = [
+    # (name, ctx, q_lens, kv, P, T)
+    ("even_at_48_chunks_t16", [1536, 300, 17, 0, 5], None, "bf16", 2, 16),
+    ("unit_at_47_chunks_t16", [1504, 300, 17, 0, 5], None, "bf16", 2, 16),
+    ("even_at_3_tiles_verify", [1480, 1025, 2, 255], [3, 1, 2, 1], "bf16", 2, 256),
+    ("unit_at_2_tiles_verify", [1024, 600, 2, 255], [3, 1, 2, 1], "bf16", 2, 256),
+    ("even_fp8_at_4_tiles", [1537, 64, 1], None, "fp8", 2, 256),
+    ("unit_fp8_at_2_tiles", [1000, 64, 1], None, "fp8", 2, 256),
+]
+
+
+@pytest.mark.parametrize("spec", DEALING, ids=[s[0] for s in DEALING])
+def test_dealing_rule_boundaries(spec):
+    name, ctx, ql, kv, P, T = spec
+    case = W.build_case(name, ctx, num_q_heads=16, num_kv_heads=2, head_dim=128, block_size=16,
+                        kv_dtype=kv, q_dtype="bf16", seed=41, q_lens=ql, device=DEV)
+    announce(f"dealing {name}")
+    out, step = _run(case, P, T, cu_count=256)
+    assert step.capacity > case.num_seqs          # several slots per request: no shared slots
+    largest = int(step.num_work[1].item())
+    chunks = largest * (T // 16)
+    assert (chunks >= 48) == name.startswith("even"), (largest, chunks)
+    got = to_f64(out)
+    assert_close(got, oracle_direct(case), tolerance_kind(case), name)
+    z = _zero_rows(case)
+    assert (got[z] == 0.0).all()
+
+
 @pytest.mark.parametrize("name", ["tiny_fp32", "long_bf16", "verify_bf16", "fp8_kv"])
 def test_full_size_workloads(name):
     announce(f"full {name}")
