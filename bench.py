@@ -70,6 +70,22 @@ def step_order(K: int, nsteps: int, seed: int = 0) -> np.ndarray:
     return np.concatenate(parts).astype(np.int64) if parts else np.zeros(0, np.int64)
 
 
+def shared_slot_pieces(work_info: np.ndarray, used: int, factor: int = 2):
+    """The pieces the decode streams when every request is one slot (shared slots): each slot of n
+    tiles in X = max(1, ceil(n / per)) pieces, per = max(1, ceil((tiles + used) / (factor * used))),
+    piece k covering the slot's tiles [floor(k n / X), floor((k + 1) n / X)); pieces in slot order.
+    Returns the pieces as plan entries (request, tile_begin, tile_end, 0) and the bound per."""
+    w = np.asarray(work_info).reshape(-1, 4)[:used]
+    n = np.maximum(w[:, 2] - w[:, 1], 0).astype(np.int64)
+    per = max(1, -(-(int(n.sum()) + used) // (factor * max(used, 1))))
+    out = []
+    for (b, t0, _, _), ns in zip(w, n):
+        X = max(1, -(-int(ns) // per))
+        for k in range(X):
+            out.append((int(b), int(t0) + (k * int(ns)) // X, int(t0) + ((k + 1) * int(ns)) // X, 0))
+    return np.asarray(out, dtype=np.int32).reshape(-1, 4), per
+
+
 def rate(bytes_per_step: np.ndarray, order: np.ndarray, total_ms: float) -> dict:
     """Throughput of a timed run over `order`: bytes of exactly those steps over the total time."""
     K = len(order)
@@ -679,6 +695,20 @@ def main():
     gat_s = [P.pa_probe_gather(c.k_cache, c.v_cache, c.kv_dtype, c.block_tables, c.context_lens, w, n, sink,
                                tile_tokens=T, prepare=True) for c, (w, r, n) in zip(batches, plans)]
     gat_slot_ms = timed([lambda i=i: gat_s[i]() for i in order], stream, [lambda: gat_s[0]()] * 8)
+    # where the decode shares the slots (every request one slot), the same gather over its pieces
+    gat_pc = None
+    if 0 < step.capacity <= B_ <= 256 and D <= 128:
+        pcs = []
+        for (w, r, n) in plans:
+            used = int(n[0].item())
+            ent, per = shared_slot_pieces(w.cpu().numpy(), used)
+            pcs.append((torch.as_tensor(ent, device=dev),
+                        torch.tensor([ent.shape[0], per], dtype=torch.int32, device=dev)))
+        sink_pc = P.sink_for(4 * max(e.shape[0] for e, _ in pcs) * Hkv, dev)
+        gat_pp = [P.pa_probe_gather(c.k_cache, c.v_cache, c.kv_dtype, c.block_tables, c.context_lens, e, nw, sink_pc,
+                                    tile_tokens=T, prepare=True) for c, (e, nw) in zip(batches, pcs)]
+        gat_pc = rate(kv_bytes, order, timed([lambda i=i: gat_pp[i]() for i in order], stream,
+                                             [lambda: gat_pp[0]()] * 8))
     # the headline step over four whole passes of the set
     full = rate(kv_bytes, full_order, timed([lambda i=i: headline(i) for i in full_order], stream))
     # the plan alone (its per-forward refresh), the one-call and three-call forms, same order
@@ -784,6 +814,8 @@ def main():
                       "pa_decode_in_slot_order": round(dec_slot_ms * 1e3 / K, 2),
                       "decode_shaped_gather_back_to_back": round(gat["us_per_step"], 2),
                       "decode_shaped_gather_in_slot_order": round(gat_slot_ms * 1e3 / K, 2),
+                      "decode_shaped_gather_over_shared_slot_pieces":
+                          None if gat_pc is None else round(gat_pc["us_per_step"], 2),
                       "evented": {"pa_decode": round(float(ev_dec.mean()), 2),
                                   "pa_merge": round(float(ev_mrg.mean()), 2),
                                   "step_p50": round(float(np.median(ev_dec + ev_mrg)), 2),
@@ -802,7 +834,12 @@ def main():
                                               "kernel": "pa_probe_gather: the decode's K/V bytes over the same "
                                                         "plans and step order, its launch shape and dispatch "
                                                         "order, no arithmetic"},
-                     "decode_pct_of_gather": round(100.0 * dec["gbps"] / gat["gbps"], 1),
+                     "decode_shaped_gather_over_shared_slot_pieces": None if gat_pc is None else {
+                         "gbps": round(gat_pc["gbps"], 1), "pct_peak": round(gat_pc["pct_peak"], 1),
+                         "us_per_launch": round(gat_pc["us_per_step"], 2),
+                         "kernel": "pa_probe_gather over the pieces the decode streams when every request is "
+                                   "one slot (shared slots), in piece order, no arithmetic"},
+                     "decode_pct_of_gather": round(100.0 * dec["gbps"] / (gat if gat_pc is None else gat_pc)["gbps"], 1),
                      "decode_pct_of_read": round(100.0 * dec["gbps"] / rc["gbps"], 1),
                      "step_pct_of_read": round(100.0 * head["gbps"] / rc["gbps"], 1)},
         "hip_graph": graph,

@@ -105,3 +105,31 @@ def test_attention_flops_counts_each_visible_pair():
                     keys = range(max(n - W, 0) if W else 0, n)
                     pairs += len(keys)
             assert bench.attention_flops(S, cu, hq, d, W) == 4.0 * d * hq * pairs
+
+
+def test_shared_slot_pieces_cover_each_slot_once():
+    """The piece-shaped gather reads what the decode streams under shared slots: every slot's tiles
+    exactly once, in slot order, in at most (factor + 1) x used pieces of at most `per` tiles."""
+    import numpy as np
+    bench = _bench_module()
+    rng = np.random.default_rng(7)
+    for _ in range(50):
+        used = int(rng.integers(1, 257))
+        n = rng.integers(1, 300, size=used)
+        t0 = rng.integers(0, 50, size=used)
+        w = np.zeros((used + int(rng.integers(0, 5)), 4), dtype=np.int32)
+        w[:used, 0] = np.arange(used)
+        w[:used, 1] = t0
+        w[:used, 2] = t0 + n
+        w[used:, 0] = -1
+        ent, per = bench.shared_slot_pieces(w, used)
+        assert per == max(1, -(-(int(n.sum()) + used) // (2 * used)))
+        assert len(ent) <= 3 * used
+        sizes = ent[:, 2] - ent[:, 1]
+        assert (sizes >= 0).all() and (sizes <= per).all()
+        for s in range(used):
+            mine = ent[ent[:, 0] == s]
+            # consecutive, contiguous, covering [t0, t0 + n) exactly
+            assert mine[0, 1] == t0[s] and mine[-1, 2] == t0[s] + n[s]
+            assert (mine[1:, 1] == mine[:-1, 2]).all()
+        assert (np.diff(ent[:, 0]) >= 0).all()
