@@ -15,7 +15,7 @@ from paged_split_kv_amd import binding as B
 from paged_split_kv_amd import workloads as W
 from paged_split_kv_amd.runner import DecodeStep, PlanConfig
 from _util import announce, assert_close, oracle_direct, to_f64, tolerance_kind
-from test_gpu_decode import SMALL, _partial_bytes, _small_case, _zero_rows
+from test_gpu_decode import DEALING, SMALL, _partial_bytes, _small_case, _zero_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -76,6 +76,21 @@ def test_small_cases(spec):
     g = to_f64(got)
     assert_close(g, oracle_direct(case), tolerance_kind(case), spec[0])
     assert (g[_zero_rows(case)] == 0.0).all()
+
+
+@pytest.mark.parametrize("spec", DEALING, ids=[s[0] for s in DEALING])
+def test_dealing_rule_boundaries(spec):
+    """Both sides of the decode's even/unit dealing boundary: the in-place plan's largest slot picks
+    the same dealing as the stored plan's, so the two routes agree bit for bit."""
+    name, ctx, ql, kv, P, T = spec
+    case = W.build_case(name, ctx, num_q_heads=16, num_kv_heads=2, head_dim=128, block_size=16,
+                        kv_dtype=kv, q_dtype="bf16", seed=43, q_lens=ql, device=DEV)
+    announce(f"attention dealing {name}")
+    cfg = PlanConfig(cu_count=256, max_partitions=P, tile_tokens=T)
+    got, ref, step = _both_routes(case, cfg)
+    _assert_same_as_three(got, ref, name)
+    _check_plan(step, ctx, 2, cfg)
+    assert_close(to_f64(got), oracle_direct(case), tolerance_kind(case), name)
 
 
 @pytest.mark.parametrize("name", ["verify_bf16", "fp8_kv", "long_bf16"])
