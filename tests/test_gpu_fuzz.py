@@ -1,0 +1,72 @@
+"""Randomised decode parity against the fp64 oracle, element by element.
+
+Each seed draws one small batch over the whole supported space: head_dim 64/128/256; pages of
+16/64/128 tokens and tiles that are multiples of them; bf16, fp8 (e4m3fn) and fp32 caches with bf16
+or fp32 queries; group sizes 1-8 with or without verify rows (per-token causal ranges, opengfx1030/
+vllm-rdna PR #29, Change 1) and padding rows; partition ceilings 1-256 and budgets from one slot
+per request (where the decode shares the slots) to 2 x 256 compute units (ROCm/ATOM PR #2366,
+section 1); sliding windows; and the three call forms (decode with the merge in the call, decode
+then pa_merge, pa_attention).  The cases are small enough for the oracle to finish in well under a
+second each; the tolerances are the ones every parity test uses.
+"""
+import numpy as np
+import pytest
+
+from paged_split_kv_amd import workloads as W
+from paged_split_kv_amd.runner import DecodeStep, PlanConfig
+from _util import announce, assert_close, oracle_direct, to_f64, tolerance_kind
+from test_gpu_decode import _zero_rows
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+MODES = ("merge_in_call", "separate_merge", "attention")
+
+
+def _draw(seed):
+    rng = np.random.default_rng(4200 + seed)
+    D = int(rng.choice([64, 128, 256]))
+    kv = str(rng.choice(["bf16", "bf16", "fp8", "f32"]))
+    qd = str(rng.choice(["bf16", "f32"]))
+    hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 4, 6, 8]))
+    bs = int(rng.choice([16, 64, 128]))
+    T = int(rng.choice([t for t in (16, 64, 128, 256, 512) if t % bs == 0]))
+    P = int(rng.choice([1, 2, 8, 256]))
+    cu = int(rng.choice([1, 8, 64, 256]))
+    Bn = int(rng.integers(1, 12))
+    ctx = rng.integers(1, 6000, size=Bn)
+    ctx[rng.random(Bn) < 0.2] = 0
+    ql = None
+    if rng.random() < 0.5:
+        lmax = min(4, 64 // G)
+        ql = rng.integers(1, lmax + 1, size=Bn).tolist()
+    pad = int(rng.integers(0, 3))
+    window = int(rng.choice([0, 0, 0, 1, 37, 700, 4000]))
+    return dict(D=D, kv=kv, qd=qd, hkv=hkv, G=G, bs=bs, T=T, P=P, cu=cu, ctx=ctx.tolist(), ql=ql, pad=pad,
+                window=window, mode=MODES[seed % 3])
+
+
+@pytest.mark.parametrize("seed", range(64))
+def test_decode_fuzz(seed):
+    c = _draw(seed)
+    announce(f"fuzz seed {seed}: " + " ".join(f"{k}={v}" for k, v in c.items() if k != "ctx") +
+             f" B={len(c['ctx'])}")
+    case = W.build_case(f"fuzz{seed}", c["ctx"], num_q_heads=c["G"] * c["hkv"], num_kv_heads=c["hkv"],
+                        head_dim=c["D"], block_size=c["bs"], kv_dtype=c["kv"], q_dtype=c["qd"], seed=seed,
+                        q_lens=c["ql"], pad_rows=c["pad"], device=DEV)
+    case.window = c["window"]
+    step = DecodeStep.for_case(case, PlanConfig(cu_count=c["cu"], max_partitions=c["P"], tile_tokens=c["T"]))
+    step.out.fill_(float("nan"))
+    step.workspace.fill_(0xFF)                      # NaN pattern in every partial and piece state
+    if c["mode"] == "attention":
+        out = step.run_case(case, whole=True)
+    else:
+        out = step.run_case(case, fused=c["mode"] == "merge_in_call")
+    got = to_f64(out)
+    ref = oracle_direct(case)
+    assert_close(got, ref, tolerance_kind(case), f"fuzz seed {seed}")
+    if case.window == 0:
+        assert (got[_zero_rows(case)] == 0.0).all()
+    else:
+        assert (got[np.all(ref == 0.0, axis=(1, 2))] == 0.0).all()
