@@ -1,4 +1,4 @@
-"""Randomised decode parity against the fp64 oracle, element by element.
+"""Randomised decode and prefill parity against the fp64 oracle, element by element.
 
 Each seed draws one small batch over the whole supported space: head_dim 64/128/256; pages of
 16/64/128 tokens and tiles that are multiples of them; bf16, fp8 (e4m3fn) and fp32 caches with bf16
@@ -6,7 +6,8 @@ or fp32 queries; group sizes 1-8 with or without verify rows (per-token causal r
 vllm-rdna PR #29, Change 1) and padding rows; partition ceilings 1-256 and budgets from one slot
 per request (where the decode shares the slots) to 2 x 256 compute units (ROCm/ATOM PR #2366,
 section 1); sliding windows; and the three call forms (decode with the merge in the call, decode
-then pa_merge, pa_attention).  The cases are small enough for the oracle to finish in well under a
+then pa_merge, pa_attention).  The prefill draws are prompts and chunks behind prefixes of up to 2000
+keys through both pa_prefill forms.  The cases are small enough for the oracle to finish in well under a
 second each; the tolerances are the ones every parity test uses.
 """
 import numpy as np
@@ -70,3 +71,51 @@ def test_decode_fuzz(seed):
         assert (got[_zero_rows(case)] == 0.0).all()
     else:
         assert (got[np.all(ref == 0.0, axis=(1, 2))] == 0.0).all()
+
+
+def _draw_prefill(seed):
+    rng = np.random.default_rng(5300 + seed)
+    D = int(rng.choice([64, 128, 256]))
+    kv = str(rng.choice(["bf16", "bf16", "fp8"]))
+    qd = str(rng.choice(["bf16", "f32"]))
+    hkv = int(rng.choice([1, 2]))
+    G = int(rng.choice([1, 2, 4, 6, 8]))
+    bs = int(rng.choice([16, 64, 128]))
+    Bn = int(rng.integers(1, 4))
+    ql = rng.integers(1, 161, size=Bn)
+    prefix = np.where(rng.random(Bn) < 0.4, 0, rng.integers(0, 2001, size=Bn))
+    ctx = (ql + prefix).tolist()
+    pad = int(rng.integers(0, 3))
+    window = int(rng.choice([0, 0, 1, 29, 300, 1500]))
+    cu = int(rng.choice([8, 64, 256]))
+    return dict(D=D, kv=kv, qd=qd, hkv=hkv, G=G, bs=bs, ctx=ctx, ql=ql.tolist(), pad=pad, window=window, cu=cu,
+                split=bool(seed % 2 == 0))
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_prefill_fuzz(seed):
+    """pa_prefill on random prompts and chunks behind prefixes, in the split form (query blocks planned,
+    computed by the query-block kernel, merged) and the one-launch form."""
+    import torch
+    from paged_split_kv_amd import binding as B
+
+    c = _draw_prefill(seed)
+    announce(f"prefill fuzz seed {seed}: " + " ".join(f"{k}={v}" for k, v in c.items()))
+    case = W.build_case(f"pfuzz{seed}", c["ctx"], num_q_heads=c["G"] * c["hkv"], num_kv_heads=c["hkv"],
+                        head_dim=c["D"], block_size=c["bs"], kv_dtype=c["kv"], q_dtype=c["qd"], seed=seed,
+                        q_lens=c["ql"], pad_rows=c["pad"], device=DEV)
+    case.window = c["window"]
+    out = torch.full_like(case.q, float("nan"))
+    ws = None
+    if c["split"]:
+        nbytes = B.pa_prefill_workspace_bytes(case.num_rows, case.num_seqs, case.num_q_heads, case.num_kv_heads,
+                                              case.head_dim, c["cu"])
+        ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=DEV)
+    B.pa_prefill(case.q, case.k_cache, case.v_cache, case.kv_dtype, case.block_tables, case.context_lens,
+                 case.cu_query_lens, out, ws, scale=case.scale, cu_count=c["cu"], k_scale=case.k_scale,
+                 v_scale=case.v_scale, sliding_window=case.window)
+    torch.cuda.synchronize()
+    got = to_f64(out)
+    ref = oracle_direct(case)
+    assert_close(got, ref, tolerance_kind(case), f"prefill fuzz seed {seed}")
+    assert (got[np.all(ref == 0.0, axis=(1, 2))] == 0.0).all()
