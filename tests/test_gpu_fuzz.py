@@ -7,7 +7,8 @@ vllm-rdna PR #29, Change 1) and padding rows; partition ceilings 1-256 and budge
 per request (where the decode shares the slots) to 2 x 256 compute units (ROCm/ATOM PR #2366,
 section 1); sliding windows; and the three call forms (decode with the merge in the call, decode
 then pa_merge, pa_attention).  The prefill draws are prompts and chunks behind prefixes of up to 2000
-keys through both pa_prefill forms.  The cases are small enough for the oracle to finish in well under a
+keys through both pa_prefill forms; the mixed draws are decodes-first batches (decodes of up to 1 + k
+rows, then prompts) through the decode-first split in its three forms.  The cases are small enough for the oracle to finish in well under a
 second each; the tolerances are the ones every parity test uses.
 """
 import numpy as np
@@ -118,4 +119,48 @@ def test_prefill_fuzz(seed):
     got = to_f64(out)
     ref = oracle_direct(case)
     assert_close(got, ref, tolerance_kind(case), f"prefill fuzz seed {seed}")
+    assert (got[np.all(ref == 0.0, axis=(1, 2))] == 0.0).all()
+
+
+def _draw_mixed(seed):
+    rng = np.random.default_rng(6100 + seed)
+    D = int(rng.choice([64, 128, 256]))
+    kv = str(rng.choice(["bf16", "fp8"]))
+    qd = str(rng.choice(["bf16", "f32"]))
+    hkv = int(rng.choice([1, 2]))
+    G = int(rng.choice([1, 2, 4, 6, 8]))
+    bs = int(rng.choice([16, 64]))
+    k = int(rng.choice([0, 0, 1, 2]))                # draft tokens: decodes carry up to 1 + k rows
+    nd = int(rng.integers(1, 9))
+    npr = int(rng.integers(0, 3))
+    dq = rng.integers(1, 2 + k, size=nd)
+    pq = rng.integers(2 + k, 130, size=npr)
+    ql = np.concatenate([dq, pq]).astype(np.int64)
+    prefix = np.where(rng.random(nd + npr) < 0.2, 0, rng.integers(0, 3000, size=nd + npr))
+    ctx = (ql + prefix).tolist()
+    window = int(rng.choice([0, 0, 0, 64, 900]))
+    mode = ("one_call", "two_calls", "two_streams")[seed % 3]
+    return dict(D=D, kv=kv, qd=qd, hkv=hkv, G=G, bs=bs, threshold=1 + k, ctx=ctx, ql=ql.tolist(),
+                window=window, mode=mode)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_mixed_fuzz(seed):
+    """Decodes-first mixed batches through the decode-first split: pa_attention_mixed in one call, and
+    pa_prefill then pa_attention on one stream and on two."""
+    import torch
+    from paged_split_kv_amd.runner import mixed_step
+
+    c = _draw_mixed(seed)
+    announce(f"mixed fuzz seed {seed}: " + " ".join(f"{k}={v}" for k, v in c.items() if k != "ctx"))
+    case = W.build_case(f"mfuzz{seed}", c["ctx"], num_q_heads=c["G"] * c["hkv"], num_kv_heads=c["hkv"],
+                        head_dim=c["D"], block_size=c["bs"], kv_dtype=c["kv"], q_dtype=c["qd"], seed=seed,
+                        q_lens=c["ql"], device=DEV)
+    case.window = c["window"]
+    out = mixed_step(case, c["threshold"], PlanConfig(cu_count=256), concurrent=c["mode"] == "two_streams",
+                     one_call=c["mode"] == "one_call")
+    torch.cuda.synchronize()
+    got = to_f64(out)
+    ref = oracle_direct(case)
+    assert_close(got, ref, tolerance_kind(case), f"mixed fuzz seed {seed}")
     assert (got[np.all(ref == 0.0, axis=(1, 2))] == 0.0).all()
