@@ -973,6 +973,20 @@ __global__ __launch_bounds__((64 * NWAVES), (Mfma<D, NCB, KV8, NWAVES>::WAVES)) 
 
     u32x4_t kreg[C::PF][C::NLD], vreg[C::PF][C::NLD];
     int nvalid_st[C::PF];
+    // The 16-byte piece of a chunk that lane `lane` holds in load step it: row r, 16-byte HBM column
+    // c.  By default the pieces go to the lanes in row-major order.  With fp8 at head_dim 128 (8 HBM
+    // columns a row) each widened piece fills LDS columns 2c and 2c + 1 of a 16-column row, and eight
+    // lanes of a row storing columns 2c would meet on the same banks (columns c and c + 4); so there
+    // each group of eight lanes takes half of two adjacent rows instead (four lanes, 64 contiguous
+    // bytes, per row), whose swizzled columns then differ in their low three bits.
+    auto piece_row = [&](int it) -> int {
+        if constexpr (KV8 && C::GCPR == 8) return 8 * it + 2 * (lane >> 4) + ((lane >> 2) & 1);
+        return (it * 64 + lane) / C::GCPR;
+    };
+    auto piece_col = [&](int it) -> int {
+        if constexpr (KV8 && C::GCPR == 8) return 4 * ((lane >> 3) & 1) + (lane & 3);
+        return (it * 64 + lane) % C::GCPR;
+    };
     // K and V of the wave's k-th chunk from page `page`: 16 rows of GRB bytes each, one 16-byte
     // load per lane and step, non-temporal.  A chunk past the wave's work, past the context or on an
     // invalid page loads zeros (no records) and stages as an empty chunk.
@@ -994,10 +1008,11 @@ __global__ __launch_bounds__((64 * NWAVES), (Mfma<D, NCB, KV8, NWAVES>::WAVES)) 
             const_cast<uint8_t*>(a.v_cache + base), 0, records, kRawBufferWord3);
 #pragma unroll
         for (int it = 0; it < C::NLD; ++it) {
+            const int off = (piece_row(it) * C::GCPR + piece_col(it)) * 16;
             kreg[st][it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                           rk, (it * 64 + lane) * 16, 0, kLoadNonTemporal));
+                                                           rk, off, 0, kLoadNonTemporal));
             vreg[st][it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                           rv, (it * 64 + lane) * 16, 0, kLoadNonTemporal));
+                                                           rv, off, 0, kLoadNonTemporal));
         }
     };
 
@@ -1007,9 +1022,8 @@ __global__ __launch_bounds__((64 * NWAVES), (Mfma<D, NCB, KV8, NWAVES>::WAVES)) 
         uint8_t* const vlds = klds + 16 * C::LRB;
 #pragma unroll
         for (int it = 0; it < C::NLD; ++it) {
-            const int f = it * 64 + lane;
-            const int r = f / C::GCPR;
-            const int c = f - r * C::GCPR;
+            const int r = piece_row(it);
+            const int c = piece_col(it);
             u32x4_t kv = kreg[st][it];
             u32x4_t vv = vreg[st][it];
             if (!full) {
