@@ -745,6 +745,18 @@ __global__ __launch_bounds__((64 * NWAVES), (Mfma<D, NCB, KV8, NWAVES>::WAVES)) 
         constexpr int PF = C::PF;
         u32x4_t kreg[PF][C::VLD], vreg[PF][C::VLD];
         int nvalid_st[PF];
+        // The 16-byte piece of the wave's slice that lane `lane` holds in load step it: row r, column c
+        // of the slice.  Row-major, except fp8 slices of 8 columns, which widen to 16 LDS columns a row:
+        // there each group of eight lanes takes half of two adjacent rows, so that the eight lanes
+        // storing in one cycle do not meet on the same banks (columns c and c + 4 of a row would).
+        auto vpiece_row = [&](int it) -> int {
+            if constexpr (KV8 && C::VGC == 8) return 8 * it + 2 * (lane >> 4) + ((lane >> 2) & 1);
+            return (it * 64 + lane) / C::VGC;
+        };
+        auto vpiece_col = [&](int it) -> int {
+            if constexpr (KV8 && C::VGC == 8) return 4 * ((lane >> 3) & 1) + (lane & 3);
+            return (it * 64 + lane) % C::VGC;
+        };
         // this wave's K and V columns, 16-byte pieces, row-major, non-temporal; a chunk past the
         // slot, the context or on an invalid page loads zeros (no records)
         auto issue = [&](int st, int k, int page) {
@@ -764,9 +776,8 @@ __global__ __launch_bounds__((64 * NWAVES), (Mfma<D, NCB, KV8, NWAVES>::WAVES)) 
                 const_cast<uint8_t*>(a.v_cache + base), 0, records, kRawBufferWord3);
 #pragma unroll
             for (int it = 0; it < C::VLD; ++it) {
-                const int f = it * 64 + lane;
-                const int r = f / C::VGC;
-                const int c = f - r * C::VGC;
+                const int r = vpiece_row(it);
+                const int c = vpiece_col(it);
                 const int o = r * C::GRB + dcol0 * C::ESZ + 16 * c;
                 kreg[st][it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, kLoadNonTemporal));
                 vreg[st][it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, kLoadNonTemporal));
@@ -792,9 +803,8 @@ __global__ __launch_bounds__((64 * NWAVES), (Mfma<D, NCB, KV8, NWAVES>::WAVES)) 
             compiler_fence();
 #pragma unroll
             for (int it = 0; it < C::VLD; ++it) {
-                const int f = it * 64 + lane;
-                const int r = f / C::VGC;
-                const int c = f - r * C::VGC;
+                const int r = vpiece_row(it);
+                const int c = vpiece_col(it);
                 u32x4_t kv = kreg[st][it];
                 u32x4_t vv = vreg[st][it];
                 if (nv < 16) {
