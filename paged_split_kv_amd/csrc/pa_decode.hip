@@ -501,6 +501,15 @@ __device__ __forceinline__ int lds_col(int r, int c) {
     return r * LRB + ((c ^ (r & SWM)) << 4);
 }
 
+// The same for the head-split path's bf16 V tiles, whose reads are the transposed 8-byte ones: with 16
+// columns a row the XOR is ((r & 7) << 1) | ((r >> 3) & 1), so rows r and r ^ 1, which a read cycle
+// takes together, land on different bank groups (verify decode 45.4 -> 45.3 us).
+template <int LRB, int SWM>
+__device__ __forceinline__ int lds_vcol(int r, int c) {
+    const int x = SWM == 15 ? (((r & 7) << 1) | ((r >> 3) & 1)) : (r & SWM);
+    return r * LRB + ((c ^ x) << 4);
+}
+
 // Rescale threshold of the running maximum, in base-2 units: probabilities stay below 2^8.
 constexpr float kRescaleSlack = 8.0f;
 
@@ -813,9 +822,8 @@ __global__ __launch_bounds__((64 * NWAVES), (Mfma<D, NCB, KV8, NWAVES>::WAVES)) 
                     vv = r < nv ? vv : z;
                 }
                 if constexpr (!KV8) {
-                    const int off = lds_col<C::VLRB, C::VSWM>(r, c);
-                    *reinterpret_cast<u32x4_t*>(klds + off) = kv;
-                    *reinterpret_cast<u32x4_t*>(vlds + off) = vv;
+                    *reinterpret_cast<u32x4_t*>(klds + lds_col<C::VLRB, C::VSWM>(r, c)) = kv;
+                    *reinterpret_cast<u32x4_t*>(vlds + lds_vcol<C::VLRB, C::VSWM>(r, c)) = vv;
                 } else {
                     // 16 fp8 codes -> 16 bf16 values = two LDS columns (2c, 2c+1), widened exactly
                     u32x4_t klo, khi, vlo, vhi;
@@ -867,7 +875,9 @@ __global__ __launch_bounds__((64 * NWAVES), (Mfma<D, NCB, KV8, NWAVES>::WAVES)) 
 #pragma unroll
             for (int t = 0; t < C::DTW; ++t) {
                 const int d0 = 16 * t + tr_d0;
-                const int off = lds_col<C::VLRB, C::VSWM>(tr_row, d0 >> 3) + ((d0 & 7) << 1);
+                // fp8 V tiles keep the K layout (their stores take two columns per lane)
+                const int off = (KV8 ? lds_col<C::VLRB, C::VSWM>(tr_row, d0 >> 3)
+                                     : lds_vcol<C::VLRB, C::VSWM>(tr_row, d0 >> 3)) + ((d0 & 7) << 1);
                 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
                 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
                 const bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(vlds + off));
