@@ -13,9 +13,11 @@ second each; the tolerances are the ones every parity test uses.
 """
 import numpy as np
 import pytest
+import torch
 
+from paged_split_kv_amd import binding as B
 from paged_split_kv_amd import workloads as W
-from paged_split_kv_amd.runner import DecodeStep, PlanConfig
+from paged_split_kv_amd.runner import DecodeStep, PlanConfig, mixed_step
 from _util import announce, assert_close, oracle_direct, to_f64, tolerance_kind
 from test_gpu_decode import _zero_rows
 
@@ -97,9 +99,6 @@ def _draw_prefill(seed):
 def test_prefill_fuzz(seed):
     """pa_prefill on random prompts and chunks behind prefixes, in the split form (query blocks planned,
     computed by the query-block kernel, merged) and the one-launch form."""
-    import torch
-    from paged_split_kv_amd import binding as B
-
     c = _draw_prefill(seed)
     announce(f"prefill fuzz seed {seed}: " + " ".join(f"{k}={v}" for k, v in c.items()))
     case = W.build_case(f"pfuzz{seed}", c["ctx"], num_q_heads=c["G"] * c["hkv"], num_kv_heads=c["hkv"],
@@ -148,9 +147,6 @@ def _draw_mixed(seed):
 def test_mixed_fuzz(seed):
     """Decodes-first mixed batches through the decode-first split: pa_attention_mixed in one call, and
     pa_prefill then pa_attention on one stream and on two."""
-    import torch
-    from paged_split_kv_amd.runner import mixed_step
-
     c = _draw_mixed(seed)
     announce(f"mixed fuzz seed {seed}: " + " ".join(f"{k}={v}" for k, v in c.items() if k != "ctx"))
     case = W.build_case(f"mfuzz{seed}", c["ctx"], num_q_heads=c["G"] * c["hkv"], num_kv_heads=c["hkv"],
