@@ -445,10 +445,11 @@ struct Mfma {
     static constexpr int KSTEPS = D / 32;              // k-steps of the S^T product
     static constexpr int DT = D / 16;                  // 16-wide d tiles of the P.V product
     static constexpr int NW = NWAVES;                  // waves per workgroup
-    // Chunk dealing: by default a wave takes units of the plan's largest slot split NW ways (small
-    // slots run fewer, fully loaded waves).  The 8-wave form, used when every request is one slot
-    // (slot sizes then follow the request lengths), splits each slot evenly over its waves instead,
-    // so short slots still run every wave and the longest gets twice the waves of a 4-wave group.
+    // Chunk dealing (see the streaming loop): the 4-wave form splits each slot evenly over its waves
+    // when the plan's largest slot is long enough, and deals units of the largest slot otherwise.
+    // The 8-wave form, used when every request is one slot (slot sizes then follow the request
+    // lengths), always splits each slot evenly, so short slots still run every wave and the longest
+    // gets twice the waves of a 4-wave group.
     static constexpr bool EVEN = NW > 4;
     // head_dim 256 (DS): the waves work in groups of SPLIT that split the head dimension, each group
     // walking its own stream of the slot's chunks (chunks s, s + NS, ...).  A wave loads its SL
